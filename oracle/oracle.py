@@ -1,0 +1,249 @@
+"""ctypes front end of the fp64 CPU oracle (``gs_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it. The product path (the HIP library and its binding)
+never imports it. It is built with gcc, independently of the HIP library.
+
+Every function takes NumPy arrays; float inputs are widened to float64
+exactly before the call, so the oracle sees the same numbers as the GPU.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gs_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libgs_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+TILE = 16
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP for independent pixels/Gaussians)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wno-unused-function",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+                build(force=True)
+            L = C.CDLL(_LIB_PATH)
+            P = C.c_void_p
+            i64, i32, f64 = C.c_int64, C.c_int, C.c_double
+            L.orc_preprocess.argtypes = [i64, P, i32, i32, f64, f64] + [P] * 5 + [P] * 10
+            L.orc_preprocess.restype = None
+            L.orc_bin_sort.argtypes = [i64, i32, i32, P, P, P, i64, P, P, P]
+            L.orc_bin_sort.restype = i64
+            L.orc_render_fwd.argtypes = [i32, i32] + [P] * 10
+            L.orc_render_fwd.restype = None
+            L.orc_render_fwd_pixels.argtypes = [i32, i32] + [P] * 7 + [i64, P, P, P, P]
+            L.orc_render_fwd_pixels.restype = None
+            L.orc_match_fwd.argtypes = [i32, i32] + [P] * 10 + [f64, i32, f64, P]
+            L.orc_match_fwd.restype = i64
+            L.orc_render_bwd.argtypes = [i32, i32, i64] + [P] * 9
+            L.orc_render_bwd.restype = None
+            L.orc_preprocess_bwd.argtypes = [i64, P, i32, i32, f64, f64] + [P] * 6 + [P] * 6
+            L.orc_preprocess_bwd.restype = None
+            L.orc_sh_basis.argtypes = [i32, f64, f64, f64, P]
+            L.orc_sh_basis_grad.argtypes = [i32, f64, f64, f64, P]
+            L.orc_decision_hash.argtypes = [i32, i32] + [P] * 5
+            L.orc_decision_hash.restype = C.c_uint64
+            L.orc_set_threads.argtypes = [i32]
+            L.orc_max_threads.restype = i32
+            _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _d(a, shape=None):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    return a if shape is None else a.reshape(shape)
+
+
+def set_threads(n: int) -> None:
+    lib().orc_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
+
+
+def sh_basis(deg, d):
+    K = (deg + 1) ** 2
+    out = np.zeros(K)
+    lib().orc_sh_basis(deg, float(d[0]), float(d[1]), float(d[2]), _p(out))
+    return out
+
+
+def sh_basis_grad(deg, d):
+    K = (deg + 1) ** 2
+    out = np.zeros((K, 3))
+    lib().orc_sh_basis_grad(deg, float(d[0]), float(d[1]), float(d[2]), _p(out))
+    return out
+
+
+def cam_array(cam) -> np.ndarray:
+    return cam.as_array() if hasattr(cam, "as_array") else _d(cam)
+
+
+def preprocess(means, scales, quats, opac, sh, cam, deg, lowpass=0.3, near=0.2):
+    """Steps O1-O10 for every Gaussian; returns a dict of float64/int arrays."""
+    means, scales, quats, opac = _d(means), _d(scales), _d(quats), _d(opac)
+    sh = _d(sh)
+    N = means.shape[0]
+    rows = sh.shape[1] if sh.ndim == 3 else 1
+    out = dict(
+        means2d=np.zeros((N, 2)), depth=np.zeros(N), cov2d=np.zeros((N, 3)), conic=np.zeros((N, 3)),
+        rgb=np.zeros((N, 3)), radii=np.zeros(N, np.int32), rect=np.zeros((N, 4), np.int64),
+        tiles=np.zeros(N, np.int64), clamp=np.zeros((N, 3), np.uint8), margin=np.zeros(N),
+    )
+    cv = cam_array(cam)
+    lib().orc_preprocess(N, _p(cv), deg, rows, float(np.float32(lowpass)), float(np.float32(near)),
+                         _p(means), _p(scales), _p(quats), _p(opac), _p(sh),
+                         _p(out["means2d"]), _p(out["depth"]), _p(out["cov2d"]), _p(out["conic"]),
+                         _p(out["rgb"]), _p(out["radii"]), _p(out["rect"]), _p(out["tiles"]),
+                         _p(out["clamp"]), _p(out["margin"]))
+    return out
+
+
+def bin_sort(means2d, radii, depth32, W, H):
+    """Step O11: returns (keys u64[P], values u32[P], ranges u32[TX*TY, 2])."""
+    means2d = _d(means2d)
+    radii = np.ascontiguousarray(radii, dtype=np.int32)
+    depth32 = np.ascontiguousarray(depth32, dtype=np.float32)
+    N = means2d.shape[0]
+    L = lib()
+    P = L.orc_bin_sort(N, W, H, _p(means2d), _p(radii), _p(depth32), 0, None, None, None)
+    TX, TY = (W + TILE - 1) // TILE, (H + TILE - 1) // TILE
+    keys = np.zeros(max(P, 1), np.uint64)
+    values = np.zeros(max(P, 1), np.uint32)
+    ranges = np.zeros((TX * TY, 2), np.uint32)
+    P2 = L.orc_bin_sort(N, W, H, _p(means2d), _p(radii), _p(depth32), P, _p(keys), _p(values), _p(ranges))
+    assert P2 == P
+    return keys[:P], values[:P], ranges
+
+
+def render_fwd(W, H, ranges, values, means2d, conic, opac, rgb, bg=(0.0, 0.0, 0.0)):
+    """Step O12 over the image: (image[3,H,W], final_T[H,W], n_contrib[H,W])."""
+    ranges = np.ascontiguousarray(ranges, np.uint32)
+    values = np.ascontiguousarray(values, np.uint32) if len(values) else np.zeros(1, np.uint32)
+    image = np.zeros((3, H, W))
+    T = np.zeros((H, W))
+    nc = np.zeros((H, W), np.uint32)
+    lib().orc_render_fwd(W, H, _p(ranges), _p(values), _p(_d(means2d)), _p(_d(conic)), _p(_d(opac)),
+                         _p(_d(rgb)), _p(_d(bg)), _p(image), _p(T), _p(nc))
+    return image, T, nc
+
+
+def render_fwd_pixels(W, H, ranges, values, means2d, conic, opac, rgb, pix, bg=(0.0, 0.0, 0.0)):
+    """Step O12 at the sampled pixels ``pix`` (flat indices py*W+px)."""
+    pix = np.ascontiguousarray(pix, np.int64)
+    n = pix.shape[0]
+    img = np.zeros((n, 3))
+    T = np.zeros(n)
+    nc = np.zeros(n, np.uint32)
+    values = np.ascontiguousarray(values, np.uint32) if len(values) else np.zeros(1, np.uint32)
+    lib().orc_render_fwd_pixels(W, H, _p(np.ascontiguousarray(ranges, np.uint32)), _p(values),
+                                _p(_d(means2d)), _p(_d(conic)), _p(_d(opac)), _p(_d(rgb)), _p(_d(bg)),
+                                n, _p(pix), _p(img), _p(T), _p(nc))
+    return img, T, nc
+
+
+def match_fwd(W, H, ranges, values, means2d, conic, opac, rgb, gpu_image, gpu_T, gpu_nc,
+              bg=(0.0, 0.0, 0.0), d_alpha=4e-6, max_amb=4, tol=1e-5):
+    """Decision-aware comparison of an fp32 forward with step O12.
+
+    Returns the per-pixel status (0 natural match, 1 match on another branch of
+    a decision within rounding of its threshold, 2 masked, 3 mismatch)."""
+    status = np.zeros((H, W), np.int8)
+    values = np.ascontiguousarray(values, np.uint32) if len(values) else np.zeros(1, np.uint32)
+    lib().orc_match_fwd(W, H, _p(np.ascontiguousarray(ranges, np.uint32)), _p(values), _p(_d(means2d)),
+                        _p(_d(conic)), _p(_d(opac)), _p(_d(rgb)), _p(_d(bg)),
+                        _p(np.ascontiguousarray(gpu_image, np.float32)),
+                        _p(np.ascontiguousarray(gpu_T, np.float32)),
+                        _p(np.ascontiguousarray(gpu_nc, np.uint32)), float(d_alpha), int(max_amb),
+                        float(tol), _p(status))
+    return status
+
+
+def render_bwd(W, H, N, ranges, values, means2d, conic, opac, rgb, dL_dimage, bg=(0.0, 0.0, 0.0)):
+    """Step O13: per-Gaussian sums grad2d[N, 9] = (drgb, dopacity, da, db, dc, du, dv)."""
+    grad2d = np.zeros((N, 9))
+    values = np.ascontiguousarray(values, np.uint32) if len(values) else np.zeros(1, np.uint32)
+    lib().orc_render_bwd(W, H, N, _p(np.ascontiguousarray(ranges, np.uint32)), _p(values), _p(_d(means2d)),
+                         _p(_d(conic)), _p(_d(opac)), _p(_d(rgb)), _p(_d(bg)), _p(_d(dL_dimage)),
+                         _p(grad2d))
+    return grad2d
+
+
+def preprocess_bwd(means, scales, quats, opac, sh, cam, deg, grad2d, lowpass=0.3, near=0.2):
+    """Step O14: parameter gradients from grad2d (fresh zero buffers)."""
+    means, scales, quats, opac, sh = _d(means), _d(scales), _d(quats), _d(opac), _d(sh)
+    N = means.shape[0]
+    rows = sh.shape[1] if sh.ndim == 3 else 1
+    g = dict(means=np.zeros((N, 3)), scales=np.zeros((N, 3)), quats=np.zeros((N, 4)),
+             opacities=np.zeros(N), sh=np.zeros_like(sh), means2d=np.zeros((N, 2)))
+    lib().orc_preprocess_bwd(N, _p(cam_array(cam)), deg, rows, float(np.float32(lowpass)),
+                             float(np.float32(near)), _p(means), _p(scales), _p(quats), _p(opac), _p(sh),
+                             _p(_d(grad2d)), _p(g["means"]), _p(g["scales"]), _p(g["quats"]),
+                             _p(g["opacities"]), _p(g["sh"]), _p(g["means2d"]))
+    return g
+
+
+def decision_hash(W, H, ranges, values, means2d, conic, opac):
+    """Hash of every pixel's O12 decisions (blended entries, alpha clamps, stop)."""
+    values = np.ascontiguousarray(values, np.uint32) if len(values) else np.zeros(1, np.uint32)
+    return int(lib().orc_decision_hash(W, H, _p(np.ascontiguousarray(ranges, np.uint32)), _p(values),
+                                       _p(_d(means2d)), _p(_d(conic)), _p(_d(opac))))
+
+
+def ldl_to_conic(q):
+    """Standard conic (a, b, c) of a quadratic form given as q = (a, beta, gamma)
+    with Q(d) = a (dx + beta dy)^2 + gamma dy^2, i.e. b = a beta, c = gamma + a beta^2."""
+    q = _d(q)
+    a, be, ga = q[:, 0], q[:, 1], q[:, 2]
+    return np.stack([a, a * be, ga + a * be * be], axis=1)
+
+
+def forward(params, cam, deg, lowpass=0.3, near=0.2, bg=(0.0, 0.0, 0.0)):
+    """O1-O12 end to end from raw parameters. ``params`` has means, scales,
+    quats, opacities, sh (NumPy). Returns every intermediate."""
+    pre = preprocess(params["means"], params["scales"], params["quats"], params["opacities"], params["sh"],
+                     cam, deg, lowpass, near)
+    W, H = int(cam.width), int(cam.height)
+    depth32 = pre["depth"].astype(np.float32)
+    keys, values, ranges = bin_sort(pre["means2d"], pre["radii"], depth32, W, H)
+    image, T, nc = render_fwd(W, H, ranges, values, pre["means2d"], pre["conic"], params["opacities"],
+                              pre["rgb"], bg)
+    return dict(pre=pre, keys=keys, values=values, ranges=ranges, image=image, final_T=T, n_contrib=nc)
+
+
+def backward(params, cam, deg, fwd, dL_dimage, lowpass=0.3, near=0.2, bg=(0.0, 0.0, 0.0)):
+    """O13-O14 end to end, using the intermediates of :func:`forward`."""
+    pre = fwd["pre"]
+    W, H = int(cam.width), int(cam.height)
+    N = pre["means2d"].shape[0]
+    grad2d = render_bwd(W, H, N, fwd["ranges"], fwd["values"], pre["means2d"], pre["conic"],
+                        params["opacities"], pre["rgb"], dL_dimage, bg)
+    g = preprocess_bwd(params["means"], params["scales"], params["quats"], params["opacities"], params["sh"],
+                       cam, deg, grad2d, lowpass, near)
+    g["grad2d"] = grad2d
+    return g

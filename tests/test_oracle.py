@@ -1,0 +1,481 @@
+"""Pins of the fp64 oracle to facts outside itself (CPU only).
+
+Each check ties the oracle to something it does not compute the same way:
+closed forms of the compositing rule, library routines (SciPy rotations and
+spherical harmonics, NumPy eigenvalues and inverses), brute-force enumeration
+and central finite differences of its own forward. Together they catch a
+dropped term, a wrong sign or index and a transposed operand anywhere in the
+O1-O14 steps.
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy.spatial.transform import Rotation
+from scipy.special import sph_harm_y
+
+from differentiable_gaussian_splat_amd.scenes import SH_C0, Camera, make_scene
+from oracle import oracle as O
+
+A_MAX = float(np.float32(0.99))
+A_MIN = float(np.float32(1.0) / np.float32(255.0))
+T_MIN = float(np.float32(1e-4))
+
+
+def cam_of(W, H, f, cx, cy, R=None, t=None, fy=None):
+    R = np.eye(3, dtype=np.float32) if R is None else np.asarray(R, np.float32)
+    t = np.zeros(3, np.float32) if t is None else np.asarray(t, np.float32)
+    return Camera(W, H, float(f), float(f if fy is None else fy), float(cx), float(cy), R, t)
+
+
+def world_of(cam, xc):
+    """World point whose camera-frame coordinates are xc (x_c = R x_w + t)."""
+    R = cam.R.astype(np.float64)
+    return (R.T @ (np.asarray(xc, np.float64) - cam.t.astype(np.float64))).astype(np.float64)
+
+
+def params_of(means, scales, quats, opac, rgb=None, sh=None):
+    means = np.atleast_2d(np.asarray(means, np.float64))
+    n = means.shape[0]
+    if sh is None:
+        rgb = np.broadcast_to(np.asarray(rgb, np.float64), (n, 3))
+        sh = ((rgb - 0.5) / SH_C0).reshape(n, 1, 3)
+    return dict(means=means, scales=np.broadcast_to(np.asarray(scales, np.float64), (n, 3)).copy(),
+                quats=np.broadcast_to(np.asarray(quats, np.float64), (n, 4)).copy(),
+                opacities=np.broadcast_to(np.asarray(opac, np.float64), (n,)).copy(), sh=np.asarray(sh, np.float64))
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("o", [0.05, 0.5, 0.9, 0.99])
+@pytest.mark.parametrize("rotated", [False, True])
+def test_lone_gaussian_at_pixel_centre(o, rotated):
+    """A: alpha at the pixel under the mean is the opacity, whatever the shape."""
+    rng = np.random.default_rng(1)
+    R = Rotation.random(random_state=rng).as_matrix() if rotated else None
+    cam = cam_of(64, 48, 90.0, 31.3, 22.7, R, [0.3, -0.2, 0.5] if rotated else None)
+    px, py, z = 20, 41 - 10, 3.0
+    xc = [(px + 0.5 - cam.cx) * z / cam.fx, (py + 0.5 - cam.cy) * z / cam.fy, z]
+    rgb = np.array([0.2, 0.7, 0.4])
+    p = params_of(world_of(cam, xc), [0.05, 0.02, 0.03], rng.standard_normal(4), o, rgb)
+    for lp in (0.0, 0.3):
+        f = O.forward(p, cam, 0, lowpass=lp)
+        np.testing.assert_allclose(f["image"][:, py, px], rgb * o, rtol=0, atol=1e-12)
+        assert abs(f["final_T"][py, px] - (1 - o)) < 1e-12
+        assert f["n_contrib"][py, px] == 1
+
+
+@pytest.mark.parametrize("lowpass", [0.0, 0.3])
+def test_on_axis_isotropic_closed_form(lowpass):
+    """B: on the optical axis Sigma' = (f^2 s^2 / z^2 + lowpass) I exactly."""
+    f, z, s, o = 100.0, 4.0, 0.08, 0.8
+    cam = cam_of(64, 64, f, 32.5, 32.5)
+    p = params_of([[0.0, 0.0, z]], [s, s, s], [1.0, 0, 0, 0], o, [1.0, 1.0, 1.0])
+    fw = O.forward(p, cam, 0, lowpass=lowpass)
+    var = f * f * s * s / (z * z) + float(np.float32(lowpass))  # lowpass is an fp32 parameter
+    np.testing.assert_allclose(fw["pre"]["cov2d"][0], [var, 0.0, var], rtol=1e-13, atol=1e-12)
+    ii, jj = np.meshgrid(np.arange(64), np.arange(64))
+    d2 = (ii + 0.5 - 32.5) ** 2 + (jj + 0.5 - 32.5) ** 2
+    alpha = np.minimum(A_MAX, o * np.exp(-0.5 * d2 / var))
+    inside = d2 <= (3 * math.sqrt(var)) ** 2   # certainly inside the tile rect
+    expect = np.where(alpha >= A_MIN, alpha, 0.0)
+    np.testing.assert_allclose(fw["image"][0][inside], expect[inside], rtol=0, atol=1e-12)
+    assert fw["pre"]["radii"][0] == math.ceil(3 * math.sqrt(var))
+
+
+def _proj(cam, mu):
+    xc = cam.R.astype(np.float64) @ mu + cam.t.astype(np.float64)
+    return np.array([cam.fx * xc[0] / xc[2] + cam.cx, cam.fy * xc[1] / xc[2] + cam.cy])
+
+
+def test_ewa_covariance_against_fd_jacobian():
+    """B (off axis): Sigma' = J_fd Sigma J_fd^T + lowpass I, with the Jacobian of
+    the projection taken by central differences and Sigma built by SciPy."""
+    rng = np.random.default_rng(7)
+    for trial in range(60):
+        R = Rotation.random(random_state=rng).as_matrix()
+        cam = cam_of(200, 150, 170.0, 101.0, 77.0, R, rng.normal(0, 0.5, 3), fy=160.0)
+        xc = np.array([rng.uniform(-1, 1), rng.uniform(-0.8, 0.8), rng.uniform(1.5, 5)])
+        mu = world_of(cam, xc)
+        q = rng.standard_normal(4)
+        s = np.exp(rng.normal(-2.5, 0.6, 3))
+        lp = float(np.float32(0.3))
+        p = params_of(mu, s, q, 0.5, [0.5, 0.5, 0.5])
+        pre = O.preprocess(p["means"], p["scales"], p["quats"], p["opacities"], p["sh"], cam, 0, lowpass=lp)
+        Rq = Rotation.from_quat([q[1], q[2], q[3], q[0]]).as_matrix()  # SciPy stores (x, y, z, w)
+        Sig = Rq @ np.diag(s * s) @ Rq.T
+        Jfd = np.zeros((2, 3))
+        for k in range(3):
+            e = np.zeros(3)
+            e[k] = 1e-5
+            Jfd[:, k] = (_proj(cam, mu + e) - _proj(cam, mu - e)) / 2e-5
+        S2 = Jfd @ Sig @ Jfd.T + lp * np.eye(2)
+        A, B, Cc = pre["cov2d"][0]
+        np.testing.assert_allclose([A, B, Cc], [S2[0, 0], S2[0, 1], S2[1, 1]], rtol=1e-7, atol=1e-9 * S2.max())
+        # O6 conic = inverse, O7 radius from the largest eigenvalue, O8 screen mean
+        a, b, c = pre["conic"][0]
+        Sx = np.array([[A, B], [B, Cc]])
+        np.testing.assert_allclose(np.array([[a, b], [b, c]]), np.linalg.inv(Sx), rtol=1e-10)
+        lam = np.linalg.eigvalsh(Sx).max()
+        if pre["radii"][0] > 0:
+            assert pre["radii"][0] == math.ceil(3 * math.sqrt(lam))
+            np.testing.assert_allclose(pre["means2d"][0], _proj(cam, mu), rtol=1e-12)
+            xc_exact = cam.R.astype(np.float64) @ mu + cam.t.astype(np.float64)  # R is fp32, not exactly orthogonal
+            assert pre["depth"][0] == pytest.approx(xc_exact[2], rel=1e-13)
+
+
+def test_partition_of_unity_and_invariants():
+    """C: constant colour b and background b give exactly b; with rgb = 1 and
+    bg = 0 the image is 1 - final_T; final_T stays in [T_min, 1]."""
+    sc = make_scene(1, 3, n=300)
+    cam = sc.cameras[0]
+    for b in (0.0, 0.37, 1.0):
+        p = params_of(sc.means, sc.scales, sc.quats, sc.opacities, [b, b, b])
+        f = O.forward(p, cam, 0, bg=(b, b, b))
+        np.testing.assert_allclose(f["image"], b, rtol=0, atol=1e-12)
+    p = params_of(sc.means, sc.scales, sc.quats, sc.opacities, [1.0, 1.0, 1.0])
+    f = O.forward(p, cam, 0)
+    for c in range(3):
+        np.testing.assert_allclose(f["image"][c], 1.0 - f["final_T"], rtol=0, atol=1e-12)
+    assert f["final_T"].min() >= T_MIN and f["final_T"].max() <= 1.0
+    lens = (f["ranges"][:, 1] - f["ranges"][:, 0]).astype(np.int64)
+    TX = (cam.width + 15) // 16
+    tile_of = (np.arange(cam.height)[:, None] // 16) * TX + np.arange(cam.width)[None, :] // 16
+    assert np.all(f["n_contrib"] <= lens[tile_of])
+    assert np.count_nonzero(f["final_T"] < 0.5) > 100  # the scene is not trivially empty
+
+
+def test_two_gaussians_one_pixel_depth_order():
+    """D: C = c1 a1 + c2 a2 (1 - a1) with the nearer one first, whatever the index order."""
+    cam = cam_of(32, 32, 50.0, 16.0, 16.0)
+    px, py = 9, 12
+    near_z, far_z = 2.0, 5.0
+    mk = lambda z: [(px + 0.5 - 16.0) * z / 50.0, (py + 0.5 - 16.0) * z / 50.0, z]
+    c_far, c_near = np.array([0.9, 0.1, 0.3]), np.array([0.2, 0.6, 0.8])
+    o_far, o_near = 0.7, 0.4
+    sh = np.stack([((c_far - 0.5) / SH_C0), ((c_near - 0.5) / SH_C0)]).reshape(2, 1, 3)
+    p = params_of([mk(far_z), mk(near_z)], [0.05, 0.05, 0.05], [1, 0, 0, 0], [o_far, o_near], sh=sh)
+    f = O.forward(p, cam, 0)
+    expect = c_near * o_near + c_far * o_far * (1 - o_near)
+    np.testing.assert_allclose(f["image"][:, py, px], expect, atol=1e-12)
+    assert f["final_T"][py, px] == pytest.approx((1 - o_near) * (1 - o_far), abs=1e-14)
+    # an opacity below 1/255 is skipped everywhere: the image is the background
+    p2 = params_of([mk(3.0)], [0.05, 0.05, 0.05], [1, 0, 0, 0], 0.0039, [1.0, 0, 0])
+    f2 = O.forward(p2, cam, 0, bg=(0.25, 0.5, 0.75))
+    for c, v in enumerate((0.25, 0.5, 0.75)):
+        np.testing.assert_allclose(f2["image"][c], v, atol=0)
+    assert f2["n_contrib"].max() == 0
+
+
+@pytest.mark.parametrize("o", [0.3, 0.5, 0.9, 0.99])
+def test_stacked_identical_gaussians_stop_rule(o):
+    """E: k identical Gaussians: T after j blends is (1-a)^j and the entry that
+    would take T below 1e-4 is not blended."""
+    cam = cam_of(32, 32, 50.0, 16.0, 16.0)
+    px, py, z, k = 5, 6, 3.0, 40
+    mu = [(px + 0.5 - 16.0) * z / 50.0, (py + 0.5 - 16.0) * z / 50.0, z]
+    rgb = np.array([0.3, 0.5, 0.9])
+    p = params_of([mu] * k, [0.04, 0.04, 0.04], [1, 0, 0, 0], o, rgb)
+    f = O.forward(p, cam, 0)
+    a = min(o, A_MAX)
+    n = 0
+    while (1 - a) ** (n + 1) >= T_MIN:
+        n += 1
+    assert f["n_contrib"][py, px] == n
+    assert f["final_T"][py, px] == pytest.approx((1 - a) ** n, rel=1e-12)
+    np.testing.assert_allclose(f["image"][:, py, px], rgb * (1 - (1 - a) ** n), atol=1e-12)
+    # equal depths: the list order is by index
+    t = (py // 16) * 2 + px // 16
+    s, e = f["ranges"][t]
+    assert list(f["values"][s:e]) == list(range(k))
+
+
+# ---------------------------------------------------------------- binning
+
+def test_bin_sort_brute_force():
+    """F: pairs from testing every (tile, Gaussian) by the definition -- a tile
+    is touched when one of its 16 columns and one of its 16 rows (the full
+    tile, also where it overhangs the image edge) lie within r of
+    (floor u, floor v) -- sorted with Python's sorted by (tile, depth bits, g)."""
+    rng = np.random.default_rng(11)
+    W, H = 77, 45
+    TX, TY = (W + 15) // 16, (H + 15) // 16
+    N = 400
+    u = rng.uniform(-40, W + 40, N)
+    v = rng.uniform(-40, H + 40, N)
+    u[:20] = np.floor(u[:20])          # exact integers and tile edges
+    u[20:30] = 16.0 * rng.integers(-2, 6, 10)
+    r = rng.integers(-1, 30, N).astype(np.int32)
+    depth = rng.choice(np.float32([1.5, 2.25, 3.0, 7.0]), N).astype(np.float32)  # many ties
+    pairs = []
+    for g in range(N):
+        if r[g] <= 0:
+            continue
+        fu, fv = math.floor(u[g]), math.floor(v[g])
+        dbits = int(np.float32(depth[g]).view(np.uint32))
+        for ty in range(TY):
+            rows = [y for y in range(16 * ty, 16 * ty + 16) if abs(y - fv) <= r[g]]
+            if not rows:
+                continue
+            for tx in range(TX):
+                cols = [x for x in range(16 * tx, 16 * tx + 16) if abs(x - fu) <= r[g]]
+                if cols:
+                    pairs.append(((ty * TX + tx) << 32 | dbits, g))
+    pairs.sort()
+    keys, values, ranges = O.bin_sort(np.stack([u, v], 1), r, depth, W, H)
+    assert [int(k) for k in keys] == [p[0] for p in pairs]
+    assert [int(x) for x in values] == [p[1] for p in pairs]
+    tiles = np.array([p[0] >> 32 for p in pairs])
+    for t in range(TX * TY):
+        idx = np.nonzero(tiles == t)[0]
+        if len(idx):
+            assert tuple(ranges[t]) == (idx[0], idx[-1] + 1)
+        else:
+            assert tuple(ranges[t]) == (0, 0)
+
+
+# ---------------------------------------------------------------- culling
+
+def test_culling_rules():
+    cam = cam_of(64, 64, 60.0, 32.0, 32.0)
+    near = float(np.float32(0.2))
+    means = np.array([[0, 0, near], [0, 0, near * (1 + 1e-9)], [0, 0, -1.0], [np.nan, 0, 3], [0, 0, 3],
+                      [0, 0, 3], [100.0, 0, 1.0]])
+    quats = np.array([[1, 0, 0, 0]] * 7, float)
+    quats[4] = 0.0  # zero quaternion
+    p = params_of(means, [0.05, 0.05, 0.05], quats, 0.5, [0.5, 0.5, 0.5])
+    p["opacities"][5] = np.inf
+    pre = O.preprocess(p["means"], p["scales"], p["quats"], p["opacities"], p["sh"], cam, 0)
+    assert list(pre["radii"] > 0) == [False, True, False, False, False, False, False]
+
+
+# ---------------------------------------------------------------- SH basis
+
+def _real_sh_scipy(l, m, d):
+    theta = math.acos(max(-1.0, min(1.0, d[2])))
+    phi = math.atan2(d[1], d[0])
+    if m == 0:
+        return sph_harm_y(l, 0, theta, phi).real
+    Y = sph_harm_y(l, abs(m), theta, phi)
+    return math.sqrt(2) * (-1) ** m * (Y.imag if m < 0 else Y.real)
+
+
+def test_sh_basis_against_scipy():
+    """H: Y_k equals (-1)^m times the standard real spherical harmonic built
+    from SciPy's complex ones (Condon-Shortley phase kept), for k = l^2+l+m."""
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        d = rng.standard_normal(3)
+        d /= np.linalg.norm(d)
+        Y = O.sh_basis(3, d)
+        for l in range(4):
+            for m in range(-l, l + 1):
+                assert Y[l * l + l + m] == pytest.approx((-1) ** m * _real_sh_scipy(l, m, d), abs=1e-13)
+
+
+def test_sh_orthonormal_by_quadrature():
+    nth, nph = 40, 80
+    xg, wg = np.polynomial.legendre.leggauss(nth)
+    G = np.zeros((16, 16))
+    for ct, w in zip(xg, wg):
+        st = math.sqrt(1 - ct * ct)
+        for j in range(nph):
+            ph = 2 * math.pi * j / nph
+            Y = O.sh_basis(3, [st * math.cos(ph), st * math.sin(ph), ct])
+            G += w * (2 * math.pi / nph) * np.outer(Y, Y)
+    assert np.abs(G - np.eye(16)).max() < 1e-12
+
+
+def test_sh_gradient_fd():
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        d = rng.standard_normal(3)
+        g = O.sh_basis_grad(3, d)
+        for k in range(3):
+            e = np.zeros(3)
+            e[k] = 1e-6
+            fd = (O.sh_basis(3, d + e) - O.sh_basis(3, d - e)) / 2e-6
+            np.testing.assert_allclose(g[:, k], fd, atol=1e-7 * (1 + np.abs(d).max() ** 2))
+
+
+# ---------------------------------------------------------------- symmetries
+
+def test_quaternion_scale_invariance_and_translation():
+    sc = make_scene(1, 4, n=200)
+    cam = sc.cameras[0]
+    p = dict(means=sc.means.astype(np.float64), scales=sc.scales.astype(np.float64),
+             quats=sc.quats.astype(np.float64), opacities=sc.opacities.astype(np.float64),
+             sh=sc.sh.astype(np.float64))
+    f0 = O.forward(p, cam, 0)
+    p2 = dict(p, quats=p["quats"] * -2.5)
+    f1 = O.forward(p2, cam, 0)
+    np.testing.assert_allclose(f1["image"], f0["image"], atol=1e-12)
+    # translate the scene by delta and the camera with it: t' = t - R delta
+    delta = np.array([0.25, -0.125, 0.5])
+    cam2 = Camera(cam.width, cam.height, cam.fx, cam.fy, cam.cx, cam.cy, cam.R,
+                  (cam.t.astype(np.float64) - cam.R.astype(np.float64) @ delta).astype(np.float32))
+    p3 = dict(p, means=p["means"] + delta)
+    f3 = O.forward(p3, cam2, 0)
+    np.testing.assert_allclose(f3["image"], f0["image"], atol=1e-9)
+
+
+# ---------------------------------------------------------------- finite differences
+
+def fd_scene(seed, n=10, W=48, H=40, deg=3):
+    rng = np.random.default_rng(seed)
+    R = Rotation.random(random_state=rng).as_matrix()
+    cam = cam_of(W, H, 60.0, W / 2 + 0.3, H / 2 - 0.2, R, rng.normal(0, 0.3, 3))
+    z = rng.uniform(2.0, 4.0, n)
+    xc = np.stack([(rng.uniform(0, W, n) - cam.cx) * z / cam.fx, (rng.uniform(0, H, n) - cam.cy) * z / cam.fy, z], 1)
+    means = np.stack([world_of(cam, x) for x in xc])
+    K = (deg + 1) ** 2
+    sh = rng.normal(0, 0.4, (n, K, 3))
+    sh[:, 0, :] = rng.normal(0.2, 1.2, (n, 3))  # some colours clamp at 0
+    p = dict(means=means, scales=np.exp(rng.normal(-2.0, 0.4, (n, 3))), quats=rng.standard_normal((n, 4)),
+             opacities=rng.uniform(0.2, 0.95, n), sh=sh)
+    p["opacities"][:2] = 0.995  # alpha clamp reached near their centres
+    p["scales"][:2] *= 3.0
+    dL = rng.standard_normal((3, H, W))
+    return p, cam, dL
+
+
+def _signature(f):
+    pre = f["pre"]
+    W, H = f["image"].shape[2], f["image"].shape[1]
+    return (pre["radii"].tobytes(), pre["clamp"].tobytes(), f["values"].tobytes(), f["ranges"].tobytes(),
+            O.decision_hash(W, H, f["ranges"], f["values"], pre["means2d"], pre["conic"], f["opac"]))
+
+
+def _fwd(p, cam, deg):
+    f = O.forward(p, cam, deg)
+    f["opac"] = p["opacities"]
+    return f
+
+
+@pytest.mark.parametrize("seed,deg", [(1, 3), (2, 1), (3, 0)])
+def test_backward_matches_central_differences(seed, deg):
+    """G: every parameter gradient of L = sum(dL * image) agrees with central
+    differences of the oracle's own forward, wherever x +- h leave every
+    discrete decision (pairs, blended sets, stops, clamps) unchanged."""
+    p, cam, dL = fd_scene(seed, deg=deg)
+    f = _fwd(p, cam, deg)
+    sig = _signature(f)
+    g = O.backward(p, cam, deg, f, dL)
+    checked, total = 0, 0
+    for name in ("means", "scales", "quats", "opacities", "sh"):
+        an = g[name]
+        fd = np.full(an.shape, np.nan)
+        flat = p[name].reshape(-1)
+        for i in range(flat.size):
+            x0 = flat[i]
+            h = 1e-6 * max(1.0, abs(x0))
+            vals = []
+            for sgn in (1, -1):
+                flat[i] = x0 + sgn * h
+                fi = _fwd(p, cam, deg)
+                vals.append((float(np.sum(dL * fi["image"])), _signature(fi) == sig))
+            flat[i] = x0
+            if vals[0][1] and vals[1][1]:
+                fd.reshape(-1)[i] = (vals[0][0] - vals[1][0]) / (2 * h)
+        ok = ~np.isnan(fd)
+        assert ok.mean() > 0.9, name
+        err = np.abs(fd[ok] - an[ok])
+        scale = np.abs(an).max() + 1e-30
+        assert err.max() <= 1e-6 * scale + 1e-5 * np.abs(an[ok]).max(), (name, err.max(), scale)
+        assert np.linalg.norm(fd[ok] - an[ok]) <= 1e-6 * np.linalg.norm(an[ok]), name
+        checked += ok.sum()
+        total += ok.size
+    assert checked >= 0.9 * total
+    # the quaternion gradient is tangent to the sphere of q
+    assert np.abs(np.sum(g["quats"] * p["quats"], axis=1)).max() < 1e-9 * np.abs(g["quats"]).max()
+
+
+def test_render_backward_matches_central_differences():
+    """G (render stage alone): grad2d from O13 against differences of O12 in
+    its own inputs (screen mean, conic, opacity, colour)."""
+    p, cam, dL = fd_scene(21, n=8, deg=0)
+    pre = O.preprocess(p["means"], p["scales"], p["quats"], p["opacities"], p["sh"], cam, 0)
+    W, H = cam.width, cam.height
+    keys, values, ranges = O.bin_sort(pre["means2d"], pre["radii"], pre["depth"].astype(np.float32), W, H)
+    ins = dict(means2d=pre["means2d"].copy(), conic=pre["conic"].copy(), opac=p["opacities"].copy(),
+               rgb=pre["rgb"].copy())
+
+    def loss():
+        img, _, _ = O.render_fwd(W, H, ranges, values, ins["means2d"], ins["conic"], ins["opac"], ins["rgb"])
+        return float(np.sum(dL * img)), O.decision_hash(W, H, ranges, values, ins["means2d"], ins["conic"],
+                                                        ins["opac"])
+
+    _, sig = loss()
+    g2 = O.render_bwd(W, H, len(p["opacities"]), ranges, values, ins["means2d"], ins["conic"], ins["opac"],
+                      ins["rgb"], dL)
+    cols = dict(rgb=[0, 1, 2], opac=[3], conic=[4, 5, 6], means2d=[7, 8])
+    for name, cidx in cols.items():
+        arr = ins[name]
+        for gi in range(arr.shape[0]):
+            for j, col in enumerate(cidx):
+                ref = arr.reshape(arr.shape[0], -1)
+                x0 = ref[gi, j]
+                h = 1e-7 * max(1.0, abs(x0))
+                ref[gi, j] = x0 + h
+                lp, sp = loss()
+                ref[gi, j] = x0 - h
+                lm, sm = loss()
+                ref[gi, j] = x0
+                if sp != sig or sm != sig:
+                    continue
+                fd = (lp - lm) / (2 * h)
+                # the conic's off-diagonal b appears twice in Q: d/db of the pair
+                assert fd == pytest.approx(g2[gi, col], rel=1e-5, abs=1e-6 * (1 + np.abs(g2[:, col]).max())), \
+                    (name, gi, j)
+
+
+# ---------------------------------------------------------------- matcher
+
+def test_matcher_accepts_exact_and_flags_planted_error():
+    sc = make_scene(1, 1, n=400)
+    cam = sc.cameras[0]
+    p = dict(means=sc.means, scales=sc.scales, quats=sc.quats, opacities=sc.opacities, sh=sc.sh)
+    f = O.forward(p, cam, 0)
+    pre = f["pre"]
+    img32 = f["image"].astype(np.float32)
+    T32 = f["final_T"].astype(np.float32)
+    st = O.match_fwd(cam.width, cam.height, f["ranges"], f["values"], pre["means2d"], pre["conic"],
+                     sc.opacities, pre["rgb"], img32, T32, f["n_contrib"])
+    assert np.all(st <= 1)
+    img_bad = img32.copy()
+    img_bad[1, 60, 70] += 3e-5
+    nc_bad = f["n_contrib"].copy()
+    nc_bad[10, 10] += 1
+    st = O.match_fwd(cam.width, cam.height, f["ranges"], f["values"], pre["means2d"], pre["conic"],
+                     sc.opacities, pre["rgb"], img_bad, T32, nc_bad)
+    assert st[60, 70] == 3 and st[10, 10] == 3
+    assert np.count_nonzero(st == 3) == 2
+
+
+def test_matcher_accepts_other_branch_of_a_boundary_skip():
+    """A pixel whose alpha sits on 1/255 (within rounding) may be skipped or
+    blended: both images are accepted, anything else is not."""
+    cam = cam_of(32, 32, 50.0, 16.0, 16.0)
+    z = 3.0
+    px, py = 8, 8
+    mu = [(px + 0.5 - 16.0) * z / 50.0, (py + 0.5 - 16.0) * z / 50.0, z]
+    rgb = np.array([0.8, 0.4, 0.2])
+    o = A_MIN * (1 + 1e-7)       # alpha = o at the centre pixel, just above the cut
+    p = params_of([mu], [0.05, 0.05, 0.05], [1, 0, 0, 0], o, rgb)
+    f = O.forward(p, cam, 0)
+    pre = f["pre"]
+    assert f["n_contrib"][py, px] == 1
+    img = f["image"].astype(np.float32)
+    T = f["final_T"].astype(np.float32)
+    nc = f["n_contrib"].copy()
+    # the other outcome: skipped
+    img[:, py, px] = 0.0
+    T[py, px] = 1.0
+    nc[py, px] = 0
+    st = O.match_fwd(32, 32, f["ranges"], f["values"], pre["means2d"], pre["conic"], p["opacities"], pre["rgb"],
+                     img, T, nc)
+    assert st[py, px] == 1 and np.all(st <= 1)
+    img[0, py, px] = 0.5         # neither outcome
+    st = O.match_fwd(32, 32, f["ranges"], f["values"], pre["means2d"], pre["conic"], p["opacities"], pre["rgb"],
+                     img, T, nc)
+    assert st[py, px] == 3
