@@ -1,0 +1,316 @@
+// C ABI of the rasterizer: argument validation, workspace carving, launches.
+// Every entry point validates before launching anything, maps HIP failures to
+// GS_ERR_HIP with the HIP message, and lets no exception escape.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/gsplat.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gs_status fail(gs_status code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+gs_status hip_check(hipError_t e, const char* where) {
+    if (e == hipSuccess) return GS_OK;
+    return fail(GS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define REQUIRE(cond, ...)                                        \
+    do {                                                          \
+        if (!(cond)) return fail(GS_ERR_INVALID_ARG, __VA_ARGS__); \
+    } while (0)
+
+#define REQUIRE_PTR(p) REQUIRE((p) != nullptr, "%s must not be NULL", #p)
+
+struct Checked {
+    gs::DevCam cam;
+    int K, sh_rows, ntiles;
+};
+
+gs_status check_common(const gs_camera* cam, const gs_options* opt, int64_t n, Checked& out) {
+    REQUIRE_PTR(cam);
+    REQUIRE_PTR(opt);
+    REQUIRE(n >= 0 && n < ((int64_t)1 << 31), "n must be in [0, 2^31), got %lld", (long long)n);
+    REQUIRE(cam->width > 0 && cam->height > 0 && cam->width <= 32768 && cam->height <= 32768,
+            "image size must be in 1..32768, got %d x %d", cam->width, cam->height);
+    REQUIRE(isfinite(cam->fx) && isfinite(cam->fy) && cam->fx > 0.f && cam->fy > 0.f,
+            "focal lengths must be finite and > 0");
+    REQUIRE(isfinite(cam->cx) && isfinite(cam->cy), "principal point must be finite");
+    for (int i = 0; i < 9; ++i) REQUIRE(isfinite(cam->R[i]), "camera R must be finite");
+    for (int i = 0; i < 3; ++i) REQUIRE(isfinite(cam->t[i]), "camera t must be finite");
+    REQUIRE(opt->sh_degree >= 0 && opt->sh_degree <= 3, "sh_degree must be in 0..3, got %d", opt->sh_degree);
+    if (opt->tile_size != gs::TILE)
+        return fail(GS_ERR_UNSUPPORTED, "tile_size must be %d, got %d", gs::TILE, opt->tile_size);
+    int K = (opt->sh_degree + 1) * (opt->sh_degree + 1);
+    int rows = opt->sh_rows == 0 ? K : opt->sh_rows;
+    REQUIRE(rows >= K && rows <= 64, "sh_rows must be 0 or in [(deg+1)^2, 64], got %d", opt->sh_rows);
+    REQUIRE(isfinite(opt->lowpass) && opt->lowpass >= 0.f, "lowpass must be finite and >= 0");
+    REQUIRE(isfinite(opt->near_plane) && opt->near_plane > 0.f, "near_plane must be finite and > 0");
+    for (int i = 0; i < 3; ++i) REQUIRE(isfinite(opt->bg[i]), "bg must be finite");
+    gs::DevCam& d = out.cam;
+    d.W = cam->width;
+    d.H = cam->height;
+    d.TX = (cam->width + gs::TILE - 1) / gs::TILE;
+    d.TY = (cam->height + gs::TILE - 1) / gs::TILE;
+    d.fx = cam->fx;
+    d.fy = cam->fy;
+    d.cx = cam->cx;
+    d.cy = cam->cy;
+    for (int i = 0; i < 9; ++i) d.R[i] = cam->R[i];
+    for (int i = 0; i < 3; ++i) d.t[i] = cam->t[i];
+    for (int j = 0; j < 3; ++j) {  // camera centre -R^T t, formed in double
+        double c = 0.0;
+        for (int i = 0; i < 3; ++i) c -= (double)cam->R[3 * i + j] * (double)cam->t[i];
+        d.campos[j] = (float)c;
+    }
+    out.K = K;
+    out.sh_rows = rows;
+    out.ntiles = d.TX * d.TY;
+    return GS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gs_options gs_default_options(void) {
+    gs_options o;
+    o.sh_degree = 3;
+    o.sh_rows = 0;
+    o.tile_size = gs::TILE;
+    o.lowpass = 0.3f;
+    o.near_plane = 0.2f;
+    o.bg[0] = o.bg[1] = o.bg[2] = 0.f;
+    return o;
+}
+
+const char* gs_version(void) { return "gsplat-hip 0.1.0 (gfx950)"; }
+
+const char* gs_last_error(void) { return g_err; }
+
+gs_status gs_preprocess(const gs_camera* cam, const gs_options* opt, int64_t n, const float* means,
+                        const float* scales, const float* quats, const float* opacities, const float* sh,
+                        float* means2d, float* depths, float* conic_opacity, float* rgb, int32_t* radii,
+                        uint32_t* tiles_touched, uint8_t* clamped, void* stream) {
+    try {
+        g_err[0] = 0;
+        Checked c;
+        gs_status st = check_common(cam, opt, n, c);
+        if (st != GS_OK) return st;
+        if (n == 0) return GS_OK;
+        REQUIRE_PTR(means);
+        REQUIRE_PTR(scales);
+        REQUIRE_PTR(quats);
+        REQUIRE_PTR(opacities);
+        REQUIRE_PTR(sh);
+        REQUIRE_PTR(means2d);
+        REQUIRE_PTR(depths);
+        REQUIRE_PTR(conic_opacity);
+        REQUIRE_PTR(rgb);
+        REQUIRE_PTR(radii);
+        REQUIRE_PTR(tiles_touched);
+        REQUIRE_PTR(clamped);
+        REQUIRE(aligned(quats, 16), "quats must be 16-byte aligned");
+        REQUIRE(aligned(conic_opacity, 16), "conic_opacity must be 16-byte aligned");
+        REQUIRE(aligned(means2d, 8), "means2d must be 8-byte aligned");
+        return hip_check(gs::launch_preprocess(c.cam, c.K, c.sh_rows, opt->lowpass, opt->near_plane, (int)n, means,
+                                               scales, quats, opacities, sh, means2d, depths, conic_opacity, rgb,
+                                               radii, tiles_touched, clamped, (hipStream_t)stream),
+                         "gs_preprocess");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_preprocess: unexpected exception");
+    }
+}
+
+size_t gs_bin_sort_workspace_size(int64_t n, int64_t pair_capacity, int32_t width, int32_t height) {
+    if (n < 0 || pair_capacity < 0 || width <= 0 || height <= 0) return 0;
+    int ntiles = ((width + 15) / 16) * ((height + 15) / 16);
+    return gs::bin_layout(n, pair_capacity, ntiles).total;
+}
+
+gs_status gs_bin_sort(const gs_camera* cam, const gs_options* opt, int64_t n, const float* means2d,
+                      const float* depths, const int32_t* radii, const uint32_t* tiles_touched, void* workspace,
+                      size_t workspace_bytes, int64_t pair_capacity, uint64_t* keys, uint32_t* values,
+                      uint32_t* ranges, int64_t* n_pairs, void* stream) {
+    try {
+        g_err[0] = 0;
+        Checked c;
+        gs_status st = check_common(cam, opt, n, c);
+        if (st != GS_OK) return st;
+        REQUIRE_PTR(n_pairs);
+        REQUIRE_PTR(ranges);
+        REQUIRE(pair_capacity >= 0 && pair_capacity < ((int64_t)1 << 31), "pair_capacity must be in [0, 2^31)");
+        REQUIRE(pair_capacity == 0 || values != nullptr, "values must not be NULL");
+        if (n > 0) {
+            REQUIRE_PTR(means2d);
+            REQUIRE_PTR(depths);
+            REQUIRE_PTR(radii);
+            REQUIRE_PTR(tiles_touched);
+            REQUIRE_PTR(workspace);
+            REQUIRE(aligned(means2d, 8), "means2d must be 8-byte aligned");
+            REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
+        }
+        gs::BinLayout L = gs::bin_layout(n, pair_capacity, c.ntiles);
+        if (n > 0)
+            REQUIRE(workspace_bytes >= L.total, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
+        hipStream_t s = (hipStream_t)stream;
+        if (n == 0) {
+            *n_pairs = 0;
+            return hip_check(gs::launch_fill_u32(ranges, (size_t)2 * c.ntiles, 0u, s), "gs_bin_sort");
+        }
+        char* ws = reinterpret_cast<char*>(workspace);
+        st = hip_check(gs::launch_bin_count((int)n, depths, tiles_touched, ws, L, s), "gs_bin_sort(count)");
+        if (st != GS_OK) return st;
+        unsigned long long counters[2] = {0, 0};
+        st = hip_check(hipMemcpyAsync(counters, ws + L.counters, sizeof(counters), hipMemcpyDeviceToHost, s),
+                       "gs_bin_sort(readback)");
+        if (st != GS_OK) return st;
+        st = hip_check(hipStreamSynchronize(s), "gs_bin_sort(sync)");
+        if (st != GS_OK) return st;
+        unsigned long long vis = counters[0], P = counters[1];
+        *n_pairs = (int64_t)P;
+        if (P >= (1ull << 31)) return fail(GS_ERR_UNSUPPORTED, "pair count %llu exceeds 2^31 - 1", P);
+        if ((int64_t)P > pair_capacity)
+            return fail(GS_ERR_CAPACITY, "pair count %llu exceeds capacity %lld", P, (long long)pair_capacity);
+        return hip_check(gs::launch_bin_emit((int)n, (int)vis, (int)P, c.cam.TX, c.cam.TY, means2d, radii, depths, ws,
+                                             L, keys, values, ranges, s),
+                         "gs_bin_sort(emit)");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_bin_sort: unexpected exception");
+    }
+}
+
+gs_status gs_render_fwd(const gs_camera* cam, const gs_options* opt, int64_t n, const uint32_t* ranges,
+                        const uint32_t* values, int64_t n_pairs, const float* means2d, const float* conic_opacity,
+                        const float* rgb, float* image, float* final_T, uint32_t* n_contrib, void* stream) {
+    try {
+        g_err[0] = 0;
+        Checked c;
+        gs_status st = check_common(cam, opt, n, c);
+        if (st != GS_OK) return st;
+        REQUIRE_PTR(ranges);
+        REQUIRE_PTR(image);
+        REQUIRE_PTR(final_T);
+        REQUIRE_PTR(n_contrib);
+        REQUIRE(n_pairs >= 0 && n_pairs < ((int64_t)1 << 31), "n_pairs must be in [0, 2^31)");
+        if (n_pairs > 0) {
+            REQUIRE(n > 0, "n_pairs > 0 needs n > 0");
+            REQUIRE_PTR(values);
+            REQUIRE_PTR(means2d);
+            REQUIRE_PTR(conic_opacity);
+            REQUIRE_PTR(rgb);
+            REQUIRE(aligned(means2d, 8), "means2d must be 8-byte aligned");
+            REQUIRE(aligned(conic_opacity, 16), "conic_opacity must be 16-byte aligned");
+        }
+        REQUIRE(aligned(ranges, 8), "ranges must be 8-byte aligned");
+        return hip_check(gs::launch_render_fwd(c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
+                                               conic_opacity, rgb, opt->bg, image, final_T, n_contrib,
+                                               (hipStream_t)stream),
+                         "gs_render_fwd");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_render_fwd: unexpected exception");
+    }
+}
+
+size_t gs_render_bwd_workspace_size(int64_t n) {
+    if (n < 0) return 0;
+    return ((size_t)(n > 0 ? n : 1) * gs::GRAD2D_STRIDE * sizeof(float) + 255) & ~(size_t)255;
+}
+
+gs_status gs_render_bwd(const gs_camera* cam, const gs_options* opt, int64_t n, const float* means,
+                        const float* scales, const float* quats, const float* opacities, const float* sh,
+                        const float* means2d, const float* conic_opacity, const float* rgb, const int32_t* radii,
+                        const uint8_t* clamped, const uint32_t* ranges, const uint32_t* values, int64_t n_pairs,
+                        const float* final_T, const uint32_t* n_contrib, const float* dL_dimage, float* dL_dmeans,
+                        float* dL_dscales, float* dL_dquats, float* dL_dopacities, float* dL_dsh,
+                        float* dL_dmeans2d, void* workspace, size_t workspace_bytes, void* stream) {
+    try {
+        g_err[0] = 0;
+        Checked c;
+        gs_status st = check_common(cam, opt, n, c);
+        if (st != GS_OK) return st;
+        if (n == 0) return GS_OK;
+        REQUIRE_PTR(means);
+        REQUIRE_PTR(scales);
+        REQUIRE_PTR(quats);
+        REQUIRE_PTR(opacities);
+        REQUIRE_PTR(sh);
+        REQUIRE_PTR(means2d);
+        REQUIRE_PTR(conic_opacity);
+        REQUIRE_PTR(rgb);
+        REQUIRE_PTR(radii);
+        REQUIRE_PTR(clamped);
+        REQUIRE_PTR(ranges);
+        REQUIRE_PTR(final_T);
+        REQUIRE_PTR(n_contrib);
+        REQUIRE_PTR(dL_dimage);
+        REQUIRE_PTR(dL_dmeans);
+        REQUIRE_PTR(dL_dscales);
+        REQUIRE_PTR(dL_dquats);
+        REQUIRE_PTR(dL_dopacities);
+        REQUIRE_PTR(dL_dsh);
+        REQUIRE_PTR(workspace);
+        REQUIRE(n_pairs >= 0 && n_pairs < ((int64_t)1 << 31), "n_pairs must be in [0, 2^31)");
+        REQUIRE(n_pairs == 0 || values != nullptr, "values must not be NULL");
+        REQUIRE(aligned(quats, 16) && aligned(dL_dquats, 16), "quats and dL_dquats must be 16-byte aligned");
+        REQUIRE(aligned(conic_opacity, 16), "conic_opacity must be 16-byte aligned");
+        REQUIRE(aligned(means2d, 8) && aligned(ranges, 8), "means2d and ranges must be 8-byte aligned");
+        REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
+        size_t need = gs_render_bwd_workspace_size(n);
+        REQUIRE(workspace_bytes >= need, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+        hipStream_t s = (hipStream_t)stream;
+        float* grad2d = reinterpret_cast<float*>(workspace);
+        st = hip_check(gs::launch_fill_u32(reinterpret_cast<uint32_t*>(grad2d), (size_t)n * gs::GRAD2D_STRIDE, 0u, s),
+                       "gs_render_bwd(zero)");
+        if (st != GS_OK) return st;
+        if (n_pairs > 0) {
+            st = hip_check(gs::launch_render_bwd(c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
+                                                 conic_opacity, rgb, opt->bg, final_T, n_contrib, dL_dimage, grad2d,
+                                                 s),
+                           "gs_render_bwd(raster)");
+            if (st != GS_OK) return st;
+        }
+        return hip_check(gs::launch_preprocess_bwd(c.cam, c.K, c.sh_rows, opt->lowpass, opt->near_plane, (int)n,
+                                                   means, scales, quats, sh, conic_opacity, radii, clamped, grad2d,
+                                                   dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh,
+                                                   dL_dmeans2d, s),
+                         "gs_render_bwd(chain)");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_render_bwd: unexpected exception");
+    }
+}
+
+gs_status gs_mb_hbm_read(const void* src, size_t bytes, float* sink, void* stream) {
+    if (!src || !sink || bytes % 16 || !aligned(src, 16)) return fail(GS_ERR_INVALID_ARG, "gs_mb_hbm_read: bad args");
+    return hip_check(gs::launch_mb_read(src, bytes, sink, (hipStream_t)stream), "gs_mb_hbm_read");
+}
+
+gs_status gs_mb_hbm_copy(void* dst, const void* src, size_t bytes, void* stream) {
+    if (!src || !dst || bytes % 16 || !aligned(src, 16) || !aligned(dst, 16))
+        return fail(GS_ERR_INVALID_ARG, "gs_mb_hbm_copy: bad args");
+    return hip_check(gs::launch_mb_copy(dst, src, bytes, (hipStream_t)stream), "gs_mb_hbm_copy");
+}
+
+gs_status gs_mb_atomic(float* records, int64_t n_records, int64_t n_ops, int32_t lanes_per_record, void* stream) {
+    if (!records || n_records < 1 || n_records > 0x7fffffff || n_ops < 0 || lanes_per_record < 1 ||
+        lanes_per_record > gs::GRAD2D_STRIDE)
+        return fail(GS_ERR_INVALID_ARG, "gs_mb_atomic: bad args");
+    return hip_check(gs::launch_mb_atomic(records, n_records, n_ops, lanes_per_record, (hipStream_t)stream),
+                     "gs_mb_atomic");
+}
+
+}  // extern "C"

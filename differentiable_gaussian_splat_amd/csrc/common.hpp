@@ -1,0 +1,178 @@
+// Device-side definitions shared by the rasterizer's kernels (gfx950, wave64).
+//
+// The method is the tile-based rasterizer of 3D Gaussian Splatting (named in the
+// abstract of the DISTWAR page, "DISTWAR: Fast Differentiable Rendering on
+// Raster-based Rendering Pipelines"). The constants below are that method's
+// compositing constants; the pages themselves print none of them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gs {
+
+constexpr int TILE = 16;             // tile edge in pixels
+constexpr float ALPHA_MAX = 0.99f;   // alpha = min(0.99, o G)
+constexpr float ALPHA_MIN = 1.0f / 255.0f;  // entries below are skipped
+constexpr float T_MIN = 1e-4f;       // a pixel stops before T would drop below
+constexpr float BIG = 16777216.0f;   // 2^24: beyond this fp32 no longer resolves pixels
+constexpr float NEG_HALF_LOG2E = -0.72134752044448170368f;  // -log2(e)/2: G = 2^(Q * this)
+
+// Per-Gaussian values the backward's reverse blend sums over pixels (see
+// k_render_bwd): colour gradient (3), then with h = o G dL/dalpha per pixel,
+// sum h, sum h w^2, sum h w dy, sum h dy^2, sum h w, sum h dy, where
+// w = dx + beta dy. The chain rule turns these into conic/mean gradients.
+constexpr int GRAD2D_N = 9;
+constexpr int GRAD2D_STRIDE = 12;    // floats per Gaussian record (48 B, 16-B aligned)
+
+// Camera as the kernels take it (by value): intrinsics, tile grid, world->camera
+// rotation R (row-major) and translation t, and the camera centre -R^T t.
+struct DevCam {
+    int W, H, TX, TY;
+    float fx, fy, cx, cy;
+    float R[9];
+    float t[3];
+    float campos[3];
+};
+
+__device__ __forceinline__ bool finitef(float x) { return __builtin_isfinite(x); }
+
+// Tile rectangle of a Gaussian with screen mean (u, v) and integer radius r:
+// the tiles holding a pixel column within r of floor(u) and a pixel row
+// within r of floor(v), clamped to the grid. Returns false when empty.
+// |u|, |v|, r <= 2^24 keeps every intermediate inside int32; ">> 4" on a
+// signed int is the floor division by 16 (arithmetic shift).
+__device__ __forceinline__ bool tile_rect(float u, float v, int r, int TX, int TY,
+                                          int& X0, int& X1, int& Y0, int& Y1) {
+    int fu = (int)floorf(u), fv = (int)floorf(v);
+    X0 = max(0, (fu - r) >> 4);
+    X1 = min(TX - 1, (fu + r) >> 4);
+    Y0 = max(0, (fv - r) >> 4);
+    Y1 = min(TY - 1, (fv + r) >> 4);
+    return X0 <= X1 && Y0 <= Y1;
+}
+
+// Opacity-weighted Gaussian falloff at offset (dx, dy) from the mean with the
+// conic in factored form: Q = a (dx + beta dy)^2 + gamma dy^2, G = exp(-Q/2).
+// The forward and the backward call this same function so that both take the
+// same skip decisions bit for bit; contraction is fixed by hand.
+__device__ __forceinline__ void falloff(float dx, float dy, float a, float beta, float gamma, float o,
+                                        float& w, float& G, float& oG) {
+#pragma clang fp contract(off)
+    w = __fmaf_rn(beta, dy, dx);
+    float aw = a * w;
+    float gdy = gamma * dy;
+    float Q = __fmaf_rn(aw, w, gdy * dy);
+    G = __builtin_amdgcn_exp2f(Q * NEG_HALF_LOG2E);
+    oG = o * G;
+}
+
+// ---------------------------------------------------------------- wave64 helpers
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_zero_fill(float src) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(src), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over the 64 lanes; the total is valid in lane 63. DPP steps: pairs,
+// quads, then rotations by 4 and 8 inside each 16-lane row (every lane holds
+// its row sum), then row broadcasts 15 and 31 fold the four rows into row 3.
+__device__ __forceinline__ float wave_sum_to_lane63(float x) {
+    x += dpp_zero_fill<0xB1, 0xF>(x);   // quad_perm [1,0,3,2]
+    x += dpp_zero_fill<0x4E, 0xF>(x);   // quad_perm [2,3,0,1]
+    x += dpp_zero_fill<0x124, 0xF>(x);  // row_ror:4
+    x += dpp_zero_fill<0x128, 0xF>(x);  // row_ror:8
+    x += dpp_zero_fill<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_zero_fill<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
+    return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    return (1ull << (threadIdx.x & 63)) - 1ull;
+}
+
+// ---------------------------------------------------------------- spherical harmonics
+// Real SH with the Condon-Shortley phase kept, index k = l^2 + l + m, degree <= 3,
+// evaluated at a unit direction (x, y, z). Constants are the textbook
+// normalisations sqrt((2l+1)/(4 pi) (l-|m|)!/(l+|m|)!) (times sqrt 2 for m != 0).
+constexpr float SH_C0 = 0.28209479177387814f;
+constexpr float SH_C1 = 0.4886025119029199f;
+constexpr float SH_C2a = 1.0925484305920792f;   // xy, yz, xz terms
+constexpr float SH_C2b = 0.31539156525252005f;  // 2z^2 - x^2 - y^2
+constexpr float SH_C2c = 0.5462742152960396f;   // x^2 - y^2
+constexpr float SH_C3a = 0.5900435899266435f;   // |m| = 3
+constexpr float SH_C3b = 2.890611442640554f;    // xyz
+constexpr float SH_C3c = 0.4570457994644658f;   // |m| = 1
+constexpr float SH_C3d = 0.3731763325901154f;   // m = 0
+constexpr float SH_C3e = 1.445305721320277f;    // m = 2
+
+__device__ __forceinline__ void sh_eval(int K, float x, float y, float z, float* Y) {
+    Y[0] = SH_C0;
+    if (K <= 1) return;
+    Y[1] = -SH_C1 * y;
+    Y[2] = SH_C1 * z;
+    Y[3] = -SH_C1 * x;
+    if (K <= 4) return;
+    float xx = x * x, yy = y * y, zz = z * z;
+    Y[4] = SH_C2a * x * y;
+    Y[5] = -SH_C2a * y * z;
+    Y[6] = SH_C2b * (2.f * zz - xx - yy);
+    Y[7] = -SH_C2a * x * z;
+    Y[8] = SH_C2c * (xx - yy);
+    if (K <= 9) return;
+    Y[9] = -SH_C3a * y * (3.f * xx - yy);
+    Y[10] = SH_C3b * x * y * z;
+    Y[11] = -SH_C3c * y * (4.f * zz - xx - yy);
+    Y[12] = SH_C3d * z * (2.f * zz - 3.f * xx - 3.f * yy);
+    Y[13] = -SH_C3c * x * (4.f * zz - xx - yy);
+    Y[14] = SH_C3e * z * (xx - yy);
+    Y[15] = -SH_C3a * x * (xx - 3.f * yy);
+}
+
+// g += sum_k c[k] * grad(Y_k) at (x, y, z), x, y, z treated as independent.
+__device__ __forceinline__ void sh_grad_accum(int K, float x, float y, float z, const float* c, float3& g) {
+    if (K <= 1) return;
+    g.y -= SH_C1 * c[1];
+    g.z += SH_C1 * c[2];
+    g.x -= SH_C1 * c[3];
+    if (K <= 4) return;
+    float xx = x * x, yy = y * y, zz = z * z;
+    g.x += SH_C2a * y * c[4];
+    g.y += SH_C2a * x * c[4];
+    g.y -= SH_C2a * z * c[5];
+    g.z -= SH_C2a * y * c[5];
+    g.x -= 2.f * SH_C2b * x * c[6];
+    g.y -= 2.f * SH_C2b * y * c[6];
+    g.z += 4.f * SH_C2b * z * c[6];
+    g.x -= SH_C2a * z * c[7];
+    g.z -= SH_C2a * x * c[7];
+    g.x += 2.f * SH_C2c * x * c[8];
+    g.y -= 2.f * SH_C2c * y * c[8];
+    if (K <= 9) return;
+    g.x -= SH_C3a * 6.f * x * y * c[9];
+    g.y -= SH_C3a * (3.f * xx - 3.f * yy) * c[9];
+    g.x += SH_C3b * y * z * c[10];
+    g.y += SH_C3b * x * z * c[10];
+    g.z += SH_C3b * x * y * c[10];
+    g.x += SH_C3c * 2.f * x * y * c[11];
+    g.y -= SH_C3c * (4.f * zz - xx - 3.f * yy) * c[11];
+    g.z -= SH_C3c * 8.f * y * z * c[11];
+    g.x -= SH_C3d * 6.f * x * z * c[12];
+    g.y -= SH_C3d * 6.f * y * z * c[12];
+    g.z += SH_C3d * (6.f * zz - 3.f * xx - 3.f * yy) * c[12];
+    g.x -= SH_C3c * (4.f * zz - 3.f * xx - yy) * c[13];
+    g.y += SH_C3c * 2.f * x * y * c[13];
+    g.z -= SH_C3c * 8.f * x * z * c[13];
+    g.x += SH_C3e * 2.f * x * z * c[14];
+    g.y -= SH_C3e * 2.f * y * z * c[14];
+    g.z += SH_C3e * (xx - yy) * c[14];
+    g.x -= SH_C3a * (3.f * xx - 3.f * yy) * c[15];
+    g.y += SH_C3a * 6.f * x * y * c[15];
+}
+
+}  // namespace gs

@@ -1,0 +1,328 @@
+// Per-Gaussian projection (forward) and its chain rule (backward), one lane per
+// Gaussian. This is the "preprocessing" phase of a 3D Gaussian Splatting
+// training iteration (Odin page, Fig. 7 caption: phases P/R/B/U/C).
+//
+// Numerics. The 2D covariance is formed as Sigma' = T T^T + lowpass I with
+// T = (J R) Rq diag(s) (2x3), so its diagonal entries are sums of squares.
+// Its determinant uses Lagrange's identity det(T T^T) = |T0 x T1|^2 with
+// T0 x T1 = (fx fy / z^3) s1 s2 s3 diag(1/s) Rq^T (mu - campos), which has no
+// cancellation, and the inverse is stored factored as
+// Q = a (dx + beta dy)^2 + gamma dy^2 (a = C/det, beta = -B/C, gamma = 1/C).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace gs {
+
+namespace {
+
+struct Geo {
+    float x, y, z;      // camera-frame mean
+    float qn[4];        // unit quaternion (w, x, y, z)
+    float qnorm;
+    float Rq[9];        // rotation of the Gaussian, row-major
+    float V[6];         // J R (2x3)
+    float P[6];         // V Rq (2x3)
+    float T[6];         // P diag(s)
+    float A0, B0, C0;   // T T^T
+};
+
+// Steps shared by the forward and the backward: camera transform, quaternion
+// rotation, and the 2x3 factor T of the projected covariance.
+__device__ __forceinline__ bool geometry(const DevCam& cam, float near_plane, float mx, float my, float mz,
+                                         float s0, float s1, float s2, float4 q, Geo& g) {
+    g.x = fmaf(cam.R[0], mx, fmaf(cam.R[1], my, fmaf(cam.R[2], mz, cam.t[0])));
+    g.y = fmaf(cam.R[3], mx, fmaf(cam.R[4], my, fmaf(cam.R[5], mz, cam.t[1])));
+    g.z = fmaf(cam.R[6], mx, fmaf(cam.R[7], my, fmaf(cam.R[8], mz, cam.t[2])));
+    if (!(g.z > near_plane)) return false;
+    float qq = q.x * q.x + q.y * q.y + q.z * q.z + q.w * q.w;
+    if (!(qq > 0.f) || !finitef(qq)) return false;
+    g.qnorm = sqrtf(qq);
+    float inv = 1.0f / g.qnorm;
+    float w = q.x * inv, x = q.y * inv, y = q.z * inv, z = q.w * inv;
+    g.qn[0] = w; g.qn[1] = x; g.qn[2] = y; g.qn[3] = z;
+    g.Rq[0] = 1.f - 2.f * (y * y + z * z);
+    g.Rq[1] = 2.f * (x * y - w * z);
+    g.Rq[2] = 2.f * (x * z + w * y);
+    g.Rq[3] = 2.f * (x * y + w * z);
+    g.Rq[4] = 1.f - 2.f * (x * x + z * z);
+    g.Rq[5] = 2.f * (y * z - w * x);
+    g.Rq[6] = 2.f * (x * z - w * y);
+    g.Rq[7] = 2.f * (y * z + w * x);
+    g.Rq[8] = 1.f - 2.f * (x * x + y * y);
+    // J = [[fx/z, 0, -fx x/z^2], [0, fy/z, -fy y/z^2]]; V = J R
+    float iz = 1.0f / g.z;
+    float xz = g.x * iz, yz = g.y * iz;
+    float fxz = cam.fx * iz, fyz = cam.fy * iz;
+    for (int j = 0; j < 3; ++j) {
+        g.V[j] = fxz * fmaf(-xz, cam.R[6 + j], cam.R[j]);
+        g.V[3 + j] = fyz * fmaf(-yz, cam.R[6 + j], cam.R[3 + j]);
+    }
+    float s[3] = {s0, s1, s2};
+    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 3; ++j) {
+            float p = fmaf(g.V[3 * i], g.Rq[j], fmaf(g.V[3 * i + 1], g.Rq[3 + j], g.V[3 * i + 2] * g.Rq[6 + j]));
+            g.P[3 * i + j] = p;
+            g.T[3 * i + j] = p * s[j];
+        }
+    g.A0 = fmaf(g.T[0], g.T[0], fmaf(g.T[1], g.T[1], g.T[2] * g.T[2]));
+    g.C0 = fmaf(g.T[3], g.T[3], fmaf(g.T[4], g.T[4], g.T[5] * g.T[5]));
+    g.B0 = fmaf(g.T[0], g.T[3], fmaf(g.T[1], g.T[4], g.T[2] * g.T[5]));
+    return true;
+}
+
+__global__ __launch_bounds__(256) void k_preprocess(
+    DevCam cam, int K, int sh_rows, float lowpass, float near_plane, int n,
+    const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
+    const float* __restrict__ opac, const float* __restrict__ sh,
+    float2* __restrict__ means2d, float* __restrict__ depths, float4* __restrict__ conic_op,
+    float* __restrict__ rgb_out, int* __restrict__ radii, uint32_t* __restrict__ tiles,
+    uint8_t* __restrict__ clamped) {
+    int gi = blockIdx.x * blockDim.x + threadIdx.x;
+    if (gi >= n) return;
+    size_t g = (size_t)gi;
+    float mx = means[3 * g], my = means[3 * g + 1], mz = means[3 * g + 2];
+    float s0 = scales[3 * g], s1 = scales[3 * g + 1], s2 = scales[3 * g + 2];
+    float4 q = quats[g];
+    float o = opac[g];
+
+    bool ok = finitef(mx) && finitef(my) && finitef(mz) && finitef(s0) && finitef(s1) && finitef(s2) &&
+              finitef(q.x) && finitef(q.y) && finitef(q.z) && finitef(q.w) && finitef(o);
+    Geo geo;
+    ok = ok && geometry(cam, near_plane, mx, my, mz, s0, s1, s2, q, geo);
+
+    float u = 0.f, v = 0.f, a = 0.f, beta = 0.f, gamma = 0.f;
+    int r = 0, X0 = 0, X1 = -1, Y0 = 0, Y1 = -1;
+    if (ok) {
+        // det(Sigma') = |T0 x T1|^2 + lowpass (A0 + C0) + lowpass^2
+        float dx = mx - cam.campos[0], dy = my - cam.campos[1], dz = mz - cam.campos[2];
+        float e0 = fmaf(geo.Rq[0], dx, fmaf(geo.Rq[3], dy, geo.Rq[6] * dz));
+        float e1 = fmaf(geo.Rq[1], dx, fmaf(geo.Rq[4], dy, geo.Rq[7] * dz));
+        float e2 = fmaf(geo.Rq[2], dx, fmaf(geo.Rq[5], dy, geo.Rq[8] * dz));
+        float iz = 1.0f / geo.z;
+        float kk = cam.fx * cam.fy * iz * iz * iz;
+        float c0 = kk * e0 * s1 * s2, c1 = kk * e1 * s0 * s2, c2 = kk * e2 * s0 * s1;
+        float cross2 = fmaf(c0, c0, fmaf(c1, c1, c2 * c2));
+        float A = geo.A0 + lowpass, C = geo.C0 + lowpass, B = geo.B0;
+        float det = fmaf(lowpass, geo.A0 + geo.C0 + lowpass, cross2);
+        ok = det > 0.f && finitef(det) && C > 0.f;
+        if (ok) {
+            a = C / det;
+            beta = -B / C;
+            gamma = 1.0f / C;
+            float half = 0.5f * (A - C);
+            float lam = 0.5f * (A + C) + sqrtf(fmaf(half, half, B * B));
+            float extent = 3.0f * sqrtf(lam);
+            u = fmaf(cam.fx, geo.x * iz, cam.cx);
+            v = fmaf(cam.fy, geo.y * iz, cam.cy);
+            ok = fabsf(u) <= BIG && fabsf(v) <= BIG && extent <= BIG;  // false on NaN
+            if (ok) {
+                r = (int)ceilf(extent);
+                ok = tile_rect(u, v, r, cam.TX, cam.TY, X0, X1, Y0, Y1);
+            }
+        }
+    }
+    float col[3] = {0.f, 0.f, 0.f};
+    uint8_t cl = 0;
+    if (ok) {
+        float dx = mx - cam.campos[0], dy = my - cam.campos[1], dz = mz - cam.campos[2];
+        float dist = sqrtf(fmaf(dx, dx, fmaf(dy, dy, dz * dz)));
+        float id = 1.0f / dist;
+        float Y[16];
+        sh_eval(K, dx * id, dy * id, dz * id, Y);
+        const float* shg = sh + g * (size_t)sh_rows * 3;
+        float raw[3] = {0.5f, 0.5f, 0.5f};
+        for (int k = 0; k < K; ++k) {
+            raw[0] = fmaf(shg[3 * k], Y[k], raw[0]);
+            raw[1] = fmaf(shg[3 * k + 1], Y[k], raw[1]);
+            raw[2] = fmaf(shg[3 * k + 2], Y[k], raw[2]);
+        }
+        ok = dist > 0.f && finitef(raw[0]) && finitef(raw[1]) && finitef(raw[2]);
+        for (int c = 0; c < 3; ++c) {
+            bool neg = raw[c] < 0.f;
+            cl |= (uint8_t)(neg ? (1u << c) : 0u);
+            col[c] = neg ? 0.f : raw[c];
+        }
+    }
+    if (ok) {
+        means2d[g] = make_float2(u, v);
+        depths[g] = geo.z;
+        conic_op[g] = make_float4(a, beta, gamma, o);
+        rgb_out[3 * g] = col[0];
+        rgb_out[3 * g + 1] = col[1];
+        rgb_out[3 * g + 2] = col[2];
+        radii[g] = r;
+        tiles[g] = (uint32_t)((X1 - X0 + 1) * (Y1 - Y0 + 1));
+        clamped[g] = cl;
+    } else {
+        means2d[g] = make_float2(0.f, 0.f);
+        depths[g] = 0.f;
+        conic_op[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+        rgb_out[3 * g] = 0.f;
+        rgb_out[3 * g + 1] = 0.f;
+        rgb_out[3 * g + 2] = 0.f;
+        radii[g] = 0;
+        tiles[g] = 0;
+        clamped[g] = 0;
+    }
+}
+
+// Chain rule, per visible Gaussian, from the summed pixel terms of the
+// backward blend to the activated parameters. Outputs accumulate (+=).
+__global__ __launch_bounds__(256) void k_preprocess_bwd(
+    DevCam cam, int K, int sh_rows, float lowpass, float near_plane, int n,
+    const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
+    const float* __restrict__ sh, const float4* __restrict__ conic_op, const int* __restrict__ radii,
+    const uint8_t* __restrict__ clamped, const float* __restrict__ grad2d,
+    float* __restrict__ d_means, float* __restrict__ d_scales, float* __restrict__ d_quats,
+    float* __restrict__ d_opac, float* __restrict__ d_sh, float* __restrict__ d_means2d) {
+    int gi = blockIdx.x * blockDim.x + threadIdx.x;
+    if (gi >= n) return;
+    size_t g = (size_t)gi;
+    if (radii[g] <= 0) return;
+    const float4* g2 = reinterpret_cast<const float4*>(grad2d + g * GRAD2D_STRIDE);
+    float4 ga = g2[0], gb = g2[1], gc = g2[2];
+    float dr[3] = {ga.x, ga.y, ga.z};
+    float Sh = ga.w, Sww = gb.x, Swy = gb.y, Syy = gb.z, Sw = gb.w, Sy = gc.x;
+    float4 con = conic_op[g];
+    float a = con.x, beta = con.y, gamma = con.z, o = con.w;
+
+    // pixel sums -> gradients of (a, beta, gamma, u, v, opacity); dL/dQ = -h/2
+    float d_o = o != 0.f ? Sh / o : 0.f;
+    float da = -0.5f * Sww;
+    float dbeta = -a * Swy;
+    float dgamma = -0.5f * Syy;
+    float du = a * Sw;
+    float dv = fmaf(a * beta, Sw, gamma * Sy);
+
+    float mx = means[3 * g], my = means[3 * g + 1], mz = means[3 * g + 2];
+    float s[3] = {scales[3 * g], scales[3 * g + 1], scales[3 * g + 2]};
+    Geo geo;
+    if (!geometry(cam, near_plane, mx, my, mz, s[0], s[1], s[2], quats[g], geo)) return;
+
+    // (a, beta, gamma) -> Sigma' = [[A, B], [B, C]] with a = C/det, beta = -B/C, gamma = 1/C
+    float a2 = a * a;
+    float dA = -a2 * da;
+    float dB = fmaf(-2.f * beta * a2, da, -gamma * dbeta);
+    float dC = fmaf(-beta * beta * a2, da, fmaf(-beta * gamma, dbeta, -gamma * gamma * dgamma));
+    // Sigma' = T T^T + lowpass I  ->  dT = 2 [[dA, dB/2], [dB/2, dC]] T
+    float dT[6];
+    for (int j = 0; j < 3; ++j) {
+        dT[j] = fmaf(2.f * dA, geo.T[j], dB * geo.T[3 + j]);
+        dT[3 + j] = fmaf(dB, geo.T[j], 2.f * dC * geo.T[3 + j]);
+    }
+    // T = P diag(s): dP = dT diag(s), ds_j = sum_i dT_ij P_ij
+    float dP[6], ds[3];
+    for (int j = 0; j < 3; ++j) {
+        ds[j] = fmaf(dT[j], geo.P[j], dT[3 + j] * geo.P[3 + j]);
+        dP[j] = dT[j] * s[j];
+        dP[3 + j] = dT[3 + j] * s[j];
+    }
+    // P = V Rq: dV = dP Rq^T, dRq = V^T dP
+    float dV[6], dRq[9];
+    for (int i = 0; i < 2; ++i)
+        for (int k = 0; k < 3; ++k)
+            dV[3 * i + k] = fmaf(dP[3 * i], geo.Rq[3 * k], fmaf(dP[3 * i + 1], geo.Rq[3 * k + 1], dP[3 * i + 2] * geo.Rq[3 * k + 2]));
+    for (int k = 0; k < 3; ++k)
+        for (int j = 0; j < 3; ++j) dRq[3 * k + j] = fmaf(geo.V[k], dP[j], geo.V[3 + k] * dP[3 + j]);
+    // V = J R: dJ = dV R^T (only the non-constant entries of J are needed)
+    float dJ00 = fmaf(dV[0], cam.R[0], fmaf(dV[1], cam.R[1], dV[2] * cam.R[2]));
+    float dJ02 = fmaf(dV[0], cam.R[6], fmaf(dV[1], cam.R[7], dV[2] * cam.R[8]));
+    float dJ11 = fmaf(dV[3], cam.R[3], fmaf(dV[4], cam.R[4], dV[5] * cam.R[5]));
+    float dJ12 = fmaf(dV[3], cam.R[6], fmaf(dV[4], cam.R[7], dV[5] * cam.R[8]));
+    // camera-space mean, through J and through (u, v)
+    float iz = 1.0f / geo.z, iz2 = iz * iz, iz3 = iz2 * iz;
+    float fx = cam.fx, fy = cam.fy;
+    float xb = fmaf(-fx * iz2, dJ02, fx * iz * du);
+    float yb = fmaf(-fy * iz2, dJ12, fy * iz * dv);
+    float zb = -fx * iz2 * dJ00 - fy * iz2 * dJ11 + 2.f * fx * geo.x * iz3 * dJ02 + 2.f * fy * geo.y * iz3 * dJ12 -
+               fx * geo.x * iz2 * du - fy * geo.y * iz2 * dv;
+    float dmu[3];
+    for (int j = 0; j < 3; ++j) dmu[j] = fmaf(cam.R[j], xb, fmaf(cam.R[3 + j], yb, cam.R[6 + j] * zb));
+
+    // quaternion: dL/dqn_k = sum_ij dRq_ij dRq_ij/dqn_k, then the normalisation's tangent projection
+    float w = geo.qn[0], x = geo.qn[1], y = geo.qn[2], z = geo.qn[3];
+    float gw = 2.f * (-z * dRq[1] + y * dRq[2] + z * dRq[3] - x * dRq[5] - y * dRq[6] + x * dRq[7]);
+    float gx = 2.f * (y * dRq[1] + z * dRq[2] + y * dRq[3] - 2.f * x * dRq[4] - w * dRq[5] + z * dRq[6] +
+                      w * dRq[7] - 2.f * x * dRq[8]);
+    float gy = 2.f * (-2.f * y * dRq[0] + x * dRq[1] + w * dRq[2] + x * dRq[3] + z * dRq[5] - w * dRq[6] +
+                      z * dRq[7] - 2.f * y * dRq[8]);
+    float gz = 2.f * (-2.f * z * dRq[0] - w * dRq[1] + x * dRq[2] + w * dRq[3] - 2.f * z * dRq[4] + y * dRq[5] +
+                      x * dRq[6] + y * dRq[7]);
+    float qdot = w * gw + x * gx + y * gy + z * gz;
+    float iq = 1.0f / geo.qnorm;
+
+    // colour: rgb = max(0, sum_k sh_k Y_k(dir) + 0.5), dir = (mu - campos) / |mu - campos|
+    uint8_t cl = clamped[g];
+    float dcol[3];
+    for (int c = 0; c < 3; ++c) dcol[c] = (cl >> c) & 1 ? 0.f : dr[c];
+    float ddx = mx - cam.campos[0], ddy = my - cam.campos[1], ddz = mz - cam.campos[2];
+    float dist = sqrtf(fmaf(ddx, ddx, fmaf(ddy, ddy, ddz * ddz)));
+    float id = 1.0f / dist;
+    float dxn = ddx * id, dyn = ddy * id, dzn = ddz * id;
+    float Y[16], wk[16];
+    sh_eval(K, dxn, dyn, dzn, Y);
+    const float* shg = sh + g * (size_t)sh_rows * 3;
+    float* dshg = d_sh + g * (size_t)sh_rows * 3;
+    for (int k = 0; k < K; ++k) {
+        dshg[3 * k] += Y[k] * dcol[0];
+        dshg[3 * k + 1] += Y[k] * dcol[1];
+        dshg[3 * k + 2] += Y[k] * dcol[2];
+        wk[k] = fmaf(shg[3 * k], dcol[0], fmaf(shg[3 * k + 1], dcol[1], shg[3 * k + 2] * dcol[2]));
+    }
+    float3 gdir = make_float3(0.f, 0.f, 0.f);
+    sh_grad_accum(K, dxn, dyn, dzn, wk, gdir);
+    float dd = dxn * gdir.x + dyn * gdir.y + dzn * gdir.z;
+    dmu[0] += (gdir.x - dxn * dd) * id;
+    dmu[1] += (gdir.y - dyn * dd) * id;
+    dmu[2] += (gdir.z - dzn * dd) * id;
+
+    d_means[3 * g] += dmu[0];
+    d_means[3 * g + 1] += dmu[1];
+    d_means[3 * g + 2] += dmu[2];
+    d_scales[3 * g] += ds[0];
+    d_scales[3 * g + 1] += ds[1];
+    d_scales[3 * g + 2] += ds[2];
+    float4* dq = reinterpret_cast<float4*>(d_quats) + g;
+    float4 dq0 = *dq;
+    dq0.x += (gw - qdot * w) * iq;
+    dq0.y += (gx - qdot * x) * iq;
+    dq0.z += (gy - qdot * y) * iq;
+    dq0.w += (gz - qdot * z) * iq;
+    *dq = dq0;
+    d_opac[g] += d_o;
+    if (d_means2d) {
+        d_means2d[2 * g] += du;
+        d_means2d[2 * g + 1] += dv;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_preprocess(const DevCam& cam, int K, int sh_rows, float lowpass, float near_plane, int n,
+                             const float* means, const float* scales, const float* quats, const float* opac,
+                             const float* sh, float* means2d, float* depths, float* conic_op, float* rgb,
+                             int* radii, uint32_t* tiles, uint8_t* clamped, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    int blocks = (n + 255) / 256;
+    k_preprocess<<<blocks, 256, 0, stream>>>(cam, K, sh_rows, lowpass, near_plane, n, means, scales,
+                                             reinterpret_cast<const float4*>(quats), opac, sh,
+                                             reinterpret_cast<float2*>(means2d), depths,
+                                             reinterpret_cast<float4*>(conic_op), rgb, radii, tiles, clamped);
+    return hipGetLastError();
+}
+
+hipError_t launch_preprocess_bwd(const DevCam& cam, int K, int sh_rows, float lowpass, float near_plane, int n,
+                                 const float* means, const float* scales, const float* quats, const float* sh,
+                                 const float* conic_op, const int* radii, const uint8_t* clamped,
+                                 const float* grad2d, float* d_means, float* d_scales, float* d_quats,
+                                 float* d_opac, float* d_sh, float* d_means2d, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    int blocks = (n + 255) / 256;
+    k_preprocess_bwd<<<blocks, 256, 0, stream>>>(cam, K, sh_rows, lowpass, near_plane, n, means, scales,
+                                                 reinterpret_cast<const float4*>(quats), sh,
+                                                 reinterpret_cast<const float4*>(conic_op), radii, clamped,
+                                                 grad2d, d_means, d_scales, d_quats, d_opac, d_sh, d_means2d);
+    return hipGetLastError();
+}
+
+}  // namespace gs

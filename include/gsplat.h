@@ -1,0 +1,218 @@
+/*
+ * gsplat.h -- C ABI of the MI355X (gfx950) tile-based 3D Gaussian splatting
+ * rasterizer: forward and backward.
+ *
+ * The method is the rasterizer of "3D Gaussian Splatting for Real-Time
+ * Radiance Field Rendering", which the DISTWAR page ("DISTWAR: Fast
+ * Differentiable Rendering on Raster-based Rendering Pipelines", abstract)
+ * names as the workload whose gradient computation is bound by atomic
+ * updates; the Odin page splits one training iteration into preprocessing,
+ * rendering and backward computation (Fig. 7 caption). The four calls below
+ * are those three phases, with rendering split into binning and blending:
+ *
+ *   gs_preprocess  per-Gaussian EWA projection to a 2D conic, screen radius,
+ *                  tile rectangle and spherical-harmonics colour   (phase P)
+ *   gs_bin_sort    one (tile, depth) pair per touched tile, sorted by tile
+ *                  then depth then Gaussian index; per-tile ranges  (phase R)
+ *   gs_render_fwd  per pixel front-to-back alpha blending           (phase R)
+ *   gs_render_bwd  reverse blend summed into per-Gaussian gradients and the
+ *                  chain rule back to the parameters                (phase B)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every array argument is a DEVICE pointer to caller-owned, contiguous,
+ *   row-major memory unless marked "host". The library allocates no device
+ *   memory: scratch comes from a caller-supplied workspace.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *   stream). The single exception is gs_bin_sort, which waits once for the
+ *   stream to read the pair count back to the host.
+ * - Arguments are validated before anything is launched. On an error nothing
+ *   is written, and gs_last_error() returns a message (thread-local). No C++
+ *   exception crosses this interface.
+ * - Gaussian parameters are the ACTIVATED ones: scales s > 0 (not log-scales),
+ *   opacities o in (0, 1] (not logits), quaternions (w, x, y, z) of any
+ *   non-zero norm (normalised inside). Gradients are with respect to exactly
+ *   these arrays; an exp / sigmoid reparameterisation is the caller's chain.
+ * - Camera: x_c = R x_w + t with R row-major; x right, y down, z forward;
+ *   pixel (px, py) has its centre at (px + 0.5, py + 0.5).
+ * - Screen-space conic. conic_opacity[g] = (a, beta, gamma, opacity) holds the
+ *   inverse 2D covariance in factored form: for d = pixel centre - (u, v),
+ *       d^T Sigma'^-1 d = a (dx + beta dy)^2 + gamma dy^2 ,
+ *   i.e. the standard conic entries are (a, a beta, gamma + a beta^2). Both
+ *   terms are non-negative, so fp32 evaluation loses no digits to cancellation.
+ * - Compositing constants: alpha = min(0.99, o exp(-Q/2)); an entry with
+ *   alpha < 1/255 is skipped; a pixel stops before the entry that would take
+ *   its transmittance below 1e-4 (that entry is not blended).
+ * - Sizes: n < 2^31 Gaussians, pair counts < 2^31, width, height <= 32768.
+ */
+#ifndef GSPLAT_H
+#define GSPLAT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t gs_status;
+#define GS_OK 0
+#define GS_ERR_INVALID_ARG (-1) /* bad argument; nothing launched or written */
+#define GS_ERR_CAPACITY (-2)    /* pair buffers too small; *n_pairs = needed  */
+#define GS_ERR_HIP (-3)         /* a HIP call failed; message in gs_last_error */
+#define GS_ERR_UNSUPPORTED (-4) /* valid but unsupported (e.g. tile_size != 16) */
+
+/* Pinhole camera. */
+typedef struct gs_camera {
+    int32_t width, height; /* image size in pixels, 1..32768 */
+    float fx, fy;          /* focal lengths in pixels, > 0 */
+    float cx, cy;          /* principal point in pixels */
+    float R[9];            /* world -> camera rotation, row-major */
+    float t[3];            /* world -> camera translation */
+} gs_camera;
+
+/* Rasterization options. */
+typedef struct gs_options {
+    int32_t sh_degree;  /* 0..3: colour uses K = (sh_degree + 1)^2 SH rows    */
+    int32_t sh_rows;    /* rows stored per Gaussian in `sh` (>= K); 0 means K */
+    int32_t tile_size;  /* must be 16                                         */
+    float lowpass;      /* added to both diagonal entries of the 2D covariance, px^2 (0.3) */
+    float near_plane;   /* Gaussians with camera-space z <= near_plane are culled (0.2)   */
+    float bg[3];        /* background colour, blended with the final transmittance       */
+} gs_options;
+
+/* Default options: sh_degree 3, sh_rows 0, tile 16, lowpass 0.3, near 0.2, bg 0. */
+gs_options gs_default_options(void);
+
+const char *gs_version(void);
+/* Message of the last failed call on this thread ("" if none). */
+const char *gs_last_error(void);
+
+/*
+ * gs_preprocess -- per-Gaussian projection (phase P).
+ *
+ * For each Gaussian g < n: cull (z <= near_plane, any non-finite input or
+ * derived value, a zero quaternion, a screen position or 3-sigma extent beyond
+ * 2^24 px, an empty tile rectangle); otherwise the EWA 2D covariance
+ * Sigma' = J W Sigma W^T J^T + lowpass I, its inverse as the factored conic,
+ * the radius r = ceil(3 sqrt(lambda_max(Sigma'))), the screen mean
+ * (u, v) = (fx x/z + cx, fy y/z + cy), the tile rectangle
+ * X0 = max(0, floor((floor(u) - r)/16)), X1 = min(TX-1, floor((floor(u) + r)/16))
+ * (same for y), and rgb = max(0, sum_k sh[g,k] Y_k(dir) + 0.5) with dir the
+ * unit vector from the camera centre to the mean and Y_k the real spherical
+ * harmonics of degree <= sh_degree.
+ *
+ * in : means[n,3], scales[n,3], quats[n,4] (w,x,y,z; 16-byte aligned),
+ *      opacities[n], sh[n, sh_rows, 3]
+ * out: means2d[n,2] (u, v; 8-byte aligned), depths[n] (camera z),
+ *      conic_opacity[n,4] (a, beta, gamma, opacity; 16-byte aligned),
+ *      rgb[n,3], radii[n] (0 = culled), tiles_touched[n] (rectangle area,
+ *      0 = culled), clamped[n] (bit c set when colour channel c was clamped at 0).
+ * A culled Gaussian gets radii = tiles_touched = 0 and zeros elsewhere.
+ */
+gs_status gs_preprocess(const gs_camera *cam, const gs_options *opt, int64_t n,
+                        const float *means, const float *scales, const float *quats,
+                        const float *opacities, const float *sh,
+                        float *means2d, float *depths, float *conic_opacity, float *rgb,
+                        int32_t *radii, uint32_t *tiles_touched, uint8_t *clamped,
+                        void *stream);
+
+/* Workspace bytes gs_bin_sort needs for n Gaussians and pair_capacity pairs. */
+size_t gs_bin_sort_workspace_size(int64_t n, int64_t pair_capacity, int32_t width, int32_t height);
+
+/*
+ * gs_bin_sort -- tile binning with a (tile, depth) key sort.
+ *
+ * Emits one pair per (visible Gaussian, tile of its rectangle), with key
+ * (tile_id << 32) | bits(fp32 depth), tile_id = ty * TX + tx, value = Gaussian
+ * index, and sorts the pairs ascending by key, equal keys by ascending index
+ * (the result is unique). ranges[t] = [first, last + 1) of tile t in the
+ * sorted order, (0, 0) for an empty tile.
+ *
+ * in : means2d, depths, radii, tiles_touched as written by gs_preprocess
+ * ws : workspace of workspace_bytes >= gs_bin_sort_workspace_size(...), 256-byte aligned
+ * out: values[pair_capacity], ranges[TX*TY, 2], keys[pair_capacity] (may be NULL:
+ *      the keys are fully determined by ranges, values and depths),
+ *      *n_pairs (host) = P.
+ * Waits for `stream` once to read P. If P > pair_capacity it returns
+ * GS_ERR_CAPACITY with *n_pairs = P and writes nothing else; the caller grows
+ * its buffers and calls again.
+ */
+gs_status gs_bin_sort(const gs_camera *cam, const gs_options *opt, int64_t n,
+                      const float *means2d, const float *depths, const int32_t *radii,
+                      const uint32_t *tiles_touched, void *workspace, size_t workspace_bytes,
+                      int64_t pair_capacity, uint64_t *keys, uint32_t *values, uint32_t *ranges,
+                      int64_t *n_pairs, void *stream);
+
+/*
+ * gs_render_fwd -- front-to-back blending per pixel (phase R).
+ *
+ * Pixel p of tile t walks values[ranges[t]] in order: alpha as above; skip
+ * alpha < 1/255; stop before the entry that would take T below 1e-4;
+ * C += rgb alpha T; T *= (1 - alpha).
+ * out: image[3,H,W] = C + T bg (planar), final_T[H,W] = T,
+ *      n_contrib[H,W] = 1-based position (within the tile's list) of the last
+ *      blended entry, 0 if none.
+ * The result is deterministic (no atomics).
+ */
+gs_status gs_render_fwd(const gs_camera *cam, const gs_options *opt, int64_t n,
+                        const uint32_t *ranges, const uint32_t *values, int64_t n_pairs,
+                        const float *means2d, const float *conic_opacity, const float *rgb,
+                        float *image, float *final_T, uint32_t *n_contrib, void *stream);
+
+/* Workspace bytes gs_render_bwd needs for n Gaussians. */
+size_t gs_render_bwd_workspace_size(int64_t n);
+
+/*
+ * gs_render_bwd -- backward of gs_render_fwd and gs_preprocess (phase B).
+ *
+ * Per pixel, walks its blended entries in reverse with the upstream gradient
+ * dL_dimage[3,H,W], forms each entry's contribution to the gradients of its
+ * colour, opacity, conic and screen mean, sums them per Gaussian (wave-level
+ * reduction first, then one fp32 atomic add per value per (tile, Gaussian)),
+ * then applies the chain rule of gs_preprocess per Gaussian.
+ *
+ * in : the inputs and outputs of gs_preprocess and gs_bin_sort, final_T and
+ *      n_contrib from gs_render_fwd, dL_dimage[3,H,W]
+ * out: ACCUMULATED (+=) dL_dmeans[n,3], dL_dscales[n,3], dL_dquats[n,4],
+ *      dL_dopacities[n], dL_dsh[n, sh_rows, 3] (rows < K), and, if non-NULL,
+ *      dL_dmeans2d[n,2] (gradient with respect to (u, v)).
+ * ws : workspace of workspace_bytes >= gs_render_bwd_workspace_size(n)
+ * The caller zeroes the gradient buffers once per step; several views
+ * rendered in turn on one stream then sum their gradients.
+ * Summation order across tiles is not fixed (atomics): results agree to
+ * rounding between runs, not bit for bit.
+ */
+gs_status gs_render_bwd(const gs_camera *cam, const gs_options *opt, int64_t n,
+                        const float *means, const float *scales, const float *quats,
+                        const float *opacities, const float *sh,
+                        const float *means2d, const float *conic_opacity, const float *rgb,
+                        const int32_t *radii, const uint8_t *clamped,
+                        const uint32_t *ranges, const uint32_t *values, int64_t n_pairs,
+                        const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
+                        float *dL_dmeans, float *dL_dscales, float *dL_dquats,
+                        float *dL_dopacities, float *dL_dsh, float *dL_dmeans2d,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Measurement helpers (used by the benchmark to set the kernels against the
+ * chip's measured limits; not part of the rasterizer).
+ * ------------------------------------------------------------------------ */
+
+/* Streaming read of `bytes` from src (summed into *sink, 1 float) -- HBM read rate. */
+gs_status gs_mb_hbm_read(const void *src, size_t bytes, float *sink, void *stream);
+/* Copy `bytes` from src to dst -- HBM copy rate; also the reference kernel for
+ * scaling rocprof FETCH_SIZE / WRITE_SIZE counters. */
+gs_status gs_mb_hbm_copy(void *dst, const void *src, size_t bytes, void *stream);
+/* n_ops no-return fp32 atomic adds into records[n_records, 12] with the pattern
+ * of the backward's flush: `lanes_per_record` consecutive lanes add to the
+ * consecutive values of one record; records are chosen by a hash of the
+ * operation index (n_records = 1 gives a single hot record). */
+gs_status gs_mb_atomic(float *records, int64_t n_records, int64_t n_ops, int32_t lanes_per_record,
+                       void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSPLAT_H */

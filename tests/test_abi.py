@@ -1,0 +1,105 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+``include/gsplat.h`` declares, and rejects bad arguments before launching."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from differentiable_gaussian_splat_amd import raster
+from differentiable_gaussian_splat_amd.scenes import Camera, make_scene
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "gsplat.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(gs_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_four_phases():
+    fns = header_functions()
+    for f in ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_render_bwd"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_function():
+    L = raster.load_library()
+    missing = [f for f in header_functions() if not hasattr(L, f)]
+    assert not missing, missing
+    assert sorted(raster.EXPORTS) == header_functions()
+
+
+def test_struct_layouts_match_header():
+    # gs_camera: 2 int32 + 4 float + 9 float + 3 float; gs_options: 3 int32 + 2 float + 3 float
+    assert C.sizeof(raster.GsCamera) == 4 * (2 + 4 + 9 + 3)
+    assert C.sizeof(raster.GsOptions) == 4 * (3 + 2 + 3)
+    d = raster.load_library().gs_default_options()
+    assert (d.sh_degree, d.sh_rows, d.tile_size) == (3, 0, 16)
+    assert abs(d.lowpass - 0.3) < 1e-7 and abs(d.near_plane - 0.2) < 1e-7
+
+
+def test_version_and_last_error():
+    assert "gfx950" in raster.gs_version()
+    assert isinstance(raster.load_library().gs_last_error(), bytes)
+
+
+def _cam():
+    return raster.make_camera(make_scene(1, 0, n=4).cameras[0])
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda c, o: setattr(o, "sh_degree", 4), raster.GS_ERR_INVALID_ARG),
+    (lambda c, o: setattr(o, "tile_size", 8), raster.GS_ERR_UNSUPPORTED),
+    (lambda c, o: setattr(c, "fx", 0.0), raster.GS_ERR_INVALID_ARG),
+    (lambda c, o: setattr(c, "width", 0), raster.GS_ERR_INVALID_ARG),
+    (lambda c, o: setattr(o, "near_plane", -1.0), raster.GS_ERR_INVALID_ARG),
+    (lambda c, o: setattr(o, "sh_rows", 3), raster.GS_ERR_INVALID_ARG),
+    (lambda c, o: setattr(o, "lowpass", float("nan")), raster.GS_ERR_INVALID_ARG),
+])
+def test_invalid_arguments_rejected_before_launch(mutate, code):
+    """Validation runs on the host and returns before any HIP call."""
+    L = raster.load_library()
+    cam, opt = _cam(), raster.make_options(3)
+    mutate(cam, opt)
+    P = C.c_void_p
+    dummy = P(4096)  # never dereferenced: validation fails first
+    st = L.gs_preprocess(C.byref(cam), C.byref(opt), 10, *([dummy] * 12), None)
+    assert st == code
+    assert len(L.gs_last_error()) > 0
+
+
+def test_null_pointers_and_sizes_rejected():
+    L = raster.load_library()
+    cam, opt = _cam(), raster.make_options(0)
+    P = C.c_void_p
+    d = P(4096)
+    assert L.gs_preprocess(None, C.byref(opt), 1, *([d] * 12), None) == raster.GS_ERR_INVALID_ARG
+    assert L.gs_preprocess(C.byref(cam), C.byref(opt), -1, *([d] * 12), None) == raster.GS_ERR_INVALID_ARG
+    args = [d] * 12
+    args[5] = None  # means2d
+    assert L.gs_preprocess(C.byref(cam), C.byref(opt), 5, *args, None) == raster.GS_ERR_INVALID_ARG
+    assert b"means2d" in L.gs_last_error()
+    misaligned = [d] * 12
+    misaligned[2] = P(4100)  # quats not 16-byte aligned
+    assert L.gs_preprocess(C.byref(cam), C.byref(opt), 5, *misaligned, None) == raster.GS_ERR_INVALID_ARG
+    # bin_sort: workspace too small, capacity out of range
+    n_pairs = C.c_int64(0)
+    st = L.gs_bin_sort(C.byref(cam), C.byref(opt), 100, d, d, d, d, P(4096 * 256), 16, 1000, None, d, d,
+                       C.byref(n_pairs), None)
+    assert st == raster.GS_ERR_INVALID_ARG and b"workspace" in L.gs_last_error()
+    st = L.gs_bin_sort(C.byref(cam), C.byref(opt), 100, d, d, d, d, P(4096 * 256), 1 << 40, -5, None, d, d,
+                       C.byref(n_pairs), None)
+    assert st == raster.GS_ERR_INVALID_ARG
+    # render_bwd: workspace too small
+    st = L.gs_render_bwd(C.byref(cam), C.byref(opt), 100, *([d] * 12), 10, d, d, d, *([d] * 6), P(4096 * 256), 64,
+                         None)
+    assert st == raster.GS_ERR_INVALID_ARG and b"workspace" in L.gs_last_error()
+
+
+def test_workspace_sizes_monotone():
+    a = raster.gs_bin_sort_workspace_size(1000, 10_000, 128, 128)
+    b = raster.gs_bin_sort_workspace_size(1000, 20_000, 128, 128)
+    assert 0 < a < b and a % 256 == 0
+    assert raster.gs_render_bwd_workspace_size(1000) >= 1000 * 12 * 4
