@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark: forward + backward splat rasterization, ms per frame, on one MI355X.
+
+A step is one pass of the whole hot path on one synthetic frame whose inputs
+are already resident in HBM: gs_preprocess -> gs_bin_sort -> gs_render_fwd ->
+(zero the parameter gradients) -> gs_render_bwd (its two halves,
+gs_render_bwd_raster and gs_preprocess_bwd, called in turn so that the
+raster half can be timed on its own). Default workload: the contention-heavy
+scene (1,000,000 Gaussians, SH degree 3, 1920x1080, 64 clusters plus 2%
+large Gaussians). Per-stage times come from HIP events recorded on the
+launch stream around each call; the step time from the host clock between
+two device synchronisations.
+
+The fp64 CPU oracle is timed on a bounded sample of the same frame on the
+host cores (cpu_baseline): a reported baseline, not a target.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd splat-raster ms/frame, 1M Gaussians @1080p; % HBM/atomic roofline"
+HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+FP32_VECTOR_TFLOPS = 157.3      # MI355X published fp32 vector rate
+STAGES = ["preprocess", "bin_sort", "render_fwd", "zero_grads", "render_bwd_raster", "preprocess_bwd"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload (1..5); 3 is the headline frame")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-baseline", type=int, default=1, help="1: time the oracle on a sample")
+    ap.add_argument("--cpu-tile-frac", type=float, default=0.005, help="fraction of tiles the oracle renders")
+    ap.add_argument("--cpu-sort-frac", type=float, default=0.1, help="fraction of Gaussians the oracle bins")
+    return ap.parse_args()
+
+
+def backward_bytes(n_contrib, ranges, W, H, n_touched):
+    """Algorithmic HBM bytes of one gs_render_bwd_raster launch: per walked list
+    entry the record read (value 4 + mean 8 + conic/opacity 16 + colour 12 =
+    40 B), per pixel its final T, n_contrib and upstream gradient (20 B), per
+    touched Gaussian its 36-byte result written once (the per-tile partial sums
+    meet in L2)."""
+    TX = (W + 15) // 16
+    TY = (H + 15) // 16
+    nc = np.zeros((TY * 16, TX * 16), np.int64)
+    nc[:H, :W] = n_contrib
+    walked = nc.reshape(TY, 16, TX, 16).max(axis=(1, 3)).reshape(-1)  # per tile: its deepest pixel
+    lens = (ranges[:, 1].astype(np.int64) - ranges[:, 0].astype(np.int64))
+    walked = np.minimum(walked, lens)
+    return int(40 * walked.sum() + 20 * W * H + 36 * n_touched), int(walked.sum())
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this rasterizer runs on one GPU only; --gpus must be 1 "
+                          "(the multi-GPU design is described, not built)"}))
+        sys.exit(2)
+
+    import torch
+
+    from differentiable_gaussian_splat_amd import raster, scenes
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    sc = scenes.make_scene(args.config, args.seed)
+    log(f"[bench] scene config {args.config}: N={sc.n}, views={len(sc.cameras)}, built in {time.time() - t0:.1f}s")
+    views = list(range(len(sc.cameras)))
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    means, scales, quats, opac, sh = to(sc.means), to(sc.scales), to(sc.quats), to(sc.opacities), to(sc.sh)
+    dLs = [to(sc.dL_dimage[v]) for v in views]
+    n = sc.n
+    cams = [raster.make_camera(sc.cameras[v]) for v in views]
+    opt = raster.make_options(sc.sh_degree, sc.sh.shape[1])
+    W, H = cams[0].width, cams[0].height
+    ntiles = ((W + 15) // 16) * ((H + 15) // 16)
+
+    # persistent buffers, sized once (a first untimed frame per view measures P)
+    r = raster.Rasterizer(dev, want_keys=True)
+    P_max = 0
+    for v in views:
+        pre = r.preprocess(cams[v], opt, means, scales, quats, opac, sh)
+        P, _ = r.bin_sort(cams[v], opt, pre)
+        P_max = max(P_max, P)
+    cap = int(P_max * 1.02) + 4096
+    r._values = None
+    r._ensure_pairs(cap)
+    r._ensure_bin_ws(n, W, H)
+    E = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+    means2d, depths, conic, rgb = E((n, 2), torch.float32), E(n, torch.float32), E((n, 4), torch.float32), \
+        E((n, 3), torch.float32)
+    radii, tiles, clamped = E(n, torch.int32), E(n, torch.int32), E(n, torch.uint8)
+    ranges = E((ntiles, 2), torch.int32)
+    image, final_T, n_contrib = E((3, H, W), torch.float32), E((H, W), torch.float32), E((H, W), torch.int32)
+    grad2d = E((n, raster.GRAD2D_STRIDE), torch.float32)
+    grads = raster.zero_grads(means, sh)
+    stream = torch.cuda.current_stream()
+    mk = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in views]
+    ev_steps = [mk() for _ in range(args.steps)]
+    ev_warm = mk()
+    stage_ms = np.zeros(len(STAGES))
+    last_P = [0] * len(views)
+
+    def step(ev):
+        for vi, v in enumerate(views):
+            e = ev[vi]
+            cam = cams[v]
+            e[0].record(stream)
+            raster.gs_preprocess(cam, opt, means, scales, quats, opac, sh, means2d, depths, conic, rgb, radii, tiles,
+                                 clamped)
+            e[1].record(stream)
+            P = raster.gs_bin_sort(cam, opt, means2d, depths, radii, tiles, r._bin_ws, r.pair_capacity, r._keys,
+                                   r._values, ranges)
+            last_P[vi] = P
+            e[2].record(stream)
+            raster.gs_render_fwd(cam, opt, n, ranges, r._values, P, means2d, conic, rgb, image, final_T, n_contrib)
+            e[3].record(stream)
+            if vi == 0:  # gradients are zeroed once per step and summed over the views
+                for g in grads.values():
+                    g.zero_()
+            e[4].record(stream)
+            raster.gs_render_bwd_raster(cam, opt, n, ranges, r._values, P, means2d, conic, rgb, final_T, n_contrib,
+                                        dLs[vi], grad2d)
+            e[5].record(stream)
+            raster.gs_preprocess_bwd(cam, opt, means, scales, quats, sh, conic, radii, clamped, grad2d,
+                                     grads["means"], grads["scales"], grads["quats"], grads["opacities"], grads["sh"])
+            e[6].record(stream)
+
+    for _ in range(args.warmup):
+        step(ev_warm)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps), P per view max {max(last_P)}")
+    # timed region: K steps between two synchronisations (per-stage events read after each view)
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(ev_steps[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    for ev in ev_steps:
+        for e in ev:
+            for k in range(len(STAGES)):
+                stage_ms[k] += e[k].elapsed_time(e[k + 1])
+    ms_per_step = 1000.0 * elapsed / args.steps
+    frames = args.steps * len(views)
+    ms_per_frame = 1000.0 * elapsed / frames
+    stage_ms /= frames
+    log(f"[bench] {args.steps} steps in {elapsed:.3f}s: {ms_per_frame:.3f} ms/frame; "
+        + ", ".join(f"{s} {t:.3f}" for s, t in zip(STAGES, stage_ms)))
+
+    # algorithmic work of the last frame (outside the timed region)
+    nc_np = n_contrib.cpu().numpy().astype(np.int64)
+    rg_np = ranges.cpu().numpy().view(np.uint32)
+    touched = int((radii > 0).sum().item())
+    bwd_bytes, walked = backward_bytes(nc_np, rg_np, W, H, touched)
+    E_b = int(nc_np.sum())
+    t_bwd = stage_ms[STAGES.index("render_bwd_raster")] * 1e-3
+    achieved = bwd_bytes / t_bwd / 1e9
+
+    # measured HBM read rate (context beside the published peak)
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        raster.gs_mb_hbm_read(buf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        raster.gs_mb_hbm_read(buf, sink)
+    e1.record(stream)
+    e1.synchronize()
+    hbm_read = 5 * buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+
+    result = {
+        "metric": METRIC,
+        "value": round(ms_per_frame, 4),
+        "unit": "ms/frame",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": scenes.CONFIG_NAMES[args.config],
+            "config": args.config, "seed": args.seed, "gaussians": n, "views_per_step": len(views),
+            "image": [W, H], "sh_degree": sc.sh_degree, "pairs": int(max(last_P)),
+            "visible": touched, "E_b": E_b, "bwd_entries_walked": walked,
+        },
+        "stages_ms": {s: round(float(t), 4) for s, t in zip(STAGES, stage_ms)},
+        "roofline": {
+            "kernel": "k_render_bwd (gs_render_bwd_raster)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 5),
+            "traffic": None,
+            "algorithmic_bytes": bwd_bytes,
+        },
+        "measured_hbm_read_GBps": round(hbm_read, 1),
+    }
+
+    if args.cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(sc, args, fr_state=dict(
+            means2d=means2d.cpu().numpy(), conic=conic.cpu().numpy(), rgb=rgb.cpu().numpy(),
+            radii=radii.cpu().numpy(), depths=depths.cpu().numpy(), values=r._values[:last_P[-1]].cpu().numpy(),
+            ranges=rg_np, P=last_P[-1]), view=views[-1])
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(sc, args, fr_state, view):
+    """The fp64 oracle on a bounded sample of the frame, scaled to ms per frame:
+    all Gaussians for the per-Gaussian steps, a random fraction of Gaussians for
+    the pair sort (scaled by the pair count), and a random fraction of tiles for
+    the per-pixel forward and backward (scaled by the tile count)."""
+    from oracle import oracle as O
+
+    cam = sc.cameras[view]
+    W, H = cam.width, cam.height
+    threads = O.max_threads()
+    rng = np.random.default_rng(1234)
+    t = {}
+    t0 = time.perf_counter()
+    pre = O.preprocess(sc.means, sc.scales, sc.quats, sc.opacities, sc.sh, cam, sc.sh_degree)
+    t["preprocess"] = time.perf_counter() - t0
+    # pair sort on a Gaussian subset, scaled by pairs
+    sub = rng.random(sc.n) < args.cpu_sort_frac
+    t0 = time.perf_counter()
+    keys, values, ranges = O.bin_sort(pre["means2d"][sub], pre["radii"][sub], pre["depth"][sub].astype(np.float32), W, H)
+    ts = time.perf_counter() - t0
+    P_full = int(pre["tiles"].sum())
+    t["bin_sort"] = ts * P_full / max(len(values), 1)
+    # per-pixel stages on sampled tiles, on the GPU's lists (the same frame)
+    TX, TY = (W + 15) // 16, (H + 15) // 16
+    ntiles = TX * TY
+    k = max(1, int(round(args.cpu_tile_frac * ntiles)))
+    tiles = rng.choice(ntiles, k, replace=False)
+    pix = []
+    for tt in tiles:
+        ty, tx = divmod(int(tt), TX)
+        ys, xs = np.meshgrid(np.arange(ty * 16, min(ty * 16 + 16, H)), np.arange(tx * 16, min(tx * 16 + 16, W)),
+                             indexing="ij")
+        pix.append((ys * W + xs).reshape(-1))
+    pix = np.concatenate(pix)
+    co = fr_state["conic"]
+    conic_std = O.ldl_to_conic(co[:, :3])
+    vals = fr_state["values"].view(np.uint32)
+    t0 = time.perf_counter()
+    O.render_fwd_pixels(W, H, fr_state["ranges"], vals, fr_state["means2d"], conic_std, co[:, 3], fr_state["rgb"], pix)
+    t["render_fwd"] = (time.perf_counter() - t0) * ntiles / k
+    t0 = time.perf_counter()
+    g2 = O.render_bwd_pixels(W, H, sc.n, fr_state["ranges"], vals, fr_state["means2d"], conic_std, co[:, 3],
+                             fr_state["rgb"], sc.dL_dimage[view], pix)
+    t["render_bwd"] = (time.perf_counter() - t0) * ntiles / k
+    t0 = time.perf_counter()
+    O.preprocess_bwd(sc.means, sc.scales, sc.quats, sc.opacities, sc.sh, cam, sc.sh_degree, g2)
+    t["preprocess_bwd"] = time.perf_counter() - t0
+    total_ms = 1000.0 * sum(t.values())
+    return {
+        "value": round(total_ms, 1),
+        "unit": "ms/frame",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 oracle, {threads} OpenMP threads: preprocess and its backward on all {sc.n} Gaussians; "
+                   f"pair sort on a random {args.cpu_sort_frac:.0%} of Gaussians scaled by pair count; per-pixel "
+                   f"forward and backward on {k} random tiles of {ntiles} scaled by tile count"),
+        "stages_s": {s: round(v, 3) for s, v in t.items()},
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -83,6 +83,32 @@ gs_status check_common(const gs_camera* cam, const gs_options* opt, int64_t n, C
     return GS_OK;
 }
 
+// Host side of gs_bin_sort's pair-count readback: a small pinned buffer and an
+// event per (thread, device), created on first use and kept for the process.
+struct Readback {
+    int device = -1;
+    unsigned long long* host = nullptr;
+    hipEvent_t ev = nullptr;
+};
+
+gs_status readback_for_current_device(Readback*& out) {
+    thread_local Readback slots[16];
+    int dev = 0;
+    gs_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+    if (st != GS_OK) return st;
+    if (dev < 0 || dev >= 16) return fail(GS_ERR_UNSUPPORTED, "device index %d >= 16", dev);
+    Readback& r = slots[dev];
+    if (r.device != dev) {
+        st = hip_check(hipHostMalloc((void**)&r.host, 64, hipHostMallocDefault), "hipHostMalloc");
+        if (st != GS_OK) return st;
+        st = hip_check(hipEventCreateWithFlags(&r.ev, hipEventDisableTiming), "hipEventCreateWithFlags");
+        if (st != GS_OK) return st;
+        r.device = dev;
+    }
+    out = &r;
+    return GS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -138,8 +164,7 @@ gs_status gs_preprocess(const gs_camera* cam, const gs_options* opt, int64_t n, 
 
 size_t gs_bin_sort_workspace_size(int64_t n, int64_t pair_capacity, int32_t width, int32_t height) {
     if (n < 0 || pair_capacity < 0 || width <= 0 || height <= 0) return 0;
-    int ntiles = ((width + 15) / 16) * ((height + 15) / 16);
-    return gs::bin_layout(n, pair_capacity, ntiles).total;
+    return gs::bin_layout(n, pair_capacity, (width + 15) / 16, (height + 15) / 16).total;
 }
 
 gs_status gs_bin_sort(const gs_camera* cam, const gs_options* opt, int64_t n, const float* means2d,
@@ -164,7 +189,7 @@ gs_status gs_bin_sort(const gs_camera* cam, const gs_options* opt, int64_t n, co
             REQUIRE(aligned(means2d, 8), "means2d must be 8-byte aligned");
             REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
         }
-        gs::BinLayout L = gs::bin_layout(n, pair_capacity, c.ntiles);
+        gs::BinLayout L = gs::bin_layout(n, pair_capacity, c.cam.TX, c.cam.TY);
         if (n > 0)
             REQUIRE(workspace_bytes >= L.total, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
         hipStream_t s = (hipStream_t)stream;
@@ -172,22 +197,23 @@ gs_status gs_bin_sort(const gs_camera* cam, const gs_options* opt, int64_t n, co
             *n_pairs = 0;
             return hip_check(gs::launch_fill_u32(ranges, (size_t)2 * c.ntiles, 0u, s), "gs_bin_sort");
         }
+        Readback* rb = nullptr;
+        st = readback_for_current_device(rb);
+        if (st != GS_OK) return st;
         char* ws = reinterpret_cast<char*>(workspace);
-        st = hip_check(gs::launch_bin_count((int)n, depths, tiles_touched, ws, L, s), "gs_bin_sort(count)");
+        st = hip_check(gs::launch_bin_count((int)n, depths, tiles_touched, ws, L, rb->host, rb->ev, s),
+                       "gs_bin_sort(count)");
         if (st != GS_OK) return st;
-        unsigned long long counters[2] = {0, 0};
-        st = hip_check(hipMemcpyAsync(counters, ws + L.counters, sizeof(counters), hipMemcpyDeviceToHost, s),
-                       "gs_bin_sort(readback)");
+        // the one wait: for the pair count only; the depth sort keeps running
+        st = hip_check(hipEventSynchronize(rb->ev), "gs_bin_sort(wait)");
         if (st != GS_OK) return st;
-        st = hip_check(hipStreamSynchronize(s), "gs_bin_sort(sync)");
-        if (st != GS_OK) return st;
-        unsigned long long vis = counters[0], P = counters[1];
+        unsigned long long P = rb->host[0];
         *n_pairs = (int64_t)P;
         if (P >= (1ull << 31)) return fail(GS_ERR_UNSUPPORTED, "pair count %llu exceeds 2^31 - 1", P);
         if ((int64_t)P > pair_capacity)
             return fail(GS_ERR_CAPACITY, "pair count %llu exceeds capacity %lld", P, (long long)pair_capacity);
-        return hip_check(gs::launch_bin_emit((int)n, (int)vis, (int)P, c.cam.TX, c.cam.TY, means2d, radii, depths, ws,
-                                             L, keys, values, ranges, s),
+        return hip_check(gs::launch_bin_emit((int)n, (int)P, c.cam.TX, c.cam.TY, means2d, radii, depths, ws, L, keys,
+                                             values, ranges, s),
                          "gs_bin_sort(emit)");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_bin_sort: unexpected exception");
@@ -291,6 +317,81 @@ gs_status gs_render_bwd(const gs_camera* cam, const gs_options* opt, int64_t n, 
                          "gs_render_bwd(chain)");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_render_bwd: unexpected exception");
+    }
+}
+
+gs_status gs_render_bwd_raster(const gs_camera* cam, const gs_options* opt, int64_t n, const uint32_t* ranges,
+                               const uint32_t* values, int64_t n_pairs, const float* means2d,
+                               const float* conic_opacity, const float* rgb, const float* final_T,
+                               const uint32_t* n_contrib, const float* dL_dimage, float* grad2d, void* stream) {
+    try {
+        g_err[0] = 0;
+        static_assert(GS_GRAD2D_STRIDE == gs::GRAD2D_STRIDE, "record stride");
+        Checked c;
+        gs_status st = check_common(cam, opt, n, c);
+        if (st != GS_OK) return st;
+        if (n == 0) return GS_OK;
+        REQUIRE_PTR(ranges);
+        REQUIRE_PTR(final_T);
+        REQUIRE_PTR(n_contrib);
+        REQUIRE_PTR(dL_dimage);
+        REQUIRE_PTR(grad2d);
+        REQUIRE(n_pairs >= 0 && n_pairs < ((int64_t)1 << 31), "n_pairs must be in [0, 2^31)");
+        if (n_pairs > 0) {
+            REQUIRE_PTR(values);
+            REQUIRE_PTR(means2d);
+            REQUIRE_PTR(conic_opacity);
+            REQUIRE_PTR(rgb);
+        }
+        REQUIRE(aligned(grad2d, 16), "grad2d must be 16-byte aligned");
+        REQUIRE(aligned(conic_opacity, 16), "conic_opacity must be 16-byte aligned");
+        REQUIRE(aligned(means2d, 8) && aligned(ranges, 8), "means2d and ranges must be 8-byte aligned");
+        hipStream_t s = (hipStream_t)stream;
+        st = hip_check(gs::launch_fill_u32(reinterpret_cast<uint32_t*>(grad2d), (size_t)n * gs::GRAD2D_STRIDE, 0u, s),
+                       "gs_render_bwd_raster(zero)");
+        if (st != GS_OK || n_pairs == 0) return st;
+        return hip_check(gs::launch_render_bwd(c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
+                                               conic_opacity, rgb, opt->bg, final_T, n_contrib, dL_dimage, grad2d,
+                                               s),
+                         "gs_render_bwd_raster");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_render_bwd_raster: unexpected exception");
+    }
+}
+
+gs_status gs_preprocess_bwd(const gs_camera* cam, const gs_options* opt, int64_t n, const float* means,
+                            const float* scales, const float* quats, const float* sh, const float* conic_opacity,
+                            const int32_t* radii, const uint8_t* clamped, const float* grad2d, float* dL_dmeans,
+                            float* dL_dscales, float* dL_dquats, float* dL_dopacities, float* dL_dsh,
+                            float* dL_dmeans2d, void* stream) {
+    try {
+        g_err[0] = 0;
+        Checked c;
+        gs_status st = check_common(cam, opt, n, c);
+        if (st != GS_OK) return st;
+        if (n == 0) return GS_OK;
+        REQUIRE_PTR(means);
+        REQUIRE_PTR(scales);
+        REQUIRE_PTR(quats);
+        REQUIRE_PTR(sh);
+        REQUIRE_PTR(conic_opacity);
+        REQUIRE_PTR(radii);
+        REQUIRE_PTR(clamped);
+        REQUIRE_PTR(grad2d);
+        REQUIRE_PTR(dL_dmeans);
+        REQUIRE_PTR(dL_dscales);
+        REQUIRE_PTR(dL_dquats);
+        REQUIRE_PTR(dL_dopacities);
+        REQUIRE_PTR(dL_dsh);
+        REQUIRE(aligned(quats, 16) && aligned(dL_dquats, 16), "quats and dL_dquats must be 16-byte aligned");
+        REQUIRE(aligned(conic_opacity, 16) && aligned(grad2d, 16), "conic_opacity and grad2d must be 16-byte aligned");
+        return hip_check(gs::launch_preprocess_bwd(c.cam, c.K, c.sh_rows, opt->lowpass, opt->near_plane, (int)n,
+                                                   means, scales, quats, sh, conic_opacity, radii, clamped, grad2d,
+                                                   dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh,
+                                                   dL_dmeans2d, (hipStream_t)stream),
+                         "gs_preprocess_bwd");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_preprocess_bwd: unexpected exception");
     }
 }
 

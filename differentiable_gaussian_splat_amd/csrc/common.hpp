@@ -52,6 +52,15 @@ __device__ __forceinline__ bool tile_rect(float u, float v, int r, int TX, int T
     return X0 <= X1 && Y0 <= Y1;
 }
 
+// j -> (j / w, j % w) for 0 <= j < 2^23 and 1 <= w <= 2^11: a float
+// reciprocal gives q within one of the quotient; one exact fixup each way.
+__device__ __forceinline__ void divmod_small(int j, int w, int& q, int& r) {
+    q = (int)(((float)j + 0.5f) * __builtin_amdgcn_rcpf((float)w));
+    r = j - q * w;
+    if (r < 0) { q -= 1; r += w; }
+    if (r >= w) { q += 1; r -= w; }
+}
+
 // Opacity-weighted Gaussian falloff at offset (dx, dy) from the mean with the
 // conic in factored form: Q = a (dx + beta dy)^2 + gamma dy^2, G = exp(-Q/2).
 // The forward and the backward call this same function so that both take the
@@ -87,6 +96,49 @@ __device__ __forceinline__ float wave_sum_to_lane63(float x) {
     return x;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float src) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(src), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each 16-lane row; every lane of the row gets the row's sum.
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp_row<0xB1>(x);   // partner lane ^ 1
+    x += dpp_row<0x4E>(x);   // partner lane ^ 2
+    x += dpp_row<0x124>(x);  // row_ror:4
+    x += dpp_row<0x128>(x);  // row_ror:8
+    return x;
+}
+
+// Reduce-scatter of 8 values over each 16-lane row in 4 butterfly steps. The
+// partners lane^1, lane^2 (quad_perm), lane^7 (row_half_mirror) and lane^8
+// (row_ror:8) form a basis of the 4-bit lane index, so recursive halving along
+// them is exact: with c1 = b0^b2, c2 = b1^b2, c3 = b2 (b = bits of lane & 15),
+// each lane keeps half of its values per step and ends with the row sum of
+// value 4 c1 + 2 c2 + c3. Lanes 0..7 of a row hold the 8 distinct values.
+// Costs 22 VALU ops instead of 8 x 4 for eight plain row sums.
+__device__ __forceinline__ float row_reduce_scatter8(const float* x, bool c1, bool c2, bool c3) {
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float keep = c1 ? x[4 + i] : x[i];
+        const float send = c1 ? x[i] : x[4 + i];
+        y[i] = keep + dpp_row<0xB1>(send);
+    }
+    float z[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float keep = c2 ? y[2 + i] : y[i];
+        const float send = c2 ? y[i] : y[2 + i];
+        z[i] = keep + dpp_row<0x4E>(send);
+    }
+    const float keep = c3 ? z[1] : z[0];
+    const float send = c3 ? z[0] : z[1];
+    float u = keep + dpp_row<0x141>(send);  // row_half_mirror: lane ^ 7 inside each 8
+    u += dpp_row<0x128>(u);                 // row_ror:8 = lane ^ 8
+    return u;
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
     return v;
@@ -94,6 +146,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
     return (1ull << (threadIdx.x & 63)) - 1ull;
+}
+
+// Point of exchange for lanes of one wave that talk through LDS without a
+// block barrier. The hardware already runs a wave's LDS accesses in order;
+// the wave-scope fences (no instructions) keep the compiler from forwarding
+// a lane's own earlier store to a later load of the same address, which
+// would miss what other lanes wrote there in between.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // ---------------------------------------------------------------- spherical harmonics

@@ -20,27 +20,32 @@ hipError_t launch_preprocess_bwd(const DevCam& cam, int K, int sh_rows, float lo
                                  const float* grad2d, float* d_means, float* d_scales, float* d_quats,
                                  float* d_opac, float* d_sh, float* d_means2d, hipStream_t stream);
 
-// Binning. The workspace layout is computed by BinLayout (binsort.hip).
+// Binning. The workspace layout is computed by bin_layout (binsort.hip).
 struct BinLayout {
     size_t dkeys[2], didx[2];  // depth-sort ping-pong (n entries each)
-    size_t offsets;            // per-sorted-Gaussian pair offsets (n + 1)
+    size_t offsets;            // per-sorted-Gaussian first pair index (n + 1)
     size_t partials;           // u64 scan partials
     size_t hist;               // radix histograms
-    size_t counters;           // u64 [0] visible count, [1] pair count
-    size_t tkeys[2];           // pair tile-key ping-pong (capacity each)
-    size_t tvals;              // pair value scratch (capacity)
+    size_t counters;           // u64 [0] visible count, [1] and [2] pair count
+    size_t chunk_counts;       // chunked placement: [chunk][tile] counts, then bases
+    size_t seg;                // chunked placement: [segment][tile] sums, then bases
+    size_t tile_total;         // chunked placement: pairs per tile
+    size_t tkeys[2];           // radix path: pair tile-key ping-pong (capacity each)
+    size_t tvals;              // radix path: pair value scratch (capacity)
     size_t total;
 };
-BinLayout bin_layout(int64_t n, int64_t capacity, int ntiles);
+BinLayout bin_layout(int64_t n, int64_t capacity, int TX, int TY);
 
-// Phase 1: visible compaction, depth sort and pair count. Leaves the visible
-// count and the pair count P in the workspace counters (device).
-hipError_t launch_bin_count(int n, const float* depths, const uint32_t* tiles_touched, char* ws,
-                            const BinLayout& L, hipStream_t stream);
-// Phase 2 (P known on the host): pair emission, tile sort, ranges, keys.
-hipError_t launch_bin_emit(int n, int n_visible, int P, int TX, int TY, const float* means2d,
-                           const int* radii, const float* depths, char* ws, const BinLayout& L,
-                           uint64_t* keys, uint32_t* values, uint32_t* ranges, hipStream_t stream);
+// Phase 1 (no host dependence): pair count P (copied to *host_P, pinned, with
+// `ev` recorded after the copy), visible compaction, depth sort and
+// per-Gaussian first pair index.
+hipError_t launch_bin_count(int n, const float* depths, const uint32_t* tiles_touched, char* ws, const BinLayout& L,
+                            unsigned long long* host_P, hipEvent_t ev, hipStream_t stream);
+// Phase 2 (P known on the host and within capacity): ranges, then the tile
+// sort of the generated pairs into `values` (and the 64-bit keys if non-NULL).
+hipError_t launch_bin_emit(int n, int P, int TX, int TY, const float* means2d, const int* radii,
+                           const float* depths, char* ws, const BinLayout& L, uint64_t* keys,
+                           uint32_t* values, uint32_t* ranges, hipStream_t stream);
 
 hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_t stream);
 

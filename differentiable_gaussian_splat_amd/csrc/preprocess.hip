@@ -70,14 +70,101 @@ __device__ __forceinline__ bool geometry(const DevCam& cam, float near_plane, fl
     return true;
 }
 
-__global__ __launch_bounds__(256) void k_preprocess(
+// Copies the first `used` floats of each of the 64 records of this block
+// (records of `rec` floats from record `base`) into LDS rows of `stride`
+// floats, and back. When the records are fully used and 16-byte aligned the
+// wave's region is one contiguous run moved with float4 accesses, all issued
+// before any is waited on; otherwise 8 records at a time.
+constexpr int STAGE_V4 = 12;  // float4s per lane for 64 records of up to 48 floats
+
+__device__ __forceinline__ void stage_in(const float* __restrict__ src, float* dst, int base, int n, int rec,
+                                         int used, int stride) {
+    const int lane = threadIdx.x;
+    const int cnt = min(64, n - base);
+    const float* r0 = src + (size_t)base * rec;
+    if (used == rec && rec <= 48 && ((uintptr_t)r0 & 15u) == 0) {
+        const int total = cnt * rec;
+        float4 v[STAGE_V4];
+#pragma unroll
+        for (int m = 0; m < STAGE_V4; ++m) {
+            const int f = (m * 64 + lane) * 4;
+            if (f + 3 < total) v[m] = *reinterpret_cast<const float4*>(r0 + f);
+        }
+#pragma unroll
+        for (int m = 0; m < STAGE_V4; ++m) {
+            const int f = (m * 64 + lane) * 4;
+            const float e4[4] = {v[m].x, v[m].y, v[m].z, v[m].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int idx = f + c;
+                if (idx < total) {
+                    int j, e;
+                    divmod_small(idx, rec, j, e);
+                    dst[j * stride + e] = f + 3 < total ? e4[c] : r0[idx];
+                }
+            }
+        }
+        return;
+    }
+    for (int j0 = 0; j0 < cnt; j0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (j0 + u < cnt && lane < used) ? src[(size_t)(base + j0 + u) * rec + lane] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (j0 + u < cnt && lane < used) dst[(j0 + u) * stride + lane] = v[u];
+        for (int e = lane + 64; e < used; e += 64)
+            for (int u = 0; u < 8 && j0 + u < cnt; ++u) dst[(j0 + u) * stride + e] = src[(size_t)(base + j0 + u) * rec + e];
+    }
+}
+
+__device__ __forceinline__ void stage_out(const float* src, float* __restrict__ dst, int base, int n, int rec,
+                                          int used, int stride) {
+    const int lane = threadIdx.x;
+    const int cnt = min(64, n - base);
+    float* r0 = dst + (size_t)base * rec;
+    if (used == rec && rec <= 48 && ((uintptr_t)r0 & 15u) == 0) {
+        const int total = cnt * rec;
+#pragma unroll
+        for (int m = 0; m < STAGE_V4; ++m) {
+            const int f = (m * 64 + lane) * 4;
+            float e4[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int idx = f + c;
+                e4[c] = 0.f;
+                if (idx < total) {
+                    int j, e;
+                    divmod_small(idx, rec, j, e);
+                    e4[c] = src[j * stride + e];
+                }
+            }
+            if (f + 3 < total) {
+                *reinterpret_cast<float4*>(r0 + f) = make_float4(e4[0], e4[1], e4[2], e4[3]);
+            } else {
+                for (int c = 0; c < 4; ++c)
+                    if (f + c < total) r0[f + c] = e4[c];
+            }
+        }
+        return;
+    }
+    for (int j = 0; j < cnt; ++j)
+        for (int e = lane; e < used; e += 64) dst[(size_t)(base + j) * rec + e] = src[j * stride + e];
+}
+
+__global__ __launch_bounds__(64) void k_preprocess(
     DevCam cam, int K, int sh_rows, float lowpass, float near_plane, int n,
     const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
     const float* __restrict__ opac, const float* __restrict__ sh,
     float2* __restrict__ means2d, float* __restrict__ depths, float4* __restrict__ conic_op,
     float* __restrict__ rgb_out, int* __restrict__ radii, uint32_t* __restrict__ tiles,
     uint8_t* __restrict__ clamped) {
-    int gi = blockIdx.x * blockDim.x + threadIdx.x;
+    extern __shared__ float s_sh[];
+    const int stride = (3 * K) | 1;  // odd row stride: lanes reading their own row hit distinct banks
+    const int base = blockIdx.x * 64;
+    stage_in(sh, s_sh, base, n, 3 * sh_rows, 3 * K, stride);
+    __syncthreads();
+    int gi = base + threadIdx.x;
     if (gi >= n) return;
     size_t g = (size_t)gi;
     float mx = means[3 * g], my = means[3 * g + 1], mz = means[3 * g + 2];
@@ -129,7 +216,7 @@ __global__ __launch_bounds__(256) void k_preprocess(
         float id = 1.0f / dist;
         float Y[16];
         sh_eval(K, dx * id, dy * id, dz * id, Y);
-        const float* shg = sh + g * (size_t)sh_rows * 3;
+        const float* shg = s_sh + threadIdx.x * stride;
         float raw[3] = {0.5f, 0.5f, 0.5f};
         for (int k = 0; k < K; ++k) {
             raw[0] = fmaf(shg[3 * k], Y[k], raw[0]);
@@ -166,17 +253,15 @@ __global__ __launch_bounds__(256) void k_preprocess(
     }
 }
 
-// Chain rule, per visible Gaussian, from the summed pixel terms of the
-// backward blend to the activated parameters. Outputs accumulate (+=).
-__global__ __launch_bounds__(256) void k_preprocess_bwd(
-    DevCam cam, int K, int sh_rows, float lowpass, float near_plane, int n,
+// The chain rule for Gaussian gi; shg and dshg are its SH row and SH-gradient
+// row (in LDS). Culled Gaussians are left untouched.
+__device__ __forceinline__ void chain_rule(
+    const DevCam& cam, int K, float near_plane, int gi,
     const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
-    const float* __restrict__ sh, const float4* __restrict__ conic_op, const int* __restrict__ radii,
+    const float* shg, const float4* __restrict__ conic_op, const int* __restrict__ radii,
     const uint8_t* __restrict__ clamped, const float* __restrict__ grad2d,
     float* __restrict__ d_means, float* __restrict__ d_scales, float* __restrict__ d_quats,
-    float* __restrict__ d_opac, float* __restrict__ d_sh, float* __restrict__ d_means2d) {
-    int gi = blockIdx.x * blockDim.x + threadIdx.x;
-    if (gi >= n) return;
+    float* __restrict__ d_opac, float* dshg, float* __restrict__ d_means2d) {
     size_t g = (size_t)gi;
     if (radii[g] <= 0) return;
     const float4* g2 = reinterpret_cast<const float4*>(grad2d + g * GRAD2D_STRIDE);
@@ -261,8 +346,6 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(
     float dxn = ddx * id, dyn = ddy * id, dzn = ddz * id;
     float Y[16], wk[16];
     sh_eval(K, dxn, dyn, dzn, Y);
-    const float* shg = sh + g * (size_t)sh_rows * 3;
-    float* dshg = d_sh + g * (size_t)sh_rows * 3;
     for (int k = 0; k < K; ++k) {
         dshg[3 * k] += Y[k] * dcol[0];
         dshg[3 * k + 1] += Y[k] * dcol[1];
@@ -296,6 +379,33 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(
     }
 }
 
+// Chain rule, per visible Gaussian, from the summed pixel terms of the
+// backward blend to the activated parameters. Outputs accumulate (+=); the
+// SH coefficients and their gradient rows go through LDS.
+__global__ __launch_bounds__(64) void k_preprocess_bwd(
+    DevCam cam, int K, int sh_rows, float lowpass, float near_plane, int n,
+    const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
+    const float* __restrict__ sh, const float4* __restrict__ conic_op, const int* __restrict__ radii,
+    const uint8_t* __restrict__ clamped, const float* __restrict__ grad2d,
+    float* __restrict__ d_means, float* __restrict__ d_scales, float* __restrict__ d_quats,
+    float* __restrict__ d_opac, float* __restrict__ d_sh, float* __restrict__ d_means2d) {
+    extern __shared__ float smem[];
+    const int stride = (3 * K) | 1;
+    float* s_sh = smem;
+    float* s_dsh = smem + 64 * stride;
+    const int base = blockIdx.x * 64;
+    stage_in(sh, s_sh, base, n, 3 * sh_rows, 3 * K, stride);
+    stage_in(d_sh, s_dsh, base, n, 3 * sh_rows, 3 * K, stride);
+    __syncthreads();
+    const int gi = base + threadIdx.x;
+    if (gi < n)
+        chain_rule(cam, K, near_plane, gi, means, scales, quats, s_sh + threadIdx.x * stride, conic_op, radii,
+                   clamped, grad2d, d_means, d_scales, d_quats, d_opac, s_dsh + threadIdx.x * stride, d_means2d);
+    __syncthreads();
+    stage_out(s_dsh, d_sh, base, n, 3 * sh_rows, 3 * K, stride);
+    (void)lowpass;
+}
+
 }  // namespace
 
 hipError_t launch_preprocess(const DevCam& cam, int K, int sh_rows, float lowpass, float near_plane, int n,
@@ -303,8 +413,9 @@ hipError_t launch_preprocess(const DevCam& cam, int K, int sh_rows, float lowpas
                              const float* sh, float* means2d, float* depths, float* conic_op, float* rgb,
                              int* radii, uint32_t* tiles, uint8_t* clamped, hipStream_t stream) {
     if (n == 0) return hipSuccess;
-    int blocks = (n + 255) / 256;
-    k_preprocess<<<blocks, 256, 0, stream>>>(cam, K, sh_rows, lowpass, near_plane, n, means, scales,
+    int blocks = (n + 63) / 64;
+    size_t lds = sizeof(float) * 64 * ((3 * K) | 1);
+    k_preprocess<<<blocks, 64, lds, stream>>>(cam, K, sh_rows, lowpass, near_plane, n, means, scales,
                                              reinterpret_cast<const float4*>(quats), opac, sh,
                                              reinterpret_cast<float2*>(means2d), depths,
                                              reinterpret_cast<float4*>(conic_op), rgb, radii, tiles, clamped);
@@ -317,8 +428,9 @@ hipError_t launch_preprocess_bwd(const DevCam& cam, int K, int sh_rows, float lo
                                  const float* grad2d, float* d_means, float* d_scales, float* d_quats,
                                  float* d_opac, float* d_sh, float* d_means2d, hipStream_t stream) {
     if (n == 0) return hipSuccess;
-    int blocks = (n + 255) / 256;
-    k_preprocess_bwd<<<blocks, 256, 0, stream>>>(cam, K, sh_rows, lowpass, near_plane, n, means, scales,
+    int blocks = (n + 63) / 64;
+    size_t lds = 2 * sizeof(float) * 64 * ((3 * K) | 1);
+    k_preprocess_bwd<<<blocks, 64, lds, stream>>>(cam, K, sh_rows, lowpass, near_plane, n, means, scales,
                                                  reinterpret_cast<const float4*>(quats), sh,
                                                  reinterpret_cast<const float4*>(conic_op), radii, clamped,
                                                  grad2d, d_means, d_scales, d_quats, d_opac, d_sh, d_means2d);

@@ -121,10 +121,18 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
     __shared__ float4 s_b[BATCH];
     __shared__ float s_c[BATCH];
     __shared__ uint32_t s_g[BATCH];
-    __shared__ float s_acc[BATCH * GRAD2D_N];
+    __shared__ float s_part[BATCH * 4 * GRAD2D_N];  // [entry][row of 16 lanes][value]
+    __shared__ uint32_t s_has[BATCH];
     const int tile = blockIdx.x;
     const int tx = tile % TX, ty = tile / TX;
     const int lane = threadIdx.x;
+    // lane roles in the in-row reduce-scatter (see row_reduce_scatter8)
+    const int rl = lane & 15, row = lane >> 4;
+    const bool c1 = ((rl ^ (rl >> 2)) & 1) != 0;
+    const bool c2 = (((rl >> 1) ^ (rl >> 2)) & 1) != 0;
+    const bool c3 = ((rl >> 2) & 1) != 0;
+    const bool writer = rl < 9;
+    const int slot = rl < 8 ? (c1 ? 4 : 0) + (c2 ? 2 : 0) + (c3 ? 1 : 0) : 8;
     const int px = tx * TILE + (lane & 15);
     const int py0 = ty * TILE + (lane >> 4);
     const float pxc = (float)px + 0.5f;
@@ -169,56 +177,64 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
             const float cb = s_c[j];
             const uint32_t pos = (uint32_t)(lo + j);
             const float dx = pxc - A.x;
-            float acc[GRAD2D_N];
-#pragma unroll
-            for (int c = 0; c < GRAD2D_N; ++c) acc[c] = 0.f;
+            // which of this lane's pixels blended this entry (same test as the forward)
+            float w[PPL], dy[PPL], oG[PPL], al[PPL];
+            bool blended[PPL];
             bool any = false;
 #pragma unroll
             for (int k = 0; k < PPL; ++k) {
-                if (pos < last[k]) {
-                    const float dy = pyc[k] - A.y;
-                    float w, G, oG;
-                    falloff(dx, dy, A.z, A.w, B.x, B.y, w, G, oG);
-                    const float alpha = fminf(ALPHA_MAX, oG);
-                    if (alpha >= ALPHA_MIN) {
-                        any = true;
-                        T[k] = T[k] * __builtin_amdgcn_rcpf(1.0f - alpha);  // T in front of this entry
-                        const float wt = alpha * T[k];
-                        acc[0] = fmaf(wt, g0[k], acc[0]);
-                        acc[1] = fmaf(wt, g1[k], acc[1]);
-                        acc[2] = fmaf(wt, g2[k], acc[2]);
-                        const float cdl = fmaf(B.z, g0[k], fmaf(B.w, g1[k], cb * g2[k]));
-                        const float dalpha = T[k] * (cdl - S[k]);
-                        S[k] = fmaf(alpha, cdl - S[k], S[k]);
-                        if (oG <= ALPHA_MAX) {
-                            const float h = oG * dalpha;  // = -2 dL/dQ
-                            const float hw = h * w, hy = h * dy;
-                            acc[3] += h;
-                            acc[4] = fmaf(hw, w, acc[4]);
-                            acc[5] = fmaf(hw, dy, acc[5]);
-                            acc[6] = fmaf(hy, dy, acc[6]);
-                            acc[7] += hw;
-                            acc[8] += hy;
-                        }
-                    }
-                }
+                float G;
+                dy[k] = pyc[k] - A.y;
+                falloff(dx, dy[k], A.z, A.w, B.x, B.y, w[k], G, oG[k]);
+                al[k] = fminf(ALPHA_MAX, oG[k]);
+                blended[k] = pos < last[k] && al[k] >= ALPHA_MIN;
+                any = any || blended[k];
             }
-            if (__any(any)) {
+            if (!__any(any)) {
+                if (lane == 0) s_has[j] = 0u;
+                continue;
+            }
+            // branch-free: a pixel that did not blend this entry takes alpha = 0,
+            // which leaves its T, S and every sum unchanged
+            float acc[GRAD2D_N];
 #pragma unroll
-                for (int c = 0; c < GRAD2D_N; ++c) acc[c] = wave_sum_to_lane63(acc[c]);
-            }
-            if (lane == 63) {
+            for (int c = 0; c < GRAD2D_N; ++c) acc[c] = 0.f;
 #pragma unroll
-                for (int c = 0; c < GRAD2D_N; ++c) s_acc[j * GRAD2D_N + c] = acc[c];
+            for (int k = 0; k < PPL; ++k) {
+                const float av = blended[k] ? al[k] : 0.f;
+                T[k] = T[k] * __builtin_amdgcn_rcpf(1.0f - av);  // T in front of this entry
+                const float wt = av * T[k];
+                acc[0] = fmaf(wt, g0[k], acc[0]);
+                acc[1] = fmaf(wt, g1[k], acc[1]);
+                acc[2] = fmaf(wt, g2[k], acc[2]);
+                const float cdl = fmaf(B.z, g0[k], fmaf(B.w, g1[k], cb * g2[k]));
+                const float d = cdl - S[k];
+                S[k] = fmaf(av, d, S[k]);
+                // h = o G dL/dalpha = -2 dL/dQ; zero where alpha sat at its 0.99 clamp
+                const float h = (blended[k] && oG[k] <= ALPHA_MAX) ? oG[k] * (T[k] * d) : 0.f;
+                const float hw = h * w[k], hy = h * dy[k];
+                acc[3] += h;
+                acc[4] = fmaf(hw, w[k], acc[4]);
+                acc[5] = fmaf(hw, dy[k], acc[5]);
+                acc[6] = fmaf(hy, dy[k], acc[6]);
+                acc[7] += hw;
+                acc[8] += hy;
             }
+            // per 16-lane row: values 0..7 by reduce-scatter (lane slot holds one), value 8 by a row sum
+            const float u = row_reduce_scatter8(acc, c1, c2, c3);
+            const float x8 = row_sum16(acc[8]);
+            if (writer) s_part[(j * 4 + row) * GRAD2D_N + slot] = rl < 8 ? u : x8;
+            if (lane == 0) s_has[j] = 1u;
         }
         __syncthreads();
+        // one atomic add per value per (tile, Gaussian): the 4 row partials summed here
         for (int v = lane; v < cnt * GRAD2D_N; v += 64) {
-            const float val = s_acc[v];
-            if (val != 0.f) {
-                const int e = v / GRAD2D_N;
-                const int c = v - e * GRAD2D_N;
-                atomicAdd(&grad2d[(size_t)s_g[e] * GRAD2D_STRIDE + c], val);
+            const int e = v / GRAD2D_N;
+            const int c = v - e * GRAD2D_N;
+            if (s_has[e]) {
+                const float* p = &s_part[e * 4 * GRAD2D_N + c];
+                const float val = (p[0] + p[GRAD2D_N]) + (p[2 * GRAD2D_N] + p[3 * GRAD2D_N]);
+                if (val != 0.f) atomicAdd(&grad2d[(size_t)s_g[e] * GRAD2D_STRIDE + c], val);
             }
         }
         __syncthreads();

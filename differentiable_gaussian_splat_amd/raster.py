@@ -46,8 +46,9 @@ class GsOptions(C.Structure):
 
 
 EXPORTS = ["gs_default_options", "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_sort_workspace_size",
-           "gs_bin_sort", "gs_render_fwd", "gs_render_bwd_workspace_size", "gs_render_bwd", "gs_mb_hbm_read",
-           "gs_mb_hbm_copy", "gs_mb_atomic"]
+           "gs_bin_sort", "gs_render_fwd", "gs_render_bwd_workspace_size", "gs_render_bwd", "gs_render_bwd_raster",
+           "gs_preprocess_bwd", "gs_mb_hbm_read", "gs_mb_hbm_copy", "gs_mb_atomic"]
+GRAD2D_STRIDE = 12
 
 _lib = None
 _lock = threading.Lock()
@@ -81,6 +82,10 @@ def load_library(path: str = LIB_PATH):
         L.gs_render_bwd.argtypes = ([cam, opt, i64] + [P] * 5 + [P] * 5 + [P, P, i64] + [P] * 3 + [P] * 6 +
                                     [P, sz, P])
         L.gs_render_bwd.restype = i32
+        L.gs_render_bwd_raster.argtypes = [cam, opt, i64, P, P, i64] + [P] * 7 + [P]
+        L.gs_render_bwd_raster.restype = i32
+        L.gs_preprocess_bwd.argtypes = [cam, opt, i64] + [P] * 8 + [P] * 6 + [P]
+        L.gs_preprocess_bwd.restype = i32
         L.gs_mb_hbm_read.argtypes = [P, sz, P, P]
         L.gs_mb_hbm_read.restype = i32
         L.gs_mb_hbm_copy.argtypes = [P, P, sz, P]
@@ -182,6 +187,24 @@ def gs_render_bwd(cam: GsCamera, opt: GsOptions, means, scales, quats, opacities
         _p(n_contrib), _p(dL_dimage), _p(dL_dmeans), _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities), _p(dL_dsh),
         _p(dL_dmeans2d), _p(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "gs_render_bwd")
+
+
+def gs_render_bwd_raster(cam: GsCamera, opt: GsOptions, n, ranges, values, n_pairs, means2d, conic_opacity, rgb,
+                         final_T, n_contrib, dL_dimage, grad2d, stream=None):
+    st = load_library().gs_render_bwd_raster(C.byref(cam), C.byref(opt), n, _p(ranges), _p(values), n_pairs,
+                                             _p(means2d), _p(conic_opacity), _p(rgb), _p(final_T), _p(n_contrib),
+                                             _p(dL_dimage), _p(grad2d), _stream(stream))
+    _check(st, "gs_render_bwd_raster")
+
+
+def gs_preprocess_bwd(cam: GsCamera, opt: GsOptions, means, scales, quats, sh, conic_opacity, radii, clamped, grad2d,
+                      dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh, dL_dmeans2d=None, stream=None):
+    n = means.shape[0]
+    st = load_library().gs_preprocess_bwd(C.byref(cam), C.byref(opt), n, _p(means), _p(scales), _p(quats), _p(sh),
+                                          _p(conic_opacity), _p(radii), _p(clamped), _p(grad2d), _p(dL_dmeans),
+                                          _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities), _p(dL_dsh),
+                                          _p(dL_dmeans2d), _stream(stream))
+    _check(st, "gs_preprocess_bwd")
 
 
 def gs_mb_hbm_read(src, sink, stream=None):

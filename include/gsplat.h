@@ -24,8 +24,8 @@
  *   row-major memory unless marked "host". The library allocates no device
  *   memory: scratch comes from a caller-supplied workspace.
  * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
- *   stream). The single exception is gs_bin_sort, which waits once for the
- *   stream to read the pair count back to the host.
+ *   stream). The single exception is gs_bin_sort, which blocks the calling
+ *   thread once, until the pair count has reached the host.
  * - Arguments are validated before anything is launched. On an error nothing
  *   is written, and gs_last_error() returns a message (thread-local). No C++
  *   exception crosses this interface.
@@ -134,7 +134,9 @@ size_t gs_bin_sort_workspace_size(int64_t n, int64_t pair_capacity, int32_t widt
  * out: values[pair_capacity], ranges[TX*TY, 2], keys[pair_capacity] (may be NULL:
  *      the keys are fully determined by ranges, values and depths),
  *      *n_pairs (host) = P.
- * Waits for `stream` once to read P. If P > pair_capacity it returns
+ * Blocks once, on an event recorded right after the reduction that yields P
+ * (the depth sort queued behind it keeps the GPU busy meanwhile), to read P
+ * on the host. If P > pair_capacity it returns
  * GS_ERR_CAPACITY with *n_pairs = P and writes nothing else; the caller grows
  * its buffers and calls again.
  */
@@ -193,6 +195,32 @@ gs_status gs_render_bwd(const gs_camera *cam, const gs_options *opt, int64_t n,
                         float *dL_dmeans, float *dL_dscales, float *dL_dquats,
                         float *dL_dopacities, float *dL_dsh, float *dL_dmeans2d,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* The two halves of gs_render_bwd, for callers that time or test them apart
+ * (gs_render_bwd = gs_render_bwd_raster followed by gs_preprocess_bwd). */
+
+/* Per-Gaussian pixel sums of the reverse blend, OVERWRITING
+ * grad2d[n, GS_GRAD2D_STRIDE] (16-byte aligned). With, per blended
+ * (pixel, Gaussian) entry, w = dx + beta dy and h = opacity G dL/dalpha
+ * (h = 0 where alpha was clamped at 0.99), record g holds
+ *   [0..2] dL/drgb, [3] sum h, [4] sum h w^2, [5] sum h w dy, [6] sum h dy^2,
+ *   [7] sum h w, [8] sum h dy, [9..11] unused (zero).
+ * The sums are linear in the pixels, so per-tile partial sums are added
+ * atomically; gs_preprocess_bwd turns them into conic and mean gradients. */
+#define GS_GRAD2D_STRIDE 12
+gs_status gs_render_bwd_raster(const gs_camera *cam, const gs_options *opt, int64_t n,
+                               const uint32_t *ranges, const uint32_t *values, int64_t n_pairs,
+                               const float *means2d, const float *conic_opacity, const float *rgb,
+                               const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
+                               float *grad2d, void *stream);
+
+/* Chain rule from grad2d (as written by gs_render_bwd_raster) to the
+ * parameters; outputs ACCUMULATE (+=) exactly as in gs_render_bwd. */
+gs_status gs_preprocess_bwd(const gs_camera *cam, const gs_options *opt, int64_t n,
+                            const float *means, const float *scales, const float *quats, const float *sh,
+                            const float *conic_opacity, const int32_t *radii, const uint8_t *clamped,
+                            const float *grad2d, float *dL_dmeans, float *dL_dscales, float *dL_dquats,
+                            float *dL_dopacities, float *dL_dsh, float *dL_dmeans2d, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Measurement helpers (used by the benchmark to set the kernels against the

@@ -924,3 +924,28 @@ uint64_t orc_decision_hash(int W, int H, const uint32_t *ranges, const uint32_t 
         }
     return total;
 }
+
+/* O13 at the sampled pixels pix[i] = py * W + px only (grad2d accumulated). */
+void orc_render_bwd_pixels(int W, int H, int64_t N, const uint32_t *ranges, const uint32_t *values,
+                           const double *means2d, const double *conic, const double *opac, const double *rgb,
+                           const double *bg, const double *dL_dimage, int64_t npix, const int64_t *pix,
+                           double *grad2d)
+{
+    raster_in in = {W, H, (W + TILE - 1) / TILE, ranges, values, means2d, conic, opac, rgb, {bg[0], bg[1], bg[2]}};
+    int TY = (H + TILE - 1) / TILE;
+    uint32_t maxlen = 0;
+    for (int t = 0; t < in.TX * TY; ++t)
+        if (ranges[2 * t + 1] - ranges[2 * t] > maxlen) maxlen = ranges[2 * t + 1] - ranges[2 * t];
+    (void)N;
+#pragma omp parallel
+    {
+        blend_rec *buf = (blend_rec *)malloc(sizeof(blend_rec) * (maxlen + 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t i = 0; i < npix; ++i) {
+            size_t p = (size_t)pix[i];
+            double dL[3] = {dL_dimage[p], dL_dimage[(size_t)W * H + p], dL_dimage[(size_t)2 * W * H + p]};
+            pixel_backward(&in, (int)(p % W), (int)(p / W), dL, grad2d, buf);
+        }
+        free(buf);
+    }
+}

@@ -57,6 +57,8 @@ def lib():
             L.orc_match_fwd.restype = i64
             L.orc_render_bwd.argtypes = [i32, i32, i64] + [P] * 9
             L.orc_render_bwd.restype = None
+            L.orc_render_bwd_pixels.argtypes = [i32, i32, i64] + [P] * 8 + [i64, P, P]
+            L.orc_render_bwd_pixels.restype = None
             L.orc_preprocess_bwd.argtypes = [i64, P, i32, i32, f64, f64] + [P] * 6 + [P] * 6
             L.orc_preprocess_bwd.restype = None
             L.orc_sh_basis.argtypes = [i32, f64, f64, f64, P]
@@ -191,6 +193,17 @@ def render_bwd(W, H, N, ranges, values, means2d, conic, opac, rgb, dL_dimage, bg
     lib().orc_render_bwd(W, H, N, _p(np.ascontiguousarray(ranges, np.uint32)), _p(values), _p(_d(means2d)),
                          _p(_d(conic)), _p(_d(opac)), _p(_d(rgb)), _p(_d(bg)), _p(_d(dL_dimage)),
                          _p(grad2d))
+    return grad2d
+
+
+def render_bwd_pixels(W, H, N, ranges, values, means2d, conic, opac, rgb, dL_dimage, pix, bg=(0.0, 0.0, 0.0)):
+    """Step O13 restricted to the sampled pixels ``pix`` (flat indices py*W+px)."""
+    grad2d = np.zeros((N, 9))
+    pix = np.ascontiguousarray(pix, np.int64)
+    values = np.ascontiguousarray(values, np.uint32) if len(values) else np.zeros(1, np.uint32)
+    lib().orc_render_bwd_pixels(W, H, N, _p(np.ascontiguousarray(ranges, np.uint32)), _p(values), _p(_d(means2d)),
+                                _p(_d(conic)), _p(_d(opac)), _p(_d(rgb)), _p(_d(bg)), _p(_d(dL_dimage)),
+                                pix.shape[0], _p(pix), _p(grad2d))
     return grad2d
 
 

@@ -288,7 +288,41 @@ def test_multi_view_accumulation():
     torch.cuda.synchronize()
     for k in total:
         s = sum(d[k] for d in singles)
-        assert rel_l2(total[k].cpu().numpy(), s) < 1e-5, k
+        # Equal up to the order of the per-tile float atomics. That order moves
+        # the summed pixel moments by ~1e-7 relative, but the chain rule through
+        # the conic amplifies it for scales and rotations (up to ~1e-4 here), so
+        # the bound is the gradient parity bar; exact accumulation is checked on
+        # the deterministic chain-rule step below.
+        assert rel_l2(total[k].cpu().numpy(), s) < 1e-3, k
+
+
+@pytest.mark.parametrize("deg", [3, 1])
+def test_chain_rule_accumulates_exactly(deg):
+    """The parameter step adds into its outputs: run twice on the same pixel
+    sums it gives exactly twice the first result (no atomics in this step).
+    Degree 3 with 16 stored rows stages whole SH records; degree 1 stages a
+    prefix of each record; 59_993 Gaussians leave a ragged last block."""
+    sc = make_scene(5, 1, n=59_993)
+    r, pd, fr = gpu_frame(sc, 0, sh_degree=deg)
+    n = sc.n
+    grad2d = torch.zeros(n * raster.GRAD2D_STRIDE, dtype=torch.float32, device=pd["means"].device)
+    raster.gs_render_bwd_raster(fr.cam, fr.opt, n, fr.ranges, fr.values, fr.n_pairs, fr.means2d, fr.conic_opacity,
+                                fr.rgb, fr.final_T, fr.n_contrib, to_dev(sc.dL_dimage[0]), grad2d)
+    g = raster.zero_grads(pd["means"], pd["sh"])
+    g["means2d"] = torch.zeros((n, 2), dtype=torch.float32, device=pd["means"].device)
+    outs = [g["means"], g["scales"], g["quats"], g["opacities"], g["sh"], g["means2d"]]
+    snap = None
+    for _ in range(2):
+        raster.gs_preprocess_bwd(fr.cam, fr.opt, pd["means"], pd["scales"], pd["quats"], pd["sh"], fr.conic_opacity,
+                                 fr.radii, fr.clamped, grad2d, *outs)
+        torch.cuda.synchronize()
+        if snap is None:
+            snap = {k: v.clone() for k, v in g.items()}
+    for k in g:
+        assert torch.any(snap[k] != 0), k
+        assert torch.equal(g[k], 2 * snap[k]), k
+    if deg == 1:
+        assert torch.all(g["sh"][:, 4:, :] == 0)
 
 
 def test_lower_active_sh_degree_than_stored():
@@ -302,3 +336,13 @@ def test_lower_active_sh_degree_than_stored():
     gg = gpu_backward(r, fr, pd, sc.dL_dimage[0])
     assert np.all(gg["sh"][:, 4:, :] == 0.0)
     del sc_deg1
+
+
+def test_large_tile_grid_radix_path():
+    """More tiles than per-chunk LDS cursors hold (2560x2200 = 22080 tiles): the
+    pairs are ordered by the radix path instead, with the same result."""
+    rng = np.random.default_rng(8)
+    cam = Camera(2560, 2200, 1500.0, 1500.0, 1280.0, 1100.0, np.eye(3, dtype=np.float32), np.zeros(3, np.float32))
+    sc = _scene_for(cam, 3000, rng, deg=1, big=20)
+    sc.scales[:20] = 0.3
+    _full_check(sc)

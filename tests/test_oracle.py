@@ -479,3 +479,23 @@ def test_matcher_accepts_other_branch_of_a_boundary_skip():
     st = O.match_fwd(32, 32, f["ranges"], f["values"], pre["means2d"], pre["conic"], p["opacities"], pre["rgb"],
                      img, T, nc)
     assert st[py, px] == 3
+
+
+def test_pixel_list_variants_equal_full_image():
+    """The sampled-pixel forward and backward are the full-image ones restricted."""
+    sc = make_scene(1, 2, n=300)
+    cam = sc.cameras[0]
+    p = dict(means=sc.means, scales=sc.scales, quats=sc.quats, opacities=sc.opacities, sh=sc.sh)
+    f = O.forward(p, cam, 0)
+    pre = f["pre"]
+    W, H = cam.width, cam.height
+    pix = np.arange(W * H)
+    img, T, nc = O.render_fwd_pixels(W, H, f["ranges"], f["values"], pre["means2d"], pre["conic"], sc.opacities,
+                                     pre["rgb"], pix)
+    np.testing.assert_array_equal(img.T.reshape(3, H, W), f["image"])
+    np.testing.assert_array_equal(nc.reshape(H, W), f["n_contrib"])
+    g_full = O.render_bwd(W, H, sc.n, f["ranges"], f["values"], pre["means2d"], pre["conic"], sc.opacities,
+                          pre["rgb"], sc.dL_dimage[0])
+    g_pix = O.render_bwd_pixels(W, H, sc.n, f["ranges"], f["values"], pre["means2d"], pre["conic"], sc.opacities,
+                                pre["rgb"], sc.dL_dimage[0], pix)
+    np.testing.assert_allclose(g_pix, g_full, rtol=1e-12, atol=1e-12)
