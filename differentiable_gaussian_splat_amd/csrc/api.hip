@@ -201,18 +201,21 @@ gs_status gs_bin_sort(const gs_camera* cam, const gs_options* opt, int64_t n, co
         st = readback_for_current_device(rb);
         if (st != GS_OK) return st;
         char* ws = reinterpret_cast<char*>(workspace);
-        st = hip_check(gs::launch_bin_count((int)n, depths, tiles_touched, ws, L, rb->host, rb->ev, s),
+        st = hip_check(gs::launch_bin_count((int)n, c.cam.TX, c.cam.TY, means2d, radii, depths, tiles_touched, ws, L,
+                                            rb->host, rb->ev, s),
                        "gs_bin_sort(count)");
         if (st != GS_OK) return st;
         // the one wait: for the pair count only; the depth sort keeps running
         st = hip_check(hipEventSynchronize(rb->ev), "gs_bin_sort(wait)");
         if (st != GS_OK) return st;
-        unsigned long long P = rb->host[0];
+        const unsigned long long P = rb->host[0], P1 = rb->host[1];
         *n_pairs = (int64_t)P;
         if (P >= (1ull << 31)) return fail(GS_ERR_UNSUPPORTED, "pair count %llu exceeds 2^31 - 1", P);
         if ((int64_t)P > pair_capacity)
             return fail(GS_ERR_CAPACITY, "pair count %llu exceeds capacity %lld", P, (long long)pair_capacity);
-        return hip_check(gs::launch_bin_emit((int)n, (int)P, c.cam.TX, c.cam.TY, means2d, radii, depths, ws, L, keys,
+        // every super-tile entry holds at least one of the Gaussian's pairs
+        if (P1 > P) return fail(GS_ERR_HIP, "super-tile entries %llu exceed pairs %llu", P1, P);
+        return hip_check(gs::launch_bin_emit((int)n, (int)P, (int)P1, c.cam.TX, c.cam.TY, ws, L, keys,
                                              values, ranges, s),
                          "gs_bin_sort(emit)");
     } catch (...) {

@@ -3,23 +3,23 @@
 // Sorting the P (tile, Gaussian) pairs by the 64-bit key (tile << 32 | depth
 // bits), equal keys by Gaussian index, gives each tile its Gaussians front to
 // back. This file reaches exactly that order without sorting the P pairs
-// (P is 44.5M for 1M Gaussians at 1920x1080):
+// (44.5M for 1M Gaussians at 1920x1080):
 //   1. stable compaction of the visible Gaussians (index order kept);
-//   2. LSD radix sort of those N by their 32 depth bits (stable: equal depths
-//      stay in index order), so the pair stream "each Gaussian's tiles, in
-//      depth order" is the order every tile's list must follow;
-//   3. exclusive scan of their tile counts in that order: each one's first
-//      pair index;
-//   4. chunked placement (below): per-tile counts of each chunk of the pair
-//      stream, their prefix over chunks, and one wave per chunk writing every
-//      pair to its final slot with per-tile LDS cursors.
-// For tile grids too large for LDS cursors, a stable LSD radix sort of the
-// generated pairs by tile id does step 4 instead.
+//   2. LSD radix sort of those by their 32 depth bits (stable: equal depths
+//      stay in index order); every tile's list is a subsequence of this order;
+//   3. super-tiles of 8 x 8 tiles: each depth-sorted Gaussian emits one entry
+//      per super-tile its tile rectangle meets (about 1.3 entries per Gaussian
+//      at 1080p), and a stable radix pass groups the entries by super-tile,
+//      keeping depth order inside each group;
+//   4. one wave per piece of a super-tile's group, lane = tile of the 8 x 8
+//      block: each lane tests every entry's rectangle and counts (first pass)
+//      or writes the Gaussian at its own cursor (second pass). Per-piece counts,
+//      their running sum per tile and a scan over tiles give the cursors, so
+//      each tile receives its Gaussians in depth order with no ranking step.
 // Radix passes rank stably with wave64 ballot matching against per-wave LDS
-// counters (no barrier per round) and stage the block in LDS so that the
-// output is written in contiguous runs. The pair count P is reduced first and
-// copied to the host asynchronously, so the host's wait for it overlaps the
-// depth sort.
+// counters and stage the block in LDS so that the output is written in
+// contiguous runs. The pair counts are reduced first and copied to the host
+// asynchronously, so the host's wait for them overlaps the depth sort.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -84,11 +84,6 @@ struct LoadPlain {
 struct LoadVisible {
     const uint32_t* tiles;
     __device__ uint32_t operator()(int i) const { return tiles[i] > 0u ? 1u : 0u; }
-};
-struct LoadSortedTiles {
-    const uint32_t* tiles;
-    const uint32_t* order;
-    __device__ uint32_t operator()(int i) const { return tiles[order[i]]; }
 };
 struct StoreInPlace {
     uint32_t* p;
@@ -262,232 +257,6 @@ hipError_t scan(Load ld, Store st, int n, const u64* dcount, u64* partials, u64*
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- chunked tile binning
-//
-// The depth-ordered pair stream is cut into chunks at Gaussian boundaries
-// (chunk c holds the Gaussians whose first pair index lies in [c CH, (c+1) CH)).
-// k_chunk_counts counts each chunk's pairs per tile; a prefix over chunks gives
-// each chunk, per tile, the number of that tile's pairs in earlier chunks; and
-// k_chunk_place walks the chunk's Gaussians in depth order with one LDS cursor
-// per tile, writing each pair straight to its final slot. The order within a
-// tile is therefore chunk order, then depth order inside the chunk: the full
-// (tile, depth, index) order, with no pass over the pairs besides the two that
-// generate them.
-
-__device__ __forceinline__ int lower_bound_u32(const uint32_t* a, int n, uint32_t x) {
-    int lo = 0, hi = n;  // first index with a[i] >= x, n if none
-    while (lo < hi) {
-        int mid = (lo + hi) >> 1;
-        if (a[mid] < x) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-}
-
-// Up to 64 consecutive depth-sorted Gaussians staged by one wave, with the
-// exclusive prefix of their tile counts: the batch's pairs are then walked
-// 64 at a time ("windows"), whatever the Gaussians' sizes.
-struct BatchLds {
-    uint32_t g[64], rect[64], wd[64], pre[64], db[64], mark[64];
-};
-
-__device__ __forceinline__ uint32_t wave_excl_scan_u32(uint32_t v, uint32_t& total) {
-    const int lane = threadIdx.x & 63;
-    uint32_t x = v;
-    for (int off = 1; off < 64; off <<= 1) {
-        uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    total = __shfl(x, 63);
-    return x - v;
-}
-
-__device__ __forceinline__ uint32_t wave_incl_max_u32(uint32_t v) {
-    const int lane = threadIdx.x & 63;
-    for (int off = 1; off < 64; off <<= 1) {
-        uint32_t y = __shfl_up(v, off);
-        if (lane >= off) v = max(v, y);
-    }
-    return v;
-}
-
-// Stages Gaussians kb .. kb+nb-1 (all loads in flight at once); returns the batch's pair count.
-__device__ __forceinline__ uint32_t load_batch(BatchLds& B, int kb, int nb, const uint32_t* __restrict__ order,
-                                               const float2* __restrict__ means2d, const int* __restrict__ radii,
-                                               const float* __restrict__ depths, int TX, int TY) {
-    const int lane = threadIdx.x & 63;
-    uint32_t nt = 0;
-    wave_lds_sync();  // the previous batch's entries have been read
-    if (lane < nb) {
-        const uint32_t g = order[kb + lane];
-        const float2 m = means2d[g];
-        int X0, X1, Y0, Y1;
-        tile_rect(m.x, m.y, radii[g], TX, TY, X0, X1, Y0, Y1);
-        nt = (uint32_t)((X1 - X0 + 1) * (Y1 - Y0 + 1));
-        B.g[lane] = g;
-        B.rect[lane] = (uint32_t)X0 | ((uint32_t)Y0 << 16);
-        B.wd[lane] = (uint32_t)(X1 - X0 + 1);
-        B.db[lane] = depths ? __float_as_uint(depths[g]) : 0u;
-    }
-    uint32_t total;
-    B.pre[lane] = wave_excl_scan_u32(nt, total);
-    wave_lds_sync();  // batch_window reads other lanes' entries
-    return total;
-}
-
-// Window of pairs f0 .. f0+63 of the batch: each lane's Gaussian (batch index)
-// and tile. `cur` is the Gaussian covering f0; it advances to the one covering f0+63.
-__device__ __forceinline__ void batch_window(BatchLds& B, int nb, uint32_t f0, uint32_t& cur, int TX, uint32_t& i,
-                                             uint32_t& t) {
-    const int lane = threadIdx.x & 63;
-    wave_lds_sync();  // every lane has read the previous window's marks
-    B.mark[lane] = 0u;
-    wave_lds_sync();
-    if (lane < nb) {
-        const uint32_t st = B.pre[lane];
-        if (st >= f0 && st < f0 + 64u) B.mark[st - f0] = (uint32_t)lane + 1u;  // one start per slot: counts >= 1
-    }
-    wave_lds_sync();  // slot `lane` may have been written by another lane
-    const uint32_t m = wave_incl_max_u32(B.mark[lane]);
-    i = m ? m - 1u : cur;
-    cur = __shfl(i, 63);
-    const int j = (int)(f0 + (uint32_t)lane - B.pre[i]);
-    const int wd = (int)B.wd[i];
-    int q, r;
-    divmod_small(j, wd, q, r);
-    const uint32_t rect = B.rect[i];
-    t = (uint32_t)(((int)(rect >> 16) + q) * TX + (int)(rect & 0xffffu) + r);
-}
-
-__global__ __launch_bounds__(256) void k_chunk_counts(int CH, const u64* vis_ptr, const uint32_t* __restrict__ offsets,
-                                                    const uint32_t* __restrict__ order,
-                                                    const float2* __restrict__ means2d, const int* __restrict__ radii,
-                                                    int TX, int TY, uint32_t* __restrict__ counts) {
-    extern __shared__ uint32_t s_cnt[];
-    __shared__ BatchLds s_b[SB / 64];
-    __shared__ int s_k[2];
-    const int ntiles = TX * TY;
-    const int c = blockIdx.x;
-    for (int t = threadIdx.x; t < ntiles; t += SB) s_cnt[t] = 0u;
-    if (threadIdx.x == 0) {
-        const int vis = (int)*vis_ptr;
-        s_k[0] = lower_bound_u32(offsets, vis, (uint32_t)c * (uint32_t)CH);
-        s_k[1] = lower_bound_u32(offsets, vis, (uint32_t)(c + 1) * (uint32_t)CH);
-    }
-    __syncthreads();
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    BatchLds& B = s_b[w];
-    // the waves take batches in turn; counting needs no order
-    for (int kb = s_k[0] + 64 * w; kb < s_k[1]; kb += 64 * (SB / 64)) {
-        const int nb = min(64, s_k[1] - kb);
-        const uint32_t T = load_batch(B, kb, nb, order, means2d, radii, nullptr, TX, TY);
-        uint32_t cur = 0;
-        for (uint32_t f0 = 0; f0 < T; f0 += 64u) {
-            uint32_t i, t;
-            batch_window(B, nb, f0, cur, TX, i, t);
-            if (f0 + (uint32_t)lane < T && t < (uint32_t)ntiles) atomicAdd(&s_cnt[t], 1u);
-        }
-    }
-    __syncthreads();
-    uint32_t* row = counts + (size_t)c * ntiles;
-    for (int t = threadIdx.x; t < ntiles; t += SB) row[t] = s_cnt[t];
-}
-
-// Per tile: segment sums of the chunk counts (segments of SEG chunks).
-__global__ __launch_bounds__(SB) void k_seg_sum(int nchunks, int ntiles, int SEG, const uint32_t* __restrict__ counts,
-                                              uint32_t* __restrict__ segsum) {
-    const int nseg = (nchunks + SEG - 1) / SEG;
-    const int idx = blockIdx.x * SB + threadIdx.x;
-    if (idx >= nseg * ntiles) return;
-    const int sg = idx / ntiles, t = idx - sg * ntiles;
-    const int c1 = min(nchunks, (sg + 1) * SEG);
-    uint32_t acc = 0;
-    for (int c = sg * SEG; c < c1; ++c) acc += counts[(size_t)c * ntiles + t];
-    segsum[idx] = acc;
-}
-
-// Per tile: exclusive scan over segments (in place) and the tile's total.
-__global__ __launch_bounds__(SB) void k_seg_scan(int nseg, int ntiles, uint32_t* __restrict__ segsum,
-                                               uint32_t* __restrict__ total) {
-    const int t = blockIdx.x * SB + threadIdx.x;
-    if (t >= ntiles) return;
-    uint32_t run = 0;
-    for (int sg = 0; sg < nseg; ++sg) {
-        const uint32_t v = segsum[(size_t)sg * ntiles + t];
-        segsum[(size_t)sg * ntiles + t] = run;
-        run += v;
-    }
-    total[t] = run;
-}
-
-// Per (segment, tile): running prefix over the segment's chunks, turning the
-// counts in place into each chunk's per-tile base.
-__global__ __launch_bounds__(SB) void k_chunk_base(int nchunks, int ntiles, int SEG, uint32_t* __restrict__ counts,
-                                                 const uint32_t* __restrict__ segbase) {
-    const int nseg = (nchunks + SEG - 1) / SEG;
-    const int idx = blockIdx.x * SB + threadIdx.x;
-    if (idx >= nseg * ntiles) return;
-    const int sg = idx / ntiles, t = idx - sg * ntiles;
-    const int c1 = min(nchunks, (sg + 1) * SEG);
-    uint32_t run = segbase[idx];
-    for (int c = sg * SEG; c < c1; ++c) {
-        const uint32_t v = counts[(size_t)c * ntiles + t];
-        counts[(size_t)c * ntiles + t] = run;
-        run += v;
-    }
-}
-
-// One wave per chunk: stable placement with per-tile LDS cursors. Each window
-// of 64 pairs ranks lanes with equal tiles by ballot matching (lanes are in
-// depth order), so the cursor of a tile advances in depth order.
-__global__ __launch_bounds__(64) void k_chunk_place(int CH, const u64* vis_ptr, const uint32_t* __restrict__ offsets,
-                                                  const uint32_t* __restrict__ order,
-                                                  const float2* __restrict__ means2d, const int* __restrict__ radii,
-                                                  const float* __restrict__ depths, int TX, int TY, int tbits, int P,
-                                                  const uint32_t* __restrict__ base, const uint2* __restrict__ ranges,
-                                                  uint32_t* __restrict__ values, u64* __restrict__ keys64) {
-    extern __shared__ uint32_t s_cur[];
-    __shared__ BatchLds B;
-    const int ntiles = TX * TY;
-    const int c = blockIdx.x;
-    const int lane = threadIdx.x;
-    const int vis = (int)*vis_ptr;
-    const int k0 = lower_bound_u32(offsets, vis, (uint32_t)c * (uint32_t)CH);
-    const int k1 = lower_bound_u32(offsets, vis, (uint32_t)(c + 1) * (uint32_t)CH);
-    const uint32_t* row = base + (size_t)c * ntiles;
-    for (int t = lane; t < ntiles; t += 64) s_cur[t] = ranges[t].x + row[t];
-    __syncthreads();
-    const uint64_t lt = lanemask_lt();
-    for (int kb = k0; kb < k1; kb += 64) {
-        const int nb = min(64, k1 - kb);
-        const uint32_t T = load_batch(B, kb, nb, order, means2d, radii, keys64 ? depths : nullptr, TX, TY);
-        uint32_t cur = 0;
-        for (uint32_t f0 = 0; f0 < T; f0 += 64u) {
-            uint32_t i, t;
-            batch_window(B, nb, f0, cur, TX, i, t);
-            // a pair always lies inside the grid and its tile's range; the
-            // check only keeps a broken invariant from writing out of bounds
-            const bool valid = f0 + (uint32_t)lane < T && t < (uint32_t)ntiles;
-            uint64_t peers = __ballot(valid);
-            for (int bb = 0; bb < tbits; ++bb) {
-                const bool bit = (t >> bb) & 1u;
-                const uint64_t m = __ballot(bit);
-                peers &= bit ? m : ~m;
-            }
-            if (valid) {
-                const uint32_t lrank = (uint32_t)__popcll(peers & lt);
-                const uint32_t b0 = s_cur[t];
-                const uint32_t pos = b0 + lrank;
-                if (lrank == 0u) s_cur[t] = b0 + (uint32_t)__popcll(peers);
-                const uint32_t g = B.g[i];
-                if (pos < (uint32_t)P) {
-                    values[pos] = g;
-                    if (keys64) keys64[pos] = ((u64)t << 32) | (u64)B.db[i];
-                }
-            }
-            wave_lds_sync();  // cursor updates seen by the next window
-        }
-    }
-}
 
 // ---------------------------------------------------------------- radix sort
 
@@ -503,105 +272,6 @@ struct SrcMem {
         k = keys[p];
         v = vals[p];
     }
-};
-
-// (tile, Gaussian) pairs generated in depth order: pair p belongs to the
-// depth-sorted Gaussian k with offsets[k] <= p < offsets[k+1] and is the
-// (p - offsets[k])-th tile of its rectangle in row-major order.
-struct SrcPairs {
-    static constexpr int E = 2048;
-    // gid, off, g, rect, width (E each), k0 and nk, per-thread maxima (SB), per-wave maxima
-    static constexpr int LDS_WORDS = 5 * E + 2 + SB + SB / 64;
-    const uint32_t* offsets;
-    const uint32_t* order;
-    const float2* means2d;
-    const int* radii;
-    const u64* vis;
-    int TX, TY;
-
-    __device__ void setup(int p0, int p1, uint32_t* lds) const {
-        uint32_t* s_gid = lds;
-        uint32_t* s_off = lds + E;
-        uint32_t* s_g = lds + 2 * E;
-        uint32_t* s_rect = lds + 3 * E;
-        uint32_t* s_wd = lds + 4 * E;
-        uint32_t* s_k = lds + 5 * E;
-        if (threadIdx.x == 0) {
-            int nvis = (int)*vis;
-            int k0 = 0, nk = 0;
-            if (p0 < p1 && nvis > 0) {
-                // largest k with offsets[k] <= p, for p = p0 and p = p1 - 1
-                int lo = 0, hi = nvis - 1;
-                while (lo < hi) {
-                    int mid = (lo + hi + 1) >> 1;
-                    if ((int)offsets[mid] <= p0) lo = mid; else hi = mid - 1;
-                }
-                k0 = lo;
-                hi = nvis - 1;
-                while (lo < hi) {
-                    int mid = (lo + hi + 1) >> 1;
-                    if ((int)offsets[mid] <= p1 - 1) lo = mid; else hi = mid - 1;
-                }
-                nk = lo - k0 + 1;  // <= p1 - p0: every visible Gaussian owns >= 1 pair
-            }
-            s_k[0] = (uint32_t)k0;
-            s_k[1] = (uint32_t)nk;
-        }
-        for (int e = threadIdx.x; e < E; e += SB) s_gid[e] = 0u;
-        __syncthreads();
-        const int k0 = (int)s_k[0], nk = (int)s_k[1];
-        for (int i = threadIdx.x; i < nk; i += SB) {
-            uint32_t g = order[k0 + i];
-            float2 m = means2d[g];
-            int X0, X1, Y0, Y1;
-            tile_rect(m.x, m.y, radii[g], TX, TY, X0, X1, Y0, Y1);
-            uint32_t off = offsets[k0 + i];
-            s_off[i] = off;
-            s_g[i] = g;
-            s_rect[i] = (uint32_t)X0 | ((uint32_t)Y0 << 16);
-            s_wd[i] = (uint32_t)(X1 - X0 + 1);
-            int e = (int)off - p0;
-            if (e > 0 && e < E) s_gid[e] = (uint32_t)i;  // Gaussian i starts at block element e
-        }
-        __syncthreads();
-        // prefix-max of the start markers: element e belongs to the last Gaussian starting at or before it
-        constexpr int R = E / SB;
-        uint32_t* s_tmax = lds + 5 * E + 2;
-        uint32_t* s_w = lds + 5 * E + 2 + SB;
-        uint32_t loc[R];
-        uint32_t m = 0;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            m = max(m, s_gid[threadIdx.x * R + r]);
-            loc[r] = m;
-        }
-        s_tmax[threadIdx.x] = block_incl_max_u32(m, s_w);
-        __syncthreads();
-        const uint32_t excl = threadIdx.x > 0 ? s_tmax[threadIdx.x - 1] : 0u;
-#pragma unroll
-        for (int r = 0; r < R; ++r) s_gid[threadIdx.x * R + r] = max(loc[r], excl);
-        __syncthreads();
-    }
-
-    __device__ void decode(int p, const uint32_t* lds, int p0, uint32_t& tile, uint32_t& g) const {
-        const uint32_t i = lds[p - p0];
-        const int j = p - (int)lds[E + i];
-        const int wdt = (int)lds[4 * E + i];
-        const uint32_t rect = lds[3 * E + i];
-        // q = j / wdt, r = j % wdt via a float reciprocal and one exact fixup
-        int q = (int)(((float)j + 0.5f) * __builtin_amdgcn_rcpf((float)wdt));
-        int rr = j - q * wdt;
-        if (rr < 0) { q -= 1; rr += wdt; }
-        if (rr >= wdt) { q += 1; rr -= wdt; }
-        tile = (uint32_t)(((int)(rect >> 16) + q) * TX + (int)(rect & 0xffffu) + rr);
-        g = lds[2 * E + i];
-    }
-    __device__ uint32_t key(int p, const uint32_t* lds, int p0) const {
-        uint32_t t, g;
-        decode(p, lds, p0, t, g);
-        return t;
-    }
-    __device__ void get(int p, uint32_t& k, uint32_t& v, const uint32_t* lds, int p0) const { decode(p, lds, p0, k, v); }
 };
 
 template <class Src>
@@ -749,19 +419,295 @@ int bits_for(int ntiles) {
     return b;
 }
 
-// Ranges from tile-sorted keys (radix path only).
-__global__ __launch_bounds__(SB) void k_ranges(int P, const uint32_t* __restrict__ tile_keys, uint2* __restrict__ ranges) {
-    int p = blockIdx.x * SB + threadIdx.x;
-    if (p >= P) return;
-    uint32_t t = tile_keys[p];
-    if (p == 0 || tile_keys[p - 1] != t) ranges[t].x = (uint32_t)p;
-    if (p == P - 1 || tile_keys[p + 1] != t) ranges[t].y = (uint32_t)(p + 1);
+
+// ---------------------------------------------------------------- two-level tile binning
+
+constexpr int SUPER = 8;      // a super-tile is SUPER x SUPER tiles: one wave lane per tile
+constexpr int PIECE = 256;    // super-tile entries one wave walks in the per-tile passes
+
+__device__ __forceinline__ uint32_t super_count(int X0, int X1, int Y0, int Y1) {
+    return (uint32_t)(((X1 >> 3) - (X0 >> 3) + 1) * ((Y1 >> 3) - (Y0 >> 3) + 1));
 }
 
-constexpr int MAX_CHUNK_TILES = 14336;  // LDS cursors or counters of one chunk: 56 KB, plus the staged batches under 64 KB
-constexpr int MAX_CHUNKS = 2048;
-constexpr int MIN_CHUNK_PAIRS = 8192;
-constexpr int SEG = 32;                  // chunks per segment of the prefix over chunks
+// P = sum of tiles_touched and P1 = number of (super-tile, Gaussian) entries,
+// over all Gaussians (index order): per-block partials, then one summing block.
+constexpr int TOTALS_BLOCKS = 1024;
+
+__global__ __launch_bounds__(SB) void k_pair_totals(int n, const uint32_t* __restrict__ tiles,
+                                                  const float2* __restrict__ means2d, const int* __restrict__ radii,
+                                                  int TX, int TY, u64* __restrict__ part) {
+    __shared__ u64 s_w[2][SB / 64];
+    u64 p = 0, p1 = 0;
+    for (int i = blockIdx.x * SB + threadIdx.x; i < n; i += gridDim.x * SB) {
+        const uint32_t t = tiles[i];
+        if (t) {
+            const float2 m = means2d[i];
+            int X0, X1, Y0, Y1;
+            tile_rect(m.x, m.y, radii[i], TX, TY, X0, X1, Y0, Y1);
+            p += t;
+            p1 += super_count(X0, X1, Y0, Y1);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        p += __shfl_xor(p, off);
+        p1 += __shfl_xor(p1, off);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        s_w[0][threadIdx.x >> 6] = p;
+        s_w[1][threadIdx.x >> 6] = p1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        part[2 * blockIdx.x] = s_w[0][0] + s_w[0][1] + s_w[0][2] + s_w[0][3];
+        part[2 * blockIdx.x + 1] = s_w[1][0] + s_w[1][1] + s_w[1][2] + s_w[1][3];
+    }
+}
+
+__global__ __launch_bounds__(1024) void k_pair_sum(int nb, const u64* __restrict__ part, u64* __restrict__ out) {
+    __shared__ u64 s_w[2][16];
+    u64 p = 0, p1 = 0;
+    for (int i = threadIdx.x; i < nb; i += 1024) {
+        p += part[2 * i];
+        p1 += part[2 * i + 1];
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        p += __shfl_xor(p, off);
+        p1 += __shfl_xor(p1, off);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        s_w[0][threadIdx.x >> 6] = p;
+        s_w[1][threadIdx.x >> 6] = p1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        u64 a = 0, c = 0;
+        for (int w = 0; w < 16; ++w) {
+            a += s_w[0][w];
+            c += s_w[1][w];
+        }
+        out[0] = a;
+        out[1] = c;
+    }
+}
+
+// Per depth-sorted Gaussian i (one gather of its projection): its record
+// (index, X0 | X1 << 16, Y0 | Y1 << 16, depth bits) and its super-tile count.
+__global__ __launch_bounds__(SB) void k_sorted_records(const u64* vis_ptr, const uint32_t* __restrict__ order,
+                                                     const float2* __restrict__ means2d, const int* __restrict__ radii,
+                                                     const float* __restrict__ depths, int TX, int TY,
+                                                     uint4* __restrict__ rec, uint32_t* __restrict__ n1) {
+    const int i = blockIdx.x * SB + threadIdx.x;
+    if (i >= (int)*vis_ptr) return;
+    const uint32_t g = order[i];
+    const float2 m = means2d[g];
+    int X0, X1, Y0, Y1;
+    tile_rect(m.x, m.y, radii[g], TX, TY, X0, X1, Y0, Y1);
+    rec[i] = make_uint4(g, (uint32_t)X0 | ((uint32_t)X1 << 16), (uint32_t)Y0 | ((uint32_t)Y1 << 16),
+                        __float_as_uint(depths[g]));
+    n1[i] = super_count(X0, X1, Y0, Y1);
+}
+
+// One thread per depth-sorted Gaussian: its entries (super-tile id, sorted
+// index), row-major over its super-tile rectangle.
+__global__ __launch_bounds__(SB) void k_super_emit(const u64* vis_ptr, const uint4* __restrict__ rec,
+                                                 const uint32_t* __restrict__ first, int SX, uint32_t P1,
+                                                 uint32_t* __restrict__ skey, uint32_t* __restrict__ sval) {
+    const int k = blockIdx.x * SB + threadIdx.x;
+    if (k >= (int)*vis_ptr) return;
+    const uint4 r = rec[k];
+    const int sx0 = (int)(r.y & 0xffffu) >> 3, sx1 = (int)(r.y >> 16) >> 3;
+    const int sy0 = (int)(r.z & 0xffffu) >> 3, sy1 = (int)(r.z >> 16) >> 3;
+    uint32_t pos = first[k];
+    for (int sy = sy0; sy <= sy1; ++sy)
+        for (int sx = sx0; sx <= sx1; ++sx, ++pos)
+            if (pos < P1) {
+                skey[pos] = (uint32_t)(sy * SX + sx);
+                sval[pos] = (uint32_t)k;
+            }
+}
+
+// [first, last + 1) of each super-tile in the grouped entries (left at (0, 0) if empty).
+__global__ __launch_bounds__(SB) void k_super_ranges(int P1, const uint32_t* __restrict__ skey, int S,
+                                                   uint2* __restrict__ sr) {
+    const int p = blockIdx.x * SB + threadIdx.x;
+    if (p >= P1) return;
+    const uint32_t s = skey[p];
+    if (s >= (uint32_t)S) return;
+    if (p == 0 || skey[p - 1] != s) sr[s].x = (uint32_t)p;
+    if (p == P1 - 1 || skey[p + 1] != s) sr[s].y = (uint32_t)(p + 1);
+}
+
+struct LoadPieces {
+    const uint2* sr;
+    __device__ uint32_t operator()(int s) const {
+        const uint2 r = sr[s];
+        return (r.y - r.x + PIECE - 1) / PIECE;
+    }
+};
+
+// The piece a wave takes: super-tile s (the last one whose first piece is at
+// or before pidx) and its entry range [e0, e1).
+__device__ __forceinline__ void piece_of(int pidx, int S, const uint32_t* __restrict__ pfirst,
+                                         const uint2* __restrict__ sr, int& s, int& e0, int& e1) {
+    int lo = 0, hi = S;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)pfirst[mid] <= pidx) lo = mid + 1; else hi = mid;
+    }
+    s = lo - 1;
+    const uint2 r = sr[s];
+    e0 = (int)r.x + (pidx - (int)pfirst[s]) * PIECE;
+    e1 = min((int)r.y, e0 + PIECE);
+}
+
+// One wave per piece, lane = tile (lane & 7, lane >> 3) of the super-tile:
+// each lane's number of the piece's entries whose rectangle holds its tile,
+// to counts[pidx][lane].
+__global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int SX, int TX, int TY,
+                                                 const uint32_t* __restrict__ pfirst, const uint2* __restrict__ sr,
+                                                 const uint32_t* __restrict__ sval, const uint4* __restrict__ rec,
+                                                 uint32_t* __restrict__ counts) {
+    const int lane = threadIdx.x & 63;
+    const int pidx = __builtin_amdgcn_readfirstlane(blockIdx.x * (SB / 64) + (int)(threadIdx.x >> 6));
+    if (pidx >= (int)*np_ptr) return;
+    int s, e0, e1;
+    piece_of(pidx, S, pfirst, sr, s, e0, e1);
+    const int tx = (s % SX) * SUPER + (lane & 7), ty = (s / SX) * SUPER + (lane >> 3);
+    const bool here = tx < TX && ty < TY;
+    uint32_t cnt = 0;
+    for (int eb = e0; eb < e1; eb += 64) {
+        const int ne = min(64, e1 - eb);
+        uint2 r = make_uint2(0u, 0u);
+        if (lane < ne) {
+            const uint4 q = rec[sval[eb + lane]];
+            r = make_uint2(q.y, q.z);
+        }
+        for (int u = 0; u < ne; ++u) {
+            const uint32_t xr = __builtin_amdgcn_readlane(r.x, u);
+            const uint32_t yr = __builtin_amdgcn_readlane(r.y, u);
+            cnt += (here && tx >= (int)(xr & 0xffffu) && tx <= (int)(xr >> 16) && ty >= (int)(yr & 0xffffu) &&
+                    ty <= (int)(yr >> 16)) ? 1u : 0u;
+        }
+    }
+    counts[(size_t)pidx * 64 + lane] = cnt;
+}
+
+// The same walk writing each such Gaussian at the lane's cursor, which starts
+// at the tile's first slot plus the counts of the super-tile's earlier pieces;
+// entries arrive in depth order, so each tile's run comes out in (depth,
+// index) order. A lane's consecutive slots are gathered in registers (four
+// values, two 64-bit keys) and stored as aligned 16-byte writes; an unaligned
+// head and the tail go one by one. Stores check their slot against P: always
+// true, it keeps a broken invariant from writing out of bounds.
+__global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int S, int SX, int TX, int TY,
+                                                 const uint32_t* __restrict__ pfirst, const uint2* __restrict__ sr,
+                                                 const uint32_t* __restrict__ sval, const uint4* __restrict__ rec,
+                                                 const uint32_t* __restrict__ offs, const uint2* __restrict__ ranges,
+                                                 uint32_t P, uint32_t* __restrict__ values, u64* __restrict__ keys64) {
+    const int lane = threadIdx.x & 63;
+    const int pidx = __builtin_amdgcn_readfirstlane(blockIdx.x * (SB / 64) + (int)(threadIdx.x >> 6));
+    if (pidx >= (int)*np_ptr) return;
+    int s, e0, e1;
+    piece_of(pidx, S, pfirst, sr, s, e0, e1);
+    const int tx = (s % SX) * SUPER + (lane & 7), ty = (s / SX) * SUPER + (lane >> 3);
+    const bool here = tx < TX && ty < TY;
+    const uint32_t t = here ? (uint32_t)(ty * TX + tx) : 0u;
+    uint32_t cur = here ? ranges[t].x + offs[(size_t)pidx * 64 + lane] : 0u;
+    uint32_t b0 = 0, b1 = 0, b2 = 0, b3 = 0;
+    uint32_t nb = 0;  // buffered values: slots [cur - nb, cur)
+    uint32_t kd = 0;  // buffered key's depth bits: slot cur - 1 when nk == 1
+    uint32_t nk = 0;
+    for (int eb = e0; eb < e1; eb += 64) {
+        const int ne = min(64, e1 - eb);
+        uint4 r = make_uint4(0u, 0u, 0u, 0u);
+        if (lane < ne) r = rec[sval[eb + lane]];
+        for (int u = 0; u < ne; ++u) {
+            const uint32_t xr = __builtin_amdgcn_readlane(r.y, u);
+            const uint32_t yr = __builtin_amdgcn_readlane(r.z, u);
+            const bool in = here && tx >= (int)(xr & 0xffffu) && tx <= (int)(xr >> 16) &&
+                            ty >= (int)(yr & 0xffffu) && ty <= (int)(yr >> 16);
+            if (in) {
+                const uint32_t g = (uint32_t)__builtin_amdgcn_readlane(r.x, u);
+                if (nb == 0u && (((uintptr_t)(values + cur)) & 15u) != 0u) {
+                    if (cur < P) values[cur] = g;
+                } else {
+                    b0 = nb == 0u ? g : b0;
+                    b1 = nb == 1u ? g : b1;
+                    b2 = nb == 2u ? g : b2;
+                    b3 = g;
+                    if (++nb == 4u) {
+                        if (cur < P) *reinterpret_cast<uint4*>(values + (cur - 3u)) = make_uint4(b0, b1, b2, b3);
+                        nb = 0u;
+                    }
+                }
+                if (keys64) {
+                    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane(r.w, u);
+                    if (nk == 0u && (((uintptr_t)(keys64 + cur)) & 15u) != 0u) {
+                        if (cur < P) keys64[cur] = ((u64)t << 32) | (u64)d;
+                    } else if (nk == 0u) {
+                        kd = d;
+                        nk = 1u;
+                    } else {
+                        if (cur < P) *reinterpret_cast<uint4*>(keys64 + (cur - 1u)) = make_uint4(kd, t, d, t);
+                        nk = 0u;
+                    }
+                }
+                ++cur;
+            }
+        }
+    }
+    const uint32_t t0 = cur - nb;
+    if (nb > 0u && t0 < P) values[t0] = b0;
+    if (nb > 1u && t0 + 1u < P) values[t0 + 1u] = b1;
+    if (nb > 2u && t0 + 2u < P) values[t0 + 2u] = b2;
+    if (nk == 1u && cur - 1u < P) keys64[cur - 1u] = ((u64)t << 32) | (u64)kd;
+}
+
+// One wave per super-tile, lane = tile: running sum over the super-tile's
+// pieces of the per-piece counts (in place, becoming each piece's offset
+// inside the tile's run) and the tile's total.
+__global__ __launch_bounds__(SB) void k_tile_prefix(const u64* np_ptr, int S, int SX, int TX, int TY,
+                                                  const uint32_t* __restrict__ pfirst, uint32_t* __restrict__ counts,
+                                                  uint32_t* __restrict__ tile_total) {
+    const int lane = threadIdx.x & 63;
+    const int s = __builtin_amdgcn_readfirstlane(blockIdx.x * (SB / 64) + (int)(threadIdx.x >> 6));
+    if (s >= S) return;
+    const int p0 = (int)pfirst[s];
+    const int p1 = s + 1 < S ? (int)pfirst[s + 1] : (int)*np_ptr;
+    uint32_t run = 0;
+    int p = p0;
+    for (; p + 8 <= p1; p += 8) {
+        uint32_t c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = counts[(size_t)(p + u) * 64 + lane];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            counts[(size_t)(p + u) * 64 + lane] = run;
+            run += c[u];
+        }
+    }
+    for (; p < p1; ++p) {
+        const uint32_t c = counts[(size_t)p * 64 + lane];
+        counts[(size_t)p * 64 + lane] = run;
+        run += c;
+    }
+    const int tx = (s % SX) * SUPER + (lane & 7), ty = (s / SX) * SUPER + (lane >> 3);
+    if (tx < TX && ty < TY) tile_total[ty * TX + tx] = run;
+}
+
+struct Grid2 {
+    int SX, SY, S;
+};
+Grid2 super_grid(int TX, int TY) {
+    Grid2 g;
+    g.SX = (TX + SUPER - 1) / SUPER;
+    g.SY = (TY + SUPER - 1) / SUPER;
+    g.S = g.SX * g.SY;
+    return g;
+}
+
+// Counters (u64): [0] visible, [1] super entries (scan), [2] P, [3] P1, [4] pieces.
+constexpr int NCOUNTERS = 8;
 
 }  // namespace
 
@@ -777,49 +723,57 @@ BinLayout bin_layout(int64_t n, int64_t capacity, int TX, int TY) {
         off += align256(bytes);
         return o;
     };
-    size_t nn = (size_t)(n > 0 ? n : 1), cap = (size_t)(capacity > 0 ? capacity : 1);
-    size_t ntiles = (size_t)TX * TY;
-    const bool chunked = ntiles <= (size_t)MAX_CHUNK_TILES;
+    const size_t nn = (size_t)(n > 0 ? n : 1), cap = (size_t)(capacity > 0 ? capacity : 1);
+    const size_t ntiles = (size_t)TX * TY;
+    const Grid2 G = super_grid(TX, TY);
+    const size_t S = (size_t)G.S;
+    const size_t max_pieces = (cap + PIECE - 1) / PIECE + S;
     L.dkeys[0] = take(4 * nn);
     L.dkeys[1] = take(4 * nn);
     L.didx[0] = take(4 * nn);
     L.didx[1] = take(4 * nn);
-    L.offsets = take(4 * (nn + 1));
-    size_t hist_entries = 256 * ((nn + SrcMem::E - 1) / SrcMem::E);
-    if (!chunked) {
-        size_t hp = 256 * ((cap + SrcPairs::E - 1) / SrcPairs::E);
-        if (hp > hist_entries) hist_entries = hp;
-    }
+    L.first = take(4 * nn);
+    L.rec = take(16 * nn);
+    L.skey[0] = take(4 * cap);  // super entries: at most one per pair
+    L.skey[1] = take(4 * cap);
+    L.sval[0] = take(4 * cap);
+    L.sval[1] = take(4 * cap);
+    L.sranges = take(8 * S);
+    L.pfirst = take(4 * (S + 1));
+    L.counts = take(4 * 64 * max_pieces);
+    L.tile_total = take(4 * ntiles);
+    size_t max_elems = nn > cap ? nn : cap;
+    const size_t hist_entries = 256 * ((max_elems + SrcMem::E - 1) / SrcMem::E);
     size_t max_scan = hist_entries;
     if (nn > max_scan) max_scan = nn;
     if (ntiles > max_scan) max_scan = ntiles;
+    if (S > max_scan) max_scan = S;
     L.partials = take(8 * ((max_scan + ST - 1) / ST + 1));
+    L.pair_part = take(8 * 2 * TOTALS_BLOCKS);
     L.hist = take(4 * hist_entries);
-    L.counters = take(8 * 4);
-    if (chunked) {
-        L.chunk_counts = take(4 * (size_t)MAX_CHUNKS * ntiles);
-        L.seg = take(4 * (size_t)((MAX_CHUNKS + SEG - 1) / SEG) * ntiles);
-        L.tile_total = take(4 * ntiles);
-        L.tkeys[0] = L.tkeys[1] = L.tvals = 0;
-    } else {
-        L.chunk_counts = L.seg = L.tile_total = 0;
-        L.tkeys[0] = take(4 * cap);
-        L.tkeys[1] = take(4 * cap);
-        L.tvals = take(4 * cap);
-    }
+    L.counters = take(8 * NCOUNTERS);
     L.total = off;
     return L;
 }
 
-hipError_t launch_bin_count(int n, const float* depths, const uint32_t* tiles_touched, char* ws, const BinLayout& L,
-                            unsigned long long* host_P, hipEvent_t ev, hipStream_t s) {
+hipError_t launch_bin_count(int n, int TX, int TY, const float* means2d, const int* radii, const float* depths,
+                            const uint32_t* tiles_touched, char* ws, const BinLayout& L,
+                            unsigned long long* host_counts, hipEvent_t ev, hipStream_t s) {
     u64* counters = reinterpret_cast<u64*>(ws + L.counters);
     u64* partials = reinterpret_cast<u64*>(ws + L.partials);
-    hipError_t e = fill(reinterpret_cast<uint32_t*>(counters), 8, 0u, s);
+    const float2* m2 = reinterpret_cast<const float2*>(means2d);
+    hipError_t e = fill(reinterpret_cast<uint32_t*>(counters), 2 * NCOUNTERS, 0u, s);
     if (e != hipSuccess) return e;
-    // the pair count first, on its way to the host while the rest runs
-    e = reduce_total(LoadPlain{tiles_touched}, n, partials, &counters[2], s);
-    if (e == hipSuccess) e = hipMemcpyAsync(host_P, &counters[2], sizeof(u64), hipMemcpyDeviceToHost, s);
+    // the pair counts first, on their way to the host while the rest runs
+    if (n > 0) {
+        int blocks = (n + SB - 1) / SB;
+        if (blocks > TOTALS_BLOCKS) blocks = TOTALS_BLOCKS;
+        u64* part = reinterpret_cast<u64*>(ws + L.pair_part);
+        k_pair_totals<<<blocks, SB, 0, s>>>(n, tiles_touched, m2, radii, TX, TY, part);
+        k_pair_sum<<<1, 1024, 0, s>>>(blocks, part, &counters[2]);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipMemcpyAsync(host_counts, &counters[2], 2 * sizeof(u64), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipEventRecord(ev, s);
     if (e != hipSuccess || n == 0) return e;
     uint32_t* dk[2] = {reinterpret_cast<uint32_t*>(ws + L.dkeys[0]), reinterpret_cast<uint32_t*>(ws + L.dkeys[1])};
@@ -835,76 +789,67 @@ hipError_t launch_bin_count(int n, const float* depths, const uint32_t* tiles_to
                        nullptr, nullptr, s);
         if (e != hipSuccess) return e;
     }
-    // 3. first pair index of each depth-sorted Gaussian
-    uint32_t* offsets = reinterpret_cast<uint32_t*>(ws + L.offsets);
-    return scan(LoadSortedTiles{tiles_touched, di[0]}, StoreInPlace{offsets}, n, &counters[0], partials, &counters[1],
-                s);
+    // 3. per depth-sorted Gaussian: record, super-tile count (in the free depth
+    //    key buffer) and first super-tile entry
+    uint32_t* first = reinterpret_cast<uint32_t*>(ws + L.first);
+    uint4* rec = reinterpret_cast<uint4*>(ws + L.rec);
+    k_sorted_records<<<(n + SB - 1) / SB, SB, 0, s>>>(&counters[0], di[0], m2, radii, depths, TX, TY, rec, dk[1]);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return scan(LoadPlain{dk[1]}, StoreInPlace{first}, n, &counters[0], partials, &counters[1], s);
 }
 
-hipError_t launch_bin_emit(int n, int P, int TX, int TY, const float* means2d, const int* radii, const float* depths,
-                           char* ws, const BinLayout& L, uint64_t* keys, uint32_t* values, uint32_t* ranges,
-                           hipStream_t s) {
+hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const BinLayout& L,
+                           uint64_t* keys, uint32_t* values, uint32_t* ranges, hipStream_t s) {
     const int ntiles = TX * TY;
+    if (P == 0 || n == 0 || P1 == 0) return fill(ranges, (size_t)2 * ntiles, 0u, s);
     u64* counters = reinterpret_cast<u64*>(ws + L.counters);
     u64* partials = reinterpret_cast<u64*>(ws + L.partials);
-    const uint32_t* offsets = reinterpret_cast<const uint32_t*>(ws + L.offsets);
-    const uint32_t* order = reinterpret_cast<const uint32_t*>(ws + L.didx[0]);
-    const float2* m2 = reinterpret_cast<const float2*>(means2d);
-    u64* k64 = reinterpret_cast<u64*>(keys);
-    if (P == 0 || n == 0) return fill(ranges, (size_t)2 * ntiles, 0u, s);
-
-    if (ntiles <= MAX_CHUNK_TILES) {
-        const int CH = max(MIN_CHUNK_PAIRS, (P + MAX_CHUNKS - 1) / MAX_CHUNKS);
-        const int nchunks = (P + CH - 1) / CH;
-        const int nseg = (nchunks + SEG - 1) / SEG;
-        uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.chunk_counts);
-        uint32_t* seg = reinterpret_cast<uint32_t*>(ws + L.seg);
-        uint32_t* total = reinterpret_cast<uint32_t*>(ws + L.tile_total);
-        const size_t lds = sizeof(uint32_t) * ntiles;
-        k_chunk_counts<<<nchunks, 256, lds, s>>>(CH, &counters[0], offsets, order, m2, radii, TX, TY, counts);
-        const int nst = nseg * ntiles;
-        k_seg_sum<<<(nst + SB - 1) / SB, SB, 0, s>>>(nchunks, ntiles, SEG, counts, seg);
-        k_seg_scan<<<(ntiles + SB - 1) / SB, SB, 0, s>>>(nseg, ntiles, seg, total);
-        hipError_t e = scan(LoadPlain{total}, StoreRanges{reinterpret_cast<uint2*>(ranges)}, ntiles, nullptr, partials,
-                            nullptr, s);
-        if (e != hipSuccess) return e;
-        k_chunk_base<<<(nst + SB - 1) / SB, SB, 0, s>>>(nchunks, ntiles, SEG, counts, seg);
-        k_chunk_place<<<nchunks, 64, lds, s>>>(CH, &counters[0], offsets, order, m2, radii, depths, TX, TY,
-                                               bits_for(ntiles), P, counts, reinterpret_cast<const uint2*>(ranges),
-                                               values, k64);
-        return hipGetLastError();
-    }
-
-    // large tile grids: stable LSD radix sort of the generated pairs by tile id
-    hipError_t e = fill(ranges, (size_t)2 * ntiles, 0u, s);
-    if (e != hipSuccess) return e;
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
-    uint32_t* tk[2] = {reinterpret_cast<uint32_t*>(ws + L.tkeys[0]), reinterpret_cast<uint32_t*>(ws + L.tkeys[1])};
-    uint32_t* tv = reinterpret_cast<uint32_t*>(ws + L.tvals);
-    const int tbits = bits_for(ntiles);
-    const int passes = (tbits + 7) / 8;
-    const int bpp = (tbits + passes - 1) / passes;
-    SrcPairs gen{offsets, order, m2, radii, &counters[0], TX, TY};
-    // value buffers alternate so that the last pass writes `values` (pass i
-    // writes `values` when passes - 1 - i is even); tile keys alternate in tk
-    uint32_t* kin = nullptr;
-    uint32_t* vin = nullptr;
+    const uint32_t* first = reinterpret_cast<const uint32_t*>(ws + L.first);
+    const uint4* rec = reinterpret_cast<const uint4*>(ws + L.rec);
+    uint32_t* sk[2] = {reinterpret_cast<uint32_t*>(ws + L.skey[0]), reinterpret_cast<uint32_t*>(ws + L.skey[1])};
+    uint32_t* sv[2] = {reinterpret_cast<uint32_t*>(ws + L.sval[0]), reinterpret_cast<uint32_t*>(ws + L.sval[1])};
+    uint2* sr = reinterpret_cast<uint2*>(ws + L.sranges);
+    uint32_t* pfirst = reinterpret_cast<uint32_t*>(ws + L.pfirst);
+    uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.counts);
+    uint32_t* tile_total = reinterpret_cast<uint32_t*>(ws + L.tile_total);
+    const Grid2 G = super_grid(TX, TY);
+
+    // 3. super-tile entries in depth order, then grouped by super-tile (stable)
+    k_super_emit<<<(n + SB - 1) / SB, SB, 0, s>>>(&counters[0], rec, first, G.SX, (uint32_t)P1, sk[0], sv[0]);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int sbits = bits_for(G.S);
+    const int passes = (sbits + 7) / 8;
+    const int bpp = (sbits + passes - 1) / passes;
+    int cur = 0;
     for (int pass = 0; pass < passes; ++pass) {
         const int shift = pass * bpp;
-        const int bits = min(bpp, tbits - shift);
-        const bool last = pass == passes - 1;
-        uint32_t* kout = tk[pass & 1];
-        uint32_t* vout = ((passes - 1 - pass) % 2 == 0) ? values : tv;
-        u64* k64out = last ? k64 : nullptr;
-        if (pass == 0)
-            e = radix_pass(gen, P, nullptr, shift, bits, hist, partials, kout, vout, k64out, depths, s);
-        else
-            e = radix_pass(SrcMem{kin, vin}, P, nullptr, shift, bits, hist, partials, kout, vout, k64out, depths, s);
+        const int bits = min(bpp, sbits - shift);
+        e = radix_pass(SrcMem{sk[cur], sv[cur]}, P1, nullptr, shift, bits, hist, partials, sk[cur ^ 1], sv[cur ^ 1],
+                       nullptr, nullptr, s);
         if (e != hipSuccess) return e;
-        kin = kout;
-        vin = vout;
+        cur ^= 1;
     }
-    k_ranges<<<(P + SB - 1) / SB, SB, 0, s>>>(P, kin, reinterpret_cast<uint2*>(ranges));
+    e = fill(reinterpret_cast<uint32_t*>(sr), (size_t)2 * G.S, 0u, s);
+    if (e != hipSuccess) return e;
+    k_super_ranges<<<(P1 + SB - 1) / SB, SB, 0, s>>>(P1, sk[cur], G.S, sr);
+    // pieces of PIECE entries, per super-tile
+    e = scan(LoadPieces{sr}, StoreInPlace{pfirst}, G.S, nullptr, partials, &counters[4], s);
+    if (e != hipSuccess) return e;
+    // 4. per-tile counts per piece, their running sums and tile totals, tile ranges, placement
+    const int max_pieces = (P1 + PIECE - 1) / PIECE + G.S;
+    const int wpb = SB / 64;
+    k_tile_count<<<(max_pieces + wpb - 1) / wpb, SB, 0, s>>>(&counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur], rec,
+                                                             counts);
+    k_tile_prefix<<<(G.S + wpb - 1) / wpb, SB, 0, s>>>(&counters[4], G.S, G.SX, TX, TY, pfirst, counts, tile_total);
+    e = scan(LoadPlain{tile_total}, StoreRanges{reinterpret_cast<uint2*>(ranges)}, ntiles, nullptr, partials, nullptr,
+             s);
+    if (e != hipSuccess) return e;
+    k_tile_place<<<(max_pieces + wpb - 1) / wpb, SB, 0, s>>>(&counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur], rec,
+                                                             counts, reinterpret_cast<const uint2*>(ranges),
+                                                             (uint32_t)P, values, reinterpret_cast<u64*>(keys));
     return hipGetLastError();
 }
 

@@ -23,29 +23,31 @@ hipError_t launch_preprocess_bwd(const DevCam& cam, int K, int sh_rows, float lo
 // Binning. The workspace layout is computed by bin_layout (binsort.hip).
 struct BinLayout {
     size_t dkeys[2], didx[2];  // depth-sort ping-pong (n entries each)
-    size_t offsets;            // per-sorted-Gaussian first pair index (n + 1)
+    size_t first;              // per depth-sorted Gaussian: first super-tile entry (n)
+    size_t rec;                // per depth-sorted Gaussian: uint4 record (n)
+    size_t skey[2], sval[2];   // super-tile entries (super-tile id, sorted index), ping-pong (capacity each)
+    size_t sranges;            // per super-tile entry range
+    size_t pfirst;             // per super-tile first piece
+    size_t counts;             // per piece and tile: count, then offset within the tile's run
+    size_t tile_total;         // pairs per tile
     size_t partials;           // u64 scan partials
+    size_t pair_part;          // u64 per-block partial pair counts
     size_t hist;               // radix histograms
-    size_t counters;           // u64 [0] visible count, [1] and [2] pair count
-    size_t chunk_counts;       // chunked placement: [chunk][tile] counts, then bases
-    size_t seg;                // chunked placement: [segment][tile] sums, then bases
-    size_t tile_total;         // chunked placement: pairs per tile
-    size_t tkeys[2];           // radix path: pair tile-key ping-pong (capacity each)
-    size_t tvals;              // radix path: pair value scratch (capacity)
+    size_t counters;           // u64 counters
     size_t total;
 };
 BinLayout bin_layout(int64_t n, int64_t capacity, int TX, int TY);
 
-// Phase 1 (no host dependence): pair count P (copied to *host_P, pinned, with
-// `ev` recorded after the copy), visible compaction, depth sort and
-// per-Gaussian first pair index.
-hipError_t launch_bin_count(int n, const float* depths, const uint32_t* tiles_touched, char* ws, const BinLayout& L,
-                            unsigned long long* host_P, hipEvent_t ev, hipStream_t stream);
-// Phase 2 (P known on the host and within capacity): ranges, then the tile
-// sort of the generated pairs into `values` (and the 64-bit keys if non-NULL).
-hipError_t launch_bin_emit(int n, int P, int TX, int TY, const float* means2d, const int* radii,
-                           const float* depths, char* ws, const BinLayout& L, uint64_t* keys,
-                           uint32_t* values, uint32_t* ranges, hipStream_t stream);
+// Phase 1 (no host dependence): pair count P and super-tile entry count P1
+// (copied to host_counts[0..1], pinned, with `ev` recorded after the copy),
+// visible compaction, depth sort and the per-Gaussian records.
+hipError_t launch_bin_count(int n, int TX, int TY, const float* means2d, const int* radii, const float* depths,
+                            const uint32_t* tiles_touched, char* ws, const BinLayout& L,
+                            unsigned long long* host_counts, hipEvent_t ev, hipStream_t stream);
+// Phase 2 (P, P1 known on the host, P within capacity): the pairs in (tile,
+// depth, index) order into `values` (and the 64-bit keys if non-NULL), and ranges.
+hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const BinLayout& L,
+                           uint64_t* keys, uint32_t* values, uint32_t* ranges, hipStream_t stream);
 
 hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_t stream);
 

@@ -99,13 +99,11 @@ def test_null_pointers_and_sizes_rejected():
 
 
 def test_workspace_sizes_monotone():
-    # grids up to 14336 tiles place pairs with per-chunk LDS cursors: no pair-sized scratch
+    # super-tile entries (at most one per pair) are sized by the pair capacity
     a = raster.gs_bin_sort_workspace_size(1000, 10_000, 128, 128)
     b = raster.gs_bin_sort_workspace_size(1000, 20_000, 128, 128)
-    assert 0 < a == b and a % 256 == 0
+    assert 0 < a < b and a % 256 == 0 and b - a >= 4 * 4 * 10_000
     assert raster.gs_bin_sort_workspace_size(2000, 10_000, 128, 128) > a
-    # larger grids sort the pairs by tile: scratch grows with the pair capacity
     c = raster.gs_bin_sort_workspace_size(1000, 10_000, 2560, 2200)
-    d = raster.gs_bin_sort_workspace_size(1000, 20_000, 2560, 2200)
-    assert 0 < c < d and c % 256 == 0 and d - c >= 3 * 4 * 10_000
+    assert c > a and c % 256 == 0
     assert raster.gs_render_bwd_workspace_size(1000) >= 1000 * 12 * 4

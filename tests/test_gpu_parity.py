@@ -338,9 +338,9 @@ def test_lower_active_sh_degree_than_stored():
     del sc_deg1
 
 
-def test_large_tile_grid_radix_path():
-    """More tiles than per-chunk LDS cursors hold (2560x2200 = 22080 tiles): the
-    pairs are ordered by the radix path instead, with the same result."""
+def test_large_tile_grid_two_pass_super_sort():
+    """2560x2200 = 22080 tiles in 20x18 = 360 super-tiles: grouping the
+    super-tile entries takes two radix passes (9 key bits) instead of one."""
     rng = np.random.default_rng(8)
     cam = Camera(2560, 2200, 1500.0, 1500.0, 1280.0, 1100.0, np.eye(3, dtype=np.float32), np.zeros(3, np.float32))
     sc = _scene_for(cam, 3000, rng, deg=1, big=20)
