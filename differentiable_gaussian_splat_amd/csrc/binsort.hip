@@ -592,20 +592,27 @@ __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int
     counts[(size_t)pidx * 64 + lane] = cnt;
 }
 
-// The same walk writing each such Gaussian at the lane's cursor, which starts
-// at the tile's first slot plus the counts of the super-tile's earlier pieces;
-// entries arrive in depth order, so each tile's run comes out in (depth,
-// index) order. A lane's consecutive slots are gathered in registers (four
-// values, two 64-bit keys) and stored as aligned 16-byte writes; an unaligned
-// head and the tail go one by one. Stores check their slot against P: always
-// true, it keeps a broken invariant from writing out of bounds.
-__global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int S, int SX, int TX, int TY,
+// The same walk, placing each such Gaussian: a lane's tile receives the
+// piece's entries in depth order, starting at the tile's first slot plus the
+// counts of the super-tile's earlier pieces, so each tile's run comes out in
+// (depth, index) order. Lanes stage their Gaussians (and depth bits) in LDS
+// bins; when a bin may overflow, and at the end, the wave writes the bins out
+// one tile at a time, consecutive lanes on consecutive slots of that tile's
+// run. Stores check their slot against P: always true, it keeps a broken
+// invariant from writing out of bounds.
+constexpr int BIN = 32;         // staged entries per tile
+constexpr int BIN_STRIDE = 33;  // odd word stride: lane-major writes and slot-major reads both spread over banks
+constexpr int BIN_STEP = 8;     // entries walked between fill checks
+
+__global__ __launch_bounds__(64) void k_tile_place(const u64* np_ptr, int S, int SX, int TX, int TY,
                                                  const uint32_t* __restrict__ pfirst, const uint2* __restrict__ sr,
                                                  const uint32_t* __restrict__ sval, const uint4* __restrict__ rec,
                                                  const uint32_t* __restrict__ offs, const uint2* __restrict__ ranges,
                                                  uint32_t P, uint32_t* __restrict__ values, u64* __restrict__ keys64) {
-    const int lane = threadIdx.x & 63;
-    const int pidx = __builtin_amdgcn_readfirstlane(blockIdx.x * (SB / 64) + (int)(threadIdx.x >> 6));
+    __shared__ uint32_t s_g[64 * BIN_STRIDE];
+    __shared__ uint32_t s_d[64 * BIN_STRIDE];
+    const int lane = threadIdx.x;
+    const int pidx = __builtin_amdgcn_readfirstlane((int)blockIdx.x);
     if (pidx >= (int)*np_ptr) return;
     int s, e0, e1;
     piece_of(pidx, S, pfirst, sr, s, e0, e1);
@@ -613,54 +620,46 @@ __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int S, int
     const bool here = tx < TX && ty < TY;
     const uint32_t t = here ? (uint32_t)(ty * TX + tx) : 0u;
     uint32_t cur = here ? ranges[t].x + offs[(size_t)pidx * 64 + lane] : 0u;
-    uint32_t b0 = 0, b1 = 0, b2 = 0, b3 = 0;
-    uint32_t nb = 0;  // buffered values: slots [cur - nb, cur)
-    uint32_t kd = 0;  // buffered key's depth bits: slot cur - 1 when nk == 1
-    uint32_t nk = 0;
+    uint32_t c = 0;  // staged in this lane's bin
+    auto flush = [&]() {
+        wave_lds_sync();
+        uint64_t m = __ballot(c > 0u);
+        while (m) {
+            const int j = __builtin_ctzll(m);
+            m &= m - 1ull;
+            const uint32_t cj = (uint32_t)__builtin_amdgcn_readlane((int)c, j);
+            const uint32_t pj = (uint32_t)__builtin_amdgcn_readlane((int)cur, j);
+            const uint32_t tj = (uint32_t)__builtin_amdgcn_readlane((int)t, j);
+            if ((uint32_t)lane < cj) {
+                const uint32_t pos = pj + (uint32_t)lane;
+                if (pos < P) {
+                    values[pos] = s_g[j * BIN_STRIDE + lane];
+                    if (keys64) keys64[pos] = ((u64)tj << 32) | (u64)s_d[j * BIN_STRIDE + lane];
+                }
+            }
+        }
+        cur += c;
+        c = 0u;
+        wave_lds_sync();
+    };
     for (int eb = e0; eb < e1; eb += 64) {
         const int ne = min(64, e1 - eb);
         uint4 r = make_uint4(0u, 0u, 0u, 0u);
         if (lane < ne) r = rec[sval[eb + lane]];
         for (int u = 0; u < ne; ++u) {
+            if ((u & (BIN_STEP - 1)) == 0 && __any(c > (uint32_t)(BIN - BIN_STEP))) flush();
             const uint32_t xr = __builtin_amdgcn_readlane(r.y, u);
             const uint32_t yr = __builtin_amdgcn_readlane(r.z, u);
             const bool in = here && tx >= (int)(xr & 0xffffu) && tx <= (int)(xr >> 16) &&
                             ty >= (int)(yr & 0xffffu) && ty <= (int)(yr >> 16);
             if (in) {
-                const uint32_t g = (uint32_t)__builtin_amdgcn_readlane(r.x, u);
-                if (nb == 0u && (((uintptr_t)(values + cur)) & 15u) != 0u) {
-                    if (cur < P) values[cur] = g;
-                } else {
-                    b0 = nb == 0u ? g : b0;
-                    b1 = nb == 1u ? g : b1;
-                    b2 = nb == 2u ? g : b2;
-                    b3 = g;
-                    if (++nb == 4u) {
-                        if (cur < P) *reinterpret_cast<uint4*>(values + (cur - 3u)) = make_uint4(b0, b1, b2, b3);
-                        nb = 0u;
-                    }
-                }
-                if (keys64) {
-                    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane(r.w, u);
-                    if (nk == 0u && (((uintptr_t)(keys64 + cur)) & 15u) != 0u) {
-                        if (cur < P) keys64[cur] = ((u64)t << 32) | (u64)d;
-                    } else if (nk == 0u) {
-                        kd = d;
-                        nk = 1u;
-                    } else {
-                        if (cur < P) *reinterpret_cast<uint4*>(keys64 + (cur - 1u)) = make_uint4(kd, t, d, t);
-                        nk = 0u;
-                    }
-                }
-                ++cur;
+                s_g[lane * BIN_STRIDE + c] = (uint32_t)__builtin_amdgcn_readlane(r.x, u);
+                s_d[lane * BIN_STRIDE + c] = (uint32_t)__builtin_amdgcn_readlane(r.w, u);
+                ++c;
             }
         }
     }
-    const uint32_t t0 = cur - nb;
-    if (nb > 0u && t0 < P) values[t0] = b0;
-    if (nb > 1u && t0 + 1u < P) values[t0 + 1u] = b1;
-    if (nb > 2u && t0 + 2u < P) values[t0 + 2u] = b2;
-    if (nk == 1u && cur - 1u < P) keys64[cur - 1u] = ((u64)t << 32) | (u64)kd;
+    flush();
 }
 
 // One wave per super-tile, lane = tile: running sum over the super-tile's
@@ -847,9 +846,9 @@ hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const
     e = scan(LoadPlain{tile_total}, StoreRanges{reinterpret_cast<uint2*>(ranges)}, ntiles, nullptr, partials, nullptr,
              s);
     if (e != hipSuccess) return e;
-    k_tile_place<<<(max_pieces + wpb - 1) / wpb, SB, 0, s>>>(&counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur], rec,
-                                                             counts, reinterpret_cast<const uint2*>(ranges),
-                                                             (uint32_t)P, values, reinterpret_cast<u64*>(keys));
+    k_tile_place<<<max_pieces, 64, 0, s>>>(&counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur], rec, counts,
+                                           reinterpret_cast<const uint2*>(ranges), (uint32_t)P, values,
+                                           reinterpret_cast<u64*>(keys));
     return hipGetLastError();
 }
 
