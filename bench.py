@@ -5,7 +5,7 @@ A step is one pass of the whole hot path on one synthetic frame whose inputs
 are already resident in HBM: gs_preprocess -> gs_bin_sort -> gs_render_fwd ->
 (zero the parameter gradients) -> gs_render_bwd (its two halves,
 gs_render_bwd_raster and gs_preprocess_bwd, called in turn so that the
-raster half can be timed on its own). Default workload: the contention-heavy
+raster kernel can be timed on its own). Default workload: the contention-heavy
 scene (1,000,000 Gaussians, SH degree 3, 1920x1080, 64 clusters plus 2%
 large Gaussians). Per-stage times come from HIP events recorded on the
 launch stream around each call; the step time from the host clock between
@@ -32,7 +32,16 @@ if ROOT not in sys.path:
 
 METRIC = "fwd+bwd splat-raster ms/frame, 1M Gaussians @1080p; % HBM/atomic roofline"
 HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
-FP32_VECTOR_TFLOPS = 157.3      # MI355X published fp32 vector rate
+# Vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane-operations/s,
+# doubled by dual-issue packed fp32 = 78.6 T op/s (the published 157.3 TFLOP/s
+# counts each fused multiply-add as two).
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 * 2 / 1e12
+# Backward arithmetic per walked (pixel, list entry): 45 fp32 vector operations
+# (falloff, alpha, transmittance, colour and the six moment sums) plus one
+# exp2 and one reciprocal.
+BWD_OPS_PER_ENTRY = 47
+ATOMICS_PER_TILE_ENTRY = 9      # one add per gradient value per (tile, Gaussian)
+PROFILES = os.path.join(ROOT, "profiles")
 STAGES = ["preprocess", "bin_sort", "render_fwd", "zero_grads", "render_bwd_raster", "preprocess_bwd"]
 
 
@@ -141,6 +150,7 @@ def main():
             if vi == 0:  # gradients are zeroed once per step and summed over the views
                 for g in grads.values():
                     g.zero_()
+            grad2d.zero_()  # the pixel sums belong to one view
             e[4].record(stream)
             raster.gs_render_bwd_raster(cam, opt, n, ranges, r._values, P, means2d, conic, rgb, final_T, n_contrib,
                                         dLs[vi], grad2d)
@@ -177,21 +187,34 @@ def main():
     bwd_bytes, walked = backward_bytes(nc_np, rg_np, W, H, touched)
     E_b = int(nc_np.sum())
     t_bwd = stage_ms[STAGES.index("render_bwd_raster")] * 1e-3
-    achieved = bwd_bytes / t_bwd / 1e9
+    valu_tops = BWD_OPS_PER_ENTRY * E_b / t_bwd / 1e12
 
-    # measured HBM read rate (context beside the published peak)
+    # measured denominators: HBM streaming read, and no-return fp32 atomic adds
+    # in the backward's flush pattern (9 lanes on one record, records hashed
+    # over the visible Gaussians)
+    def timed(fn, reps):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
     buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1, dtype=torch.float32, device=dev)
-    for _ in range(2):
-        raster.gs_mb_hbm_read(buf, sink)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(5):
-        raster.gs_mb_hbm_read(buf, sink)
-    e1.record(stream)
-    e1.synchronize()
-    hbm_read = 5 * buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    hbm_read = buf.numel() / timed(lambda: raster.gs_mb_hbm_read(buf, sink), 5) / 1e9
+    # known-size copy: the reference for scaling rocprof's FETCH_SIZE / WRITE_SIZE
+    half = buf.numel() // 4
+    raster.gs_mb_hbm_copy(buf[half:2 * half], buf[:half])
     del buf
+    n_atomics = ATOMICS_PER_TILE_ENTRY * walked
+    recs = torch.zeros((max(touched, 1), raster.GRAD2D_STRIDE), dtype=torch.float32, device=dev)
+    t_at = timed(lambda: raster.gs_mb_atomic(recs, recs.shape[0], n_atomics, ATOMICS_PER_TILE_ENTRY), 3)
+    atomic_rate = n_atomics / t_at
+    del recs
+    t_hbm_floor = bwd_bytes / (hbm_read * 1e9)
+    t_atomic_floor = n_atomics / atomic_rate
 
     result = {
         "metric": METRIC,
@@ -210,18 +233,27 @@ def main():
             "workload": scenes.CONFIG_NAMES[args.config],
             "config": args.config, "seed": args.seed, "gaussians": n, "views_per_step": len(views),
             "image": [W, H], "sh_degree": sc.sh_degree, "pairs": int(max(last_P)),
-            "visible": touched, "E_b": E_b, "bwd_entries_walked": walked,
+            "visible": touched, "E_b": E_b, "bwd_tile_entries_walked": walked,
         },
         "stages_ms": {s: round(float(t), 4) for s, t in zip(STAGES, stage_ms)},
         "roofline": {
-            "kernel": "k_render_bwd (gs_render_bwd_raster)",
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 5),
-            "traffic": None,
-            "algorithmic_bytes": bwd_bytes,
+            "kernel": "k_render_bwd",
+            "bound": "alu",
+            "achieved": round(valu_tops, 2),
+            "peak": round(VALU_PEAK_TOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(valu_tops / VALU_PEAK_TOPS, 4),
+            "traffic": pmc_traffic("k_render_bwd", args.config),
+            "work": f"{BWD_OPS_PER_ENTRY} fp32 vector ops (an FMA counted once) per walked pixel-entry x E_b",
+            "launch_ms": round(t_bwd * 1e3, 4),
+        },
+        "bwd_hbm_atomic_roofline": {
+            "hbm_bytes": bwd_bytes,
+            "hbm_floor_ms": round(t_hbm_floor * 1e3, 4),
+            "atomics": n_atomics,
+            "atomic_rate_per_s": round(atomic_rate, 1),
+            "atomic_floor_ms": round(t_atomic_floor * 1e3, 4),
+            "frac": round(max(t_hbm_floor, t_atomic_floor) / t_bwd, 4),
         },
         "measured_hbm_read_GBps": round(hbm_read, 1),
     }
@@ -232,6 +264,31 @@ def main():
             radii=radii.cpu().numpy(), depths=depths.cpu().numpy(), values=r._values[:last_P[-1]].cpu().numpy(),
             ranges=rg_np, P=last_P[-1]), view=views[-1])
     print(json.dumps(result), flush=True)
+
+
+def pmc_traffic(kernel, config):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (rocprofv3 FETCH_SIZE and WRITE_SIZE, scaled by the copy kernel's own
+    reading), or None if there is none for this workload or the kernel's
+    sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(PROFILES, f"{kernel}_c{config}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    srcs = fields.get("sources", "").split()
+    h = hashlib.sha256()
+    for rel in srcs:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    if not srcs or h.hexdigest() != fields.get("sources_sha256"):
+        return None
+    return int(float(fields["hbm_bytes_per_launch"]))
 
 
 def cpu_baseline(sc, args, fr_state, view):

@@ -349,13 +349,10 @@ gs_status gs_render_bwd_raster(const gs_camera* cam, const gs_options* opt, int6
         REQUIRE(aligned(grad2d, 16), "grad2d must be 16-byte aligned");
         REQUIRE(aligned(conic_opacity, 16), "conic_opacity must be 16-byte aligned");
         REQUIRE(aligned(means2d, 8) && aligned(ranges, 8), "means2d and ranges must be 8-byte aligned");
-        hipStream_t s = (hipStream_t)stream;
-        st = hip_check(gs::launch_fill_u32(reinterpret_cast<uint32_t*>(grad2d), (size_t)n * gs::GRAD2D_STRIDE, 0u, s),
-                       "gs_render_bwd_raster(zero)");
-        if (st != GS_OK || n_pairs == 0) return st;
+        if (n_pairs == 0) return GS_OK;
         return hip_check(gs::launch_render_bwd(c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
                                                conic_opacity, rgb, opt->bg, final_T, n_contrib, dL_dimage, grad2d,
-                                               s),
+                                               (hipStream_t)stream),
                          "gs_render_bwd_raster");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_render_bwd_raster: unexpected exception");

@@ -199,8 +199,9 @@ gs_status gs_render_bwd(const gs_camera *cam, const gs_options *opt, int64_t n,
 /* The two halves of gs_render_bwd, for callers that time or test them apart
  * (gs_render_bwd = gs_render_bwd_raster followed by gs_preprocess_bwd). */
 
-/* Per-Gaussian pixel sums of the reverse blend, OVERWRITING
- * grad2d[n, GS_GRAD2D_STRIDE] (16-byte aligned). With, per blended
+/* Per-Gaussian pixel sums of the reverse blend of ONE view, ADDED to
+ * grad2d[n, GS_GRAD2D_STRIDE] (16-byte aligned; the caller zeroes it before
+ * each view: the sums belong to that view's projection). With, per blended
  * (pixel, Gaussian) entry, w = dx + beta dy and h = opacity G dL/dalpha
  * (h = 0 where alpha was clamped at 0.99), record g holds
  *   [0..2] dL/drgb, [3] sum h, [4] sum h w^2, [5] sum h w dy, [6] sum h dy^2,

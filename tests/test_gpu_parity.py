@@ -298,8 +298,9 @@ def test_multi_view_accumulation():
 
 @pytest.mark.parametrize("deg", [3, 1])
 def test_chain_rule_accumulates_exactly(deg):
-    """The parameter step adds into its outputs: run twice on the same pixel
-    sums it gives exactly twice the first result (no atomics in this step).
+    """Both backward halves add into their outputs. The parameter step run
+    twice on the same pixel sums gives exactly twice the first result (no
+    atomics in this step).
     Degree 3 with 16 stored rows stages whole SH records; degree 1 stages a
     prefix of each record; 59_993 Gaussians leave a ragged last block."""
     sc = make_scene(5, 1, n=59_993)
@@ -308,6 +309,14 @@ def test_chain_rule_accumulates_exactly(deg):
     grad2d = torch.zeros(n * raster.GRAD2D_STRIDE, dtype=torch.float32, device=pd["means"].device)
     raster.gs_render_bwd_raster(fr.cam, fr.opt, n, fr.ranges, fr.values, fr.n_pairs, fr.means2d, fr.conic_opacity,
                                 fr.rgb, fr.final_T, fr.n_contrib, to_dev(sc.dL_dimage[0]), grad2d)
+    # the raster half adds into grad2d too: two calls give twice one (to atomic-order rounding)
+    twice = torch.zeros_like(grad2d)
+    for _ in range(2):
+        raster.gs_render_bwd_raster(fr.cam, fr.opt, n, fr.ranges, fr.values, fr.n_pairs, fr.means2d,
+                                    fr.conic_opacity, fr.rgb, fr.final_T, fr.n_contrib, to_dev(sc.dL_dimage[0]),
+                                    twice)
+    torch.cuda.synchronize()
+    assert rel_l2(twice.cpu().numpy().astype(np.float64), 2.0 * grad2d.cpu().numpy().astype(np.float64)) < 1e-5
     g = raster.zero_grads(pd["means"], pd["sh"])
     g["means2d"] = torch.zeros((n, 2), dtype=torch.float32, device=pd["means"].device)
     outs = [g["means"], g["scales"], g["quats"], g["opacities"], g["sh"], g["means2d"]]
