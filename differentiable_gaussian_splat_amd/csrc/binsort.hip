@@ -592,74 +592,53 @@ __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int
     counts[(size_t)pidx * 64 + lane] = cnt;
 }
 
-// The same walk, placing each such Gaussian: a lane's tile receives the
-// piece's entries in depth order, starting at the tile's first slot plus the
-// counts of the super-tile's earlier pieces, so each tile's run comes out in
-// (depth, index) order. Lanes stage their Gaussians (and depth bits) in LDS
-// bins; when a bin may overflow, and at the end, the wave writes the bins out
-// one tile at a time, consecutive lanes on consecutive slots of that tile's
-// run. Stores check their slot against P: always true, it keeps a broken
+// Placement, with the roles turned: lane = entry of a 64-entry group of the
+// piece, and a uniform loop over the super-tile's 64 tiles. For tile lt a
+// ballot of the rectangle tests gives the group's entries that hold it; in
+// depth order they take the next slots of the tile's run, lane at cursor +
+// (matching lanes below it). One store instruction therefore writes
+// consecutive slots of one run. The cursors (the tile's first slot plus the
+// counts of the super-tile's earlier pieces) live one per lane, lane lt for
+// tile lt. Stores check their slot against P: always true, it keeps a broken
 // invariant from writing out of bounds.
-constexpr int BIN = 32;         // staged entries per tile
-constexpr int BIN_STRIDE = 33;  // odd word stride: lane-major writes and slot-major reads both spread over banks
-constexpr int BIN_STEP = 8;     // entries walked between fill checks
-
-__global__ __launch_bounds__(64) void k_tile_place(const u64* np_ptr, int S, int SX, int TX, int TY,
+__global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int S, int SX, int TX, int TY,
                                                  const uint32_t* __restrict__ pfirst, const uint2* __restrict__ sr,
                                                  const uint32_t* __restrict__ sval, const uint4* __restrict__ rec,
                                                  const uint32_t* __restrict__ offs, const uint2* __restrict__ ranges,
                                                  uint32_t P, uint32_t* __restrict__ values, u64* __restrict__ keys64) {
-    __shared__ uint32_t s_g[64 * BIN_STRIDE];
-    __shared__ uint32_t s_d[64 * BIN_STRIDE];
-    const int lane = threadIdx.x;
-    const int pidx = __builtin_amdgcn_readfirstlane((int)blockIdx.x);
+    const int lane = threadIdx.x & 63;
+    const int pidx = __builtin_amdgcn_readfirstlane(blockIdx.x * (SB / 64) + (int)(threadIdx.x >> 6));
     if (pidx >= (int)*np_ptr) return;
     int s, e0, e1;
     piece_of(pidx, S, pfirst, sr, s, e0, e1);
-    const int tx = (s % SX) * SUPER + (lane & 7), ty = (s / SX) * SUPER + (lane >> 3);
-    const bool here = tx < TX && ty < TY;
-    const uint32_t t = here ? (uint32_t)(ty * TX + tx) : 0u;
-    uint32_t cur = here ? ranges[t].x + offs[(size_t)pidx * 64 + lane] : 0u;
-    uint32_t c = 0;  // staged in this lane's bin
-    auto flush = [&]() {
-        wave_lds_sync();
-        uint64_t m = __ballot(c > 0u);
-        while (m) {
-            const int j = __builtin_ctzll(m);
-            m &= m - 1ull;
-            const uint32_t cj = (uint32_t)__builtin_amdgcn_readlane((int)c, j);
-            const uint32_t pj = (uint32_t)__builtin_amdgcn_readlane((int)cur, j);
-            const uint32_t tj = (uint32_t)__builtin_amdgcn_readlane((int)t, j);
-            if ((uint32_t)lane < cj) {
-                const uint32_t pos = pj + (uint32_t)lane;
-                if (pos < P) {
-                    values[pos] = s_g[j * BIN_STRIDE + lane];
-                    if (keys64) keys64[pos] = ((u64)tj << 32) | (u64)s_d[j * BIN_STRIDE + lane];
-                }
-            }
-        }
-        cur += c;
-        c = 0u;
-        wave_lds_sync();
-    };
+    const int sx0 = (s % SX) * SUPER, sy0 = (s / SX) * SUPER;
+    const int mtx = sx0 + (lane & 7), mty = sy0 + (lane >> 3);
+    uint32_t cur = (mtx < TX && mty < TY) ? ranges[mty * TX + mtx].x + offs[(size_t)pidx * 64 + lane] : 0u;
+    const uint64_t lt_mask = lanemask_lt();
     for (int eb = e0; eb < e1; eb += 64) {
         const int ne = min(64, e1 - eb);
+        const bool live = lane < ne;
         uint4 r = make_uint4(0u, 0u, 0u, 0u);
-        if (lane < ne) r = rec[sval[eb + lane]];
-        for (int u = 0; u < ne; ++u) {
-            if ((u & (BIN_STEP - 1)) == 0 && __any(c > (uint32_t)(BIN - BIN_STEP))) flush();
-            const uint32_t xr = __builtin_amdgcn_readlane(r.y, u);
-            const uint32_t yr = __builtin_amdgcn_readlane(r.z, u);
-            const bool in = here && tx >= (int)(xr & 0xffffu) && tx <= (int)(xr >> 16) &&
-                            ty >= (int)(yr & 0xffffu) && ty <= (int)(yr >> 16);
+        if (live) r = rec[sval[eb + lane]];
+        const int X0 = (int)(r.y & 0xffffu), X1 = (int)(r.y >> 16);
+        const int Y0 = (int)(r.z & 0xffffu), Y1 = (int)(r.z >> 16);
+        for (int l = 0; l < 64; ++l) {
+            const int tx = sx0 + (l & 7), ty = sy0 + (l >> 3);
+            if (tx >= TX || ty >= TY) continue;  // uniform: the super-tile overhangs the grid
+            const bool in = live && tx >= X0 && tx <= X1 && ty >= Y0 && ty <= Y1;
+            const uint64_t m = __ballot(in);
+            if (m == 0ull) continue;
+            const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)cur, l);
             if (in) {
-                s_g[lane * BIN_STRIDE + c] = (uint32_t)__builtin_amdgcn_readlane(r.x, u);
-                s_d[lane * BIN_STRIDE + c] = (uint32_t)__builtin_amdgcn_readlane(r.w, u);
-                ++c;
+                const uint32_t pos = base + (uint32_t)__popcll(m & lt_mask);
+                if (pos < P) {
+                    values[pos] = r.x;
+                    if (keys64) keys64[pos] = ((u64)(uint32_t)(ty * TX + tx) << 32) | (u64)r.w;
+                }
             }
+            cur = lane == l ? base + (uint32_t)__popcll(m) : cur;
         }
     }
-    flush();
 }
 
 // One wave per super-tile, lane = tile: running sum over the super-tile's
@@ -846,9 +825,9 @@ hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const
     e = scan(LoadPlain{tile_total}, StoreRanges{reinterpret_cast<uint2*>(ranges)}, ntiles, nullptr, partials, nullptr,
              s);
     if (e != hipSuccess) return e;
-    k_tile_place<<<max_pieces, 64, 0, s>>>(&counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur], rec, counts,
-                                           reinterpret_cast<const uint2*>(ranges), (uint32_t)P, values,
-                                           reinterpret_cast<u64*>(keys));
+    k_tile_place<<<(max_pieces + wpb - 1) / wpb, SB, 0, s>>>(&counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur], rec,
+                                                             counts, reinterpret_cast<const uint2*>(ranges),
+                                                             (uint32_t)P, values, reinterpret_cast<u64*>(keys));
     return hipGetLastError();
 }
 

@@ -16,7 +16,7 @@ constexpr float ALPHA_MAX = 0.99f;   // alpha = min(0.99, o G)
 constexpr float ALPHA_MIN = 1.0f / 255.0f;  // entries below are skipped
 constexpr float T_MIN = 1e-4f;       // a pixel stops before T would drop below
 constexpr float BIG = 16777216.0f;   // 2^24: beyond this fp32 no longer resolves pixels
-constexpr float NEG_HALF_LOG2E = -0.72134752044448170368f;  // -log2(e)/2: G = 2^(Q * this)
+constexpr float NEG_HALF_LOG2E = -0.72134752044448170368f;  // -log2(e)/2: exp(-Q/2) = 2^(Q * this)
 
 // Per-Gaussian values the backward's reverse blend sums over pixels (see
 // k_render_bwd): colour gradient (3), then with h = o G dL/dalpha per pixel,
@@ -61,19 +61,25 @@ __device__ __forceinline__ void divmod_small(int j, int w, int& q, int& r) {
     if (r >= w) { q += 1; r -= w; }
 }
 
-// Opacity-weighted Gaussian falloff at offset (dx, dy) from the mean with the
-// conic in factored form: Q = a (dx + beta dy)^2 + gamma dy^2, G = exp(-Q/2).
-// The forward and the backward call this same function so that both take the
-// same skip decisions bit for bit; contraction is fixed by hand.
-__device__ __forceinline__ void falloff(float dx, float dy, float a, float beta, float gamma, float o,
-                                        float& w, float& G, float& oG) {
+// Opacity-weighted Gaussian falloff o G at offset (dx, dy) from the mean, with
+// the conic in factored form Q = a (dx + beta dy)^2 + gamma dy^2 and the
+// per-record constants staged as a2 = -a log2(e)/2, g2 = -gamma log2(e)/2 and
+// lo = log2(o): o G = o exp(-Q/2) = 2^(a2 w^2 + g2 dy^2 + lo), w = dx + beta dy.
+// The forward and the backward call this same function on the same staged
+// constants so that both take the same skip decisions bit for bit;
+// contraction is fixed by hand.
+__device__ __forceinline__ void falloff(float dx, float dy, float a2, float beta, float g2, float lo, float& w,
+                                        float& oG) {
 #pragma clang fp contract(off)
     w = __fmaf_rn(beta, dy, dx);
-    float aw = a * w;
-    float gdy = gamma * dy;
-    float Q = __fmaf_rn(aw, w, gdy * dy);
-    G = __builtin_amdgcn_exp2f(Q * NEG_HALF_LOG2E);
-    oG = o * G;
+    const float aw = a2 * w;
+    const float gdy = g2 * dy;
+    oG = __builtin_amdgcn_exp2f(__fmaf_rn(aw, w, __fmaf_rn(gdy, dy, lo)));
+}
+
+// The staged constants of one record (conic_opacity = (a, beta, gamma, o)).
+__device__ __forceinline__ float4 falloff_consts(float4 c) {
+    return make_float4(c.x * NEG_HALF_LOG2E, c.y, c.z * NEG_HALF_LOG2E, __builtin_amdgcn_logf(c.w));
 }
 
 // ---------------------------------------------------------------- wave64 helpers

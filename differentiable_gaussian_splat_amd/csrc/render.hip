@@ -1,22 +1,23 @@
 // Per-tile alpha blending, forward and backward.
 //
-// Work layout (CDNA4, wave64): one 64-lane wave per 16x16 tile, each lane
-// owning the 4 pixels (px, py0 + 4k), k = 0..3, of one column of the tile.
-// The tile's depth-sorted Gaussian list is staged through LDS 64 records at a
-// time (each lane gathers one record); every lane then reads each record by
-// LDS broadcast. One wave per tile needs no barrier between waves, and 4
-// pixels per lane give four independent blends per LDS read.
+// Work layout (CDNA4, wave64): the 16x16 pixels of a tile are split into bands
+// of 16 columns x 4 PPL rows, one 64-lane wave per band, each lane owning the
+// PPL pixels (px, py0 + 4k), k < PPL, of one column of its band. A wave walks
+// its tile's depth-sorted list on its own: it stages the records through LDS
+// 64 at a time (each lane gathers one) and every lane reads each record by
+// LDS broadcast. A band stops as soon as its own pixels are done, so a deep
+// corner of a tile no longer holds the whole tile's pixels.
 //
 // Backward. The DISTWAR page ("DISTWAR: Fast Differentiable Rendering on
 // Raster-based Rendering Pipelines", abstract) and the ARC page ("ARC:
 // Warp-level Adaptive Atomic Reduction in GPUs to Accelerate Differentiable
 // Rendering", abstract) find this step bound by atomic updates that flood the
 // L2 atomic units, because all lanes of a warp update the same Gaussian. Here
-// each lane first sums its 4 pixels' terms in registers, the wave then sums
-// its 64 lanes with DPP (6 cross-lane adds per value, result in lane 63) --
-// only for entries where some lane contributed -- and the per-tile totals of a
-// 64-record batch are flushed with all lanes active: one fp32 atomic add per
-// value per (tile, Gaussian), 9 consecutive lanes per Gaussian record.
+// each lane first sums its pixels' terms in registers, each 16-lane row then
+// reduces them with DPP (a reduce-scatter: 8 values land in 8 lanes), the row
+// partials of a 64-record batch meet in LDS, and the batch is flushed with all
+// lanes active: one fp32 atomic add per value per (band, Gaussian), 9
+// consecutive lanes per Gaussian record.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -24,73 +25,100 @@ namespace gs {
 
 namespace {
 
-constexpr int PPL = 4;     // pixels per lane
 constexpr int BATCH = 64;  // records staged per LDS batch
 
+// Tiles differ in depth by up to ~6x the mean, and the deepest band's wave
+// alone takes most of the kernel's time while it shares its SIMD with light
+// ones. Waves with long walks get a higher issue priority on their SIMD
+// (s_setprio: arbitration among the SIMD's waves only), so they finish early
+// while the light bands fill the other SIMDs.
+__device__ __forceinline__ void set_walk_priority(uint32_t walk) {
+    if (walk >= 512u) __builtin_amdgcn_s_setprio(3);
+    else if (walk >= 256u) __builtin_amdgcn_s_setprio(2);
+    else if (walk >= 128u) __builtin_amdgcn_s_setprio(1);
+}
+
+// Stages record `lane` of a batch: (u, v, a2, beta), (g2, log2 o, r, g), b.
+__device__ __forceinline__ void stage_record(uint32_t g, const float2* __restrict__ means2d,
+                                             const float4* __restrict__ conic_op, const float* __restrict__ rgb,
+                                             float4* s_a, float4* s_b, float* s_c, int lane) {
+    const float2 m = means2d[g];
+    const float4 k = falloff_consts(conic_op[g]);
+    s_a[lane] = make_float4(m.x, m.y, k.x, k.y);
+    s_b[lane] = make_float4(k.z, k.w, rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1]);
+    s_c[lane] = rgb[3 * (size_t)g + 2];
+}
+
+// Forward. Per pixel: alpha = min(0.99, o G); entries with alpha < 1/255 are
+// skipped; an entry that would take T below 1e-4 is not blended and ends the
+// pixel; otherwise C += rgb alpha T and T -= alpha T. L is 1 while the pixel
+// walks and 0 once it has stopped (or lies outside the image): a stopped
+// pixel's effective alpha is 0, which changes nothing, and its T (>= 1e-4)
+// can never trigger the stop test again.
+template <int PPL>
 __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, const uint2* __restrict__ ranges,
                                                  const uint32_t* __restrict__ values,
                                                  const float2* __restrict__ means2d,
                                                  const float4* __restrict__ conic_op, const float* __restrict__ rgb,
                                                  float bg0, float bg1, float bg2, float* __restrict__ image,
                                                  float* __restrict__ final_T, uint32_t* __restrict__ n_contrib) {
-    __shared__ float4 s_a[BATCH];  // u, v, a, beta
-    __shared__ float4 s_b[BATCH];  // gamma, opacity, r, g
-    __shared__ float s_c[BATCH];   // b
-    const int tile = blockIdx.x;
+    constexpr int BANDS = 4 / PPL;
+    __shared__ float4 s_a[BATCH];
+    __shared__ float4 s_b[BATCH];
+    __shared__ float s_c[BATCH];
+    const int tile = blockIdx.x / BANDS, band = blockIdx.x - tile * BANDS;
     const int tx = tile % TX, ty = tile / TX;
     const int lane = threadIdx.x;
     const int px = tx * TILE + (lane & 15);
-    const int py0 = ty * TILE + (lane >> 4);
+    const int py0 = ty * TILE + band * 4 * PPL + (lane >> 4);
     const float pxc = (float)px + 0.5f;
-    float pyc[PPL], T[PPL], C0[PPL], C1[PPL], C2[PPL];
+    float pyc[PPL], T[PPL], C0[PPL], C1[PPL], C2[PPL], L[PPL];
     uint32_t last[PPL];
-    bool done[PPL];
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
-        int py = py0 + 4 * k;
+        const int py = py0 + 4 * k;
         pyc[k] = (float)py + 0.5f;
         T[k] = 1.f;
         C0[k] = C1[k] = C2[k] = 0.f;
         last[k] = 0u;
-        done[k] = !(px < W && py < H);
+        L[k] = (px < W && py < H) ? 1.f : 0.f;
     }
+    auto walking = [&]() {
+        float l = 0.f;
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) l += L[k];
+        return __any(l != 0.f);
+    };
     const uint2 rg = ranges[tile];
     for (uint32_t bs = rg.x; bs < rg.y; bs += BATCH) {
-        if (__all(done[0] && done[1] && done[2] && done[3])) break;
-        uint32_t idx = bs + lane;
-        if (idx < rg.y) {
-            uint32_t g = values[idx];
-            float2 m = means2d[g];
-            float4 c = conic_op[g];
-            s_a[lane] = make_float4(m.x, m.y, c.x, c.y);
-            s_b[lane] = make_float4(c.z, c.w, rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1]);
-            s_c[lane] = rgb[3 * (size_t)g + 2];
-        }
+        if (!walking()) break;
+        set_walk_priority(bs - rg.x);  // a wave still walking deep into its list is a heavy one
+        const uint32_t idx = bs + lane;
+        if (idx < rg.y) stage_record(values[idx], means2d, conic_op, rgb, s_a, s_b, s_c, lane);
         __syncthreads();
         const int cnt = (int)min((uint32_t)BATCH, rg.y - bs);
         const uint32_t pos0 = bs - rg.x + 1;
         for (int j = 0; j < cnt; ++j) {
-            if ((j & 7) == 7 && __all(done[0] && done[1] && done[2] && done[3])) break;
+            if ((j & 7) == 7 && !walking()) break;
             const float4 A = s_a[j];
             const float4 B = s_b[j];
             const float cb = s_c[j];
             const float dx = pxc - A.x;
 #pragma unroll
             for (int k = 0; k < PPL; ++k) {
-                float w, G, oG;
-                falloff(dx, pyc[k] - A.y, A.z, A.w, B.x, B.y, w, G, oG);
-                const float alpha = fminf(ALPHA_MAX, oG);
-                bool take = !done[k] && alpha >= ALPHA_MIN;
-                const float Tn = T[k] * (1.0f - alpha);
-                const bool stop = take && Tn < T_MIN;
-                take = take && !stop;
-                done[k] = done[k] || stop;
-                const float wt = take ? alpha * T[k] : 0.f;
+                float w, oG;
+                falloff(dx, pyc[k] - A.y, A.z, A.w, B.x, B.y, w, oG);
+                const float al = fminf(ALPHA_MAX, oG);
+                float ae = (al >= ALPHA_MIN ? al : 0.f) * L[k];
+                const bool stop = __fmaf_rn(-ae, T[k], T[k]) < T_MIN;
+                L[k] = stop ? 0.f : L[k];
+                ae = stop ? 0.f : ae;
+                const float wt = ae * T[k];
                 C0[k] = fmaf(B.z, wt, C0[k]);
                 C1[k] = fmaf(B.w, wt, C1[k]);
                 C2[k] = fmaf(cb, wt, C2[k]);
-                T[k] = take ? Tn : T[k];
-                last[k] = take ? pos0 + (uint32_t)j : last[k];
+                T[k] = __fmaf_rn(-ae, T[k], T[k]);
+                last[k] = ae > 0.f ? pos0 + (uint32_t)j : last[k];
             }
         }
         __syncthreads();
@@ -98,9 +126,9 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, const u
     const size_t HW = (size_t)W * H;
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
-        int py = py0 + 4 * k;
+        const int py = py0 + 4 * k;
         if (px < W && py < H) {
-            size_t p = (size_t)py * W + px;
+            const size_t p = (size_t)py * W + px;
             image[p] = fmaf(T[k], bg0, C0[k]);
             image[HW + p] = fmaf(T[k], bg1, C1[k]);
             image[2 * HW + p] = fmaf(T[k], bg2, C2[k]);
@@ -110,6 +138,11 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, const u
     }
 }
 
+// Backward: the forward's blended entries in reverse, per pixel. T is
+// restored entry by entry (T in front = T behind / (1 - alpha)); S = A . dL/dC
+// with A the colour behind the current entry (starting as the background), so
+// dL/dalpha = T (rgb . dL/dC - S).
+template <int PPL, int NB>
 __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const uint2* __restrict__ ranges,
                                                  const uint32_t* __restrict__ values,
                                                  const float2* __restrict__ means2d,
@@ -117,13 +150,14 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
                                                  float bg0, float bg1, float bg2, const float* __restrict__ final_T,
                                                  const uint32_t* __restrict__ n_contrib,
                                                  const float* __restrict__ dL_dimage, float* __restrict__ grad2d) {
-    __shared__ float4 s_a[BATCH];
-    __shared__ float4 s_b[BATCH];
-    __shared__ float s_c[BATCH];
-    __shared__ uint32_t s_g[BATCH];
-    __shared__ float s_part[BATCH * 4 * GRAD2D_N];  // [entry][row of 16 lanes][value]
-    __shared__ uint32_t s_has[BATCH];
-    const int tile = blockIdx.x;
+    constexpr int BANDS = 4 / PPL;
+    __shared__ float4 s_a[NB];
+    __shared__ float4 s_b[NB];
+    __shared__ float s_c[NB];
+    __shared__ uint32_t s_g[NB];
+    __shared__ float s_part[NB * 4 * GRAD2D_N];  // [entry][row of 16 lanes][value]
+    __shared__ uint32_t s_has[NB];
+    const int tile = blockIdx.x / BANDS, band = blockIdx.x - tile * BANDS;
     const int tx = tile % TX, ty = tile / TX;
     const int lane = threadIdx.x;
     // lane roles in the in-row reduce-scatter (see row_reduce_scatter8)
@@ -134,7 +168,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
     const bool writer = rl < 9;
     const int slot = rl < 8 ? (c1 ? 4 : 0) + (c2 ? 2 : 0) + (c3 ? 1 : 0) : 8;
     const int px = tx * TILE + (lane & 15);
-    const int py0 = ty * TILE + (lane >> 4);
+    const int py0 = ty * TILE + band * 4 * PPL + (lane >> 4);
     const float pxc = (float)px + 0.5f;
     const size_t HW = (size_t)W * H;
     float pyc[PPL], T[PPL], g0[PPL], g1[PPL], g2[PPL], S[PPL];
@@ -142,32 +176,28 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
     uint32_t mylast = 0;
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
-        int py = py0 + 4 * k;
+        const int py = py0 + 4 * k;
         pyc[k] = (float)py + 0.5f;
-        bool in = px < W && py < H;
-        size_t p = in ? (size_t)py * W + px : 0;
+        const bool in = px < W && py < H;
+        const size_t p = in ? (size_t)py * W + px : 0;
         T[k] = in ? final_T[p] : 1.f;
         last[k] = in ? n_contrib[p] : 0u;
         g0[k] = in ? dL_dimage[p] : 0.f;
         g1[k] = in ? dL_dimage[HW + p] : 0.f;
         g2[k] = in ? dL_dimage[2 * HW + p] : 0.f;
-        // S = A . dL/dC with A the normalised colour behind the current entry (starts as bg)
         S[k] = fmaf(bg0, g0[k], fmaf(bg1, g1[k], bg2 * g2[k]));
         mylast = max(mylast, last[k]);
     }
     const uint2 rg = ranges[tile];
     // never walk past the tile's list, whatever n_contrib holds
     const uint32_t maxlast = min(wave_max_u32(mylast), rg.y - rg.x);
-    for (int hi = (int)maxlast; hi > 0; hi -= BATCH) {
-        const int lo = max(0, hi - BATCH);
+    set_walk_priority(maxlast);
+    for (int hi = (int)maxlast; hi > 0; hi -= NB) {
+        const int lo = max(0, hi - NB);
         const int cnt = hi - lo;
         if (lane < cnt) {
-            uint32_t g = values[rg.x + lo + lane];
-            float2 m = means2d[g];
-            float4 c = conic_op[g];
-            s_a[lane] = make_float4(m.x, m.y, c.x, c.y);
-            s_b[lane] = make_float4(c.z, c.w, rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1]);
-            s_c[lane] = rgb[3 * (size_t)g + 2];
+            const uint32_t g = values[rg.x + lo + lane];
+            stage_record(g, means2d, conic_op, rgb, s_a, s_b, s_c, lane);
             s_g[lane] = g;
         }
         __syncthreads();
@@ -183,9 +213,8 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
             bool any = false;
 #pragma unroll
             for (int k = 0; k < PPL; ++k) {
-                float G;
                 dy[k] = pyc[k] - A.y;
-                falloff(dx, dy[k], A.z, A.w, B.x, B.y, w[k], G, oG[k]);
+                falloff(dx, dy[k], A.z, A.w, B.x, B.y, w[k], oG[k]);
                 al[k] = fminf(ALPHA_MAX, oG[k]);
                 blended[k] = pos < last[k] && al[k] >= ALPHA_MIN;
                 any = any || blended[k];
@@ -227,7 +256,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
             if (lane == 0) s_has[j] = 1u;
         }
         __syncthreads();
-        // one atomic add per value per (tile, Gaussian): the 4 row partials summed here
+        // one atomic add per value per (band, Gaussian): the 4 row partials summed here
         for (int v = lane; v < cnt * GRAD2D_N; v += 64) {
             const int e = v / GRAD2D_N;
             const int c = v - e * GRAD2D_N;
@@ -243,15 +272,22 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
 
 }  // namespace
 
+// Measured on the contention scene (1M Gaussians, 1920x1080): the forward is
+// fastest with one pixel per lane (four band waves per tile: a band stops on
+// its own), the backward with four (one wave per tile: each band would add its
+// own atomics) and 32-record batches (half the LDS, more resident waves).
+constexpr int FWD_PPL = 1;
+constexpr int BWD_PPL = 4;
+constexpr int BWD_BATCH = 32;
+
 hipError_t launch_render_fwd(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
                              const float* means2d, const float* conic_op, const float* rgb, const float* bg,
                              float* image, float* final_T, uint32_t* n_contrib, hipStream_t stream) {
-    int ntiles = TX * TY;
+    const int ntiles = TX * TY;
     if (ntiles == 0) return hipSuccess;
-    k_render_fwd<<<ntiles, 64, 0, stream>>>(W, H, TX, reinterpret_cast<const uint2*>(ranges), values,
-                                            reinterpret_cast<const float2*>(means2d),
-                                            reinterpret_cast<const float4*>(conic_op), rgb, bg[0], bg[1], bg[2],
-                                            image, final_T, n_contrib);
+    k_render_fwd<FWD_PPL><<<ntiles * (4 / FWD_PPL), 64, 0, stream>>>(
+        W, H, TX, reinterpret_cast<const uint2*>(ranges), values, reinterpret_cast<const float2*>(means2d),
+        reinterpret_cast<const float4*>(conic_op), rgb, bg[0], bg[1], bg[2], image, final_T, n_contrib);
     return hipGetLastError();
 }
 
@@ -259,12 +295,11 @@ hipError_t launch_render_bwd(int W, int H, int TX, int TY, const uint32_t* range
                              const float* means2d, const float* conic_op, const float* rgb, const float* bg,
                              const float* final_T, const uint32_t* n_contrib, const float* dL_dimage,
                              float* grad2d, hipStream_t stream) {
-    int ntiles = TX * TY;
+    const int ntiles = TX * TY;
     if (ntiles == 0) return hipSuccess;
-    k_render_bwd<<<ntiles, 64, 0, stream>>>(W, H, TX, reinterpret_cast<const uint2*>(ranges), values,
-                                            reinterpret_cast<const float2*>(means2d),
-                                            reinterpret_cast<const float4*>(conic_op), rgb, bg[0], bg[1], bg[2],
-                                            final_T, n_contrib, dL_dimage, grad2d);
+    k_render_bwd<BWD_PPL, BWD_BATCH><<<ntiles * (4 / BWD_PPL), 64, 0, stream>>>(
+        W, H, TX, reinterpret_cast<const uint2*>(ranges), values, reinterpret_cast<const float2*>(means2d),
+        reinterpret_cast<const float4*>(conic_op), rgb, bg[0], bg[1], bg[2], final_T, n_contrib, dL_dimage, grad2d);
     return hipGetLastError();
 }
 
