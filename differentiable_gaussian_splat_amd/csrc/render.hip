@@ -38,15 +38,40 @@ __device__ __forceinline__ void set_walk_priority(uint32_t walk) {
     else if (walk >= 128u) __builtin_amdgcn_s_setprio(1);
 }
 
+// True when no pixel centre of the band [x_lo, x_hi] x [y_lo, y_hi] can reach
+// alpha >= 1/255 for this record: with the conic's smaller eigenvalue lmin,
+// Q(d) >= lmin |d|^2 >= lmin dist(mean, band)^2, and alpha >= 1/255 needs
+// Q <= 2 ln(255 o). The margins (0.1% and 1e-3) lie far above fp32 rounding,
+// so a skipped record is one the per-pixel test would skip too: results are
+// unchanged, only the per-pixel work for such records is saved.
+__device__ __forceinline__ bool band_misses(float u, float v, float4 c, float lo, float x_lo, float x_hi, float y_lo,
+                                            float y_hi) {
+    const float a = c.x, beta = c.y, gamma = c.z;  // Q = a (dx + beta dy)^2 + gamma dy^2
+    const float m11 = a * beta * beta + gamma;
+    const float tr = a + m11, det = a * gamma;
+    const float h = 0.5f * tr;
+    const float lmax = h + sqrtf(fmaxf(h * h - det, 0.f));
+    const float lmin = det / lmax;
+    const float ddx = fmaxf(0.f, fmaxf(x_lo - u, u - x_hi));
+    const float ddy = fmaxf(0.f, fmaxf(y_lo - v, v - y_hi));
+    // 2 ln(255 o) = 2 ln 2 (log2 o + log2 255)
+    const float qthr = 1.3862943611198906f * (lo + 7.9943534368588578f);
+    return lmin * (ddx * ddx + ddy * ddy) * 0.999f > qthr + 1e-3f;
+}
+
 // Stages record `lane` of a batch: (u, v, a2, beta), (g2, log2 o, r, g), b.
-__device__ __forceinline__ void stage_record(uint32_t g, const float2* __restrict__ means2d,
+// Returns whether the record misses the band (see band_misses).
+__device__ __forceinline__ bool stage_record(uint32_t g, const float2* __restrict__ means2d,
                                              const float4* __restrict__ conic_op, const float* __restrict__ rgb,
-                                             float4* s_a, float4* s_b, float* s_c, int lane) {
+                                             float4* s_a, float4* s_b, float* s_c, int lane, float x_lo, float x_hi,
+                                             float y_lo, float y_hi) {
     const float2 m = means2d[g];
-    const float4 k = falloff_consts(conic_op[g]);
+    const float4 c = conic_op[g];
+    const float4 k = falloff_consts(c);
     s_a[lane] = make_float4(m.x, m.y, k.x, k.y);
     s_b[lane] = make_float4(k.z, k.w, rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1]);
     s_c[lane] = rgb[3 * (size_t)g + 2];
+    return band_misses(m.x, m.y, c, k.w, x_lo, x_hi, y_lo, y_hi);
 }
 
 // Forward. Per pixel: alpha = min(0.99, o G); entries with alpha < 1/255 are
@@ -83,6 +108,9 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, const u
         last[k] = 0u;
         L[k] = (px < W && py < H) ? 1.f : 0.f;
     }
+    // pixel-centre rectangle of the band
+    const float bx_lo = (float)(tx * TILE) + 0.5f, bx_hi = bx_lo + 15.f;
+    const float by_lo = (float)(ty * TILE + band * 4 * PPL) + 0.5f, by_hi = by_lo + (float)(4 * PPL - 1);
     auto walking = [&]() {
         float l = 0.f;
 #pragma unroll
@@ -94,12 +122,16 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, const u
         if (!walking()) break;
         set_walk_priority(bs - rg.x);  // a wave still walking deep into its list is a heavy one
         const uint32_t idx = bs + lane;
-        if (idx < rg.y) stage_record(values[idx], means2d, conic_op, rgb, s_a, s_b, s_c, lane);
+        bool miss = true;
+        if (idx < rg.y)
+            miss = stage_record(values[idx], means2d, conic_op, rgb, s_a, s_b, s_c, lane, bx_lo, bx_hi, by_lo, by_hi);
+        uint64_t todo = __ballot(!miss);  // records some pixel of the band may blend, in list order
         __syncthreads();
-        const int cnt = (int)min((uint32_t)BATCH, rg.y - bs);
         const uint32_t pos0 = bs - rg.x + 1;
-        for (int j = 0; j < cnt; ++j) {
-            if ((j & 7) == 7 && !walking()) break;
+        for (int n = 1; todo; ++n) {
+            const int j = __builtin_ctzll(todo);
+            todo &= todo - 1ull;
+            if ((n & 7) == 0 && !walking()) break;
             const float4 A = s_a[j];
             const float4 B = s_b[j];
             const float cb = s_c[j];
@@ -188,6 +220,8 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
         S[k] = fmaf(bg0, g0[k], fmaf(bg1, g1[k], bg2 * g2[k]));
         mylast = max(mylast, last[k]);
     }
+    const float bx_lo = (float)(tx * TILE) + 0.5f, bx_hi = bx_lo + 15.f;
+    const float by_lo = (float)(ty * TILE + band * 4 * PPL) + 0.5f, by_hi = by_lo + (float)(4 * PPL - 1);
     const uint2 rg = ranges[tile];
     // never walk past the tile's list, whatever n_contrib holds
     const uint32_t maxlast = min(wave_max_u32(mylast), rg.y - rg.x);
@@ -195,13 +229,18 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
     for (int hi = (int)maxlast; hi > 0; hi -= NB) {
         const int lo = max(0, hi - NB);
         const int cnt = hi - lo;
+        bool miss = true;
         if (lane < cnt) {
             const uint32_t g = values[rg.x + lo + lane];
-            stage_record(g, means2d, conic_op, rgb, s_a, s_b, s_c, lane);
+            miss = stage_record(g, means2d, conic_op, rgb, s_a, s_b, s_c, lane, bx_lo, bx_hi, by_lo, by_hi);
             s_g[lane] = g;
+            s_has[lane] = 0u;
         }
+        uint64_t todo = __ballot(!miss);  // records some pixel of the band may blend
         __syncthreads();
-        for (int j = cnt - 1; j >= 0; --j) {
+        while (todo) {
+            const int j = 63 - __builtin_clzll(todo);  // backwards through the list
+            todo &= ~(1ull << j);
             const float4 A = s_a[j];
             const float4 B = s_b[j];
             const float cb = s_c[j];
@@ -219,10 +258,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
                 blended[k] = pos < last[k] && al[k] >= ALPHA_MIN;
                 any = any || blended[k];
             }
-            if (!__any(any)) {
-                if (lane == 0) s_has[j] = 0u;
-                continue;
-            }
+            if (!__any(any)) continue;
             // branch-free: a pixel that did not blend this entry takes alpha = 0,
             // which leaves its T, S and every sum unchanged
             float acc[GRAD2D_N];
