@@ -275,8 +275,11 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
                 const float cdl = fmaf(B.z, g0[k], fmaf(B.w, g1[k], cb * g2[k]));
                 const float d = cdl - S[k];
                 S[k] = fmaf(av, d, S[k]);
-                // h = o G dL/dalpha = -2 dL/dQ; zero where alpha sat at its 0.99 clamp
-                const float h = (blended[k] && oG[k] <= ALPHA_MAX) ? oG[k] * (T[k] * d) : 0.f;
+                // h = o G dL/dalpha = -2 dL/dQ = alpha T d where alpha = o G; zero where alpha
+                // sat at its 0.99 clamp (and wherever the pixel did not blend: wt = 0). The
+                // moments stay in (w, dy), the conic's own axes: sums in (dx, dy) would
+                // cancel for elongated Gaussians.
+                const float h = oG[k] <= ALPHA_MAX ? wt * d : 0.f;
                 const float hw = h * w[k], hy = h * dy[k];
                 acc[3] += h;
                 acc[4] = fmaf(hw, w[k], acc[4]);
