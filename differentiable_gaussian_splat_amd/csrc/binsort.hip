@@ -575,12 +575,18 @@ __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int
     const int tx = (s % SX) * SUPER + (lane & 7), ty = (s / SX) * SUPER + (lane >> 3);
     const bool here = tx < TX && ty < TY;
     uint32_t cnt = 0;
+    // the next group's records are fetched while this group is tested
+    uint2 rn = make_uint2(0u, 0u);
+    if (e0 + lane < e1) {
+        const uint4 q = rec[sval[e0 + lane]];
+        rn = make_uint2(q.y, q.z);
+    }
     for (int eb = e0; eb < e1; eb += 64) {
         const int ne = min(64, e1 - eb);
-        uint2 r = make_uint2(0u, 0u);
-        if (lane < ne) {
-            const uint4 q = rec[sval[eb + lane]];
-            r = make_uint2(q.y, q.z);
+        const uint2 r = rn;
+        if (eb + 64 + lane < e1) {
+            const uint4 q = rec[sval[eb + 64 + lane]];
+            rn = make_uint2(q.y, q.z);
         }
         for (int u = 0; u < ne; ++u) {
             const uint32_t xr = __builtin_amdgcn_readlane(r.x, u);
@@ -615,11 +621,14 @@ __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int S, int
     const int mtx = sx0 + (lane & 7), mty = sy0 + (lane >> 3);
     uint32_t cur = (mtx < TX && mty < TY) ? ranges[mty * TX + mtx].x + offs[(size_t)pidx * 64 + lane] : 0u;
     const uint64_t lt_mask = lanemask_lt();
+    // the next group's records are fetched while this group is placed
+    uint4 rn = make_uint4(0u, 0u, 0u, 0u);
+    if (e0 + lane < e1) rn = rec[sval[e0 + lane]];
     for (int eb = e0; eb < e1; eb += 64) {
         const int ne = min(64, e1 - eb);
         const bool live = lane < ne;
-        uint4 r = make_uint4(0u, 0u, 0u, 0u);
-        if (live) r = rec[sval[eb + lane]];
+        const uint4 r = rn;
+        if (eb + 64 + lane < e1) rn = rec[sval[eb + 64 + lane]];
         const int X0 = (int)(r.y & 0xffffu), X1 = (int)(r.y >> 16);
         const int Y0 = (int)(r.z & 0xffffu), Y1 = (int)(r.z >> 16);
         for (int l = 0; l < 64; ++l) {

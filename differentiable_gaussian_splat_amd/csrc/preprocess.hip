@@ -152,6 +152,48 @@ __device__ __forceinline__ void stage_out(const float* src, float* __restrict__ 
         for (int e = lane; e < used; e += 64) dst[(size_t)(base + j) * rec + e] = src[j * stride + e];
 }
 
+// As stage_out, adding the LDS rows into the destination records.
+__device__ __forceinline__ void stage_out_add(const float* src, float* __restrict__ dst, int base, int n, int rec,
+                                              int used, int stride) {
+    const int lane = threadIdx.x;
+    const int cnt = min(64, n - base);
+    float* r0 = dst + (size_t)base * rec;
+    if (used == rec && rec <= 48 && ((uintptr_t)r0 & 15u) == 0) {
+        const int total = cnt * rec;
+        float4 v[STAGE_V4];
+#pragma unroll
+        for (int m = 0; m < STAGE_V4; ++m) {
+            const int f = (m * 64 + lane) * 4;
+            if (f + 3 < total) v[m] = *reinterpret_cast<const float4*>(r0 + f);
+        }
+#pragma unroll
+        for (int m = 0; m < STAGE_V4; ++m) {
+            const int f = (m * 64 + lane) * 4;
+            float e4[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int idx = f + c;
+                e4[c] = 0.f;
+                if (idx < total) {
+                    int j, e;
+                    divmod_small(idx, rec, j, e);
+                    e4[c] = src[j * stride + e];
+                }
+            }
+            if (f + 3 < total) {
+                *reinterpret_cast<float4*>(r0 + f) =
+                    make_float4(v[m].x + e4[0], v[m].y + e4[1], v[m].z + e4[2], v[m].w + e4[3]);
+            } else {
+                for (int c = 0; c < 4; ++c)
+                    if (f + c < total) r0[f + c] += e4[c];
+            }
+        }
+        return;
+    }
+    for (int j = 0; j < cnt; ++j)
+        for (int e = lane; e < used; e += 64) dst[(size_t)(base + j) * rec + e] += src[j * stride + e];
+}
+
 __global__ __launch_bounds__(64) void k_preprocess(
     DevCam cam, int K, int sh_rows, float lowpass, float near_plane, int n,
     const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
@@ -253,17 +295,22 @@ __global__ __launch_bounds__(64) void k_preprocess(
     }
 }
 
-// The chain rule for Gaussian gi; shg and dshg are its SH row and SH-gradient
-// row (in LDS). Culled Gaussians are left untouched.
+// The chain rule for Gaussian gi. shg is its SH row in LDS: the coefficients
+// on entry, replaced coefficient by coefficient by their gradient
+// contributions (zero for a culled Gaussian), which the caller adds to dL/dsh.
+// The other outputs of culled Gaussians are left untouched.
 __device__ __forceinline__ void chain_rule(
     const DevCam& cam, int K, float near_plane, int gi,
     const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
-    const float* shg, const float4* __restrict__ conic_op, const int* __restrict__ radii,
+    float* shg, const float4* __restrict__ conic_op, const int* __restrict__ radii,
     const uint8_t* __restrict__ clamped, const float* __restrict__ grad2d,
     float* __restrict__ d_means, float* __restrict__ d_scales, float* __restrict__ d_quats,
-    float* __restrict__ d_opac, float* dshg, float* __restrict__ d_means2d) {
+    float* __restrict__ d_opac, float* __restrict__ d_means2d) {
     size_t g = (size_t)gi;
-    if (radii[g] <= 0) return;
+    auto culled = [&]() {
+        for (int k = 0; k < 3 * K; ++k) shg[k] = 0.f;
+    };
+    if (radii[g] <= 0) return culled();
     const float4* g2 = reinterpret_cast<const float4*>(grad2d + g * GRAD2D_STRIDE);
     float4 ga = g2[0], gb = g2[1], gc = g2[2];
     float dr[3] = {ga.x, ga.y, ga.z};
@@ -282,7 +329,7 @@ __device__ __forceinline__ void chain_rule(
     float mx = means[3 * g], my = means[3 * g + 1], mz = means[3 * g + 2];
     float s[3] = {scales[3 * g], scales[3 * g + 1], scales[3 * g + 2]};
     Geo geo;
-    if (!geometry(cam, near_plane, mx, my, mz, s[0], s[1], s[2], quats[g], geo)) return;
+    if (!geometry(cam, near_plane, mx, my, mz, s[0], s[1], s[2], quats[g], geo)) return culled();
 
     // (a, beta, gamma) -> Sigma' = [[A, B], [B, C]] with a = C/det, beta = -B/C, gamma = 1/C
     float a2 = a * a;
@@ -347,10 +394,11 @@ __device__ __forceinline__ void chain_rule(
     float Y[16], wk[16];
     sh_eval(K, dxn, dyn, dzn, Y);
     for (int k = 0; k < K; ++k) {
-        dshg[3 * k] += Y[k] * dcol[0];
-        dshg[3 * k + 1] += Y[k] * dcol[1];
-        dshg[3 * k + 2] += Y[k] * dcol[2];
-        wk[k] = fmaf(shg[3 * k], dcol[0], fmaf(shg[3 * k + 1], dcol[1], shg[3 * k + 2] * dcol[2]));
+        const float s0 = shg[3 * k], s1 = shg[3 * k + 1], s2 = shg[3 * k + 2];
+        wk[k] = fmaf(s0, dcol[0], fmaf(s1, dcol[1], s2 * dcol[2]));
+        shg[3 * k] = Y[k] * dcol[0];
+        shg[3 * k + 1] = Y[k] * dcol[1];
+        shg[3 * k + 2] = Y[k] * dcol[2];
     }
     float3 gdir = make_float3(0.f, 0.f, 0.f);
     sh_grad_accum(K, dxn, dyn, dzn, wk, gdir);
@@ -389,20 +437,17 @@ __global__ __launch_bounds__(64) void k_preprocess_bwd(
     const uint8_t* __restrict__ clamped, const float* __restrict__ grad2d,
     float* __restrict__ d_means, float* __restrict__ d_scales, float* __restrict__ d_quats,
     float* __restrict__ d_opac, float* __restrict__ d_sh, float* __restrict__ d_means2d) {
-    extern __shared__ float smem[];
+    extern __shared__ float s_sh[];
     const int stride = (3 * K) | 1;
-    float* s_sh = smem;
-    float* s_dsh = smem + 64 * stride;
     const int base = blockIdx.x * 64;
     stage_in(sh, s_sh, base, n, 3 * sh_rows, 3 * K, stride);
-    stage_in(d_sh, s_dsh, base, n, 3 * sh_rows, 3 * K, stride);
     __syncthreads();
     const int gi = base + threadIdx.x;
     if (gi < n)
         chain_rule(cam, K, near_plane, gi, means, scales, quats, s_sh + threadIdx.x * stride, conic_op, radii,
-                   clamped, grad2d, d_means, d_scales, d_quats, d_opac, s_dsh + threadIdx.x * stride, d_means2d);
+                   clamped, grad2d, d_means, d_scales, d_quats, d_opac, d_means2d);
     __syncthreads();
-    stage_out(s_dsh, d_sh, base, n, 3 * sh_rows, 3 * K, stride);
+    stage_out_add(s_sh, d_sh, base, n, 3 * sh_rows, 3 * K, stride);
     (void)lowpass;
 }
 
@@ -429,7 +474,7 @@ hipError_t launch_preprocess_bwd(const DevCam& cam, int K, int sh_rows, float lo
                                  float* d_opac, float* d_sh, float* d_means2d, hipStream_t stream) {
     if (n == 0) return hipSuccess;
     int blocks = (n + 63) / 64;
-    size_t lds = 2 * sizeof(float) * 64 * ((3 * K) | 1);
+    size_t lds = sizeof(float) * 64 * ((3 * K) | 1);
     k_preprocess_bwd<<<blocks, 64, lds, stream>>>(cam, K, sh_rows, lowpass, near_plane, n, means, scales,
                                                  reinterpret_cast<const float4*>(quats), sh,
                                                  reinterpret_cast<const float4*>(conic_op), radii, clamped,
