@@ -61,20 +61,22 @@ __device__ __forceinline__ void divmod_small(int j, int w, int& q, int& r) {
     if (r >= w) { q += 1; r -= w; }
 }
 
-// Opacity-weighted Gaussian falloff o G at offset (dx, dy) from the mean, with
-// the conic in factored form Q = a (dx + beta dy)^2 + gamma dy^2 and the
-// per-record constants staged as a2 = -a log2(e)/2, g2 = -gamma log2(e)/2 and
-// lo = log2(o): o G = o exp(-Q/2) = 2^(a2 w^2 + g2 dy^2 + lo), w = dx + beta dy.
-// The forward and the backward call this same function on the same staged
-// constants so that both take the same skip decisions bit for bit;
-// contraction is fixed by hand.
-__device__ __forceinline__ void falloff(float dx, float dy, float a2, float beta, float g2, float lo, float& w,
-                                        float& oG) {
+// Opacity-weighted Gaussian falloff o G at a pixel, with the conic in
+// factored form Q = a w^2 + gamma dy^2, w = dx + beta dy, (dx, dy) = pixel
+// centre - screen mean, and the per-record constants staged as
+// a2 = -a log2(e)/2, g2 = -gamma log2(e)/2 and lo = log2(o):
+// o G = o exp(-Q/2) = 2^(a2 w^2 + g2 dy^2 + lo). The caller forms w and dy from
+// their values at the tile's first pixel (staged per record with extra
+// precision) plus the pixel's small offset in the tile: a Gaussian whose mean
+// lies thousands of pixels away would otherwise lose w to cancellation
+// between dx and beta dy. The forward and the backward call this same function
+// on the same staged values so that both take the same skip decisions bit for
+// bit; contraction is fixed by hand.
+__device__ __forceinline__ float falloff(float w, float dy, float a2, float g2, float lo) {
 #pragma clang fp contract(off)
-    w = __fmaf_rn(beta, dy, dx);
     const float aw = a2 * w;
     const float gdy = g2 * dy;
-    oG = __builtin_amdgcn_exp2f(__fmaf_rn(aw, w, __fmaf_rn(gdy, dy, lo)));
+    return __builtin_amdgcn_exp2f(__fmaf_rn(aw, w, __fmaf_rn(gdy, dy, lo)));
 }
 
 // The staged constants of one record (conic_opacity = (a, beta, gamma, o)).

@@ -60,15 +60,20 @@ __device__ __forceinline__ bool band_misses(float u, float v, float4 c, float lo
 }
 
 // Stages record `lane` of a batch: (u, v, a2, beta), (g2, log2 o, r, g), b.
-// Returns whether the record misses the band (see band_misses).
+// Stages record `lane` of a batch: (w0, dy0, a2, beta), (g2, log2 o, r, g), b,
+// where w0 and dy0 are w and dy at the tile's first pixel centre (ox, oy),
+// formed in double and rounded once. Returns whether the record misses the
+// band (see band_misses).
 __device__ __forceinline__ bool stage_record(uint32_t g, const float2* __restrict__ means2d,
                                              const float4* __restrict__ conic_op, const float* __restrict__ rgb,
-                                             float4* s_a, float4* s_b, float* s_c, int lane, float x_lo, float x_hi,
-                                             float y_lo, float y_hi) {
+                                             float4* s_a, float4* s_b, float* s_c, int lane, double ox, double oy,
+                                             float x_lo, float x_hi, float y_lo, float y_hi) {
     const float2 m = means2d[g];
     const float4 c = conic_op[g];
     const float4 k = falloff_consts(c);
-    s_a[lane] = make_float4(m.x, m.y, k.x, k.y);
+    const double ddy = oy - (double)m.y;
+    const double w0 = (ox - (double)m.x) + (double)c.y * ddy;
+    s_a[lane] = make_float4((float)w0, (float)ddy, k.x, k.y);
     s_b[lane] = make_float4(k.z, k.w, rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1]);
     s_c[lane] = rgb[3 * (size_t)g + 2];
     return band_misses(m.x, m.y, c, k.w, x_lo, x_hi, y_lo, y_hi);
@@ -96,13 +101,14 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, const u
     const int lane = threadIdx.x;
     const int px = tx * TILE + (lane & 15);
     const int py0 = ty * TILE + band * 4 * PPL + (lane >> 4);
-    const float pxc = (float)px + 0.5f;
-    float pyc[PPL], T[PPL], C0[PPL], C1[PPL], C2[PPL], L[PPL];
+    const double ox = (double)(tx * TILE) + 0.5, oy = (double)(ty * TILE) + 0.5;  // the tile's first pixel centre
+    const float lx = (float)(lane & 15);                                         // this lane's offset from it
+    float ly[PPL], T[PPL], C0[PPL], C1[PPL], C2[PPL], L[PPL];
     uint32_t last[PPL];
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
         const int py = py0 + 4 * k;
-        pyc[k] = (float)py + 0.5f;
+        ly[k] = (float)(py - ty * TILE);
         T[k] = 1.f;
         C0[k] = C1[k] = C2[k] = 0.f;
         last[k] = 0u;
@@ -124,7 +130,8 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, const u
         const uint32_t idx = bs + lane;
         bool miss = true;
         if (idx < rg.y)
-            miss = stage_record(values[idx], means2d, conic_op, rgb, s_a, s_b, s_c, lane, bx_lo, bx_hi, by_lo, by_hi);
+            miss = stage_record(values[idx], means2d, conic_op, rgb, s_a, s_b, s_c, lane, ox, oy, bx_lo, bx_hi, by_lo,
+                                by_hi);
         uint64_t todo = __ballot(!miss);  // records some pixel of the band may blend, in list order
         __syncthreads();
         const uint32_t pos0 = bs - rg.x + 1;
@@ -135,11 +142,10 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, const u
             const float4 A = s_a[j];
             const float4 B = s_b[j];
             const float cb = s_c[j];
-            const float dx = pxc - A.x;
+            const float wl = A.x + lx;  // w at this lane's column, tile's first row
 #pragma unroll
             for (int k = 0; k < PPL; ++k) {
-                float w, oG;
-                falloff(dx, pyc[k] - A.y, A.z, A.w, B.x, B.y, w, oG);
+                const float oG = falloff(__fmaf_rn(A.w, ly[k], wl), A.y + ly[k], A.z, B.x, B.y);
                 const float al = fminf(ALPHA_MAX, oG);
                 float ae = (al >= ALPHA_MIN ? al : 0.f) * L[k];
                 const bool stop = __fmaf_rn(-ae, T[k], T[k]) < T_MIN;
@@ -201,15 +207,16 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
     const int slot = rl < 8 ? (c1 ? 4 : 0) + (c2 ? 2 : 0) + (c3 ? 1 : 0) : 8;
     const int px = tx * TILE + (lane & 15);
     const int py0 = ty * TILE + band * 4 * PPL + (lane >> 4);
-    const float pxc = (float)px + 0.5f;
+    const double ox = (double)(tx * TILE) + 0.5, oy = (double)(ty * TILE) + 0.5;  // the tile's first pixel centre
+    const float lx = (float)(lane & 15);                                         // this lane's offset from it
     const size_t HW = (size_t)W * H;
-    float pyc[PPL], T[PPL], g0[PPL], g1[PPL], g2[PPL], S[PPL];
+    float ly[PPL], T[PPL], g0[PPL], g1[PPL], g2[PPL], S[PPL];
     uint32_t last[PPL];
     uint32_t mylast = 0;
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
         const int py = py0 + 4 * k;
-        pyc[k] = (float)py + 0.5f;
+        ly[k] = (float)(py - ty * TILE);
         const bool in = px < W && py < H;
         const size_t p = in ? (size_t)py * W + px : 0;
         T[k] = in ? final_T[p] : 1.f;
@@ -232,7 +239,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
         bool miss = true;
         if (lane < cnt) {
             const uint32_t g = values[rg.x + lo + lane];
-            miss = stage_record(g, means2d, conic_op, rgb, s_a, s_b, s_c, lane, bx_lo, bx_hi, by_lo, by_hi);
+            miss = stage_record(g, means2d, conic_op, rgb, s_a, s_b, s_c, lane, ox, oy, bx_lo, bx_hi, by_lo, by_hi);
             s_g[lane] = g;
             s_has[lane] = 0u;
         }
@@ -245,15 +252,16 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
             const float4 B = s_b[j];
             const float cb = s_c[j];
             const uint32_t pos = (uint32_t)(lo + j);
-            const float dx = pxc - A.x;
+            const float wl = A.x + lx;  // w at this lane's column, tile's first row
             // which of this lane's pixels blended this entry (same test as the forward)
             float w[PPL], dy[PPL], oG[PPL], al[PPL];
             bool blended[PPL];
             bool any = false;
 #pragma unroll
             for (int k = 0; k < PPL; ++k) {
-                dy[k] = pyc[k] - A.y;
-                falloff(dx, dy[k], A.z, A.w, B.x, B.y, w[k], oG[k]);
+                dy[k] = A.y + ly[k];
+                w[k] = __fmaf_rn(A.w, ly[k], wl);
+                oG[k] = falloff(w[k], dy[k], A.z, B.x, B.y);
                 al[k] = fminf(ALPHA_MAX, oG[k]);
                 blended[k] = pos < last[k] && al[k] >= ALPHA_MIN;
                 any = any || blended[k];

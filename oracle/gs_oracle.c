@@ -664,6 +664,30 @@ int64_t orc_match_fwd(int W, int H, const uint32_t *ranges, const uint32_t *valu
     return bad;
 }
 
+/* orc_match_fwd restricted to the pixels pix[npix] (flat py*W+px); the
+ * GPU values come per sampled pixel: gpu_rgbT[npix][4] = (r, g, b, T). */
+int64_t orc_match_fwd_pixels(int W, int H, const uint32_t *ranges, const uint32_t *values,
+                             const double *means2d, const double *conic, const double *opac, const double *rgb,
+                             const double *bg, int64_t npix, const int64_t *pix, const float *gpu_rgbT,
+                             const uint32_t *gpu_nc, double d_alpha, int max_amb, double tol, int8_t *status)
+{
+    raster_in in = {W, H, (W + TILE - 1) / TILE, ranges, values, means2d, conic, opac, rgb, {bg[0], bg[1], bg[2]}};
+    int64_t bad = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(+ : bad)
+    for (int64_t k = 0; k < npix; ++k) {
+        int px = (int)(pix[k] % W), py = (int)(pix[k] / W);
+        int t = (py / TILE) * in.TX + px / TILE;
+        explorer x = {&in, ranges[2 * t], ranges[2 * t + 1], px + 0.5, py + 0.5, d_alpha, max_amb,
+                      &gpu_rgbT[4 * k], gpu_nc[k], tol, 0, 0};
+        double C[3] = {0, 0, 0};
+        explore(&x, x.s, 1.0, C, 0, 0, 0.0, 1);
+        int st = x.found == 1 ? 0 : x.found == 2 ? 1 : x.overflow ? 2 : 3;
+        status[k] = (int8_t)st;
+        if (st == 3) ++bad;
+    }
+    return bad;
+}
+
 /* ------------------------------------------------------------------ */
 /* O13: backward per pixel                                              */
 /* grad2d[N,9] = (drgb[3], dopacity, da, db, dc, du, dv), accumulated.   */

@@ -55,6 +55,8 @@ def lib():
             L.orc_render_fwd_pixels.restype = None
             L.orc_match_fwd.argtypes = [i32, i32] + [P] * 10 + [f64, i32, f64, P]
             L.orc_match_fwd.restype = i64
+            L.orc_match_fwd_pixels.argtypes = [i32, i32] + [P] * 7 + [i64, P, P, P] + [f64, i32, f64, P]
+            L.orc_match_fwd_pixels.restype = i64
             L.orc_render_bwd.argtypes = [i32, i32, i64] + [P] * 9
             L.orc_render_bwd.restype = None
             L.orc_render_bwd_pixels.argtypes = [i32, i32, i64] + [P] * 8 + [i64, P, P]
@@ -183,6 +185,25 @@ def match_fwd(W, H, ranges, values, means2d, conic, opac, rgb, gpu_image, gpu_T,
                         _p(np.ascontiguousarray(gpu_T, np.float32)),
                         _p(np.ascontiguousarray(gpu_nc, np.uint32)), float(d_alpha), int(max_amb),
                         float(tol), _p(status))
+    return status
+
+
+def match_fwd_pixels(W, H, ranges, values, means2d, conic, opac, rgb, pix, gpu_image, gpu_T, gpu_nc,
+                     bg=(0.0, 0.0, 0.0), d_alpha=4e-6, max_amb=4, tol=1e-5):
+    """:func:`match_fwd` at the sampled pixels ``pix`` (flat py*W+px); the GPU
+    image/final_T/n_contrib are the full-frame arrays."""
+    pix = np.ascontiguousarray(pix, np.int64)
+    n = pix.shape[0]
+    HW = W * H
+    img = np.asarray(gpu_image, np.float32).reshape(3, HW)
+    rgbT = np.ascontiguousarray(np.stack([img[0, pix], img[1, pix], img[2, pix],
+                                          np.asarray(gpu_T, np.float32).reshape(HW)[pix]], axis=1), np.float32)
+    nc = np.ascontiguousarray(np.asarray(gpu_nc).reshape(HW)[pix], np.uint32)
+    status = np.zeros(n, np.int8)
+    values = np.ascontiguousarray(values, np.uint32) if len(values) else np.zeros(1, np.uint32)
+    lib().orc_match_fwd_pixels(W, H, _p(np.ascontiguousarray(ranges, np.uint32)), _p(values), _p(_d(means2d)),
+                               _p(_d(conic)), _p(_d(opac)), _p(_d(rgb)), _p(_d(bg)), n, _p(pix), _p(rgbT), _p(nc),
+                               float(d_alpha), int(max_amb), float(tol), _p(status))
     return status
 
 

@@ -75,3 +75,55 @@ def rel_l2(a, b):
     if nb == 0:
         return float(np.linalg.norm(a))
     return float(np.linalg.norm(a - b) / nb)
+
+
+def check_preprocess(sc, v, g, idx=None):
+    """Projection of view v: GPU stage outputs ``g`` (frame_np) against the
+    oracle, for all Gaussians or the subset ``idx``: continuous outputs within
+    1e-5 relative, integer outputs exact except where the oracle flags its
+    value within 1e-5 of a cut (and rare)."""
+    cam = sc.cameras[v]
+    if idx is None:
+        idx = np.arange(sc.n)
+    o = O.preprocess(sc.means[idx], sc.scales[idx], sc.quats[idx], sc.opacities[idx], sc.sh[idx], cam,
+                     sc.sh_degree)
+    g = {k: (val[idx] if isinstance(val, np.ndarray) and val.shape[:1] == (sc.n,) else val) for k, val in g.items()}
+    amb = o["margin"] < 1e-5
+    vis_g, vis_o = g["radii"] > 0, o["radii"] > 0
+    assert np.all((vis_g == vis_o) | amb)
+    assert vis_o.sum() > 0
+    same = vis_g & vis_o
+    assert np.all((g["radii"] == o["radii"])[same & ~amb])
+    assert np.all((g["tiles"] == o["tiles"])[same & ~amb])
+    # integer disagreements only ever at flagged Gaussians, and rare
+    n_int = (((g["radii"] != o["radii"]) | (g["tiles"] != o["tiles"])) & (vis_g | vis_o)).sum()
+    assert n_int <= max(2, 1e-3 * vis_o.sum()), n_int
+    sc_uv = np.abs(g["means2d"] - np.array([cam.cx, cam.cy])) + np.array([cam.cx, cam.cy]) + 1.0
+    np.testing.assert_array_less(np.abs(g["means2d"] - o["means2d"])[same], 1e-5 * sc_uv[same])
+    np.testing.assert_array_less(np.abs(g["depth32"] - o["depth"])[same], 1e-5 * o["depth"][same])
+    np.testing.assert_array_less(np.abs(g["rgb"] - o["rgb"])[same], 1e-5 * (1 + np.abs(o["rgb"][same])))
+    # conic in factored form against the oracle's 2D covariance (a = C/det, beta = -B/C, gamma = 1/C)
+    A, B, Cc = o["cov2d"][same].T
+    det = A * Cc - B * B
+    a_o, be_o, ga_o = Cc / det, -B / Cc, 1.0 / Cc
+    kappa = A * Cc / det  # conditioning of det(Sigma')
+    # conditioning of C itself: C sums the squares of the second projected row
+    # V1 R_q diag(s), |V1|^2 = (fy/z)^2 (1 + (y/z)^2); when that row is nearly
+    # orthogonal to the Gaussian's long axes, C is small beside |V1|^2 |s|^2
+    R = np.asarray(cam.R, np.float64)
+    xc = sc.means[idx].astype(np.float64) @ R.T + np.asarray(cam.t, np.float64)
+    zc, yc = xc[:, 2], xc[:, 1]
+    v1sq = (cam.fy / zc) ** 2 * (1.0 + (yc / zc) ** 2)
+    ssq = (sc.scales[idx].astype(np.float64) ** 2).sum(1)
+    kC = (v1sq * ssq)[same] / Cc
+    ldl = g["ldl"][same].astype(np.float64)
+    err_a = np.abs(ldl[:, 0] - a_o) / a_o
+    err_g = np.abs(ldl[:, 2] - ga_o) / ga_o
+    err_b = np.abs(ldl[:, 1] - be_o) / np.sqrt(A / Cc)
+    tol = 2e-6 * (1 + kappa + kC)
+    tol_g = np.maximum(1e-5, 2e-6 * kC)
+    worst = int(np.argmax(np.maximum(err_a / tol, np.maximum(err_g / tol_g, err_b / tol))))
+    assert np.all(err_a <= tol) and np.all(err_g <= tol_g) and np.all(err_b <= tol), \
+        (err_a.max(), err_g.max(), err_b.max(), "worst", err_a[worst], err_g[worst], err_b[worst], kappa[worst],
+         kC[worst])
+    np.testing.assert_array_equal(g["clamped"][same], (o["clamp"][same] * [1, 2, 4]).sum(1))

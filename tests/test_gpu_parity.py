@@ -16,7 +16,8 @@ import torch
 from differentiable_gaussian_splat_amd import raster
 from differentiable_gaussian_splat_amd.scenes import Camera, make_scene, subset
 from oracle import oracle as O
-from tests.gpu_helpers import (frame_np, gpu_backward, gpu_frame, params_dev, params_np, rel_l2, to_dev)
+from tests.gpu_helpers import (check_preprocess, frame_np, gpu_backward, gpu_frame, params_dev, params_np,
+                               rel_l2, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,36 +40,7 @@ def test_preprocess_parity(c, s, n):
     sc = scene(c, s, n)
     v = _view(sc)
     r, pd, fr = gpu_frame(sc, v)
-    g = frame_np(fr)
-    o = O.preprocess(sc.means, sc.scales, sc.quats, sc.opacities, sc.sh, sc.cameras[v], sc.sh_degree)
-    amb = o["margin"] < 1e-5
-    vis_g, vis_o = g["radii"] > 0, o["radii"] > 0
-    assert np.all((vis_g == vis_o) | amb)
-    assert vis_o.sum() > 0
-    same = vis_g & vis_o
-    assert np.all((g["radii"] == o["radii"])[same & ~amb])
-    assert np.all((g["tiles"] == o["tiles"])[same & ~amb])
-    # integer disagreements only ever at flagged Gaussians, and rare
-    n_int = (((g["radii"] != o["radii"]) | (g["tiles"] != o["tiles"])) & (vis_g | vis_o)).sum()
-    assert n_int <= max(2, 1e-3 * vis_o.sum()), n_int
-    cam = sc.cameras[v]
-    sc_uv = np.abs(g["means2d"] - np.array([cam.cx, cam.cy])) + np.array([cam.cx, cam.cy]) + 1.0
-    np.testing.assert_array_less(np.abs(g["means2d"] - o["means2d"])[same], 1e-5 * sc_uv[same])
-    np.testing.assert_array_less(np.abs(g["depth32"] - o["depth"])[same], 1e-5 * o["depth"][same])
-    np.testing.assert_array_less(np.abs(g["rgb"] - o["rgb"])[same], 1e-5 * (1 + np.abs(o["rgb"][same])))
-    # conic in factored form against the oracle's 2D covariance (a = C/det, beta = -B/C, gamma = 1/C)
-    A, B, Cc = o["cov2d"][same].T
-    det = A * Cc - B * B
-    a_o, be_o, ga_o = Cc / det, -B / Cc, 1.0 / Cc
-    kappa = A * Cc / det  # conditioning of det(Sigma')
-    ldl = g["ldl"][same].astype(np.float64)
-    err_a = np.abs(ldl[:, 0] - a_o) / a_o
-    err_g = np.abs(ldl[:, 2] - ga_o) / ga_o
-    err_b = np.abs(ldl[:, 1] - be_o) / np.sqrt(A / Cc)
-    tol = 2e-6 * (1 + kappa)
-    assert np.all(err_a <= tol) and np.all(err_g <= 1e-5) and np.all(err_b <= tol), \
-        (err_a.max(), err_g.max(), err_b.max())
-    np.testing.assert_array_equal(g["clamped"][same], (o["clamp"][same] * [1, 2, 4]).sum(1))
+    check_preprocess(sc, v, frame_np(fr))
 
 
 @pytest.mark.parametrize("c,s,n", CASES, ids=IDS)

@@ -450,6 +450,12 @@ def test_matcher_accepts_exact_and_flags_planted_error():
                      sc.opacities, pre["rgb"], img_bad, T32, nc_bad)
     assert st[60, 70] == 3 and st[10, 10] == 3
     assert np.count_nonzero(st == 3) == 2
+    # the sampled-pixel matcher gives the full matcher's status at every sampled pixel
+    pix = np.concatenate([np.random.default_rng(5).choice(cam.width * cam.height, 300, replace=False),
+                          [60 * cam.width + 70, 10 * cam.width + 10]])
+    sp = O.match_fwd_pixels(cam.width, cam.height, f["ranges"], f["values"], pre["means2d"], pre["conic"],
+                            sc.opacities, pre["rgb"], pix, img_bad, T32, nc_bad)
+    np.testing.assert_array_equal(sp, st.reshape(-1)[pix])
 
 
 def test_matcher_accepts_other_branch_of_a_boundary_skip():
