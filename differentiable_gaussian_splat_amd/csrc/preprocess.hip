@@ -194,6 +194,42 @@ __device__ __forceinline__ void stage_out_add(const float* src, float* __restric
         for (int e = lane; e < used; e += 64) dst[(size_t)(base + j) * rec + e] += src[j * stride + e];
 }
 
+// Blocks with few visible Gaussians (a camera that sees a fifth of the scene)
+// move only the visible lanes' rows, each lane its own; dense blocks stage all
+// 64 rows with coalesced accesses.
+constexpr int SH_DENSE = 16;
+
+__device__ __forceinline__ void copy_own_row(const float* __restrict__ src, float* row, size_t g, int rec, int used) {
+    const float* r = src + g * (size_t)rec;
+    if ((used & 3) == 0 && ((uintptr_t)r & 15u) == 0) {
+        for (int e = 0; e < used; e += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(r + e);
+            row[e] = v.x;
+            row[e + 1] = v.y;
+            row[e + 2] = v.z;
+            row[e + 3] = v.w;
+        }
+    } else {
+        for (int e = 0; e < used; ++e) row[e] = r[e];
+    }
+}
+
+__device__ __forceinline__ void add_own_row(const float* row, float* __restrict__ dst, size_t g, int rec, int used) {
+    float* r = dst + g * (size_t)rec;
+    if ((used & 3) == 0 && ((uintptr_t)r & 15u) == 0) {
+        for (int e = 0; e < used; e += 4) {
+            float4 v = *reinterpret_cast<const float4*>(r + e);
+            v.x += row[e];
+            v.y += row[e + 1];
+            v.z += row[e + 2];
+            v.w += row[e + 3];
+            *reinterpret_cast<float4*>(r + e) = v;
+        }
+    } else {
+        for (int e = 0; e < used; ++e) r[e] += row[e];
+    }
+}
+
 __global__ __launch_bounds__(64) void k_preprocess(
     DevCam cam, int K, int sh_rows, float lowpass, float near_plane, int n,
     const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
@@ -204,17 +240,15 @@ __global__ __launch_bounds__(64) void k_preprocess(
     extern __shared__ float s_sh[];
     const int stride = (3 * K) | 1;  // odd row stride: lanes reading their own row hit distinct banks
     const int base = blockIdx.x * 64;
-    stage_in(sh, s_sh, base, n, 3 * sh_rows, 3 * K, stride);
-    __syncthreads();
-    int gi = base + threadIdx.x;
-    if (gi >= n) return;
-    size_t g = (size_t)gi;
+    const int gi = base + threadIdx.x;
+    const bool live = gi < n;
+    const size_t g = live ? (size_t)gi : (size_t)base;
     float mx = means[3 * g], my = means[3 * g + 1], mz = means[3 * g + 2];
     float s0 = scales[3 * g], s1 = scales[3 * g + 1], s2 = scales[3 * g + 2];
     float4 q = quats[g];
     float o = opac[g];
 
-    bool ok = finitef(mx) && finitef(my) && finitef(mz) && finitef(s0) && finitef(s1) && finitef(s2) &&
+    bool ok = live && finitef(mx) && finitef(my) && finitef(mz) && finitef(s0) && finitef(s1) && finitef(s2) &&
               finitef(q.x) && finitef(q.y) && finitef(q.z) && finitef(q.w) && finitef(o);
     Geo geo;
     ok = ok && geometry(cam, near_plane, mx, my, mz, s0, s1, s2, q, geo);
@@ -250,6 +284,12 @@ __global__ __launch_bounds__(64) void k_preprocess(
             }
         }
     }
+    // the SH rows of the visible Gaussians
+    float* shg = s_sh + threadIdx.x * stride;
+    if (__popcll(__ballot(ok)) > SH_DENSE) stage_in(sh, s_sh, base, n, 3 * sh_rows, 3 * K, stride);
+    else if (ok) copy_own_row(sh, shg, g, 3 * sh_rows, 3 * K);
+    __syncthreads();
+    if (!live) return;
     float col[3] = {0.f, 0.f, 0.f};
     uint8_t cl = 0;
     if (ok) {
@@ -258,7 +298,6 @@ __global__ __launch_bounds__(64) void k_preprocess(
         float id = 1.0f / dist;
         float Y[16];
         sh_eval(K, dx * id, dy * id, dz * id, Y);
-        const float* shg = s_sh + threadIdx.x * stride;
         float raw[3] = {0.5f, 0.5f, 0.5f};
         for (int k = 0; k < K; ++k) {
             raw[0] = fmaf(shg[3 * k], Y[k], raw[0]);
@@ -300,7 +339,7 @@ __global__ __launch_bounds__(64) void k_preprocess(
 // contributions (zero for a culled Gaussian), which the caller adds to dL/dsh.
 // The other outputs of culled Gaussians are left untouched.
 __device__ __forceinline__ void chain_rule(
-    const DevCam& cam, int K, float near_plane, int gi,
+    const DevCam& cam, int K, float lowpass, float near_plane, int gi,
     const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
     float* shg, const float4* __restrict__ conic_op, const int* __restrict__ radii,
     const uint8_t* __restrict__ clamped, const float* __restrict__ grad2d,
@@ -318,11 +357,8 @@ __device__ __forceinline__ void chain_rule(
     float4 con = conic_op[g];
     float a = con.x, beta = con.y, gamma = con.z, o = con.w;
 
-    // pixel sums -> gradients of (a, beta, gamma, u, v, opacity); dL/dQ = -h/2
+    // pixel sums -> gradients of (u, v, opacity); dL/dQ = -h/2 and dQ/du = -2 a w
     float d_o = o != 0.f ? Sh / o : 0.f;
-    float da = -0.5f * Sww;
-    float dbeta = -a * Swy;
-    float dgamma = -0.5f * Syy;
     float du = a * Sw;
     float dv = fmaf(a * beta, Sw, gamma * Sy);
 
@@ -330,17 +366,32 @@ __device__ __forceinline__ void chain_rule(
     float s[3] = {scales[3 * g], scales[3 * g + 1], scales[3 * g + 2]};
     Geo geo;
     if (!geometry(cam, near_plane, mx, my, mz, s[0], s[1], s[2], quats[g], geo)) return culled();
+    float ddx = mx - cam.campos[0], ddy = my - cam.campos[1], ddz = mz - cam.campos[2];
 
-    // (a, beta, gamma) -> Sigma' = [[A, B], [B, C]] with a = C/det, beta = -B/C, gamma = 1/C
-    float a2 = a * a;
-    float dA = -a2 * da;
-    float dB = fmaf(-2.f * beta * a2, da, -gamma * dbeta);
-    float dC = fmaf(-beta * beta * a2, da, fmaf(-beta * gamma, dbeta, -gamma * gamma * dgamma));
-    // Sigma' = T T^T + lowpass I  ->  dT = 2 [[dA, dB/2], [dB/2, dC]] T
+    // dL/dSigma' = (1/2) sum_p h (Sigma'^-1 d)(Sigma'^-1 d)^T with Sigma'^-1 d = a w e + gamma dy f,
+    // e = (1, beta), f = (0, 1). Since Sigma' = T T^T + lowpass I, dT = 2 dL/dSigma' T
+    //   = e k^T + f m^T,  k = a^2 Sww U + a gamma Swy T1,  m = a gamma Swy U + gamma^2 Syy T1,
+    // with U = e^T T = T0 + beta T1. For a thin footprint T0 and T1 are nearly parallel and
+    // T0 + beta T1 cancels; U = gamma (T1 x (T0 x T1) + lowpass T0) is the same vector without
+    // the cancellation, T0 x T1 taken in the closed form the projection uses.
+    float e0 = fmaf(geo.Rq[0], ddx, fmaf(geo.Rq[3], ddy, geo.Rq[6] * ddz));
+    float e1 = fmaf(geo.Rq[1], ddx, fmaf(geo.Rq[4], ddy, geo.Rq[7] * ddz));
+    float e2 = fmaf(geo.Rq[2], ddx, fmaf(geo.Rq[5], ddy, geo.Rq[8] * ddz));
+    float izc = 1.0f / geo.z;
+    float kk = cam.fx * cam.fy * izc * izc * izc;
+    float c0 = kk * e0 * s[1] * s[2], c1 = kk * e1 * s[0] * s[2], c2 = kk * e2 * s[0] * s[1];
+    const float* T0 = geo.T;
+    const float* T1 = geo.T + 3;
+    float U[3] = {gamma * fmaf(lowpass, T0[0], fmaf(T1[1], c2, -T1[2] * c1)),
+                  gamma * fmaf(lowpass, T0[1], fmaf(T1[2], c0, -T1[0] * c2)),
+                  gamma * fmaf(lowpass, T0[2], fmaf(T1[0], c1, -T1[1] * c0))};
+    float kU = a * a * Sww, kT = a * gamma * Swy, mT = gamma * gamma * Syy;
     float dT[6];
     for (int j = 0; j < 3; ++j) {
-        dT[j] = fmaf(2.f * dA, geo.T[j], dB * geo.T[3 + j]);
-        dT[3 + j] = fmaf(dB, geo.T[j], 2.f * dC * geo.T[3 + j]);
+        float kj = fmaf(kU, U[j], kT * T1[j]);
+        float mj = fmaf(kT, U[j], mT * T1[j]);
+        dT[j] = kj;
+        dT[3 + j] = fmaf(beta, kj, mj);
     }
     // T = P diag(s): dP = dT diag(s), ds_j = sum_i dT_ij P_ij
     float dP[6], ds[3];
@@ -387,7 +438,6 @@ __device__ __forceinline__ void chain_rule(
     uint8_t cl = clamped[g];
     float dcol[3];
     for (int c = 0; c < 3; ++c) dcol[c] = (cl >> c) & 1 ? 0.f : dr[c];
-    float ddx = mx - cam.campos[0], ddy = my - cam.campos[1], ddz = mz - cam.campos[2];
     float dist = sqrtf(fmaf(ddx, ddx, fmaf(ddy, ddy, ddz * ddz)));
     float id = 1.0f / dist;
     float dxn = ddx * id, dyn = ddy * id, dzn = ddz * id;
@@ -440,15 +490,21 @@ __global__ __launch_bounds__(64) void k_preprocess_bwd(
     extern __shared__ float s_sh[];
     const int stride = (3 * K) | 1;
     const int base = blockIdx.x * 64;
-    stage_in(sh, s_sh, base, n, 3 * sh_rows, 3 * K, stride);
-    __syncthreads();
     const int gi = base + threadIdx.x;
-    if (gi < n)
-        chain_rule(cam, K, near_plane, gi, means, scales, quats, s_sh + threadIdx.x * stride, conic_op, radii,
-                   clamped, grad2d, d_means, d_scales, d_quats, d_opac, d_means2d);
+    const bool vis = gi < n && radii[gi] > 0;
+    const int nvis = __popcll(__ballot(vis));
+    if (nvis == 0) return;  // nothing of this block was drawn: no gradient
+    const bool dense = nvis > SH_DENSE;
+    float* shg = s_sh + threadIdx.x * stride;
+    if (dense) stage_in(sh, s_sh, base, n, 3 * sh_rows, 3 * K, stride);
+    else if (vis) copy_own_row(sh, shg, (size_t)gi, 3 * sh_rows, 3 * K);
     __syncthreads();
-    stage_out_add(s_sh, d_sh, base, n, 3 * sh_rows, 3 * K, stride);
-    (void)lowpass;
+    if (gi < n)
+        chain_rule(cam, K, lowpass, near_plane, gi, means, scales, quats, shg, conic_op, radii, clamped, grad2d, d_means,
+                   d_scales, d_quats, d_opac, d_means2d);
+    __syncthreads();
+    if (dense) stage_out_add(s_sh, d_sh, base, n, 3 * sh_rows, 3 * K, stride);
+    else if (vis) add_own_row(shg, d_sh, (size_t)gi, 3 * sh_rows, 3 * K);
 }
 
 }  // namespace
