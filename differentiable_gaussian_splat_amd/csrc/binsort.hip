@@ -260,88 +260,166 @@ hipError_t scan(Load ld, Store st, int n, const u64* dcount, u64* partials, u64*
 
 // ---------------------------------------------------------------- radix sort
 
-// Keys and values read from memory.
+// One LSD pass of up to 8 bits over (key, value) pairs in memory. RB-thread
+// blocks own RE consecutive elements each.
+//   k_radix_hist: per-block digit counts into hist[block][digit], and the
+//     digit totals added atomically into tot[RT][256] (zero on entry; block b
+//     adds into row b % RT, which spreads the atomics over RT addresses);
+//   k_radix_offsets (one 64-lane block per digit): the table becomes the
+//     pass's output offsets, digit-major: offset[b][d] = sum over digits < d of
+//     their totals + sum over blocks < b of digit d's counts. It also clears
+//     the next pass's totals (spare[RT][256]), so passes alternate two buffers.
+//   k_radix_scatter: stable scatter with those offsets.
+constexpr int RB = 1024;             // threads per radix block (16 waves)
+constexpr int RE = 4096;             // elements per radix block
+constexpr int RW = RB / 64;          // waves per radix block
+constexpr int RR = RE / RB;          // elements per thread
+constexpr int RT = 8;                // rows of the digit-total buffers
+
 struct SrcMem {
-    static constexpr int E = 4096;          // elements per block
-    static constexpr int LDS_WORDS = 0;
     const uint32_t* keys;
     const uint32_t* vals;
-    __device__ void setup(int, int, uint32_t*) const {}
-    __device__ uint32_t key(int p, const uint32_t*, int) const { return keys[p]; }
-    __device__ void get(int p, uint32_t& k, uint32_t& v, const uint32_t*, int) const {
-        k = keys[p];
-        v = vals[p];
-    }
 };
 
-template <class Src>
-__global__ __launch_bounds__(SB) void k_ms_hist(Src src, int n, const u64* dcount, int shift, int bits, int nblocks,
-                                              uint32_t* __restrict__ hist) {
-    constexpr int E = Src::E, R = E / SB;
-    __shared__ uint32_t lds[Src::LDS_WORDS > 0 ? Src::LDS_WORDS : 1];
-    __shared__ uint32_t s_h[4][256];
-    for (int k = threadIdx.x; k < 4 * 256; k += SB) (&s_h[0][0])[k] = 0u;
-    const int cnt = eff_count(n, dcount);
-    const int p0 = blockIdx.x * E;
-    const int p1 = min(cnt, p0 + E);
-    src.setup(p0, p1, lds);
-    __syncthreads();
-    const uint32_t mask = (1u << bits) - 1u;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll 4
-    for (int r = 0; r < R; ++r) {
-        int p = p0 + w * R * 64 + r * 64 + lane;
-        if (p < p1) atomicAdd(&s_h[w][(src.key(p, lds, p0) >> shift) & mask], 1u);
+// Exclusive scan of v over threads 0..255 of the block (other threads pass 0
+// and get 0); s_w holds 4 words.
+__device__ __forceinline__ uint32_t digit_excl_scan(uint32_t v, uint32_t* s_w) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    uint32_t x = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
     }
+    if (lane == 63 && w < 4) s_w[w] = x;
     __syncthreads();
-    const int nbins = 1 << bits;
-    if ((int)threadIdx.x < nbins)
-        hist[(size_t)threadIdx.x * nblocks + blockIdx.x] =
-            s_h[0][threadIdx.x] + s_h[1][threadIdx.x] + s_h[2][threadIdx.x] + s_h[3][threadIdx.x];
+    uint32_t pre = 0;
+    for (int i = 0; i < 4; ++i) pre += i < w ? s_w[i] : 0u;
+    __syncthreads();
+    return tid < 256 ? pre + x - v : 0u;
 }
 
-// Stable scatter of one radix digit. Wave w owns the block's elements
-// [w E/4, (w+1) E/4) in rounds of 64 consecutive ones; within a round, lanes
-// with equal digits are matched by ballots and ranked against the wave's own
-// LDS counters (no barrier per round); after one barrier the per-digit wave
-// offsets are combined, the block is reordered in LDS by (digit, rank), and
-// written out so that each digit's elements form one contiguous run.
-template <class Src>
-__global__ __launch_bounds__(SB) void k_ms_scatter(Src src, int n, const u64* dcount, int shift, int bits,
-                                                 int nblocks, const uint32_t* __restrict__ hist_scanned,
-                                                 uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out,
-                                                 u64* __restrict__ keys64_out, const float* __restrict__ depths) {
-    constexpr int E = Src::E, R = E / SB;
-    constexpr int LW = Src::LDS_WORDS > 2 * E ? Src::LDS_WORDS : 2 * E;
-    __shared__ uint32_t lds[LW];  // the source's staging, later the output staging
-    __shared__ uint32_t s_wcnt[4][256];
-    __shared__ uint32_t s_wpre[4][256];
+__global__ __launch_bounds__(RB) void k_radix_hist(SrcMem src, int n, const u64* dcount, int shift, int bits,
+                                                 uint32_t* __restrict__ hist, uint32_t* __restrict__ tot) {
+    __shared__ uint32_t s_h[RW][256];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int k = tid; k < RW * 256; k += RB) (&s_h[0][0])[k] = 0u;
+    const int cnt = eff_count(n, dcount);
+    const int p0 = blockIdx.x * RE;
+    const int p1 = min(cnt, p0 + RE);
+    __syncthreads();
+    const uint32_t mask = (1u << bits) - 1u;
+    uint32_t kk[RR];
+#pragma unroll
+    for (int r = 0; r < RR; ++r) {
+        const int p = p0 + (w * RR + r) * 64 + lane;
+        kk[r] = p < p1 ? src.keys[p] : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < RR; ++r) {
+        const int p = p0 + (w * RR + r) * 64 + lane;
+        if (p < p1) atomicAdd(&s_h[w][(kk[r] >> shift) & mask], 1u);
+    }
+    __syncthreads();
+    if (tid < 256) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int k = 0; k < RW; ++k) c += s_h[k][tid];
+        hist[(size_t)blockIdx.x * 256 + tid] = c;
+        if (c) atomicAdd(&tot[(blockIdx.x % RT) * 256 + tid], c);
+    }
+}
+
+// Block d (64 lanes): digit d's base from the totals, then its running offsets
+// over the blocks, each lane a contiguous run of blocks.
+__global__ __launch_bounds__(64) void k_radix_offsets(int nblocks, uint32_t* __restrict__ hist,
+                                                    const uint32_t* __restrict__ tot, uint32_t* __restrict__ spare) {
+    const int d = blockIdx.x, lane = threadIdx.x;
+    // base = sum of the totals of digits below d
+    const int j = 4 * lane;
+    uint32_t below = 0;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const uint4 t4 = reinterpret_cast<const uint4*>(tot + r * 256)[lane];
+        below += (j < d ? t4.x : 0u) + (j + 1 < d ? t4.y : 0u) + (j + 2 < d ? t4.z : 0u) + (j + 3 < d ? t4.w : 0u);
+    }
+    for (int off = 32; off > 0; off >>= 1) below += (uint32_t)__shfl_xor((int)below, off);
+    constexpr int U = 8;
+    const int per = (nblocks + 63) / 64;
+    const int b0 = lane * per;
+    uint32_t v[U];
+    uint32_t sum = 0;
+    for (int c = 0; c < per; c += U) {
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int b = b0 + c + k;
+            v[k] = (c + k < per && b < nblocks) ? hist[(size_t)b * 256 + d] : 0u;
+            sum += v[k];
+        }
+    }
+    // exclusive scan of the lane sums
+    uint32_t x = sum;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)x, off);
+        if (lane >= off) x += y;
+    }
+    uint32_t run = below + x - sum;
+    for (int c = 0; c < per; c += U) {
+        uint32_t w[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int b = b0 + c + k;
+            w[k] = (c + k < per && b < nblocks) ? hist[(size_t)b * 256 + d] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int b = b0 + c + k;
+            if (c + k < per && b < nblocks) hist[(size_t)b * 256 + d] = run;
+            run += w[k];
+        }
+    }
+    if (lane < RT) spare[lane * 256 + d] = 0u;
+}
+
+// Stable scatter of one digit. Wave w owns the block's elements
+// [w RE/RW, (w+1) RE/RW) in rounds of 64 consecutive ones; within a round,
+// lanes with equal digits are matched by ballots and ranked against the wave's
+// own LDS counters (no barrier per round); after one barrier the per-digit
+// wave offsets are combined, the block is reordered in LDS by (digit, rank),
+// and written out so that each digit's elements form one contiguous run.
+__global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem src, int n, const u64* dcount, int shift, int bits,
+                                                    const uint32_t* __restrict__ offsets,
+                                                    uint32_t* __restrict__ keys_out,
+                                                    uint32_t* __restrict__ vals_out) {
+    __shared__ uint32_t s_keys[RE];
+    __shared__ uint32_t s_vals[RE];
+    __shared__ uint32_t s_wcnt[RW][256];  // per-wave digit counts, then each wave's first slot per digit
     __shared__ uint32_t s_dstart[256];
     __shared__ uint32_t s_gbase[256];
-    __shared__ uint32_t s_w[SB / 64];
+    __shared__ uint32_t s_w[4];
     const int cnt = eff_count(n, dcount);
-    const int p0 = blockIdx.x * E;
+    const int p0 = blockIdx.x * RE;
     if (p0 >= cnt) return;
-    const int p1 = min(cnt, p0 + E);
+    const int p1 = min(cnt, p0 + RE);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int nbins = 1 << bits;
-    const uint32_t mask = (uint32_t)nbins - 1u;
-    src.setup(p0, p1, lds);
+    const uint32_t mask = (1u << bits) - 1u;
     for (int k = lane; k < 256; k += 64) s_wcnt[w][k] = 0u;
     wave_lds_sync();
-    s_gbase[tid] = tid < nbins ? hist_scanned[(size_t)tid * nblocks + blockIdx.x] : 0u;
-    uint32_t kk[R], vv[R], rk[R];
-    const int ebase = p0 + w * R * 64 + lane;
+    if (tid < 256) s_gbase[tid] = offsets[(size_t)blockIdx.x * 256 + tid];
+    uint32_t kk[RR], vv[RR], rk[RR];
+    const int ebase = p0 + w * RR * 64 + lane;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        int p = ebase + r * 64;
+    for (int r = 0; r < RR; ++r) {
+        const int p = ebase + r * 64;
         kk[r] = 0u;
         vv[r] = 0u;
-        if (p < p1) src.get(p, kk[r], vv[r], lds, p0);
+        if (p < p1) {
+            kk[r] = src.keys[p];
+            vv[r] = src.vals[p];
+        }
     }
     const uint64_t lt = lanemask_lt();
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < RR; ++r) {
         const bool valid = ebase + r * 64 < p1;
         const uint32_t d = (kk[r] >> shift) & mask;
         uint64_t peers = __ballot(valid);
@@ -357,57 +435,52 @@ __global__ __launch_bounds__(SB) void k_ms_scatter(Src src, int n, const u64* dc
         wave_lds_sync();  // the wave's counters are read by other lanes next round
     }
     __syncthreads();
-    uint32_t c0 = 0, c1 = 0, c2 = 0;
     uint32_t tot = 0;
-    if (tid < nbins) {
-        c0 = s_wcnt[0][tid];
-        c1 = s_wcnt[1][tid];
-        c2 = s_wcnt[2][tid];
-        tot = c0 + c1 + c2 + s_wcnt[3][tid];
-    }
-    uint32_t all;
-    const uint32_t ds = block_excl_scan_u32(tot, s_w, all);
-    if (tid < nbins) {
+    if (tid < 256)
+        for (int k = 0; k < RW; ++k) tot += s_wcnt[k][tid];
+    const uint32_t ds = digit_excl_scan(tot, s_w);
+    if (tid < 256) {
         s_dstart[tid] = ds;
-        s_wpre[0][tid] = ds;
-        s_wpre[1][tid] = ds + c0;
-        s_wpre[2][tid] = ds + c0 + c1;
-        s_wpre[3][tid] = ds + c0 + c1 + c2;
+        uint32_t run = ds;
+        for (int k = 0; k < RW; ++k) {
+            const uint32_t c = s_wcnt[k][tid];
+            s_wcnt[k][tid] = run;
+            run += c;
+        }
     }
     __syncthreads();
-    uint32_t* s_keys = lds;
-    uint32_t* s_vals = lds + E;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < RR; ++r) {
         if (ebase + r * 64 < p1) {
-            const uint32_t slot = s_wpre[w][(kk[r] >> shift) & mask] + rk[r];
+            const uint32_t slot = s_wcnt[w][(kk[r] >> shift) & mask] + rk[r];
             s_keys[slot] = kk[r];
             s_vals[slot] = vv[r];
         }
     }
     __syncthreads();
     const int here = p1 - p0;
-    for (int sl = tid; sl < here; sl += SB) {
+    for (int sl = tid; sl < here; sl += RB) {
         const uint32_t key = s_keys[sl];
-        const uint32_t val = s_vals[sl];
         const uint32_t d = (key >> shift) & mask;
         const uint32_t dst = s_gbase[d] + ((uint32_t)sl - s_dstart[d]);
-        if (keys_out) keys_out[dst] = key;
-        vals_out[dst] = val;
-        if (keys64_out) keys64_out[dst] = ((u64)key << 32) | (u64)__float_as_uint(depths[val]);
+        if (dst < (uint32_t)cnt) {  // always true for a consistent offset table
+            keys_out[dst] = key;
+            vals_out[dst] = s_vals[sl];
+        }
     }
 }
 
-template <class Src>
-hipError_t radix_pass(Src src, int n, const u64* dcount, int shift, int bits, uint32_t* hist, u64* partials,
-                      uint32_t* keys_out, uint32_t* vals_out, u64* keys64_out, const float* depths, hipStream_t s) {
-    const int nblocks = (n + Src::E - 1) / Src::E;
+// hist: 256 words per block. rtot: two RT x 256-word total buffers; pass number
+// `pass` adds into rtot[pass & 1] (zero on entry) and clears the other.
+hipError_t radix_pass(SrcMem src, int n, const u64* dcount, int shift, int bits, uint32_t* hist, uint32_t* rtot,
+                      int pass, uint32_t* keys_out, uint32_t* vals_out, hipStream_t s) {
+    const int nblocks = (n + RE - 1) / RE;
     if (nblocks == 0) return hipSuccess;
-    k_ms_hist<Src><<<nblocks, SB, 0, s>>>(src, n, dcount, shift, bits, nblocks, hist);
-    hipError_t e = scan(LoadPlain{hist}, StoreInPlace{hist}, (1 << bits) * nblocks, nullptr, partials, nullptr, s);
-    if (e != hipSuccess) return e;
-    k_ms_scatter<Src><<<nblocks, SB, 0, s>>>(src, n, dcount, shift, bits, nblocks, hist, keys_out, vals_out, keys64_out,
-                                             depths);
+    uint32_t* tot = rtot + RT * 256 * (pass & 1);
+    uint32_t* spare = rtot + RT * 256 * ((pass & 1) ^ 1);
+    k_radix_hist<<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, tot);
+    k_radix_offsets<<<256, 64, 0, s>>>(nblocks, hist, tot, spare);
+    k_radix_scatter<<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, keys_out, vals_out);
     return hipGetLastError();
 }
 
@@ -730,7 +803,7 @@ BinLayout bin_layout(int64_t n, int64_t capacity, int TX, int TY) {
     L.counts = take(4 * 64 * max_pieces);
     L.tile_total = take(4 * ntiles);
     size_t max_elems = nn > cap ? nn : cap;
-    const size_t hist_entries = 256 * ((max_elems + SrcMem::E - 1) / SrcMem::E);
+    const size_t hist_entries = 256 * ((max_elems + RE - 1) / RE);
     size_t max_scan = hist_entries;
     if (nn > max_scan) max_scan = nn;
     if (ntiles > max_scan) max_scan = ntiles;
@@ -738,7 +811,7 @@ BinLayout bin_layout(int64_t n, int64_t capacity, int TX, int TY) {
     L.partials = take(8 * ((max_scan + ST - 1) / ST + 1));
     L.pair_part = take(8 * 2 * TOTALS_BLOCKS);
     L.hist = take(4 * hist_entries);
-    L.counters = take(8 * NCOUNTERS);
+    L.counters = take(8 * NCOUNTERS + 4 * 2 * RT * 256);  // counters, then the radix passes' two digit-total buffers
     L.total = off;
     return L;
 }
@@ -749,7 +822,9 @@ hipError_t launch_bin_count(int n, int TX, int TY, const float* means2d, const i
     u64* counters = reinterpret_cast<u64*>(ws + L.counters);
     u64* partials = reinterpret_cast<u64*>(ws + L.partials);
     const float2* m2 = reinterpret_cast<const float2*>(means2d);
-    hipError_t e = fill(reinterpret_cast<uint32_t*>(counters), 2 * NCOUNTERS, 0u, s);
+    // counters and both radix total buffers; the depth sort's four passes leave
+    // buffer 0 clear again for the super-tile pass of launch_bin_emit
+    hipError_t e = fill(reinterpret_cast<uint32_t*>(counters), 2 * NCOUNTERS + 2 * RT * 256, 0u, s);
     if (e != hipSuccess) return e;
     // the pair counts first, on their way to the host while the rest runs
     if (n > 0) {
@@ -770,10 +845,10 @@ hipError_t launch_bin_count(int n, int TX, int TY, const float* means2d, const i
     if (e != hipSuccess) return e;
     // 2. stable sort by the 32 depth bits, 4 passes of 8: the result returns to buffer 0
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+    uint32_t* rtot = reinterpret_cast<uint32_t*>(ws + L.counters) + 2 * NCOUNTERS;
     for (int pass = 0; pass < 4; ++pass) {
         int c = pass & 1;
-        e = radix_pass(SrcMem{dk[c], di[c]}, n, &counters[0], 8 * pass, 8, hist, partials, dk[c ^ 1], di[c ^ 1],
-                       nullptr, nullptr, s);
+        e = radix_pass(SrcMem{dk[c], di[c]}, n, &counters[0], 8 * pass, 8, hist, rtot, pass, dk[c ^ 1], di[c ^ 1], s);
         if (e != hipSuccess) return e;
     }
     // 3. per depth-sorted Gaussian: record, super-tile count (in the free depth
@@ -793,6 +868,7 @@ hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const
     u64* counters = reinterpret_cast<u64*>(ws + L.counters);
     u64* partials = reinterpret_cast<u64*>(ws + L.partials);
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+    uint32_t* rtot = reinterpret_cast<uint32_t*>(ws + L.counters) + 2 * NCOUNTERS;
     const uint32_t* first = reinterpret_cast<const uint32_t*>(ws + L.first);
     const uint4* rec = reinterpret_cast<const uint4*>(ws + L.rec);
     uint32_t* sk[2] = {reinterpret_cast<uint32_t*>(ws + L.skey[0]), reinterpret_cast<uint32_t*>(ws + L.skey[1])};
@@ -814,8 +890,7 @@ hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const
     for (int pass = 0; pass < passes; ++pass) {
         const int shift = pass * bpp;
         const int bits = min(bpp, sbits - shift);
-        e = radix_pass(SrcMem{sk[cur], sv[cur]}, P1, nullptr, shift, bits, hist, partials, sk[cur ^ 1], sv[cur ^ 1],
-                       nullptr, nullptr, s);
+        e = radix_pass(SrcMem{sk[cur], sv[cur]}, P1, nullptr, shift, bits, hist, rtot, pass, sk[cur ^ 1], sv[cur ^ 1], s);
         if (e != hipSuccess) return e;
         cur ^= 1;
     }

@@ -44,22 +44,30 @@ __device__ __forceinline__ void set_walk_priority(uint32_t walk) {
 // Q <= 2 ln(255 o). The margins (0.1% and 1e-3) lie far above fp32 rounding,
 // so a skipped record is one the per-pixel test would skip too: results are
 // unchanged, only the per-pixel work for such records is saved.
+struct MissTest {
+    float lmin, qthr;
+    __device__ __forceinline__ MissTest(float4 c, float lo) {
+        const float a = c.x, beta = c.y, gamma = c.z;  // Q = a (dx + beta dy)^2 + gamma dy^2
+        const float m11 = a * beta * beta + gamma;
+        const float tr = a + m11, det = a * gamma;
+        const float h = 0.5f * tr;
+        const float lmax = h + sqrtf(fmaxf(h * h - det, 0.f));
+        lmin = det / lmax;
+        // 2 ln(255 o) = 2 ln 2 (log2 o + log2 255)
+        qthr = 1.3862943611198906f * (lo + 7.9943534368588578f) + 1e-3f;
+    }
+    __device__ __forceinline__ bool misses(float u, float v, float x_lo, float x_hi, float y_lo, float y_hi) const {
+        const float ddx = fmaxf(0.f, fmaxf(x_lo - u, u - x_hi));
+        const float ddy = fmaxf(0.f, fmaxf(y_lo - v, v - y_hi));
+        return lmin * (ddx * ddx + ddy * ddy) * 0.999f > qthr;
+    }
+};
+
 __device__ __forceinline__ bool band_misses(float u, float v, float4 c, float lo, float x_lo, float x_hi, float y_lo,
                                             float y_hi) {
-    const float a = c.x, beta = c.y, gamma = c.z;  // Q = a (dx + beta dy)^2 + gamma dy^2
-    const float m11 = a * beta * beta + gamma;
-    const float tr = a + m11, det = a * gamma;
-    const float h = 0.5f * tr;
-    const float lmax = h + sqrtf(fmaxf(h * h - det, 0.f));
-    const float lmin = det / lmax;
-    const float ddx = fmaxf(0.f, fmaxf(x_lo - u, u - x_hi));
-    const float ddy = fmaxf(0.f, fmaxf(y_lo - v, v - y_hi));
-    // 2 ln(255 o) = 2 ln 2 (log2 o + log2 255)
-    const float qthr = 1.3862943611198906f * (lo + 7.9943534368588578f);
-    return lmin * (ddx * ddx + ddy * ddy) * 0.999f > qthr + 1e-3f;
+    return MissTest(c, lo).misses(u, v, x_lo, x_hi, y_lo, y_hi);
 }
 
-// Stages record `lane` of a batch: (u, v, a2, beta), (g2, log2 o, r, g), b.
 // Stages record `lane` of a batch: (w0, dy0, a2, beta), (g2, log2 o, r, g), b,
 // where w0 and dy0 are w and dy at the tile's first pixel centre (ox, oy),
 // formed in double and rounded once. Returns whether the record misses the
@@ -77,6 +85,35 @@ __device__ __forceinline__ bool stage_record(uint32_t g, const float2* __restric
     s_b[lane] = make_float4(k.z, k.w, rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1]);
     s_c[lane] = rgb[3 * (size_t)g + 2];
     return band_misses(m.x, m.y, c, k.w, x_lo, x_hi, y_lo, y_hi);
+}
+
+// The backward's staging: as stage_record, but returns a mask of the PPL row
+// bands of the tile (rows [4k, 4k + 4)) the record may reach; bit k is also
+// clear when the record lies at or past every blended entry of band k
+// (pos >= band_last[k]).
+template <int PPL>
+__device__ __forceinline__ uint32_t stage_record_bands(uint32_t g, uint32_t pos, const uint32_t* band_last,
+                                                       const float2* __restrict__ means2d,
+                                                       const float4* __restrict__ conic_op,
+                                                       const float* __restrict__ rgb, float4* s_a, float4* s_b,
+                                                       float* s_c, int lane, double ox, double oy, float x_lo,
+                                                       float x_hi, float y_lo) {
+    const float2 m = means2d[g];
+    const float4 c = conic_op[g];
+    const float4 k = falloff_consts(c);
+    const double ddy = oy - (double)m.y;
+    const double w0 = (ox - (double)m.x) + (double)c.y * ddy;
+    s_a[lane] = make_float4((float)w0, (float)ddy, k.x, k.y);
+    s_b[lane] = make_float4(k.z, k.w, rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1]);
+    s_c[lane] = rgb[3 * (size_t)g + 2];
+    const MissTest mt(c, k.w);
+    uint32_t mask = 0u;
+#pragma unroll
+    for (int b = 0; b < PPL; ++b) {
+        const float y0 = y_lo + 4.f * b;
+        if (pos < band_last[b] && !mt.misses(m.x, m.y, x_lo, x_hi, y0, y0 + 3.f)) mask |= 1u << b;
+    }
+    return mask;
 }
 
 // Forward. Per pixel: alpha = min(0.99, o G); entries with alpha < 1/255 are
@@ -211,8 +248,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
     const float lx = (float)(lane & 15);                                         // this lane's offset from it
     const size_t HW = (size_t)W * H;
     float ly[PPL], T[PPL], g0[PPL], g1[PPL], g2[PPL], S[PPL];
-    uint32_t last[PPL];
-    uint32_t mylast = 0;
+    uint32_t last[PPL], band_last[PPL];
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
         const int py = py0 + 4 * k;
@@ -225,56 +261,57 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
         g1[k] = in ? dL_dimage[HW + p] : 0.f;
         g2[k] = in ? dL_dimage[2 * HW + p] : 0.f;
         S[k] = fmaf(bg0, g0[k], fmaf(bg1, g1[k], bg2 * g2[k]));
-        mylast = max(mylast, last[k]);
+        band_last[k] = __builtin_amdgcn_readfirstlane(wave_max_u32(last[k]));  // deepest blended entry of band k
     }
+    uint32_t mylast = 0;
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) mylast = max(mylast, band_last[k]);
     const float bx_lo = (float)(tx * TILE) + 0.5f, bx_hi = bx_lo + 15.f;
-    const float by_lo = (float)(ty * TILE + band * 4 * PPL) + 0.5f, by_hi = by_lo + (float)(4 * PPL - 1);
+    const float by_lo = (float)(ty * TILE + band * 4 * PPL) + 0.5f;
     const uint2 rg = ranges[tile];
     // never walk past the tile's list, whatever n_contrib holds
-    const uint32_t maxlast = min(wave_max_u32(mylast), rg.y - rg.x);
+    const uint32_t maxlast = min(mylast, rg.y - rg.x);
     set_walk_priority(maxlast);
     for (int hi = (int)maxlast; hi > 0; hi -= NB) {
         const int lo = max(0, hi - NB);
         const int cnt = hi - lo;
-        bool miss = true;
+        uint32_t bands = 0u;
         if (lane < cnt) {
             const uint32_t g = values[rg.x + lo + lane];
-            miss = stage_record(g, means2d, conic_op, rgb, s_a, s_b, s_c, lane, ox, oy, bx_lo, bx_hi, by_lo, by_hi);
+            bands = stage_record_bands<PPL>(g, (uint32_t)(lo + lane), band_last, means2d, conic_op, rgb, s_a, s_b,
+                                            s_c, lane, ox, oy, bx_lo, bx_hi, by_lo);
             s_g[lane] = g;
             s_has[lane] = 0u;
         }
-        uint64_t todo = __ballot(!miss);  // records some pixel of the band may blend
+        uint64_t todo = __ballot(bands != 0u);  // records some row band may blend
         __syncthreads();
         while (todo) {
             const int j = 63 - __builtin_clzll(todo);  // backwards through the list
             todo &= ~(1ull << j);
+            const uint32_t bm = __builtin_amdgcn_readlane(bands, j);  // row bands this record may reach
             const float4 A = s_a[j];
             const float4 B = s_b[j];
             const float cb = s_c[j];
             const uint32_t pos = (uint32_t)(lo + j);
             const float wl = A.x + lx;  // w at this lane's column, tile's first row
-            // which of this lane's pixels blended this entry (same test as the forward)
-            float w[PPL], dy[PPL], oG[PPL], al[PPL];
-            bool blended[PPL];
-            bool any = false;
-#pragma unroll
-            for (int k = 0; k < PPL; ++k) {
-                dy[k] = A.y + ly[k];
-                w[k] = __fmaf_rn(A.w, ly[k], wl);
-                oG[k] = falloff(w[k], dy[k], A.z, B.x, B.y);
-                al[k] = fminf(ALPHA_MAX, oG[k]);
-                blended[k] = pos < last[k] && al[k] >= ALPHA_MIN;
-                any = any || blended[k];
-            }
-            if (!__any(any)) continue;
-            // branch-free: a pixel that did not blend this entry takes alpha = 0,
-            // which leaves its T, S and every sum unchanged
             float acc[GRAD2D_N];
 #pragma unroll
             for (int c = 0; c < GRAD2D_N; ++c) acc[c] = 0.f;
+            bool any = false;
 #pragma unroll
             for (int k = 0; k < PPL; ++k) {
-                const float av = blended[k] ? al[k] : 0.f;
+                if (!((bm >> k) & 1u)) continue;  // no pixel of band k blends this entry
+                // did this pixel blend the entry (the forward's own test)
+                const float dy = A.y + ly[k];
+                const float w = __fmaf_rn(A.w, ly[k], wl);
+                const float oG = falloff(w, dy, A.z, B.x, B.y);
+                const float al = fminf(ALPHA_MAX, oG);
+                const bool blended = pos < last[k] && al >= ALPHA_MIN;
+                if (!__any(blended)) continue;
+                any = true;
+                // branch-free within the band: a pixel that did not blend this entry takes
+                // alpha = 0, which leaves its T, S and every sum unchanged
+                const float av = blended ? al : 0.f;
                 T[k] = T[k] * __builtin_amdgcn_rcpf(1.0f - av);  // T in front of this entry
                 const float wt = av * T[k];
                 acc[0] = fmaf(wt, g0[k], acc[0]);
@@ -287,15 +324,16 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
                 // sat at its 0.99 clamp (and wherever the pixel did not blend: wt = 0). The
                 // moments stay in (w, dy), the conic's own axes: sums in (dx, dy) would
                 // cancel for elongated Gaussians.
-                const float h = oG[k] <= ALPHA_MAX ? wt * d : 0.f;
-                const float hw = h * w[k], hy = h * dy[k];
+                const float h = oG <= ALPHA_MAX ? wt * d : 0.f;
+                const float hw = h * w, hy = h * dy;
                 acc[3] += h;
-                acc[4] = fmaf(hw, w[k], acc[4]);
-                acc[5] = fmaf(hw, dy[k], acc[5]);
-                acc[6] = fmaf(hy, dy[k], acc[6]);
+                acc[4] = fmaf(hw, w, acc[4]);
+                acc[5] = fmaf(hw, dy, acc[5]);
+                acc[6] = fmaf(hy, dy, acc[6]);
                 acc[7] += hw;
                 acc[8] += hy;
             }
+            if (!any) continue;
             // per 16-lane row: values 0..7 by reduce-scatter (lane slot holds one), value 8 by a row sum
             const float u = row_reduce_scatter8(acc, c1, c2, c3);
             const float x8 = row_sum16(acc[8]);
