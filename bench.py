@@ -42,7 +42,7 @@ VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 * 2 / 1e12
 BWD_OPS_PER_ENTRY = 47
 ATOMICS_PER_TILE_ENTRY = 9      # one add per gradient value per (tile, Gaussian)
 PROFILES = os.path.join(ROOT, "profiles")
-STAGES = ["preprocess", "bin_sort", "render_fwd", "zero_grads", "render_bwd_raster", "preprocess_bwd"]
+STAGES = ["preprocess", "bin_sort", "render_fwd", "zero_pixel_sums", "render_bwd_raster", "preprocess_bwd"]
 
 
 def log(msg):
@@ -104,6 +104,8 @@ def main():
     n = sc.n
     cams = [raster.make_camera(sc.cameras[v]) for v in views]
     opt = raster.make_options(sc.sh_degree, sc.sh.shape[1])
+    # the step's first view writes the parameter gradients, the others add into them
+    opt_first = raster.make_options(sc.sh_degree, sc.sh.shape[1], overwrite_grads=True)
     W, H = cams[0].width, cams[0].height
     ntiles = ((W + 15) // 16) * ((H + 15) // 16)
 
@@ -125,7 +127,7 @@ def main():
     ranges = E((ntiles, 2), torch.int32)
     image, final_T, n_contrib = E((3, H, W), torch.float32), E((H, W), torch.float32), E((H, W), torch.int32)
     grad2d = E((n, raster.GRAD2D_STRIDE), torch.float32)
-    grads = raster.zero_grads(means, sh)
+    grads = raster.empty_grads(means, sh)
     stream = torch.cuda.current_stream()
     mk = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in views]
     ev_steps = [mk() for _ in range(args.steps)]
@@ -147,16 +149,14 @@ def main():
             e[2].record(stream)
             raster.gs_render_fwd(cam, opt, n, ranges, r._values, P, means2d, conic, rgb, image, final_T, n_contrib)
             e[3].record(stream)
-            if vi == 0:  # gradients are zeroed once per step and summed over the views
-                for g in grads.values():
-                    g.zero_()
             grad2d.zero_()  # the pixel sums belong to one view
             e[4].record(stream)
             raster.gs_render_bwd_raster(cam, opt, n, ranges, r._values, P, means2d, conic, rgb, final_T, n_contrib,
                                         dLs[vi], grad2d)
             e[5].record(stream)
-            raster.gs_preprocess_bwd(cam, opt, means, scales, quats, sh, conic, radii, clamped, grad2d,
-                                     grads["means"], grads["scales"], grads["quats"], grads["opacities"], grads["sh"])
+            raster.gs_preprocess_bwd(cam, opt_first if vi == 0 else opt, means, scales, quats, sh, conic, radii,
+                                     clamped, grad2d, grads["means"], grads["scales"], grads["quats"],
+                                     grads["opacities"], grads["sh"])
             e[6].record(stream)
 
     for _ in range(args.warmup):

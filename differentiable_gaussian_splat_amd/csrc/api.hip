@@ -61,6 +61,8 @@ gs_status check_common(const gs_camera* cam, const gs_options* opt, int64_t n, C
     REQUIRE(isfinite(opt->lowpass) && opt->lowpass >= 0.f, "lowpass must be finite and >= 0");
     REQUIRE(isfinite(opt->near_plane) && opt->near_plane > 0.f, "near_plane must be finite and > 0");
     for (int i = 0; i < 3; ++i) REQUIRE(isfinite(opt->bg[i]), "bg must be finite");
+    REQUIRE(opt->overwrite_grads == 0 || opt->overwrite_grads == 1, "overwrite_grads must be 0 or 1, got %d",
+            opt->overwrite_grads);
     gs::DevCam& d = out.cam;
     d.W = cam->width;
     d.H = cam->height;
@@ -121,6 +123,7 @@ gs_options gs_default_options(void) {
     o.lowpass = 0.3f;
     o.near_plane = 0.2f;
     o.bg[0] = o.bg[1] = o.bg[2] = 0.f;
+    o.overwrite_grads = 0;
     return o;
 }
 
@@ -316,7 +319,7 @@ gs_status gs_render_bwd(const gs_camera* cam, const gs_options* opt, int64_t n, 
         return hip_check(gs::launch_preprocess_bwd(c.cam, c.K, c.sh_rows, opt->lowpass, opt->near_plane, (int)n,
                                                    means, scales, quats, sh, conic_opacity, radii, clamped, grad2d,
                                                    dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh,
-                                                   dL_dmeans2d, s),
+                                                   dL_dmeans2d, opt->overwrite_grads != 0, s),
                          "gs_render_bwd(chain)");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_render_bwd: unexpected exception");
@@ -388,7 +391,7 @@ gs_status gs_preprocess_bwd(const gs_camera* cam, const gs_options* opt, int64_t
         return hip_check(gs::launch_preprocess_bwd(c.cam, c.K, c.sh_rows, opt->lowpass, opt->near_plane, (int)n,
                                                    means, scales, quats, sh, conic_opacity, radii, clamped, grad2d,
                                                    dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh,
-                                                   dL_dmeans2d, (hipStream_t)stream),
+                                                   dL_dmeans2d, opt->overwrite_grads != 0, (hipStream_t)stream),
                          "gs_preprocess_bwd");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_preprocess_bwd: unexpected exception");

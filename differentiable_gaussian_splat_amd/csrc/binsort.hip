@@ -672,14 +672,17 @@ __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int
 }
 
 // Placement, with the roles turned: lane = entry of a 64-entry group of the
-// piece, and a uniform loop over the super-tile's 64 tiles. For tile lt a
-// ballot of the rectangle tests gives the group's entries that hold it; in
+// piece, and a uniform loop over the super-tile's tiles that some entry of
+// the group holds. Each lane holds its entry's tiles as a 64-bit mask (bit
+// 8 row + column inside the super-tile); the OR of the masks lists the tiles
+// to visit. For tile lt a ballot gives the group's entries that hold it; in
 // depth order they take the next slots of the tile's run, lane at cursor +
 // (matching lanes below it). One store instruction therefore writes
 // consecutive slots of one run. The cursors (the tile's first slot plus the
 // counts of the super-tile's earlier pieces) live one per lane, lane lt for
 // tile lt. Stores check their slot against P: always true, it keeps a broken
 // invariant from writing out of bounds.
+template <bool KEYS>
 __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int S, int SX, int TX, int TY,
                                                  const uint32_t* __restrict__ pfirst, const uint2* __restrict__ sr,
                                                  const uint32_t* __restrict__ sval, const uint4* __restrict__ rec,
@@ -691,6 +694,7 @@ __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int S, int
     int s, e0, e1;
     piece_of(pidx, S, pfirst, sr, s, e0, e1);
     const int sx0 = (s % SX) * SUPER, sy0 = (s / SX) * SUPER;
+    const int vw = min(SUPER, TX - sx0), vh = min(SUPER, TY - sy0);  // the super-tile's tiles inside the grid
     const int mtx = sx0 + (lane & 7), mty = sy0 + (lane >> 3);
     uint32_t cur = (mtx < TX && mty < TY) ? ranges[mty * TX + mtx].x + offs[(size_t)pidx * 64 + lane] : 0u;
     const uint64_t lt_mask = lanemask_lt();
@@ -699,24 +703,37 @@ __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int S, int
     if (e0 + lane < e1) rn = rec[sval[e0 + lane]];
     for (int eb = e0; eb < e1; eb += 64) {
         const int ne = min(64, e1 - eb);
-        const bool live = lane < ne;
         const uint4 r = rn;
         if (eb + 64 + lane < e1) rn = rec[sval[eb + 64 + lane]];
-        const int X0 = (int)(r.y & 0xffffu), X1 = (int)(r.y >> 16);
-        const int Y0 = (int)(r.z & 0xffffu), Y1 = (int)(r.z >> 16);
-        for (int l = 0; l < 64; ++l) {
-            const int tx = sx0 + (l & 7), ty = sy0 + (l >> 3);
-            if (tx >= TX || ty >= TY) continue;  // uniform: the super-tile overhangs the grid
-            const bool in = live && tx >= X0 && tx <= X1 && ty >= Y0 && ty <= Y1;
+        // this lane's tiles of the super-tile
+        uint64_t mask = 0ull;
+        if (lane < ne) {
+            const int cx0 = max((int)(r.y & 0xffffu) - sx0, 0), cx1 = min((int)(r.y >> 16) - sx0, vw - 1);
+            const int cy0 = max((int)(r.z & 0xffffu) - sy0, 0), cy1 = min((int)(r.z >> 16) - sy0, vh - 1);
+            if (cx0 <= cx1 && cy0 <= cy1) {
+                const uint64_t cols = (uint64_t)(((2u << cx1) - 1u) & ~((1u << cx0) - 1u));
+                const uint64_t below_hi = cy1 == SUPER - 1 ? ~0ull : (1ull << (8 * (cy1 + 1))) - 1ull;
+                const uint64_t rows = below_hi & ~((1ull << (8 * cy0)) - 1ull) & 0x0101010101010101ull;
+                mask = rows * cols;
+            }
+        }
+        const uint32_t mlo = (uint32_t)mask, mhi = (uint32_t)(mask >> 32);
+        uint32_t ulo = mlo, uhi = mhi;
+        for (int off = 1; off < 64; off <<= 1) {
+            ulo |= (uint32_t)__shfl_xor((int)ulo, off);
+            uhi |= (uint32_t)__shfl_xor((int)uhi, off);
+        }
+        uint64_t todo = ((uint64_t)__builtin_amdgcn_readfirstlane(uhi) << 32) | __builtin_amdgcn_readfirstlane(ulo);
+        while (todo) {
+            const int l = __builtin_ctzll(todo);
+            todo &= todo - 1ull;
+            const bool in = (((l < 32 ? mlo : mhi) >> (l & 31)) & 1u) != 0u;
             const uint64_t m = __ballot(in);
-            if (m == 0ull) continue;
             const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)cur, l);
-            if (in) {
-                const uint32_t pos = base + (uint32_t)__popcll(m & lt_mask);
-                if (pos < P) {
-                    values[pos] = r.x;
-                    if (keys64) keys64[pos] = ((u64)(uint32_t)(ty * TX + tx) << 32) | (u64)r.w;
-                }
+            const uint32_t pos = base + (uint32_t)__popcll(m & lt_mask);
+            if (in && pos < P) {
+                values[pos] = r.x;
+                if (KEYS) keys64[pos] = ((u64)(uint32_t)((sy0 + (l >> 3)) * TX + sx0 + (l & 7)) << 32) | (u64)r.w;
             }
             cur = lane == l ? base + (uint32_t)__popcll(m) : cur;
         }
@@ -909,9 +926,14 @@ hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const
     e = scan(LoadPlain{tile_total}, StoreRanges{reinterpret_cast<uint2*>(ranges)}, ntiles, nullptr, partials, nullptr,
              s);
     if (e != hipSuccess) return e;
-    k_tile_place<<<(max_pieces + wpb - 1) / wpb, SB, 0, s>>>(&counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur], rec,
-                                                             counts, reinterpret_cast<const uint2*>(ranges),
-                                                             (uint32_t)P, values, reinterpret_cast<u64*>(keys));
+    if (keys)
+        k_tile_place<true><<<(max_pieces + wpb - 1) / wpb, SB, 0, s>>>(
+            &counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur], rec, counts,
+            reinterpret_cast<const uint2*>(ranges), (uint32_t)P, values, reinterpret_cast<u64*>(keys));
+    else
+        k_tile_place<false><<<(max_pieces + wpb - 1) / wpb, SB, 0, s>>>(
+            &counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur], rec, counts,
+            reinterpret_cast<const uint2*>(ranges), (uint32_t)P, values, nullptr);
     return hipGetLastError();
 }
 

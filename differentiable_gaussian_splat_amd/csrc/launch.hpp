@@ -18,7 +18,7 @@ hipError_t launch_preprocess_bwd(const DevCam& cam, int K, int sh_rows, float lo
                                  const float* means, const float* scales, const float* quats, const float* sh,
                                  const float* conic_op, const int* radii, const uint8_t* clamped,
                                  const float* grad2d, float* d_means, float* d_scales, float* d_quats,
-                                 float* d_opac, float* d_sh, float* d_means2d, hipStream_t stream);
+                                 float* d_opac, float* d_sh, float* d_means2d, bool overwrite, hipStream_t stream);
 
 // Binning. The workspace layout is computed by bin_layout (binsort.hip).
 struct BinLayout {

@@ -336,8 +336,11 @@ __global__ __launch_bounds__(64) void k_preprocess(
 
 // The chain rule for Gaussian gi. shg is its SH row in LDS: the coefficients
 // on entry, replaced coefficient by coefficient by their gradient
-// contributions (zero for a culled Gaussian), which the caller adds to dL/dsh.
-// The other outputs of culled Gaussians are left untouched.
+// contributions (zero for a culled Gaussian), which the caller adds to (or,
+// with OVERWRITE, writes as) dL/dsh. The other outputs are added to, or with
+// OVERWRITE written (zeros for a culled Gaussian); without OVERWRITE those of
+// culled Gaussians are left untouched.
+template <bool OVERWRITE>
 __device__ __forceinline__ void chain_rule(
     const DevCam& cam, int K, float lowpass, float near_plane, int gi,
     const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
@@ -348,6 +351,13 @@ __device__ __forceinline__ void chain_rule(
     size_t g = (size_t)gi;
     auto culled = [&]() {
         for (int k = 0; k < 3 * K; ++k) shg[k] = 0.f;
+        if (OVERWRITE) {
+            d_means[3 * g] = d_means[3 * g + 1] = d_means[3 * g + 2] = 0.f;
+            d_scales[3 * g] = d_scales[3 * g + 1] = d_scales[3 * g + 2] = 0.f;
+            reinterpret_cast<float4*>(d_quats)[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+            d_opac[g] = 0.f;
+            if (d_means2d) d_means2d[2 * g] = d_means2d[2 * g + 1] = 0.f;
+        }
     };
     if (radii[g] <= 0) return culled();
     const float4* g2 = reinterpret_cast<const float4*>(grad2d + g * GRAD2D_STRIDE);
@@ -457,29 +467,33 @@ __device__ __forceinline__ void chain_rule(
     dmu[1] += (gdir.y - dyn * dd) * id;
     dmu[2] += (gdir.z - dzn * dd) * id;
 
-    d_means[3 * g] += dmu[0];
-    d_means[3 * g + 1] += dmu[1];
-    d_means[3 * g + 2] += dmu[2];
-    d_scales[3 * g] += ds[0];
-    d_scales[3 * g + 1] += ds[1];
-    d_scales[3 * g + 2] += ds[2];
+    // prior values: zero when overwriting (the compiler drops the loads)
+    auto prior = [&](const float* p) { return OVERWRITE ? 0.f : *p; };
+    d_means[3 * g] = prior(&d_means[3 * g]) + dmu[0];
+    d_means[3 * g + 1] = prior(&d_means[3 * g + 1]) + dmu[1];
+    d_means[3 * g + 2] = prior(&d_means[3 * g + 2]) + dmu[2];
+    d_scales[3 * g] = prior(&d_scales[3 * g]) + ds[0];
+    d_scales[3 * g + 1] = prior(&d_scales[3 * g + 1]) + ds[1];
+    d_scales[3 * g + 2] = prior(&d_scales[3 * g + 2]) + ds[2];
     float4* dq = reinterpret_cast<float4*>(d_quats) + g;
-    float4 dq0 = *dq;
+    float4 dq0 = OVERWRITE ? make_float4(0.f, 0.f, 0.f, 0.f) : *dq;
     dq0.x += (gw - qdot * w) * iq;
     dq0.y += (gx - qdot * x) * iq;
     dq0.z += (gy - qdot * y) * iq;
     dq0.w += (gz - qdot * z) * iq;
     *dq = dq0;
-    d_opac[g] += d_o;
+    d_opac[g] = prior(&d_opac[g]) + d_o;
     if (d_means2d) {
-        d_means2d[2 * g] += du;
-        d_means2d[2 * g + 1] += dv;
+        d_means2d[2 * g] = prior(&d_means2d[2 * g]) + du;
+        d_means2d[2 * g + 1] = prior(&d_means2d[2 * g + 1]) + dv;
     }
 }
 
 // Chain rule, per visible Gaussian, from the summed pixel terms of the
-// backward blend to the activated parameters. Outputs accumulate (+=); the
-// SH coefficients and their gradient rows go through LDS.
+// backward blend to the activated parameters. Outputs accumulate (+=), or with
+// OVERWRITE are written for every Gaussian; the SH coefficients and their
+// gradient rows go through LDS.
+template <bool OVERWRITE>
 __global__ __launch_bounds__(64) void k_preprocess_bwd(
     DevCam cam, int K, int sh_rows, float lowpass, float near_plane, int n,
     const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
@@ -493,18 +507,27 @@ __global__ __launch_bounds__(64) void k_preprocess_bwd(
     const int gi = base + threadIdx.x;
     const bool vis = gi < n && radii[gi] > 0;
     const int nvis = __popcll(__ballot(vis));
-    if (nvis == 0) return;  // nothing of this block was drawn: no gradient
+    if (!OVERWRITE && nvis == 0) return;  // nothing of this block was drawn: no gradient
     const bool dense = nvis > SH_DENSE;
     float* shg = s_sh + threadIdx.x * stride;
     if (dense) stage_in(sh, s_sh, base, n, 3 * sh_rows, 3 * K, stride);
     else if (vis) copy_own_row(sh, shg, (size_t)gi, 3 * sh_rows, 3 * K);
     __syncthreads();
     if (gi < n)
-        chain_rule(cam, K, lowpass, near_plane, gi, means, scales, quats, shg, conic_op, radii, clamped, grad2d, d_means,
-                   d_scales, d_quats, d_opac, d_means2d);
+        chain_rule<OVERWRITE>(cam, K, lowpass, near_plane, gi, means, scales, quats, shg, conic_op, radii, clamped,
+                              grad2d, d_means, d_scales, d_quats, d_opac, d_means2d);
     __syncthreads();
-    if (dense) stage_out_add(s_sh, d_sh, base, n, 3 * sh_rows, 3 * K, stride);
-    else if (vis) add_own_row(shg, d_sh, (size_t)gi, 3 * sh_rows, 3 * K);
+    if (OVERWRITE) {
+        // every row of the block: the gradient rows (zero for culled Gaussians), then zeros
+        // for the stored rows beyond the active degree
+        stage_out(s_sh, d_sh, base, n, 3 * sh_rows, 3 * K, stride);
+        if (gi < n)
+            for (int e = 3 * K; e < 3 * sh_rows; ++e) d_sh[(size_t)gi * 3 * sh_rows + e] = 0.f;
+    } else if (dense) {
+        stage_out_add(s_sh, d_sh, base, n, 3 * sh_rows, 3 * K, stride);
+    } else if (vis) {
+        add_own_row(shg, d_sh, (size_t)gi, 3 * sh_rows, 3 * K);
+    }
 }
 
 }  // namespace
@@ -527,14 +550,15 @@ hipError_t launch_preprocess_bwd(const DevCam& cam, int K, int sh_rows, float lo
                                  const float* means, const float* scales, const float* quats, const float* sh,
                                  const float* conic_op, const int* radii, const uint8_t* clamped,
                                  const float* grad2d, float* d_means, float* d_scales, float* d_quats,
-                                 float* d_opac, float* d_sh, float* d_means2d, hipStream_t stream) {
+                                 float* d_opac, float* d_sh, float* d_means2d, bool overwrite, hipStream_t stream) {
     if (n == 0) return hipSuccess;
     int blocks = (n + 63) / 64;
     size_t lds = sizeof(float) * 64 * ((3 * K) | 1);
-    k_preprocess_bwd<<<blocks, 64, lds, stream>>>(cam, K, sh_rows, lowpass, near_plane, n, means, scales,
-                                                 reinterpret_cast<const float4*>(quats), sh,
-                                                 reinterpret_cast<const float4*>(conic_op), radii, clamped,
-                                                 grad2d, d_means, d_scales, d_quats, d_opac, d_sh, d_means2d);
+    auto kernel = overwrite ? k_preprocess_bwd<true> : k_preprocess_bwd<false>;
+    kernel<<<blocks, 64, lds, stream>>>(cam, K, sh_rows, lowpass, near_plane, n, means, scales,
+                                        reinterpret_cast<const float4*>(quats), sh,
+                                        reinterpret_cast<const float4*>(conic_op), radii, clamped, grad2d, d_means,
+                                        d_scales, d_quats, d_opac, d_sh, d_means2d);
     return hipGetLastError();
 }
 

@@ -42,7 +42,8 @@ class GsCamera(C.Structure):
 
 class GsOptions(C.Structure):
     _fields_ = [("sh_degree", C.c_int32), ("sh_rows", C.c_int32), ("tile_size", C.c_int32),
-                ("lowpass", C.c_float), ("near_plane", C.c_float), ("bg", C.c_float * 3)]
+                ("lowpass", C.c_float), ("near_plane", C.c_float), ("bg", C.c_float * 3),
+                ("overwrite_grads", C.c_int32)]
 
 
 EXPORTS = ["gs_default_options", "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_sort_workspace_size",
@@ -122,11 +123,13 @@ def make_camera(cam) -> GsCamera:
     return c
 
 
-def make_options(sh_degree=3, sh_rows=0, lowpass=0.3, near_plane=0.2, bg=(0.0, 0.0, 0.0), tile_size=16) -> GsOptions:
+def make_options(sh_degree=3, sh_rows=0, lowpass=0.3, near_plane=0.2, bg=(0.0, 0.0, 0.0), tile_size=16,
+                 overwrite_grads=False) -> GsOptions:
     o = GsOptions()
     o.sh_degree, o.sh_rows, o.tile_size = int(sh_degree), int(sh_rows), int(tile_size)
     o.lowpass, o.near_plane = float(lowpass), float(near_plane)
     o.bg = (C.c_float * 3)(*[float(x) for x in bg])
+    o.overwrite_grads = 1 if overwrite_grads else 0
     return o
 
 
@@ -322,16 +325,22 @@ class Rasterizer:
                      n_contrib)
 
     def backward(self, frame: Frame, means, scales, quats, opacities, sh, dL_dimage, grads: dict,
-                 want_means2d: bool = False):
+                 want_means2d: bool = False, overwrite: bool = False):
         """Accumulates parameter gradients into ``grads`` (keys means, scales,
-        quats, opacities, sh and optionally means2d)."""
+        quats, opacities, sh and optionally means2d), or with ``overwrite``
+        writes them (every row), so that ``grads`` need not be zeroed."""
         n = means.shape[0]
         need = gs_render_bwd_workspace_size(n)
         if self._bwd_ws is None or self._bwd_ws.numel() < need:
             self._bwd_ws = _empty(need, torch.uint8, self.device)
         if want_means2d and "means2d" not in grads:
-            grads["means2d"] = torch.zeros((n, 2), dtype=torch.float32, device=means.device)
-        gs_render_bwd(frame.cam, frame.opt, means, scales, quats, opacities, sh, frame.means2d, frame.conic_opacity,
+            grads["means2d"] = (_empty((n, 2), torch.float32, means.device) if overwrite else
+                                torch.zeros((n, 2), dtype=torch.float32, device=means.device))
+        opt = frame.opt
+        if overwrite:
+            opt = GsOptions.from_buffer_copy(frame.opt)
+            opt.overwrite_grads = 1
+        gs_render_bwd(frame.cam, opt, means, scales, quats, opacities, sh, frame.means2d, frame.conic_opacity,
                       frame.rgb, frame.radii, frame.clamped, frame.ranges, frame.values, frame.n_pairs,
                       frame.final_T, frame.n_contrib, dL_dimage, grads["means"], grads["scales"], grads["quats"],
                       grads["opacities"], grads["sh"], grads.get("means2d") if want_means2d else None,
@@ -345,6 +354,15 @@ def zero_grads(means, sh):
     return dict(means=torch.zeros((n, 3), device=dev), scales=torch.zeros((n, 3), device=dev),
                 quats=torch.zeros((n, 4), device=dev), opacities=torch.zeros(n, device=dev),
                 sh=torch.zeros_like(sh))
+
+
+def empty_grads(means, sh):
+    """Gradient buffers for a backward with overwrite=True (contents undefined)."""
+    n = means.shape[0]
+    dev = means.device
+    return dict(means=_empty((n, 3), torch.float32, dev), scales=_empty((n, 3), torch.float32, dev),
+                quats=_empty((n, 4), torch.float32, dev), opacities=_empty(n, torch.float32, dev),
+                sh=torch.empty_like(sh))
 
 
 class _RasterizeFn(torch.autograd.Function):
@@ -363,9 +381,9 @@ class _RasterizeFn(torch.autograd.Function):
         means, scales, quats, opacities, sh = ctx.saved_tensors
         frame = ctx.frame
         frame.values = ctx.values
-        grads = zero_grads(means, sh)
+        grads = empty_grads(means, sh)
         ctx.rasterizer.backward(frame, means.contiguous(), scales.contiguous(), quats.contiguous(),
-                                opacities.contiguous(), sh.contiguous(), dL_dimage.contiguous(), grads)
+                                opacities.contiguous(), sh.contiguous(), dL_dimage.contiguous(), grads, overwrite=True)
         return grads["means"], grads["scales"], grads["quats"], grads["opacities"], grads["sh"], None, None, None, \
             None, None, None
 

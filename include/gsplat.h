@@ -79,9 +79,13 @@ typedef struct gs_options {
     float lowpass;      /* added to both diagonal entries of the 2D covariance, px^2 (0.3) */
     float near_plane;   /* Gaussians with camera-space z <= near_plane are culled (0.2)   */
     float bg[3];        /* background colour, blended with the final transmittance       */
+    int32_t overwrite_grads; /* 0: the backward ADDS into the parameter gradients; 1: it
+                                WRITES them, every row (zeros for culled Gaussians and for
+                                SH rows at or beyond K), as if they had been zeroed first */
 } gs_options;
 
-/* Default options: sh_degree 3, sh_rows 0, tile 16, lowpass 0.3, near 0.2, bg 0. */
+/* Default options: sh_degree 3, sh_rows 0, tile 16, lowpass 0.3, near 0.2, bg 0,
+ * overwrite_grads 0. */
 gs_options gs_default_options(void);
 
 const char *gs_version(void);
@@ -178,10 +182,12 @@ size_t gs_render_bwd_workspace_size(int64_t n);
  *      n_contrib from gs_render_fwd, dL_dimage[3,H,W]
  * out: ACCUMULATED (+=) dL_dmeans[n,3], dL_dscales[n,3], dL_dquats[n,4],
  *      dL_dopacities[n], dL_dsh[n, sh_rows, 3] (rows < K), and, if non-NULL,
- *      dL_dmeans2d[n,2] (gradient with respect to (u, v)).
+ *      dL_dmeans2d[n,2] (gradient with respect to (u, v)); with
+ *      opt->overwrite_grads = 1 all of them are WRITTEN instead (every row).
  * ws : workspace of workspace_bytes >= gs_render_bwd_workspace_size(n)
- * The caller zeroes the gradient buffers once per step; several views
- * rendered in turn on one stream then sum their gradients.
+ * The caller zeroes the gradient buffers once per step (or renders the step's
+ * first view with overwrite_grads = 1); several views rendered in turn on one
+ * stream then sum their gradients.
  * Summation order across tiles is not fixed (atomics): results agree to
  * rounding between runs, not bit for bit.
  */
@@ -216,7 +222,8 @@ gs_status gs_render_bwd_raster(const gs_camera *cam, const gs_options *opt, int6
                                float *grad2d, void *stream);
 
 /* Chain rule from grad2d (as written by gs_render_bwd_raster) to the
- * parameters; outputs ACCUMULATE (+=) exactly as in gs_render_bwd. */
+ * parameters; outputs ACCUMULATE (+=), or are written with
+ * opt->overwrite_grads = 1, exactly as in gs_render_bwd. */
 gs_status gs_preprocess_bwd(const gs_camera *cam, const gs_options *opt, int64_t n,
                             const float *means, const float *scales, const float *quats, const float *sh,
                             const float *conic_opacity, const int32_t *radii, const uint8_t *clamped,

@@ -32,11 +32,11 @@ def test_library_exports_every_declared_function():
 
 
 def test_struct_layouts_match_header():
-    # gs_camera: 2 int32 + 4 float + 9 float + 3 float; gs_options: 3 int32 + 2 float + 3 float
+    # gs_camera: 2 int32 + 4 float + 9 float + 3 float; gs_options: 3 int32 + 2 float + 3 float + 1 int32
     assert C.sizeof(raster.GsCamera) == 4 * (2 + 4 + 9 + 3)
-    assert C.sizeof(raster.GsOptions) == 4 * (3 + 2 + 3)
+    assert C.sizeof(raster.GsOptions) == 4 * (3 + 2 + 3 + 1)
     d = raster.load_library().gs_default_options()
-    assert (d.sh_degree, d.sh_rows, d.tile_size) == (3, 0, 16)
+    assert (d.sh_degree, d.sh_rows, d.tile_size, d.overwrite_grads) == (3, 0, 16, 0)
     assert abs(d.lowpass - 0.3) < 1e-7 and abs(d.near_plane - 0.2) < 1e-7
 
 
@@ -57,6 +57,7 @@ def _cam():
     (lambda c, o: setattr(o, "near_plane", -1.0), raster.GS_ERR_INVALID_ARG),
     (lambda c, o: setattr(o, "sh_rows", 3), raster.GS_ERR_INVALID_ARG),
     (lambda c, o: setattr(o, "lowpass", float("nan")), raster.GS_ERR_INVALID_ARG),
+    (lambda c, o: setattr(o, "overwrite_grads", 2), raster.GS_ERR_INVALID_ARG),
 ])
 def test_invalid_arguments_rejected_before_launch(mutate, code):
     """Validation runs on the host and returns before any HIP call."""

@@ -304,6 +304,42 @@ def test_chain_rule_accumulates_exactly(deg):
         assert torch.equal(g[k], 2 * snap[k]), k
     if deg == 1:
         assert torch.all(g["sh"][:, 4:, :] == 0)
+    # overwrite_grads = 1 writes every row: from NaN-filled buffers it gives exactly
+    # the one-call result into zeroed buffers (zeros for culled Gaussians and for the
+    # stored SH rows beyond the active degree)
+    ow = raster.GsOptions.from_buffer_copy(fr.opt)
+    ow.overwrite_grads = 1
+    w = {k: torch.full_like(v, float("nan")) for k, v in g.items()}
+    for _ in range(2):
+        raster.gs_preprocess_bwd(fr.cam, ow, pd["means"], pd["scales"], pd["quats"], pd["sh"], fr.conic_opacity,
+                                 fr.radii, fr.clamped, grad2d, w["means"], w["scales"], w["quats"], w["opacities"],
+                                 w["sh"], w["means2d"])
+        torch.cuda.synchronize()
+        for k in g:
+            assert torch.equal(w[k], snap[k]), k
+    assert torch.any(fr.radii <= 0)
+
+
+def test_backward_overwrite_matches_accumulate_into_zeros():
+    """The whole backward with overwrite: gradient buffers full of NaN come out
+    equal (to atomic-order rounding in the pixel sums) to a backward into
+    zeroed buffers, culled Gaussians at exactly zero."""
+    sc = make_scene(5, 2, n=40_000)
+    r, pd, fr = gpu_frame(sc, 3)
+    dL = to_dev(sc.dL_dimage[3])
+    acc = raster.zero_grads(pd["means"], pd["sh"])
+    r.backward(fr, pd["means"], pd["scales"], pd["quats"], pd["opacities"], pd["sh"], dL, acc, want_means2d=True)
+    ow = {k: torch.full_like(v, float("nan")) for k, v in acc.items()}
+    r.backward(fr, pd["means"], pd["scales"], pd["quats"], pd["opacities"], pd["sh"], dL, ow, want_means2d=True,
+               overwrite=True)
+    torch.cuda.synchronize()
+    culled = (fr.radii <= 0).cpu().numpy()
+    assert culled.any() and (~culled).any()
+    for k in acc:
+        a, o = acc[k].cpu().numpy().astype(np.float64), ow[k].cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(o)), k
+        assert np.all(o[culled] == 0.0), k
+        assert rel_l2(o, a) < 1e-5, k
 
 
 def test_lower_active_sh_degree_than_stored():
