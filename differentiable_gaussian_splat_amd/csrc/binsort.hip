@@ -89,14 +89,28 @@ struct StoreInPlace {
     uint32_t* p;
     __device__ void operator()(int i, u64 pos, uint32_t) const { p[i] = (uint32_t)pos; }
 };
+// Visible Gaussian i, the pos-th in index order: its depth bits and compact
+// position (the depth sort's keys and values) and its record (index, tile
+// rectangle X0 | X1 << 16, Y0 | Y1 << 16, depth bits), read here in index
+// order so that the sorted order later gathers one 16-byte record each.
 struct StoreCompact {
     const float* depths;
+    const float2* means2d;
+    const int* radii;
+    int TX, TY;
     uint32_t* keys;
     uint32_t* idx;
+    uint4* crec;
     __device__ void operator()(int i, u64 pos, uint32_t flag) const {
         if (flag) {
-            keys[pos] = __float_as_uint(depths[i]);
-            idx[pos] = (uint32_t)i;
+            const uint32_t d = __float_as_uint(depths[i]);
+            const float2 m = means2d[i];
+            int X0, X1, Y0, Y1;
+            tile_rect(m.x, m.y, radii[i], TX, TY, X0, X1, Y0, Y1);
+            keys[pos] = d;
+            idx[pos] = (uint32_t)pos;
+            crec[pos] = make_uint4((uint32_t)i, (uint32_t)X0 | ((uint32_t)X1 << 16),
+                                   (uint32_t)Y0 | ((uint32_t)Y1 << 16), d);
         }
     }
 };
@@ -563,21 +577,16 @@ __global__ __launch_bounds__(1024) void k_pair_sum(int nb, const u64* __restrict
     }
 }
 
-// Per depth-sorted Gaussian i (one gather of its projection): its record
+// Per depth-sorted Gaussian i (one gather of its compact record): its record
 // (index, X0 | X1 << 16, Y0 | Y1 << 16, depth bits) and its super-tile count.
 __global__ __launch_bounds__(SB) void k_sorted_records(const u64* vis_ptr, const uint32_t* __restrict__ order,
-                                                     const float2* __restrict__ means2d, const int* __restrict__ radii,
-                                                     const float* __restrict__ depths, int TX, int TY,
-                                                     uint4* __restrict__ rec, uint32_t* __restrict__ n1) {
+                                                     const uint4* __restrict__ crec, uint4* __restrict__ rec,
+                                                     uint32_t* __restrict__ n1) {
     const int i = blockIdx.x * SB + threadIdx.x;
     if (i >= (int)*vis_ptr) return;
-    const uint32_t g = order[i];
-    const float2 m = means2d[g];
-    int X0, X1, Y0, Y1;
-    tile_rect(m.x, m.y, radii[g], TX, TY, X0, X1, Y0, Y1);
-    rec[i] = make_uint4(g, (uint32_t)X0 | ((uint32_t)X1 << 16), (uint32_t)Y0 | ((uint32_t)Y1 << 16),
-                        __float_as_uint(depths[g]));
-    n1[i] = super_count(X0, X1, Y0, Y1);
+    const uint4 r = crec[order[i]];
+    rec[i] = r;
+    n1[i] = super_count((int)(r.y & 0xffffu), (int)(r.y >> 16), (int)(r.z & 0xffffu), (int)(r.z >> 16));
 }
 
 // One thread per depth-sorted Gaussian: its entries (super-tile id, sorted
@@ -633,9 +642,60 @@ __device__ __forceinline__ void piece_of(int pidx, int S, const uint32_t* __rest
     e1 = min((int)r.y, e0 + PIECE);
 }
 
-// One wave per piece, lane = tile (lane & 7, lane >> 3) of the super-tile:
-// each lane's number of the piece's entries whose rectangle holds its tile,
-// to counts[pidx][lane].
+// Each lane's tiles of the super-tile at (sx0, sy0) (vw x vh of them inside
+// the grid) for its entry of group q of a piece [e0, e1): a 64-bit mask, bit
+// 8 row + column.
+__device__ __forceinline__ uint64_t entry_tiles(uint4 r, bool valid, int sx0, int sy0, int vw, int vh) {
+    const int cx0 = max((int)(r.y & 0xffffu) - sx0, 0), cx1 = min((int)(r.y >> 16) - sx0, vw - 1);
+    const int cy0 = max((int)(r.z & 0xffffu) - sy0, 0), cy1 = min((int)(r.z >> 16) - sy0, vh - 1);
+    if (!valid || cx0 > cx1 || cy0 > cy1) return 0ull;
+    const uint64_t cols = (uint64_t)(((2u << cx1) - 1u) & ~((1u << cx0) - 1u));
+    const uint64_t below_hi = cy1 == SUPER - 1 ? ~0ull : (1ull << (8 * (cy1 + 1))) - 1ull;
+    const uint64_t rows = below_hi & ~((1ull << (8 * cy0)) - 1ull) & 0x0101010101010101ull;
+    return rows * cols;
+}
+
+constexpr int PIECE_GROUPS = PIECE / 64;
+
+// A piece's records (at most PIECE_GROUPS groups of 64), all loaded up front,
+// their tile masks, and the OR of the masks over the piece.
+struct PieceTiles {
+    uint4 rq[PIECE_GROUPS];
+    uint32_t mlo[PIECE_GROUPS], mhi[PIECE_GROUPS];
+    uint64_t any;
+    int ng;
+    __device__ __forceinline__ void load(int e0, int e1, int sx0, int sy0, int vw, int vh,
+                                         const uint32_t* __restrict__ sval, const uint4* __restrict__ rec) {
+        const int lane = threadIdx.x & 63;
+        ng = (e1 - e0 + 63) / 64;
+        uint32_t gi[PIECE_GROUPS];
+#pragma unroll
+        for (int q = 0; q < PIECE_GROUPS; ++q) gi[q] = sval[min(e0 + 64 * q + lane, e1 - 1)];  // lanes past e1 repeat
+#pragma unroll
+        for (int q = 0; q < PIECE_GROUPS; ++q) rq[q] = rec[gi[q]];  // an entry; masked out below
+        uint32_t ulo = 0u, uhi = 0u;
+#pragma unroll
+        for (int q = 0; q < PIECE_GROUPS; ++q) {
+            const uint64_t mask = entry_tiles(rq[q], e0 + 64 * q + lane < e1, sx0, sy0, vw, vh);
+            mlo[q] = (uint32_t)mask;
+            mhi[q] = (uint32_t)(mask >> 32);
+            ulo |= mlo[q];
+            uhi |= mhi[q];
+        }
+        for (int off = 1; off < 64; off <<= 1) {
+            ulo |= (uint32_t)__shfl_xor((int)ulo, off);
+            uhi |= (uint32_t)__shfl_xor((int)uhi, off);
+        }
+        any = ((uint64_t)__builtin_amdgcn_readfirstlane(uhi) << 32) | __builtin_amdgcn_readfirstlane(ulo);
+    }
+    __device__ __forceinline__ bool holds(int q, int l) const {
+        return (((l < 32 ? mlo[q] : mhi[q]) >> (l & 31)) & 1u) != 0u;
+    }
+};
+
+// One wave per piece: for each tile lt of the super-tile (lane lt), the number
+// of the piece's entries whose rectangle holds it, to counts[pidx][lt]
+// (column sums of the piece's tile masks, one ballot per group and tile).
 __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int SX, int TX, int TY,
                                                  const uint32_t* __restrict__ pfirst, const uint2* __restrict__ sr,
                                                  const uint32_t* __restrict__ sval, const uint4* __restrict__ rec,
@@ -645,52 +705,50 @@ __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int
     if (pidx >= (int)*np_ptr) return;
     int s, e0, e1;
     piece_of(pidx, S, pfirst, sr, s, e0, e1);
-    const int tx = (s % SX) * SUPER + (lane & 7), ty = (s / SX) * SUPER + (lane >> 3);
-    const bool here = tx < TX && ty < TY;
+    const int sx0 = (s % SX) * SUPER, sy0 = (s / SX) * SUPER;
+    PieceTiles pt;
+    pt.load(e0, e1, sx0, sy0, min(SUPER, TX - sx0), min(SUPER, TY - sy0), sval, rec);
     uint32_t cnt = 0;
-    // the next group's records are fetched while this group is tested
-    uint2 rn = make_uint2(0u, 0u);
-    if (e0 + lane < e1) {
-        const uint4 q = rec[sval[e0 + lane]];
-        rn = make_uint2(q.y, q.z);
-    }
-    for (int eb = e0; eb < e1; eb += 64) {
-        const int ne = min(64, e1 - eb);
-        const uint2 r = rn;
-        if (eb + 64 + lane < e1) {
-            const uint4 q = rec[sval[eb + 64 + lane]];
-            rn = make_uint2(q.y, q.z);
+    uint64_t todo = pt.any;
+    while (todo) {
+        const int l = __builtin_ctzll(todo);
+        todo &= todo - 1ull;
+        uint32_t c = 0;
+#pragma unroll
+        for (int q = 0; q < PIECE_GROUPS; ++q) {
+            if (q >= pt.ng) break;
+            c += (uint32_t)__popcll(__ballot(pt.holds(q, l)));
         }
-        for (int u = 0; u < ne; ++u) {
-            const uint32_t xr = __builtin_amdgcn_readlane(r.x, u);
-            const uint32_t yr = __builtin_amdgcn_readlane(r.y, u);
-            cnt += (here && tx >= (int)(xr & 0xffffu) && tx <= (int)(xr >> 16) && ty >= (int)(yr & 0xffffu) &&
-                    ty <= (int)(yr >> 16)) ? 1u : 0u;
-        }
+        cnt = lane == l ? c : cnt;
     }
     counts[(size_t)pidx * 64 + lane] = cnt;
 }
 
 // Placement, with the roles turned: lane = entry of a 64-entry group of the
-// piece, and a uniform loop over the super-tile's tiles that some entry of
-// the group holds. Each lane holds its entry's tiles as a 64-bit mask (bit
-// 8 row + column inside the super-tile); the OR of the masks lists the tiles
-// to visit. For tile lt a ballot gives the group's entries that hold it; in
-// depth order they take the next slots of the tile's run, lane at cursor +
-// (matching lanes below it). One store instruction therefore writes
-// consecutive slots of one run. The cursors (the tile's first slot plus the
-// counts of the super-tile's earlier pieces) live one per lane, lane lt for
-// tile lt. Stores check their slot against P: always true, it keeps a broken
-// invariant from writing out of bounds.
+// piece (a piece holds at most four groups, whose records are all loaded
+// before the first store), and a uniform loop over the super-tile's tiles
+// that some entry of the piece holds. Each lane holds its entry's tiles as a
+// 64-bit mask per group (bit 8 row + column inside the super-tile); the OR of
+// the masks lists the tiles to visit. For tile lt, one ballot per group gives
+// the group's entries that hold it; in depth order (group, then lane) they
+// are packed into an LDS staging run, which the wave then writes to the
+// tile's slots with every lane busy: a store instruction costs the address
+// unit about the same whatever its active lanes, so full ones are the cheap
+// ones. The cursors (the tile's first slot plus the counts of the
+// super-tile's earlier pieces) live one per lane, lane lt for tile lt. Stores
+// check their slot against P: always true, it keeps a broken invariant from
+// writing out of bounds.
 template <bool KEYS>
 __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int S, int SX, int TX, int TY,
                                                  const uint32_t* __restrict__ pfirst, const uint2* __restrict__ sr,
                                                  const uint32_t* __restrict__ sval, const uint4* __restrict__ rec,
                                                  const uint32_t* __restrict__ offs, const uint2* __restrict__ ranges,
                                                  uint32_t P, uint32_t* __restrict__ values, u64* __restrict__ keys64) {
+    __shared__ uint2 s_stage[SB / 64][PIECE];  // per wave: (Gaussian, depth bits) of one tile's run
     const int lane = threadIdx.x & 63;
     const int pidx = __builtin_amdgcn_readfirstlane(blockIdx.x * (SB / 64) + (int)(threadIdx.x >> 6));
     if (pidx >= (int)*np_ptr) return;
+    uint2* stage = s_stage[threadIdx.x >> 6];
     int s, e0, e1;
     piece_of(pidx, S, pfirst, sr, s, e0, e1);
     const int sx0 = (s % SX) * SUPER, sy0 = (s / SX) * SUPER;
@@ -698,45 +756,35 @@ __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int S, int
     const int mtx = sx0 + (lane & 7), mty = sy0 + (lane >> 3);
     uint32_t cur = (mtx < TX && mty < TY) ? ranges[mty * TX + mtx].x + offs[(size_t)pidx * 64 + lane] : 0u;
     const uint64_t lt_mask = lanemask_lt();
-    // the next group's records are fetched while this group is placed
-    uint4 rn = make_uint4(0u, 0u, 0u, 0u);
-    if (e0 + lane < e1) rn = rec[sval[e0 + lane]];
-    for (int eb = e0; eb < e1; eb += 64) {
-        const int ne = min(64, e1 - eb);
-        const uint4 r = rn;
-        if (eb + 64 + lane < e1) rn = rec[sval[eb + 64 + lane]];
-        // this lane's tiles of the super-tile
-        uint64_t mask = 0ull;
-        if (lane < ne) {
-            const int cx0 = max((int)(r.y & 0xffffu) - sx0, 0), cx1 = min((int)(r.y >> 16) - sx0, vw - 1);
-            const int cy0 = max((int)(r.z & 0xffffu) - sy0, 0), cy1 = min((int)(r.z >> 16) - sy0, vh - 1);
-            if (cx0 <= cx1 && cy0 <= cy1) {
-                const uint64_t cols = (uint64_t)(((2u << cx1) - 1u) & ~((1u << cx0) - 1u));
-                const uint64_t below_hi = cy1 == SUPER - 1 ? ~0ull : (1ull << (8 * (cy1 + 1))) - 1ull;
-                const uint64_t rows = below_hi & ~((1ull << (8 * cy0)) - 1ull) & 0x0101010101010101ull;
-                mask = rows * cols;
-            }
-        }
-        const uint32_t mlo = (uint32_t)mask, mhi = (uint32_t)(mask >> 32);
-        uint32_t ulo = mlo, uhi = mhi;
-        for (int off = 1; off < 64; off <<= 1) {
-            ulo |= (uint32_t)__shfl_xor((int)ulo, off);
-            uhi |= (uint32_t)__shfl_xor((int)uhi, off);
-        }
-        uint64_t todo = ((uint64_t)__builtin_amdgcn_readfirstlane(uhi) << 32) | __builtin_amdgcn_readfirstlane(ulo);
-        while (todo) {
-            const int l = __builtin_ctzll(todo);
-            todo &= todo - 1ull;
-            const bool in = (((l < 32 ? mlo : mhi) >> (l & 31)) & 1u) != 0u;
+    PieceTiles pt;
+    pt.load(e0, e1, sx0, sy0, vw, vh, sval, rec);
+    uint64_t todo = pt.any;
+    while (todo) {
+        const int l = __builtin_ctzll(todo);
+        todo &= todo - 1ull;
+        // pack the piece's entries holding tile l, in depth order, into the staging run
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int q = 0; q < PIECE_GROUPS; ++q) {
+            if (q >= pt.ng) break;
+            const bool in = pt.holds(q, l);
             const uint64_t m = __ballot(in);
-            const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)cur, l);
-            const uint32_t pos = base + (uint32_t)__popcll(m & lt_mask);
-            if (in && pos < P) {
-                values[pos] = r.x;
-                if (KEYS) keys64[pos] = ((u64)(uint32_t)((sy0 + (l >> 3)) * TX + sx0 + (l & 7)) << 32) | (u64)r.w;
-            }
-            cur = lane == l ? base + (uint32_t)__popcll(m) : cur;
+            if (in) stage[cnt + (uint32_t)__popcll(m & lt_mask)] = make_uint2(pt.rq[q].x, pt.rq[q].w);
+            cnt += (uint32_t)__popcll(m);
         }
+        wave_lds_sync();
+        const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)cur, l);
+        const uint32_t tile = (uint32_t)((sy0 + (l >> 3)) * TX + sx0 + (l & 7));
+        for (uint32_t k = (uint32_t)lane; k < cnt; k += 64) {
+            const uint2 e = stage[k];
+            const uint32_t pos = base + k;
+            if (pos < P) {
+                values[pos] = e.x;
+                if (KEYS) keys64[pos] = ((u64)tile << 32) | (u64)e.y;
+            }
+        }
+        wave_lds_sync();  // the run is read before the next tile overwrites it
+        cur = lane == l ? base + cnt : cur;
     }
 }
 
@@ -811,6 +859,7 @@ BinLayout bin_layout(int64_t n, int64_t capacity, int TX, int TY) {
     L.didx[1] = take(4 * nn);
     L.first = take(4 * nn);
     L.rec = take(16 * nn);
+    L.crec = take(16 * nn);
     L.skey[0] = take(4 * cap);  // super entries: at most one per pair
     L.skey[1] = take(4 * cap);
     L.sval[0] = take(4 * cap);
@@ -858,7 +907,9 @@ hipError_t launch_bin_count(int n, int TX, int TY, const float* means2d, const i
     uint32_t* dk[2] = {reinterpret_cast<uint32_t*>(ws + L.dkeys[0]), reinterpret_cast<uint32_t*>(ws + L.dkeys[1])};
     uint32_t* di[2] = {reinterpret_cast<uint32_t*>(ws + L.didx[0]), reinterpret_cast<uint32_t*>(ws + L.didx[1])};
     // 1. visible compaction (index order kept): depth bits and indices
-    e = scan(LoadVisible{tiles_touched}, StoreCompact{depths, dk[0], di[0]}, n, nullptr, partials, &counters[0], s);
+    uint4* crec = reinterpret_cast<uint4*>(ws + L.crec);
+    e = scan(LoadVisible{tiles_touched}, StoreCompact{depths, m2, radii, TX, TY, dk[0], di[0], crec}, n, nullptr,
+             partials, &counters[0], s);
     if (e != hipSuccess) return e;
     // 2. stable sort by the 32 depth bits, 4 passes of 8: the result returns to buffer 0
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
@@ -872,7 +923,7 @@ hipError_t launch_bin_count(int n, int TX, int TY, const float* means2d, const i
     //    key buffer) and first super-tile entry
     uint32_t* first = reinterpret_cast<uint32_t*>(ws + L.first);
     uint4* rec = reinterpret_cast<uint4*>(ws + L.rec);
-    k_sorted_records<<<(n + SB - 1) / SB, SB, 0, s>>>(&counters[0], di[0], m2, radii, depths, TX, TY, rec, dk[1]);
+    k_sorted_records<<<(n + SB - 1) / SB, SB, 0, s>>>(&counters[0], di[0], crec, rec, dk[1]);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return scan(LoadPlain{dk[1]}, StoreInPlace{first}, n, &counters[0], partials, &counters[1], s);

@@ -25,6 +25,7 @@ struct BinLayout {
     size_t dkeys[2], didx[2];  // depth-sort ping-pong (n entries each)
     size_t first;              // per depth-sorted Gaussian: first super-tile entry (n)
     size_t rec;                // per depth-sorted Gaussian: uint4 record (n)
+    size_t crec;               // per visible Gaussian in index order: the same record (n)
     size_t skey[2], sval[2];   // super-tile entries (super-tile id, sorted index), ping-pong (capacity each)
     size_t sranges;            // per super-tile entry range
     size_t pfirst;             // per super-tile first piece
