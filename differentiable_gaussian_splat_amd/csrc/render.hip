@@ -27,6 +27,14 @@ namespace {
 
 constexpr int BATCH = 64;  // records staged per LDS batch
 
+// A staged record: (w0, dy0, a2, beta), (g2, log2 o, r, g), b. One LDS
+// address serves all three reads.
+struct alignas(16) Staged {
+    float4 a;
+    float4 b;
+    float4 c;  // (b, -, -, -)
+};
+
 // Tiles differ in depth by up to ~6x the mean, and the deepest band's wave
 // alone takes most of the kernel's time while it shares its SIMD with light
 // ones. Waves with long walks get a higher issue priority on their SIMD
@@ -74,16 +82,16 @@ __device__ __forceinline__ bool band_misses(float u, float v, float4 c, float lo
 // band (see band_misses).
 __device__ __forceinline__ bool stage_record(uint32_t g, const float2* __restrict__ means2d,
                                              const float4* __restrict__ conic_op, const float* __restrict__ rgb,
-                                             float4* s_a, float4* s_b, float* s_c, int lane, double ox, double oy,
+                                             Staged* s_rec, int lane, double ox, double oy,
                                              float x_lo, float x_hi, float y_lo, float y_hi) {
     const float2 m = means2d[g];
     const float4 c = conic_op[g];
     const float4 k = falloff_consts(c);
     const double ddy = oy - (double)m.y;
     const double w0 = (ox - (double)m.x) + (double)c.y * ddy;
-    s_a[lane] = make_float4((float)w0, (float)ddy, k.x, k.y);
-    s_b[lane] = make_float4(k.z, k.w, rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1]);
-    s_c[lane] = rgb[3 * (size_t)g + 2];
+    s_rec[lane].a = make_float4((float)w0, (float)ddy, k.x, k.y);
+    s_rec[lane].b = make_float4(k.z, k.w, rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1]);
+    s_rec[lane].c.x = rgb[3 * (size_t)g + 2];
     return band_misses(m.x, m.y, c, k.w, x_lo, x_hi, y_lo, y_hi);
 }
 
@@ -95,17 +103,17 @@ template <int PPL>
 __device__ __forceinline__ uint32_t stage_record_bands(uint32_t g, uint32_t pos, const uint32_t* band_last,
                                                        const float2* __restrict__ means2d,
                                                        const float4* __restrict__ conic_op,
-                                                       const float* __restrict__ rgb, float4* s_a, float4* s_b,
-                                                       float* s_c, int lane, double ox, double oy, float x_lo,
+                                                       const float* __restrict__ rgb, Staged* s_rec, int lane,
+                                                       double ox, double oy, float x_lo,
                                                        float x_hi, float y_lo) {
     const float2 m = means2d[g];
     const float4 c = conic_op[g];
     const float4 k = falloff_consts(c);
     const double ddy = oy - (double)m.y;
     const double w0 = (ox - (double)m.x) + (double)c.y * ddy;
-    s_a[lane] = make_float4((float)w0, (float)ddy, k.x, k.y);
-    s_b[lane] = make_float4(k.z, k.w, rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1]);
-    s_c[lane] = rgb[3 * (size_t)g + 2];
+    s_rec[lane].a = make_float4((float)w0, (float)ddy, k.x, k.y);
+    s_rec[lane].b = make_float4(k.z, k.w, rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1]);
+    s_rec[lane].c.x = rgb[3 * (size_t)g + 2];
     const MissTest mt(c, k.w);
     uint32_t mask = 0u;
 #pragma unroll
@@ -130,9 +138,7 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, const u
                                                  float bg0, float bg1, float bg2, float* __restrict__ image,
                                                  float* __restrict__ final_T, uint32_t* __restrict__ n_contrib) {
     constexpr int BANDS = 4 / PPL;
-    __shared__ float4 s_a[BATCH];
-    __shared__ float4 s_b[BATCH];
-    __shared__ float s_c[BATCH];
+    __shared__ Staged s_rec[BATCH];
     const int tile = blockIdx.x / BANDS, band = blockIdx.x - tile * BANDS;
     const int tx = tile % TX, ty = tile / TX;
     const int lane = threadIdx.x;
@@ -167,7 +173,7 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, const u
         const uint32_t idx = bs + lane;
         bool miss = true;
         if (idx < rg.y)
-            miss = stage_record(values[idx], means2d, conic_op, rgb, s_a, s_b, s_c, lane, ox, oy, bx_lo, bx_hi, by_lo,
+            miss = stage_record(values[idx], means2d, conic_op, rgb, s_rec, lane, ox, oy, bx_lo, bx_hi, by_lo,
                                 by_hi);
         uint64_t todo = __ballot(!miss);  // records some pixel of the band may blend, in list order
         __syncthreads();
@@ -176,9 +182,9 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, const u
             const int j = __builtin_ctzll(todo);
             todo &= todo - 1ull;
             if ((n & 7) == 0 && !walking()) break;
-            const float4 A = s_a[j];
-            const float4 B = s_b[j];
-            const float cb = s_c[j];
+            const float4 A = s_rec[j].a;
+            const float4 B = s_rec[j].b;
+            const float cb = s_rec[j].c.x;
             const float wl = A.x + lx;  // w at this lane's column, tile's first row
 #pragma unroll
             for (int k = 0; k < PPL; ++k) {
@@ -226,9 +232,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
                                                  const uint32_t* __restrict__ n_contrib,
                                                  const float* __restrict__ dL_dimage, float* __restrict__ grad2d) {
     constexpr int BANDS = 4 / PPL;
-    __shared__ float4 s_a[NB];
-    __shared__ float4 s_b[NB];
-    __shared__ float s_c[NB];
+    __shared__ Staged s_rec[NB];
     __shared__ uint32_t s_g[NB];
     __shared__ float s_part[NB * 4 * GRAD2D_N];  // [entry][row of 16 lanes][value]
     __shared__ uint32_t s_has[NB];
@@ -278,8 +282,8 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
         uint32_t bands = 0u;
         if (lane < cnt) {
             const uint32_t g = values[rg.x + lo + lane];
-            bands = stage_record_bands<PPL>(g, (uint32_t)(lo + lane), band_last, means2d, conic_op, rgb, s_a, s_b,
-                                            s_c, lane, ox, oy, bx_lo, bx_hi, by_lo);
+            bands = stage_record_bands<PPL>(g, (uint32_t)(lo + lane), band_last, means2d, conic_op, rgb, s_rec,
+                                            lane, ox, oy, bx_lo, bx_hi, by_lo);
             s_g[lane] = g;
             s_has[lane] = 0u;
         }
@@ -289,9 +293,9 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
             const int j = 63 - __builtin_clzll(todo);  // backwards through the list
             todo &= ~(1ull << j);
             const uint32_t bm = __builtin_amdgcn_readlane(bands, j);  // row bands this record may reach
-            const float4 A = s_a[j];
-            const float4 B = s_b[j];
-            const float cb = s_c[j];
+            const float4 A = s_rec[j].a;
+            const float4 B = s_rec[j].b;
+            const float cb = s_rec[j].c.x;
             const uint32_t pos = (uint32_t)(lo + j);
             const float wl = A.x + lx;  // w at this lane's column, tile's first row
             float acc[GRAD2D_N];
