@@ -226,35 +226,59 @@ hipError_t reduce_total(Load ld, int n, u64* partials, u64* total, hipStream_t s
     return hipGetLastError();
 }
 
-// Small arrays (n <= 16K): one 1024-thread block, each thread a contiguous run of <= 16.
+// Small arrays (n <= 16K): one 1024-thread block, in chunks of SC items. A
+// chunk is loaded into LDS with coalesced reads (all issued before any is
+// waited on), each thread then scans a contiguous run of SC / 1024 items.
+constexpr int SC = 8192;
+
 template <class Load, class Store>
 __global__ __launch_bounds__(1024) void k_scan_single(Load ld, Store st, int n, const u64* dcount, u64* total) {
+    constexpr int PER = SC / 1024;
+    __shared__ uint32_t s_val[SC];
     __shared__ u64 s_w[16];
     const int cnt = eff_count(n, dcount);
-    const int per = (cnt + 1023) / 1024;
-    const int b = threadIdx.x * per, e = min(cnt, b + per);
-    u64 sum = 0;
-    for (int i = b; i < e; ++i) sum += ld(i);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    u64 x = sum;
-    for (int off = 1; off < 64; off <<= 1) {
-        u64 y = __shfl_up(x, off);
-        if (lane >= off) x += y;
+    u64 carry = 0;
+    for (int c0 = 0; c0 < cnt; c0 += SC) {
+        uint32_t v[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = c0 + k * 1024 + (int)threadIdx.x;
+            v[k] = i < cnt ? ld(i) : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) s_val[k * 1024 + threadIdx.x] = v[k];
+        __syncthreads();
+        uint32_t run[PER];
+        u64 sum = 0;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            run[k] = s_val[threadIdx.x * PER + k];
+            sum += run[k];
+        }
+        u64 x = sum;
+        for (int off = 1; off < 64; off <<= 1) {
+            const u64 y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) s_w[w] = x;
+        __syncthreads();
+        u64 pre = 0, tot = 0;
+        for (int k = 0; k < 16; ++k) {
+            pre += k < w ? s_w[k] : 0ull;
+            tot += s_w[k];
+        }
+        u64 pos = carry + pre + x - sum;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = c0 + (int)threadIdx.x * PER + k;
+            if (i < cnt) st(i, pos, run[k]);
+            pos += run[k];
+        }
+        carry += tot;
+        __syncthreads();  // s_val and s_w are reused by the next chunk
     }
-    if (lane == 63) s_w[w] = x;
-    __syncthreads();
-    u64 pre = 0, tot = 0;
-    for (int k = 0; k < 16; ++k) {
-        pre += k < w ? s_w[k] : 0ull;
-        tot += s_w[k];
-    }
-    u64 run = pre + x - sum;
-    for (int i = b; i < e; ++i) {
-        const uint32_t v = ld(i);
-        st(i, run, v);
-        run += v;
-    }
-    if (threadIdx.x == 0 && total) *total = tot;
+    if (threadIdx.x == 0 && total) *total = carry;
 }
 
 template <class Load, class Store>
@@ -516,77 +540,142 @@ __device__ __forceinline__ uint32_t super_count(int X0, int X1, int Y0, int Y1) 
     return (uint32_t)(((X1 >> 3) - (X0 >> 3) + 1) * ((Y1 >> 3) - (Y0 >> 3) + 1));
 }
 
-// P = sum of tiles_touched and P1 = number of (super-tile, Gaussian) entries,
-// over all Gaussians (index order): per-block partials, then one summing block.
-constexpr int TOTALS_BLOCKS = 1024;
-
+// P = sum of tiles_touched, P1 = number of (super-tile, Gaussian) entries and
+// the number of visible Gaussians, per block of ST Gaussians (index order),
+// into part[3 b .. 3 b + 2]; k_pair_sum then totals P and P1 and scans the
+// visible counts, so that the compaction (k_scan_down with LoadVisible) runs
+// straight after it.
 __global__ __launch_bounds__(SB) void k_pair_totals(int n, const uint32_t* __restrict__ tiles,
                                                   const float2* __restrict__ means2d, const int* __restrict__ radii,
                                                   int TX, int TY, u64* __restrict__ part) {
-    __shared__ u64 s_w[2][SB / 64];
-    u64 p = 0, p1 = 0;
-    for (int i = blockIdx.x * SB + threadIdx.x; i < n; i += gridDim.x * SB) {
-        const uint32_t t = tiles[i];
-        if (t) {
+    __shared__ u64 s_w[3][SB / 64];
+    u64 p = 0, p1 = 0, v = 0;
+    const int base = blockIdx.x * ST;
+    uint32_t t[SI];
+#pragma unroll
+    for (int j = 0; j < SI; ++j) {
+        const int i = base + j * SB + threadIdx.x;
+        t[j] = i < n ? tiles[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < SI; ++j) {
+        if (t[j]) {
+            const int i = base + j * SB + threadIdx.x;
             const float2 m = means2d[i];
             int X0, X1, Y0, Y1;
             tile_rect(m.x, m.y, radii[i], TX, TY, X0, X1, Y0, Y1);
-            p += t;
+            p += t[j];
             p1 += super_count(X0, X1, Y0, Y1);
+            v += 1;
         }
     }
     for (int off = 32; off > 0; off >>= 1) {
         p += __shfl_xor(p, off);
         p1 += __shfl_xor(p1, off);
+        v += __shfl_xor(v, off);
     }
     if ((threadIdx.x & 63) == 0) {
         s_w[0][threadIdx.x >> 6] = p;
         s_w[1][threadIdx.x >> 6] = p1;
+        s_w[2][threadIdx.x >> 6] = v;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        part[2 * blockIdx.x] = s_w[0][0] + s_w[0][1] + s_w[0][2] + s_w[0][3];
-        part[2 * blockIdx.x + 1] = s_w[1][0] + s_w[1][1] + s_w[1][2] + s_w[1][3];
-    }
+    if (threadIdx.x < 3)
+        part[3 * blockIdx.x + threadIdx.x] =
+            s_w[threadIdx.x][0] + s_w[threadIdx.x][1] + s_w[threadIdx.x][2] + s_w[threadIdx.x][3];
 }
 
-__global__ __launch_bounds__(1024) void k_pair_sum(int nb, const u64* __restrict__ part, u64* __restrict__ out) {
+// One 1024-thread block: counters[2] = P, counters[3] = P1, vis_scan[b] = the
+// exclusive scan of the blocks' visible counts, counters[0] = their total;
+// also clears the radix passes' digit-total buffers (rtot_words words).
+__global__ __launch_bounds__(1024) void k_pair_sum(int nb, const u64* __restrict__ part, u64* __restrict__ vis_scan,
+                                                 u64* __restrict__ counters, uint32_t* __restrict__ rtot,
+                                                 int rtot_words) {
     __shared__ u64 s_w[2][16];
+    __shared__ u64 s_v[16];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int k = threadIdx.x; k < rtot_words; k += 1024) rtot[k] = 0u;
     u64 p = 0, p1 = 0;
     for (int i = threadIdx.x; i < nb; i += 1024) {
-        p += part[2 * i];
-        p1 += part[2 * i + 1];
+        p += part[3 * i];
+        p1 += part[3 * i + 1];
     }
     for (int off = 32; off > 0; off >>= 1) {
         p += __shfl_xor(p, off);
         p1 += __shfl_xor(p1, off);
     }
-    if ((threadIdx.x & 63) == 0) {
-        s_w[0][threadIdx.x >> 6] = p;
-        s_w[1][threadIdx.x >> 6] = p1;
+    if (lane == 0) {
+        s_w[0][w] = p;
+        s_w[1][w] = p1;
     }
-    __syncthreads();
+    // exclusive scan of the visible counts, 1024 blocks at a time
+    u64 carry = 0;
+    for (int b0 = 0; b0 < nb; b0 += 1024) {
+        const int i = b0 + threadIdx.x;
+        const u64 v = i < nb ? part[3 * i + 2] : 0ull;
+        u64 x = v;
+        for (int off = 1; off < 64; off <<= 1) {
+            const u64 y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) s_v[w] = x;
+        __syncthreads();
+        u64 pre = 0, tot = 0;
+        for (int k = 0; k < 16; ++k) {
+            pre += k < w ? s_v[k] : 0ull;
+            tot += s_v[k];
+        }
+        if (i < nb) vis_scan[i] = carry + pre + x - v;
+        carry += tot;
+        __syncthreads();
+    }
     if (threadIdx.x == 0) {
         u64 a = 0, c = 0;
-        for (int w = 0; w < 16; ++w) {
-            a += s_w[0][w];
-            c += s_w[1][w];
+        for (int k = 0; k < 16; ++k) {
+            a += s_w[0][k];
+            c += s_w[1][k];
         }
-        out[0] = a;
-        out[1] = c;
+        counters[0] = carry;
+        counters[1] = 0ull;
+        counters[2] = a;
+        counters[3] = c;
+        counters[4] = 0ull;
     }
 }
 
 // Per depth-sorted Gaussian i (one gather of its compact record): its record
-// (index, X0 | X1 << 16, Y0 | Y1 << 16, depth bits) and its super-tile count.
+// (index, X0 | X1 << 16, Y0 | Y1 << 16, depth bits) and its super-tile count
+// n1[i]; per block of ST Gaussians, the sum of the counts (the reduce step of
+// the scan that gives each Gaussian its first super-tile entry).
 __global__ __launch_bounds__(SB) void k_sorted_records(const u64* vis_ptr, const uint32_t* __restrict__ order,
                                                      const uint4* __restrict__ crec, uint4* __restrict__ rec,
-                                                     uint32_t* __restrict__ n1) {
-    const int i = blockIdx.x * SB + threadIdx.x;
-    if (i >= (int)*vis_ptr) return;
-    const uint4 r = crec[order[i]];
-    rec[i] = r;
-    n1[i] = super_count((int)(r.y & 0xffffu), (int)(r.y >> 16), (int)(r.z & 0xffffu), (int)(r.z >> 16));
+                                                     uint32_t* __restrict__ n1, u64* __restrict__ partials) {
+    __shared__ u64 s_w[SB / 64];
+    const int cnt = (int)*vis_ptr;
+    const int base = blockIdx.x * ST;
+    uint32_t o[SI];
+#pragma unroll
+    for (int j = 0; j < SI; ++j) {
+        const int i = base + j * SB + threadIdx.x;
+        o[j] = i < cnt ? order[i] : 0u;
+    }
+    u64 sum = 0;
+#pragma unroll
+    for (int j = 0; j < SI; ++j) {
+        const int i = base + j * SB + threadIdx.x;
+        if (i < cnt) {
+            const uint4 r = crec[o[j]];
+            rec[i] = r;
+            const uint32_t c = super_count((int)(r.y & 0xffffu), (int)(r.y >> 16), (int)(r.z & 0xffffu),
+                                           (int)(r.z >> 16));
+            n1[i] = c;
+            sum += c;
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = sum;
+    __syncthreads();
+    if (threadIdx.x == 0) partials[blockIdx.x] = s_w[0] + s_w[1] + s_w[2] + s_w[3];
 }
 
 // One thread per depth-sorted Gaussian: its entries (super-tile id, sorted
@@ -875,7 +964,7 @@ BinLayout bin_layout(int64_t n, int64_t capacity, int TX, int TY) {
     if (ntiles > max_scan) max_scan = ntiles;
     if (S > max_scan) max_scan = S;
     L.partials = take(8 * ((max_scan + ST - 1) / ST + 1));
-    L.pair_part = take(8 * 2 * TOTALS_BLOCKS);
+    L.pair_part = take(8 * 3 * ((nn + ST - 1) / ST));
     L.hist = take(4 * hist_entries);
     L.counters = take(8 * NCOUNTERS + 4 * 2 * RT * 256);  // counters, then the radix passes' two digit-total buffers
     L.total = off;
@@ -888,32 +977,37 @@ hipError_t launch_bin_count(int n, int TX, int TY, const float* means2d, const i
     u64* counters = reinterpret_cast<u64*>(ws + L.counters);
     u64* partials = reinterpret_cast<u64*>(ws + L.partials);
     const float2* m2 = reinterpret_cast<const float2*>(means2d);
-    // counters and both radix total buffers; the depth sort's four passes leave
-    // buffer 0 clear again for the super-tile pass of launch_bin_emit
-    hipError_t e = fill(reinterpret_cast<uint32_t*>(counters), 2 * NCOUNTERS + 2 * RT * 256, 0u, s);
-    if (e != hipSuccess) return e;
-    // the pair counts first, on their way to the host while the rest runs
-    if (n > 0) {
-        int blocks = (n + SB - 1) / SB;
-        if (blocks > TOTALS_BLOCKS) blocks = TOTALS_BLOCKS;
-        u64* part = reinterpret_cast<u64*>(ws + L.pair_part);
-        k_pair_totals<<<blocks, SB, 0, s>>>(n, tiles_touched, m2, radii, TX, TY, part);
-        k_pair_sum<<<1, 1024, 0, s>>>(blocks, part, &counters[2]);
-        e = hipGetLastError();
+    uint32_t* rtot = reinterpret_cast<uint32_t*>(ws + L.counters) + 2 * NCOUNTERS;
+    const int rtot_words = 2 * RT * 256;
+    hipError_t e = hipSuccess;
+    if (n == 0) {
+        e = fill(reinterpret_cast<uint32_t*>(counters), 2 * NCOUNTERS + rtot_words, 0u, s);
+        if (e == hipSuccess) e = hipMemcpyAsync(host_counts, &counters[2], 2 * sizeof(u64), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipEventRecord(ev, s);
+        return e;
     }
+    // the pair counts first, on their way to the host while the rest runs; the
+    // same pass counts the visible Gaussians per block for the compaction, and
+    // clears both radix total buffers (the depth sort's four passes leave
+    // buffer 0 clear again for the super-tile pass of launch_bin_emit)
+    const int nb = (n + ST - 1) / ST;
+    u64* part = reinterpret_cast<u64*>(ws + L.pair_part);
+    k_pair_totals<<<nb, SB, 0, s>>>(n, tiles_touched, m2, radii, TX, TY, part);
+    k_pair_sum<<<1, 1024, 0, s>>>(nb, part, partials, counters, rtot, rtot_words);
+    e = hipGetLastError();
     if (e == hipSuccess) e = hipMemcpyAsync(host_counts, &counters[2], 2 * sizeof(u64), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipEventRecord(ev, s);
-    if (e != hipSuccess || n == 0) return e;
+    if (e != hipSuccess) return e;
     uint32_t* dk[2] = {reinterpret_cast<uint32_t*>(ws + L.dkeys[0]), reinterpret_cast<uint32_t*>(ws + L.dkeys[1])};
     uint32_t* di[2] = {reinterpret_cast<uint32_t*>(ws + L.didx[0]), reinterpret_cast<uint32_t*>(ws + L.didx[1])};
-    // 1. visible compaction (index order kept): depth bits and indices
+    // 1. visible compaction (index order kept): depth bits, compact positions, records
     uint4* crec = reinterpret_cast<uint4*>(ws + L.crec);
-    e = scan(LoadVisible{tiles_touched}, StoreCompact{depths, m2, radii, TX, TY, dk[0], di[0], crec}, n, nullptr,
-             partials, &counters[0], s);
+    k_scan_down<LoadVisible, StoreCompact><<<nb, SB, 0, s>>>(
+        LoadVisible{tiles_touched}, StoreCompact{depths, m2, radii, TX, TY, dk[0], di[0], crec}, n, nullptr, partials);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     // 2. stable sort by the 32 depth bits, 4 passes of 8: the result returns to buffer 0
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
-    uint32_t* rtot = reinterpret_cast<uint32_t*>(ws + L.counters) + 2 * NCOUNTERS;
     for (int pass = 0; pass < 4; ++pass) {
         int c = pass & 1;
         e = radix_pass(SrcMem{dk[c], di[c]}, n, &counters[0], 8 * pass, 8, hist, rtot, pass, dk[c ^ 1], di[c ^ 1], s);
@@ -923,10 +1017,11 @@ hipError_t launch_bin_count(int n, int TX, int TY, const float* means2d, const i
     //    key buffer) and first super-tile entry
     uint32_t* first = reinterpret_cast<uint32_t*>(ws + L.first);
     uint4* rec = reinterpret_cast<uint4*>(ws + L.rec);
-    k_sorted_records<<<(n + SB - 1) / SB, SB, 0, s>>>(&counters[0], di[0], crec, rec, dk[1]);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return scan(LoadPlain{dk[1]}, StoreInPlace{first}, n, &counters[0], partials, &counters[1], s);
+    k_sorted_records<<<nb, SB, 0, s>>>(&counters[0], di[0], crec, rec, dk[1], partials);
+    k_scan_top<<<1, 1024, 0, s>>>(partials, nb, &counters[1]);
+    k_scan_down<LoadPlain, StoreInPlace><<<nb, SB, 0, s>>>(LoadPlain{dk[1]}, StoreInPlace{first}, n, &counters[0],
+                                                          partials);
+    return hipGetLastError();
 }
 
 hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const BinLayout& L,
