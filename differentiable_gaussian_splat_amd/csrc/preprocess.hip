@@ -230,7 +230,157 @@ __device__ __forceinline__ void add_own_row(const float* row, float* __restrict_
     }
 }
 
-__global__ __launch_bounds__(64) void k_preprocess(
+// SH rows move through LDS in chunks of CHUNK_K coefficients (24 floats per
+// Gaussian), so that a 64-Gaussian block needs 6.4 KB of LDS, not 12.5 KB:
+// LDS, not registers, is what limits the resident waves of these kernels.
+constexpr int CHUNK_K = 8;
+constexpr int CHUNK_F = 3 * CHUNK_K;
+constexpr int CHUNK_STRIDE = CHUNK_F + 1;  // odd: lanes reading their own row hit distinct banks
+
+// Floats [c0, c0 + used) (used <= CHUNK_F) of each of the block's records
+// (records of `rec` floats from record `base`) to LDS rows of CHUNK_STRIDE
+// floats. With 16-byte aligned pieces the wave moves them as float4s, all
+// loads issued before any is waited on; otherwise 8 records at a time.
+__device__ __forceinline__ void chunk_in(const float* __restrict__ src, float* dst, int base, int n, int rec, int c0,
+                                         int used) {
+    const int lane = threadIdx.x;
+    const int cnt = min(64, n - base);
+    const float* r0 = src + (size_t)base * rec + c0;
+    if (((rec | c0 | used) & 3) == 0 && ((uintptr_t)src & 15u) == 0) {
+        const int q = used >> 2;  // float4s per record, <= 6
+        const int total = cnt * q;
+        float4 v[6];
+#pragma unroll
+        for (int m = 0; m < 6; ++m) {
+            const int f = m * 64 + lane;
+            if (f < total) {
+                int j, c;
+                divmod_small(f, q, j, c);
+                v[m] = *reinterpret_cast<const float4*>(r0 + (size_t)j * rec + 4 * c);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 6; ++m) {
+            const int f = m * 64 + lane;
+            if (f < total) {
+                int j, c;
+                divmod_small(f, q, j, c);
+                float* d = dst + j * CHUNK_STRIDE + 4 * c;
+                d[0] = v[m].x;
+                d[1] = v[m].y;
+                d[2] = v[m].z;
+                d[3] = v[m].w;
+            }
+        }
+        return;
+    }
+    for (int j0 = 0; j0 < cnt; j0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (j0 + u < cnt && lane < used) ? r0[(size_t)(j0 + u) * rec + lane] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (j0 + u < cnt && lane < used) dst[(j0 + u) * CHUNK_STRIDE + lane] = v[u];
+    }
+}
+
+// The LDS rows back into floats [c0, c0 + used) of the records: written, or
+// with ADD added to what the records hold.
+template <bool ADD>
+__device__ __forceinline__ void chunk_out(const float* src, float* __restrict__ dst, int base, int n, int rec, int c0,
+                                          int used) {
+    const int lane = threadIdx.x;
+    const int cnt = min(64, n - base);
+    float* r0 = dst + (size_t)base * rec + c0;
+    if (((rec | c0 | used) & 3) == 0 && ((uintptr_t)dst & 15u) == 0) {
+        const int q = used >> 2;
+        const int total = cnt * q;
+        float4 v[6];
+        if (ADD) {
+#pragma unroll
+            for (int m = 0; m < 6; ++m) {
+                const int f = m * 64 + lane;
+                if (f < total) {
+                    int j, c;
+                    divmod_small(f, q, j, c);
+                    v[m] = *reinterpret_cast<const float4*>(r0 + (size_t)j * rec + 4 * c);
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 6; ++m) {
+            const int f = m * 64 + lane;
+            if (f < total) {
+                int j, c;
+                divmod_small(f, q, j, c);
+                const float* sp = src + j * CHUNK_STRIDE + 4 * c;
+                float4 w = make_float4(sp[0], sp[1], sp[2], sp[3]);
+                if (ADD) w = make_float4(v[m].x + w.x, v[m].y + w.y, v[m].z + w.z, v[m].w + w.w);
+                *reinterpret_cast<float4*>(r0 + (size_t)j * rec + 4 * c) = w;
+            }
+        }
+        return;
+    }
+    for (int j = 0; j < cnt; ++j)
+        if (lane < used) {
+            float* d = r0 + (size_t)j * rec + lane;
+            *d = (ADD ? *d : 0.f) + src[j * CHUNK_STRIDE + lane];
+        }
+}
+
+// One lane's own record: floats [c0, c0 + used) to its LDS row, and back
+// (written, or with ADD added).
+__device__ __forceinline__ void chunk_in_own(const float* __restrict__ src, float* row, size_t g, int rec, int c0,
+                                             int used) {
+    const float* r = src + g * (size_t)rec + c0;
+    if (((used & 3) == 0) && ((uintptr_t)r & 15u) == 0) {
+        for (int e = 0; e < used; e += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(r + e);
+            row[e] = v.x;
+            row[e + 1] = v.y;
+            row[e + 2] = v.z;
+            row[e + 3] = v.w;
+        }
+    } else {
+        for (int e = 0; e < used; ++e) row[e] = r[e];
+    }
+}
+
+template <bool ADD>
+__device__ __forceinline__ void chunk_out_own(const float* row, float* __restrict__ dst, size_t g, int rec, int c0,
+                                              int used) {
+    float* r = dst + g * (size_t)rec + c0;
+    if (((used & 3) == 0) && ((uintptr_t)r & 15u) == 0) {
+        for (int e = 0; e < used; e += 4) {
+            float4 v = make_float4(row[e], row[e + 1], row[e + 2], row[e + 3]);
+            if (ADD) {
+                const float4 o = *reinterpret_cast<const float4*>(r + e);
+                v = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+            }
+            *reinterpret_cast<float4*>(r + e) = v;
+        }
+    } else {
+        for (int e = 0; e < used; ++e) r[e] = (ADD ? r[e] : 0.f) + row[e];
+    }
+}
+
+// Outputs of a culled Gaussian: zero radius, no tiles, zeros elsewhere.
+__device__ __forceinline__ void write_culled(size_t g, float2* __restrict__ means2d, float* __restrict__ depths,
+                                             float4* __restrict__ conic_op, float* __restrict__ rgb_out,
+                                             int* __restrict__ radii, uint32_t* __restrict__ tiles,
+                                             uint8_t* __restrict__ clamped) {
+    means2d[g] = make_float2(0.f, 0.f);
+    depths[g] = 0.f;
+    conic_op[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+    rgb_out[3 * g] = 0.f;
+    rgb_out[3 * g + 1] = 0.f;
+    rgb_out[3 * g + 2] = 0.f;
+    radii[g] = 0;
+    tiles[g] = 0;
+    clamped[g] = 0;
+}
+
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(6))) void k_preprocess(
     DevCam cam, int K, int sh_rows, float lowpass, float near_plane, int n,
     const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
     const float* __restrict__ opac, const float* __restrict__ sh,
@@ -238,7 +388,6 @@ __global__ __launch_bounds__(64) void k_preprocess(
     float* __restrict__ rgb_out, int* __restrict__ radii, uint32_t* __restrict__ tiles,
     uint8_t* __restrict__ clamped) {
     extern __shared__ float s_sh[];
-    const int stride = (3 * K) | 1;  // odd row stride: lanes reading their own row hit distinct banks
     const int base = blockIdx.x * 64;
     const int gi = base + threadIdx.x;
     const bool live = gi < n;
@@ -284,54 +433,58 @@ __global__ __launch_bounds__(64) void k_preprocess(
             }
         }
     }
-    // the SH rows of the visible Gaussians
-    float* shg = s_sh + threadIdx.x * stride;
-    if (__popcll(__ballot(ok)) > SH_DENSE) stage_in(sh, s_sh, base, n, 3 * sh_rows, 3 * K, stride);
-    else if (ok) copy_own_row(sh, shg, g, 3 * sh_rows, 3 * K);
-    __syncthreads();
-    if (!live) return;
-    float col[3] = {0.f, 0.f, 0.f};
+    // the projection's outputs first: the SH rows staged below need the registers
+    if (live) {
+        if (ok) {
+            means2d[g] = make_float2(u, v);
+            depths[g] = geo.z;
+            conic_op[g] = make_float4(a, beta, gamma, o);
+            radii[g] = r;
+            tiles[g] = (uint32_t)((X1 - X0 + 1) * (Y1 - Y0 + 1));
+        } else {
+            write_culled(g, means2d, depths, conic_op, rgb_out, radii, tiles, clamped);
+        }
+    }
+    // colour from the SH rows of the visible Gaussians, chunk by chunk through LDS
+    float dx = mx - cam.campos[0], dy = my - cam.campos[1], dz = mz - cam.campos[2];
+    float dist = sqrtf(fmaf(dx, dx, fmaf(dy, dy, dz * dz)));
+    float id = 1.0f / dist;
+    float Y[16];
+    sh_eval(K, dx * id, dy * id, dz * id, Y);
+    float raw[3] = {0.5f, 0.5f, 0.5f};
+    float* shg = s_sh + threadIdx.x * CHUNK_STRIDE;
+    const bool dense = __popcll(__ballot(ok)) > SH_DENSE;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int k0 = c * CHUNK_K;
+        if (k0 >= K) break;
+        const int kc = min(CHUNK_K, K - k0);
+        if (c > 0) __syncthreads();  // the previous chunk has been read
+        if (dense) chunk_in(sh, s_sh, base, n, 3 * sh_rows, 3 * k0, 3 * kc);
+        else if (ok) chunk_in_own(sh, shg, g, 3 * sh_rows, 3 * k0, 3 * kc);
+        __syncthreads();
+        if (ok) {
+#pragma unroll
+            for (int k = 0; k < CHUNK_K; ++k) {
+                if (k >= kc) break;
+                raw[0] = fmaf(shg[3 * k], Y[k0 + k], raw[0]);
+                raw[1] = fmaf(shg[3 * k + 1], Y[k0 + k], raw[1]);
+                raw[2] = fmaf(shg[3 * k + 2], Y[k0 + k], raw[2]);
+            }
+        }
+    }
+    if (!ok) return;
+    if (!(dist > 0.f && finitef(raw[0]) && finitef(raw[1]) && finitef(raw[2]))) {
+        write_culled(g, means2d, depths, conic_op, rgb_out, radii, tiles, clamped);  // culled after all
+        return;
+    }
     uint8_t cl = 0;
-    if (ok) {
-        float dx = mx - cam.campos[0], dy = my - cam.campos[1], dz = mz - cam.campos[2];
-        float dist = sqrtf(fmaf(dx, dx, fmaf(dy, dy, dz * dz)));
-        float id = 1.0f / dist;
-        float Y[16];
-        sh_eval(K, dx * id, dy * id, dz * id, Y);
-        float raw[3] = {0.5f, 0.5f, 0.5f};
-        for (int k = 0; k < K; ++k) {
-            raw[0] = fmaf(shg[3 * k], Y[k], raw[0]);
-            raw[1] = fmaf(shg[3 * k + 1], Y[k], raw[1]);
-            raw[2] = fmaf(shg[3 * k + 2], Y[k], raw[2]);
-        }
-        ok = dist > 0.f && finitef(raw[0]) && finitef(raw[1]) && finitef(raw[2]);
-        for (int c = 0; c < 3; ++c) {
-            bool neg = raw[c] < 0.f;
-            cl |= (uint8_t)(neg ? (1u << c) : 0u);
-            col[c] = neg ? 0.f : raw[c];
-        }
+    for (int c = 0; c < 3; ++c) {
+        const bool neg = raw[c] < 0.f;
+        cl |= (uint8_t)(neg ? (1u << c) : 0u);
+        rgb_out[3 * g + c] = neg ? 0.f : raw[c];
     }
-    if (ok) {
-        means2d[g] = make_float2(u, v);
-        depths[g] = geo.z;
-        conic_op[g] = make_float4(a, beta, gamma, o);
-        rgb_out[3 * g] = col[0];
-        rgb_out[3 * g + 1] = col[1];
-        rgb_out[3 * g + 2] = col[2];
-        radii[g] = r;
-        tiles[g] = (uint32_t)((X1 - X0 + 1) * (Y1 - Y0 + 1));
-        clamped[g] = cl;
-    } else {
-        means2d[g] = make_float2(0.f, 0.f);
-        depths[g] = 0.f;
-        conic_op[g] = make_float4(0.f, 0.f, 0.f, 0.f);
-        rgb_out[3 * g] = 0.f;
-        rgb_out[3 * g + 1] = 0.f;
-        rgb_out[3 * g + 2] = 0.f;
-        radii[g] = 0;
-        tiles[g] = 0;
-        clamped[g] = 0;
-    }
+    clamped[g] = cl;
 }
 
 // The chain rule for Gaussian gi. shg is its SH row in LDS: the coefficients
@@ -538,7 +691,7 @@ hipError_t launch_preprocess(const DevCam& cam, int K, int sh_rows, float lowpas
                              int* radii, uint32_t* tiles, uint8_t* clamped, hipStream_t stream) {
     if (n == 0) return hipSuccess;
     int blocks = (n + 63) / 64;
-    size_t lds = sizeof(float) * 64 * ((3 * K) | 1);
+    size_t lds = sizeof(float) * 64 * CHUNK_STRIDE;
     k_preprocess<<<blocks, 64, lds, stream>>>(cam, K, sh_rows, lowpass, near_plane, n, means, scales,
                                              reinterpret_cast<const float4*>(quats), opac, sh,
                                              reinterpret_cast<float2*>(means2d), depths,
