@@ -364,10 +364,19 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
 // Measured on the contention scene (1M Gaussians, 1920x1080): the forward is
 // fastest with one pixel per lane (four band waves per tile: a band stops on
 // its own), the backward with four (one wave per tile: each band would add its
-// own atomics) and 32-record batches (half the LDS, more resident waves).
+// own atomics and its own reductions) and 32-record batches (half the LDS,
+// more resident waves). On small frames one wave per tile leaves most SIMDs
+// idle, and the backward's per-wave walk time decides: there it splits a tile
+// over two or four band waves (measured on a 128x128 frame, 64 tiles: 87 ->
+// 42 us with four; 800x800, 2500 tiles: 247 -> 228 us with two).
 constexpr int FWD_PPL = 1;
-constexpr int BWD_PPL = 4;
 constexpr int BWD_BATCH = 32;
+
+int bwd_pixels_per_lane(int ntiles) {
+    if (ntiles < 2048) return 1;
+    if (ntiles < 4096) return 2;
+    return 4;
+}
 
 hipError_t launch_render_fwd(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
                              const float* means2d, const float* conic_op, const float* rgb, const float* bg,
@@ -386,9 +395,22 @@ hipError_t launch_render_bwd(int W, int H, int TX, int TY, const uint32_t* range
                              float* grad2d, hipStream_t stream) {
     const int ntiles = TX * TY;
     if (ntiles == 0) return hipSuccess;
-    k_render_bwd<BWD_PPL, BWD_BATCH><<<ntiles * (4 / BWD_PPL), 64, 0, stream>>>(
-        W, H, TX, reinterpret_cast<const uint2*>(ranges), values, reinterpret_cast<const float2*>(means2d),
-        reinterpret_cast<const float4*>(conic_op), rgb, bg[0], bg[1], bg[2], final_T, n_contrib, dL_dimage, grad2d);
+    const uint2* rg = reinterpret_cast<const uint2*>(ranges);
+    const float2* m2 = reinterpret_cast<const float2*>(means2d);
+    const float4* co = reinterpret_cast<const float4*>(conic_op);
+    switch (bwd_pixels_per_lane(ntiles)) {
+        case 1:
+            k_render_bwd<1, BWD_BATCH><<<ntiles * 4, 64, 0, stream>>>(W, H, TX, rg, values, m2, co, rgb, bg[0], bg[1],
+                                                                     bg[2], final_T, n_contrib, dL_dimage, grad2d);
+            break;
+        case 2:
+            k_render_bwd<2, BWD_BATCH><<<ntiles * 2, 64, 0, stream>>>(W, H, TX, rg, values, m2, co, rgb, bg[0], bg[1],
+                                                                     bg[2], final_T, n_contrib, dL_dimage, grad2d);
+            break;
+        default:
+            k_render_bwd<4, BWD_BATCH><<<ntiles, 64, 0, stream>>>(W, H, TX, rg, values, m2, co, rgb, bg[0], bg[1],
+                                                                 bg[2], final_T, n_contrib, dL_dimage, grad2d);
+    }
     return hipGetLastError();
 }
 
