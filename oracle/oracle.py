@@ -281,3 +281,57 @@ def backward(params, cam, deg, fwd, dL_dimage, lowpass=0.3, near=0.2, bg=(0.0, 0
                        cam, deg, grad2d, lowpass, near)
     g["grad2d"] = grad2d
     return g
+
+
+# ---------------------------------------------------------------- phase U: the optimizer update
+
+ADAM_GROUPS = ("means", "log_scales", "quats", "opacity_logits", "sh")
+
+
+def adam_step(params, grads, exp_avg, exp_avg_sq, step, lr, beta1=0.9, beta2=0.999, eps=1e-15):
+    """Step O15 (phase U, the optimizer update the Odin page's Fig. 7 caption
+    names, with the Adam optimizer of its referee report, major comment 1), in
+    float64, plain NumPy, from the published definition of Adam.
+
+    params, exp_avg, exp_avg_sq: dicts over ADAM_GROUPS of raw parameters and
+    moments (means, log-scales, quaternions, opacity logits, SH [N, rows, 3]);
+    grads: the rasterizer's gradients keyed means, scales, quats, opacities,
+    sh, with respect to the ACTIVATED scales = exp(log_scales) and opacities =
+    sigmoid(logits); lr: dict with keys means, scales, quats, opacity, sh_dc,
+    sh_rest. Returns (params, exp_avg, exp_avg_sq, scales, opacities,
+    grad_norm), all new arrays.
+
+    Steps: chain the activated gradients to the raw ones at the parameters'
+    values before the update; per scalar m <- b1 m + (1 - b1) g,
+    v <- b2 v + (1 - b2) g^2, p <- p - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps);
+    grad_norm = L2 norm of each Gaussian's raw gradient."""
+    d = {k: np.asarray(params[k], np.float64) for k in ADAM_GROUPS}
+    scales_before = np.exp(d["log_scales"])
+    sig_before = 1.0 / (1.0 + np.exp(-d["opacity_logits"]))
+    raw = {
+        "means": np.asarray(grads["means"], np.float64),
+        "log_scales": np.asarray(grads["scales"], np.float64) * scales_before,
+        "quats": np.asarray(grads["quats"], np.float64),
+        "opacity_logits": np.asarray(grads["opacities"], np.float64) * sig_before * (1.0 - sig_before),
+        "sh": np.asarray(grads["sh"], np.float64),
+    }
+    rows = d["sh"].shape[1]
+    lr_sh = np.full((1, rows, 1), lr["sh_rest"], np.float64)
+    lr_sh[0, 0, 0] = lr["sh_dc"]
+    lrs = {"means": lr["means"], "log_scales": lr["scales"], "quats": lr["quats"], "opacity_logits": lr["opacity"],
+           "sh": lr_sh}
+    bc1 = 1.0 - beta1 ** step
+    bc2 = 1.0 - beta2 ** step
+    out_p, out_m, out_v = {}, {}, {}
+    for k in ADAM_GROUPS:
+        g = raw[k]
+        m = beta1 * np.asarray(exp_avg[k], np.float64) + (1.0 - beta1) * g
+        v = beta2 * np.asarray(exp_avg_sq[k], np.float64) + (1.0 - beta2) * g * g
+        out_p[k] = d[k] - lrs[k] * (m / bc1) / (np.sqrt(v / bc2) + eps)
+        out_m[k], out_v[k] = m, v
+    n = d["means"].shape[0]
+    norm2 = np.zeros(n)
+    for k in ADAM_GROUPS:
+        norm2 += (raw[k].reshape(n, -1) ** 2).sum(axis=1)
+    return (out_p, out_m, out_v, np.exp(out_p["log_scales"]), 1.0 / (1.0 + np.exp(-out_p["opacity_logits"])),
+            np.sqrt(norm2))

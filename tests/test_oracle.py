@@ -505,3 +505,94 @@ def test_pixel_list_variants_equal_full_image():
     g_pix = O.render_bwd_pixels(W, H, sc.n, f["ranges"], f["values"], pre["means2d"], pre["conic"], sc.opacities,
                                 pre["rgb"], sc.dL_dimage[0], pix)
     np.testing.assert_allclose(g_pix, g_full, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- O15: the optimizer update
+
+def _adam_case(n, rows, seed):
+    rng = np.random.default_rng(seed)
+    params = dict(means=rng.normal(0, 1, (n, 3)), log_scales=rng.normal(-4, 0.8, (n, 3)),
+                  quats=rng.normal(0, 1, (n, 4)), opacity_logits=rng.normal(0, 1.5, n),
+                  sh=rng.normal(0, 0.2, (n, rows, 3)))
+    return params, rng
+
+
+def _adam_grads(rng, n, rows):
+    return dict(means=rng.normal(0, 1, (n, 3)), scales=rng.normal(0, 50, (n, 3)), quats=rng.normal(0, 1, (n, 4)),
+                opacities=rng.normal(0, 1, n), sh=rng.normal(0, 0.3, (n, rows, 3)))
+
+
+LR = dict(means=1.6e-4, scales=5e-3, quats=1e-3, opacity=5e-2, sh_dc=2.5e-3, sh_rest=1.25e-4)
+
+
+def test_adam_matches_torch_optimizer_with_the_activation_chain():
+    """Three steps against torch.optim.Adam in float64 on the CPU, the raw
+    gradients from autograd through exp and sigmoid; grad_norm against the
+    autograd gradients' per-Gaussian norm."""
+    torch = pytest.importorskip("torch")
+    n, rows = 37, 4
+    params, rng = _adam_case(n, rows, 5)
+    tp = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in params.items()}
+    sh_dc = tp["sh"]  # one tensor, two learning rates: split by a gradient mask below
+    groups = [dict(params=[tp["means"]], lr=LR["means"]), dict(params=[tp["log_scales"]], lr=LR["scales"]),
+              dict(params=[tp["quats"]], lr=LR["quats"]), dict(params=[tp["opacity_logits"]], lr=LR["opacity"])]
+    # SH rows 0 and >= 1 have different rates: two copies of the SH tensor, each trained on its own rows
+    sh_a = torch.tensor(params["sh"], dtype=torch.float64, requires_grad=True)
+    sh_b = torch.tensor(params["sh"], dtype=torch.float64, requires_grad=True)
+    groups += [dict(params=[sh_a], lr=LR["sh_dc"]), dict(params=[sh_b], lr=LR["sh_rest"])]
+    opt = torch.optim.Adam(groups, betas=(0.9, 0.999), eps=1e-15)
+    m = {k: np.zeros_like(v) for k, v in params.items()}
+    v = {k: np.zeros_like(val) for k, val in params.items()}
+    cur = {k: val.copy() for k, val in params.items()}
+    row0 = torch.zeros((1, rows, 1), dtype=torch.float64)
+    row0[0, 0, 0] = 1.0
+    for step in (1, 2, 3):
+        g = _adam_grads(rng, n, rows)
+        opt.zero_grad()
+        G = {k: torch.tensor(val, dtype=torch.float64) for k, val in g.items()}
+        loss = ((tp["means"] * G["means"]).sum() + (torch.exp(tp["log_scales"]) * G["scales"]).sum() +
+                (tp["quats"] * G["quats"]).sum() + (torch.sigmoid(tp["opacity_logits"]) * G["opacities"]).sum() +
+                (sh_a * G["sh"] * row0).sum() + (sh_b * G["sh"] * (1 - row0)).sum())
+        loss.backward()
+        raw_norm = torch.sqrt(tp["means"].grad.pow(2).sum(1) + tp["log_scales"].grad.pow(2).sum(1) +
+                              tp["quats"].grad.pow(2).sum(1) + tp["opacity_logits"].grad.pow(2) +
+                              (sh_a.grad + sh_b.grad).pow(2).reshape(n, -1).sum(1)).numpy()
+        opt.step()
+        cur, m, v, scales, opac, norm = O.adam_step(cur, g, m, v, step, LR)
+        for k in ("means", "log_scales", "quats", "opacity_logits"):
+            np.testing.assert_allclose(cur[k], tp[k].detach().numpy(), rtol=1e-12, atol=1e-15)
+        sh_t = torch.where(row0.bool(), sh_a, sh_b).detach().numpy()
+        np.testing.assert_allclose(cur["sh"], sh_t, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(scales, np.exp(tp["log_scales"].detach().numpy()), rtol=1e-12)
+        np.testing.assert_allclose(norm, raw_norm, rtol=1e-12)
+    del sh_dc
+
+
+def test_adam_first_step_and_zero_gradient_closed_forms():
+    """First step from zero moments: every scalar moves by -lr g / (|g| + eps).
+    A zero gradient on zero moments moves nothing."""
+    n, rows = 9, 16
+    params, rng = _adam_case(n, rows, 6)
+    g = _adam_grads(rng, n, rows)
+    z = {k: np.zeros_like(v) for k, v in params.items()}
+    p1, m1, v1, scales, opac, norm = O.adam_step(params, g, z, z, 1, LR, eps=1e-8)
+    s0 = np.exp(params["log_scales"])
+    raw = g["means"]
+    # differences of parameters of order 1: absolute rounding ~1e-16
+    np.testing.assert_allclose(p1["means"] - params["means"], -LR["means"] * raw / (np.abs(raw) + 1e-8),
+                               rtol=1e-10, atol=1e-14)
+    raw_s = g["scales"] * s0
+    np.testing.assert_allclose(p1["log_scales"] - params["log_scales"],
+                               -LR["scales"] * raw_s / (np.abs(raw_s) + 1e-8), rtol=1e-10, atol=1e-14)
+    dsh = p1["sh"] - params["sh"]
+    np.testing.assert_allclose(dsh[:, 0], -LR["sh_dc"] * g["sh"][:, 0] / (np.abs(g["sh"][:, 0]) + 1e-8), rtol=1e-10,
+                               atol=1e-14)
+    np.testing.assert_allclose(dsh[:, 1:], -LR["sh_rest"] * g["sh"][:, 1:] / (np.abs(g["sh"][:, 1:]) + 1e-8),
+                               rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(m1["means"], 0.1 * raw, rtol=1e-14)
+    np.testing.assert_allclose(v1["means"], 0.001 * raw * raw, rtol=1e-14)
+    zg = {k: np.zeros_like(val) for k, val in g.items()}
+    p2, m2, v2, _, _, norm0 = O.adam_step(params, zg, z, z, 1, LR)
+    for k in params:
+        np.testing.assert_array_equal(p2[k], params[k])
+    assert np.all(norm0 == 0.0)
