@@ -398,6 +398,46 @@ gs_status gs_preprocess_bwd(const gs_camera* cam, const gs_options* opt, int64_t
     }
 }
 
+gs_status gs_adam_step(const gs_adam_options* opt, int64_t n, int32_t sh_rows, float* const params[5],
+                       const float* const grads[5], float* const exp_avg[5], float* const exp_avg_sq[5],
+                       float* scales, float* opacities, float* grad_norm, void* stream) {
+    try {
+        g_err[0] = 0;
+        REQUIRE_PTR(opt);
+        REQUIRE(n >= 0 && n < ((int64_t)1 << 31), "n must be in [0, 2^31), got %lld", (long long)n);
+        REQUIRE(sh_rows >= 1 && sh_rows <= 64, "sh_rows must be in [1, 64], got %d", sh_rows);
+        REQUIRE(opt->step >= 1, "step must be >= 1, got %d", opt->step);
+        REQUIRE(opt->beta1 >= 0.f && opt->beta1 < 1.f && opt->beta2 >= 0.f && opt->beta2 < 1.f,
+                "beta1 and beta2 must be in [0, 1)");
+        REQUIRE(isfinite(opt->eps) && opt->eps >= 0.f, "eps must be finite and >= 0");
+        const float lrs[6] = {opt->lr_means, opt->lr_scales, opt->lr_quats, opt->lr_opacity, opt->lr_sh_dc,
+                              opt->lr_sh_rest};
+        for (float l : lrs) REQUIRE(isfinite(l), "learning rates must be finite");
+        if (n == 0) return GS_OK;
+        REQUIRE_PTR(params);
+        REQUIRE_PTR(grads);
+        REQUIRE_PTR(exp_avg);
+        REQUIRE_PTR(exp_avg_sq);
+        REQUIRE_PTR(scales);
+        REQUIRE_PTR(opacities);
+        for (int i = 0; i < 5; ++i) {
+            REQUIRE(params[i] && grads[i] && exp_avg[i] && exp_avg_sq[i], "array %d of params/grads/state is NULL", i);
+            REQUIRE(aligned(params[i], 16) && aligned(grads[i], 16) && aligned(exp_avg[i], 16) &&
+                        aligned(exp_avg_sq[i], 16),
+                    "array %d of params/grads/state must be 16-byte aligned", i);
+        }
+        REQUIRE(aligned(scales, 16) && aligned(opacities, 16) && aligned(grad_norm, 16),
+                "scales, opacities and grad_norm must be 16-byte aligned");
+        gs::AdamLr lr{opt->lr_means, opt->lr_scales, opt->lr_quats, opt->lr_opacity, opt->lr_sh_dc, opt->lr_sh_rest};
+        return hip_check(gs::launch_adam_step(lr, opt->beta1, opt->beta2, opt->eps, opt->step, (int)n, sh_rows,
+                                              params, grads, exp_avg, exp_avg_sq, scales, opacities, grad_norm,
+                                              (hipStream_t)stream),
+                         "gs_adam_step");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_adam_step: unexpected exception");
+    }
+}
+
 gs_status gs_mb_hbm_read(const void* src, size_t bytes, float* sink, void* stream) {
     if (!src || !sink || bytes % 16 || !aligned(src, 16)) return fail(GS_ERR_INVALID_ARG, "gs_mb_hbm_read: bad args");
     return hip_check(gs::launch_mb_read(src, bytes, sink, (hipStream_t)stream), "gs_mb_hbm_read");

@@ -65,4 +65,14 @@ hipError_t launch_mb_read(const void* src, size_t bytes, float* sink, hipStream_
 hipError_t launch_mb_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_mb_atomic(float* records, int64_t n_records, int64_t n_ops, int lanes, hipStream_t stream);
 
+// Learning rates of the optimizer's parameter groups.
+struct AdamLr {
+    float means, scales, quats, opacity, sh_dc, sh_rest;
+};
+
+hipError_t launch_adam_step(const AdamLr& lr, float beta1, float beta2, float eps, int step, int n, int sh_rows,
+                            float* const params[5], const float* const grads[5], float* const m[5],
+                            float* const v[5], float* scales, float* opacities, float* grad_norm,
+                            hipStream_t stream);
+
 }  // namespace gs

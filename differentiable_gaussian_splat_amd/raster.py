@@ -46,9 +46,15 @@ class GsOptions(C.Structure):
                 ("overwrite_grads", C.c_int32)]
 
 
+class GsAdamOptions(C.Structure):
+    _fields_ = [("lr_means", C.c_float), ("lr_scales", C.c_float), ("lr_quats", C.c_float),
+                ("lr_opacity", C.c_float), ("lr_sh_dc", C.c_float), ("lr_sh_rest", C.c_float),
+                ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float), ("step", C.c_int32)]
+
+
 EXPORTS = ["gs_default_options", "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_sort_workspace_size",
            "gs_bin_sort", "gs_render_fwd", "gs_render_bwd_workspace_size", "gs_render_bwd", "gs_render_bwd_raster",
-           "gs_preprocess_bwd", "gs_mb_hbm_read", "gs_mb_hbm_copy", "gs_mb_atomic"]
+           "gs_preprocess_bwd", "gs_adam_step", "gs_mb_hbm_read", "gs_mb_hbm_copy", "gs_mb_atomic"]
 GRAD2D_STRIDE = 12
 
 _lib = None
@@ -87,6 +93,9 @@ def load_library(path: str = LIB_PATH):
         L.gs_render_bwd_raster.restype = i32
         L.gs_preprocess_bwd.argtypes = [cam, opt, i64] + [P] * 8 + [P] * 6 + [P]
         L.gs_preprocess_bwd.restype = i32
+        PP = C.POINTER(C.c_void_p)  # five device pointers
+        L.gs_adam_step.argtypes = [C.POINTER(GsAdamOptions), i64, i32, PP, PP, PP, PP, P, P, P, P]
+        L.gs_adam_step.restype = i32
         L.gs_mb_hbm_read.argtypes = [P, sz, P, P]
         L.gs_mb_hbm_read.restype = i32
         L.gs_mb_hbm_copy.argtypes = [P, P, sz, P]
@@ -208,6 +217,35 @@ def gs_preprocess_bwd(cam: GsCamera, opt: GsOptions, means, scales, quats, sh, c
                                           _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities), _p(dL_dsh),
                                           _p(dL_dmeans2d), _stream(stream))
     _check(st, "gs_preprocess_bwd")
+
+
+PARAM_GROUPS = ("means", "log_scales", "quats", "opacity_logits", "sh")
+
+
+def make_adam_options(step, lr_means=1.6e-4, lr_scales=5e-3, lr_quats=1e-3, lr_opacity=5e-2, lr_sh_dc=2.5e-3,
+                      lr_sh_rest=2.5e-3 / 20, beta1=0.9, beta2=0.999, eps=1e-15) -> GsAdamOptions:
+    o = GsAdamOptions()
+    o.lr_means, o.lr_scales, o.lr_quats, o.lr_opacity = lr_means, lr_scales, lr_quats, lr_opacity
+    o.lr_sh_dc, o.lr_sh_rest = lr_sh_dc, lr_sh_rest
+    o.beta1, o.beta2, o.eps, o.step = beta1, beta2, eps, int(step)
+    return o
+
+
+def gs_adam_step(opt: GsAdamOptions, params: dict, grads: dict, exp_avg: dict, exp_avg_sq: dict, scales,
+                 opacities, grad_norm=None, stream=None):
+    """One fused Adam update. params / exp_avg / exp_avg_sq: dicts over
+    PARAM_GROUPS (raw parameters and their moments, updated in place); grads:
+    the rasterizer's gradients keyed means, scales, quats, opacities, sh (with
+    respect to the activated scales and opacities)."""
+    n = params["means"].shape[0]
+    sh_rows = params["sh"].shape[1]
+    arr = lambda ts: (C.c_void_p * 5)(*[t.data_ptr() for t in ts])
+    gkeys = ("means", "scales", "quats", "opacities", "sh")
+    st = load_library().gs_adam_step(C.byref(opt), n, sh_rows, arr([params[k] for k in PARAM_GROUPS]),
+                                     arr([grads[k] for k in gkeys]), arr([exp_avg[k] for k in PARAM_GROUPS]),
+                                     arr([exp_avg_sq[k] for k in PARAM_GROUPS]), _p(scales), _p(opacities),
+                                     _p(grad_norm), _stream(stream))
+    _check(st, "gs_adam_step")
 
 
 def gs_mb_hbm_read(src, sink, stream=None):

@@ -231,6 +231,48 @@ gs_status gs_preprocess_bwd(const gs_camera *cam, const gs_options *opt, int64_t
                             float *dL_dopacities, float *dL_dsh, float *dL_dmeans2d, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Optimizer update (phase U)
+ * ------------------------------------------------------------------------ */
+
+/*
+ * gs_adam_step -- one Adam update of every Gaussian's raw parameters, fused
+ * with the activation chain and a per-Gaussian gradient magnitude.
+ *
+ * The Odin page names the phase (Fig. 7 caption: U, the optimizer update) and
+ * the optimizer (Adam, referee report, major comment 1), and reads a
+ * per-primitive gradient magnitude from a post-backward hook (same comment).
+ * Raw parameters (the five arrays of `params`, in this order):
+ *   means[n,3]; log_scales[n,3] (scales = exp); quats[n,4] (normalised inside
+ *   the rasterizer); opacity_logits[n] (opacities = sigmoid); sh[n,sh_rows,3].
+ * grads[5] are the rasterizer's gradients, in the same order and layouts, with
+ * respect to the ACTIVATED scales and opacities (as gs_render_bwd writes
+ * them); the call chains them to the raw ones with the parameters' values
+ * before the update: g_log_scale = g_scale * exp(log_scale),
+ * g_logit = g_opacity * sigmoid(logit) * (1 - sigmoid(logit)).
+ * Per raw scalar p with raw gradient g, at step t = opt->step (>= 1):
+ *   m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g^2;
+ *   p -= lr * (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps),
+ * with lr by group: means, log-scales, quaternions, opacity logits, SH row 0
+ * (colour DC) and SH rows >= 1. exp_avg[5] and exp_avg_sq[5] hold m and v in
+ * the parameters' layouts (zeros before the first step).
+ * out: params, exp_avg, exp_avg_sq updated in place; scales[n,3] =
+ *      exp(new log_scales) and opacities[n] = sigmoid(new logits), the next
+ *      forward's inputs; grad_norm[n] (nullable) = the L2 norm of each
+ *      Gaussian's raw gradient (all its 11 + 3 sh_rows scalars).
+ * Every pointer is 16-byte aligned; the arrays of different roles do not
+ * overlap. Deterministic except for the summation order of grad_norm.
+ */
+typedef struct gs_adam_options {
+    float lr_means, lr_scales, lr_quats, lr_opacity, lr_sh_dc, lr_sh_rest;
+    float beta1, beta2, eps; /* beta in [0, 1), eps >= 0 */
+    int32_t step;            /* t >= 1: this update's index */
+} gs_adam_options;
+
+gs_status gs_adam_step(const gs_adam_options *opt, int64_t n, int32_t sh_rows, float *const params[5],
+                       const float *const grads[5], float *const exp_avg[5], float *const exp_avg_sq[5],
+                       float *scales, float *opacities, float *grad_norm, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Measurement helpers (used by the benchmark to set the kernels against the
  * chip's measured limits; not part of the rasterizer).
  * ------------------------------------------------------------------------ */

@@ -108,3 +108,19 @@ def test_workspace_sizes_monotone():
     c = raster.gs_bin_sort_workspace_size(1000, 10_000, 2560, 2200)
     assert c > a and c % 256 == 0
     assert raster.gs_render_bwd_workspace_size(1000) >= 1000 * 12 * 4
+
+
+def test_adam_arguments_rejected_before_launch():
+    """Validation runs on the host and returns before any HIP call."""
+    L = raster.load_library()
+    P5 = C.c_void_p * 5
+    d = C.c_void_p(256)
+    five = P5(*([d] * 5))
+    for step, b1, eps in ((0, 0.9, 1e-15), (1, 1.0, 1e-15), (1, 0.9, -1.0)):
+        o = raster.make_adam_options(step, beta1=b1, eps=eps)
+        st = L.gs_adam_step(C.byref(o), 4, 16, five, five, five, five, d, d, None, None)
+        assert st == raster.GS_ERR_INVALID_ARG, (step, b1, eps)
+    o = raster.make_adam_options(1)
+    assert L.gs_adam_step(C.byref(o), 4, 0, five, five, five, five, d, d, None, None) == raster.GS_ERR_INVALID_ARG
+    assert L.gs_adam_step(C.byref(o), 0, 16, None, None, None, None, None, None, None, None) == raster.GS_OK
+
