@@ -335,3 +335,21 @@ def adam_step(params, grads, exp_avg, exp_avg_sq, step, lr, beta1=0.9, beta2=0.9
         norm2 += (raw[k].reshape(n, -1) ** 2).sum(axis=1)
     return (out_p, out_m, out_v, np.exp(out_p["log_scales"]), 1.0 / (1.0 + np.exp(-out_p["opacity_logits"])),
             np.sqrt(norm2))
+
+
+def densify_stats(grad2d, radii, grad_accum, count, max_radius):
+    """Densification statistics of one view (the inputs of the densify and
+    prune steps whose structural changes the Odin page synchronises): for
+    every Gaussian drawn in the view (radius > 0), add the norm of its
+    screen-mean gradient (dL/du, dL/dv) -- the last two of the nine pixel
+    sums of :func:`render_bwd` -- count the view, and keep the largest radius.
+    Returns new arrays."""
+    g = np.asarray(grad2d, np.float64)
+    drawn = np.asarray(radii) > 0
+    acc = np.asarray(grad_accum, np.float64).copy()
+    cnt = np.asarray(count, np.int64).copy()
+    mr = np.asarray(max_radius, np.int64).copy()
+    acc[drawn] += np.sqrt(g[drawn, 7] ** 2 + g[drawn, 8] ** 2)
+    cnt[drawn] += 1
+    mr[drawn] = np.maximum(mr[drawn], np.asarray(radii)[drawn])
+    return acc, cnt, mr

@@ -596,3 +596,35 @@ def test_adam_first_step_and_zero_gradient_closed_forms():
     for k in params:
         np.testing.assert_array_equal(p2[k], params[k])
     assert np.all(norm0 == 0.0)
+
+
+def test_densify_stats_closed_form():
+    """Two views: the screen-mean gradient (3, 4) and then (0, -2) add 5 and 2;
+    an undrawn Gaussian is left alone; the radius keeps its maximum."""
+    g1 = np.zeros((3, 9))
+    g1[0, 7:9] = (3.0, 4.0)
+    g1[1, 7:9] = (1.0, 1.0)
+    acc, cnt, mr = O.densify_stats(g1, np.array([7, 0, 2]), np.zeros(3), np.zeros(3, np.int32),
+                                   np.zeros(3, np.int32))
+    g2 = np.zeros((3, 9))
+    g2[0, 7:9] = (0.0, -2.0)
+    acc, cnt, mr = O.densify_stats(g2, np.array([4, 0, 9]), acc, cnt, mr)
+    np.testing.assert_allclose(acc, [7.0, 0.0, 0.0], rtol=1e-15)
+    np.testing.assert_array_equal(cnt, [2, 0, 2])
+    np.testing.assert_array_equal(mr, [7, 0, 9])
+
+
+def test_densify_stats_use_the_screen_mean_gradient():
+    """The statistic's vector is dL/d(u, v): the pixel sums' columns 7 and 8,
+    which the render-stage finite-difference test above pins, equal the
+    oracle's screen-mean gradient output, whose norm the statistic adds."""
+    sc = make_scene(1, 0, n=60)
+    cam = sc.cameras[0]
+    params = dict(means=sc.means, scales=sc.scales, quats=sc.quats, opacities=sc.opacities, sh=sc.sh)
+    fwd = O.forward(params, cam, sc.sh_degree)
+    g = O.backward(params, cam, sc.sh_degree, fwd, sc.dL_dimage[0])
+    acc, cnt, _ = O.densify_stats(g["grad2d"], fwd["pre"]["radii"], np.zeros(sc.n), np.zeros(sc.n, np.int32),
+                                  np.zeros(sc.n, np.int32))
+    drawn = fwd["pre"]["radii"] > 0
+    np.testing.assert_allclose(acc[drawn], np.hypot(g["means2d"][drawn, 0], g["means2d"][drawn, 1]), rtol=1e-12)
+    assert np.all(cnt == drawn)
