@@ -237,6 +237,19 @@ def main():
         raster.gs_adam_step(raster.make_adam_options(adam_step[0]), raw, grads, m_state, v_state, act_scales,
                             act_opac, gnorm)
     t_adam = timed(adam, 10)
+    # densification statistics: the chain-rule step of the last view with and without them
+    d_acc = torch.zeros(n, dtype=torch.float32, device=dev)
+    d_cnt = torch.zeros(n, dtype=torch.int32, device=dev)
+    d_mr = torch.zeros(n, dtype=torch.int32, device=dev)
+    dstats = raster.make_densify_stats(d_acc, d_cnt, d_mr)
+    cam_last = cams[views[-1]]
+
+    def chain(st):
+        raster.gs_preprocess_bwd(cam_last, opt, means, scales, quats, sh, conic, radii, clamped, grad2d,
+                                 grads["means"], grads["scales"], grads["quats"], grads["opacities"], grads["sh"],
+                                 stats=st)
+    t_chain = timed(lambda: chain(None), 5)
+    t_chain_stats = timed(lambda: chain(dstats), 5)
     adam_bytes = n * (4 * 4 * (11 + 3 * rows) + 3 * 4 * (11 + 3 * rows) + 4 * 5)
     del raw, m_state, v_state
     n_atomics = ATOMICS_PER_TILE_ENTRY * walked
@@ -293,6 +306,11 @@ def main():
             "frac_hbm_peak": round(adam_bytes / t_adam / 1e9 / HBM_PEAK_GBPS, 4),
             "note": "fused Adam update of the raw parameters with the exp / sigmoid chain and per-Gaussian "
                     "gradient norm (4 arrays read, 3 written per parameter); timed apart, not in value",
+        },
+        "densify_stats": {
+            "chain_rule_ms": round(t_chain * 1e3, 4), "chain_rule_with_stats_ms": round(t_chain_stats * 1e3, 4),
+            "note": "gs_preprocess_bwd of the last view without and with the densification statistics (12 B "
+                    "read-modify-written per drawn Gaussian); timed apart, not in value",
         },
     }
 

@@ -29,6 +29,13 @@ gs_status hip_check(hipError_t e, const char* where) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// The densification statistics' arrays, or all null when none are asked for.
+gs::DensifyStats densify_arrays(const gs_densify_stats* st) {
+    gs::DensifyStats d{nullptr, nullptr, nullptr};
+    if (st) d = gs::DensifyStats{st->grad_accum, st->count, st->max_radius};
+    return d;
+}
+
 #define REQUIRE(cond, ...)                                        \
     do {                                                          \
         if (!(cond)) return fail(GS_ERR_INVALID_ARG, __VA_ARGS__); \
@@ -269,7 +276,8 @@ gs_status gs_render_bwd(const gs_camera* cam, const gs_options* opt, int64_t n, 
                         const uint8_t* clamped, const uint32_t* ranges, const uint32_t* values, int64_t n_pairs,
                         const float* final_T, const uint32_t* n_contrib, const float* dL_dimage, float* dL_dmeans,
                         float* dL_dscales, float* dL_dquats, float* dL_dopacities, float* dL_dsh,
-                        float* dL_dmeans2d, void* workspace, size_t workspace_bytes, void* stream) {
+                        float* dL_dmeans2d, void* workspace, size_t workspace_bytes, const gs_densify_stats* stats,
+                        void* stream) {
     try {
         g_err[0] = 0;
         Checked c;
@@ -302,6 +310,8 @@ gs_status gs_render_bwd(const gs_camera* cam, const gs_options* opt, int64_t n, 
         REQUIRE(aligned(conic_opacity, 16), "conic_opacity must be 16-byte aligned");
         REQUIRE(aligned(means2d, 8) && aligned(ranges, 8), "means2d and ranges must be 8-byte aligned");
         REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
+        REQUIRE(!stats || (stats->grad_accum && stats->count && stats->max_radius),
+                "stats: grad_accum, count and max_radius must all be set");
         size_t need = gs_render_bwd_workspace_size(n);
         REQUIRE(workspace_bytes >= need, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
         hipStream_t s = (hipStream_t)stream;
@@ -319,7 +329,7 @@ gs_status gs_render_bwd(const gs_camera* cam, const gs_options* opt, int64_t n, 
         return hip_check(gs::launch_preprocess_bwd(c.cam, c.K, c.sh_rows, opt->lowpass, opt->near_plane, (int)n,
                                                    means, scales, quats, sh, conic_opacity, radii, clamped, grad2d,
                                                    dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh,
-                                                   dL_dmeans2d, opt->overwrite_grads != 0, s),
+                                                   dL_dmeans2d, opt->overwrite_grads != 0, densify_arrays(stats), s),
                          "gs_render_bwd(chain)");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_render_bwd: unexpected exception");
@@ -366,7 +376,7 @@ gs_status gs_preprocess_bwd(const gs_camera* cam, const gs_options* opt, int64_t
                             const float* scales, const float* quats, const float* sh, const float* conic_opacity,
                             const int32_t* radii, const uint8_t* clamped, const float* grad2d, float* dL_dmeans,
                             float* dL_dscales, float* dL_dquats, float* dL_dopacities, float* dL_dsh,
-                            float* dL_dmeans2d, void* stream) {
+                            float* dL_dmeans2d, const gs_densify_stats* stats, void* stream) {
     try {
         g_err[0] = 0;
         Checked c;
@@ -388,10 +398,13 @@ gs_status gs_preprocess_bwd(const gs_camera* cam, const gs_options* opt, int64_t
         REQUIRE_PTR(dL_dsh);
         REQUIRE(aligned(quats, 16) && aligned(dL_dquats, 16), "quats and dL_dquats must be 16-byte aligned");
         REQUIRE(aligned(conic_opacity, 16) && aligned(grad2d, 16), "conic_opacity and grad2d must be 16-byte aligned");
+        REQUIRE(!stats || (stats->grad_accum && stats->count && stats->max_radius),
+                "stats: grad_accum, count and max_radius must all be set");
         return hip_check(gs::launch_preprocess_bwd(c.cam, c.K, c.sh_rows, opt->lowpass, opt->near_plane, (int)n,
                                                    means, scales, quats, sh, conic_opacity, radii, clamped, grad2d,
                                                    dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh,
-                                                   dL_dmeans2d, opt->overwrite_grads != 0, (hipStream_t)stream),
+                                                   dL_dmeans2d, opt->overwrite_grads != 0, densify_arrays(stats),
+                                                   (hipStream_t)stream),
                          "gs_preprocess_bwd");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_preprocess_bwd: unexpected exception");

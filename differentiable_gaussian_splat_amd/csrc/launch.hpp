@@ -14,11 +14,19 @@ hipError_t launch_preprocess(const DevCam& cam, int K, int sh_rows, float lowpas
                              const float* sh, float* means2d, float* depths, float* conic_op, float* rgb,
                              int* radii, uint32_t* tiles, uint8_t* clamped, hipStream_t stream);
 
+// Densification statistics (all null: none).
+struct DensifyStats {
+    float* grad_accum;
+    int32_t* count;
+    int32_t* max_radius;
+};
+
 hipError_t launch_preprocess_bwd(const DevCam& cam, int K, int sh_rows, float lowpass, float near_plane, int n,
                                  const float* means, const float* scales, const float* quats, const float* sh,
                                  const float* conic_op, const int* radii, const uint8_t* clamped,
                                  const float* grad2d, float* d_means, float* d_scales, float* d_quats,
-                                 float* d_opac, float* d_sh, float* d_means2d, bool overwrite, hipStream_t stream);
+                                 float* d_opac, float* d_sh, float* d_means2d, bool overwrite,
+                                 const DensifyStats& stats, hipStream_t stream);
 
 // Binning. The workspace layout is computed by bin_layout (binsort.hip).
 struct BinLayout {

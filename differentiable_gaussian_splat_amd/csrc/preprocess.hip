@@ -500,7 +500,7 @@ __device__ __forceinline__ void chain_rule(
     float* shg, const float4* __restrict__ conic_op, const int* __restrict__ radii,
     const uint8_t* __restrict__ clamped, const float* __restrict__ grad2d,
     float* __restrict__ d_means, float* __restrict__ d_scales, float* __restrict__ d_quats,
-    float* __restrict__ d_opac, float* __restrict__ d_means2d) {
+    float* __restrict__ d_opac, float* __restrict__ d_means2d, const DensifyStats& stats) {
     size_t g = (size_t)gi;
     auto culled = [&]() {
         for (int k = 0; k < 3 * K; ++k) shg[k] = 0.f;
@@ -640,6 +640,11 @@ __device__ __forceinline__ void chain_rule(
         d_means2d[2 * g] = prior(&d_means2d[2 * g]) + du;
         d_means2d[2 * g + 1] = prior(&d_means2d[2 * g + 1]) + dv;
     }
+    if (stats.grad_accum) {  // this view's screen-mean gradient norm, count and radius
+        stats.grad_accum[g] += sqrtf(fmaf(du, du, dv * dv));
+        stats.count[g] += 1;
+        stats.max_radius[g] = max(stats.max_radius[g], radii[g]);
+    }
 }
 
 // Chain rule, per visible Gaussian, from the summed pixel terms of the
@@ -653,7 +658,7 @@ __global__ __launch_bounds__(64) void k_preprocess_bwd(
     const float* __restrict__ sh, const float4* __restrict__ conic_op, const int* __restrict__ radii,
     const uint8_t* __restrict__ clamped, const float* __restrict__ grad2d,
     float* __restrict__ d_means, float* __restrict__ d_scales, float* __restrict__ d_quats,
-    float* __restrict__ d_opac, float* __restrict__ d_sh, float* __restrict__ d_means2d) {
+    float* __restrict__ d_opac, float* __restrict__ d_sh, float* __restrict__ d_means2d, DensifyStats stats) {
     extern __shared__ float s_sh[];
     const int stride = (3 * K) | 1;
     const int base = blockIdx.x * 64;
@@ -668,7 +673,7 @@ __global__ __launch_bounds__(64) void k_preprocess_bwd(
     __syncthreads();
     if (gi < n)
         chain_rule<OVERWRITE>(cam, K, lowpass, near_plane, gi, means, scales, quats, shg, conic_op, radii, clamped,
-                              grad2d, d_means, d_scales, d_quats, d_opac, d_means2d);
+                              grad2d, d_means, d_scales, d_quats, d_opac, d_means2d, stats);
     __syncthreads();
     if (OVERWRITE) {
         // every row of the block: the gradient rows (zero for culled Gaussians), then zeros
@@ -703,7 +708,8 @@ hipError_t launch_preprocess_bwd(const DevCam& cam, int K, int sh_rows, float lo
                                  const float* means, const float* scales, const float* quats, const float* sh,
                                  const float* conic_op, const int* radii, const uint8_t* clamped,
                                  const float* grad2d, float* d_means, float* d_scales, float* d_quats,
-                                 float* d_opac, float* d_sh, float* d_means2d, bool overwrite, hipStream_t stream) {
+                                 float* d_opac, float* d_sh, float* d_means2d, bool overwrite,
+                                 const DensifyStats& stats, hipStream_t stream) {
     if (n == 0) return hipSuccess;
     int blocks = (n + 63) / 64;
     size_t lds = sizeof(float) * 64 * ((3 * K) | 1);
@@ -711,7 +717,7 @@ hipError_t launch_preprocess_bwd(const DevCam& cam, int K, int sh_rows, float lo
     kernel<<<blocks, 64, lds, stream>>>(cam, K, sh_rows, lowpass, near_plane, n, means, scales,
                                         reinterpret_cast<const float4*>(quats), sh,
                                         reinterpret_cast<const float4*>(conic_op), radii, clamped, grad2d, d_means,
-                                        d_scales, d_quats, d_opac, d_sh, d_means2d);
+                                        d_scales, d_quats, d_opac, d_sh, d_means2d, stats);
     return hipGetLastError();
 }
 

@@ -46,6 +46,20 @@ class GsOptions(C.Structure):
                 ("overwrite_grads", C.c_int32)]
 
 
+class GsDensifyStats(C.Structure):
+    _fields_ = [("grad_accum", C.c_void_p), ("count", C.c_void_p), ("max_radius", C.c_void_p)]
+
+
+def make_densify_stats(grad_accum, count, max_radius) -> GsDensifyStats:
+    """Densification statistics arrays (float32 [n], int32 [n], int32 [n]),
+    accumulated by the backward when passed as ``stats``."""
+    return GsDensifyStats(grad_accum.data_ptr(), count.data_ptr(), max_radius.data_ptr())
+
+
+def _stats(st):
+    return None if st is None else C.byref(st)
+
+
 class GsAdamOptions(C.Structure):
     _fields_ = [("lr_means", C.c_float), ("lr_scales", C.c_float), ("lr_quats", C.c_float),
                 ("lr_opacity", C.c_float), ("lr_sh_dc", C.c_float), ("lr_sh_rest", C.c_float),
@@ -86,12 +100,13 @@ def load_library(path: str = LIB_PATH):
         L.gs_render_fwd.restype = i32
         L.gs_render_bwd_workspace_size.argtypes = [i64]
         L.gs_render_bwd_workspace_size.restype = sz
+        dst = C.POINTER(GsDensifyStats)
         L.gs_render_bwd.argtypes = ([cam, opt, i64] + [P] * 5 + [P] * 5 + [P, P, i64] + [P] * 3 + [P] * 6 +
-                                    [P, sz, P])
+                                    [P, sz, dst, P])
         L.gs_render_bwd.restype = i32
         L.gs_render_bwd_raster.argtypes = [cam, opt, i64, P, P, i64] + [P] * 7 + [P]
         L.gs_render_bwd_raster.restype = i32
-        L.gs_preprocess_bwd.argtypes = [cam, opt, i64] + [P] * 8 + [P] * 6 + [P]
+        L.gs_preprocess_bwd.argtypes = [cam, opt, i64] + [P] * 8 + [P] * 6 + [dst, P]
         L.gs_preprocess_bwd.restype = i32
         PP = C.POINTER(C.c_void_p)  # five device pointers
         L.gs_adam_step.argtypes = [C.POINTER(GsAdamOptions), i64, i32, PP, PP, PP, PP, P, P, P, P]
@@ -191,13 +206,13 @@ def gs_render_bwd_workspace_size(n) -> int:
 
 def gs_render_bwd(cam: GsCamera, opt: GsOptions, means, scales, quats, opacities, sh, means2d, conic_opacity, rgb,
                   radii, clamped, ranges, values, n_pairs, final_T, n_contrib, dL_dimage, dL_dmeans, dL_dscales,
-                  dL_dquats, dL_dopacities, dL_dsh, dL_dmeans2d, workspace, stream=None):
+                  dL_dquats, dL_dopacities, dL_dsh, dL_dmeans2d, workspace, stats=None, stream=None):
     n = means.shape[0]
     st = load_library().gs_render_bwd(
         C.byref(cam), C.byref(opt), n, _p(means), _p(scales), _p(quats), _p(opacities), _p(sh), _p(means2d),
         _p(conic_opacity), _p(rgb), _p(radii), _p(clamped), _p(ranges), _p(values), n_pairs, _p(final_T),
         _p(n_contrib), _p(dL_dimage), _p(dL_dmeans), _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities), _p(dL_dsh),
-        _p(dL_dmeans2d), _p(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+        _p(dL_dmeans2d), _p(workspace), workspace.numel() * workspace.element_size(), _stats(stats), _stream(stream))
     _check(st, "gs_render_bwd")
 
 
@@ -210,12 +225,13 @@ def gs_render_bwd_raster(cam: GsCamera, opt: GsOptions, n, ranges, values, n_pai
 
 
 def gs_preprocess_bwd(cam: GsCamera, opt: GsOptions, means, scales, quats, sh, conic_opacity, radii, clamped, grad2d,
-                      dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh, dL_dmeans2d=None, stream=None):
+                      dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh, dL_dmeans2d=None, stats=None,
+                      stream=None):
     n = means.shape[0]
     st = load_library().gs_preprocess_bwd(C.byref(cam), C.byref(opt), n, _p(means), _p(scales), _p(quats), _p(sh),
                                           _p(conic_opacity), _p(radii), _p(clamped), _p(grad2d), _p(dL_dmeans),
                                           _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities), _p(dL_dsh),
-                                          _p(dL_dmeans2d), _stream(stream))
+                                          _p(dL_dmeans2d), _stats(stats), _stream(stream))
     _check(st, "gs_preprocess_bwd")
 
 
@@ -363,7 +379,7 @@ class Rasterizer:
                      n_contrib)
 
     def backward(self, frame: Frame, means, scales, quats, opacities, sh, dL_dimage, grads: dict,
-                 want_means2d: bool = False, overwrite: bool = False):
+                 want_means2d: bool = False, overwrite: bool = False, stats: GsDensifyStats | None = None):
         """Accumulates parameter gradients into ``grads`` (keys means, scales,
         quats, opacities, sh and optionally means2d), or with ``overwrite``
         writes them (every row), so that ``grads`` need not be zeroed."""
@@ -382,7 +398,7 @@ class Rasterizer:
                       frame.rgb, frame.radii, frame.clamped, frame.ranges, frame.values, frame.n_pairs,
                       frame.final_T, frame.n_contrib, dL_dimage, grads["means"], grads["scales"], grads["quats"],
                       grads["opacities"], grads["sh"], grads.get("means2d") if want_means2d else None,
-                      self._bwd_ws)
+                      self._bwd_ws, stats)
         return grads
 
 

@@ -185,12 +185,33 @@ size_t gs_render_bwd_workspace_size(int64_t n);
  *      dL_dmeans2d[n,2] (gradient with respect to (u, v)); with
  *      opt->overwrite_grads = 1 all of them are WRITTEN instead (every row).
  * ws : workspace of workspace_bytes >= gs_render_bwd_workspace_size(n)
+ * stats (nullable): densification statistics of this view, added (see
+ *      gs_densify_stats).
  * The caller zeroes the gradient buffers once per step (or renders the step's
  * first view with overwrite_grads = 1); several views rendered in turn on one
  * stream then sum their gradients.
  * Summation order across tiles is not fixed (atomics): results agree to
  * rounding between runs, not bit for bit.
  */
+/*
+ * Densification statistics (optional output of the backward): the inputs to
+ * the densify and prune steps whose structural changes the Odin page
+ * synchronises (referee report, weakest assumptions: structural versions for
+ * densification, pruning and opacity reset). For every Gaussian drawn in the
+ * view (radius > 0), per call:
+ *   grad_accum[g] += |(dL/du, dL/dv)|   (the view's screen-mean gradient norm)
+ *   count[g]      += 1
+ *   max_radius[g]  = max(max_radius[g], radius[g])
+ * The three arrays have n entries each (int32 for count and max_radius) and
+ * are the caller's to zero. Each Gaussian is updated by one thread per call:
+ * no atomics, deterministic.
+ */
+typedef struct gs_densify_stats {
+    float *grad_accum;
+    int32_t *count;
+    int32_t *max_radius;
+} gs_densify_stats;
+
 gs_status gs_render_bwd(const gs_camera *cam, const gs_options *opt, int64_t n,
                         const float *means, const float *scales, const float *quats,
                         const float *opacities, const float *sh,
@@ -200,7 +221,7 @@ gs_status gs_render_bwd(const gs_camera *cam, const gs_options *opt, int64_t n,
                         const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
                         float *dL_dmeans, float *dL_dscales, float *dL_dquats,
                         float *dL_dopacities, float *dL_dsh, float *dL_dmeans2d,
-                        void *workspace, size_t workspace_bytes, void *stream);
+                        void *workspace, size_t workspace_bytes, const gs_densify_stats *stats, void *stream);
 
 /* The two halves of gs_render_bwd, for callers that time or test them apart
  * (gs_render_bwd = gs_render_bwd_raster followed by gs_preprocess_bwd). */
@@ -228,7 +249,8 @@ gs_status gs_preprocess_bwd(const gs_camera *cam, const gs_options *opt, int64_t
                             const float *means, const float *scales, const float *quats, const float *sh,
                             const float *conic_opacity, const int32_t *radii, const uint8_t *clamped,
                             const float *grad2d, float *dL_dmeans, float *dL_dscales, float *dL_dquats,
-                            float *dL_dopacities, float *dL_dsh, float *dL_dmeans2d, void *stream);
+                            float *dL_dopacities, float *dL_dsh, float *dL_dmeans2d,
+                            const gs_densify_stats *stats, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Optimizer update (phase U)

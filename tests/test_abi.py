@@ -95,7 +95,7 @@ def test_null_pointers_and_sizes_rejected():
     assert st == raster.GS_ERR_INVALID_ARG
     # render_bwd: workspace too small
     st = L.gs_render_bwd(C.byref(cam), C.byref(opt), 100, *([d] * 12), 10, d, d, d, *([d] * 6), P(4096 * 256), 64,
-                         None)
+                         None, None)
     assert st == raster.GS_ERR_INVALID_ARG and b"workspace" in L.gs_last_error()
 
 
