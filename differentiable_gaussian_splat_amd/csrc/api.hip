@@ -92,6 +92,40 @@ gs_status check_common(const gs_camera* cam, const gs_options* opt, int64_t n, C
     return GS_OK;
 }
 
+// The cameras of a batched call: each one checked as a single view, all of
+// one image size; n is the number of Gaussians (per-view arrays hold V n).
+struct CheckedViews {
+    Checked first;
+    gs::CamSet set;
+    int V;
+};
+
+gs_status check_views(const gs_camera* cams, int32_t V, const gs_options* opt, int64_t n, CheckedViews& out) {
+    REQUIRE_PTR(cams);
+    REQUIRE(V >= 1 && V <= GS_MAX_VIEWS, "n_views must be in 1..%d, got %d", GS_MAX_VIEWS, V);
+    REQUIRE(n >= 0 && n * V < ((int64_t)1 << 31), "n x n_views must be below 2^31, got %lld x %d", (long long)n, V);
+    memset(&out.set, 0, sizeof(out.set));
+    for (int v = 0; v < V; ++v) {
+        Checked c;
+        gs_status st = check_common(&cams[v], opt, n, c);
+        if (st != GS_OK) {
+            char msg[sizeof(g_err)];
+            snprintf(msg, sizeof(msg), "%s", g_err);
+            return fail(st, "camera %d: %s", v, msg);
+        }
+        REQUIRE(cams[v].width == cams[0].width && cams[v].height == cams[0].height,
+                "all views must have one image size: camera %d is %d x %d, camera 0 %d x %d", v, cams[v].width,
+                cams[v].height, cams[0].width, cams[0].height);
+        if (v == 0) out.first = c;
+        out.set.c[v] = c.cam;
+    }
+    // one workgroup per tile and band: keep the launch's work-items below 2^32
+    REQUIRE((int64_t)V * out.first.ntiles <= ((int64_t)1 << 24), "n_views x tiles per view must be <= 2^24, got %lld",
+            (long long)V * out.first.ntiles);
+    out.V = V;
+    return GS_OK;
+}
+
 // Host side of gs_bin_sort's pair-count readback: a small pinned buffer and an
 // event per (thread, device), created on first use and kept for the process.
 struct Readback {
@@ -211,7 +245,7 @@ gs_status gs_bin_sort(const gs_camera* cam, const gs_options* opt, int64_t n, co
         st = readback_for_current_device(rb);
         if (st != GS_OK) return st;
         char* ws = reinterpret_cast<char*>(workspace);
-        st = hip_check(gs::launch_bin_count((int)n, c.cam.TX, c.cam.TY, means2d, radii, depths, tiles_touched, ws, L,
+        st = hip_check(gs::launch_bin_count((int)n, 0, c.cam.TX, c.cam.TY, means2d, radii, depths, tiles_touched, ws, L,
                                             rb->host, rb->ev, s),
                        "gs_bin_sort(count)");
         if (st != GS_OK) return st;
@@ -256,7 +290,7 @@ gs_status gs_render_fwd(const gs_camera* cam, const gs_options* opt, int64_t n, 
             REQUIRE(aligned(conic_opacity, 16), "conic_opacity must be 16-byte aligned");
         }
         REQUIRE(aligned(ranges, 8), "ranges must be 8-byte aligned");
-        return hip_check(gs::launch_render_fwd(c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
+        return hip_check(gs::launch_render_fwd(1, c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
                                                conic_opacity, rgb, opt->bg, image, final_T, n_contrib,
                                                (hipStream_t)stream),
                          "gs_render_fwd");
@@ -320,7 +354,7 @@ gs_status gs_render_bwd(const gs_camera* cam, const gs_options* opt, int64_t n, 
                        "gs_render_bwd(zero)");
         if (st != GS_OK) return st;
         if (n_pairs > 0) {
-            st = hip_check(gs::launch_render_bwd(c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
+            st = hip_check(gs::launch_render_bwd(1, c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
                                                  conic_opacity, rgb, opt->bg, final_T, n_contrib, dL_dimage, grad2d,
                                                  s),
                            "gs_render_bwd(raster)");
@@ -363,7 +397,7 @@ gs_status gs_render_bwd_raster(const gs_camera* cam, const gs_options* opt, int6
         REQUIRE(aligned(conic_opacity, 16), "conic_opacity must be 16-byte aligned");
         REQUIRE(aligned(means2d, 8) && aligned(ranges, 8), "means2d and ranges must be 8-byte aligned");
         if (n_pairs == 0) return GS_OK;
-        return hip_check(gs::launch_render_bwd(c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
+        return hip_check(gs::launch_render_bwd(1, c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
                                                conic_opacity, rgb, opt->bg, final_T, n_contrib, dL_dimage, grad2d,
                                                (hipStream_t)stream),
                          "gs_render_bwd_raster");
@@ -408,6 +442,218 @@ gs_status gs_preprocess_bwd(const gs_camera* cam, const gs_options* opt, int64_t
                          "gs_preprocess_bwd");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_preprocess_bwd: unexpected exception");
+    }
+}
+
+// ---------------------------------------------------------------- several views per launch
+
+gs_status gs_preprocess_views(const gs_camera* cams, int32_t n_views, const gs_options* opt, int64_t n,
+                              const float* means, const float* scales, const float* quats, const float* opacities,
+                              const float* sh, float* means2d, float* depths, float* conic_opacity, float* rgb,
+                              int32_t* radii, uint32_t* tiles_touched, uint8_t* clamped, uint32_t* vis_mask,
+                              void* stream) {
+    try {
+        g_err[0] = 0;
+        CheckedViews c;
+        gs_status st = check_views(cams, n_views, opt, n, c);
+        if (st != GS_OK) return st;
+        if (n == 0) return GS_OK;
+        REQUIRE_PTR(means);
+        REQUIRE_PTR(scales);
+        REQUIRE_PTR(quats);
+        REQUIRE_PTR(opacities);
+        REQUIRE_PTR(sh);
+        REQUIRE_PTR(means2d);
+        REQUIRE_PTR(depths);
+        REQUIRE_PTR(conic_opacity);
+        REQUIRE_PTR(rgb);
+        REQUIRE_PTR(radii);
+        REQUIRE_PTR(tiles_touched);
+        REQUIRE_PTR(clamped);
+        REQUIRE(aligned(quats, 16), "quats must be 16-byte aligned");
+        REQUIRE(aligned(conic_opacity, 16), "conic_opacity must be 16-byte aligned");
+        REQUIRE(aligned(means2d, 8), "means2d must be 8-byte aligned");
+        return hip_check(gs::launch_preprocess_views(c.set, c.V, c.first.K, c.first.sh_rows, opt->lowpass,
+                                                     opt->near_plane, (int)n, means, scales, quats, opacities, sh,
+                                                     means2d, depths, conic_opacity, rgb, radii, tiles_touched,
+                                                     clamped, vis_mask, (hipStream_t)stream),
+                         "gs_preprocess_views");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_preprocess_views: unexpected exception");
+    }
+}
+
+size_t gs_bin_sort_views_workspace_size(int32_t n_views, int64_t n, int64_t pair_capacity, int32_t width,
+                                        int32_t height) {
+    if (n_views < 1 || n_views > GS_MAX_VIEWS || n < 0 || pair_capacity < 0 || width <= 0 || height <= 0) return 0;
+    return gs::bin_layout(n * n_views, pair_capacity, (width + 15) / 16, n_views * ((height + 15) / 16)).total;
+}
+
+gs_status gs_bin_sort_views(const gs_camera* cams, int32_t n_views, const gs_options* opt, int64_t n,
+                            const float* means2d, const float* depths, const int32_t* radii,
+                            const uint32_t* tiles_touched, void* workspace, size_t workspace_bytes,
+                            int64_t pair_capacity, uint64_t* keys, uint32_t* values, uint32_t* ranges,
+                            int64_t* n_pairs, void* stream) {
+    try {
+        g_err[0] = 0;
+        CheckedViews c;
+        gs_status st = check_views(cams, n_views, opt, n, c);
+        if (st != GS_OK) return st;
+        REQUIRE_PTR(n_pairs);
+        REQUIRE_PTR(ranges);
+        REQUIRE(pair_capacity >= 0 && pair_capacity < ((int64_t)1 << 31), "pair_capacity must be in [0, 2^31)");
+        REQUIRE(pair_capacity == 0 || values != nullptr, "values must not be NULL");
+        const int64_t total = n * c.V;
+        const int TX = c.first.cam.TX, TY = c.first.cam.TY;
+        if (total > 0) {
+            REQUIRE_PTR(means2d);
+            REQUIRE_PTR(depths);
+            REQUIRE_PTR(radii);
+            REQUIRE_PTR(tiles_touched);
+            REQUIRE_PTR(workspace);
+            REQUIRE(aligned(means2d, 8), "means2d must be 8-byte aligned");
+            REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
+        }
+        gs::BinLayout L = gs::bin_layout(total, pair_capacity, TX, c.V * TY);
+        if (total > 0)
+            REQUIRE(workspace_bytes >= L.total, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
+        hipStream_t s = (hipStream_t)stream;
+        if (total == 0) {
+            *n_pairs = 0;
+            return hip_check(gs::launch_fill_u32(ranges, (size_t)2 * c.V * c.first.ntiles, 0u, s),
+                             "gs_bin_sort_views");
+        }
+        Readback* rb = nullptr;
+        st = readback_for_current_device(rb);
+        if (st != GS_OK) return st;
+        char* ws = reinterpret_cast<char*>(workspace);
+        st = hip_check(gs::launch_bin_count((int)total, c.V > 1 ? (int)n : 0, TX, TY, means2d, radii, depths,
+                                            tiles_touched, ws, L, rb->host, rb->ev, s),
+                       "gs_bin_sort_views(count)");
+        if (st != GS_OK) return st;
+        st = hip_check(hipEventSynchronize(rb->ev), "gs_bin_sort_views(wait)");
+        if (st != GS_OK) return st;
+        const unsigned long long P = rb->host[0], P1 = rb->host[1];
+        *n_pairs = (int64_t)P;
+        if (P >= (1ull << 31)) return fail(GS_ERR_UNSUPPORTED, "pair count %llu exceeds 2^31 - 1", P);
+        if ((int64_t)P > pair_capacity)
+            return fail(GS_ERR_CAPACITY, "pair count %llu exceeds capacity %lld", P, (long long)pair_capacity);
+        if (P1 > P) return fail(GS_ERR_HIP, "super-tile entries %llu exceed pairs %llu", P1, P);
+        return hip_check(gs::launch_bin_emit((int)total, (int)P, (int)P1, TX, c.V * TY, ws, L, keys, values, ranges,
+                                             s),
+                         "gs_bin_sort_views(emit)");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_bin_sort_views: unexpected exception");
+    }
+}
+
+gs_status gs_render_fwd_views(const gs_camera* cams, int32_t n_views, const gs_options* opt, int64_t n,
+                              const uint32_t* ranges, const uint32_t* values, int64_t n_pairs, const float* means2d,
+                              const float* conic_opacity, const float* rgb, float* image, float* final_T,
+                              uint32_t* n_contrib, void* stream) {
+    try {
+        g_err[0] = 0;
+        CheckedViews c;
+        gs_status st = check_views(cams, n_views, opt, n, c);
+        if (st != GS_OK) return st;
+        REQUIRE_PTR(ranges);
+        REQUIRE_PTR(image);
+        REQUIRE_PTR(final_T);
+        REQUIRE_PTR(n_contrib);
+        REQUIRE(n_pairs >= 0 && n_pairs < ((int64_t)1 << 31), "n_pairs must be in [0, 2^31)");
+        if (n_pairs > 0) {
+            REQUIRE(n > 0, "n_pairs > 0 needs n > 0");
+            REQUIRE_PTR(values);
+            REQUIRE_PTR(means2d);
+            REQUIRE_PTR(conic_opacity);
+            REQUIRE_PTR(rgb);
+            REQUIRE(aligned(means2d, 8), "means2d must be 8-byte aligned");
+            REQUIRE(aligned(conic_opacity, 16), "conic_opacity must be 16-byte aligned");
+        }
+        REQUIRE(aligned(ranges, 8), "ranges must be 8-byte aligned");
+        const gs::DevCam& d = c.first.cam;
+        return hip_check(gs::launch_render_fwd(c.V, d.W, d.H, d.TX, d.TY, ranges, values, means2d, conic_opacity, rgb,
+                                               opt->bg, image, final_T, n_contrib, (hipStream_t)stream),
+                         "gs_render_fwd_views");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_render_fwd_views: unexpected exception");
+    }
+}
+
+gs_status gs_render_bwd_raster_views(const gs_camera* cams, int32_t n_views, const gs_options* opt, int64_t n,
+                                     const uint32_t* ranges, const uint32_t* values, int64_t n_pairs,
+                                     const float* means2d, const float* conic_opacity, const float* rgb,
+                                     const float* final_T, const uint32_t* n_contrib, const float* dL_dimage,
+                                     float* grad2d, void* stream) {
+    try {
+        g_err[0] = 0;
+        CheckedViews c;
+        gs_status st = check_views(cams, n_views, opt, n, c);
+        if (st != GS_OK) return st;
+        if (n == 0) return GS_OK;
+        REQUIRE_PTR(ranges);
+        REQUIRE_PTR(final_T);
+        REQUIRE_PTR(n_contrib);
+        REQUIRE_PTR(dL_dimage);
+        REQUIRE_PTR(grad2d);
+        REQUIRE(n_pairs >= 0 && n_pairs < ((int64_t)1 << 31), "n_pairs must be in [0, 2^31)");
+        if (n_pairs > 0) {
+            REQUIRE_PTR(values);
+            REQUIRE_PTR(means2d);
+            REQUIRE_PTR(conic_opacity);
+            REQUIRE_PTR(rgb);
+        }
+        REQUIRE(aligned(grad2d, 16), "grad2d must be 16-byte aligned");
+        REQUIRE(aligned(conic_opacity, 16), "conic_opacity must be 16-byte aligned");
+        REQUIRE(aligned(means2d, 8) && aligned(ranges, 8), "means2d and ranges must be 8-byte aligned");
+        if (n_pairs == 0) return GS_OK;
+        const gs::DevCam& d = c.first.cam;
+        return hip_check(gs::launch_render_bwd(c.V, d.W, d.H, d.TX, d.TY, ranges, values, means2d, conic_opacity, rgb,
+                                               opt->bg, final_T, n_contrib, dL_dimage, grad2d, (hipStream_t)stream),
+                         "gs_render_bwd_raster_views");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_render_bwd_raster_views: unexpected exception");
+    }
+}
+
+gs_status gs_preprocess_bwd_views(const gs_camera* cams, int32_t n_views, const gs_options* opt, int64_t n,
+                                  const float* means, const float* scales, const float* quats, const float* sh,
+                                  const float* conic_opacity, const int32_t* radii, const uint8_t* clamped,
+                                  const float* grad2d, float* dL_dmeans, float* dL_dscales, float* dL_dquats,
+                                  float* dL_dopacities, float* dL_dsh, float* dL_dmeans2d,
+                                  const gs_densify_stats* stats, void* stream) {
+    try {
+        g_err[0] = 0;
+        CheckedViews c;
+        gs_status st = check_views(cams, n_views, opt, n, c);
+        if (st != GS_OK) return st;
+        if (n == 0) return GS_OK;
+        REQUIRE_PTR(means);
+        REQUIRE_PTR(scales);
+        REQUIRE_PTR(quats);
+        REQUIRE_PTR(sh);
+        REQUIRE_PTR(conic_opacity);
+        REQUIRE_PTR(radii);
+        REQUIRE_PTR(clamped);
+        REQUIRE_PTR(grad2d);
+        REQUIRE_PTR(dL_dmeans);
+        REQUIRE_PTR(dL_dscales);
+        REQUIRE_PTR(dL_dquats);
+        REQUIRE_PTR(dL_dopacities);
+        REQUIRE_PTR(dL_dsh);
+        REQUIRE(aligned(quats, 16) && aligned(dL_dquats, 16), "quats and dL_dquats must be 16-byte aligned");
+        REQUIRE(aligned(conic_opacity, 16) && aligned(grad2d, 16), "conic_opacity and grad2d must be 16-byte aligned");
+        REQUIRE(!stats || (stats->grad_accum && stats->count && stats->max_radius),
+                "stats: grad_accum, count and max_radius must all be set");
+        return hip_check(gs::launch_preprocess_bwd_views(c.set, c.V, c.first.K, c.first.sh_rows, opt->lowpass,
+                                                         opt->near_plane, (int)n, means, scales, quats, sh,
+                                                         conic_opacity, radii, clamped, grad2d, dL_dmeans, dL_dscales,
+                                                         dL_dquats, dL_dopacities, dL_dsh, dL_dmeans2d,
+                                                         opt->overwrite_grads != 0, densify_arrays(stats),
+                                                         (hipStream_t)stream),
+                         "gs_preprocess_bwd_views");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_preprocess_bwd_views: unexpected exception");
     }
 }
 

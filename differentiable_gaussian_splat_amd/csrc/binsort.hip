@@ -16,6 +16,10 @@
 //      or writes the Gaussian at its own cursor (second pass). Per-piece counts,
 //      their running sum per tile and a scan over tiles give the cursors, so
 //      each tile receives its Gaussians in depth order with no ranking step.
+// Several views of one image size are binned in one pass by stacking their
+// tile grids vertically: entry i of the per-view arrays (view i / n_view)
+// has its tile rectangle moved down by view x TY rows, so the tile id, and
+// with it the sort key, leads with the view and no rectangle crosses a view.
 // Radix passes rank stably with wave64 ballot matching against per-wave LDS
 // counters and stage the block in LDS so that the output is written in
 // contiguous runs. The pair counts are reduced first and copied to the host
@@ -93,11 +97,21 @@ struct StoreInPlace {
 // position (the depth sort's keys and values) and its record (index, tile
 // rectangle X0 | X1 << 16, Y0 | Y1 << 16, depth bits), read here in index
 // order so that the sorted order later gathers one 16-byte record each.
+// Tile rectangle of entry i in the stacked grid of the views (nper entries
+// and TYv tile rows per view; nper = 0 for a single view).
+__device__ __forceinline__ void stacked_rect(int i, int nper, int TX, int TYv, float2 m, int r, int& X0, int& X1,
+                                             int& Y0, int& Y1) {
+    tile_rect(m.x, m.y, r, TX, TYv, X0, X1, Y0, Y1);
+    const int yo = nper ? (int)((uint32_t)i / (uint32_t)nper) * TYv : 0;
+    Y0 += yo;
+    Y1 += yo;
+}
+
 struct StoreCompact {
     const float* depths;
     const float2* means2d;
     const int* radii;
-    int TX, TY;
+    int nper, TX, TYv;
     uint32_t* keys;
     uint32_t* idx;
     uint4* crec;
@@ -106,7 +120,7 @@ struct StoreCompact {
             const uint32_t d = __float_as_uint(depths[i]);
             const float2 m = means2d[i];
             int X0, X1, Y0, Y1;
-            tile_rect(m.x, m.y, radii[i], TX, TY, X0, X1, Y0, Y1);
+            stacked_rect(i, nper, TX, TYv, m, radii[i], X0, X1, Y0, Y1);
             keys[pos] = d;
             idx[pos] = (uint32_t)pos;
             crec[pos] = make_uint4((uint32_t)i, (uint32_t)X0 | ((uint32_t)X1 << 16),
@@ -547,7 +561,7 @@ __device__ __forceinline__ uint32_t super_count(int X0, int X1, int Y0, int Y1) 
 // straight after it.
 __global__ __launch_bounds__(SB) void k_pair_totals(int n, const uint32_t* __restrict__ tiles,
                                                   const float2* __restrict__ means2d, const int* __restrict__ radii,
-                                                  int TX, int TY, u64* __restrict__ part) {
+                                                  int nper, int TX, int TYv, u64* __restrict__ part) {
     __shared__ u64 s_w[3][SB / 64];
     u64 p = 0, p1 = 0, v = 0;
     const int base = blockIdx.x * ST;
@@ -563,7 +577,7 @@ __global__ __launch_bounds__(SB) void k_pair_totals(int n, const uint32_t* __res
             const int i = base + j * SB + threadIdx.x;
             const float2 m = means2d[i];
             int X0, X1, Y0, Y1;
-            tile_rect(m.x, m.y, radii[i], TX, TY, X0, X1, Y0, Y1);
+            stacked_rect(i, nper, TX, TYv, m, radii[i], X0, X1, Y0, Y1);
             p += t[j];
             p1 += super_count(X0, X1, Y0, Y1);
             v += 1;
@@ -971,8 +985,8 @@ BinLayout bin_layout(int64_t n, int64_t capacity, int TX, int TY) {
     return L;
 }
 
-hipError_t launch_bin_count(int n, int TX, int TY, const float* means2d, const int* radii, const float* depths,
-                            const uint32_t* tiles_touched, char* ws, const BinLayout& L,
+hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means2d, const int* radii,
+                            const float* depths, const uint32_t* tiles_touched, char* ws, const BinLayout& L,
                             unsigned long long* host_counts, hipEvent_t ev, hipStream_t s) {
     u64* counters = reinterpret_cast<u64*>(ws + L.counters);
     u64* partials = reinterpret_cast<u64*>(ws + L.partials);
@@ -992,7 +1006,7 @@ hipError_t launch_bin_count(int n, int TX, int TY, const float* means2d, const i
     // buffer 0 clear again for the super-tile pass of launch_bin_emit)
     const int nb = (n + ST - 1) / ST;
     u64* part = reinterpret_cast<u64*>(ws + L.pair_part);
-    k_pair_totals<<<nb, SB, 0, s>>>(n, tiles_touched, m2, radii, TX, TY, part);
+    k_pair_totals<<<nb, SB, 0, s>>>(n, tiles_touched, m2, radii, nper, TX, TYv, part);
     k_pair_sum<<<1, 1024, 0, s>>>(nb, part, partials, counters, rtot, rtot_words);
     e = hipGetLastError();
     if (e == hipSuccess) e = hipMemcpyAsync(host_counts, &counters[2], 2 * sizeof(u64), hipMemcpyDeviceToHost, s);
@@ -1003,7 +1017,8 @@ hipError_t launch_bin_count(int n, int TX, int TY, const float* means2d, const i
     // 1. visible compaction (index order kept): depth bits, compact positions, records
     uint4* crec = reinterpret_cast<uint4*>(ws + L.crec);
     k_scan_down<LoadVisible, StoreCompact><<<nb, SB, 0, s>>>(
-        LoadVisible{tiles_touched}, StoreCompact{depths, m2, radii, TX, TY, dk[0], di[0], crec}, n, nullptr, partials);
+        LoadVisible{tiles_touched}, StoreCompact{depths, m2, radii, nper, TX, TYv, dk[0], di[0], crec}, n, nullptr,
+        partials);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // 2. stable sort by the 32 depth bits, 4 passes of 8: the result returns to buffer 0

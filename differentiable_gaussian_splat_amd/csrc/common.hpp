@@ -35,6 +35,14 @@ struct DevCam {
     float campos[3];
 };
 
+// The cameras of one batched launch (views of one image size), passed by
+// value: a launch's view index is wave-uniform, so they are read with scalar
+// loads from the kernel arguments.
+constexpr int MAX_VIEWS = 32;
+struct CamSet {
+    DevCam c[MAX_VIEWS];
+};
+
 __device__ __forceinline__ bool finitef(float x) { return __builtin_isfinite(x); }
 
 // Tile rectangle of a Gaussian with screen mean (u, v) and integer radius r:

@@ -28,6 +28,19 @@ hipError_t launch_preprocess_bwd(const DevCam& cam, int K, int sh_rows, float lo
                                  float* d_opac, float* d_sh, float* d_means2d, bool overwrite,
                                  const DensifyStats& stats, hipStream_t stream);
 
+// The same for V views of one image size (per-view arrays of V x n entries).
+hipError_t launch_preprocess_views(const CamSet& cams, int V, int K, int sh_rows, float lowpass, float near_plane,
+                                   int n, const float* means, const float* scales, const float* quats,
+                                   const float* opac, const float* sh, float* means2d, float* depths,
+                                   float* conic_op, float* rgb, int* radii, uint32_t* tiles, uint8_t* clamped,
+                                   uint32_t* vis_mask, hipStream_t stream);
+hipError_t launch_preprocess_bwd_views(const CamSet& cams, int V, int K, int sh_rows, float lowpass, float near_plane,
+                                       int n, const float* means, const float* scales, const float* quats,
+                                       const float* sh, const float* conic_op, const int* radii,
+                                       const uint8_t* clamped, const float* grad2d, float* d_means, float* d_scales,
+                                       float* d_quats, float* d_opac, float* d_sh, float* d_means2d, bool overwrite,
+                                       const DensifyStats& stats, hipStream_t stream);
+
 // Binning. The workspace layout is computed by bin_layout (binsort.hip).
 struct BinLayout {
     size_t dkeys[2], didx[2];  // depth-sort ping-pong (n entries each)
@@ -49,25 +62,30 @@ BinLayout bin_layout(int64_t n, int64_t capacity, int TX, int TY);
 
 // Phase 1 (no host dependence): pair count P and super-tile entry count P1
 // (copied to host_counts[0..1], pinned, with `ev` recorded after the copy),
-// visible compaction, depth sort and the per-Gaussian records.
-hipError_t launch_bin_count(int n, int TX, int TY, const float* means2d, const int* radii, const float* depths,
-                            const uint32_t* tiles_touched, char* ws, const BinLayout& L,
+// visible compaction, depth sort and the per-Gaussian records. n entries; for
+// several views, nper entries per view and views stacked in a grid of TX x
+// (views * TYv) tiles (nper = 0: one view of TX x TYv tiles).
+hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means2d, const int* radii,
+                            const float* depths, const uint32_t* tiles_touched, char* ws, const BinLayout& L,
                             unsigned long long* host_counts, hipEvent_t ev, hipStream_t stream);
 // Phase 2 (P, P1 known on the host, P within capacity): the pairs in (tile,
-// depth, index) order into `values` (and the 64-bit keys if non-NULL), and ranges.
+// depth, index) order into `values` (and the 64-bit keys if non-NULL), and
+// ranges; TY is the whole (stacked) grid's tile rows.
 hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const BinLayout& L,
                            uint64_t* keys, uint32_t* values, uint32_t* ranges, hipStream_t stream);
 
 hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_t stream);
 
-hipError_t launch_render_fwd(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
-                             const float* means2d, const float* conic_op, const float* rgb, const float* bg,
-                             float* image, float* final_T, uint32_t* n_contrib, hipStream_t stream);
+// Blending of `views` views of W x H pixels (TX x TY tiles each) whose tile
+// lists are binned in one stacked grid; per-view images follow one another.
+hipError_t launch_render_fwd(int views, int W, int H, int TX, int TY, const uint32_t* ranges,
+                             const uint32_t* values, const float* means2d, const float* conic_op, const float* rgb,
+                             const float* bg, float* image, float* final_T, uint32_t* n_contrib, hipStream_t stream);
 
-hipError_t launch_render_bwd(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
-                             const float* means2d, const float* conic_op, const float* rgb, const float* bg,
-                             const float* final_T, const uint32_t* n_contrib, const float* dL_dimage,
-                             float* grad2d, hipStream_t stream);
+hipError_t launch_render_bwd(int views, int W, int H, int TX, int TY, const uint32_t* ranges,
+                             const uint32_t* values, const float* means2d, const float* conic_op, const float* rgb,
+                             const float* bg, const float* final_T, const uint32_t* n_contrib,
+                             const float* dL_dimage, float* grad2d, hipStream_t stream);
 
 hipError_t launch_mb_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_mb_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);

@@ -380,6 +380,44 @@ __device__ __forceinline__ void write_culled(size_t g, float2* __restrict__ mean
     clamped[g] = 0;
 }
 
+// Screen-space footprint of one Gaussian in one camera.
+struct Proj {
+    float u, v, depth, a, beta, gamma;
+    int r, X0, X1, Y0, Y1;
+};
+
+// The projection of one Gaussian (finite inputs) into one camera: EWA conic
+// in factored form, 3-sigma radius, tile rectangle. False when it is culled.
+__device__ __forceinline__ bool project(const DevCam& cam, float lowpass, float near_plane, float mx, float my,
+                                       float mz, float s0, float s1, float s2, float4 q, Proj& p) {
+    Geo geo;
+    if (!geometry(cam, near_plane, mx, my, mz, s0, s1, s2, q, geo)) return false;
+    // det(Sigma') = |T0 x T1|^2 + lowpass (A0 + C0) + lowpass^2
+    float dx = mx - cam.campos[0], dy = my - cam.campos[1], dz = mz - cam.campos[2];
+    float e0 = fmaf(geo.Rq[0], dx, fmaf(geo.Rq[3], dy, geo.Rq[6] * dz));
+    float e1 = fmaf(geo.Rq[1], dx, fmaf(geo.Rq[4], dy, geo.Rq[7] * dz));
+    float e2 = fmaf(geo.Rq[2], dx, fmaf(geo.Rq[5], dy, geo.Rq[8] * dz));
+    float iz = 1.0f / geo.z;
+    float kk = cam.fx * cam.fy * iz * iz * iz;
+    float c0 = kk * e0 * s1 * s2, c1 = kk * e1 * s0 * s2, c2 = kk * e2 * s0 * s1;
+    float cross2 = fmaf(c0, c0, fmaf(c1, c1, c2 * c2));
+    float A = geo.A0 + lowpass, C = geo.C0 + lowpass, B = geo.B0;
+    float det = fmaf(lowpass, geo.A0 + geo.C0 + lowpass, cross2);
+    if (!(det > 0.f && finitef(det) && C > 0.f)) return false;
+    p.a = C / det;
+    p.beta = -B / C;
+    p.gamma = 1.0f / C;
+    float half = 0.5f * (A - C);
+    float lam = 0.5f * (A + C) + sqrtf(fmaf(half, half, B * B));
+    float extent = 3.0f * sqrtf(lam);
+    p.u = fmaf(cam.fx, geo.x * iz, cam.cx);
+    p.v = fmaf(cam.fy, geo.y * iz, cam.cy);
+    p.depth = geo.z;
+    if (!(fabsf(p.u) <= BIG && fabsf(p.v) <= BIG && extent <= BIG)) return false;  // also false on NaN
+    p.r = (int)ceilf(extent);
+    return tile_rect(p.u, p.v, p.r, cam.TX, cam.TY, p.X0, p.X1, p.Y0, p.Y1);
+}
+
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(6))) void k_preprocess(
     DevCam cam, int K, int sh_rows, float lowpass, float near_plane, int n,
     const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
@@ -399,48 +437,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(6))) void k_
 
     bool ok = live && finitef(mx) && finitef(my) && finitef(mz) && finitef(s0) && finitef(s1) && finitef(s2) &&
               finitef(q.x) && finitef(q.y) && finitef(q.z) && finitef(q.w) && finitef(o);
-    Geo geo;
-    ok = ok && geometry(cam, near_plane, mx, my, mz, s0, s1, s2, q, geo);
-
-    float u = 0.f, v = 0.f, a = 0.f, beta = 0.f, gamma = 0.f;
-    int r = 0, X0 = 0, X1 = -1, Y0 = 0, Y1 = -1;
-    if (ok) {
-        // det(Sigma') = |T0 x T1|^2 + lowpass (A0 + C0) + lowpass^2
-        float dx = mx - cam.campos[0], dy = my - cam.campos[1], dz = mz - cam.campos[2];
-        float e0 = fmaf(geo.Rq[0], dx, fmaf(geo.Rq[3], dy, geo.Rq[6] * dz));
-        float e1 = fmaf(geo.Rq[1], dx, fmaf(geo.Rq[4], dy, geo.Rq[7] * dz));
-        float e2 = fmaf(geo.Rq[2], dx, fmaf(geo.Rq[5], dy, geo.Rq[8] * dz));
-        float iz = 1.0f / geo.z;
-        float kk = cam.fx * cam.fy * iz * iz * iz;
-        float c0 = kk * e0 * s1 * s2, c1 = kk * e1 * s0 * s2, c2 = kk * e2 * s0 * s1;
-        float cross2 = fmaf(c0, c0, fmaf(c1, c1, c2 * c2));
-        float A = geo.A0 + lowpass, C = geo.C0 + lowpass, B = geo.B0;
-        float det = fmaf(lowpass, geo.A0 + geo.C0 + lowpass, cross2);
-        ok = det > 0.f && finitef(det) && C > 0.f;
-        if (ok) {
-            a = C / det;
-            beta = -B / C;
-            gamma = 1.0f / C;
-            float half = 0.5f * (A - C);
-            float lam = 0.5f * (A + C) + sqrtf(fmaf(half, half, B * B));
-            float extent = 3.0f * sqrtf(lam);
-            u = fmaf(cam.fx, geo.x * iz, cam.cx);
-            v = fmaf(cam.fy, geo.y * iz, cam.cy);
-            ok = fabsf(u) <= BIG && fabsf(v) <= BIG && extent <= BIG;  // false on NaN
-            if (ok) {
-                r = (int)ceilf(extent);
-                ok = tile_rect(u, v, r, cam.TX, cam.TY, X0, X1, Y0, Y1);
-            }
-        }
-    }
+    Proj pr;
+    ok = ok && project(cam, lowpass, near_plane, mx, my, mz, s0, s1, s2, q, pr);
     // the projection's outputs first: the SH rows staged below need the registers
     if (live) {
         if (ok) {
-            means2d[g] = make_float2(u, v);
-            depths[g] = geo.z;
-            conic_op[g] = make_float4(a, beta, gamma, o);
-            radii[g] = r;
-            tiles[g] = (uint32_t)((X1 - X0 + 1) * (Y1 - Y0 + 1));
+            means2d[g] = make_float2(pr.u, pr.v);
+            depths[g] = pr.depth;
+            conic_op[g] = make_float4(pr.a, pr.beta, pr.gamma, o);
+            radii[g] = pr.r;
+            tiles[g] = (uint32_t)((pr.X1 - pr.X0 + 1) * (pr.Y1 - pr.Y0 + 1));
         } else {
             write_culled(g, means2d, depths, conic_op, rgb_out, radii, tiles, clamped);
         }
@@ -487,48 +493,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(6))) void k_
     clamped[g] = cl;
 }
 
-// The chain rule for Gaussian gi. shg is its SH row in LDS: the coefficients
-// on entry, replaced coefficient by coefficient by their gradient
-// contributions (zero for a culled Gaussian), which the caller adds to (or,
-// with OVERWRITE, writes as) dL/dsh. The other outputs are added to, or with
-// OVERWRITE written (zeros for a culled Gaussian); without OVERWRITE those of
-// culled Gaussians are left untouched.
-template <bool OVERWRITE>
-__device__ __forceinline__ void chain_rule(
-    const DevCam& cam, int K, float lowpass, float near_plane, int gi,
-    const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
-    float* shg, const float4* __restrict__ conic_op, const int* __restrict__ radii,
-    const uint8_t* __restrict__ clamped, const float* __restrict__ grad2d,
-    float* __restrict__ d_means, float* __restrict__ d_scales, float* __restrict__ d_quats,
-    float* __restrict__ d_opac, float* __restrict__ d_means2d, const DensifyStats& stats) {
-    size_t g = (size_t)gi;
-    auto culled = [&]() {
-        for (int k = 0; k < 3 * K; ++k) shg[k] = 0.f;
-        if (OVERWRITE) {
-            d_means[3 * g] = d_means[3 * g + 1] = d_means[3 * g + 2] = 0.f;
-            d_scales[3 * g] = d_scales[3 * g + 1] = d_scales[3 * g + 2] = 0.f;
-            reinterpret_cast<float4*>(d_quats)[g] = make_float4(0.f, 0.f, 0.f, 0.f);
-            d_opac[g] = 0.f;
-            if (d_means2d) d_means2d[2 * g] = d_means2d[2 * g + 1] = 0.f;
-        }
-    };
-    if (radii[g] <= 0) return culled();
-    const float4* g2 = reinterpret_cast<const float4*>(grad2d + g * GRAD2D_STRIDE);
+// Gradient contributions of one view to one Gaussian's activated parameters
+// and to its screen mean (u, v).
+struct ViewGrad {
+    float dmu[3], ds[3], dq[4], d_o, du, dv;
+};
+
+// The chain rule of one view for one drawn Gaussian, from its summed pixel
+// terms g2 (a grad2d record) and its conic / opacity `con`. `sh` gives the SH
+// coefficients (sh.coef(k, c)) and takes the gradient of row k (sh.grad(k, d0,
+// d1, d2)), row by row in order. False when the Gaussian does not project (its
+// contribution is zero; sh.grad is not called).
+template <class Sh>
+__device__ __forceinline__ bool view_grad(const DevCam& cam, int K, float lowpass, float near_plane, float mx, float my,
+                                          float mz, const float* s, float4 q, float4 con, const float4* g2, uint8_t cl,
+                                          Sh& sh, ViewGrad& out) {
     float4 ga = g2[0], gb = g2[1], gc = g2[2];
     float dr[3] = {ga.x, ga.y, ga.z};
-    float Sh = ga.w, Sww = gb.x, Swy = gb.y, Syy = gb.z, Sw = gb.w, Sy = gc.x;
-    float4 con = conic_op[g];
+    float Sh_ = ga.w, Sww = gb.x, Swy = gb.y, Syy = gb.z, Sw = gb.w, Sy = gc.x;
     float a = con.x, beta = con.y, gamma = con.z, o = con.w;
 
     // pixel sums -> gradients of (u, v, opacity); dL/dQ = -h/2 and dQ/du = -2 a w
-    float d_o = o != 0.f ? Sh / o : 0.f;
+    out.d_o = o != 0.f ? Sh_ / o : 0.f;
     float du = a * Sw;
     float dv = fmaf(a * beta, Sw, gamma * Sy);
+    out.du = du;
+    out.dv = dv;
 
-    float mx = means[3 * g], my = means[3 * g + 1], mz = means[3 * g + 2];
-    float s[3] = {scales[3 * g], scales[3 * g + 1], scales[3 * g + 2]};
     Geo geo;
-    if (!geometry(cam, near_plane, mx, my, mz, s[0], s[1], s[2], quats[g], geo)) return culled();
+    if (!geometry(cam, near_plane, mx, my, mz, s[0], s[1], s[2], q, geo)) return false;
     float ddx = mx - cam.campos[0], ddy = my - cam.campos[1], ddz = mz - cam.campos[2];
 
     // dL/dSigma' = (1/2) sum_p h (Sigma'^-1 d)(Sigma'^-1 d)^T with Sigma'^-1 d = a w e + gamma dy f,
@@ -557,9 +550,9 @@ __device__ __forceinline__ void chain_rule(
         dT[3 + j] = fmaf(beta, kj, mj);
     }
     // T = P diag(s): dP = dT diag(s), ds_j = sum_i dT_ij P_ij
-    float dP[6], ds[3];
+    float dP[6];
     for (int j = 0; j < 3; ++j) {
-        ds[j] = fmaf(dT[j], geo.P[j], dT[3 + j] * geo.P[3 + j]);
+        out.ds[j] = fmaf(dT[j], geo.P[j], dT[3 + j] * geo.P[3 + j]);
         dP[j] = dT[j] * s[j];
         dP[3 + j] = dT[3 + j] * s[j];
     }
@@ -596,9 +589,12 @@ __device__ __forceinline__ void chain_rule(
                       x * dRq[6] + y * dRq[7]);
     float qdot = w * gw + x * gx + y * gy + z * gz;
     float iq = 1.0f / geo.qnorm;
+    out.dq[0] = (gw - qdot * w) * iq;
+    out.dq[1] = (gx - qdot * x) * iq;
+    out.dq[2] = (gy - qdot * y) * iq;
+    out.dq[3] = (gz - qdot * z) * iq;
 
     // colour: rgb = max(0, sum_k sh_k Y_k(dir) + 0.5), dir = (mu - campos) / |mu - campos|
-    uint8_t cl = clamped[g];
     float dcol[3];
     for (int c = 0; c < 3; ++c) dcol[c] = (cl >> c) & 1 ? 0.f : dr[c];
     float dist = sqrtf(fmaf(ddx, ddx, fmaf(ddy, ddy, ddz * ddz)));
@@ -606,42 +602,89 @@ __device__ __forceinline__ void chain_rule(
     float dxn = ddx * id, dyn = ddy * id, dzn = ddz * id;
     float Y[16], wk[16];
     sh_eval(K, dxn, dyn, dzn, Y);
-    for (int k = 0; k < K; ++k) {
-        const float s0 = shg[3 * k], s1 = shg[3 * k + 1], s2 = shg[3 * k + 2];
-        wk[k] = fmaf(s0, dcol[0], fmaf(s1, dcol[1], s2 * dcol[2]));
-        shg[3 * k] = Y[k] * dcol[0];
-        shg[3 * k + 1] = Y[k] * dcol[1];
-        shg[3 * k + 2] = Y[k] * dcol[2];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        if (k < K) {
+            wk[k] = fmaf(sh.coef(k, 0), dcol[0], fmaf(sh.coef(k, 1), dcol[1], sh.coef(k, 2) * dcol[2]));
+            sh.grad(k, Y[k] * dcol[0], Y[k] * dcol[1], Y[k] * dcol[2]);
+        }
     }
     float3 gdir = make_float3(0.f, 0.f, 0.f);
     sh_grad_accum(K, dxn, dyn, dzn, wk, gdir);
     float dd = dxn * gdir.x + dyn * gdir.y + dzn * gdir.z;
-    dmu[0] += (gdir.x - dxn * dd) * id;
-    dmu[1] += (gdir.y - dyn * dd) * id;
-    dmu[2] += (gdir.z - dzn * dd) * id;
+    out.dmu[0] = dmu[0] + (gdir.x - dxn * dd) * id;
+    out.dmu[1] = dmu[1] + (gdir.y - dyn * dd) * id;
+    out.dmu[2] = dmu[2] + (gdir.z - dzn * dd) * id;
+    return true;
+}
+
+// An SH row in LDS whose coefficients are replaced, row by row, by their
+// gradient contributions.
+struct ShInPlace {
+    float* row;
+    __device__ float coef(int k, int c) const { return row[3 * k + c]; }
+    __device__ void grad(int k, float d0, float d1, float d2) {
+        row[3 * k] = d0;
+        row[3 * k + 1] = d1;
+        row[3 * k + 2] = d2;
+    }
+};
+
+// The chain rule for Gaussian gi. shg is its SH row in LDS: the coefficients
+// on entry, replaced by their gradient contributions (zero for a culled
+// Gaussian), which the caller adds to (or, with OVERWRITE, writes as) dL/dsh.
+// The other outputs are added to, or with OVERWRITE written (zeros for a
+// culled Gaussian); without OVERWRITE those of culled Gaussians are left
+// untouched.
+template <bool OVERWRITE>
+__device__ __forceinline__ void chain_rule(
+    const DevCam& cam, int K, float lowpass, float near_plane, int gi,
+    const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
+    float* shg, const float4* __restrict__ conic_op, const int* __restrict__ radii,
+    const uint8_t* __restrict__ clamped, const float* __restrict__ grad2d,
+    float* __restrict__ d_means, float* __restrict__ d_scales, float* __restrict__ d_quats,
+    float* __restrict__ d_opac, float* __restrict__ d_means2d, const DensifyStats& stats) {
+    size_t g = (size_t)gi;
+    auto culled = [&]() {
+        for (int k = 0; k < 3 * K; ++k) shg[k] = 0.f;
+        if (OVERWRITE) {
+            d_means[3 * g] = d_means[3 * g + 1] = d_means[3 * g + 2] = 0.f;
+            d_scales[3 * g] = d_scales[3 * g + 1] = d_scales[3 * g + 2] = 0.f;
+            reinterpret_cast<float4*>(d_quats)[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+            d_opac[g] = 0.f;
+            if (d_means2d) d_means2d[2 * g] = d_means2d[2 * g + 1] = 0.f;
+        }
+    };
+    if (radii[g] <= 0) return culled();
+    const float s[3] = {scales[3 * g], scales[3 * g + 1], scales[3 * g + 2]};
+    ShInPlace sh{shg};
+    ViewGrad vg;
+    if (!view_grad(cam, K, lowpass, near_plane, means[3 * g], means[3 * g + 1], means[3 * g + 2], s, quats[g],
+                   conic_op[g], reinterpret_cast<const float4*>(grad2d + g * GRAD2D_STRIDE), clamped[g], sh, vg))
+        return culled();
 
     // prior values: zero when overwriting (the compiler drops the loads)
     auto prior = [&](const float* p) { return OVERWRITE ? 0.f : *p; };
-    d_means[3 * g] = prior(&d_means[3 * g]) + dmu[0];
-    d_means[3 * g + 1] = prior(&d_means[3 * g + 1]) + dmu[1];
-    d_means[3 * g + 2] = prior(&d_means[3 * g + 2]) + dmu[2];
-    d_scales[3 * g] = prior(&d_scales[3 * g]) + ds[0];
-    d_scales[3 * g + 1] = prior(&d_scales[3 * g + 1]) + ds[1];
-    d_scales[3 * g + 2] = prior(&d_scales[3 * g + 2]) + ds[2];
+    d_means[3 * g] = prior(&d_means[3 * g]) + vg.dmu[0];
+    d_means[3 * g + 1] = prior(&d_means[3 * g + 1]) + vg.dmu[1];
+    d_means[3 * g + 2] = prior(&d_means[3 * g + 2]) + vg.dmu[2];
+    d_scales[3 * g] = prior(&d_scales[3 * g]) + vg.ds[0];
+    d_scales[3 * g + 1] = prior(&d_scales[3 * g + 1]) + vg.ds[1];
+    d_scales[3 * g + 2] = prior(&d_scales[3 * g + 2]) + vg.ds[2];
     float4* dq = reinterpret_cast<float4*>(d_quats) + g;
     float4 dq0 = OVERWRITE ? make_float4(0.f, 0.f, 0.f, 0.f) : *dq;
-    dq0.x += (gw - qdot * w) * iq;
-    dq0.y += (gx - qdot * x) * iq;
-    dq0.z += (gy - qdot * y) * iq;
-    dq0.w += (gz - qdot * z) * iq;
+    dq0.x += vg.dq[0];
+    dq0.y += vg.dq[1];
+    dq0.z += vg.dq[2];
+    dq0.w += vg.dq[3];
     *dq = dq0;
-    d_opac[g] = prior(&d_opac[g]) + d_o;
+    d_opac[g] = prior(&d_opac[g]) + vg.d_o;
     if (d_means2d) {
-        d_means2d[2 * g] = prior(&d_means2d[2 * g]) + du;
-        d_means2d[2 * g + 1] = prior(&d_means2d[2 * g + 1]) + dv;
+        d_means2d[2 * g] = prior(&d_means2d[2 * g]) + vg.du;
+        d_means2d[2 * g + 1] = prior(&d_means2d[2 * g + 1]) + vg.dv;
     }
     if (stats.grad_accum) {  // this view's screen-mean gradient norm, count and radius
-        stats.grad_accum[g] += sqrtf(fmaf(du, du, dv * dv));
+        stats.grad_accum[g] += sqrtf(fmaf(vg.du, vg.du, vg.dv * vg.dv));
         stats.count[g] += 1;
         stats.max_radius[g] = max(stats.max_radius[g], radii[g]);
     }
@@ -688,6 +731,195 @@ __global__ __launch_bounds__(64) void k_preprocess_bwd(
     }
 }
 
+// ---------------------------------------------------------------- several views per launch
+
+// Projection of every Gaussian into V cameras of one image size. The
+// parameters and SH rows are read once per Gaussian; view v's outputs go to
+// entry v n + g of the per-view arrays, and bit v of vis_mask[g] (if
+// non-null) is set when the Gaussian is drawn in view v. Each view's outputs
+// are those of the single-view kernel, operation for operation.
+__global__ __launch_bounds__(64) void k_preprocess_views(
+    CamSet cams, int V, int K, int sh_rows, float lowpass, float near_plane, int n,
+    const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
+    const float* __restrict__ opac, const float* __restrict__ sh,
+    float2* __restrict__ means2d, float* __restrict__ depths, float4* __restrict__ conic_op,
+    float* __restrict__ rgb_out, int* __restrict__ radii, uint32_t* __restrict__ tiles,
+    uint8_t* __restrict__ clamped, uint32_t* __restrict__ vis_mask) {
+    extern __shared__ float s_sh[];
+    const int stride = (3 * K) | 1;
+    const int base = blockIdx.x * 64;
+    const int gi = base + threadIdx.x;
+    const bool live = gi < n;
+    const size_t g = live ? (size_t)gi : (size_t)base;
+    const float mx = means[3 * g], my = means[3 * g + 1], mz = means[3 * g + 2];
+    const float s0 = scales[3 * g], s1 = scales[3 * g + 1], s2 = scales[3 * g + 2];
+    const float4 q = quats[g];
+    const float o = opac[g];
+    const bool fin = live && finitef(mx) && finitef(my) && finitef(mz) && finitef(s0) && finitef(s1) &&
+                     finitef(s2) && finitef(q.x) && finitef(q.y) && finitef(q.z) && finitef(q.w) && finitef(o);
+    // the block's SH rows, once, through LDS with coalesced reads
+    stage_in(sh, s_sh, base, n, 3 * sh_rows, 3 * K, stride);
+    __syncthreads();
+    const float* shg = s_sh + threadIdx.x * stride;
+    uint32_t mask = 0u;
+    for (int v = 0; v < V; ++v) {
+        const DevCam& cam = cams.c[v];
+        const size_t e = (size_t)v * n + g;
+        Proj pr;
+        bool ok = fin && project(cam, lowpass, near_plane, mx, my, mz, s0, s1, s2, q, pr);
+        float raw[3] = {0.5f, 0.5f, 0.5f};
+        if (ok) {
+            const float dx = mx - cam.campos[0], dy = my - cam.campos[1], dz = mz - cam.campos[2];
+            const float dist = sqrtf(fmaf(dx, dx, fmaf(dy, dy, dz * dz)));
+            const float id = 1.0f / dist;
+            float Y[16];
+            sh_eval(K, dx * id, dy * id, dz * id, Y);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                if (k >= K) break;
+                raw[0] = fmaf(shg[3 * k], Y[k], raw[0]);
+                raw[1] = fmaf(shg[3 * k + 1], Y[k], raw[1]);
+                raw[2] = fmaf(shg[3 * k + 2], Y[k], raw[2]);
+            }
+            ok = dist > 0.f && finitef(raw[0]) && finitef(raw[1]) && finitef(raw[2]);
+        }
+        if (!live) continue;
+        if (!ok) {
+            write_culled(e, means2d, depths, conic_op, rgb_out, radii, tiles, clamped);
+            continue;
+        }
+        means2d[e] = make_float2(pr.u, pr.v);
+        depths[e] = pr.depth;
+        conic_op[e] = make_float4(pr.a, pr.beta, pr.gamma, o);
+        radii[e] = pr.r;
+        tiles[e] = (uint32_t)((pr.X1 - pr.X0 + 1) * (pr.Y1 - pr.Y0 + 1));
+        uint8_t cl = 0;
+        for (int c = 0; c < 3; ++c) {
+            const bool neg = raw[c] < 0.f;
+            cl |= (uint8_t)(neg ? (1u << c) : 0u);
+            rgb_out[3 * e + c] = neg ? 0.f : raw[c];
+        }
+        clamped[e] = cl;
+        mask |= 1u << v;
+    }
+    if (live && vis_mask) vis_mask[g] = mask;
+}
+
+// An SH row in LDS read for its coefficients, with the gradient rows of
+// every view summed in registers.
+struct ShAccum {
+    const float* row;
+    float acc[48];
+    __device__ float coef(int k, int c) const { return row[3 * k + c]; }
+    __device__ void grad(int k, float d0, float d1, float d2) {
+        acc[3 * k] += d0;
+        acc[3 * k + 1] += d1;
+        acc[3 * k + 2] += d2;
+    }
+};
+
+// Chain rule of V views per Gaussian: the per-view inputs (conic, radius,
+// clamp bits and pixel sums of view v at entry v n + g) are read view by view;
+// the parameter gradients are summed over the views in registers and written
+// once (added, or with OVERWRITE written for every Gaussian). dL/d(u, v) of
+// view v goes to d_means2d[v n + g] when asked for; the densification
+// statistics take every drawn view in turn.
+template <bool OVERWRITE>
+__global__ __launch_bounds__(64) void k_preprocess_bwd_views(
+    CamSet cams, int V, int K, int sh_rows, float lowpass, float near_plane, int n,
+    const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
+    const float* __restrict__ sh, const float4* __restrict__ conic_op, const int* __restrict__ radii,
+    const uint8_t* __restrict__ clamped, const float* __restrict__ grad2d,
+    float* __restrict__ d_means, float* __restrict__ d_scales, float* __restrict__ d_quats,
+    float* __restrict__ d_opac, float* __restrict__ d_sh, float* __restrict__ d_means2d, DensifyStats stats) {
+    extern __shared__ float s_sh[];
+    const int stride = (3 * K) | 1;
+    const int base = blockIdx.x * 64;
+    const int gi = base + threadIdx.x;
+    const bool live = gi < n;
+    const size_t g = live ? (size_t)gi : (size_t)base;
+    uint32_t mask = 0u;  // the views that drew this Gaussian
+    if (live)
+        for (int v = 0; v < V; ++v) mask |= radii[(size_t)v * n + g] > 0 ? 1u << v : 0u;
+    const int nvis = __popcll(__ballot(mask != 0u));
+    if (!OVERWRITE && nvis == 0) return;  // nothing of this block was drawn: no gradient
+    const bool dense = nvis > SH_DENSE;
+    float* shg = s_sh + threadIdx.x * stride;
+    if (dense) stage_in(sh, s_sh, base, n, 3 * sh_rows, 3 * K, stride);
+    else if (mask) copy_own_row(sh, shg, g, 3 * sh_rows, 3 * K);
+    __syncthreads();
+    const float mx = means[3 * g], my = means[3 * g + 1], mz = means[3 * g + 2];
+    const float s[3] = {scales[3 * g], scales[3 * g + 1], scales[3 * g + 2]};
+    const float4 q = quats[g];
+    ShAccum sha;
+    sha.row = shg;
+#pragma unroll
+    for (int k = 0; k < 48; ++k) sha.acc[k] = 0.f;
+    float dmu[3] = {0.f, 0.f, 0.f}, ds[3] = {0.f, 0.f, 0.f}, dq[4] = {0.f, 0.f, 0.f, 0.f}, d_o = 0.f;
+    float nsum = 0.f;
+    int cnt = 0, rmax = 0;
+    for (int v = 0; v < V; ++v) {
+        const size_t e = (size_t)v * n + g;
+        bool contrib = false;
+        ViewGrad vg;
+        if ((mask >> v) & 1u) {
+            contrib = view_grad(cams.c[v], K, lowpass, near_plane, mx, my, mz, s, q, conic_op[e],
+                                reinterpret_cast<const float4*>(grad2d + e * GRAD2D_STRIDE), clamped[e], sha, vg);
+            if (contrib) {
+                for (int j = 0; j < 3; ++j) dmu[j] += vg.dmu[j];
+                for (int j = 0; j < 3; ++j) ds[j] += vg.ds[j];
+                for (int j = 0; j < 4; ++j) dq[j] += vg.dq[j];
+                d_o += vg.d_o;
+                nsum += sqrtf(fmaf(vg.du, vg.du, vg.dv * vg.dv));
+                cnt += 1;
+                rmax = max(rmax, radii[e]);
+            }
+        }
+        if (d_means2d && live) {
+            if (OVERWRITE) {
+                d_means2d[2 * e] = contrib ? vg.du : 0.f;
+                d_means2d[2 * e + 1] = contrib ? vg.dv : 0.f;
+            } else if (contrib) {
+                d_means2d[2 * e] += vg.du;
+                d_means2d[2 * e + 1] += vg.dv;
+            }
+        }
+    }
+    if (live && (OVERWRITE || mask)) {
+        auto prior = [&](const float* p) { return OVERWRITE ? 0.f : *p; };
+        for (int j = 0; j < 3; ++j) d_means[3 * g + j] = prior(&d_means[3 * g + j]) + dmu[j];
+        for (int j = 0; j < 3; ++j) d_scales[3 * g + j] = prior(&d_scales[3 * g + j]) + ds[j];
+        float4* dqp = reinterpret_cast<float4*>(d_quats) + g;
+        float4 dq0 = OVERWRITE ? make_float4(0.f, 0.f, 0.f, 0.f) : *dqp;
+        *dqp = make_float4(dq0.x + dq[0], dq0.y + dq[1], dq0.z + dq[2], dq0.w + dq[3]);
+        d_opac[g] = prior(&d_opac[g]) + d_o;
+    }
+    if (stats.grad_accum && live && cnt > 0) {
+        stats.grad_accum[g] += nsum;
+        stats.count[g] += cnt;
+        stats.max_radius[g] = max(stats.max_radius[g], rmax);
+    }
+    // the summed SH gradient rows replace the coefficients (each lane its own row), then leave through LDS
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        if (k < K) {
+            shg[3 * k] = sha.acc[3 * k];
+            shg[3 * k + 1] = sha.acc[3 * k + 1];
+            shg[3 * k + 2] = sha.acc[3 * k + 2];
+        }
+    }
+    __syncthreads();
+    if (OVERWRITE) {
+        stage_out(s_sh, d_sh, base, n, 3 * sh_rows, 3 * K, stride);
+        if (live)
+            for (int e = 3 * K; e < 3 * sh_rows; ++e) d_sh[g * 3 * sh_rows + e] = 0.f;
+    } else if (dense) {
+        stage_out_add(s_sh, d_sh, base, n, 3 * sh_rows, 3 * K, stride);
+    } else if (mask) {
+        add_own_row(shg, d_sh, g, 3 * sh_rows, 3 * K);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_preprocess(const DevCam& cam, int K, int sh_rows, float lowpass, float near_plane, int n,
@@ -715,6 +947,39 @@ hipError_t launch_preprocess_bwd(const DevCam& cam, int K, int sh_rows, float lo
     size_t lds = sizeof(float) * 64 * ((3 * K) | 1);
     auto kernel = overwrite ? k_preprocess_bwd<true> : k_preprocess_bwd<false>;
     kernel<<<blocks, 64, lds, stream>>>(cam, K, sh_rows, lowpass, near_plane, n, means, scales,
+                                        reinterpret_cast<const float4*>(quats), sh,
+                                        reinterpret_cast<const float4*>(conic_op), radii, clamped, grad2d, d_means,
+                                        d_scales, d_quats, d_opac, d_sh, d_means2d, stats);
+    return hipGetLastError();
+}
+
+hipError_t launch_preprocess_views(const CamSet& cams, int V, int K, int sh_rows, float lowpass, float near_plane,
+                                   int n, const float* means, const float* scales, const float* quats,
+                                   const float* opac, const float* sh, float* means2d, float* depths,
+                                   float* conic_op, float* rgb, int* radii, uint32_t* tiles, uint8_t* clamped,
+                                   uint32_t* vis_mask, hipStream_t stream) {
+    if (n == 0 || V == 0) return hipSuccess;
+    const int blocks = (n + 63) / 64;
+    const size_t lds = sizeof(float) * 64 * ((3 * K) | 1);
+    k_preprocess_views<<<blocks, 64, lds, stream>>>(cams, V, K, sh_rows, lowpass, near_plane, n, means, scales,
+                                                    reinterpret_cast<const float4*>(quats), opac, sh,
+                                                    reinterpret_cast<float2*>(means2d), depths,
+                                                    reinterpret_cast<float4*>(conic_op), rgb, radii, tiles, clamped,
+                                                    vis_mask);
+    return hipGetLastError();
+}
+
+hipError_t launch_preprocess_bwd_views(const CamSet& cams, int V, int K, int sh_rows, float lowpass, float near_plane,
+                                       int n, const float* means, const float* scales, const float* quats,
+                                       const float* sh, const float* conic_op, const int* radii,
+                                       const uint8_t* clamped, const float* grad2d, float* d_means, float* d_scales,
+                                       float* d_quats, float* d_opac, float* d_sh, float* d_means2d, bool overwrite,
+                                       const DensifyStats& stats, hipStream_t stream) {
+    if (n == 0 || V == 0) return hipSuccess;
+    const int blocks = (n + 63) / 64;
+    const size_t lds = sizeof(float) * 64 * ((3 * K) | 1);
+    auto kernel = overwrite ? k_preprocess_bwd_views<true> : k_preprocess_bwd_views<false>;
+    kernel<<<blocks, 64, lds, stream>>>(cams, V, K, sh_rows, lowpass, near_plane, n, means, scales,
                                         reinterpret_cast<const float4*>(quats), sh,
                                         reinterpret_cast<const float4*>(conic_op), radii, clamped, grad2d, d_means,
                                         d_scales, d_quats, d_opac, d_sh, d_means2d, stats);

@@ -130,8 +130,18 @@ __device__ __forceinline__ uint32_t stage_record_bands(uint32_t g, uint32_t pos,
 // walks and 0 once it has stopped (or lies outside the image): a stopped
 // pixel's effective alpha is 0, which changes nothing, and its T (>= 1e-4)
 // can never trigger the stop test again.
+// Tile `tile` of the grid of views stacked vertically (TX x TY tiles each):
+// its view, returned, and its column and row inside that view.
+__device__ __forceinline__ int view_of_tile(int tile, int TX, int TY, int& tx, int& ty) {
+    const int row = tile / TX;
+    const int view = row / TY;
+    tx = tile - row * TX;
+    ty = row - view * TY;
+    return view;
+}
+
 template <int PPL>
-__global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, const uint2* __restrict__ ranges,
+__global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY, const uint2* __restrict__ ranges,
                                                  const uint32_t* __restrict__ values,
                                                  const float2* __restrict__ means2d,
                                                  const float4* __restrict__ conic_op, const float* __restrict__ rgb,
@@ -140,7 +150,11 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, const u
     constexpr int BANDS = 4 / PPL;
     __shared__ Staged s_rec[BATCH];
     const int tile = blockIdx.x / BANDS, band = blockIdx.x - tile * BANDS;
-    const int tx = tile % TX, ty = tile / TX;
+    int tx, ty;
+    const size_t view_px = view_of_tile(tile, TX, TY, tx, ty) * (size_t)W * H;
+    image += 3 * view_px;
+    final_T += view_px;
+    n_contrib += view_px;
     const int lane = threadIdx.x;
     const int px = tx * TILE + (lane & 15);
     const int py0 = ty * TILE + band * 4 * PPL + (lane >> 4);
@@ -224,7 +238,7 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, const u
 // with A the colour behind the current entry (starting as the background), so
 // dL/dalpha = T (rgb . dL/dC - S).
 template <int PPL, int NB>
-__global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const uint2* __restrict__ ranges,
+__global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, int TY, const uint2* __restrict__ ranges,
                                                  const uint32_t* __restrict__ values,
                                                  const float2* __restrict__ means2d,
                                                  const float4* __restrict__ conic_op, const float* __restrict__ rgb,
@@ -237,7 +251,11 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, const u
     __shared__ float s_part[NB * 4 * GRAD2D_N];  // [entry][row of 16 lanes][value]
     __shared__ uint32_t s_has[NB];
     const int tile = blockIdx.x / BANDS, band = blockIdx.x - tile * BANDS;
-    const int tx = tile % TX, ty = tile / TX;
+    int tx, ty;
+    const size_t view_px = view_of_tile(tile, TX, TY, tx, ty) * (size_t)W * H;
+    final_T += view_px;
+    n_contrib += view_px;
+    dL_dimage += 3 * view_px;
     const int lane = threadIdx.x;
     // lane roles in the in-row reduce-scatter (see row_reduce_scatter8)
     const int rl = lane & 15, row = lane >> 4;
@@ -378,37 +396,37 @@ int bwd_pixels_per_lane(int ntiles) {
     return 4;
 }
 
-hipError_t launch_render_fwd(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
-                             const float* means2d, const float* conic_op, const float* rgb, const float* bg,
-                             float* image, float* final_T, uint32_t* n_contrib, hipStream_t stream) {
-    const int ntiles = TX * TY;
+hipError_t launch_render_fwd(int views, int W, int H, int TX, int TY, const uint32_t* ranges,
+                             const uint32_t* values, const float* means2d, const float* conic_op, const float* rgb,
+                             const float* bg, float* image, float* final_T, uint32_t* n_contrib, hipStream_t stream) {
+    const int ntiles = views * TX * TY;
     if (ntiles == 0) return hipSuccess;
     k_render_fwd<FWD_PPL><<<ntiles * (4 / FWD_PPL), 64, 0, stream>>>(
-        W, H, TX, reinterpret_cast<const uint2*>(ranges), values, reinterpret_cast<const float2*>(means2d),
+        W, H, TX, TY, reinterpret_cast<const uint2*>(ranges), values, reinterpret_cast<const float2*>(means2d),
         reinterpret_cast<const float4*>(conic_op), rgb, bg[0], bg[1], bg[2], image, final_T, n_contrib);
     return hipGetLastError();
 }
 
-hipError_t launch_render_bwd(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
-                             const float* means2d, const float* conic_op, const float* rgb, const float* bg,
-                             const float* final_T, const uint32_t* n_contrib, const float* dL_dimage,
-                             float* grad2d, hipStream_t stream) {
-    const int ntiles = TX * TY;
+hipError_t launch_render_bwd(int views, int W, int H, int TX, int TY, const uint32_t* ranges,
+                             const uint32_t* values, const float* means2d, const float* conic_op, const float* rgb,
+                             const float* bg, const float* final_T, const uint32_t* n_contrib,
+                             const float* dL_dimage, float* grad2d, hipStream_t stream) {
+    const int ntiles = views * TX * TY;
     if (ntiles == 0) return hipSuccess;
     const uint2* rg = reinterpret_cast<const uint2*>(ranges);
     const float2* m2 = reinterpret_cast<const float2*>(means2d);
     const float4* co = reinterpret_cast<const float4*>(conic_op);
     switch (bwd_pixels_per_lane(ntiles)) {
         case 1:
-            k_render_bwd<1, BWD_BATCH><<<ntiles * 4, 64, 0, stream>>>(W, H, TX, rg, values, m2, co, rgb, bg[0], bg[1],
+            k_render_bwd<1, BWD_BATCH><<<ntiles * 4, 64, 0, stream>>>(W, H, TX, TY, rg, values, m2, co, rgb, bg[0], bg[1],
                                                                      bg[2], final_T, n_contrib, dL_dimage, grad2d);
             break;
         case 2:
-            k_render_bwd<2, BWD_BATCH><<<ntiles * 2, 64, 0, stream>>>(W, H, TX, rg, values, m2, co, rgb, bg[0], bg[1],
+            k_render_bwd<2, BWD_BATCH><<<ntiles * 2, 64, 0, stream>>>(W, H, TX, TY, rg, values, m2, co, rgb, bg[0], bg[1],
                                                                      bg[2], final_T, n_contrib, dL_dimage, grad2d);
             break;
         default:
-            k_render_bwd<4, BWD_BATCH><<<ntiles, 64, 0, stream>>>(W, H, TX, rg, values, m2, co, rgb, bg[0], bg[1],
+            k_render_bwd<4, BWD_BATCH><<<ntiles, 64, 0, stream>>>(W, H, TX, TY, rg, values, m2, co, rgb, bg[0], bg[1],
                                                                  bg[2], final_T, n_contrib, dL_dimage, grad2d);
     }
     return hipGetLastError();

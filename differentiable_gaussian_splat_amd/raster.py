@@ -68,7 +68,10 @@ class GsAdamOptions(C.Structure):
 
 EXPORTS = ["gs_default_options", "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_sort_workspace_size",
            "gs_bin_sort", "gs_render_fwd", "gs_render_bwd_workspace_size", "gs_render_bwd", "gs_render_bwd_raster",
-           "gs_preprocess_bwd", "gs_adam_step", "gs_mb_hbm_read", "gs_mb_hbm_copy", "gs_mb_atomic"]
+           "gs_preprocess_bwd", "gs_preprocess_views", "gs_bin_sort_views_workspace_size", "gs_bin_sort_views",
+           "gs_render_fwd_views", "gs_render_bwd_raster_views", "gs_preprocess_bwd_views", "gs_adam_step",
+           "gs_mb_hbm_read", "gs_mb_hbm_copy", "gs_mb_atomic"]
+MAX_VIEWS = 32
 GRAD2D_STRIDE = 12
 
 _lib = None
@@ -109,6 +112,18 @@ def load_library(path: str = LIB_PATH):
         L.gs_preprocess_bwd.argtypes = [cam, opt, i64] + [P] * 8 + [P] * 6 + [dst, P]
         L.gs_preprocess_bwd.restype = i32
         PP = C.POINTER(C.c_void_p)  # five device pointers
+        L.gs_preprocess_views.argtypes = [cam, i32, opt, i64] + [P] * 5 + [P] * 8 + [P]
+        L.gs_preprocess_views.restype = i32
+        L.gs_bin_sort_views_workspace_size.argtypes = [i32, i64, i64, i32, i32]
+        L.gs_bin_sort_views_workspace_size.restype = sz
+        L.gs_bin_sort_views.argtypes = [cam, i32, opt, i64, P, P, P, P, P, sz, i64, P, P, P, C.POINTER(C.c_int64), P]
+        L.gs_bin_sort_views.restype = i32
+        L.gs_render_fwd_views.argtypes = [cam, i32, opt, i64, P, P, i64, P, P, P, P, P, P, P]
+        L.gs_render_fwd_views.restype = i32
+        L.gs_render_bwd_raster_views.argtypes = [cam, i32, opt, i64, P, P, i64] + [P] * 7 + [P]
+        L.gs_render_bwd_raster_views.restype = i32
+        L.gs_preprocess_bwd_views.argtypes = [cam, i32, opt, i64] + [P] * 8 + [P] * 6 + [dst, P]
+        L.gs_preprocess_bwd_views.restype = i32
         L.gs_adam_step.argtypes = [C.POINTER(GsAdamOptions), i64, i32, PP, PP, PP, PP, P, P, P, P]
         L.gs_adam_step.restype = i32
         L.gs_mb_hbm_read.argtypes = [P, sz, P, P]
@@ -233,6 +248,71 @@ def gs_preprocess_bwd(cam: GsCamera, opt: GsOptions, means, scales, quats, sh, c
                                           _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities), _p(dL_dsh),
                                           _p(dL_dmeans2d), _stats(stats), _stream(stream))
     _check(st, "gs_preprocess_bwd")
+
+
+# ------------------------------------------------------------------ several views per launch
+
+def make_cameras(cameras):
+    """ctypes array of GsCamera (one image size) for the *_views calls."""
+    cams = [c if isinstance(c, GsCamera) else make_camera(c) for c in cameras]
+    return (GsCamera * len(cams))(*cams)
+
+
+def gs_preprocess_views(cams, opt: GsOptions, means, scales, quats, opacities, sh, means2d, depths, conic_opacity,
+                        rgb, radii, tiles_touched, clamped, vis_mask=None, stream=None):
+    n = means.shape[0]
+    st = load_library().gs_preprocess_views(cams, len(cams), C.byref(opt), n, _p(means), _p(scales), _p(quats),
+                                            _p(opacities), _p(sh), _p(means2d), _p(depths), _p(conic_opacity),
+                                            _p(rgb), _p(radii), _p(tiles_touched), _p(clamped), _p(vis_mask),
+                                            _stream(stream))
+    _check(st, "gs_preprocess_views")
+
+
+def gs_bin_sort_views_workspace_size(n_views, n, pair_capacity, width, height) -> int:
+    return int(load_library().gs_bin_sort_views_workspace_size(n_views, n, pair_capacity, width, height))
+
+
+def gs_bin_sort_views(cams, opt: GsOptions, n, means2d, depths, radii, tiles_touched, workspace, pair_capacity, keys,
+                      values, ranges, stream=None) -> int:
+    """Returns the pair count P over all views; raises GsCapacityError (with
+    .needed) if P > pair_capacity."""
+    npairs = C.c_int64(0)
+    st = load_library().gs_bin_sort_views(cams, len(cams), C.byref(opt), n, _p(means2d), _p(depths), _p(radii),
+                                          _p(tiles_touched), _p(workspace),
+                                          workspace.numel() * workspace.element_size() if workspace is not None
+                                          else 0, pair_capacity, _p(keys), _p(values), _p(ranges),
+                                          C.byref(npairs), _stream(stream))
+    if st == GS_ERR_CAPACITY:
+        raise GsCapacityError(st, load_library().gs_last_error().decode(), npairs.value)
+    _check(st, "gs_bin_sort_views")
+    return int(npairs.value)
+
+
+def gs_render_fwd_views(cams, opt: GsOptions, n, ranges, values, n_pairs, means2d, conic_opacity, rgb, image, final_T,
+                        n_contrib, stream=None):
+    st = load_library().gs_render_fwd_views(cams, len(cams), C.byref(opt), n, _p(ranges), _p(values), n_pairs,
+                                            _p(means2d), _p(conic_opacity), _p(rgb), _p(image), _p(final_T),
+                                            _p(n_contrib), _stream(stream))
+    _check(st, "gs_render_fwd_views")
+
+
+def gs_render_bwd_raster_views(cams, opt: GsOptions, n, ranges, values, n_pairs, means2d, conic_opacity, rgb,
+                               final_T, n_contrib, dL_dimage, grad2d, stream=None):
+    st = load_library().gs_render_bwd_raster_views(cams, len(cams), C.byref(opt), n, _p(ranges), _p(values),
+                                                   n_pairs, _p(means2d), _p(conic_opacity), _p(rgb), _p(final_T),
+                                                   _p(n_contrib), _p(dL_dimage), _p(grad2d), _stream(stream))
+    _check(st, "gs_render_bwd_raster_views")
+
+
+def gs_preprocess_bwd_views(cams, opt: GsOptions, means, scales, quats, sh, conic_opacity, radii, clamped, grad2d,
+                            dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh, dL_dmeans2d=None, stats=None,
+                            stream=None):
+    n = means.shape[0]
+    st = load_library().gs_preprocess_bwd_views(cams, len(cams), C.byref(opt), n, _p(means), _p(scales), _p(quats),
+                                                _p(sh), _p(conic_opacity), _p(radii), _p(clamped), _p(grad2d),
+                                                _p(dL_dmeans), _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities),
+                                                _p(dL_dsh), _p(dL_dmeans2d), _stats(stats), _stream(stream))
+    _check(st, "gs_preprocess_bwd_views")
 
 
 PARAM_GROUPS = ("means", "log_scales", "quats", "opacity_logits", "sh")
@@ -399,6 +479,93 @@ class Rasterizer:
                       frame.final_T, frame.n_contrib, dL_dimage, grads["means"], grads["scales"], grads["quats"],
                       grads["opacities"], grads["sh"], grads.get("means2d") if want_means2d else None,
                       self._bwd_ws, stats)
+        return grads
+
+
+@dataclass
+class ViewsFrame:
+    """Device state of V views rendered in one batch: per-view arrays carry a
+    leading view axis (entry v n + g), the pair list covers all views."""
+    cams: object
+    opt: GsOptions
+    width: int
+    height: int
+    means2d: torch.Tensor
+    depths: torch.Tensor
+    conic_opacity: torch.Tensor
+    rgb: torch.Tensor
+    radii: torch.Tensor
+    tiles_touched: torch.Tensor
+    clamped: torch.Tensor
+    vis_mask: torch.Tensor
+    n_pairs: int
+    keys: torch.Tensor | None
+    values: torch.Tensor
+    ranges: torch.Tensor
+    image: torch.Tensor
+    final_T: torch.Tensor
+    n_contrib: torch.Tensor
+
+
+class ViewsRasterizer(Rasterizer):
+    """Rasterizer of V views of one image size per launch."""
+
+    def forward_views(self, cameras, means, scales, quats, opacities, sh, sh_degree, lowpass=0.3, near_plane=0.2,
+                      bg=(0.0, 0.0, 0.0)) -> ViewsFrame:
+        cams = cameras if isinstance(cameras, C.Array) else make_cameras(cameras)
+        V, n, dev = len(cams), means.shape[0], means.device
+        opt = make_options(sh_degree, sh.shape[1], lowpass, near_plane, bg)
+        pre = dict(means2d=_empty((V, n, 2), torch.float32, dev), depths=_empty((V, n), torch.float32, dev),
+                   conic_opacity=_empty((V, n, 4), torch.float32, dev), rgb=_empty((V, n, 3), torch.float32, dev),
+                   radii=_empty((V, n), torch.int32, dev), tiles_touched=_empty((V, n), torch.int32, dev),
+                   clamped=_empty((V, n), torch.uint8, dev), vis_mask=_empty(n, torch.int32, dev))
+        gs_preprocess_views(cams, opt, means, scales, quats, opacities, sh, pre["means2d"], pre["depths"],
+                            pre["conic_opacity"], pre["rgb"], pre["radii"], pre["tiles_touched"], pre["clamped"],
+                            pre["vis_mask"])
+        W, H = cams[0].width, cams[0].height
+        ntiles = ((W + 15) // 16) * ((H + 15) // 16)
+        ranges = _empty((V * ntiles, 2), torch.int32, self.device)
+        self._ensure_pairs(self.pair_capacity)
+        while True:
+            need = gs_bin_sort_views_workspace_size(V, n, self.pair_capacity, W, H)
+            if self._bin_ws is None or self._bin_ws.numel() < need:
+                self._bin_ws = _empty(need, torch.uint8, self.device)
+            try:
+                P = gs_bin_sort_views(cams, opt, n, pre["means2d"], pre["depths"], pre["radii"],
+                                      pre["tiles_touched"], self._bin_ws, self.pair_capacity, self._keys,
+                                      self._values, ranges)
+                break
+            except GsCapacityError as e:
+                self._values = None
+                self._ensure_pairs(int(e.needed * 1.15) + 1024)
+        image = _empty((V, 3, H, W), torch.float32, self.device)
+        final_T = _empty((V, H, W), torch.float32, self.device)
+        n_contrib = _empty((V, H, W), torch.int32, self.device)
+        gs_render_fwd_views(cams, opt, n, ranges, self._values, P, pre["means2d"], pre["conic_opacity"], pre["rgb"],
+                            image, final_T, n_contrib)
+        return ViewsFrame(cams, opt, W, H, pre["means2d"], pre["depths"], pre["conic_opacity"], pre["rgb"],
+                          pre["radii"], pre["tiles_touched"], pre["clamped"], pre["vis_mask"], P, self._keys,
+                          self._values, ranges, image, final_T, n_contrib)
+
+    def backward_views(self, frame: ViewsFrame, means, scales, quats, opacities, sh, dL_dimage, grads: dict,
+                       want_means2d: bool = False, overwrite: bool = False, stats: GsDensifyStats | None = None):
+        """Sum over the frame's views of the gradients (added into ``grads``,
+        or written with ``overwrite``); grads["means2d"] gets [V, n, 2]."""
+        V, n = len(frame.cams), means.shape[0]
+        grad2d = torch.zeros((V, n, GRAD2D_STRIDE), dtype=torch.float32, device=means.device)
+        if want_means2d and "means2d" not in grads:
+            grads["means2d"] = (_empty((V, n, 2), torch.float32, means.device) if overwrite else
+                                torch.zeros((V, n, 2), dtype=torch.float32, device=means.device))
+        opt = frame.opt
+        if overwrite:
+            opt = GsOptions.from_buffer_copy(frame.opt)
+            opt.overwrite_grads = 1
+        gs_render_bwd_raster_views(frame.cams, opt, n, frame.ranges, frame.values, frame.n_pairs, frame.means2d,
+                                   frame.conic_opacity, frame.rgb, frame.final_T, frame.n_contrib, dL_dimage, grad2d)
+        gs_preprocess_bwd_views(frame.cams, opt, means, scales, quats, sh, frame.conic_opacity, frame.radii,
+                                frame.clamped, grad2d, grads["means"], grads["scales"], grads["quats"],
+                                grads["opacities"], grads["sh"], grads.get("means2d") if want_means2d else None,
+                                stats)
         return grads
 
 

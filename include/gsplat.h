@@ -253,6 +253,86 @@ gs_status gs_preprocess_bwd(const gs_camera *cam, const gs_options *opt, int64_t
                             const gs_densify_stats *stats, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Several views per launch
+ *
+ * On the Odin page each training view reads and updates only a sparse,
+ * view-dependent subset of the primitives, held as that view's primitive
+ * scope (axioms, first domain assumption), which its runtime checks before
+ * overlapping views (central objects: read / update primitive scopes); the
+ * Gaian page traces which points each pass reads or writes (methodology,
+ * static access profiling). The calls below render V views of ONE
+ * image size in one launch per phase instead of V: the parameters are read
+ * once per Gaussian, the views' tile grids are stacked into one binning pass
+ * (the view leads the sort key), and the chain rule sums the views' gradients
+ * per Gaussian before writing them once.
+ *
+ * Layout: the same per-Gaussian arrays as the single-view calls, with a
+ * leading view axis: means2d[V, n, 2], depths[V, n], conic_opacity[V, n, 4],
+ * rgb[V, n, 3], radii[V, n], tiles_touched[V, n], clamped[V, n],
+ * grad2d[V, n, GS_GRAD2D_STRIDE], dL_dmeans2d[V, n, 2]; images
+ * image[V, 3, H, W], final_T[V, H, W], n_contrib[V, H, W], dL_dimage[V, 3, H, W].
+ * Entry v n + g holds Gaussian g in view v; each view's values are those the
+ * single-view call computes for that camera. The parameters and their
+ * gradients keep their single-view shapes. Requires 1 <= V <= GS_MAX_VIEWS,
+ * V n < 2^31, V times the tiles of one view <= 2^24, and every camera of one
+ * width and height (GS_ERR_INVALID_ARG otherwise, naming the camera).
+ * ------------------------------------------------------------------------ */
+#define GS_MAX_VIEWS 32
+
+/* gs_preprocess for V cameras (host array cams[V]). vis_mask (nullable) gets
+ * one word per Gaussian: bit v set iff it is drawn in view v (radius > 0), the
+ * per-view scope of the Gaussian. */
+gs_status gs_preprocess_views(const gs_camera *cams, int32_t n_views, const gs_options *opt, int64_t n,
+                              const float *means, const float *scales, const float *quats,
+                              const float *opacities, const float *sh,
+                              float *means2d, float *depths, float *conic_opacity, float *rgb,
+                              int32_t *radii, uint32_t *tiles_touched, uint8_t *clamped, uint32_t *vis_mask,
+                              void *stream);
+
+/* Workspace bytes gs_bin_sort_views needs. */
+size_t gs_bin_sort_views_workspace_size(int32_t n_views, int64_t n, int64_t pair_capacity, int32_t width,
+                                        int32_t height);
+
+/* gs_bin_sort over all V views at once. The views' grids of TX x TY tiles are
+ * stacked: tile t of view v has the id v TX TY + t, so the key
+ * (id << 32) | depth bits orders the pairs by view, then tile, then depth,
+ * then entry index; the value is the entry index v n + g. ranges[V TX TY, 2].
+ * View v's part of the result is the single-view result for that camera
+ * with its values offset by v n and its ranges by the pairs of views < v. */
+gs_status gs_bin_sort_views(const gs_camera *cams, int32_t n_views, const gs_options *opt, int64_t n,
+                            const float *means2d, const float *depths, const int32_t *radii,
+                            const uint32_t *tiles_touched, void *workspace, size_t workspace_bytes,
+                            int64_t pair_capacity, uint64_t *keys, uint32_t *values, uint32_t *ranges,
+                            int64_t *n_pairs, void *stream);
+
+/* gs_render_fwd of all V views, one launch, on the output of gs_bin_sort_views. */
+gs_status gs_render_fwd_views(const gs_camera *cams, int32_t n_views, const gs_options *opt, int64_t n,
+                              const uint32_t *ranges, const uint32_t *values, int64_t n_pairs,
+                              const float *means2d, const float *conic_opacity, const float *rgb,
+                              float *image, float *final_T, uint32_t *n_contrib, void *stream);
+
+/* gs_render_bwd_raster of all V views: per entry v n + g, the pixel sums of
+ * view v, ADDED into grad2d[V, n, GS_GRAD2D_STRIDE] (zeroed by the caller). */
+gs_status gs_render_bwd_raster_views(const gs_camera *cams, int32_t n_views, const gs_options *opt, int64_t n,
+                                     const uint32_t *ranges, const uint32_t *values, int64_t n_pairs,
+                                     const float *means2d, const float *conic_opacity, const float *rgb,
+                                     const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
+                                     float *grad2d, void *stream);
+
+/* gs_preprocess_bwd of all V views: each Gaussian's gradient is the sum over
+ * the views that drew it, added once into (or with overwrite_grads = 1
+ * written as) the parameter gradients; dL_dmeans2d (nullable) gets each
+ * view's dL/d(u, v) at entry v n + g. stats (nullable) takes every drawn view
+ * as one call of gs_preprocess_bwd would (count += the number of such views).
+ * Equal to V single-view calls up to the order of the summation. */
+gs_status gs_preprocess_bwd_views(const gs_camera *cams, int32_t n_views, const gs_options *opt, int64_t n,
+                                  const float *means, const float *scales, const float *quats, const float *sh,
+                                  const float *conic_opacity, const int32_t *radii, const uint8_t *clamped,
+                                  const float *grad2d, float *dL_dmeans, float *dL_dscales, float *dL_dquats,
+                                  float *dL_dopacities, float *dL_dsh, float *dL_dmeans2d,
+                                  const gs_densify_stats *stats, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Optimizer update (phase U)
  * ------------------------------------------------------------------------ */
 

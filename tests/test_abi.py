@@ -124,3 +124,41 @@ def test_adam_arguments_rejected_before_launch():
     assert L.gs_adam_step(C.byref(o), 4, 0, five, five, five, five, d, d, None, None) == raster.GS_ERR_INVALID_ARG
     assert L.gs_adam_step(C.byref(o), 0, 16, None, None, None, None, None, None, None, None) == raster.GS_OK
 
+
+
+def test_views_arguments_rejected_before_launch():
+    """The batched calls check the view count, the total size and that every
+    camera is valid and of one image size, before any HIP call."""
+    L = raster.load_library()
+    sc = make_scene(5, 0, n=4)
+    opt = raster.make_options(3)
+    d = C.c_void_p(4096)
+    cams = raster.make_cameras(sc.cameras[:3])
+
+    def pre(cs, V, n=10):
+        return L.gs_preprocess_views(cs, V, C.byref(opt), n, *([d] * 12), None, None)
+
+    assert pre(cams, 0) == raster.GS_ERR_INVALID_ARG and b"n_views" in L.gs_last_error()
+    big = raster.make_cameras(sc.cameras * 3)  # 48 cameras
+    assert pre(big, raster.MAX_VIEWS + 1) == raster.GS_ERR_INVALID_ARG
+    assert pre(cams, 3, n=1 << 30) == raster.GS_ERR_INVALID_ARG
+    odd = raster.make_cameras(sc.cameras[:3])
+    odd[2].width = 1280
+    assert pre(odd, 3) == raster.GS_ERR_INVALID_ARG and b"camera 2" in L.gs_last_error()
+    bad = raster.make_cameras(sc.cameras[:3])
+    bad[1].fy = float("nan")
+    assert pre(bad, 3) == raster.GS_ERR_INVALID_ARG and b"camera 1" in L.gs_last_error()
+    n_pairs = C.c_int64(0)
+    st = L.gs_bin_sort_views(cams, 3, C.byref(opt), 100, d, d, d, d, C.c_void_p(4096 * 256), 16, 1000, None, d, d,
+                             C.byref(n_pairs), None)
+    assert st == raster.GS_ERR_INVALID_ARG and b"workspace" in L.gs_last_error()
+    assert L.gs_preprocess_views(cams, 3, C.byref(opt), 0, *([None] * 12), None, None) == raster.GS_OK
+
+
+def test_views_workspace_grows_with_views():
+    one = raster.gs_bin_sort_views_workspace_size(1, 1000, 10_000, 128, 128)
+    assert one == raster.gs_bin_sort_workspace_size(1000, 10_000, 128, 128)
+    four = raster.gs_bin_sort_views_workspace_size(4, 1000, 10_000, 128, 128)
+    assert four > one and four % 256 == 0
+    assert raster.gs_bin_sort_views_workspace_size(0, 1000, 10_000, 128, 128) == 0
+    assert raster.gs_bin_sort_views_workspace_size(raster.MAX_VIEWS + 1, 1000, 10_000, 128, 128) == 0
