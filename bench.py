@@ -203,6 +203,9 @@ def main():
     t_bwd = bwd_launch_ms * 1e-3  # the backward raster kernel's mean launch time in the timed steps
     valu_tops = BWD_OPS_PER_ENTRY * E_b / t_bwd / 1e12
 
+    batched = time_batched_views(args, raster, dev, sc, cams, opt, means, scales, quats, opac, sh, dLs, last_P,
+                                 1000.0 * elapsed / args.steps) if len(views) > 1 else None
+
     # measured denominators: HBM streaming read, and no-return fp32 atomic adds
     # in the backward's flush pattern (9 lanes on one record, records hashed
     # over the visible Gaussians)
@@ -314,12 +317,89 @@ def main():
         },
     }
 
+    if batched is not None:
+        result["batched_views"] = batched
     if args.cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sc, args, fr_state=dict(
             means2d=means2d.cpu().numpy(), conic=conic.cpu().numpy(), rgb=rgb.cpu().numpy(),
             radii=radii.cpu().numpy(), depths=depths.cpu().numpy(), values=r._values[:last_P[-1]].cpu().numpy(),
             ranges=rg_np, P=last_P[-1]), view=views[-1])
     print(json.dumps(result), flush=True)
+
+
+BATCH_STAGES = ["preprocess_views", "bin_sort_views", "render_fwd_views", "zero_pixel_sums",
+                "render_bwd_raster_views", "preprocess_bwd_views"]
+
+
+def time_batched_views(args, raster, dev, sc, cams, opt, means, scales, quats, opac, sh, dLs, last_P, serial_ms):
+    """The same step with all views in one launch per phase (the *_views
+    calls), timed the same way; per-view figures beside the serial loop's."""
+    import torch
+    V, n = len(cams), sc.n
+    W, H = cams[0].width, cams[0].height
+    ntiles = ((W + 15) // 16) * ((H + 15) // 16)
+    ca = raster.make_cameras(cams)
+    opt_w = raster.GsOptions.from_buffer_copy(opt)
+    opt_w.overwrite_grads = 1
+    E = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+    means2d, depths, conic, rgb = E((V, n, 2), torch.float32), E((V, n), torch.float32), E((V, n, 4), torch.float32), \
+        E((V, n, 3), torch.float32)
+    radii, tiles, clamped, mask = E((V, n), torch.int32), E((V, n), torch.int32), E((V, n), torch.uint8), \
+        E(n, torch.int32)
+    ranges = E((V * ntiles, 2), torch.int32)
+    cap = int(sum(last_P) * 1.02) + 4096
+    values = E(cap, torch.int32)
+    ws = E(raster.gs_bin_sort_views_workspace_size(V, n, cap, W, H), torch.uint8)
+    image, final_T, n_contrib = E((V, 3, H, W), torch.float32), E((V, H, W), torch.float32), E((V, H, W), torch.int32)
+    dL = torch.stack(dLs)
+    grad2d = E((V, n, raster.GRAD2D_STRIDE), torch.float32)
+    grads = raster.empty_grads(means, sh)
+    stream = torch.cuda.current_stream()
+    P_box = [0]
+
+    def step(ev):
+        mark = (lambda k: ev[k].record(stream)) if ev else (lambda k: None)
+        mark(0)
+        raster.gs_preprocess_views(ca, opt, means, scales, quats, opac, sh, means2d, depths, conic, rgb, radii, tiles,
+                                   clamped, mask)
+        mark(1)
+        P = raster.gs_bin_sort_views(ca, opt, n, means2d, depths, radii, tiles, ws, cap, None, values, ranges)
+        P_box[0] = P
+        mark(2)
+        raster.gs_render_fwd_views(ca, opt, n, ranges, values, P, means2d, conic, rgb, image, final_T, n_contrib)
+        mark(3)
+        grad2d.zero_()
+        mark(4)
+        raster.gs_render_bwd_raster_views(ca, opt, n, ranges, values, P, means2d, conic, rgb, final_T, n_contrib, dL,
+                                          grad2d)
+        mark(5)
+        raster.gs_preprocess_bwd_views(ca, opt_w, means, scales, quats, sh, conic, radii, clamped, grad2d,
+                                       grads["means"], grads["scales"], grads["quats"], grads["opacities"],
+                                       grads["sh"])
+        mark(6)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(None)
+    torch.cuda.synchronize()
+    ms = 1000.0 * (time.perf_counter() - t0) / args.steps
+    reps = min(args.steps, 5)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(BATCH_STAGES) + 1)] for _ in range(reps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    st = [sum(e[k].elapsed_time(e[k + 1]) for e in evs) / reps / V for k in range(len(BATCH_STAGES))]
+    log(f"[bench] batched {V} views: {ms:.3f} ms/step, {ms / V:.3f} ms/view (serial {serial_ms / V:.3f}); "
+        + ", ".join(f"{s} {t:.3f}" for s, t in zip(BATCH_STAGES, st)))
+    del ws, grad2d, dL, image
+    return {"views": V, "ms_per_step": round(ms, 4), "ms_per_view": round(ms / V, 4),
+            "serial_ms_per_view": round(serial_ms / V, 4), "speedup_vs_serial": round(serial_ms / ms, 3),
+            "pairs": P_box[0], "stages_ms_per_view": {s: round(float(t), 4) for s, t in zip(BATCH_STAGES, st)},
+            "note": "all views in one launch per phase (gs_*_views): parameters read once, one binning pass over "
+                    "the stacked tile grids, gradients summed per Gaussian before one write"}
 
 
 def pmc_traffic(kernel, config):
