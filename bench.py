@@ -114,7 +114,8 @@ def main():
     ntiles = ((W + 15) // 16) * ((H + 15) // 16)
 
     # persistent buffers, sized once (a first untimed frame per view measures P)
-    r = raster.Rasterizer(dev, want_keys=True)
+    # values and ranges only: the renderer reads no 64-bit keys (gs_bin_sort takes keys = NULL)
+    r = raster.Rasterizer(dev, want_keys=False)
     P_max = 0
     for v in views:
         pre = r.preprocess(cams[v], opt, means, scales, quats, opac, sh)
