@@ -6,7 +6,8 @@
   for all Gaussians, the full pair sort bit for bit, every pixel through the
   branch-exploring matcher, and the full backward), in seconds on the host's
   cores.
-- Config 5 (6M Gaussians, 16 views accumulated into one gradient) is checked
+- Config 5 (6M Gaussians, 16 views accumulated into one gradient, by the serial
+  view loop and by the batched calls) is checked
   on two views in full and, for the accumulation over all 16 views, on
   sampled Gaussians: the oracle's backward over just the pixels of a
   Gaussian's tile rectangle gives that Gaussian's pixel sums exactly, since
@@ -129,6 +130,87 @@ def test_full_multi_view_share():
         for k in acc:
             acc[k] += og[k]
     torch.cuda.synchronize()
+    for k in acc:
+        e = rel_l2(total[k].cpu().numpy().astype(np.float64)[pick], acc[k])
+        assert e <= 1e-3, (k, e)
+
+
+def _views_slice(fb, i, n):
+    """View i of a batched frame (the *_views calls) as frame_np gives a
+    single view: pair values and ranges shifted back to the view's own."""
+    W, H = fb.width, fb.height
+    ntiles = ((W + 15) // 16) * ((H + 15) // 16)
+    rg = fb.ranges.view(-1, ntiles, 2)[i].cpu().numpy().view(np.uint32).astype(np.int64)
+    full = rg[:, 1] > rg[:, 0]
+    start, end = (int(rg[full, 0].min()), int(rg[full, 1].max())) if full.any() else (0, 0)
+    co = fb.conic_opacity[i].cpu().numpy()
+    return dict(
+        means2d=fb.means2d[i].cpu().numpy().astype(np.float64), depth32=fb.depths[i].cpu().numpy(),
+        ldl=co[:, :3], conic=O.ldl_to_conic(co[:, :3]), opac=co[:, 3].astype(np.float64),
+        rgb=fb.rgb[i].cpu().numpy().astype(np.float64), radii=fb.radii[i].cpu().numpy(),
+        tiles=fb.tiles_touched[i].cpu().numpy().view(np.uint32), clamped=fb.clamped[i].cpu().numpy(),
+        values=(fb.values[start:end].cpu().numpy().view(np.uint32).astype(np.int64) - i * n).astype(np.uint32),
+        ranges=np.where(full[:, None], rg - start, 0).astype(np.uint32), image=fb.image[i].cpu().numpy(),
+        final_T=fb.final_T[i].cpu().numpy(), n_contrib=fb.n_contrib[i].cpu().numpy().view(np.uint32), P=end - start)
+
+
+def test_full_multi_view_batched():
+    """The 16 views of the 6M-Gaussian share in one launch per phase, as the
+    benchmark's batched step runs them: views 3 and 12 checked stage by stage
+    in full (projection, the pair sort bit for bit, every pixel), and the
+    16-view gradient sums of sampled Gaussians against the oracle's."""
+    sc = make_scene(5)
+    n, V = sc.n, len(sc.cameras)
+    rng = np.random.default_rng(57)
+    cand = np.sort(rng.choice(n, 4000, replace=False))
+    vis_any = np.zeros(len(cand), bool)
+    small = np.ones(len(cand), bool)
+    for cam in sc.cameras:
+        o = O.preprocess(sc.means[cand], sc.scales[cand], sc.quats[cand], sc.opacities[cand], sc.sh[cand], cam,
+                         sc.sh_degree)
+        vis_any |= o["radii"] > 0
+        small &= o["radii"] <= 60
+    pick = cand[vis_any & small][:24]
+    assert len(pick) >= 8, len(pick)
+    pd = params_dev(sc)
+    r = raster.ViewsRasterizer(pd["means"].device)
+    fb = r.forward_views(sc.cameras, pd["means"], pd["scales"], pd["quats"], pd["opacities"], pd["sh"],
+                         sc.sh_degree)
+    total = raster.zero_grads(pd["means"], pd["sh"])
+    r.backward_views(fb, pd["means"], pd["scales"], pd["quats"], pd["opacities"], pd["sh"],
+                     to_dev(sc.dL_dimage), total, overwrite=True)
+    torch.cuda.synchronize()
+    mask = fb.vis_mask.cpu().numpy().view(np.uint32)
+    acc = {k: np.zeros((len(pick),) + shape, np.float64) for k, shape in
+           (("means", (3,)), ("scales", (3,)), ("quats", (4,)), ("opacities", ()), ("sh", sc.sh.shape[1:]))}
+    P_sum = 0
+    for v in range(V):
+        cam = sc.cameras[v]
+        W, H = cam.width, cam.height
+        g = _views_slice(fb, v, n)
+        P_sum += g["P"]
+        np.testing.assert_array_equal((mask >> v) & 1, (g["radii"] > 0).astype(np.uint32))
+        if v in (3, 12):
+            check_preprocess(sc, v, g)
+            _, values, ranges = O.bin_sort(g["means2d"], g["radii"], g["depth32"], W, H)
+            assert g["P"] == len(values)
+            np.testing.assert_array_equal(g["values"], values)
+            np.testing.assert_array_equal(g["ranges"], ranges)
+            st = O.match_fwd(W, H, g["ranges"], g["values"], g["means2d"], g["conic"], g["opac"], g["rgb"],
+                             g["image"], g["final_T"], g["n_contrib"])
+            assert int((st == 3).sum()) == 0, (v, int((st == 3).sum()))
+            assert int((st >= 1).sum()) <= max(4, 1e-3 * st.size), int((st >= 1).sum())
+        vis = g["radii"][pick] > 0
+        if not vis.any():
+            continue
+        pix = _rect_pixels(g, pick[vis], W, H)
+        grad2d = O.render_bwd_pixels(W, H, n, g["ranges"], g["values"], g["means2d"], g["conic"], g["opac"],
+                                     g["rgb"], sc.dL_dimage[v], pix)
+        og = O.preprocess_bwd(sc.means[pick], sc.scales[pick], sc.quats[pick], sc.opacities[pick], sc.sh[pick], cam,
+                              sc.sh_degree, grad2d[pick])
+        for k in acc:
+            acc[k] += og[k]
+    assert P_sum == fb.n_pairs
     for k in acc:
         e = rel_l2(total[k].cpu().numpy().astype(np.float64)[pick], acc[k])
         assert e <= 1e-3, (k, e)
