@@ -126,11 +126,13 @@ gs_status check_views(const gs_camera* cams, int32_t V, const gs_options* opt, i
     return GS_OK;
 }
 
-// Host side of gs_bin_sort's pair-count readback: a small pinned buffer and an
-// event per (thread, device), created on first use and kept for the process.
+// Host side of gs_bin_sort's pair-count readback: a small pinned, host-coherent
+// buffer (written by a kernel through its device address) and an event per
+// (thread, device), created on first use and kept for the process.
 struct Readback {
     int device = -1;
     unsigned long long* host = nullptr;
+    unsigned long long* mapped = nullptr;
     hipEvent_t ev = nullptr;
 };
 
@@ -142,7 +144,10 @@ gs_status readback_for_current_device(Readback*& out) {
     if (dev < 0 || dev >= 16) return fail(GS_ERR_UNSUPPORTED, "device index %d >= 16", dev);
     Readback& r = slots[dev];
     if (r.device != dev) {
-        st = hip_check(hipHostMalloc((void**)&r.host, 64, hipHostMallocDefault), "hipHostMalloc");
+        st = hip_check(hipHostMalloc((void**)&r.host, 64, hipHostMallocMapped | hipHostMallocCoherent),
+                       "hipHostMalloc");
+        if (st != GS_OK) return st;
+        st = hip_check(hipHostGetDevicePointer((void**)&r.mapped, r.host, 0), "hipHostGetDevicePointer");
         if (st != GS_OK) return st;
         st = hip_check(hipEventCreateWithFlags(&r.ev, hipEventDisableTiming), "hipEventCreateWithFlags");
         if (st != GS_OK) return st;
@@ -246,7 +251,7 @@ gs_status gs_bin_sort(const gs_camera* cam, const gs_options* opt, int64_t n, co
         if (st != GS_OK) return st;
         char* ws = reinterpret_cast<char*>(workspace);
         st = hip_check(gs::launch_bin_count((int)n, 0, c.cam.TX, c.cam.TY, means2d, radii, depths, tiles_touched, ws, L,
-                                            rb->host, rb->ev, s),
+                                            rb->mapped, rb->ev, s),
                        "gs_bin_sort(count)");
         if (st != GS_OK) return st;
         // the one wait: for the pair count only; the depth sort keeps running
@@ -528,7 +533,7 @@ gs_status gs_bin_sort_views(const gs_camera* cams, int32_t n_views, const gs_opt
         if (st != GS_OK) return st;
         char* ws = reinterpret_cast<char*>(workspace);
         st = hip_check(gs::launch_bin_count((int)total, c.V > 1 ? (int)n : 0, TX, TY, means2d, radii, depths,
-                                            tiles_touched, ws, L, rb->host, rb->ev, s),
+                                            tiles_touched, ws, L, rb->mapped, rb->ev, s),
                        "gs_bin_sort_views(count)");
         if (st != GS_OK) return st;
         st = hip_check(hipEventSynchronize(rb->ev), "gs_bin_sort_views(wait)");

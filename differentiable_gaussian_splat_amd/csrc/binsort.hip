@@ -601,10 +601,13 @@ __global__ __launch_bounds__(SB) void k_pair_totals(int n, const uint32_t* __res
 
 // One 1024-thread block: counters[2] = P, counters[3] = P1, vis_scan[b] = the
 // exclusive scan of the blocks' visible counts, counters[0] = their total;
-// also clears the radix passes' digit-total buffers (rtot_words words).
+// also clears the radix passes' digit-total buffers (rtot_words words). P and
+// P1 also go straight to host[0..1]: pinned, host-coherent memory mapped into
+// the device's address space, so that the host reads them after the stream's
+// next event without a copy in the stream.
 __global__ __launch_bounds__(1024) void k_pair_sum(int nb, const u64* __restrict__ part, u64* __restrict__ vis_scan,
                                                  u64* __restrict__ counters, uint32_t* __restrict__ rtot,
-                                                 int rtot_words) {
+                                                 int rtot_words, u64* __restrict__ host) {
     __shared__ u64 s_w[2][16];
     __shared__ u64 s_v[16];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -654,6 +657,9 @@ __global__ __launch_bounds__(1024) void k_pair_sum(int nb, const u64* __restrict
         counters[2] = a;
         counters[3] = c;
         counters[4] = 0ull;
+        host[0] = a;
+        host[1] = c;
+        __threadfence_system();
     }
 }
 
@@ -987,16 +993,17 @@ BinLayout bin_layout(int64_t n, int64_t capacity, int TX, int TY) {
 
 hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means2d, const int* radii,
                             const float* depths, const uint32_t* tiles_touched, char* ws, const BinLayout& L,
-                            unsigned long long* host_counts, hipEvent_t ev, hipStream_t s) {
+                            unsigned long long* mapped_counts, hipEvent_t ev, hipStream_t s) {
     u64* counters = reinterpret_cast<u64*>(ws + L.counters);
     u64* partials = reinterpret_cast<u64*>(ws + L.partials);
     const float2* m2 = reinterpret_cast<const float2*>(means2d);
     uint32_t* rtot = reinterpret_cast<uint32_t*>(ws + L.counters) + 2 * NCOUNTERS;
     const int rtot_words = 2 * RT * 256;
+    u64* host = reinterpret_cast<u64*>(mapped_counts);
     hipError_t e = hipSuccess;
-    if (n == 0) {
-        e = fill(reinterpret_cast<uint32_t*>(counters), 2 * NCOUNTERS + rtot_words, 0u, s);
-        if (e == hipSuccess) e = hipMemcpyAsync(host_counts, &counters[2], 2 * sizeof(u64), hipMemcpyDeviceToHost, s);
+    if (n == 0) {  // no blocks: the totals are zero
+        k_pair_sum<<<1, 1024, 0, s>>>(0, nullptr, partials, counters, rtot, rtot_words, host);
+        e = hipGetLastError();
         if (e == hipSuccess) e = hipEventRecord(ev, s);
         return e;
     }
@@ -1007,9 +1014,8 @@ hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means
     const int nb = (n + ST - 1) / ST;
     u64* part = reinterpret_cast<u64*>(ws + L.pair_part);
     k_pair_totals<<<nb, SB, 0, s>>>(n, tiles_touched, m2, radii, nper, TX, TYv, part);
-    k_pair_sum<<<1, 1024, 0, s>>>(nb, part, partials, counters, rtot, rtot_words);
+    k_pair_sum<<<1, 1024, 0, s>>>(nb, part, partials, counters, rtot, rtot_words, host);
     e = hipGetLastError();
-    if (e == hipSuccess) e = hipMemcpyAsync(host_counts, &counters[2], 2 * sizeof(u64), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipEventRecord(ev, s);
     if (e != hipSuccess) return e;
     uint32_t* dk[2] = {reinterpret_cast<uint32_t*>(ws + L.dkeys[0]), reinterpret_cast<uint32_t*>(ws + L.dkeys[1])};

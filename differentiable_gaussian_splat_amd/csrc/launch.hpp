@@ -61,13 +61,14 @@ struct BinLayout {
 BinLayout bin_layout(int64_t n, int64_t capacity, int TX, int TY);
 
 // Phase 1 (no host dependence): pair count P and super-tile entry count P1
-// (copied to host_counts[0..1], pinned, with `ev` recorded after the copy),
+// (written by a kernel to mapped_counts[0..1], the device address of pinned
+// host-coherent memory, with `ev` recorded after that kernel),
 // visible compaction, depth sort and the per-Gaussian records. n entries; for
 // several views, nper entries per view and views stacked in a grid of TX x
 // (views * TYv) tiles (nper = 0: one view of TX x TYv tiles).
 hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means2d, const int* radii,
                             const float* depths, const uint32_t* tiles_touched, char* ws, const BinLayout& L,
-                            unsigned long long* host_counts, hipEvent_t ev, hipStream_t stream);
+                            unsigned long long* mapped_counts, hipEvent_t ev, hipStream_t stream);
 // Phase 2 (P, P1 known on the host, P within capacity): the pairs in (tile,
 // depth, index) order into `values` (and the 64-bit keys if non-NULL), and
 // ranges; TY is the whole (stacked) grid's tile rows.
