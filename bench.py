@@ -66,6 +66,33 @@ def parse():
     return ap.parse_args()
 
 
+def stage_rooflines(n, rows, pairs, ntiles, pixels, walked, bwd_bytes, stage_ms, views):
+    """Each stage's algorithmic HBM bytes per frame (the least any design
+    moves), its floor at the published 8 TB/s and its fraction of that floor;
+    the whole frame's floor is their sum. The two blending stages are VALU
+    bound (their fraction here is of the HBM floor only); both count a 40-byte
+    record per walked (tile, entry), the walk of each tile's deepest pixel."""
+    par = 4 * (11 + 3 * rows)  # one Gaussian's parameters (or their gradients)
+    P = float(np.mean(pairs))
+    by = {
+        "preprocess": n * (par + 49),                        # parameters in, projection out
+        "bin_sort": n * 20 + P * 4 + ntiles * 8,             # projection in, values and ranges out
+        "render_fwd": walked * 40 + pixels * 20,             # walked records in, image / T / n_contrib out
+        "zero_pixel_sums": n * 48,
+        "render_bwd_raster": bwd_bytes,                      # walked records, per-pixel inputs, sums out
+        # parameters, projection and sums in; gradients written (first view of a step) or read and written
+        "preprocess_bwd": n * (par + 16 + 4 + 1 + 48) + n * par * (1 + (views - 1) / views),
+    }
+    out, floor_total = {}, 0.0
+    for k, t in zip(STAGES, stage_ms):
+        floor = by[k] / (HBM_PEAK_GBPS * 1e9) * 1e3
+        floor_total += floor
+        out[k] = {"bound": "hbm", "bytes": int(by[k]), "floor_ms": round(floor, 4), "frac": round(floor / t, 4)}
+    out["frame"] = {"floor_ms": round(floor_total, 4), "frac": round(floor_total / float(sum(stage_ms)), 4),
+                    "note": "sum of the stage floors over the sum of the stage times; blending is VALU bound"}
+    return out
+
+
 def backward_bytes(n_contrib, ranges, W, H, n_touched):
     """Algorithmic HBM bytes of one gs_render_bwd_raster launch: per walked list
     entry the record read (value 4 + mean 8 + conic/opacity 16 + colour 12 =
@@ -259,9 +286,16 @@ def main():
     n_atomics = ATOMICS_PER_TILE_ENTRY * walked
     recs = torch.zeros((max(touched, 1), raster.GRAD2D_STRIDE), dtype=torch.float32, device=dev)
     t_at = timed(lambda: raster.gs_mb_atomic(recs, recs.shape[0], n_atomics, ATOMICS_PER_TILE_ENTRY), 3)
+    # the same backward raster with per-pixel atomics (no wave reduction): the pattern the pages measure
+    g2n = torch.zeros_like(grad2d)
+    cam_last, dl_last = cams[views[-1]], dLs[-1]
+    t_naive = timed(lambda: raster.gs_mb_render_bwd_naive(cam_last, opt, n, ranges, r._values, last_P[-1], means2d,
+                                                          conic, rgb, final_T, n_contrib, dl_last, g2n), 2)
+    del g2n
     atomic_rate = n_atomics / t_at
     del recs
     t_hbm_floor = bwd_bytes / (hbm_read * 1e9)
+    stage_roof = stage_rooflines(n, sh.shape[1], last_P, ntiles, W * H, walked, bwd_bytes, stage_ms, len(views))
     t_atomic_floor = n_atomics / atomic_rate
 
     result = {
@@ -294,6 +328,13 @@ def main():
             "traffic": pmc_traffic("k_render_bwd", args.config),
             "work": f"{BWD_OPS_PER_ENTRY} fp32 vector ops (an FMA counted once) per walked pixel-entry x E_b",
             "launch_ms": round(t_bwd * 1e3, 4),
+        },
+        "stage_rooflines": stage_roof,
+        "naive_atomic_bwd": {
+            "ms": round(t_naive * 1e3, 3), "atomics": 9 * E_b, "reduced_ms": round(t_bwd * 1e3, 4),
+            "atomics_reduced": n_atomics, "slowdown": round(t_naive / t_bwd, 1),
+            "note": "gs_mb_render_bwd_naive: each lane adds its own pixel's nine terms with its own atomics (about "
+                    "9 per blended pixel-entry), against the wave-reduced backward raster (9 per tile-entry)",
         },
         "bwd_hbm_atomic_roofline": {
             "hbm_bytes": bwd_bytes,

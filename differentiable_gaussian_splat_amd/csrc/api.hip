@@ -702,6 +702,30 @@ gs_status gs_adam_step(const gs_adam_options* opt, int64_t n, int32_t sh_rows, f
     }
 }
 
+gs_status gs_mb_render_bwd_naive(const gs_camera* cam, const gs_options* opt, int64_t n, const uint32_t* ranges,
+                                 const uint32_t* values, int64_t n_pairs, const float* means2d,
+                                 const float* conic_opacity, const float* rgb, const float* final_T,
+                                 const uint32_t* n_contrib, const float* dL_dimage, float* grad2d, void* stream) {
+    try {
+        g_err[0] = 0;
+        Checked c;
+        gs_status st = check_common(cam, opt, n, c);
+        if (st != GS_OK) return st;
+        if (n == 0 || n_pairs == 0) return GS_OK;
+        REQUIRE(n_pairs > 0 && n_pairs < ((int64_t)1 << 31), "n_pairs must be in [0, 2^31)");
+        REQUIRE(ranges && values && means2d && conic_opacity && rgb && final_T && n_contrib && dL_dimage && grad2d,
+                "gs_mb_render_bwd_naive: NULL array");
+        REQUIRE(aligned(grad2d, 16) && aligned(conic_opacity, 16) && aligned(means2d, 8) && aligned(ranges, 8),
+                "gs_mb_render_bwd_naive: misaligned array");
+        return hip_check(gs::launch_render_bwd_naive(c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
+                                                     conic_opacity, rgb, opt->bg, final_T, n_contrib, dL_dimage,
+                                                     grad2d, (hipStream_t)stream),
+                         "gs_mb_render_bwd_naive");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_mb_render_bwd_naive: unexpected exception");
+    }
+}
+
 gs_status gs_mb_hbm_read(const void* src, size_t bytes, float* sink, void* stream) {
     if (!src || !sink || bytes % 16 || !aligned(src, 16)) return fail(GS_ERR_INVALID_ARG, "gs_mb_hbm_read: bad args");
     return hip_check(gs::launch_mb_read(src, bytes, sink, (hipStream_t)stream), "gs_mb_hbm_read");

@@ -237,7 +237,10 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
 // restored entry by entry (T in front = T behind / (1 - alpha)); S = A . dL/dC
 // with A the colour behind the current entry (starting as the background), so
 // dL/dalpha = T (rgb . dL/dC - S).
-template <int PPL, int NB>
+// NAIVE (measurement only, PPL = 1): every lane adds its own pixel's terms
+// with its own atomics, the per-pixel pattern the DISTWAR and ARC pages
+// measure, instead of reducing over the wave first.
+template <int PPL, int NB, bool NAIVE = false>
 __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, int TY, const uint2* __restrict__ ranges,
                                                  const uint32_t* __restrict__ values,
                                                  const float2* __restrict__ means2d,
@@ -319,7 +322,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, int TY,
             float acc[GRAD2D_N];
 #pragma unroll
             for (int c = 0; c < GRAD2D_N; ++c) acc[c] = 0.f;
-            bool any = false;
+            bool any = false, mine = false;
 #pragma unroll
             for (int k = 0; k < PPL; ++k) {
                 if (!((bm >> k) & 1u)) continue;  // no pixel of band k blends this entry
@@ -331,6 +334,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, int TY,
                 const bool blended = pos < last[k] && al >= ALPHA_MIN;
                 if (!__any(blended)) continue;
                 any = true;
+                mine = mine || blended;
                 // branch-free within the band: a pixel that did not blend this entry takes
                 // alpha = 0, which leaves its T, S and every sum unchanged
                 const float av = blended ? al : 0.f;
@@ -356,6 +360,14 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, int TY,
                 acc[8] += hy;
             }
             if (!any) continue;
+            if (NAIVE) {
+                if (mine) {
+                    float* dst = grad2d + (size_t)s_g[j] * GRAD2D_STRIDE;
+#pragma unroll
+                    for (int c = 0; c < GRAD2D_N; ++c) atomicAdd(&dst[c], acc[c]);
+                }
+                continue;
+            }
             // per 16-lane row: values 0..7 by reduce-scatter (lane slot holds one), value 8 by a row sum
             const float u = row_reduce_scatter8(acc, c1, c2, c3);
             const float x8 = row_sum16(acc[8]);
@@ -429,6 +441,18 @@ hipError_t launch_render_bwd(int views, int W, int H, int TX, int TY, const uint
             k_render_bwd<4, BWD_BATCH><<<ntiles, 64, 0, stream>>>(W, H, TX, TY, rg, values, m2, co, rgb, bg[0], bg[1],
                                                                  bg[2], final_T, n_contrib, dL_dimage, grad2d);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_render_bwd_naive(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
+                                   const float* means2d, const float* conic_op, const float* rgb, const float* bg,
+                                   const float* final_T, const uint32_t* n_contrib, const float* dL_dimage,
+                                   float* grad2d, hipStream_t stream) {
+    const int ntiles = TX * TY;
+    if (ntiles == 0) return hipSuccess;
+    k_render_bwd<1, BWD_BATCH, true><<<ntiles * 4, 64, 0, stream>>>(
+        W, H, TX, TY, reinterpret_cast<const uint2*>(ranges), values, reinterpret_cast<const float2*>(means2d),
+        reinterpret_cast<const float4*>(conic_op), rgb, bg[0], bg[1], bg[2], final_T, n_contrib, dL_dimage, grad2d);
     return hipGetLastError();
 }
 

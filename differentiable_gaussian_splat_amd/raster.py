@@ -70,7 +70,7 @@ EXPORTS = ["gs_default_options", "gs_version", "gs_last_error", "gs_preprocess",
            "gs_bin_sort", "gs_render_fwd", "gs_render_bwd_workspace_size", "gs_render_bwd", "gs_render_bwd_raster",
            "gs_preprocess_bwd", "gs_preprocess_views", "gs_bin_sort_views_workspace_size", "gs_bin_sort_views",
            "gs_render_fwd_views", "gs_render_bwd_raster_views", "gs_preprocess_bwd_views", "gs_adam_step",
-           "gs_mb_hbm_read", "gs_mb_hbm_copy", "gs_mb_atomic"]
+           "gs_mb_render_bwd_naive", "gs_mb_hbm_read", "gs_mb_hbm_copy", "gs_mb_atomic"]
 MAX_VIEWS = 32
 GRAD2D_STRIDE = 12
 
@@ -126,6 +126,8 @@ def load_library(path: str = LIB_PATH):
         L.gs_preprocess_bwd_views.restype = i32
         L.gs_adam_step.argtypes = [C.POINTER(GsAdamOptions), i64, i32, PP, PP, PP, PP, P, P, P, P]
         L.gs_adam_step.restype = i32
+        L.gs_mb_render_bwd_naive.argtypes = [cam, opt, i64, P, P, i64] + [P] * 7 + [P]
+        L.gs_mb_render_bwd_naive.restype = i32
         L.gs_mb_hbm_read.argtypes = [P, sz, P, P]
         L.gs_mb_hbm_read.restype = i32
         L.gs_mb_hbm_copy.argtypes = [P, P, sz, P]
@@ -342,6 +344,14 @@ def gs_adam_step(opt: GsAdamOptions, params: dict, grads: dict, exp_avg: dict, e
                                      arr([exp_avg_sq[k] for k in PARAM_GROUPS]), _p(scales), _p(opacities),
                                      _p(grad_norm), _stream(stream))
     _check(st, "gs_adam_step")
+
+
+def gs_mb_render_bwd_naive(cam: GsCamera, opt: GsOptions, n, ranges, values, n_pairs, means2d, conic_opacity, rgb,
+                           final_T, n_contrib, dL_dimage, grad2d, stream=None):
+    st = load_library().gs_mb_render_bwd_naive(C.byref(cam), C.byref(opt), n, _p(ranges), _p(values), n_pairs,
+                                               _p(means2d), _p(conic_opacity), _p(rgb), _p(final_T), _p(n_contrib),
+                                               _p(dL_dimage), _p(grad2d), _stream(stream))
+    _check(st, "gs_mb_render_bwd_naive")
 
 
 def gs_mb_hbm_read(src, sink, stream=None):
