@@ -291,6 +291,10 @@ def main():
     cam_last, dl_last = cams[views[-1]], dLs[-1]
     t_naive = timed(lambda: raster.gs_mb_render_bwd_naive(cam_last, opt, n, ranges, r._values, last_P[-1], means2d,
                                                           conic, rgb, final_T, n_contrib, dl_last, g2n), 2)
+    lane_hist = torch.zeros(65, dtype=torch.int32, device=dev)
+    raster.gs_mb_render_bwd_naive(cam_last, opt, n, ranges, r._values, last_P[-1], means2d, conic, rgb, final_T,
+                                  n_contrib, dl_last, g2n, lane_hist)
+    lh = lane_hist.cpu().numpy().astype(np.float64)
     del g2n
     atomic_rate = n_atomics / t_at
     del recs
@@ -333,6 +337,11 @@ def main():
         "naive_atomic_bwd": {
             "ms": round(t_naive * 1e3, 3), "atomics": 9 * E_b, "reduced_ms": round(t_bwd * 1e3, 4),
             "atomics_reduced": n_atomics, "slowdown": round(t_naive / t_bwd, 1),
+            "lanes_per_update": {"steps": int(lh.sum()), "mean": round(float((lh * np.arange(65)).sum() / lh.sum()), 2),
+                                 "all_64": round(float(lh[64] / lh.sum()), 4),
+                                 "at_most_8": round(float(lh[1:9].sum() / lh.sum()), 4),
+                                 "quartiles": [int(np.searchsorted(np.cumsum(lh) / lh.sum(), q)) for q in
+                                               (0.25, 0.5, 0.75)]},
             "note": "gs_mb_render_bwd_naive: each lane adds its own pixel's nine terms with its own atomics (about "
                     "9 per blended pixel-entry), against the wave-reduced backward raster (9 per tile-entry)",
         },

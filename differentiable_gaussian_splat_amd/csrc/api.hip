@@ -705,7 +705,8 @@ gs_status gs_adam_step(const gs_adam_options* opt, int64_t n, int32_t sh_rows, f
 gs_status gs_mb_render_bwd_naive(const gs_camera* cam, const gs_options* opt, int64_t n, const uint32_t* ranges,
                                  const uint32_t* values, int64_t n_pairs, const float* means2d,
                                  const float* conic_opacity, const float* rgb, const float* final_T,
-                                 const uint32_t* n_contrib, const float* dL_dimage, float* grad2d, void* stream) {
+                                 const uint32_t* n_contrib, const float* dL_dimage, float* grad2d,
+                                 uint32_t* lane_hist, void* stream) {
     try {
         g_err[0] = 0;
         Checked c;
@@ -719,7 +720,7 @@ gs_status gs_mb_render_bwd_naive(const gs_camera* cam, const gs_options* opt, in
                 "gs_mb_render_bwd_naive: misaligned array");
         return hip_check(gs::launch_render_bwd_naive(c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
                                                      conic_opacity, rgb, opt->bg, final_T, n_contrib, dL_dimage,
-                                                     grad2d, (hipStream_t)stream),
+                                                     grad2d, lane_hist, (hipStream_t)stream),
                          "gs_mb_render_bwd_naive");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_mb_render_bwd_naive: unexpected exception");

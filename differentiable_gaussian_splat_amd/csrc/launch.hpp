@@ -89,10 +89,11 @@ hipError_t launch_render_bwd(int views, int W, int H, int TX, int TY, const uint
                              const float* dL_dimage, float* grad2d, hipStream_t stream);
 
 // The backward raster with per-pixel atomics (no wave reduction), one view: measurement only.
+// lane_hist (nullable, 65 counters): per (wave, entry) step, the count of lanes updating the Gaussian.
 hipError_t launch_render_bwd_naive(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
                                    const float* means2d, const float* conic_op, const float* rgb, const float* bg,
                                    const float* final_T, const uint32_t* n_contrib, const float* dL_dimage,
-                                   float* grad2d, hipStream_t stream);
+                                   float* grad2d, uint32_t* lane_hist, hipStream_t stream);
 
 hipError_t launch_mb_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_mb_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);

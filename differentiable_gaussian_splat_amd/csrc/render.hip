@@ -247,7 +247,8 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, int TY,
                                                  const float4* __restrict__ conic_op, const float* __restrict__ rgb,
                                                  float bg0, float bg1, float bg2, const float* __restrict__ final_T,
                                                  const uint32_t* __restrict__ n_contrib,
-                                                 const float* __restrict__ dL_dimage, float* __restrict__ grad2d) {
+                                                 const float* __restrict__ dL_dimage, float* __restrict__ grad2d,
+                                                 uint32_t* __restrict__ lane_hist = nullptr) {
     constexpr int BANDS = 4 / PPL;
     __shared__ Staged s_rec[NB];
     __shared__ uint32_t s_g[NB];
@@ -366,6 +367,9 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, int TY,
 #pragma unroll
                     for (int c = 0; c < GRAD2D_N; ++c) atomicAdd(&dst[c], acc[c]);
                 }
+                // how many lanes of the wave update this Gaussian together (the whole wave votes)
+                const uint64_t who = __ballot(mine);
+                if (lane_hist && lane == 0) atomicAdd(&lane_hist[__popcll(who)], 1u);
                 continue;
             }
             // per 16-lane row: values 0..7 by reduce-scatter (lane slot holds one), value 8 by a row sum
@@ -447,12 +451,13 @@ hipError_t launch_render_bwd(int views, int W, int H, int TX, int TY, const uint
 hipError_t launch_render_bwd_naive(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
                                    const float* means2d, const float* conic_op, const float* rgb, const float* bg,
                                    const float* final_T, const uint32_t* n_contrib, const float* dL_dimage,
-                                   float* grad2d, hipStream_t stream) {
+                                   float* grad2d, uint32_t* lane_hist, hipStream_t stream) {
     const int ntiles = TX * TY;
     if (ntiles == 0) return hipSuccess;
     k_render_bwd<1, BWD_BATCH, true><<<ntiles * 4, 64, 0, stream>>>(
         W, H, TX, TY, reinterpret_cast<const uint2*>(ranges), values, reinterpret_cast<const float2*>(means2d),
-        reinterpret_cast<const float4*>(conic_op), rgb, bg[0], bg[1], bg[2], final_T, n_contrib, dL_dimage, grad2d);
+        reinterpret_cast<const float4*>(conic_op), rgb, bg[0], bg[1], bg[2], final_T, n_contrib, dL_dimage, grad2d,
+        lane_hist);
     return hipGetLastError();
 }
 

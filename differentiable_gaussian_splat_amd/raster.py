@@ -126,7 +126,7 @@ def load_library(path: str = LIB_PATH):
         L.gs_preprocess_bwd_views.restype = i32
         L.gs_adam_step.argtypes = [C.POINTER(GsAdamOptions), i64, i32, PP, PP, PP, PP, P, P, P, P]
         L.gs_adam_step.restype = i32
-        L.gs_mb_render_bwd_naive.argtypes = [cam, opt, i64, P, P, i64] + [P] * 7 + [P]
+        L.gs_mb_render_bwd_naive.argtypes = [cam, opt, i64, P, P, i64] + [P] * 7 + [P, P]
         L.gs_mb_render_bwd_naive.restype = i32
         L.gs_mb_hbm_read.argtypes = [P, sz, P, P]
         L.gs_mb_hbm_read.restype = i32
@@ -347,10 +347,10 @@ def gs_adam_step(opt: GsAdamOptions, params: dict, grads: dict, exp_avg: dict, e
 
 
 def gs_mb_render_bwd_naive(cam: GsCamera, opt: GsOptions, n, ranges, values, n_pairs, means2d, conic_opacity, rgb,
-                           final_T, n_contrib, dL_dimage, grad2d, stream=None):
+                           final_T, n_contrib, dL_dimage, grad2d, lane_hist=None, stream=None):
     st = load_library().gs_mb_render_bwd_naive(C.byref(cam), C.byref(opt), n, _p(ranges), _p(values), n_pairs,
                                                _p(means2d), _p(conic_opacity), _p(rgb), _p(final_T), _p(n_contrib),
-                                               _p(dL_dimage), _p(grad2d), _stream(stream))
+                                               _p(dL_dimage), _p(grad2d), _p(lane_hist), _stream(stream))
     _check(st, "gs_mb_render_bwd_naive")
 
 

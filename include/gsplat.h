@@ -385,12 +385,15 @@ gs_status gs_adam_step(const gs_adam_options *opt, int64_t n, int32_t sh_rows, f
  * blended pixel-entry), the per-pixel pattern whose atomics the DISTWAR page
  * (abstract) finds to flood the L2 atomic units. Same arguments and result as
  * gs_render_bwd_raster, up to summation order; for timing the two against
- * each other only. */
+ * each other only. lane_hist (nullable, 65 uint32 counters, added to) gets,
+ * per (wave, list entry) step that some pixel blends, one count at the number
+ * of the wave's lanes that update that Gaussian together (the page observes
+ * that a warp's lanes mostly hit the same address, in varying numbers). */
 gs_status gs_mb_render_bwd_naive(const gs_camera *cam, const gs_options *opt, int64_t n,
                                  const uint32_t *ranges, const uint32_t *values, int64_t n_pairs,
                                  const float *means2d, const float *conic_opacity, const float *rgb,
                                  const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
-                                 float *grad2d, void *stream);
+                                 float *grad2d, uint32_t *lane_hist, void *stream);
 
 gs_status gs_mb_hbm_read(const void *src, size_t bytes, float *sink, void *stream);
 /* Copy `bytes` from src to dst -- HBM copy rate; also the reference kernel for

@@ -377,8 +377,13 @@ def test_naive_atomic_backward_matches_reduced():
     args = (fr.cam, fr.opt, n, fr.ranges, fr.values, fr.n_pairs, fr.means2d, fr.conic_opacity, fr.rgb, fr.final_T,
             fr.n_contrib, dL)
     raster.gs_render_bwd_raster(*args, red)
-    raster.gs_mb_render_bwd_naive(*args, naive)
+    hist = torch.zeros(65, dtype=torch.int32, device=red.device)
+    raster.gs_mb_render_bwd_naive(*args, naive, hist)
     torch.cuda.synchronize()
+    # lanes per (wave, entry) update: at least one, and never more updates than blended pixel-entries
+    h = hist.cpu().numpy().astype(np.int64)
+    assert h[0] == 0 and h.sum() > 0
+    assert (h * np.arange(65)).sum() <= int(fr.n_contrib.sum())
     a, b = red.cpu().numpy().astype(np.float64), naive.cpu().numpy().astype(np.float64)
     assert np.count_nonzero(a[:, :9]) > 0
     for c in range(9):
