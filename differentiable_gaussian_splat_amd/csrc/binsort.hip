@@ -803,34 +803,76 @@ struct PieceTiles {
 };
 
 // One wave per piece: for each tile lt of the super-tile (lane lt), the number
-// of the piece's entries whose rectangle holds it, to counts[pidx][lt]
-// (column sums of the piece's tile masks, one ballot per group and tile).
+// of the piece's entries whose rectangle holds it, to counts[pidx][lt]. An
+// entry's tiles inside the super-tile form a rectangle, so the counts are a
+// 2D prefix sum of a (SUPER + 1)^2 difference array: each entry adds +1 / -1
+// at its rectangle's four corners (LDS integer atomics, exact), then a row
+// pass and a column pass of running sums give every tile's count.
+constexpr int DGRID = SUPER + 1;
+
 __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int SX, int TX, int TY,
                                                  const uint32_t* __restrict__ pfirst, const uint2* __restrict__ sr,
                                                  const uint32_t* __restrict__ sval, const uint4* __restrict__ rec,
                                                  uint32_t* __restrict__ counts) {
+    __shared__ int s_diff[SB / 64][DGRID * DGRID];
     const int lane = threadIdx.x & 63;
     const int pidx = __builtin_amdgcn_readfirstlane(blockIdx.x * (SB / 64) + (int)(threadIdx.x >> 6));
-    if (pidx >= (int)*np_ptr) return;
+    if (pidx >= (int)*np_ptr) return;  // the whole wave: no block barrier follows
+    int* d = s_diff[threadIdx.x >> 6];
+    for (int k = lane; k < DGRID * DGRID; k += 64) d[k] = 0;
     int s, e0, e1;
     piece_of(pidx, S, pfirst, sr, s, e0, e1);
     const int sx0 = (s % SX) * SUPER, sy0 = (s / SX) * SUPER;
-    PieceTiles pt;
-    pt.load(e0, e1, sx0, sy0, min(SUPER, TX - sx0), min(SUPER, TY - sy0), sval, rec);
-    uint32_t cnt = 0;
-    uint64_t todo = pt.any;
-    while (todo) {
-        const int l = __builtin_ctzll(todo);
-        todo &= todo - 1ull;
-        uint32_t c = 0;
+    const int vw = min(SUPER, TX - sx0), vh = min(SUPER, TY - sy0);  // the super-tile's tiles inside the grid
+    uint32_t gi[PIECE_GROUPS];
+    uint4 rq[PIECE_GROUPS];
 #pragma unroll
-        for (int q = 0; q < PIECE_GROUPS; ++q) {
-            if (q >= pt.ng) break;
-            c += (uint32_t)__popcll(__ballot(pt.holds(q, l)));
+    for (int q = 0; q < PIECE_GROUPS; ++q) gi[q] = sval[min(e0 + 64 * q + lane, e1 - 1)];  // lanes past e1 repeat
+#pragma unroll
+    for (int q = 0; q < PIECE_GROUPS; ++q) rq[q] = rec[gi[q]];
+    wave_lds_sync();  // the cleared array is seen before the corners are added
+    // entries covering the whole super-tile (large Gaussians) share their four corners: they are
+    // counted with one ballot per group and added once, the others add their own corners
+    int n_full = 0;
+#pragma unroll
+    for (int q = 0; q < PIECE_GROUPS; ++q) {
+        const uint4 r = rq[q];
+        const int cx0 = max((int)(r.y & 0xffffu) - sx0, 0), cx1 = min((int)(r.y >> 16) - sx0, vw - 1);
+        const int cy0 = max((int)(r.z & 0xffffu) - sy0, 0), cy1 = min((int)(r.z >> 16) - sy0, vh - 1);
+        const bool valid = e0 + 64 * q + lane < e1 && cx0 <= cx1 && cy0 <= cy1;
+        const bool full = valid && cx0 == 0 && cy0 == 0 && cx1 == vw - 1 && cy1 == vh - 1;
+        n_full += __popcll(__ballot(full));
+        if (valid && !full) {
+            atomicAdd(&d[cy0 * DGRID + cx0], 1);
+            atomicAdd(&d[cy0 * DGRID + cx1 + 1], -1);
+            atomicAdd(&d[(cy1 + 1) * DGRID + cx0], -1);
+            atomicAdd(&d[(cy1 + 1) * DGRID + cx1 + 1], 1);
         }
-        cnt = lane == l ? c : cnt;
     }
-    counts[(size_t)pidx * 64 + lane] = cnt;
+    if (n_full && lane == 0) {
+        atomicAdd(&d[0], n_full);
+        atomicAdd(&d[vw], -n_full);
+        atomicAdd(&d[vh * DGRID], -n_full);
+        atomicAdd(&d[vh * DGRID + vw], n_full);
+    }
+    wave_lds_sync();
+    if (lane < DGRID) {  // running sums along each row
+        int run = 0;
+        for (int c = 0; c < DGRID; ++c) {
+            run += d[lane * DGRID + c];
+            d[lane * DGRID + c] = run;
+        }
+    }
+    wave_lds_sync();
+    if (lane < DGRID) {  // then down each column
+        int run = 0;
+        for (int r = 0; r < DGRID; ++r) {
+            run += d[r * DGRID + lane];
+            d[r * DGRID + lane] = run;
+        }
+    }
+    wave_lds_sync();
+    counts[(size_t)pidx * 64 + lane] = (uint32_t)d[(lane >> 3) * DGRID + (lane & 7)];
 }
 
 // Placement, with the roles turned: lane = entry of a 64-entry group of the
