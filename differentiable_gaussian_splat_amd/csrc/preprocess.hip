@@ -230,12 +230,15 @@ __device__ __forceinline__ void add_own_row(const float* row, float* __restrict_
     }
 }
 
-// SH rows move through LDS in chunks of CHUNK_K coefficients (24 floats per
-// Gaussian), so that a 64-Gaussian block needs 6.4 KB of LDS, not 12.5 KB:
+// SH rows move through LDS in chunks of CHUNK_K coefficients (3 CHUNK_K floats
+// per Gaussian; 8 rows: a 64-Gaussian block needs 6.4 KB of LDS, not 12.5 KB):
 // LDS, not registers, is what limits the resident waves of these kernels.
 constexpr int CHUNK_K = 8;
 constexpr int CHUNK_F = 3 * CHUNK_K;
+constexpr int CHUNK_Q = CHUNK_F / 4;                        // float4s per record and chunk
+constexpr int CHUNKS = (16 + CHUNK_K - 1) / CHUNK_K;        // chunks of the 16 rows of degree 3
 constexpr int CHUNK_STRIDE = CHUNK_F + 1;  // odd: lanes reading their own row hit distinct banks
+static_assert(CHUNK_K % 4 == 0, "a chunk is whole float4s");
 
 // Floats [c0, c0 + used) (used <= CHUNK_F) of each of the block's records
 // (records of `rec` floats from record `base`) to LDS rows of CHUNK_STRIDE
@@ -247,11 +250,11 @@ __device__ __forceinline__ void chunk_in(const float* __restrict__ src, float* d
     const int cnt = min(64, n - base);
     const float* r0 = src + (size_t)base * rec + c0;
     if (((rec | c0 | used) & 3) == 0 && ((uintptr_t)src & 15u) == 0) {
-        const int q = used >> 2;  // float4s per record, <= 6
+        const int q = used >> 2;  // float4s per record, <= CHUNK_Q
         const int total = cnt * q;
-        float4 v[6];
+        float4 v[CHUNK_Q];
 #pragma unroll
-        for (int m = 0; m < 6; ++m) {
+        for (int m = 0; m < CHUNK_Q; ++m) {
             const int f = m * 64 + lane;
             if (f < total) {
                 int j, c;
@@ -260,7 +263,7 @@ __device__ __forceinline__ void chunk_in(const float* __restrict__ src, float* d
             }
         }
 #pragma unroll
-        for (int m = 0; m < 6; ++m) {
+        for (int m = 0; m < CHUNK_Q; ++m) {
             const int f = m * 64 + lane;
             if (f < total) {
                 int j, c;
@@ -284,52 +287,7 @@ __device__ __forceinline__ void chunk_in(const float* __restrict__ src, float* d
     }
 }
 
-// The LDS rows back into floats [c0, c0 + used) of the records: written, or
-// with ADD added to what the records hold.
-template <bool ADD>
-__device__ __forceinline__ void chunk_out(const float* src, float* __restrict__ dst, int base, int n, int rec, int c0,
-                                          int used) {
-    const int lane = threadIdx.x;
-    const int cnt = min(64, n - base);
-    float* r0 = dst + (size_t)base * rec + c0;
-    if (((rec | c0 | used) & 3) == 0 && ((uintptr_t)dst & 15u) == 0) {
-        const int q = used >> 2;
-        const int total = cnt * q;
-        float4 v[6];
-        if (ADD) {
-#pragma unroll
-            for (int m = 0; m < 6; ++m) {
-                const int f = m * 64 + lane;
-                if (f < total) {
-                    int j, c;
-                    divmod_small(f, q, j, c);
-                    v[m] = *reinterpret_cast<const float4*>(r0 + (size_t)j * rec + 4 * c);
-                }
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < 6; ++m) {
-            const int f = m * 64 + lane;
-            if (f < total) {
-                int j, c;
-                divmod_small(f, q, j, c);
-                const float* sp = src + j * CHUNK_STRIDE + 4 * c;
-                float4 w = make_float4(sp[0], sp[1], sp[2], sp[3]);
-                if (ADD) w = make_float4(v[m].x + w.x, v[m].y + w.y, v[m].z + w.z, v[m].w + w.w);
-                *reinterpret_cast<float4*>(r0 + (size_t)j * rec + 4 * c) = w;
-            }
-        }
-        return;
-    }
-    for (int j = 0; j < cnt; ++j)
-        if (lane < used) {
-            float* d = r0 + (size_t)j * rec + lane;
-            *d = (ADD ? *d : 0.f) + src[j * CHUNK_STRIDE + lane];
-        }
-}
-
-// One lane's own record: floats [c0, c0 + used) to its LDS row, and back
-// (written, or with ADD added).
+// One lane's own record: floats [c0, c0 + used) to its LDS row.
 __device__ __forceinline__ void chunk_in_own(const float* __restrict__ src, float* row, size_t g, int rec, int c0,
                                              int used) {
     const float* r = src + g * (size_t)rec + c0;
@@ -343,24 +301,6 @@ __device__ __forceinline__ void chunk_in_own(const float* __restrict__ src, floa
         }
     } else {
         for (int e = 0; e < used; ++e) row[e] = r[e];
-    }
-}
-
-template <bool ADD>
-__device__ __forceinline__ void chunk_out_own(const float* row, float* __restrict__ dst, size_t g, int rec, int c0,
-                                              int used) {
-    float* r = dst + g * (size_t)rec + c0;
-    if (((used & 3) == 0) && ((uintptr_t)r & 15u) == 0) {
-        for (int e = 0; e < used; e += 4) {
-            float4 v = make_float4(row[e], row[e + 1], row[e + 2], row[e + 3]);
-            if (ADD) {
-                const float4 o = *reinterpret_cast<const float4*>(r + e);
-                v = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
-            }
-            *reinterpret_cast<float4*>(r + e) = v;
-        }
-    } else {
-        for (int e = 0; e < used; ++e) r[e] = (ADD ? r[e] : 0.f) + row[e];
     }
 }
 
@@ -461,7 +401,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(6))) void k_
     float* shg = s_sh + threadIdx.x * CHUNK_STRIDE;
     const bool dense = __popcll(__ballot(ok)) > SH_DENSE;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < CHUNKS; ++c) {
         const int k0 = c * CHUNK_K;
         if (k0 >= K) break;
         const int kc = min(CHUNK_K, K - k0);
