@@ -141,15 +141,21 @@ __device__ __forceinline__ int view_of_tile(int tile, int TX, int TY, int& tx, i
 }
 
 template <int PPL>
-__global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY, const uint2* __restrict__ ranges,
+__global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY, int ntiles,
+                                                 const uint2* __restrict__ ranges,
                                                  const uint32_t* __restrict__ values,
                                                  const float2* __restrict__ means2d,
                                                  const float4* __restrict__ conic_op, const float* __restrict__ rgb,
                                                  float bg0, float bg1, float bg2, float* __restrict__ image,
                                                  float* __restrict__ final_T, uint32_t* __restrict__ n_contrib) {
-    constexpr int BANDS = 4 / PPL;
+    static_assert(PPL == 1, "one band of 16x4 pixels per wave");
     __shared__ Staged s_rec[BATCH];
-    const int tile = blockIdx.x / BANDS, band = blockIdx.x - tile * BANDS;
+    // Workgroups go to the 8 XCDs round-robin by index (b -> XCD b % 8). Tile
+    // 8q + x takes workgroups 32q + 8 band + x, so its four band waves, which
+    // stage the same records, share XCD x and its L2.
+    const int b = blockIdx.x;
+    const int tile = ((b >> 5) << 3) + (b & 7), band = (b >> 3) & 3;
+    if (tile >= ntiles) return;
     int tx, ty;
     const size_t view_px = view_of_tile(tile, TX, TY, tx, ty) * (size_t)W * H;
     image += 3 * view_px;
@@ -240,21 +246,31 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
 // NAIVE (measurement only, PPL = 1): every lane adds its own pixel's terms
 // with its own atomics, the per-pixel pattern the DISTWAR and ARC pages
 // measure, instead of reducing over the wave first.
-template <int PPL, int NB, bool NAIVE = false>
-__global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, int TY, const uint2* __restrict__ ranges,
-                                                 const uint32_t* __restrict__ values,
-                                                 const float2* __restrict__ means2d,
-                                                 const float4* __restrict__ conic_op, const float* __restrict__ rgb,
-                                                 float bg0, float bg1, float bg2, const float* __restrict__ final_T,
-                                                 const uint32_t* __restrict__ n_contrib,
-                                                 const float* __restrict__ dL_dimage, float* __restrict__ grad2d,
-                                                 uint32_t* __restrict__ lane_hist = nullptr) {
-    constexpr int BANDS = 4 / PPL;
-    __shared__ Staged s_rec[NB];
-    __shared__ uint32_t s_g[NB];
-    __shared__ float s_part[NB * 4 * GRAD2D_N];  // [entry][row of 16 lanes][value]
-    __shared__ uint32_t s_has[NB];
-    const int tile = blockIdx.x / BANDS, band = blockIdx.x - tile * BANDS;
+// LDS of one backward wave: a batch of staged records, their Gaussians, the
+// per-row partial sums and which entries some pixel blended.
+template <int NB>
+struct BwdShared {
+    Staged rec[NB];
+    uint32_t g[NB];
+    float part[NB * 4 * GRAD2D_N];  // [entry][row of 16 lanes][value]
+    uint32_t has[NB];
+};
+
+// The backward of one wave: band `band` (of 4 / PPL) of tile `tile`. Of its
+// PPL row bands (16x4 pixels each, band k holding the lanes' k-th pixels),
+// only those set in band_sel are walked.
+template <int PPL, int NB, bool NAIVE>
+__device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, int W, int H, int TX, int TY,
+                                         const uint2* __restrict__ ranges, const uint32_t* __restrict__ values,
+                                         const float2* __restrict__ means2d, const float4* __restrict__ conic_op,
+                                         const float* __restrict__ rgb, float bg0, float bg1, float bg2,
+                                         const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib,
+                                         const float* __restrict__ dL_dimage, float* __restrict__ grad2d,
+                                         uint32_t* __restrict__ lane_hist, BwdShared<NB>& sh) {
+    Staged* s_rec = sh.rec;
+    uint32_t* s_g = sh.g;
+    float* s_part = sh.part;
+    uint32_t* s_has = sh.has;
     int tx, ty;
     const size_t view_px = view_of_tile(tile, TX, TY, tx, ty) * (size_t)W * H;
     final_T += view_px;
@@ -288,6 +304,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, int TY,
         g2[k] = in ? dL_dimage[2 * HW + p] : 0.f;
         S[k] = fmaf(bg0, g0[k], fmaf(bg1, g1[k], bg2 * g2[k]));
         band_last[k] = __builtin_amdgcn_readfirstlane(wave_max_u32(last[k]));  // deepest blended entry of band k
+        if (!((band_sel >> k) & 1u)) band_last[k] = 0u;  // no entry of row k is walked
     }
     uint32_t mylast = 0;
 #pragma unroll
@@ -393,6 +410,70 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, int TY,
     }
 }
 
+// One wave per band group: tile blockIdx.x / (4 / PPL), bands of PPL rows.
+template <int PPL, int NB, bool NAIVE = false>
+__global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, int TY, const uint2* __restrict__ ranges,
+                                                 const uint32_t* __restrict__ values,
+                                                 const float2* __restrict__ means2d,
+                                                 const float4* __restrict__ conic_op, const float* __restrict__ rgb,
+                                                 float bg0, float bg1, float bg2, const float* __restrict__ final_T,
+                                                 const uint32_t* __restrict__ n_contrib,
+                                                 const float* __restrict__ dL_dimage, float* __restrict__ grad2d,
+                                                 uint32_t* __restrict__ lane_hist = nullptr) {
+    constexpr int BANDS = 4 / PPL;
+    __shared__ BwdShared<NB> sh;
+    const int tile = blockIdx.x / BANDS, band = blockIdx.x - tile * BANDS;
+    bwd_walk<PPL, NB, NAIVE>(tile, band, 0xFu, W, H, TX, TY, ranges, values, means2d, conic_op, rgb, bg0, bg1, bg2,
+                             final_T, n_contrib, dL_dimage, grad2d, lane_hist, sh);
+}
+
+// Two waves per tile, the tile's walk deciding their roles. A wave walks its
+// list serially, entry after entry, so a tile whose walk is many times the
+// mean (a dense cluster) holds its SIMD long after the light tiles are done,
+// with few waves left to hide its latencies. Tiles that walk at least
+// `split_walk` entries go to both waves, each taking two of the four 16x4 row
+// bands (half the pixel work per entry, at the price of a second reduction);
+// the others stay with the first wave, four pixels per lane, and the second
+// returns at once. Both roles run the same four-band code.
+template <int NB>
+__global__ __launch_bounds__(64) void k_render_bwd_split(int W, int H, int TX, int TY, int ntiles,
+                                                       uint32_t split_walk, const uint2* __restrict__ ranges,
+                                                       const uint32_t* __restrict__ values,
+                                                       const float2* __restrict__ means2d,
+                                                       const float4* __restrict__ conic_op,
+                                                       const float* __restrict__ rgb, float bg0, float bg1, float bg2,
+                                                       const float* __restrict__ final_T,
+                                                       const uint32_t* __restrict__ n_contrib,
+                                                       const float* __restrict__ dL_dimage,
+                                                       float* __restrict__ grad2d) {
+    __shared__ BwdShared<NB> sh;
+    // Workgroups [0, ntiles) are the tiles' second waves (most return at once; a
+    // split tile's starts walking right away), then [ntiles, 2 ntiles) their
+    // first waves: one contiguous run of real work. (Interleaving a tile's
+    // waves instead put the working ones on a fixed stride of the dispatch
+    // order, which the hardware's round-robin placement mapped onto a fraction
+    // of the CUs.)
+    const int b = blockIdx.x;
+    const int sub = b < ntiles ? 1 : 0, tile = b - (1 - sub) * ntiles;
+    // the tile's walk: its deepest blended entry over all 256 pixels, at most the list's length
+    int tx, ty;
+    const uint32_t* nc = n_contrib + view_of_tile(tile, TX, TY, tx, ty) * (size_t)W * H;
+    const int lane = threadIdx.x;
+    const int px = tx * TILE + (lane & 15);
+    uint32_t walk = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int py = ty * TILE + (lane >> 4) + 4 * k;
+        if (px < W && py < H) walk = max(walk, nc[(size_t)py * W + px]);
+    }
+    const uint2 rg = ranges[tile];
+    walk = min((uint32_t)__builtin_amdgcn_readfirstlane(wave_max_u32(walk)), rg.y - rg.x);
+    const bool split = walk >= split_walk;
+    if (!split && sub != 0) return;
+    bwd_walk<4, NB, false>(tile, 0, split ? 3u << (2 * sub) : 0xFu, W, H, TX, TY, ranges, values, means2d, conic_op,
+                           rgb, bg0, bg1, bg2, final_T, n_contrib, dL_dimage, grad2d, nullptr, sh);
+}
+
 }  // namespace
 
 // Measured on the contention scene (1M Gaussians, 1920x1080): the forward is
@@ -402,9 +483,15 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, int TY,
 // more resident waves). On small frames one wave per tile leaves most SIMDs
 // idle, and the backward's per-wave walk time decides: there it splits a tile
 // over two or four band waves (measured on a 128x128 frame, 64 tiles: 87 ->
-// 42 us with four; 800x800, 2500 tiles: 247 -> 228 us with two).
+// 42 us with four; 800x800, 2500 tiles: 247 -> 228 us with two). On large
+// frames a tile walking 512 entries or more splits over two waves (k_render_bwd_split):
+// 1M Gaussians at 1080p 0.58 -> 0.52 ms, the first of 16 views of 6M
+// Gaussians 1.77 -> 1.58 ms, 20k large Gaussians unchanged; splitting from 256
+// or 384 entries, or into four waves, was slower (the extra reductions cost
+// more than the shorter walks give back).
 constexpr int FWD_PPL = 1;
 constexpr int BWD_BATCH = 32;
+constexpr uint32_t BWD_SPLIT_WALK = 512;
 
 int bwd_pixels_per_lane(int ntiles) {
     if (ntiles < 2048) return 1;
@@ -417,8 +504,8 @@ hipError_t launch_render_fwd(int views, int W, int H, int TX, int TY, const uint
                              const float* bg, float* image, float* final_T, uint32_t* n_contrib, hipStream_t stream) {
     const int ntiles = views * TX * TY;
     if (ntiles == 0) return hipSuccess;
-    k_render_fwd<FWD_PPL><<<ntiles * (4 / FWD_PPL), 64, 0, stream>>>(
-        W, H, TX, TY, reinterpret_cast<const uint2*>(ranges), values, reinterpret_cast<const float2*>(means2d),
+    k_render_fwd<FWD_PPL><<<32 * ((ntiles + 7) / 8), 64, 0, stream>>>(
+        W, H, TX, TY, ntiles, reinterpret_cast<const uint2*>(ranges), values, reinterpret_cast<const float2*>(means2d),
         reinterpret_cast<const float4*>(conic_op), rgb, bg[0], bg[1], bg[2], image, final_T, n_contrib);
     return hipGetLastError();
 }
@@ -442,8 +529,9 @@ hipError_t launch_render_bwd(int views, int W, int H, int TX, int TY, const uint
                                                                      bg[2], final_T, n_contrib, dL_dimage, grad2d);
             break;
         default:
-            k_render_bwd<4, BWD_BATCH><<<ntiles, 64, 0, stream>>>(W, H, TX, TY, rg, values, m2, co, rgb, bg[0], bg[1],
-                                                                 bg[2], final_T, n_contrib, dL_dimage, grad2d);
+            k_render_bwd_split<BWD_BATCH><<<2 * ntiles, 64, 0, stream>>>(W, H, TX, TY, ntiles, BWD_SPLIT_WALK, rg,
+                                                                        values, m2, co, rgb, bg[0], bg[1], bg[2],
+                                                                        final_T, n_contrib, dL_dimage, grad2d);
     }
     return hipGetLastError();
 }

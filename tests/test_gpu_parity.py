@@ -365,6 +365,27 @@ def test_large_tile_grid_two_pass_super_sort():
     _full_check(sc)
 
 
+def test_backward_split_of_deep_tiles():
+    """On grids of 4096 tiles or more, a tile whose walk reaches 512 entries is
+    shared by two backward waves (two row bands each), the others keep one.
+    1500 faint Gaussians heaped on the middle of a 1024x1024 frame walk about a
+    thousand entries there; a few hundred more are spread thinly elsewhere."""
+    rng = np.random.default_rng(11)
+    cam = Camera(1024, 1024, 1000.0, 1000.0, 512.0, 512.0, np.eye(3, dtype=np.float32), np.zeros(3, np.float32))
+    n_heap, n_rest = 1500, 400
+    sc = _scene_for(cam, n_heap + n_rest, rng, deg=1)
+    z = rng.uniform(3.0, 5.0, n_heap)
+    uv = rng.normal(512.0, 12.0, (n_heap, 2))
+    sc.means[:n_heap] = np.stack([(uv[:, 0] - 512.0) * z / 1000.0, (uv[:, 1] - 512.0) * z / 1000.0, z],
+                                 1).astype(np.float32)
+    sc.scales[:n_heap] = np.exp(rng.normal(-3.5, 0.2, (n_heap, 3))).astype(np.float32)
+    sc.opacities[:n_heap] = rng.uniform(0.01, 0.03, n_heap).astype(np.float32)
+    g, _ = _full_check(sc)
+    nc = g["n_contrib"].astype(np.int64)
+    walks = nc.reshape(64, 16, 64, 16).max(axis=(1, 3))
+    assert walks.max() >= 768 and ((walks > 0) & (walks < 512)).sum() > 100, (walks.max(), (walks >= 512).sum())
+
+
 def test_naive_atomic_backward_matches_reduced():
     """The measurement kernel with per-pixel atomics computes the same pixel
     sums as the wave-reduced backward raster (up to summation order)."""
