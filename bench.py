@@ -302,6 +302,8 @@ def main():
     stage_roof = stage_rooflines(n, sh.shape[1], last_P, ntiles, W * H, walked, bwd_bytes, stage_ms, len(views))
     t_atomic_floor = n_atomics / atomic_rate
 
+    # the backward raster's kernel at this grid size (see bwd_pixels_per_lane in render.hip)
+    bwd_kernel = "k_render_bwd_split" if ntiles >= 4096 else "k_render_bwd"
     result = {
         "metric": METRIC,
         "value": round(ms_per_frame, 4),
@@ -323,13 +325,13 @@ def main():
         },
         "stages_ms": {s: round(float(t), 4) for s, t in zip(STAGES, stage_ms)},
         "roofline": {
-            "kernel": "k_render_bwd",
+            "kernel": bwd_kernel,
             "bound": "alu",
             "achieved": round(valu_tops, 2),
             "peak": round(VALU_PEAK_TOPS, 1),
             "unit": "TFLOP/s",
             "frac": round(valu_tops / VALU_PEAK_TOPS, 4),
-            "traffic": pmc_traffic("k_render_bwd", args.config),
+            "traffic": pmc_traffic(bwd_kernel, args.config),
             "work": f"{BWD_OPS_PER_ENTRY} fp32 vector ops (an FMA counted once) per walked pixel-entry x E_b",
             "launch_ms": round(t_bwd * 1e3, 4),
         },
