@@ -302,8 +302,8 @@ def main():
     stage_roof = stage_rooflines(n, sh.shape[1], last_P, ntiles, W * H, walked, bwd_bytes, stage_ms, len(views))
     t_atomic_floor = n_atomics / atomic_rate
 
-    # the backward raster's kernel at this grid size (see bwd_pixels_per_lane in render.hip)
-    bwd_kernel = "k_render_bwd_split" if ntiles >= 4096 else "k_render_bwd"
+    # the backward raster's kernel for one view's grid (see bwd_layout in render.hip)
+    bwd_kernel = "k_render_bwd_split" if 4096 <= ntiles < 32768 else "k_render_bwd"
     result = {
         "metric": METRIC,
         "value": round(ms_per_frame, 4),

@@ -483,20 +483,26 @@ __global__ __launch_bounds__(64) void k_render_bwd_split(int W, int H, int TX, i
 // more resident waves). On small frames one wave per tile leaves most SIMDs
 // idle, and the backward's per-wave walk time decides: there it splits a tile
 // over two or four band waves (measured on a 128x128 frame, 64 tiles: 87 ->
-// 42 us with four; 800x800, 2500 tiles: 247 -> 228 us with two). On large
-// frames a tile walking 512 entries or more splits over two waves (k_render_bwd_split):
-// 1M Gaussians at 1080p 0.58 -> 0.52 ms, the first of 16 views of 6M
-// Gaussians 1.77 -> 1.58 ms, 20k large Gaussians unchanged; splitting from 256
-// or 384 entries, or into four waves, was slower (the extra reductions cost
-// more than the shorter walks give back).
+// 42 us with four; 800x800, 2500 tiles: 247 -> 228 us with two). On one
+// large frame a tile walking 512 entries or more splits over two waves
+// (k_render_bwd_split): 1M Gaussians at 1080p 0.59 -> 0.52 ms (means over 200
+// launches), one 1080p view of 6M Gaussians 1.94 -> 1.56 ms, 20k large
+// Gaussians 0.584 -> 0.598 ms; splitting from 256 or 384 entries, or into four
+// waves, was slower (the extra reductions cost more than the shorter walks give
+// back). A launch of many views (16 x 8160 tiles) keeps every SIMD busy to the
+// end without it, and there the split only adds work (0.515 -> 0.641 ms per
+// view): from 32768 tiles on, one wave per tile.
 constexpr int FWD_PPL = 1;
 constexpr int BWD_BATCH = 32;
 constexpr uint32_t BWD_SPLIT_WALK = 512;
 
-int bwd_pixels_per_lane(int ntiles) {
-    if (ntiles < 2048) return 1;
-    if (ntiles < 4096) return 2;
-    return 4;
+// Backward layouts by launch size (tiles over all views of the launch).
+enum class BwdLayout { Bands1, Bands2, Split, Tile };
+BwdLayout bwd_layout(int ntiles) {
+    if (ntiles < 2048) return BwdLayout::Bands1;   // four band waves per tile
+    if (ntiles < 4096) return BwdLayout::Bands2;   // two
+    if (ntiles < 32768) return BwdLayout::Split;   // one, two for deep tiles
+    return BwdLayout::Tile;                        // one
 }
 
 hipError_t launch_render_fwd(int views, int W, int H, int TX, int TY, const uint32_t* ranges,
@@ -519,19 +525,24 @@ hipError_t launch_render_bwd(int views, int W, int H, int TX, int TY, const uint
     const uint2* rg = reinterpret_cast<const uint2*>(ranges);
     const float2* m2 = reinterpret_cast<const float2*>(means2d);
     const float4* co = reinterpret_cast<const float4*>(conic_op);
-    switch (bwd_pixels_per_lane(ntiles)) {
-        case 1:
+    switch (bwd_layout(ntiles)) {
+        case BwdLayout::Bands1:
             k_render_bwd<1, BWD_BATCH><<<ntiles * 4, 64, 0, stream>>>(W, H, TX, TY, rg, values, m2, co, rgb, bg[0], bg[1],
                                                                      bg[2], final_T, n_contrib, dL_dimage, grad2d);
             break;
-        case 2:
+        case BwdLayout::Bands2:
             k_render_bwd<2, BWD_BATCH><<<ntiles * 2, 64, 0, stream>>>(W, H, TX, TY, rg, values, m2, co, rgb, bg[0], bg[1],
                                                                      bg[2], final_T, n_contrib, dL_dimage, grad2d);
             break;
-        default:
+        case BwdLayout::Split:
             k_render_bwd_split<BWD_BATCH><<<2 * ntiles, 64, 0, stream>>>(W, H, TX, TY, ntiles, BWD_SPLIT_WALK, rg,
                                                                         values, m2, co, rgb, bg[0], bg[1], bg[2],
                                                                         final_T, n_contrib, dL_dimage, grad2d);
+            break;
+        case BwdLayout::Tile:
+            k_render_bwd<4, BWD_BATCH><<<ntiles, 64, 0, stream>>>(W, H, TX, TY, rg, values, m2, co, rgb, bg[0], bg[1],
+                                                                 bg[2], final_T, n_contrib, dL_dimage, grad2d);
+            break;
     }
     return hipGetLastError();
 }
