@@ -159,6 +159,9 @@ def main():
     ranges = E((ntiles, 2), torch.int32)
     image, final_T, n_contrib = E((3, H, W), torch.float32), E((H, W), torch.float32), E((H, W), torch.int32)
     grad2d = E((n, raster.GRAD2D_STRIDE), torch.float32)
+    # the forward's render checkpoints, read by the backward raster of the same view (none on small grids)
+    nck = raster.gs_render_ckpt_bytes(W, H)
+    ckpt = E(nck, torch.uint8) if nck else None
     grads = raster.empty_grads(means, sh)
     stream = torch.cuda.current_stream()
     mk = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in views]
@@ -182,12 +185,13 @@ def main():
                                    r._values, ranges)
             last_P[vi] = P
             mark(2)
-            raster.gs_render_fwd(cam, opt, n, ranges, r._values, P, means2d, conic, rgb, image, final_T, n_contrib)
+            raster.gs_render_fwd(cam, opt, n, ranges, r._values, P, means2d, conic, rgb, image, final_T, n_contrib,
+                                 ckpt)
             mark(3)
             grad2d.zero_()  # the pixel sums belong to one view
             e[BWD0].record(stream)
             raster.gs_render_bwd_raster(cam, opt, n, ranges, r._values, P, means2d, conic, rgb, final_T, n_contrib,
-                                        dLs[vi], grad2d)
+                                        dLs[vi], grad2d, ckpt)
             e[BWD1].record(stream)
             raster.gs_preprocess_bwd(cam, opt_first if vi == 0 else opt, means, scales, quats, sh, conic, radii,
                                      clamped, grad2d, grads["means"], grads["scales"], grads["quats"],
@@ -303,7 +307,7 @@ def main():
     t_atomic_floor = n_atomics / atomic_rate
 
     # the backward raster's kernel for one view's grid (see bwd_layout in render.hip)
-    bwd_kernel = "k_render_bwd_split" if 4096 <= ntiles < 32768 else "k_render_bwd"
+    bwd_kernel = "k_render_bwd_pieces" if 4096 <= ntiles < 32768 else "k_render_bwd"
     result = {
         "metric": METRIC,
         "value": round(ms_per_frame, 4),

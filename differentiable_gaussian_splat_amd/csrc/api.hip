@@ -216,6 +216,11 @@ size_t gs_bin_sort_workspace_size(int64_t n, int64_t pair_capacity, int32_t widt
     return gs::bin_layout(n, pair_capacity, (width + 15) / 16, (height + 15) / 16).total;
 }
 
+size_t gs_render_ckpt_bytes(int32_t width, int32_t height) {
+    if (width <= 0 || height <= 0 || width > 32768 || height > 32768) return 0;
+    return gs::render_ckpt_bytes((width + 15) / 16, (height + 15) / 16);
+}
+
 gs_status gs_bin_sort(const gs_camera* cam, const gs_options* opt, int64_t n, const float* means2d,
                       const float* depths, const int32_t* radii, const uint32_t* tiles_touched, void* workspace,
                       size_t workspace_bytes, int64_t pair_capacity, uint64_t* keys, uint32_t* values,
@@ -272,9 +277,20 @@ gs_status gs_bin_sort(const gs_camera* cam, const gs_options* opt, int64_t n, co
     }
 }
 
+// The render checkpoints: null, or 16-byte aligned and at least
+// gs_render_ckpt_bytes of the camera's image size.
+static gs_status check_ckpt(const void* ckpt, size_t ckpt_bytes, const Checked& c) {
+    if (!ckpt) return GS_OK;
+    REQUIRE(aligned(ckpt, 16), "ckpt must be 16-byte aligned");
+    REQUIRE(ckpt_bytes >= gs::render_ckpt_bytes(c.cam.TX, c.cam.TY),
+            "ckpt_bytes %zu < gs_render_ckpt_bytes %zu", ckpt_bytes, gs::render_ckpt_bytes(c.cam.TX, c.cam.TY));
+    return GS_OK;
+}
+
 gs_status gs_render_fwd(const gs_camera* cam, const gs_options* opt, int64_t n, const uint32_t* ranges,
                         const uint32_t* values, int64_t n_pairs, const float* means2d, const float* conic_opacity,
-                        const float* rgb, float* image, float* final_T, uint32_t* n_contrib, void* stream) {
+                        const float* rgb, float* image, float* final_T, uint32_t* n_contrib, void* ckpt,
+                        size_t ckpt_bytes, void* stream) {
     try {
         g_err[0] = 0;
         Checked c;
@@ -295,9 +311,11 @@ gs_status gs_render_fwd(const gs_camera* cam, const gs_options* opt, int64_t n, 
             REQUIRE(aligned(conic_opacity, 16), "conic_opacity must be 16-byte aligned");
         }
         REQUIRE(aligned(ranges, 8), "ranges must be 8-byte aligned");
+        st = check_ckpt(ckpt, ckpt_bytes, c);
+        if (st != GS_OK) return st;
         return hip_check(gs::launch_render_fwd(1, c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
                                                conic_opacity, rgb, opt->bg, image, final_T, n_contrib,
-                                               (hipStream_t)stream),
+                                               static_cast<float*>(ckpt), (hipStream_t)stream),
                          "gs_render_fwd");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_render_fwd: unexpected exception");
@@ -315,8 +333,8 @@ gs_status gs_render_bwd(const gs_camera* cam, const gs_options* opt, int64_t n, 
                         const uint8_t* clamped, const uint32_t* ranges, const uint32_t* values, int64_t n_pairs,
                         const float* final_T, const uint32_t* n_contrib, const float* dL_dimage, float* dL_dmeans,
                         float* dL_dscales, float* dL_dquats, float* dL_dopacities, float* dL_dsh,
-                        float* dL_dmeans2d, void* workspace, size_t workspace_bytes, const gs_densify_stats* stats,
-                        void* stream) {
+                        float* dL_dmeans2d, void* workspace, size_t workspace_bytes, const void* ckpt,
+                        size_t ckpt_bytes, const gs_densify_stats* stats, void* stream) {
     try {
         g_err[0] = 0;
         Checked c;
@@ -353,6 +371,8 @@ gs_status gs_render_bwd(const gs_camera* cam, const gs_options* opt, int64_t n, 
                 "stats: grad_accum, count and max_radius must all be set");
         size_t need = gs_render_bwd_workspace_size(n);
         REQUIRE(workspace_bytes >= need, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+        st = check_ckpt(ckpt, ckpt_bytes, c);
+        if (st != GS_OK) return st;
         hipStream_t s = (hipStream_t)stream;
         float* grad2d = reinterpret_cast<float*>(workspace);
         st = hip_check(gs::launch_fill_u32(reinterpret_cast<uint32_t*>(grad2d), (size_t)n * gs::GRAD2D_STRIDE, 0u, s),
@@ -361,7 +381,7 @@ gs_status gs_render_bwd(const gs_camera* cam, const gs_options* opt, int64_t n, 
         if (n_pairs > 0) {
             st = hip_check(gs::launch_render_bwd(1, c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
                                                  conic_opacity, rgb, opt->bg, final_T, n_contrib, dL_dimage, grad2d,
-                                                 s),
+                                                 static_cast<const float*>(ckpt), s),
                            "gs_render_bwd(raster)");
             if (st != GS_OK) return st;
         }
@@ -378,7 +398,8 @@ gs_status gs_render_bwd(const gs_camera* cam, const gs_options* opt, int64_t n, 
 gs_status gs_render_bwd_raster(const gs_camera* cam, const gs_options* opt, int64_t n, const uint32_t* ranges,
                                const uint32_t* values, int64_t n_pairs, const float* means2d,
                                const float* conic_opacity, const float* rgb, const float* final_T,
-                               const uint32_t* n_contrib, const float* dL_dimage, float* grad2d, void* stream) {
+                               const uint32_t* n_contrib, const float* dL_dimage, float* grad2d, const void* ckpt,
+                               size_t ckpt_bytes, void* stream) {
     try {
         g_err[0] = 0;
         static_assert(GS_GRAD2D_STRIDE == gs::GRAD2D_STRIDE, "record stride");
@@ -402,9 +423,11 @@ gs_status gs_render_bwd_raster(const gs_camera* cam, const gs_options* opt, int6
         REQUIRE(aligned(conic_opacity, 16), "conic_opacity must be 16-byte aligned");
         REQUIRE(aligned(means2d, 8) && aligned(ranges, 8), "means2d and ranges must be 8-byte aligned");
         if (n_pairs == 0) return GS_OK;
+        st = check_ckpt(ckpt, ckpt_bytes, c);
+        if (st != GS_OK) return st;
         return hip_check(gs::launch_render_bwd(1, c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
                                                conic_opacity, rgb, opt->bg, final_T, n_contrib, dL_dimage, grad2d,
-                                               (hipStream_t)stream),
+                                               static_cast<const float*>(ckpt), (hipStream_t)stream),
                          "gs_render_bwd_raster");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_render_bwd_raster: unexpected exception");
@@ -578,7 +601,7 @@ gs_status gs_render_fwd_views(const gs_camera* cams, int32_t n_views, const gs_o
         REQUIRE(aligned(ranges, 8), "ranges must be 8-byte aligned");
         const gs::DevCam& d = c.first.cam;
         return hip_check(gs::launch_render_fwd(c.V, d.W, d.H, d.TX, d.TY, ranges, values, means2d, conic_opacity, rgb,
-                                               opt->bg, image, final_T, n_contrib, (hipStream_t)stream),
+                                               opt->bg, image, final_T, n_contrib, nullptr, (hipStream_t)stream),
                          "gs_render_fwd_views");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_render_fwd_views: unexpected exception");
@@ -614,7 +637,8 @@ gs_status gs_render_bwd_raster_views(const gs_camera* cams, int32_t n_views, con
         if (n_pairs == 0) return GS_OK;
         const gs::DevCam& d = c.first.cam;
         return hip_check(gs::launch_render_bwd(c.V, d.W, d.H, d.TX, d.TY, ranges, values, means2d, conic_opacity, rgb,
-                                               opt->bg, final_T, n_contrib, dL_dimage, grad2d, (hipStream_t)stream),
+                                               opt->bg, final_T, n_contrib, dL_dimage, grad2d, nullptr,
+                                               (hipStream_t)stream),
                          "gs_render_bwd_raster_views");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_render_bwd_raster_views: unexpected exception");

@@ -79,14 +79,19 @@ hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_
 
 // Blending of `views` views of W x H pixels (TX x TY tiles each) whose tile
 // lists are binned in one stacked grid; per-view images follow one another.
+// ckpt (nullable, render_ckpt_bytes(TX, TY) bytes): the forward's per-tile
+// checkpoints, which the backward of a one-view launch reads to cut deep tiles
+// into pieces; both ignore it where the backward's layout does not use it.
+size_t render_ckpt_bytes(int TX, int TY);
 hipError_t launch_render_fwd(int views, int W, int H, int TX, int TY, const uint32_t* ranges,
                              const uint32_t* values, const float* means2d, const float* conic_op, const float* rgb,
-                             const float* bg, float* image, float* final_T, uint32_t* n_contrib, hipStream_t stream);
+                             const float* bg, float* image, float* final_T, uint32_t* n_contrib, float* ckpt,
+                             hipStream_t stream);
 
 hipError_t launch_render_bwd(int views, int W, int H, int TX, int TY, const uint32_t* ranges,
                              const uint32_t* values, const float* means2d, const float* conic_op, const float* rgb,
                              const float* bg, const float* final_T, const uint32_t* n_contrib,
-                             const float* dL_dimage, float* grad2d, hipStream_t stream);
+                             const float* dL_dimage, float* grad2d, const float* ckpt, hipStream_t stream);
 
 // The backward raster with per-pixel atomics (no wave reduction), one view: measurement only.
 // lane_hist (nullable, 65 counters): per (wave, entry) step, the count of lanes updating the Gaussian.

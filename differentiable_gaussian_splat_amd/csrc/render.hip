@@ -27,6 +27,16 @@ namespace {
 
 constexpr int BATCH = 64;  // records staged per LDS batch
 
+// Render checkpoints (one view's tile grid): for each tile, the forward's
+// per-pixel state (T, C) after list entries CKPT_EVERY k - 1, k = 1..CKPT_SLOTS,
+// then the pixel's final colour: (CKPT_SLOTS + 1) x 256 float4 per tile, pixel
+// (row r, column c) of the tile at float4 16 r + c of a slot. A slot is written
+// only when the tile's band wave walks past its entry; the backward reads only
+// such slots (see bwd_walk).
+constexpr int CKPT_EVERY = 256;
+constexpr int CKPT_SLOTS = 4;
+static_assert(CKPT_EVERY % BATCH == 0, "checkpoints fall on batch ends");
+
 // A staged record: (w0, dy0, a2, beta), (g2, log2 o, r, g), b. One LDS
 // address serves all three reads.
 struct alignas(16) Staged {
@@ -147,7 +157,8 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
                                                  const float2* __restrict__ means2d,
                                                  const float4* __restrict__ conic_op, const float* __restrict__ rgb,
                                                  float bg0, float bg1, float bg2, float* __restrict__ image,
-                                                 float* __restrict__ final_T, uint32_t* __restrict__ n_contrib) {
+                                                 float* __restrict__ final_T, uint32_t* __restrict__ n_contrib,
+                                                 float4* __restrict__ ckpt) {
     static_assert(PPL == 1, "one band of 16x4 pixels per wave");
     __shared__ Staged s_rec[BATCH];
     // Workgroups go to the 8 XCDs round-robin by index (b -> XCD b % 8). Tile
@@ -187,6 +198,7 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
         return __any(l != 0.f);
     };
     const uint2 rg = ranges[tile];
+    bool wrote_ckpt = false;
     for (uint32_t bs = rg.x; bs < rg.y; bs += BATCH) {
         if (!walking()) break;
         set_walk_priority(bs - rg.x);  // a wave still walking deep into its list is a heavy one
@@ -223,7 +235,19 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
             }
         }
         __syncthreads();
+        if (ckpt) {
+            // the state after a whole batch that ends a checkpoint interval, while still walking
+            const uint32_t done = bs - rg.x + BATCH;
+            if (bs + BATCH <= rg.y && done % CKPT_EVERY == 0 && done / CKPT_EVERY <= CKPT_SLOTS && walking()) {
+                ckpt[((size_t)tile * (CKPT_SLOTS + 1) + done / CKPT_EVERY - 1) * 256 + band * 64 + lane] =
+                    make_float4(T[0], C0[0], C1[0], C2[0]);
+                wrote_ckpt = true;
+            }
+        }
     }
+    if (wrote_ckpt)  // the final colour, beside the checkpoints
+        ckpt[((size_t)tile * (CKPT_SLOTS + 1) + CKPT_SLOTS) * 256 + band * 64 + lane] =
+            make_float4(C0[0], C1[0], C2[0], T[0]);
     const size_t HW = (size_t)W * H;
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
@@ -258,9 +282,16 @@ struct BwdShared {
 
 // The backward of one wave: band `band` (of 4 / PPL) of tile `tile`. Of its
 // PPL row bands (16x4 pixels each, band k holding the lanes' k-th pixels),
-// only those set in band_sel are walked.
+// only those set in band_sel are walked, and only list entries [walk_lo,
+// walk_hi). A row band whose pixels blend nothing at or past walk_hi starts
+// from the final state (T = final_T, colour behind = background); the others
+// start from the forward's checkpoint `ck` after entry walk_hi - 1 (T there,
+// and the colour behind it, (C_final - C there + final_T bg) / T), with
+// ck_end holding C_final. ck is null when walk_hi is past the walk.
 template <int PPL, int NB, bool NAIVE>
-__device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, int W, int H, int TX, int TY,
+__device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, int walk_lo, int walk_hi,
+                                         const float4* __restrict__ ck, const float4* __restrict__ ck_end,
+                                         int W, int H, int TX, int TY,
                                          const uint2* __restrict__ ranges, const uint32_t* __restrict__ values,
                                          const float2* __restrict__ means2d, const float4* __restrict__ conic_op,
                                          const float* __restrict__ rgb, float bg0, float bg1, float bg2,
@@ -305,6 +336,13 @@ __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, 
         S[k] = fmaf(bg0, g0[k], fmaf(bg1, g1[k], bg2 * g2[k]));
         band_last[k] = __builtin_amdgcn_readfirstlane(wave_max_u32(last[k]));  // deepest blended entry of band k
         if (!((band_sel >> k) & 1u)) band_last[k] = 0u;  // no entry of row k is walked
+        if (ck && band_last[k] > (uint32_t)walk_hi) {   // row band k walked past walk_hi in the forward
+            const int lp = (band * PPL + k) * 64 + lane;  // the pixel's float4 in a checkpoint slot
+            const float4 c = ck[lp], e = ck_end[lp];
+            const float behind = fmaf(g0[k], e.x - c.y, fmaf(g1[k], e.y - c.z, g2[k] * (e.z - c.w)));
+            S[k] = in ? fmaf(T[k], S[k], behind) / c.x : 0.f;
+            T[k] = in ? c.x : 1.f;
+        }
     }
     uint32_t mylast = 0;
 #pragma unroll
@@ -313,10 +351,10 @@ __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, 
     const float by_lo = (float)(ty * TILE + band * 4 * PPL) + 0.5f;
     const uint2 rg = ranges[tile];
     // never walk past the tile's list, whatever n_contrib holds
-    const uint32_t maxlast = min(mylast, rg.y - rg.x);
-    set_walk_priority(maxlast);
-    for (int hi = (int)maxlast; hi > 0; hi -= NB) {
-        const int lo = max(0, hi - NB);
+    const uint32_t maxlast = min(min(mylast, rg.y - rg.x), (uint32_t)walk_hi);
+    set_walk_priority(maxlast - min(maxlast, (uint32_t)walk_lo));
+    for (int hi = (int)maxlast; hi > walk_lo; hi -= NB) {
+        const int lo = max(walk_lo, hi - NB);
         const int cnt = hi - lo;
         uint32_t bands = 0u;
         if (lane < cnt) {
@@ -423,8 +461,9 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, int TY,
     constexpr int BANDS = 4 / PPL;
     __shared__ BwdShared<NB> sh;
     const int tile = blockIdx.x / BANDS, band = blockIdx.x - tile * BANDS;
-    bwd_walk<PPL, NB, NAIVE>(tile, band, 0xFu, W, H, TX, TY, ranges, values, means2d, conic_op, rgb, bg0, bg1, bg2,
-                             final_T, n_contrib, dL_dimage, grad2d, lane_hist, sh);
+    bwd_walk<PPL, NB, NAIVE>(tile, band, 0xFu, 0, INT32_MAX, nullptr, nullptr, W, H, TX, TY, ranges, values,
+                             means2d, conic_op, rgb, bg0, bg1, bg2, final_T, n_contrib, dL_dimage, grad2d, lane_hist,
+                             sh);
 }
 
 // Two waves per tile, the tile's walk deciding their roles. A wave walks its
@@ -470,8 +509,56 @@ __global__ __launch_bounds__(64) void k_render_bwd_split(int W, int H, int TX, i
     walk = min((uint32_t)__builtin_amdgcn_readfirstlane(wave_max_u32(walk)), rg.y - rg.x);
     const bool split = walk >= split_walk;
     if (!split && sub != 0) return;
-    bwd_walk<4, NB, false>(tile, 0, split ? 3u << (2 * sub) : 0xFu, W, H, TX, TY, ranges, values, means2d, conic_op,
-                           rgb, bg0, bg1, bg2, final_T, n_contrib, dL_dimage, grad2d, nullptr, sh);
+    bwd_walk<4, NB, false>(tile, 0, split ? 3u << (2 * sub) : 0xFu, 0, INT32_MAX, nullptr, nullptr, W, H, TX, TY,
+                           ranges, values, means2d, conic_op, rgb, bg0, bg1, bg2, final_T, n_contrib, dL_dimage,
+                           grad2d, nullptr, sh);
+}
+
+// With the forward's checkpoints: a tile's walk is cut into pieces of
+// CKPT_EVERY entries (the last piece taking the rest, at most CKPT_SLOTS + 1
+// pieces), one wave each, every wave over all four row bands. The piece
+// [lo, hi) starts from the checkpoint after entry hi - 1, so the pieces are
+// independent: a deep tile's walk is spread over several waves without the
+// extra per-entry reductions of a split by bands. Workgroup b is piece
+// (b / ntiles + 1) % (CKPT_SLOTS + 1) of tile b % ntiles: the later pieces of
+// every tile come first (most return at once), the first pieces last.
+template <int NB>
+__global__ __launch_bounds__(64) void k_render_bwd_pieces(int W, int H, int TX, int TY, int ntiles,
+                                                        const float4* __restrict__ ckpt,
+                                                        const uint2* __restrict__ ranges,
+                                                        const uint32_t* __restrict__ values,
+                                                        const float2* __restrict__ means2d,
+                                                        const float4* __restrict__ conic_op,
+                                                        const float* __restrict__ rgb, float bg0, float bg1, float bg2,
+                                                        const float* __restrict__ final_T,
+                                                        const uint32_t* __restrict__ n_contrib,
+                                                        const float* __restrict__ dL_dimage,
+                                                        float* __restrict__ grad2d) {
+    __shared__ BwdShared<NB> sh;
+    constexpr int PIECES = CKPT_SLOTS + 1;
+    const int b = blockIdx.x;
+    const int tile = b % ntiles, piece = (b / ntiles + 1) % PIECES;
+    // the tile's walk: its deepest blended entry over all 256 pixels, at most the list's length
+    int tx, ty;
+    const uint32_t* nc = n_contrib + view_of_tile(tile, TX, TY, tx, ty) * (size_t)W * H;
+    const int lane = threadIdx.x;
+    const int px = tx * TILE + (lane & 15);
+    uint32_t walk = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int py = ty * TILE + (lane >> 4) + 4 * k;
+        if (px < W && py < H) walk = max(walk, nc[(size_t)py * W + px]);
+    }
+    const uint2 rg = ranges[tile];
+    walk = min((uint32_t)__builtin_amdgcn_readfirstlane(wave_max_u32(walk)), rg.y - rg.x);
+    const int pieces = min((int)((walk + CKPT_EVERY - 1) / CKPT_EVERY), PIECES);
+    if (piece >= max(pieces, 1)) return;
+    const bool tail = piece >= pieces - 1;  // the last piece walks to the end from the final state
+    const int lo = piece * CKPT_EVERY, hi = tail ? INT32_MAX : lo + CKPT_EVERY;
+    const float4* tck = ckpt + (size_t)tile * PIECES * 256;
+    bwd_walk<4, NB, false>(tile, 0, 0xFu, lo, hi, tail ? nullptr : tck + (size_t)piece * 256, tck + CKPT_SLOTS * 256,
+                           W, H, TX, TY, ranges, values, means2d, conic_op, rgb, bg0, bg1, bg2, final_T, n_contrib,
+                           dL_dimage, grad2d, nullptr, sh);
 }
 
 }  // namespace
@@ -505,26 +592,41 @@ BwdLayout bwd_layout(int ntiles) {
     return BwdLayout::Tile;                        // one
 }
 
+size_t render_ckpt_bytes(int TX, int TY) {
+    const int ntiles = TX * TY;
+    if (bwd_layout(ntiles) != BwdLayout::Split) return 0;
+    return (size_t)ntiles * (CKPT_SLOTS + 1) * 256 * sizeof(float4);
+}
+
 hipError_t launch_render_fwd(int views, int W, int H, int TX, int TY, const uint32_t* ranges,
                              const uint32_t* values, const float* means2d, const float* conic_op, const float* rgb,
-                             const float* bg, float* image, float* final_T, uint32_t* n_contrib, hipStream_t stream) {
+                             const float* bg, float* image, float* final_T, uint32_t* n_contrib, float* ckpt,
+                             hipStream_t stream) {
     const int ntiles = views * TX * TY;
     if (ntiles == 0) return hipSuccess;
+    // checkpoints only where the backward reads them: one view, the split layout
+    float4* ck = (views == 1 && bwd_layout(ntiles) == BwdLayout::Split) ? reinterpret_cast<float4*>(ckpt) : nullptr;
     k_render_fwd<FWD_PPL><<<32 * ((ntiles + 7) / 8), 64, 0, stream>>>(
         W, H, TX, TY, ntiles, reinterpret_cast<const uint2*>(ranges), values, reinterpret_cast<const float2*>(means2d),
-        reinterpret_cast<const float4*>(conic_op), rgb, bg[0], bg[1], bg[2], image, final_T, n_contrib);
+        reinterpret_cast<const float4*>(conic_op), rgb, bg[0], bg[1], bg[2], image, final_T, n_contrib, ck);
     return hipGetLastError();
 }
 
 hipError_t launch_render_bwd(int views, int W, int H, int TX, int TY, const uint32_t* ranges,
                              const uint32_t* values, const float* means2d, const float* conic_op, const float* rgb,
                              const float* bg, const float* final_T, const uint32_t* n_contrib,
-                             const float* dL_dimage, float* grad2d, hipStream_t stream) {
+                             const float* dL_dimage, float* grad2d, const float* ckpt, hipStream_t stream) {
     const int ntiles = views * TX * TY;
     if (ntiles == 0) return hipSuccess;
     const uint2* rg = reinterpret_cast<const uint2*>(ranges);
     const float2* m2 = reinterpret_cast<const float2*>(means2d);
     const float4* co = reinterpret_cast<const float4*>(conic_op);
+    if (ckpt && views == 1 && bwd_layout(ntiles) == BwdLayout::Split) {
+        k_render_bwd_pieces<BWD_BATCH><<<(CKPT_SLOTS + 1) * ntiles, 64, 0, stream>>>(
+            W, H, TX, TY, ntiles, reinterpret_cast<const float4*>(ckpt), rg, values, m2, co, rgb, bg[0], bg[1], bg[2],
+            final_T, n_contrib, dL_dimage, grad2d);
+        return hipGetLastError();
+    }
     switch (bwd_layout(ntiles)) {
         case BwdLayout::Bands1:
             k_render_bwd<1, BWD_BATCH><<<ntiles * 4, 64, 0, stream>>>(W, H, TX, TY, rg, values, m2, co, rgb, bg[0], bg[1],

@@ -67,7 +67,8 @@ class GsAdamOptions(C.Structure):
 
 
 EXPORTS = ["gs_default_options", "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_sort_workspace_size",
-           "gs_bin_sort", "gs_render_fwd", "gs_render_bwd_workspace_size", "gs_render_bwd", "gs_render_bwd_raster",
+           "gs_bin_sort", "gs_render_fwd", "gs_render_ckpt_bytes", "gs_render_bwd_workspace_size", "gs_render_bwd",
+           "gs_render_bwd_raster",
            "gs_preprocess_bwd", "gs_preprocess_views", "gs_bin_sort_views_workspace_size", "gs_bin_sort_views",
            "gs_render_fwd_views", "gs_render_bwd_raster_views", "gs_preprocess_bwd_views", "gs_adam_step",
            "gs_mb_render_bwd_naive", "gs_mb_hbm_read", "gs_mb_hbm_copy", "gs_mb_atomic"]
@@ -99,15 +100,17 @@ def load_library(path: str = LIB_PATH):
         L.gs_bin_sort_workspace_size.restype = sz
         L.gs_bin_sort.argtypes = [cam, opt, i64, P, P, P, P, P, sz, i64, P, P, P, C.POINTER(C.c_int64), P]
         L.gs_bin_sort.restype = i32
-        L.gs_render_fwd.argtypes = [cam, opt, i64, P, P, i64, P, P, P, P, P, P, P]
+        L.gs_render_fwd.argtypes = [cam, opt, i64, P, P, i64, P, P, P, P, P, P, P, sz, P]
         L.gs_render_fwd.restype = i32
+        L.gs_render_ckpt_bytes.argtypes = [i32, i32]
+        L.gs_render_ckpt_bytes.restype = sz
         L.gs_render_bwd_workspace_size.argtypes = [i64]
         L.gs_render_bwd_workspace_size.restype = sz
         dst = C.POINTER(GsDensifyStats)
         L.gs_render_bwd.argtypes = ([cam, opt, i64] + [P] * 5 + [P] * 5 + [P, P, i64] + [P] * 3 + [P] * 6 +
-                                    [P, sz, dst, P])
+                                    [P, sz, P, sz, dst, P])
         L.gs_render_bwd.restype = i32
-        L.gs_render_bwd_raster.argtypes = [cam, opt, i64, P, P, i64] + [P] * 7 + [P]
+        L.gs_render_bwd_raster.argtypes = [cam, opt, i64, P, P, i64] + [P] * 7 + [P, sz, P]
         L.gs_render_bwd_raster.restype = i32
         L.gs_preprocess_bwd.argtypes = [cam, opt, i64] + [P] * 8 + [P] * 6 + [dst, P]
         L.gs_preprocess_bwd.restype = i32
@@ -209,11 +212,20 @@ def gs_bin_sort(cam: GsCamera, opt: GsOptions, means2d, depths, radii, tiles_tou
     return int(npairs.value)
 
 
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def gs_render_ckpt_bytes(width, height) -> int:
+    """Bytes of render checkpoints for one view of this size (0: not used)."""
+    return int(load_library().gs_render_ckpt_bytes(width, height))
+
+
 def gs_render_fwd(cam: GsCamera, opt: GsOptions, n, ranges, values, n_pairs, means2d, conic_opacity, rgb, image,
-                  final_T, n_contrib, stream=None):
+                  final_T, n_contrib, ckpt=None, stream=None):
     st = load_library().gs_render_fwd(C.byref(cam), C.byref(opt), n, _p(ranges), _p(values), n_pairs, _p(means2d),
-                                      _p(conic_opacity), _p(rgb), _p(image), _p(final_T), _p(n_contrib),
-                                      _stream(stream))
+                                      _p(conic_opacity), _p(rgb), _p(image), _p(final_T), _p(n_contrib), _p(ckpt),
+                                      _nbytes(ckpt), _stream(stream))
     _check(st, "gs_render_fwd")
 
 
@@ -223,21 +235,22 @@ def gs_render_bwd_workspace_size(n) -> int:
 
 def gs_render_bwd(cam: GsCamera, opt: GsOptions, means, scales, quats, opacities, sh, means2d, conic_opacity, rgb,
                   radii, clamped, ranges, values, n_pairs, final_T, n_contrib, dL_dimage, dL_dmeans, dL_dscales,
-                  dL_dquats, dL_dopacities, dL_dsh, dL_dmeans2d, workspace, stats=None, stream=None):
+                  dL_dquats, dL_dopacities, dL_dsh, dL_dmeans2d, workspace, stats=None, ckpt=None, stream=None):
     n = means.shape[0]
     st = load_library().gs_render_bwd(
         C.byref(cam), C.byref(opt), n, _p(means), _p(scales), _p(quats), _p(opacities), _p(sh), _p(means2d),
         _p(conic_opacity), _p(rgb), _p(radii), _p(clamped), _p(ranges), _p(values), n_pairs, _p(final_T),
         _p(n_contrib), _p(dL_dimage), _p(dL_dmeans), _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities), _p(dL_dsh),
-        _p(dL_dmeans2d), _p(workspace), workspace.numel() * workspace.element_size(), _stats(stats), _stream(stream))
+        _p(dL_dmeans2d), _p(workspace), workspace.numel() * workspace.element_size(), _p(ckpt), _nbytes(ckpt),
+        _stats(stats), _stream(stream))
     _check(st, "gs_render_bwd")
 
 
 def gs_render_bwd_raster(cam: GsCamera, opt: GsOptions, n, ranges, values, n_pairs, means2d, conic_opacity, rgb,
-                         final_T, n_contrib, dL_dimage, grad2d, stream=None):
+                         final_T, n_contrib, dL_dimage, grad2d, ckpt=None, stream=None):
     st = load_library().gs_render_bwd_raster(C.byref(cam), C.byref(opt), n, _p(ranges), _p(values), n_pairs,
                                              _p(means2d), _p(conic_opacity), _p(rgb), _p(final_T), _p(n_contrib),
-                                             _p(dL_dimage), _p(grad2d), _stream(stream))
+                                             _p(dL_dimage), _p(grad2d), _p(ckpt), _nbytes(ckpt), _stream(stream))
     _check(st, "gs_render_bwd_raster")
 
 
@@ -392,6 +405,7 @@ class Frame:
     image: torch.Tensor
     final_T: torch.Tensor
     n_contrib: torch.Tensor
+    ckpt: torch.Tensor | None = None  # the forward's render checkpoints, read by this frame's backward
 
 
 def _empty(shape, dtype, device):
@@ -462,11 +476,14 @@ class Rasterizer:
         image = _empty((3, H, W), torch.float32, self.device)
         final_T = _empty((H, W), torch.float32, self.device)
         n_contrib = _empty((H, W), torch.int32, self.device)
+        # checkpoints belong to this frame (its backward reads them), so each frame gets its own
+        nck = gs_render_ckpt_bytes(W, H)
+        ckpt = _empty(nck, torch.uint8, self.device) if nck else None
         gs_render_fwd(cam, opt, means.shape[0], ranges, self._values, P, pre["means2d"], pre["conic_opacity"],
-                      pre["rgb"], image, final_T, n_contrib)
+                      pre["rgb"], image, final_T, n_contrib, ckpt)
         return Frame(cam, opt, W, H, pre["means2d"], pre["depths"], pre["conic_opacity"], pre["rgb"], pre["radii"],
                      pre["tiles_touched"], pre["clamped"], P, self._keys, self._values, ranges, image, final_T,
-                     n_contrib)
+                     n_contrib, ckpt)
 
     def backward(self, frame: Frame, means, scales, quats, opacities, sh, dL_dimage, grads: dict,
                  want_means2d: bool = False, overwrite: bool = False, stats: GsDensifyStats | None = None):
@@ -488,7 +505,7 @@ class Rasterizer:
                       frame.rgb, frame.radii, frame.clamped, frame.ranges, frame.values, frame.n_pairs,
                       frame.final_T, frame.n_contrib, dL_dimage, grads["means"], grads["scales"], grads["quats"],
                       grads["opacities"], grads["sh"], grads.get("means2d") if want_means2d else None,
-                      self._bwd_ws, stats)
+                      self._bwd_ws, stats, frame.ckpt)
         return grads
 
 

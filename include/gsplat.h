@@ -159,12 +159,26 @@ gs_status gs_bin_sort(const gs_camera *cam, const gs_options *opt, int64_t n,
  * out: image[3,H,W] = C + T bg (planar), final_T[H,W] = T,
  *      n_contrib[H,W] = 1-based position (within the tile's list) of the last
  *      blended entry, 0 if none.
+ * ckpt (nullable): render checkpoints for the backward of the same frame, a
+ *      16-byte aligned device buffer of ckpt_bytes >= gs_render_ckpt_bytes(W, H)
+ *      (caller-owned; only its parts for tiles whose walk passes 256 entries
+ *      are written). Passed again to gs_render_bwd / gs_render_bwd_raster with
+ *      the same frame, it lets the backward cut a deep tile's walk into pieces
+ *      of 256 entries run by separate waves, each starting from the state the
+ *      forward saw there. The backward's results do not depend on it beyond
+ *      rounding. NULL, or a size where gs_render_ckpt_bytes is 0: none.
  * The result is deterministic (no atomics).
  */
 gs_status gs_render_fwd(const gs_camera *cam, const gs_options *opt, int64_t n,
                         const uint32_t *ranges, const uint32_t *values, int64_t n_pairs,
                         const float *means2d, const float *conic_opacity, const float *rgb,
-                        float *image, float *final_T, uint32_t *n_contrib, void *stream);
+                        float *image, float *final_T, uint32_t *n_contrib,
+                        void *ckpt, size_t ckpt_bytes, void *stream);
+
+/* Bytes of render checkpoints for one view of width x height pixels; 0 where
+ * the backward does not use them (grids of fewer than 4096 or of 32768 or more
+ * 16x16 tiles, or an invalid size). */
+size_t gs_render_ckpt_bytes(int32_t width, int32_t height);
 
 /* Workspace bytes gs_render_bwd needs for n Gaussians. */
 size_t gs_render_bwd_workspace_size(int64_t n);
@@ -185,6 +199,8 @@ size_t gs_render_bwd_workspace_size(int64_t n);
  *      dL_dmeans2d[n,2] (gradient with respect to (u, v)); with
  *      opt->overwrite_grads = 1 all of them are WRITTEN instead (every row).
  * ws : workspace of workspace_bytes >= gs_render_bwd_workspace_size(n)
+ * ckpt (nullable): the checkpoints gs_render_fwd wrote for this frame (same
+ *      buffer and size), or NULL.
  * stats (nullable): densification statistics of this view, added (see
  *      gs_densify_stats).
  * The caller zeroes the gradient buffers once per step (or renders the step's
@@ -221,7 +237,8 @@ gs_status gs_render_bwd(const gs_camera *cam, const gs_options *opt, int64_t n,
                         const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
                         float *dL_dmeans, float *dL_dscales, float *dL_dquats,
                         float *dL_dopacities, float *dL_dsh, float *dL_dmeans2d,
-                        void *workspace, size_t workspace_bytes, const gs_densify_stats *stats, void *stream);
+                        void *workspace, size_t workspace_bytes, const void *ckpt, size_t ckpt_bytes,
+                        const gs_densify_stats *stats, void *stream);
 
 /* The two halves of gs_render_bwd, for callers that time or test them apart
  * (gs_render_bwd = gs_render_bwd_raster followed by gs_preprocess_bwd). */
@@ -234,13 +251,14 @@ gs_status gs_render_bwd(const gs_camera *cam, const gs_options *opt, int64_t n,
  *   [0..2] dL/drgb, [3] sum h, [4] sum h w^2, [5] sum h w dy, [6] sum h dy^2,
  *   [7] sum h w, [8] sum h dy, [9..11] unused (zero).
  * The sums are linear in the pixels, so per-tile partial sums are added
- * atomically; gs_preprocess_bwd turns them into conic and mean gradients. */
+ * atomically; gs_preprocess_bwd turns them into conic and mean gradients.
+ * ckpt (nullable): as in gs_render_bwd. */
 #define GS_GRAD2D_STRIDE 12
 gs_status gs_render_bwd_raster(const gs_camera *cam, const gs_options *opt, int64_t n,
                                const uint32_t *ranges, const uint32_t *values, int64_t n_pairs,
                                const float *means2d, const float *conic_opacity, const float *rgb,
                                const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
-                               float *grad2d, void *stream);
+                               float *grad2d, const void *ckpt, size_t ckpt_bytes, void *stream);
 
 /* Chain rule from grad2d (as written by gs_render_bwd_raster) to the
  * parameters; outputs ACCUMULATE (+=), or are written with

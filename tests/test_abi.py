@@ -95,8 +95,29 @@ def test_null_pointers_and_sizes_rejected():
     assert st == raster.GS_ERR_INVALID_ARG
     # render_bwd: workspace too small
     st = L.gs_render_bwd(C.byref(cam), C.byref(opt), 100, *([d] * 12), 10, d, d, d, *([d] * 6), P(4096 * 256), 64,
-                         None, None)
+                         None, 0, None, None)
     assert st == raster.GS_ERR_INVALID_ARG and b"workspace" in L.gs_last_error()
+    # render checkpoints: too small, or misaligned (on a 1920x1080 camera: 8160 tiles)
+    import numpy as np
+    cam = raster.make_camera(Camera(1920, 1080, 1400.0, 1400.0, 960.0, 540.0, np.eye(3, dtype=np.float32),
+                                    np.zeros(3, np.float32)))
+    need = raster.gs_render_ckpt_bytes(cam.width, cam.height)
+    assert need == 8160 * 5 * 256 * 16
+    img = [d] * 6
+    st = L.gs_render_fwd(C.byref(cam), C.byref(opt), 100, d, d, 10, d, d, d, *img[:3], P(4096 * 256), need - 16, None)
+    assert st == raster.GS_ERR_INVALID_ARG and b"ckpt" in L.gs_last_error()
+    st = L.gs_render_bwd_raster(C.byref(cam), C.byref(opt), 100, d, d, 10, *([d] * 7), P(4096 * 256 + 8), need, None)
+    assert st == raster.GS_ERR_INVALID_ARG and b"ckpt" in L.gs_last_error()
+
+
+def test_render_ckpt_bytes_by_grid_size():
+    # checkpoints only for one-view grids of 4096..32767 tiles
+    assert raster.gs_render_ckpt_bytes(128, 128) == 0
+    assert raster.gs_render_ckpt_bytes(800, 800) == 0
+    assert raster.gs_render_ckpt_bytes(1024, 1024) == 4096 * 5 * 256 * 16
+    assert raster.gs_render_ckpt_bytes(1920, 1080) == 8160 * 5 * 256 * 16
+    assert raster.gs_render_ckpt_bytes(4096, 2048) == 0  # 32768 tiles
+    assert raster.gs_render_ckpt_bytes(0, 100) == 0 and raster.gs_render_ckpt_bytes(40000, 100) == 0
 
 
 def test_workspace_sizes_monotone():

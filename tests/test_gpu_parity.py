@@ -384,6 +384,20 @@ def test_backward_split_of_deep_tiles():
     nc = g["n_contrib"].astype(np.int64)
     walks = nc.reshape(64, 16, 64, 16).max(axis=(1, 3))
     assert walks.max() >= 768 and ((walks > 0) & (walks < 512)).sum() > 100, (walks.max(), (walks >= 512).sum())
+    # the deep tiles' walks cut into pieces from the forward's checkpoints, and split by row bands
+    # without them (ckpt = NULL): the same pixel sums up to summation order
+    r, pd, fr = gpu_frame(sc, 0)
+    assert fr.ckpt is not None
+    dL = to_dev(sc.dL_dimage[0])
+    sums = []
+    for ck in (fr.ckpt, None):
+        g2 = torch.zeros((sc.n, raster.GRAD2D_STRIDE), dtype=torch.float32, device=dL.device)
+        raster.gs_render_bwd_raster(fr.cam, fr.opt, sc.n, fr.ranges, fr.values, fr.n_pairs, fr.means2d,
+                                    fr.conic_opacity, fr.rgb, fr.final_T, fr.n_contrib, dL, g2, ck)
+        torch.cuda.synchronize()
+        sums.append(g2.cpu().numpy().astype(np.float64))
+    for c in range(9):
+        assert rel_l2(sums[0][:, c], sums[1][:, c]) < 1e-5, (c, rel_l2(sums[0][:, c], sums[1][:, c]))
 
 
 def test_naive_atomic_backward_matches_reduced():
