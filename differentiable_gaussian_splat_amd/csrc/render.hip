@@ -32,7 +32,8 @@ constexpr int BATCH = 64;  // records staged per LDS batch
 // then the pixel's final colour: (CKPT_SLOTS + 1) x 256 float4 per tile, pixel
 // (row r, column c) of the tile at float4 16 r + c of a slot. A slot is written
 // only when the tile's band wave walks past its entry; the backward reads only
-// such slots (see bwd_walk).
+// such slots (see bwd_walk). After all tiles' slots, one uint4 per tile: each
+// row band's walk (its deepest blended entry), always written.
 constexpr int CKPT_EVERY = 256;
 constexpr int CKPT_SLOTS = 4;
 static_assert(CKPT_EVERY % BATCH == 0, "checkpoints fall on batch ends");
@@ -248,6 +249,11 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
     if (wrote_ckpt)  // the final colour, beside the checkpoints
         ckpt[((size_t)tile * (CKPT_SLOTS + 1) + CKPT_SLOTS) * 256 + band * 64 + lane] =
             make_float4(C0[0], C1[0], C2[0], T[0]);
+    if (ckpt) {  // the band's walk, for the backward's choice of pieces
+        const uint32_t bw = wave_max_u32(last[0]);
+        if (lane == 0)
+            reinterpret_cast<uint32_t*>(ckpt + (size_t)ntiles * (CKPT_SLOTS + 1) * 256)[4 * tile + band] = bw;
+    }
     const size_t HW = (size_t)W * H;
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
@@ -515,13 +521,14 @@ __global__ __launch_bounds__(64) void k_render_bwd_split(int W, int H, int TX, i
 }
 
 // With the forward's checkpoints: a tile's walk is cut into pieces of
-// CKPT_EVERY entries (the last piece taking the rest, at most CKPT_SLOTS + 1
-// pieces), one wave each, every wave over all four row bands. The piece
-// [lo, hi) starts from the checkpoint after entry hi - 1, so the pieces are
-// independent: a deep tile's walk is spread over several waves without the
-// extra per-entry reductions of a split by bands. Workgroup b is piece
-// (b / ntiles + 1) % (CKPT_SLOTS + 1) of tile b % ntiles: the later pieces of
-// every tile come first (most return at once), the first pieces last.
+// CKPT_EVERY entries, one wave each, every wave over all four row bands. The
+// piece [lo, hi) starts from the checkpoint after entry hi - 1, so the pieces
+// are independent: a deep tile's walk is spread over several waves without the
+// extra per-entry reductions of a split by bands. A walk longer than
+// (CKPT_SLOTS + 1) pieces ends in a tail piece [CKPT_SLOTS CKPT_EVERY, walk)
+// from the final state, which two waves share by row bands. Workgroup b is
+// wave (b / ntiles + 1) % (CKPT_SLOTS + 2) of tile b % ntiles: the later
+// waves of every tile come first (most return at once), the first pieces last.
 template <int NB>
 __global__ __launch_bounds__(64) void k_render_bwd_pieces(int W, int H, int TX, int TY, int ntiles,
                                                         const float4* __restrict__ ckpt,
@@ -535,28 +542,34 @@ __global__ __launch_bounds__(64) void k_render_bwd_pieces(int W, int H, int TX, 
                                                         const float* __restrict__ dL_dimage,
                                                         float* __restrict__ grad2d) {
     __shared__ BwdShared<NB> sh;
-    constexpr int PIECES = CKPT_SLOTS + 1;
+    constexpr int PIECES = CKPT_SLOTS + 1;  // slots in the checkpoint buffer per tile
+    constexpr int WAVES = CKPT_SLOTS + 2;   // waves per tile
     const int b = blockIdx.x;
-    const int tile = b % ntiles, piece = (b / ntiles + 1) % PIECES;
-    // the tile's walk: its deepest blended entry over all 256 pixels, at most the list's length
-    int tx, ty;
-    const uint32_t* nc = n_contrib + view_of_tile(tile, TX, TY, tx, ty) * (size_t)W * H;
-    const int lane = threadIdx.x;
-    const int px = tx * TILE + (lane & 15);
-    uint32_t walk = 0u;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int py = ty * TILE + (lane >> 4) + 4 * k;
-        if (px < W && py < H) walk = max(walk, nc[(size_t)py * W + px]);
-    }
+    const int tile = b % ntiles, w = (b / ntiles + 1) % WAVES;
+    // the tile's walk, from its row bands' walks the forward left after the checkpoints, at most
+    // the list's length
+    const uint4 bw = reinterpret_cast<const uint4*>(ckpt + (size_t)ntiles * PIECES * 256)[tile];
     const uint2 rg = ranges[tile];
-    walk = min((uint32_t)__builtin_amdgcn_readfirstlane(wave_max_u32(walk)), rg.y - rg.x);
-    const int pieces = min((int)((walk + CKPT_EVERY - 1) / CKPT_EVERY), PIECES);
-    if (piece >= max(pieces, 1)) return;
+    uint32_t walk = min(max(max(bw.x, bw.y), max(bw.z, bw.w)), rg.y - rg.x);
+    // pieces of CKPT_EVERY entries; a walk longer than the checkpoints reach ends in a tail
+    // piece from the last checkpoint on, shared by two waves by row bands
+    const int need = (int)((walk + CKPT_EVERY - 1) / CKPT_EVERY);
+    const bool deep = need > PIECES;
+    int piece = w;
+    uint32_t sel = 0xFu;
+    if (deep) {
+        if (w >= CKPT_SLOTS) {  // the tail, bands 0-1 or 2-3
+            piece = CKPT_SLOTS;
+            sel = w == CKPT_SLOTS ? 0x3u : 0xCu;
+        }
+    } else if (w >= max(need, 1)) {
+        return;
+    }
+    const int pieces = deep ? PIECES : need;
     const bool tail = piece >= pieces - 1;  // the last piece walks to the end from the final state
     const int lo = piece * CKPT_EVERY, hi = tail ? INT32_MAX : lo + CKPT_EVERY;
     const float4* tck = ckpt + (size_t)tile * PIECES * 256;
-    bwd_walk<4, NB, false>(tile, 0, 0xFu, lo, hi, tail ? nullptr : tck + (size_t)piece * 256, tck + CKPT_SLOTS * 256,
+    bwd_walk<4, NB, false>(tile, 0, sel, lo, hi, tail ? nullptr : tck + (size_t)piece * 256, tck + CKPT_SLOTS * 256,
                            W, H, TX, TY, ranges, values, means2d, conic_op, rgb, bg0, bg1, bg2, final_T, n_contrib,
                            dL_dimage, grad2d, nullptr, sh);
 }
@@ -571,14 +584,23 @@ __global__ __launch_bounds__(64) void k_render_bwd_pieces(int W, int H, int TX, 
 // idle, and the backward's per-wave walk time decides: there it splits a tile
 // over two or four band waves (measured on a 128x128 frame, 64 tiles: 87 ->
 // 42 us with four; 800x800, 2500 tiles: 247 -> 228 us with two). On one
-// large frame a tile walking 512 entries or more splits over two waves
-// (k_render_bwd_split): 1M Gaussians at 1080p 0.59 -> 0.52 ms (means over 200
-// launches), one 1080p view of 6M Gaussians 1.94 -> 1.56 ms, 20k large
-// Gaussians 0.584 -> 0.598 ms; splitting from 256 or 384 entries, or into four
-// waves, was slower (the extra reductions cost more than the shorter walks give
-// back). A launch of many views (16 x 8160 tiles) keeps every SIMD busy to the
-// end without it, and there the split only adds work (0.515 -> 0.641 ms per
-// view): from 32768 tiles on, one wave per tile.
+// large frame a wave per tile leaves the deep tiles (a cluster's core walks
+// ten times the median) running with few waves beside them at the end. With
+// the forward's checkpoints a deep tile's walk is cut into pieces of 256
+// entries, one wave each, and a walk past the fifth piece ends in a tail
+// piece shared by two waves by row bands (k_render_bwd_pieces). Means over 100
+// launches: 1M Gaussians at 1080p 0.505 -> 0.425 ms against the band split
+// alone, 20k large Gaussians 0.593 -> 0.587 ms, the 16 views of config 5 one
+// at a time 24.7 -> 21.8 ms. Checkpoints every 128 or 192 entries were slower;
+// 2, 6 or 10 checkpoint slots instead of 4 trade config 5's deep walks
+// (23.1, 21.2, 18.7 ms) against the cost of every tile's extra waves (config
+// 4: 0.579, 0.604, 0.630 ms). Without checkpoints a tile walking 512 entries
+// or more splits over two waves by row bands (k_render_bwd_split; from 256 or
+// 384 entries, or into four waves, it was slower: each extra wave repeats the
+// per-entry reduction). A launch of many views (16 x 8160 tiles in one) keeps
+// every SIMD busy to the end without either, and there the band split only
+// added work (0.515 -> 0.641 ms per view): from 32768 tiles on, one wave per
+// tile.
 constexpr int FWD_PPL = 1;
 constexpr int BWD_BATCH = 32;
 constexpr uint32_t BWD_SPLIT_WALK = 512;
@@ -595,7 +617,7 @@ BwdLayout bwd_layout(int ntiles) {
 size_t render_ckpt_bytes(int TX, int TY) {
     const int ntiles = TX * TY;
     if (bwd_layout(ntiles) != BwdLayout::Split) return 0;
-    return (size_t)ntiles * (CKPT_SLOTS + 1) * 256 * sizeof(float4);
+    return (size_t)ntiles * ((CKPT_SLOTS + 1) * 256 + 1) * sizeof(float4);
 }
 
 hipError_t launch_render_fwd(int views, int W, int H, int TX, int TY, const uint32_t* ranges,
@@ -622,7 +644,7 @@ hipError_t launch_render_bwd(int views, int W, int H, int TX, int TY, const uint
     const float2* m2 = reinterpret_cast<const float2*>(means2d);
     const float4* co = reinterpret_cast<const float4*>(conic_op);
     if (ckpt && views == 1 && bwd_layout(ntiles) == BwdLayout::Split) {
-        k_render_bwd_pieces<BWD_BATCH><<<(CKPT_SLOTS + 1) * ntiles, 64, 0, stream>>>(
+        k_render_bwd_pieces<BWD_BATCH><<<(CKPT_SLOTS + 2) * ntiles, 64, 0, stream>>>(
             W, H, TX, TY, ntiles, reinterpret_cast<const float4*>(ckpt), rg, values, m2, co, rgb, bg[0], bg[1], bg[2],
             final_T, n_contrib, dL_dimage, grad2d);
         return hipGetLastError();

@@ -102,7 +102,7 @@ def test_null_pointers_and_sizes_rejected():
     cam = raster.make_camera(Camera(1920, 1080, 1400.0, 1400.0, 960.0, 540.0, np.eye(3, dtype=np.float32),
                                     np.zeros(3, np.float32)))
     need = raster.gs_render_ckpt_bytes(cam.width, cam.height)
-    assert need == 8160 * 5 * 256 * 16
+    assert need == 8160 * (5 * 256 + 1) * 16
     img = [d] * 6
     st = L.gs_render_fwd(C.byref(cam), C.byref(opt), 100, d, d, 10, d, d, d, *img[:3], P(4096 * 256), need - 16, None)
     assert st == raster.GS_ERR_INVALID_ARG and b"ckpt" in L.gs_last_error()
@@ -114,8 +114,8 @@ def test_render_ckpt_bytes_by_grid_size():
     # checkpoints only for one-view grids of 4096..32767 tiles
     assert raster.gs_render_ckpt_bytes(128, 128) == 0
     assert raster.gs_render_ckpt_bytes(800, 800) == 0
-    assert raster.gs_render_ckpt_bytes(1024, 1024) == 4096 * 5 * 256 * 16
-    assert raster.gs_render_ckpt_bytes(1920, 1080) == 8160 * 5 * 256 * 16
+    assert raster.gs_render_ckpt_bytes(1024, 1024) == 4096 * (5 * 256 + 1) * 16
+    assert raster.gs_render_ckpt_bytes(1920, 1080) == 8160 * (5 * 256 + 1) * 16
     assert raster.gs_render_ckpt_bytes(4096, 2048) == 0  # 32768 tiles
     assert raster.gs_render_ckpt_bytes(0, 100) == 0 and raster.gs_render_ckpt_bytes(40000, 100) == 0
 
