@@ -304,20 +304,34 @@ def test_chain_rule_accumulates_exactly(deg):
         assert torch.equal(g[k], 2 * snap[k]), k
     if deg == 1:
         assert torch.all(g["sh"][:, 4:, :] == 0)
-    # overwrite_grads = 1 writes every row: from NaN-filled buffers it gives exactly
-    # the one-call result into zeroed buffers (zeros for culled Gaussians and for the
-    # stored SH rows beyond the active degree)
+    # overwrite_grads = 1 writes every row: from NaN-filled buffers it gives the
+    # one-call result into zeroed buffers (zeros for culled Gaussians and for the
+    # stored SH rows beyond the active degree). Degree-3 rows are written by a kernel of
+    # their own (rows in registers), whose compiled arithmetic may round differently
+    # from the adding kernel's: equal to rounding, and bit for bit from call to call.
     ow = raster.GsOptions.from_buffer_copy(fr.opt)
     ow.overwrite_grads = 1
     w = {k: torch.full_like(v, float("nan")) for k, v in g.items()}
+    culled = fr.radii <= 0
+    first = None
     for _ in range(2):
         raster.gs_preprocess_bwd(fr.cam, ow, pd["means"], pd["scales"], pd["quats"], pd["sh"], fr.conic_opacity,
                                  fr.radii, fr.clamped, grad2d, w["means"], w["scales"], w["quats"], w["opacities"],
                                  w["sh"], w["means2d"])
         torch.cuda.synchronize()
         for k in g:
-            assert torch.equal(w[k], snap[k]), k
-    assert torch.any(fr.radii <= 0)
+            assert torch.all(torch.isfinite(w[k])), k
+            assert torch.all(w[k][culled] == 0), k
+            e = rel_l2(w[k].cpu().numpy().astype(np.float64), snap[k].cpu().numpy().astype(np.float64))
+            assert e < 1e-6, (k, e)
+        if first is None:
+            first = {k: v.clone() for k, v in w.items()}
+        else:
+            for k in g:
+                assert torch.equal(w[k], first[k]), k
+    if deg == 1:
+        assert torch.all(w["sh"][:, 4:, :] == 0)
+    assert torch.any(culled)
 
 
 def test_backward_overwrite_matches_accumulate_into_zeros():
