@@ -198,6 +198,8 @@ __device__ __forceinline__ void stage_out_add(const float* src, float* __restric
 // move only the visible lanes' rows, each lane its own; dense blocks stage all
 // 64 rows with coalesced accesses.
 constexpr int SH_DENSE = 16;
+// Adding degree-3 gradients, blocks with at most this many drawn Gaussians take the register kernel.
+constexpr int BWD_REGS_MAX_VISIBLE = 32;
 
 __device__ __forceinline__ void copy_own_row(const float* __restrict__ src, float* row, size_t g, int rec, int used) {
     const float* r = src + g * (size_t)rec;
@@ -659,14 +661,17 @@ __global__ __launch_bounds__(64) void k_preprocess_bwd(
     const float* __restrict__ sh, const float4* __restrict__ conic_op, const int* __restrict__ radii,
     const uint8_t* __restrict__ clamped, const float* __restrict__ grad2d,
     float* __restrict__ d_means, float* __restrict__ d_scales, float* __restrict__ d_quats,
-    float* __restrict__ d_opac, float* __restrict__ d_sh, float* __restrict__ d_means2d, DensifyStats stats) {
+    float* __restrict__ d_opac, float* __restrict__ d_sh, float* __restrict__ d_means2d, DensifyStats stats,
+    int min_visible) {
     extern __shared__ float s_sh[];
     const int stride = (3 * K) | 1;
     const int base = blockIdx.x * 64;
     const int gi = base + threadIdx.x;
     const bool vis = gi < n && radii[gi] > 0;
     const int nvis = __popcll(__ballot(vis));
-    if (!OVERWRITE && nvis == 0) return;  // nothing of this block was drawn: no gradient
+    // adding: nothing to do for a block none of whose Gaussians was drawn, and blocks with
+    // fewer than min_visible drawn are left to k_preprocess_bwd_add_regs
+    if (!OVERWRITE && (nvis == 0 || nvis < min_visible)) return;
     const bool dense = nvis > SH_DENSE;
     float* shg = s_sh + threadIdx.x * stride;
     if (dense) stage_in(sh, s_sh, base, n, 3 * sh_rows, 3 * K, stride);
@@ -719,6 +724,43 @@ __global__ __launch_bounds__(64) void k_preprocess_bwd_write_regs(
 #pragma unroll
     for (int q = 0; q < 12; ++q)
         d_sh[(size_t)gi * 12 + q] = make_float4(acc.c[4 * q], acc.c[4 * q + 1], acc.c[4 * q + 2], acc.c[4 * q + 3]);
+}
+
+// Adding degree-3 gradients for the blocks with at most max_visible of their
+// 64 Gaussians drawn (the others return; k_preprocess_bwd takes them): each
+// drawn lane moves its own rows (coefficients, then the gradient row it adds
+// to) through registers, so a sparse block needs no LDS.
+__global__ __launch_bounds__(64) void k_preprocess_bwd_add_regs(
+    DevCam cam, float lowpass, float near_plane, int n, int max_visible,
+    const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
+    const float4* __restrict__ sh, const float4* __restrict__ conic_op, const int* __restrict__ radii,
+    const uint8_t* __restrict__ clamped, const float* __restrict__ grad2d,
+    float* __restrict__ d_means, float* __restrict__ d_scales, float* __restrict__ d_quats,
+    float* __restrict__ d_opac, float4* __restrict__ d_sh, float* __restrict__ d_means2d, DensifyStats stats) {
+    const int gi = blockIdx.x * 64 + threadIdx.x;
+    const bool vis = gi < n && radii[gi] > 0;
+    const int nvis = __popcll(__ballot(vis));
+    if (nvis > max_visible || !vis) return;
+    ShRegs16 acc;
+#pragma unroll
+    for (int q = 0; q < 12; ++q) {
+        const float4 v = sh[(size_t)gi * 12 + q];
+        acc.c[4 * q] = v.x;
+        acc.c[4 * q + 1] = v.y;
+        acc.c[4 * q + 2] = v.z;
+        acc.c[4 * q + 3] = v.w;
+    }
+    chain_rule<false>(cam, 16, lowpass, near_plane, gi, means, scales, quats, acc, conic_op, radii, clamped, grad2d,
+                      d_means, d_scales, d_quats, d_opac, d_means2d, stats);
+#pragma unroll
+    for (int q = 0; q < 12; ++q) {
+        float4 v = d_sh[(size_t)gi * 12 + q];
+        v.x += acc.c[4 * q];
+        v.y += acc.c[4 * q + 1];
+        v.z += acc.c[4 * q + 2];
+        v.w += acc.c[4 * q + 3];
+        d_sh[(size_t)gi * 12 + q] = v;
+    }
 }
 
 // ---------------------------------------------------------------- several views per launch
@@ -946,12 +988,25 @@ hipError_t launch_preprocess_bwd(const DevCam& cam, int K, int sh_rows, float lo
             d_means, d_scales, d_quats, d_opac, reinterpret_cast<float4*>(d_sh), d_means2d, stats);
         return hipGetLastError();
     }
+    // Adding degree-3 gradients: blocks with at most BWD_REGS_MAX_VISIBLE of their Gaussians
+    // drawn go through registers, the denser ones through the LDS staging (one view of 6M
+    // Gaussians, 22% drawn: 0.787 -> 0.52 ms; 1M at 1080p, 99% drawn: unchanged).
+    int min_visible = 1;
+    if (!overwrite && K == 16 && sh_rows == 16 && ((uintptr_t)sh & 15u) == 0 && ((uintptr_t)d_sh & 15u) == 0) {
+        k_preprocess_bwd_add_regs<<<blocks, 64, 0, stream>>>(
+            cam, lowpass, near_plane, n, BWD_REGS_MAX_VISIBLE, means, scales, reinterpret_cast<const float4*>(quats),
+            reinterpret_cast<const float4*>(sh), reinterpret_cast<const float4*>(conic_op), radii, clamped, grad2d,
+            d_means, d_scales, d_quats, d_opac, reinterpret_cast<float4*>(d_sh), d_means2d, stats);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        min_visible = BWD_REGS_MAX_VISIBLE + 1;
+    }
     size_t lds = sizeof(float) * 64 * ((3 * K) | 1);
     auto kernel = overwrite ? k_preprocess_bwd<true> : k_preprocess_bwd<false>;
     kernel<<<blocks, 64, lds, stream>>>(cam, K, sh_rows, lowpass, near_plane, n, means, scales,
                                         reinterpret_cast<const float4*>(quats), sh,
                                         reinterpret_cast<const float4*>(conic_op), radii, clamped, grad2d, d_means,
-                                        d_scales, d_quats, d_opac, d_sh, d_means2d, stats);
+                                        d_scales, d_quats, d_opac, d_sh, d_means2d, stats, min_visible);
     return hipGetLastError();
 }
 
