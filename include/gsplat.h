@@ -161,12 +161,15 @@ gs_status gs_bin_sort(const gs_camera *cam, const gs_options *opt, int64_t n,
  *      blended entry, 0 if none.
  * ckpt (nullable): render checkpoints for the backward of the same frame, a
  *      16-byte aligned device buffer of ckpt_bytes >= gs_render_ckpt_bytes(W, H)
- *      (caller-owned; only its parts for tiles whose walk passes 256 entries
- *      are written). Passed again to gs_render_bwd / gs_render_bwd_raster with
- *      the same frame, it lets the backward cut a deep tile's walk into pieces
- *      of 256 entries run by separate waves, each starting from the state the
- *      forward saw there. The backward's results do not depend on it beyond
- *      rounding. NULL, or a size where gs_render_ckpt_bytes is 0: none.
+ *      (caller-owned, no initialisation needed: every tile's 16-byte walk
+ *      summary is written, the per-pixel states only for tiles whose walk
+ *      passes 256 entries). Passed again to gs_render_bwd / gs_render_bwd_raster
+ *      with the same frame, it lets the backward cut a deep tile's walk into
+ *      pieces of 256 entries run by separate waves, each starting from the
+ *      state the forward saw there. The backward's results do not depend on it
+ *      beyond rounding. A buffer from another frame gives wrong gradients (no
+ *      out-of-bounds access). NULL, or a size where gs_render_ckpt_bytes is 0:
+ *      none.
  * The result is deterministic (no atomics).
  */
 gs_status gs_render_fwd(const gs_camera *cam, const gs_options *opt, int64_t n,
