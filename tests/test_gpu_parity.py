@@ -379,11 +379,16 @@ def test_large_tile_grid_two_pass_super_sort():
     _full_check(sc)
 
 
-def test_backward_split_of_deep_tiles():
-    """On grids of 4096 tiles or more, a tile whose walk reaches 512 entries is
-    shared by two backward waves (two row bands each), the others keep one.
-    1500 faint Gaussians heaped on the middle of a 1024x1024 frame walk about a
-    thousand entries there; a few hundred more are spread thinly elsewhere."""
+@pytest.mark.parametrize("bg", [(0.0, 0.0, 0.0), (0.2, 0.5, 0.9)])
+def test_backward_split_of_deep_tiles(bg):
+    """On grids of 4096 tiles or more the backward cuts a deep tile's walk into
+    pieces of 256 entries from the forward's checkpoints (a walk past the fifth
+    piece ends in a tail shared by two waves by row bands); without
+    checkpoints a tile walking 512 entries or more is shared by two waves by
+    row bands. 1500 faint Gaussians heaped on the middle of a 1024x1024 frame
+    walk about 1400 entries there; a few hundred more are spread thinly
+    elsewhere. With a background, each piece's colour behind its start takes
+    the T_final bg term."""
     rng = np.random.default_rng(11)
     cam = Camera(1024, 1024, 1000.0, 1000.0, 512.0, 512.0, np.eye(3, dtype=np.float32), np.zeros(3, np.float32))
     n_heap, n_rest = 1500, 400
@@ -394,13 +399,13 @@ def test_backward_split_of_deep_tiles():
                                  1).astype(np.float32)
     sc.scales[:n_heap] = np.exp(rng.normal(-3.5, 0.2, (n_heap, 3))).astype(np.float32)
     sc.opacities[:n_heap] = rng.uniform(0.01, 0.03, n_heap).astype(np.float32)
-    g, _ = _full_check(sc)
+    g, _ = _full_check(sc, bg=bg)
     nc = g["n_contrib"].astype(np.int64)
     walks = nc.reshape(64, 16, 64, 16).max(axis=(1, 3))
     assert walks.max() >= 768 and ((walks > 0) & (walks < 512)).sum() > 100, (walks.max(), (walks >= 512).sum())
     # the deep tiles' walks cut into pieces from the forward's checkpoints, and split by row bands
     # without them (ckpt = NULL): the same pixel sums up to summation order
-    r, pd, fr = gpu_frame(sc, 0)
+    r, pd, fr = gpu_frame(sc, 0, bg=bg)
     assert fr.ckpt is not None
     dL = to_dev(sc.dL_dimage[0])
     sums = []
