@@ -590,11 +590,12 @@ __global__ __launch_bounds__(64) void k_render_bwd_pieces(int W, int H, int TX, 
 // entries, one wave each, and a walk past the fifth piece ends in a tail
 // piece shared by two waves by row bands (k_render_bwd_pieces). Means over 100
 // launches: 1M Gaussians at 1080p 0.505 -> 0.425 ms against the band split
-// alone, 20k large Gaussians 0.593 -> 0.587 ms, the 16 views of config 5 one
-// at a time 24.7 -> 21.8 ms. Checkpoints every 128 or 192 entries were slower;
-// 2, 6 or 10 checkpoint slots instead of 4 trade config 5's deep walks
-// (23.1, 21.2, 18.7 ms) against the cost of every tile's extra waves (config
-// 4: 0.579, 0.604, 0.630 ms). Without checkpoints a tile walking 512 entries
+// alone, 20k large Gaussians 0.593 -> 0.587 ms, 6M Gaussians seen by 16
+// 1080p cameras one at a time 24.7 -> 21.8 ms. Checkpoints every 128 or 192
+// entries were slower; 2, 6 or 10 checkpoint slots instead of 4 trade the 6M
+// scene's deep walks (up to 10k entries: 23.1, 21.2, 18.7 ms) against the cost
+// of every tile's extra waves (20k large Gaussians: 0.579, 0.604, 0.630 ms).
+// Without checkpoints a tile walking 512 entries
 // or more splits over two waves by row bands (k_render_bwd_split; from 256 or
 // 384 entries, or into four waves, it was slower: each extra wave repeats the
 // per-entry reduction). A launch of many views (16 x 8160 tiles in one) keeps
