@@ -34,6 +34,7 @@ constexpr int BATCH = 64;  // records staged per LDS batch
 // only when the tile's band wave walks past its entry; the backward reads only
 // such slots (see bwd_walk). After all tiles' slots, one uint4 per tile: each
 // row band's walk (its deepest blended entry), always written.
+constexpr int PIECES_CHUNK = 1024;  // tiles per dispatch chunk of the pieces backward
 constexpr int CKPT_EVERY = 256;
 constexpr int CKPT_SLOTS = 4;
 static_assert(CKPT_EVERY % BATCH == 0, "checkpoints fall on batch ends");
@@ -526,9 +527,7 @@ __global__ __launch_bounds__(64) void k_render_bwd_split(int W, int H, int TX, i
 // are independent: a deep tile's walk is spread over several waves without the
 // extra per-entry reductions of a split by bands. A walk longer than
 // (CKPT_SLOTS + 1) pieces ends in a tail piece [CKPT_SLOTS CKPT_EVERY, walk)
-// from the final state, which two waves share by row bands. Workgroup b is
-// wave (b / ntiles + 1) % (CKPT_SLOTS + 2) of tile b % ntiles: the later
-// waves of every tile come first (most return at once), the first pieces last.
+// from the final state, which two waves share by row bands.
 template <int NB>
 __global__ __launch_bounds__(64) void k_render_bwd_pieces(int W, int H, int TX, int TY, int ntiles,
                                                         const float4* __restrict__ ckpt,
@@ -545,7 +544,22 @@ __global__ __launch_bounds__(64) void k_render_bwd_pieces(int W, int H, int TX, 
     constexpr int PIECES = CKPT_SLOTS + 1;  // slots in the checkpoint buffer per tile
     constexpr int WAVES = CKPT_SLOTS + 2;   // waves per tile
     const int b = blockIdx.x;
-    const int tile = b % ntiles, w = (b / ntiles + 1) % WAVES;
+    // Dispatch order, by chunks of PIECES_CHUNK tiles: the chunk's later waves (most return at
+    // once), then its first pieces. A deep tile's pieces start together, and the first
+    // pieces of the early chunks do not wait behind every tile's later waves (one chunk
+    // for the whole grid: 0.466 -> 0.451 ms on 1M Gaussians at 1080p, 0.572 -> 0.567 ms on
+    // 20k large ones).
+    const int cb = b / (WAVES * PIECES_CHUNK), r = b - cb * WAVES * PIECES_CHUNK;
+    const int t0 = cb * PIECES_CHUNK, tn = min(PIECES_CHUNK, ntiles - t0);
+    if (r >= WAVES * tn) return;  // past the last tile
+    int w, tile;
+    if (r < (WAVES - 1) * tn) {
+        w = 1 + r / tn;
+        tile = t0 + r % tn;
+    } else {
+        w = 0;
+        tile = t0 + r - (WAVES - 1) * tn;
+    }
     // the tile's walk, from its row bands' walks the forward left after the checkpoints, at most
     // the list's length
     const uint4 bw = reinterpret_cast<const uint4*>(ckpt + (size_t)ntiles * PIECES * 256)[tile];
@@ -645,7 +659,8 @@ hipError_t launch_render_bwd(int views, int W, int H, int TX, int TY, const uint
     const float2* m2 = reinterpret_cast<const float2*>(means2d);
     const float4* co = reinterpret_cast<const float4*>(conic_op);
     if (ckpt && views == 1 && bwd_layout(ntiles) == BwdLayout::Split) {
-        k_render_bwd_pieces<BWD_BATCH><<<(CKPT_SLOTS + 2) * ntiles, 64, 0, stream>>>(
+        k_render_bwd_pieces<BWD_BATCH><<<(CKPT_SLOTS + 2) * PIECES_CHUNK * ((ntiles + PIECES_CHUNK - 1) / PIECES_CHUNK),
+                                         64, 0, stream>>>(
             W, H, TX, TY, ntiles, reinterpret_cast<const float4*>(ckpt), rg, values, m2, co, rgb, bg[0], bg[1], bg[2],
             final_T, n_contrib, dL_dimage, grad2d);
         return hipGetLastError();
