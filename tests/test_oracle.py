@@ -319,6 +319,50 @@ def test_quaternion_scale_invariance_and_translation():
     np.testing.assert_allclose(f3["image"], f0["image"], atol=1e-9)
 
 
+def _posed_sh3_scene(seed, n=24, W=64, H=48):
+    p, cam, dL = fd_scene(seed, n=n, W=W, H=H, deg=3)
+    return p, cam, dL
+
+
+def test_view_direction_from_the_camera_centre_degree3():
+    """O1/O10 at SH degree 3 under a rotated, translated camera: each colour is
+    the real-SH expansion (SciPy's harmonics, Condon-Shortley phase) at the unit
+    direction from the camera centre c, solved here from R c + t = 0, to the
+    mean, plus 0.5 and clamped at 0. A camera centre formed as -R t instead of
+    -R^T t, or a direction from the mean to the camera, fails this."""
+    p, cam, _ = _posed_sh3_scene(11)
+    pre = O.preprocess(p["means"], p["scales"], p["quats"], p["opacities"], p["sh"], cam, 3)
+    R = cam.R.astype(np.float64)
+    c = np.linalg.solve(R, -cam.t.astype(np.float64))
+    vis = pre["radii"] > 0
+    assert vis.sum() >= 12
+    for g in np.nonzero(vis)[0]:
+        d = p["means"][g] - c
+        d /= np.linalg.norm(d)
+        Y = np.array([(-1) ** m * _real_sh_scipy(l, m, d) for l in range(4) for m in range(-l, l + 1)])
+        raw = Y @ p["sh"][g] + 0.5
+        np.testing.assert_allclose(pre["rgb"][g], np.maximum(raw, 0.0), atol=1e-6)
+        np.testing.assert_array_equal(pre["clamp"][g], (raw < 0).astype(np.uint8))
+
+
+def test_translation_invariance_degree3_posed_camera():
+    """G: translating the scene by delta and the camera with it (R delta' = t - t',
+    solved in fp64 for a t' that fp32 holds exactly) leaves every colour, the
+    image and the pair lists unchanged at SH degree 3; only the direction from
+    the camera centre enters the colour."""
+    p, cam, _ = _posed_sh3_scene(12)
+    f0 = O.forward(p, cam, 3)
+    R = cam.R.astype(np.float64)
+    t2 = (cam.t.astype(np.float64) + np.array([0.75, -0.5, 1.25])).astype(np.float32)
+    delta = np.linalg.solve(R, cam.t.astype(np.float64) - t2.astype(np.float64))
+    cam2 = Camera(cam.width, cam.height, cam.fx, cam.fy, cam.cx, cam.cy, cam.R, t2)
+    f1 = O.forward(dict(p, means=p["means"] + delta), cam2, 3)
+    np.testing.assert_array_equal(f1["values"], f0["values"])
+    np.testing.assert_allclose(f1["pre"]["rgb"], f0["pre"]["rgb"], atol=1e-6)
+    np.testing.assert_allclose(f1["image"], f0["image"], atol=1e-6)
+    assert np.abs(f0["pre"]["rgb"]).max() > 0.1
+
+
 # ---------------------------------------------------------------- finite differences
 
 def fd_scene(seed, n=10, W=48, H=40, deg=3):
