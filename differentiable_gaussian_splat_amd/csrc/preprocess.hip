@@ -2,12 +2,13 @@
 // Gaussian. This is the "preprocessing" phase of a 3D Gaussian Splatting
 // training iteration (Odin page, Fig. 7 caption: phases P/R/B/U/C).
 //
-// Numerics. The 2D covariance is formed as Sigma' = T T^T + lowpass I with
-// T = (J R) Rq diag(s) (2x3), so its diagonal entries are sums of squares.
-// Its determinant uses Lagrange's identity det(T T^T) = |T0 x T1|^2 with
-// T0 x T1 = (fx fy / z^3) s1 s2 s3 diag(1/s) Rq^T (mu - campos), which has no
-// cancellation, and the inverse is stored factored as
+// Numerics. The 2D covariance is Sigma' = T T^T + lowpass I with
+// T = (J R) Rq diag(s) (2x3), and its inverse is stored factored as
 // Q = a (dx + beta dy)^2 + gamma dy^2 (a = C/det, beta = -B/C, gamma = 1/C).
+// The projection forms it in double (see project). The chain rule works in
+// fp32; where it needs T0 x T1 it uses the closed form
+// T0 x T1 = (fx fy / z^3) s1 s2 s3 diag(1/s) Rq^T (mu - campos) (Lagrange's
+// identity gives det(T T^T) = |T0 x T1|^2), which has no cancellation.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -33,7 +34,10 @@ __device__ __forceinline__ bool geometry(const DevCam& cam, float near_plane, fl
     g.x = fmaf(cam.R[0], mx, fmaf(cam.R[1], my, fmaf(cam.R[2], mz, cam.t[0])));
     g.y = fmaf(cam.R[3], mx, fmaf(cam.R[4], my, fmaf(cam.R[5], mz, cam.t[1])));
     g.z = fmaf(cam.R[6], mx, fmaf(cam.R[7], my, fmaf(cam.R[8], mz, cam.t[2])));
-    if (!(g.z > near_plane)) return false;
+    // the near-plane test on the depth formed in double, as the projection takes it
+    const double zd = fma((double)cam.R[6], (double)mx,
+                          fma((double)cam.R[7], (double)my, fma((double)cam.R[8], (double)mz, (double)cam.t[2])));
+    if (!(zd > (double)near_plane)) return false;
     float qq = q.x * q.x + q.y * q.y + q.z * q.z + q.w * q.w;
     if (!(qq > 0.f) || !finitef(qq)) return false;
     g.qnorm = sqrtf(qq);
@@ -330,33 +334,70 @@ struct Proj {
 
 // The projection of one Gaussian (finite inputs) into one camera: EWA conic
 // in factored form, 3-sigma radius, tile rectangle. False when it is culled.
+//
+// Evaluated in double from the fp32 inputs and rounded once per output. The
+// entries of T = (J R) Rq diag(s) are dot products that cancel when a
+// Gaussian's long axes lie nearly along the viewing ray, and the conic is the
+// inverse of T T^T + lowpass I: in fp32 both lose digits in proportion to
+// those condition numbers (thin footprints seen edge-on reach 10^5). In double
+// the outputs carry only their own fp32 rounding, for about a hundred extra
+// double operations per Gaussian in a kernel bound by its memory traffic.
 __device__ __forceinline__ bool project(const DevCam& cam, float lowpass, float near_plane, float mx, float my,
                                        float mz, float s0, float s1, float s2, float4 q, Proj& p) {
-    Geo geo;
-    if (!geometry(cam, near_plane, mx, my, mz, s0, s1, s2, q, geo)) return false;
-    // det(Sigma') = |T0 x T1|^2 + lowpass (A0 + C0) + lowpass^2
-    float dx = mx - cam.campos[0], dy = my - cam.campos[1], dz = mz - cam.campos[2];
-    float e0 = fmaf(geo.Rq[0], dx, fmaf(geo.Rq[3], dy, geo.Rq[6] * dz));
-    float e1 = fmaf(geo.Rq[1], dx, fmaf(geo.Rq[4], dy, geo.Rq[7] * dz));
-    float e2 = fmaf(geo.Rq[2], dx, fmaf(geo.Rq[5], dy, geo.Rq[8] * dz));
-    float iz = 1.0f / geo.z;
-    float kk = cam.fx * cam.fy * iz * iz * iz;
-    float c0 = kk * e0 * s1 * s2, c1 = kk * e1 * s0 * s2, c2 = kk * e2 * s0 * s1;
-    float cross2 = fmaf(c0, c0, fmaf(c1, c1, c2 * c2));
-    float A = geo.A0 + lowpass, C = geo.C0 + lowpass, B = geo.B0;
-    float det = fmaf(lowpass, geo.A0 + geo.C0 + lowpass, cross2);
-    if (!(det > 0.f && finitef(det) && C > 0.f)) return false;
-    p.a = C / det;
-    p.beta = -B / C;
-    p.gamma = 1.0f / C;
-    float half = 0.5f * (A - C);
-    float lam = 0.5f * (A + C) + sqrtf(fmaf(half, half, B * B));
-    float extent = 3.0f * sqrtf(lam);
-    p.u = fmaf(cam.fx, geo.x * iz, cam.cx);
-    p.v = fmaf(cam.fy, geo.y * iz, cam.cy);
-    p.depth = geo.z;
-    if (!(fabsf(p.u) <= BIG && fabsf(p.v) <= BIG && extent <= BIG)) return false;  // also false on NaN
-    p.r = (int)ceilf(extent);
+    const double X = mx, Y = my, Z = mz;
+    double R[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) R[i] = (double)cam.R[i];
+    const double x = fma(R[0], X, fma(R[1], Y, fma(R[2], Z, (double)cam.t[0])));
+    const double y = fma(R[3], X, fma(R[4], Y, fma(R[5], Z, (double)cam.t[1])));
+    const double z = fma(R[6], X, fma(R[7], Y, fma(R[8], Z, (double)cam.t[2])));
+    if (!(z > (double)near_plane)) return false;
+    const double qw = q.x, qx = q.y, qy = q.z, qz = q.w;
+    const double qq = fma(qw, qw, fma(qx, qx, fma(qy, qy, qz * qz)));
+    if (!(qq > 0.0)) return false;
+    const double inv = 1.0 / sqrt(qq);
+    const double w = qw * inv, a = qx * inv, b = qy * inv, c = qz * inv;
+    const double Rq[9] = {1.0 - 2.0 * (b * b + c * c), 2.0 * (a * b - w * c),       2.0 * (a * c + w * b),
+                          2.0 * (a * b + w * c),       1.0 - 2.0 * (a * a + c * c), 2.0 * (b * c - w * a),
+                          2.0 * (a * c - w * b),       2.0 * (b * c + w * a),       1.0 - 2.0 * (a * a + b * b)};
+    // J = [[fx/z, 0, -fx x/z^2], [0, fy/z, -fy y/z^2]]; V = J R; T = V Rq diag(s)
+    const double iz = 1.0 / z;
+    const double xz = x * iz, yz = y * iz;
+    const double fxz = (double)cam.fx * iz, fyz = (double)cam.fy * iz;
+    double V[6];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        V[j] = fxz * fma(-xz, R[6 + j], R[j]);
+        V[3 + j] = fyz * fma(-yz, R[6 + j], R[3 + j]);
+    }
+    const double s[3] = {s0, s1, s2};
+    double T[6];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            T[3 * i + j] = fma(V[3 * i], Rq[j], fma(V[3 * i + 1], Rq[3 + j], V[3 * i + 2] * Rq[6 + j])) * s[j];
+    const double lp = lowpass;
+    const double A = fma(T[0], T[0], fma(T[1], T[1], fma(T[2], T[2], lp)));
+    const double C = fma(T[3], T[3], fma(T[4], T[4], fma(T[5], T[5], lp)));
+    const double B = fma(T[0], T[3], fma(T[1], T[4], T[2] * T[5]));
+    const double det = fma(A, C, -B * B);
+    if (!(det > 0.0 && C > 0.0)) return false;
+    p.a = (float)(C / det);
+    p.beta = (float)(-B / C);
+    p.gamma = (float)(1.0 / C);
+    if (!(finitef(p.a) && p.a > 0.f && finitef(p.beta) && p.gamma > 0.f)) return false;
+    const double half = 0.5 * (A - C);
+    const double lam = 0.5 * (A + C) + sqrt(fma(half, half, B * B));
+    const double extent = 3.0 * sqrt(lam);
+    const double u = fma((double)cam.fx, xz, (double)cam.cx);
+    const double v = fma((double)cam.fy, yz, (double)cam.cy);
+    if (!(fabs(u) <= (double)BIG && fabs(v) <= (double)BIG && extent <= (double)BIG)) return false;  // also on NaN
+    p.u = (float)u;
+    p.v = (float)v;
+    p.depth = (float)z;
+    p.r = (int)ceil(extent);
+    // the rectangle from the stored (rounded) screen mean: binning reads the same values
     return tile_rect(p.u, p.v, p.r, cam.TX, cam.TY, p.X0, p.X1, p.Y0, p.Y1);
 }
 

@@ -77,6 +77,13 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / nb)
 
 
+# Bound on the factored conic's relative error: each of a, beta, gamma is one
+# fp32 rounding (2^-24 relative) of a double value that agrees with the fp64
+# oracle's to about 1e-16 times the condition number (at most about 5e5 in
+# the seeded workloads), so 4 ulps leaves room for both.
+CONIC_TOL = 4 * 2.0 ** -24
+
+
 def check_preprocess(sc, v, g, idx=None):
     """Projection of view v: GPU stage outputs ``g`` (frame_np) against the
     oracle, for all Gaussians or the subset ``idx``: continuous outputs within
@@ -102,14 +109,16 @@ def check_preprocess(sc, v, g, idx=None):
     np.testing.assert_array_less(np.abs(g["means2d"] - o["means2d"])[same], 1e-5 * sc_uv[same])
     np.testing.assert_array_less(np.abs(g["depth32"] - o["depth"])[same], 1e-5 * o["depth"][same])
     np.testing.assert_array_less(np.abs(g["rgb"] - o["rgb"])[same], 1e-5 * (1 + np.abs(o["rgb"][same])))
-    # conic in factored form against the oracle's 2D covariance (a = C/det, beta = -B/C, gamma = 1/C)
+    # conic in factored form against the oracle's 2D covariance (a = C/det, beta = -B/C, gamma = 1/C).
+    # The HIP projection forms Sigma' and its inverse in double and rounds each output once, so
+    # the bound is flat: a few fp32 roundings, whatever the conditioning. The condition numbers
+    # are printed for the record: kappa = A C / det (of the inverse) and kappa_C, that of C
+    # itself, which sums the squares of the second projected row V1 Rq diag(s) and cancels
+    # when that row is nearly orthogonal to the Gaussian's long axes.
     A, B, Cc = o["cov2d"][same].T
     det = A * Cc - B * B
     a_o, be_o, ga_o = Cc / det, -B / Cc, 1.0 / Cc
-    kappa = A * Cc / det  # conditioning of det(Sigma')
-    # conditioning of C itself: C sums the squares of the second projected row
-    # V1 R_q diag(s), |V1|^2 = (fy/z)^2 (1 + (y/z)^2); when that row is nearly
-    # orthogonal to the Gaussian's long axes, C is small beside |V1|^2 |s|^2
+    kappa = A * Cc / det
     R = np.asarray(cam.R, np.float64)
     xc = sc.means[idx].astype(np.float64) @ R.T + np.asarray(cam.t, np.float64)
     zc, yc = xc[:, 2], xc[:, 1]
@@ -120,10 +129,9 @@ def check_preprocess(sc, v, g, idx=None):
     err_a = np.abs(ldl[:, 0] - a_o) / a_o
     err_g = np.abs(ldl[:, 2] - ga_o) / ga_o
     err_b = np.abs(ldl[:, 1] - be_o) / np.sqrt(A / Cc)
-    tol = 2e-6 * (1 + kappa + kC)
-    tol_g = np.maximum(1e-5, 2e-6 * kC)
-    worst = int(np.argmax(np.maximum(err_a / tol, np.maximum(err_g / tol_g, err_b / tol))))
-    assert np.all(err_a <= tol) and np.all(err_g <= tol_g) and np.all(err_b <= tol), \
-        (err_a.max(), err_g.max(), err_b.max(), "worst", err_a[worst], err_g[worst], err_b[worst], kappa[worst],
-         kC[worst])
+    print(f"conic: {same.sum()} Gaussians, max kappa {kappa.max():.3g}, max kappa_C {kC.max():.3g}, "
+          f"max rel err a {err_a.max():.2e} beta {err_b.max():.2e} gamma {err_g.max():.2e}")
+    tol = CONIC_TOL
+    assert err_a.max() <= tol and err_g.max() <= tol and err_b.max() <= tol, \
+        (err_a.max(), err_g.max(), err_b.max(), kappa.max(), kC.max())
     np.testing.assert_array_equal(g["clamped"][same], (o["clamp"][same] * [1, 2, 4]).sum(1))

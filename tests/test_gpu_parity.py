@@ -402,7 +402,10 @@ def test_backward_split_of_deep_tiles(bg):
     g, _ = _full_check(sc, bg=bg)
     nc = g["n_contrib"].astype(np.int64)
     walks = nc.reshape(64, 16, 64, 16).max(axis=(1, 3))
-    assert walks.max() >= 768 and ((walks > 0) & (walks < 512)).sum() > 100, (walks.max(), (walks >= 512).sum())
+    # pieces of 256 entries from four checkpoint slots reach entry 1280: tiles walking further
+    # take the tail piece that two waves share by row bands (4 tiles here, the deepest at 1471)
+    assert (walks > 1280).sum() >= 1 and ((walks > 0) & (walks < 512)).sum() > 100, \
+        (walks.max(), (walks > 1280).sum())
     # the deep tiles' walks cut into pieces from the forward's checkpoints, and split by row bands
     # without them (ckpt = NULL): the same pixel sums up to summation order
     r, pd, fr = gpu_frame(sc, 0, bg=bg)

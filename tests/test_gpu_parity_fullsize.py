@@ -1,7 +1,9 @@
 """Parity at the workloads' full sizes, in the configuration the benchmark times.
 
-- Config 3 (1M Gaussians, 1080p, 44.5M pairs) and config 4 (20k large
-  Gaussians, ~105M pairs) are checked stage-wise over the whole frame: the
+- Config 2 (100k Gaussians, 800x800, whose 2500 tiles take the two-wave
+  band backward without checkpoints), config 3 (1M Gaussians, 1080p, 44.5M
+  pairs) and config 4 (20k large Gaussians, ~105M pairs) are checked
+  stage-wise over the whole frame: the
   oracle runs each stage on the GPU's own inputs to that stage (projection
   for all Gaussians, the full pair sort bit for bit, every pixel through the
   branch-exploring matcher, and the full backward), in seconds on the host's
@@ -64,7 +66,7 @@ def _check_frame(sc, v, r, pd, fr, backward=True):
     return g
 
 
-@pytest.mark.parametrize("c", [3, 4])
+@pytest.mark.parametrize("c", [2, 3, 4])
 def test_full_frame_stagewise(c):
     sc = make_scene(c, 0)
     r, pd, fr = gpu_frame(sc, 0)
