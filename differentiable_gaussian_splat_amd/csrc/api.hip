@@ -6,6 +6,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+#include <string>
+
 #include "../../include/gsplat.h"
 #include "common.hpp"
 #include "launch.hpp"
@@ -322,6 +325,106 @@ gs_status gs_render_fwd(const gs_camera* cam, const gs_options* opt, int64_t n, 
     }
 }
 
+}  // extern "C"
+
+namespace {
+
+// gs_render_bwd with its pixel-sum records at grad2d (n records of 48 bytes,
+// 256-byte aligned): arguments checked, records zeroed by a fill kernel, the
+// backward raster, the chain rule.
+gs_status render_bwd_into(const char* name, const gs_camera* cam, const gs_options* opt, int64_t n,
+                          const float* means, const float* scales, const float* quats, const float* opacities,
+                          const float* sh, const float* means2d, const float* conic_opacity, const float* rgb,
+                          const int32_t* radii, const uint8_t* clamped, const uint32_t* ranges,
+                          const uint32_t* values, int64_t n_pairs, const float* final_T, const uint32_t* n_contrib,
+                          const float* dL_dimage, float* dL_dmeans, float* dL_dscales, float* dL_dquats,
+                          float* dL_dopacities, float* dL_dsh, float* dL_dmeans2d, float* grad2d, const void* ckpt,
+                          size_t ckpt_bytes, const gs_densify_stats* stats, void* stream) {
+    REQUIRE_PTR(means);
+    REQUIRE_PTR(scales);
+    REQUIRE_PTR(quats);
+    REQUIRE_PTR(opacities);
+    REQUIRE_PTR(sh);
+    REQUIRE_PTR(means2d);
+    REQUIRE_PTR(conic_opacity);
+    REQUIRE_PTR(rgb);
+    REQUIRE_PTR(radii);
+    REQUIRE_PTR(clamped);
+    REQUIRE_PTR(ranges);
+    REQUIRE_PTR(final_T);
+    REQUIRE_PTR(n_contrib);
+    REQUIRE_PTR(dL_dimage);
+    REQUIRE_PTR(dL_dmeans);
+    REQUIRE_PTR(dL_dscales);
+    REQUIRE_PTR(dL_dquats);
+    REQUIRE_PTR(dL_dopacities);
+    REQUIRE_PTR(dL_dsh);
+    REQUIRE(n_pairs >= 0 && n_pairs < ((int64_t)1 << 31), "n_pairs must be in [0, 2^31)");
+    REQUIRE(n_pairs == 0 || values != nullptr, "values must not be NULL");
+    REQUIRE(aligned(quats, 16) && aligned(dL_dquats, 16), "quats and dL_dquats must be 16-byte aligned");
+    REQUIRE(aligned(conic_opacity, 16), "conic_opacity must be 16-byte aligned");
+    REQUIRE(aligned(means2d, 8) && aligned(ranges, 8), "means2d and ranges must be 8-byte aligned");
+    REQUIRE(!stats || (stats->grad_accum && stats->count && stats->max_radius),
+            "stats: grad_accum, count and max_radius must all be set");
+    Checked c;
+    gs_status st = check_common(cam, opt, n, c);
+    if (st != GS_OK) return st;
+    st = check_ckpt(ckpt, ckpt_bytes, c);
+    if (st != GS_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    std::string where = std::string(name) + "(zero)";
+    st = hip_check(gs::launch_fill_u32(reinterpret_cast<uint32_t*>(grad2d), (size_t)n * gs::GRAD2D_STRIDE, 0u, s),
+                   where.c_str());
+    if (st != GS_OK) return st;
+    if (n_pairs > 0) {
+        where = std::string(name) + "(raster)";
+        st = hip_check(gs::launch_render_bwd(1, c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
+                                             conic_opacity, rgb, opt->bg, final_T, n_contrib, dL_dimage, grad2d,
+                                             static_cast<const float*>(ckpt), s),
+                       where.c_str());
+        if (st != GS_OK) return st;
+    }
+    where = std::string(name) + "(chain)";
+    return hip_check(gs::launch_preprocess_bwd(c.cam, c.K, c.sh_rows, opt->lowpass, opt->near_plane, (int)n, means,
+                                               scales, quats, sh, conic_opacity, radii, clamped, grad2d, dL_dmeans,
+                                               dL_dscales, dL_dquats, dL_dopacities, dL_dsh, dL_dmeans2d,
+                                               opt->overwrite_grads != 0, densify_arrays(stats), s),
+                     where.c_str());
+}
+
+// Pixel-sum records of gs_render_bwd_noalloc: GS_NOALLOC_MAX_N records of
+// 48 bytes (48 MiB), one copy per GPU, held from the library's load on that
+// GPU until the process ends. Host code never passes this name to a kernel
+// (on the host it is a stand-in, not a device address): it takes the
+// device's own address from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) float scratch[(size_t)GS_NOALLOC_MAX_N * gs::GRAD2D_STRIDE];
+
+struct ScratchSlot {
+    std::once_flag once;
+    float* ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+
+gs_status scratch_for_current_device(float*& out) {
+    static ScratchSlot slots[16];
+    int dev = 0;
+    gs_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+    if (st != GS_OK) return st;
+    if (dev < 0 || dev >= 16) return fail(GS_ERR_UNSUPPORTED, "device index %d >= 16", dev);
+    ScratchSlot& sl = slots[dev];
+    // the current device is `dev` here, so the address is that device's copy
+    std::call_once(sl.once, [&sl] { sl.err = hipGetSymbolAddress((void**)&sl.ptr, HIP_SYMBOL(scratch)); });
+    if (sl.err != hipSuccess || sl.ptr == nullptr)
+        return fail(GS_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                    sl.err != hipSuccess ? hipGetErrorString(sl.err) : "null address");
+    out = sl.ptr;
+    return GS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t gs_render_bwd_workspace_size(int64_t n) {
     if (n < 0) return 0;
     return ((size_t)(n > 0 ? n : 1) * gs::GRAD2D_STRIDE * sizeof(float) + 255) & ~(size_t)255;
@@ -341,57 +444,46 @@ gs_status gs_render_bwd(const gs_camera* cam, const gs_options* opt, int64_t n, 
         gs_status st = check_common(cam, opt, n, c);
         if (st != GS_OK) return st;
         if (n == 0) return GS_OK;
-        REQUIRE_PTR(means);
-        REQUIRE_PTR(scales);
-        REQUIRE_PTR(quats);
-        REQUIRE_PTR(opacities);
-        REQUIRE_PTR(sh);
-        REQUIRE_PTR(means2d);
-        REQUIRE_PTR(conic_opacity);
-        REQUIRE_PTR(rgb);
-        REQUIRE_PTR(radii);
-        REQUIRE_PTR(clamped);
-        REQUIRE_PTR(ranges);
-        REQUIRE_PTR(final_T);
-        REQUIRE_PTR(n_contrib);
-        REQUIRE_PTR(dL_dimage);
-        REQUIRE_PTR(dL_dmeans);
-        REQUIRE_PTR(dL_dscales);
-        REQUIRE_PTR(dL_dquats);
-        REQUIRE_PTR(dL_dopacities);
-        REQUIRE_PTR(dL_dsh);
         REQUIRE_PTR(workspace);
-        REQUIRE(n_pairs >= 0 && n_pairs < ((int64_t)1 << 31), "n_pairs must be in [0, 2^31)");
-        REQUIRE(n_pairs == 0 || values != nullptr, "values must not be NULL");
-        REQUIRE(aligned(quats, 16) && aligned(dL_dquats, 16), "quats and dL_dquats must be 16-byte aligned");
-        REQUIRE(aligned(conic_opacity, 16), "conic_opacity must be 16-byte aligned");
-        REQUIRE(aligned(means2d, 8) && aligned(ranges, 8), "means2d and ranges must be 8-byte aligned");
         REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
-        REQUIRE(!stats || (stats->grad_accum && stats->count && stats->max_radius),
-                "stats: grad_accum, count and max_radius must all be set");
         size_t need = gs_render_bwd_workspace_size(n);
         REQUIRE(workspace_bytes >= need, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
-        st = check_ckpt(ckpt, ckpt_bytes, c);
-        if (st != GS_OK) return st;
-        hipStream_t s = (hipStream_t)stream;
-        float* grad2d = reinterpret_cast<float*>(workspace);
-        st = hip_check(gs::launch_fill_u32(reinterpret_cast<uint32_t*>(grad2d), (size_t)n * gs::GRAD2D_STRIDE, 0u, s),
-                       "gs_render_bwd(zero)");
-        if (st != GS_OK) return st;
-        if (n_pairs > 0) {
-            st = hip_check(gs::launch_render_bwd(1, c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
-                                                 conic_opacity, rgb, opt->bg, final_T, n_contrib, dL_dimage, grad2d,
-                                                 static_cast<const float*>(ckpt), s),
-                           "gs_render_bwd(raster)");
-            if (st != GS_OK) return st;
-        }
-        return hip_check(gs::launch_preprocess_bwd(c.cam, c.K, c.sh_rows, opt->lowpass, opt->near_plane, (int)n,
-                                                   means, scales, quats, sh, conic_opacity, radii, clamped, grad2d,
-                                                   dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh,
-                                                   dL_dmeans2d, opt->overwrite_grads != 0, densify_arrays(stats), s),
-                         "gs_render_bwd(chain)");
+        return render_bwd_into("gs_render_bwd", cam, opt, n, means, scales, quats, opacities, sh, means2d,
+                               conic_opacity, rgb, radii, clamped, ranges, values, n_pairs, final_T, n_contrib,
+                               dL_dimage, dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh, dL_dmeans2d,
+                               reinterpret_cast<float*>(workspace), ckpt, ckpt_bytes, stats, stream);
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_render_bwd: unexpected exception");
+    }
+}
+
+gs_status gs_render_bwd_noalloc(const gs_camera* cam, const gs_options* opt, int64_t n, const float* means,
+                                const float* scales, const float* quats, const float* opacities, const float* sh,
+                                const float* means2d, const float* conic_opacity, const float* rgb,
+                                const int32_t* radii, const uint8_t* clamped, const uint32_t* ranges,
+                                const uint32_t* values, int64_t n_pairs, const float* final_T,
+                                const uint32_t* n_contrib, const float* dL_dimage, float* dL_dmeans,
+                                float* dL_dscales, float* dL_dquats, float* dL_dopacities, float* dL_dsh,
+                                float* dL_dmeans2d, const void* ckpt, size_t ckpt_bytes,
+                                const gs_densify_stats* stats, void* stream) {
+    try {
+        g_err[0] = 0;
+        Checked c;
+        gs_status st = check_common(cam, opt, n, c);
+        if (st != GS_OK) return st;
+        if (n > GS_NOALLOC_MAX_N)
+            return fail(GS_ERR_CAPACITY, "gs_render_bwd_noalloc: n = %lld exceeds its fixed scratch of %d Gaussians",
+                        (long long)n, GS_NOALLOC_MAX_N);
+        if (n == 0) return GS_OK;
+        float* grad2d = nullptr;
+        st = scratch_for_current_device(grad2d);
+        if (st != GS_OK) return st;
+        return render_bwd_into("gs_render_bwd_noalloc", cam, opt, n, means, scales, quats, opacities, sh, means2d,
+                               conic_opacity, rgb, radii, clamped, ranges, values, n_pairs, final_T, n_contrib,
+                               dL_dimage, dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh, dL_dmeans2d,
+                               grad2d, ckpt, ckpt_bytes, stats, stream);
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_render_bwd_noalloc: unexpected exception");
     }
 }
 

@@ -71,7 +71,8 @@ EXPORTS = ["gs_default_options", "gs_version", "gs_last_error", "gs_preprocess",
            "gs_render_bwd_raster",
            "gs_preprocess_bwd", "gs_preprocess_views", "gs_bin_sort_views_workspace_size", "gs_bin_sort_views",
            "gs_render_fwd_views", "gs_render_bwd_raster_views", "gs_preprocess_bwd_views", "gs_adam_step",
-           "gs_mb_render_bwd_naive", "gs_mb_hbm_read", "gs_mb_hbm_copy", "gs_mb_atomic"]
+           "gs_mb_render_bwd_naive", "gs_mb_hbm_read", "gs_mb_hbm_copy", "gs_mb_atomic", "gs_render_bwd_noalloc"]
+NOALLOC_MAX_N = 1 << 20  # GS_NOALLOC_MAX_N
 MAX_VIEWS = 32
 GRAD2D_STRIDE = 12
 
@@ -110,6 +111,9 @@ def load_library(path: str = LIB_PATH):
         L.gs_render_bwd.argtypes = ([cam, opt, i64] + [P] * 5 + [P] * 5 + [P, P, i64] + [P] * 3 + [P] * 6 +
                                     [P, sz, P, sz, dst, P])
         L.gs_render_bwd.restype = i32
+        L.gs_render_bwd_noalloc.argtypes = ([cam, opt, i64] + [P] * 5 + [P] * 5 + [P, P, i64] + [P] * 3 + [P] * 6 +
+                                            [P, sz, dst, P])
+        L.gs_render_bwd_noalloc.restype = i32
         L.gs_render_bwd_raster.argtypes = [cam, opt, i64, P, P, i64] + [P] * 7 + [P, sz, P]
         L.gs_render_bwd_raster.restype = i32
         L.gs_preprocess_bwd.argtypes = [cam, opt, i64] + [P] * 8 + [P] * 6 + [dst, P]
@@ -244,6 +248,21 @@ def gs_render_bwd(cam: GsCamera, opt: GsOptions, means, scales, quats, opacities
         _p(dL_dmeans2d), _p(workspace), workspace.numel() * workspace.element_size(), _p(ckpt), _nbytes(ckpt),
         _stats(stats), _stream(stream))
     _check(st, "gs_render_bwd")
+
+
+def gs_render_bwd_noalloc(cam: GsCamera, opt: GsOptions, means, scales, quats, opacities, sh, means2d, conic_opacity,
+                          rgb, radii, clamped, ranges, values, n_pairs, final_T, n_contrib, dL_dimage, dL_dmeans,
+                          dL_dscales, dL_dquats, dL_dopacities, dL_dsh, dL_dmeans2d, stats=None, ckpt=None,
+                          stream=None):
+    """gs_render_bwd with the library's own fixed scratch instead of a workspace
+    (at most NOALLOC_MAX_N Gaussians; calls on one GPU must not overlap)."""
+    n = means.shape[0]
+    st = load_library().gs_render_bwd_noalloc(
+        C.byref(cam), C.byref(opt), n, _p(means), _p(scales), _p(quats), _p(opacities), _p(sh), _p(means2d),
+        _p(conic_opacity), _p(rgb), _p(radii), _p(clamped), _p(ranges), _p(values), n_pairs, _p(final_T),
+        _p(n_contrib), _p(dL_dimage), _p(dL_dmeans), _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities), _p(dL_dsh),
+        _p(dL_dmeans2d), _p(ckpt), _nbytes(ckpt), _stats(stats), _stream(stream))
+    _check(st, "gs_render_bwd_noalloc")
 
 
 def gs_render_bwd_raster(cam: GsCamera, opt: GsOptions, n, ranges, values, n_pairs, means2d, conic_opacity, rgb,

@@ -243,6 +243,34 @@ gs_status gs_render_bwd(const gs_camera *cam, const gs_options *opt, int64_t n,
                         void *workspace, size_t workspace_bytes, const void *ckpt, size_t ckpt_bytes,
                         const gs_densify_stats *stats, void *stream);
 
+/*
+ * gs_render_bwd_noalloc -- gs_render_bwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same arguments, results and error behaviour as
+ * gs_render_bwd, without workspace / workspace_bytes: the per-Gaussian pixel
+ * sums go to a scratch array inside the library (GS_NOALLOC_MAX_N records of
+ * 48 bytes, 48 MiB, one copy per GPU, held from the library's load on that GPU
+ * until the process ends). The call allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine.
+ *   n > GS_NOALLOC_MAX_N -> GS_ERR_CAPACITY, nothing launched.
+ * The scratch array keeps the last call's contents; each call clears the part
+ * it uses (a fill kernel on the stream, no hipMemsetAsync). All calls on one
+ * GPU share it, so calls that overlap on one GPU (concurrent streams or host
+ * threads) race: the caller serialises them.
+ */
+#define GS_NOALLOC_MAX_N (1 << 20)
+gs_status gs_render_bwd_noalloc(const gs_camera *cam, const gs_options *opt, int64_t n,
+                                const float *means, const float *scales, const float *quats,
+                                const float *opacities, const float *sh,
+                                const float *means2d, const float *conic_opacity, const float *rgb,
+                                const int32_t *radii, const uint8_t *clamped,
+                                const uint32_t *ranges, const uint32_t *values, int64_t n_pairs,
+                                const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
+                                float *dL_dmeans, float *dL_dscales, float *dL_dquats,
+                                float *dL_dopacities, float *dL_dsh, float *dL_dmeans2d,
+                                const void *ckpt, size_t ckpt_bytes,
+                                const gs_densify_stats *stats, void *stream);
+
 /* The two halves of gs_render_bwd, for callers that time or test them apart
  * (gs_render_bwd = gs_render_bwd_raster followed by gs_preprocess_bwd). */
 

@@ -183,3 +183,15 @@ def test_views_workspace_grows_with_views():
     assert four > one and four % 256 == 0
     assert raster.gs_bin_sort_views_workspace_size(0, 1000, 10_000, 128, 128) == 0
     assert raster.gs_bin_sort_views_workspace_size(raster.MAX_VIEWS + 1, 1000, 10_000, 128, 128) == 0
+
+
+def test_noalloc_backward_rejects_more_than_its_scratch():
+    """gs_render_bwd_noalloc refuses n above its fixed scratch before it touches
+    any pointer or launches anything."""
+    L = raster.load_library()
+    cam, opt = _cam(), L.gs_default_options()
+    args = [None] * 5 + [None] * 5 + [None, None, 0] + [None] * 3 + [None] * 6 + [None, 0, None, None]
+    st = L.gs_render_bwd_noalloc(C.byref(cam), C.byref(opt), raster.NOALLOC_MAX_N + 1, *args)
+    assert st == raster.GS_ERR_CAPACITY
+    assert b"scratch" in L.gs_last_error()
+    assert L.gs_render_bwd_noalloc(C.byref(cam), C.byref(opt), 0, *args) == raster.GS_OK
