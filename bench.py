@@ -36,14 +36,21 @@ if ROOT not in sys.path:
 
 METRIC = "fwd+bwd splat-raster ms/frame, 1M Gaussians @1080p; % HBM/atomic roofline"
 HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
-# Vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane-operations/s,
-# doubled by dual-issue packed fp32 = 78.6 T op/s (the published 157.3 TFLOP/s
-# counts each fused multiply-add as two).
-VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 * 2 / 1e12
-# Backward arithmetic per walked (pixel, list entry): 45 fp32 vector operations
-# (falloff, alpha, transmittance, colour and the six moment sums) plus one
-# exp2 and one reciprocal.
-BWD_OPS_PER_ENTRY = 47
+# Published fp32 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz x 2 (dual-issue
+# packed fp32) x 2 (an FMA is two flops) = 157.3 TFLOP/s. This build compiles packed
+# fp32 off, so an all-FMA stream reaches at most half of it.
+FP32_PEAK_TFLOPS = 256 * 4 * 16 * 2.4e9 * 2 * 2 / 1e12
+# Flops of the blending arithmetic, an FMA counted as two, exp2 and reciprocal as
+# one each, comparisons and selects not at all (the kernels' own formulation):
+# - evaluating alpha at a (pixel, entry): w and dy from the record's values at the
+#   tile's first pixel (4), the exponent a2 w^2 + g2 dy^2 + log2 o (6), exp2 (1);
+ALPHA_FLOPS = 11
+# - forward, per blended entry: alpha T (1), three colour FMAs (6), T update (2);
+FWD_BLEND_FLOPS = 9
+# - backward, per blended entry: T in front of it (1 - alpha, rcp, mul: 3), alpha T (1),
+#   colour gradient (6), rgb . dL/dC (5), its difference with S (1), S update (2),
+#   h (1), h w and h dy (2), the six moment sums (9).
+BWD_GRAD_FLOPS = 30
 ATOMICS_PER_TILE_ENTRY = 9      # one add per gradient value per (tile, Gaussian)
 PROFILES = os.path.join(ROOT, "profiles")
 STAGES = ["preprocess", "bin_sort", "render_fwd", "zero_pixel_sums", "render_bwd_raster", "preprocess_bwd"]
@@ -172,7 +179,7 @@ def main():
 
     BWD0, BWD1 = STAGES.index("render_bwd_raster"), STAGES.index("render_bwd_raster") + 1
 
-    def step(ev, all_stages):
+    def step(ev, all_stages, keys=None):
         for vi, v in enumerate(views):
             e = ev[vi]
             mark = (lambda k: e[k].record(stream)) if all_stages else (lambda k: None)
@@ -181,7 +188,7 @@ def main():
             raster.gs_preprocess(cam, opt, means, scales, quats, opac, sh, means2d, depths, conic, rgb, radii, tiles,
                                  clamped)
             mark(1)
-            P = raster.gs_bin_sort(cam, opt, means2d, depths, radii, tiles, r._bin_ws, r.pair_capacity, r._keys,
+            P = raster.gs_bin_sort(cam, opt, means2d, depths, radii, tiles, r._bin_ws, r.pair_capacity, keys,
                                    r._values, ranges)
             last_P[vi] = P
             mark(2)
@@ -225,6 +232,21 @@ def main():
     stage_ms /= n_stage_steps * len(views)
     log(f"[bench] {args.steps} steps in {elapsed:.3f}s: {ms_per_frame:.3f} ms/frame; "
         + ", ".join(f"{s} {t:.3f}" for s, t in zip(STAGES, stage_ms)))
+    # the same steps with the sorted 64-bit keys written too (the renderer does not read them)
+    keys_buf = E(r.pair_capacity, torch.int64)
+    step(ev_warm, False, keys_buf)
+    torch.cuda.synchronize()
+    t_k = time.perf_counter()
+    for i in range(args.steps):
+        step(ev_steps[i], False, keys_buf)
+    torch.cuda.synchronize()
+    ms_keys = 1000.0 * (time.perf_counter() - t_k) / frames
+    ev_k = [mk() for _ in range(n_stage_steps)]
+    for i in range(n_stage_steps):
+        step(ev_k[i], True, keys_buf)
+    torch.cuda.synchronize()
+    bin_keys_ms = sum(e[1].elapsed_time(e[2]) for ev in ev_k for e in ev) / (n_stage_steps * len(views))
+    del keys_buf
 
     # algorithmic work of the last frame (outside the timed region)
     nc_np = n_contrib.cpu().numpy().astype(np.int64)
@@ -233,7 +255,15 @@ def main():
     bwd_bytes, walked = backward_bytes(nc_np, rg_np, W, H, touched)
     E_b = int(nc_np.sum())
     t_bwd = bwd_launch_ms * 1e-3  # the backward raster kernel's mean launch time in the timed steps
-    valu_tops = BWD_OPS_PER_ENTRY * E_b / t_bwd / 1e12
+    # blending work of the last view, counted with the forward's own decisions (gs_mb_render_counts)
+    cnt = torch.zeros(8, dtype=torch.int64, device=dev)
+    raster.gs_mb_render_counts(cams[views[-1]], opt, ranges, r._values, last_P[-1], means2d, conic, rgb, cnt)
+    cnt = [int(x) for x in cnt.cpu().tolist()]
+    E_f, E_f_eval, E_blend, E_b_cnt, P_c, band_exec, walked_cnt = cnt[:7]
+    # the backward: gradient math on blended entries, alpha on the walked ones that did not blend
+    bwd_flops = (ALPHA_FLOPS + BWD_GRAD_FLOPS) * E_blend + ALPHA_FLOPS * (E_b_cnt - E_blend)
+    fwd_flops = (ALPHA_FLOPS + FWD_BLEND_FLOPS) * E_blend + ALPHA_FLOPS * (E_f_eval - E_blend)
+    bwd_tflops = bwd_flops / t_bwd / 1e12
 
     batched = time_batched_views(args, raster, dev, sc, cams, opt, means, scales, quats, opac, sh, dLs, last_P,
                                  1000.0 * elapsed / args.steps) if len(views) > 1 else None
@@ -325,19 +355,42 @@ def main():
             "workload": scenes.CONFIG_NAMES[args.config],
             "config": args.config, "seed": args.seed, "gaussians": n, "views_per_step": len(views),
             "image": [W, H], "sh_degree": sc.sh_degree, "pairs": int(max(last_P)),
-            "visible": touched, "E_b": E_b, "bwd_tile_entries_walked": walked,
+            "visible": touched, "E_b": E_b, "bwd_tile_entries_walked": walked, "keys": False,
         },
+        "keys_on": {"ms_per_frame": round(ms_keys, 4), "bin_sort_ms": round(bin_keys_ms, 4),
+                    "note": "the same steps with gs_bin_sort also writing the sorted 64-bit (tile, depth) keys; "
+                            "the timed steps pass keys = NULL (the renderer reads values and ranges only)"},
         "stages_ms": {s: round(float(t), 4) for s, t in zip(STAGES, stage_ms)},
         "roofline": {
             "kernel": bwd_kernel,
             "bound": "alu",
-            "achieved": round(valu_tops, 2),
-            "peak": round(VALU_PEAK_TOPS, 1),
+            "achieved": round(bwd_tflops, 2),
+            "peak": round(FP32_PEAK_TFLOPS, 1),
             "unit": "TFLOP/s",
-            "frac": round(valu_tops / VALU_PEAK_TOPS, 4),
+            "frac": round(bwd_tflops / FP32_PEAK_TFLOPS, 4),
             "traffic": pmc_traffic(bwd_kernel, args.config),
-            "work": f"{BWD_OPS_PER_ENTRY} fp32 vector ops (an FMA counted once) per walked pixel-entry x E_b",
+            "work": (f"{ALPHA_FLOPS + BWD_GRAD_FLOPS} flops (FMA = 2) per blended pixel-entry x E_blend + "
+                     f"{ALPHA_FLOPS} per walked, unblended pixel-entry x (E_b - E_blend) = {bwd_flops}"),
             "launch_ms": round(t_bwd * 1e3, 4),
+            "note": "packed fp32 is compiled off, so 0.5 is the ceiling of an all-FMA stream",
+        },
+        "forward_roofline": {
+            "kernel": "k_render_fwd", "bound": "alu",
+            "achieved": round(fwd_flops / (stage_ms[STAGES.index("render_fwd")] * 1e-3) / 1e12, 2),
+            "peak": round(FP32_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
+            "frac": round(fwd_flops / (stage_ms[STAGES.index("render_fwd")] * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 4),
+            "work": (f"{ALPHA_FLOPS + FWD_BLEND_FLOPS} flops per blended pixel-entry x E_blend + {ALPHA_FLOPS} per "
+                     f"evaluated, unblended pixel-entry x (E_f_eval - E_blend) = {fwd_flops}"),
+            "stage_ms": round(float(stage_ms[STAGES.index("render_fwd")]), 4),
+        },
+        "blend_counts": {
+            "E_f": E_f, "E_f_eval": E_f_eval, "E_blend": E_blend, "E_b": E_b_cnt, "P": int(last_P[-1]), "P_c": P_c,
+            "bwd_band_steps": band_exec, "bwd_lane_use": round(E_blend / max(64 * band_exec, 1), 4),
+            "bwd_tile_entries_walked": walked_cnt,
+            "note": "one view, the forward's own decisions: E_f entries evaluated per pixel up to its stop (E_f_eval "
+                    "those passing the 16x4 band's bound), E_blend blended, E_b walked by the reverse pass, P_c "
+                    "(tile, entry) pairs with a blended pixel, bwd_band_steps (16x4 band, entry) pairs the backward "
+                    "executes, bwd_lane_use = E_blend / (64 bwd_band_steps)",
         },
         "stage_rooflines": stage_roof,
         "naive_atomic_bwd": {
@@ -491,9 +544,33 @@ def cpu_baseline(sc, args, fr_state, view):
     the per-pixel forward and backward (scaled by the tile count)."""
     from oracle import oracle as O
 
+    full = _cpu_sample(O, sc, args, fr_state, view)
+    threads = O.max_threads()
+    O.set_threads(1)
+    try:
+        one = _cpu_sample(O, sc, args, fr_state, view)
+    finally:
+        O.set_threads(threads)
+    total_ms = 1000.0 * sum(full["t"].values())
+    total_1 = 1000.0 * sum(one["t"].values())
+    return {
+        "value": round(total_ms, 1),
+        "unit": "ms/frame",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 oracle, {threads} OpenMP threads: preprocess and its backward on all {sc.n} Gaussians; "
+                   f"pair sort on a random {args.cpu_sort_frac:.0%} of Gaussians scaled by pair count; per-pixel "
+                   f"forward and backward on {full['k']} random tiles of {full['ntiles']} scaled by tile count"),
+        "stages_s": {s: round(v, 3) for s, v in full["t"].items()},
+        "one_thread": {"value": round(total_1, 1), "unit": "ms/frame", "cores": 1,
+                       "stages_s": {s: round(v, 3) for s, v in one["t"].items()}},
+    }
+
+
+def _cpu_sample(O, sc, args, fr_state, view):
+    """One timing of the oracle's stages on the sample, scaled to the frame."""
     cam = sc.cameras[view]
     W, H = cam.width, cam.height
-    threads = O.max_threads()
     rng = np.random.default_rng(1234)
     t = {}
     t0 = time.perf_counter()
@@ -531,17 +608,7 @@ def cpu_baseline(sc, args, fr_state, view):
     t0 = time.perf_counter()
     O.preprocess_bwd(sc.means, sc.scales, sc.quats, sc.opacities, sc.sh, cam, sc.sh_degree, g2)
     t["preprocess_bwd"] = time.perf_counter() - t0
-    total_ms = 1000.0 * sum(t.values())
-    return {
-        "value": round(total_ms, 1),
-        "unit": "ms/frame",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": (f"fp64 oracle, {threads} OpenMP threads: preprocess and its backward on all {sc.n} Gaussians; "
-                   f"pair sort on a random {args.cpu_sort_frac:.0%} of Gaussians scaled by pair count; per-pixel "
-                   f"forward and backward on {k} random tiles of {ntiles} scaled by tile count"),
-        "stages_s": {s: round(v, 3) for s, v in t.items()},
-    }
+    return {"t": t, "k": k, "ntiles": ntiles}
 
 
 if __name__ == "__main__":

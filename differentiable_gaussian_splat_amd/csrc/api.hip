@@ -843,6 +843,29 @@ gs_status gs_mb_render_bwd_naive(const gs_camera* cam, const gs_options* opt, in
     }
 }
 
+gs_status gs_mb_render_counts(const gs_camera* cam, const gs_options* opt, const uint32_t* ranges,
+                              const uint32_t* values, int64_t n_pairs, const float* means2d,
+                              const float* conic_opacity, const float* rgb, uint64_t* counts, void* stream) {
+    try {
+        g_err[0] = 0;
+        Checked c;
+        gs_status st = check_common(cam, opt, 0, c);
+        if (st != GS_OK) return st;
+        REQUIRE(counts && ranges, "gs_mb_render_counts: NULL array");
+        REQUIRE(n_pairs >= 0 && n_pairs < ((int64_t)1 << 31), "n_pairs must be in [0, 2^31)");
+        if (n_pairs == 0) return GS_OK;
+        REQUIRE(values && means2d && conic_opacity && rgb, "gs_mb_render_counts: NULL array");
+        REQUIRE(aligned(conic_opacity, 16) && aligned(means2d, 8) && aligned(ranges, 8) && aligned(counts, 8),
+                "gs_mb_render_counts: misaligned array");
+        return hip_check(gs::launch_render_counts(c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
+                                                  conic_opacity, rgb, reinterpret_cast<unsigned long long*>(counts),
+                                                  (hipStream_t)stream),
+                         "gs_mb_render_counts");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_mb_render_counts: unexpected exception");
+    }
+}
+
 gs_status gs_mb_hbm_read(const void* src, size_t bytes, float* sink, void* stream) {
     if (!src || !sink || bytes % 16 || !aligned(src, 16)) return fail(GS_ERR_INVALID_ARG, "gs_mb_hbm_read: bad args");
     return hip_check(gs::launch_mb_read(src, bytes, sink, (hipStream_t)stream), "gs_mb_hbm_read");

@@ -100,6 +100,9 @@ hipError_t launch_render_bwd_naive(int W, int H, int TX, int TY, const uint32_t*
                                    const float* final_T, const uint32_t* n_contrib, const float* dL_dimage,
                                    float* grad2d, uint32_t* lane_hist, hipStream_t stream);
 
+hipError_t launch_render_counts(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
+                               const float* means2d, const float* conic_op, const float* rgb,
+                               unsigned long long* counts, hipStream_t stream);
 hipError_t launch_mb_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_mb_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_mb_atomic(float* records, int64_t n_records, int64_t n_ops, int lanes, hipStream_t stream);

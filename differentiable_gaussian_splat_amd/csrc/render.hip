@@ -588,6 +588,114 @@ __global__ __launch_bounds__(64) void k_render_bwd_pieces(int W, int H, int TX, 
                            dL_dimage, grad2d, nullptr, sh);
 }
 
+// Measurement: the work of one view's blending, counted with the forward's own
+// decisions (the same staged records and falloff). One wave per tile, four
+// pixels per lane (rows lane / 16 + 4 k), walking the list front to back until
+// every pixel has stopped. counts[] (u64, added):
+//   0 E_f        entries each pixel evaluates: list positions up to and
+//                including the one that stops it, else the whole list
+//   1 E_f_kernel those the forward evaluates (the entry passes its row band's
+//                eigenvalue bound)
+//   2 E_blend    blended (pixel, entry) pairs
+//   3 E_b        sum of n_contrib: entries each pixel's reverse walk passes
+//   4 P_c        (tile, entry) pairs with at least one blended pixel
+//   5 band_exec  (16x4 row band, entry) pairs with at least one blended pixel:
+//                what the backward executes, 64 lanes each
+//   6 walked     sum over tiles of the deepest n_contrib (the backward's walk)
+__global__ __launch_bounds__(64) void k_render_counts(int W, int H, int TX, int TY, int ntiles,
+                                                     const uint2* __restrict__ ranges,
+                                                     const uint32_t* __restrict__ values,
+                                                     const float2* __restrict__ means2d,
+                                                     const float4* __restrict__ conic_op,
+                                                     const float* __restrict__ rgb,
+                                                     unsigned long long* __restrict__ counts) {
+    __shared__ Staged s_rec[BATCH];
+    const int tile = blockIdx.x;
+    if (tile >= ntiles) return;
+    int tx, ty;
+    view_of_tile(tile, TX, TY, tx, ty);
+    const int lane = threadIdx.x;
+    const int px = tx * TILE + (lane & 15);
+    const double ox = (double)(tx * TILE) + 0.5, oy = (double)(ty * TILE) + 0.5;
+    const float lx = (float)(lane & 15);
+    float ly[4], T[4], L[4];
+    uint32_t last[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int r = (lane >> 4) + 4 * k;
+        ly[k] = (float)r;
+        T[k] = 1.f;
+        last[k] = 0u;
+        L[k] = (px < W && ty * TILE + r < H) ? 1.f : 0.f;
+    }
+    const float bx_lo = (float)(tx * TILE) + 0.5f, bx_hi = bx_lo + 15.f;
+    const float by_lo = (float)(ty * TILE) + 0.5f;
+    const uint32_t no_last[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+    unsigned long long ef = 0, efk = 0, eblend = 0, pc = 0, bandx = 0;
+    const uint2 rg = ranges[tile];
+    for (uint32_t bs = rg.x; bs < rg.y; bs += BATCH) {
+        if (!__any(L[0] + L[1] + L[2] + L[3] != 0.f)) break;
+        const uint32_t idx = bs + lane;
+        uint32_t bands = 0u;
+        if (idx < rg.y)
+            bands = stage_record_bands<4>(values[idx], 0u, no_last, means2d, conic_op, rgb, s_rec, lane, ox, oy,
+                                          bx_lo, bx_hi, by_lo);
+        __syncthreads();
+        const int cnt = (int)min((uint32_t)BATCH, rg.y - bs);
+        for (int j = 0; j < cnt; ++j) {
+            const uint32_t bm = __builtin_amdgcn_readlane(bands, j);
+            const float4 A = s_rec[j].a;
+            const float4 B = s_rec[j].b;
+            const uint32_t pos = bs - rg.x + 1 + (uint32_t)j;
+            const float wl = A.x + lx;
+            bool any_tile = false;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                ef += L[k] != 0.f ? 1u : 0u;
+                if (!((bm >> k) & 1u)) continue;
+                efk += L[k] != 0.f ? 1u : 0u;
+                const float oG = falloff(__fmaf_rn(A.w, ly[k], wl), A.y + ly[k], A.z, B.x, B.y);
+                const float al = fminf(ALPHA_MAX, oG);
+                float ae = (al >= ALPHA_MIN ? al : 0.f) * L[k];
+                const bool stop = __fmaf_rn(-ae, T[k], T[k]) < T_MIN;
+                L[k] = stop ? 0.f : L[k];
+                ae = stop ? 0.f : ae;
+                T[k] = __fmaf_rn(-ae, T[k], T[k]);
+                const bool blended = ae > 0.f;
+                last[k] = blended ? pos : last[k];
+                eblend += blended ? 1u : 0u;
+                if (__any(blended)) {
+                    any_tile = true;
+                    ++bandx;
+                }
+            }
+            if (any_tile) ++pc;
+        }
+        __syncthreads();
+    }
+    // per pixel n_contrib, the tile's deepest, and the wave's totals
+    unsigned long long eb = 0;
+    uint32_t deepest = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        eb += last[k];
+        deepest = max(deepest, last[k]);
+    }
+    deepest = wave_max_u32(deepest);
+    const unsigned long long per[5] = {ef, efk, eblend, eb, 0ull};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        unsigned long long v = per[c];
+        for (int off = 32; off > 0; off >>= 1) v += (unsigned long long)__shfl_xor((long long)v, off);
+        if (lane == 0) atomicAdd(&counts[c], v);
+    }
+    if (lane == 0) {
+        atomicAdd(&counts[4], pc);
+        atomicAdd(&counts[5], bandx);
+        atomicAdd(&counts[6], (unsigned long long)deepest);
+    }
+}
+
 }  // namespace
 
 // Measured on the contention scene (1M Gaussians, 1920x1080): the forward is
@@ -684,6 +792,17 @@ hipError_t launch_render_bwd(int views, int W, int H, int TX, int TY, const uint
                                                                  bg[2], final_T, n_contrib, dL_dimage, grad2d);
             break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_render_counts(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
+                               const float* means2d, const float* conic_op, const float* rgb,
+                               unsigned long long* counts, hipStream_t stream) {
+    const int ntiles = TX * TY;
+    if (ntiles == 0) return hipSuccess;
+    k_render_counts<<<ntiles, 64, 0, stream>>>(W, H, TX, TY, ntiles, reinterpret_cast<const uint2*>(ranges), values,
+                                               reinterpret_cast<const float2*>(means2d),
+                                               reinterpret_cast<const float4*>(conic_op), rgb, counts);
     return hipGetLastError();
 }
 

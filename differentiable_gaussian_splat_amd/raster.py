@@ -71,7 +71,8 @@ EXPORTS = ["gs_default_options", "gs_version", "gs_last_error", "gs_preprocess",
            "gs_render_bwd_raster",
            "gs_preprocess_bwd", "gs_preprocess_views", "gs_bin_sort_views_workspace_size", "gs_bin_sort_views",
            "gs_render_fwd_views", "gs_render_bwd_raster_views", "gs_preprocess_bwd_views", "gs_adam_step",
-           "gs_mb_render_bwd_naive", "gs_mb_hbm_read", "gs_mb_hbm_copy", "gs_mb_atomic", "gs_render_bwd_noalloc"]
+           "gs_mb_render_bwd_naive", "gs_mb_hbm_read", "gs_mb_hbm_copy", "gs_mb_atomic", "gs_render_bwd_noalloc",
+           "gs_mb_render_counts"]
 NOALLOC_MAX_N = 1 << 20  # GS_NOALLOC_MAX_N
 MAX_VIEWS = 32
 GRAD2D_STRIDE = 12
@@ -135,6 +136,8 @@ def load_library(path: str = LIB_PATH):
         L.gs_adam_step.restype = i32
         L.gs_mb_render_bwd_naive.argtypes = [cam, opt, i64, P, P, i64] + [P] * 7 + [P, P]
         L.gs_mb_render_bwd_naive.restype = i32
+        L.gs_mb_render_counts.argtypes = [cam, opt, P, P, i64, P, P, P, P, P]
+        L.gs_mb_render_counts.restype = i32
         L.gs_mb_hbm_read.argtypes = [P, sz, P, P]
         L.gs_mb_hbm_read.restype = i32
         L.gs_mb_hbm_copy.argtypes = [P, P, sz, P]
@@ -384,6 +387,16 @@ def gs_mb_render_bwd_naive(cam: GsCamera, opt: GsOptions, n, ranges, values, n_p
                                                _p(means2d), _p(conic_opacity), _p(rgb), _p(final_T), _p(n_contrib),
                                                _p(dL_dimage), _p(grad2d), _p(lane_hist), _stream(stream))
     _check(st, "gs_mb_render_bwd_naive")
+
+
+def gs_mb_render_counts(cam: GsCamera, opt: GsOptions, ranges, values, n_pairs, means2d, conic_opacity, rgb, counts,
+                        stream=None):
+    """Adds the blending work counts of one view to counts (int64 [7]): E_f, E_f
+    evaluated by the forward, E_blend, E_b, P_c, executed backward band-steps,
+    the backward's walked tile-entries."""
+    st = load_library().gs_mb_render_counts(C.byref(cam), C.byref(opt), _p(ranges), _p(values), n_pairs,
+                                            _p(means2d), _p(conic_opacity), _p(rgb), _p(counts), _stream(stream))
+    _check(st, "gs_mb_render_counts")
 
 
 def gs_mb_hbm_read(src, sink, stream=None):

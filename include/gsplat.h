@@ -444,6 +444,18 @@ gs_status gs_mb_render_bwd_naive(const gs_camera *cam, const gs_options *opt, in
                                  const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
                                  float *grad2d, uint32_t *lane_hist, void *stream);
 
+/* The work of one view's blending, counted with the forward's own decisions
+ * (one wave per tile, 4 pixels per lane), ADDED to counts[7] (u64):
+ *   [0] E_f: entries each pixel evaluates (up to and including the one that
+ *       stops it, else its tile's whole list); [1] those the forward evaluates
+ *       (passing its 16x4 row band's bound); [2] blended (pixel, entry) pairs;
+ *   [3] E_b = sum of n_contrib; [4] P_c: (tile, entry) pairs with a blended
+ *       pixel; [5] (row band, entry) pairs with a blended pixel (the
+ *       backward's executed band-steps, 64 lanes each); [6] sum over tiles of
+ *       the deepest n_contrib. Inputs as gs_render_fwd; nothing else written. */
+gs_status gs_mb_render_counts(const gs_camera *cam, const gs_options *opt, const uint32_t *ranges,
+                              const uint32_t *values, int64_t n_pairs, const float *means2d,
+                              const float *conic_opacity, const float *rgb, uint64_t *counts, void *stream);
 gs_status gs_mb_hbm_read(const void *src, size_t bytes, float *sink, void *stream);
 /* Copy `bytes` from src to dst -- HBM copy rate; also the reference kernel for
  * scaling rocprof FETCH_SIZE / WRITE_SIZE counters. */
