@@ -475,11 +475,29 @@ typedef struct {
     const uint32_t *ranges, *values;
     const double *means2d, *conic, *opac, *rgb;
     double bg[3];
+    int surfel;         /* 1: 2D Gaussian surfels (S8), records in tf; 0: 3D Gaussians (conic) */
+    const double *tf;   /* surfels: the screen homography M[N,3,3] of S3, row-major */
 } raster_in;
+
+/* S8 for surfel g at pixel centre (pxc, pyc); returns alpha, fills *e. */
+typedef struct {
+    double hx[3], hy[3], k[3], u, v, rho3, rho2, dx, dy, G, oG;
+    int branch3;        /* 1: the surfel's own falloff is the larger, 0: the screen filter's */
+} surfel_eval_t;
+static double surfel_eval(const raster_in *in, uint32_t g, double pxc, double pyc, surfel_eval_t *e);
 
 static double eval_alpha(const raster_in *in, uint32_t g, double pxc, double pyc, double *G_out,
                          double *dx_out, double *dy_out, double *oG_out)
 {
+    if (in->surfel) {
+        surfel_eval_t e;
+        double alpha = surfel_eval(in, g, pxc, pyc, &e);
+        if (G_out) *G_out = e.G;
+        if (dx_out) *dx_out = e.dx;
+        if (dy_out) *dy_out = e.dy;
+        if (oG_out) *oG_out = e.oG;
+        return alpha;
+    }
     double dx = pxc - in->means2d[2 * g], dy = pyc - in->means2d[2 * g + 1];
     double a = in->conic[3 * g], b = in->conic[3 * g + 1], c = in->conic[3 * g + 2];
     double Q = a * dx * dx + 2.0 * b * dx * dy + c * dy * dy;
@@ -520,22 +538,28 @@ static void pixel_forward(const raster_in *in, int px, int py, double C[3], doub
  * final_T[H,W], n_contrib[H,W] (1-based list position of the last blended
  * entry within the tile's list; 0 if none).
  */
-void orc_render_fwd(int W, int H, const uint32_t *ranges, const uint32_t *values,
-                    const double *means2d, const double *conic, const double *opac, const double *rgb,
-                    const double *bg, double *image, double *final_T, uint32_t *n_contrib)
+static void render_fwd_in(const raster_in *in, double *image, double *final_T, uint32_t *n_contrib)
 {
-    raster_in in = {W, H, (W + TILE - 1) / TILE, ranges, values, means2d, conic, opac, rgb, {bg[0], bg[1], bg[2]}};
+    const int W = in->W, H = in->H;
 #pragma omp parallel for schedule(dynamic, 4)
     for (int py = 0; py < H; ++py)
         for (int px = 0; px < W; ++px) {
             double C[3], T;
             uint32_t last;
-            pixel_forward(&in, px, py, C, &T, &last);
+            pixel_forward(in, px, py, C, &T, &last);
             size_t p = (size_t)py * W + px;
-            for (int c = 0; c < 3; ++c) image[(size_t)c * W * H + p] = C[c] + T * in.bg[c];
+            for (int c = 0; c < 3; ++c) image[(size_t)c * W * H + p] = C[c] + T * in->bg[c];
             final_T[p] = T;
             n_contrib[p] = last;
         }
+}
+
+void orc_render_fwd(int W, int H, const uint32_t *ranges, const uint32_t *values,
+                    const double *means2d, const double *conic, const double *opac, const double *rgb,
+                    const double *bg, double *image, double *final_T, uint32_t *n_contrib)
+{
+    raster_in in = {W, H, (W + TILE - 1) / TILE, ranges, values, means2d, conic, opac, rgb, {bg[0], bg[1], bg[2]}};
+    render_fwd_in(&in, image, final_T, n_contrib);
 }
 
 /* Forward of a list of sampled pixels (pix[i] = py * W + px). */
@@ -640,20 +664,18 @@ static void explore(explorer *x, uint32_t i, double T, const double C0[3], uint3
  * ambiguous decision, 2 no match but more than max_amb ambiguous decisions
  * (masked), 3 mismatch. Returns the number of status-3 pixels.
  */
-int64_t orc_match_fwd(int W, int H, const uint32_t *ranges, const uint32_t *values,
-                      const double *means2d, const double *conic, const double *opac, const double *rgb,
-                      const double *bg, const float *gpu_image, const float *gpu_T,
-                      const uint32_t *gpu_nc, double d_alpha, int max_amb, double tol, int8_t *status)
+static int64_t match_in(const raster_in *in, const float *gpu_image, const float *gpu_T, const uint32_t *gpu_nc,
+                        double d_alpha, int max_amb, double tol, int8_t *status)
 {
-    raster_in in = {W, H, (W + TILE - 1) / TILE, ranges, values, means2d, conic, opac, rgb, {bg[0], bg[1], bg[2]}};
+    const int W = in->W, H = in->H;
     int64_t bad = 0;
 #pragma omp parallel for schedule(dynamic, 4) reduction(+ : bad)
     for (int py = 0; py < H; ++py)
         for (int px = 0; px < W; ++px) {
             size_t p = (size_t)py * W + px;
-            int t = (py / TILE) * in.TX + px / TILE;
+            int t = (py / TILE) * in->TX + px / TILE;
             float want[4] = {gpu_image[p], gpu_image[(size_t)W * H + p], gpu_image[(size_t)2 * W * H + p], gpu_T[p]};
-            explorer x = {&in, ranges[2 * t], ranges[2 * t + 1], px + 0.5, py + 0.5, d_alpha, max_amb,
+            explorer x = {in, in->ranges[2 * t], in->ranges[2 * t + 1], px + 0.5, py + 0.5, d_alpha, max_amb,
                           want, gpu_nc[p], tol, 0, 0};
             double C[3] = {0, 0, 0};
             explore(&x, x.s, 1.0, C, 0, 0, 0.0, 1);
@@ -662,6 +684,15 @@ int64_t orc_match_fwd(int W, int H, const uint32_t *ranges, const uint32_t *valu
             if (st == 3) ++bad;
         }
     return bad;
+}
+
+int64_t orc_match_fwd(int W, int H, const uint32_t *ranges, const uint32_t *values,
+                      const double *means2d, const double *conic, const double *opac, const double *rgb,
+                      const double *bg, const float *gpu_image, const float *gpu_T,
+                      const uint32_t *gpu_nc, double d_alpha, int max_amb, double tol, int8_t *status)
+{
+    raster_in in = {W, H, (W + TILE - 1) / TILE, ranges, values, means2d, conic, opac, rgb, {bg[0], bg[1], bg[2]}};
+    return match_in(&in, gpu_image, gpu_T, gpu_nc, d_alpha, max_amb, tol, status);
 }
 
 /* orc_match_fwd restricted to the pixels pix[npix] (flat py*W+px); the
@@ -697,6 +728,9 @@ typedef struct {
     double alpha, T, G, dx, dy, oG;
 } blend_rec;
 
+#define SURFEL_GRAD_N 15
+static void surfel_pixel_grad(const raster_in *in, uint32_t g, double pxc, double pyc, double dalpha, double *d);
+
 static void pixel_backward(const raster_in *in, int px, int py, const double dL[3], double *grad2d,
                            blend_rec *buf)
 {
@@ -726,11 +760,14 @@ static void pixel_backward(const raster_in *in, int px, int py, const double dL[
         double dalpha = 0.0;
         for (int ch = 0; ch < 3; ++ch) dalpha += (c[ch] - A[ch]) * dL[ch];
         dalpha *= r->T;
-        double *gg = &grad2d[9 * (size_t)g];
-        double d[9] = {0};
+        const int nrec = in->surfel ? SURFEL_GRAD_N : 9;
+        double *gg = &grad2d[(size_t)nrec * g];
+        double d[SURFEL_GRAD_N] = {0};
         for (int ch = 0; ch < 3; ++ch) d[ch] = r->alpha * r->T * dL[ch];
         for (int ch = 0; ch < 3; ++ch) A[ch] = r->alpha * c[ch] + (1.0 - r->alpha) * A[ch];
-        if (!(r->oG > ALPHA_MAX)) {
+        if (in->surfel) {
+            if (!(r->oG > ALPHA_MAX)) surfel_pixel_grad(in, g, pxc, pyc, dalpha, d);
+        } else if (!(r->oG > ALPHA_MAX)) {
             double a = in->conic[3 * g], b = in->conic[3 * g + 1], cc = in->conic[3 * g + 2];
             double dQ = -0.5 * r->G * in->opac[g] * dalpha;
             d[3] = r->G * dalpha;
@@ -740,23 +777,20 @@ static void pixel_backward(const raster_in *in, int px, int py, const double dL[
             d[7] = dQ * -2.0 * (a * r->dx + b * r->dy);
             d[8] = dQ * -2.0 * (b * r->dx + cc * r->dy);
         }
-        for (int k = 0; k < 9; ++k) {
+        for (int k = 0; k < nrec; ++k) {
 #pragma omp atomic
             gg[k] += d[k];
         }
     }
 }
 
-void orc_render_bwd(int W, int H, int64_t N, const uint32_t *ranges, const uint32_t *values,
-                    const double *means2d, const double *conic, const double *opac, const double *rgb,
-                    const double *bg, const double *dL_dimage, double *grad2d)
+static void render_bwd_in(const raster_in *in, const double *dL_dimage, double *grad2d)
 {
-    raster_in in = {W, H, (W + TILE - 1) / TILE, ranges, values, means2d, conic, opac, rgb, {bg[0], bg[1], bg[2]}};
+    const int W = in->W, H = in->H;
     int TY = (H + TILE - 1) / TILE;
     uint32_t maxlen = 0;
-    for (int t = 0; t < in.TX * TY; ++t)
-        if (ranges[2 * t + 1] - ranges[2 * t] > maxlen) maxlen = ranges[2 * t + 1] - ranges[2 * t];
-    (void)N;
+    for (int t = 0; t < in->TX * TY; ++t)
+        if (in->ranges[2 * t + 1] - in->ranges[2 * t] > maxlen) maxlen = in->ranges[2 * t + 1] - in->ranges[2 * t];
 #pragma omp parallel
     {
         blend_rec *buf = (blend_rec *)malloc(sizeof(blend_rec) * (maxlen + 1));
@@ -765,10 +799,19 @@ void orc_render_bwd(int W, int H, int64_t N, const uint32_t *ranges, const uint3
             for (int px = 0; px < W; ++px) {
                 size_t p = (size_t)py * W + px;
                 double dL[3] = {dL_dimage[p], dL_dimage[(size_t)W * H + p], dL_dimage[(size_t)2 * W * H + p]};
-                pixel_backward(&in, px, py, dL, grad2d, buf);
+                pixel_backward(in, px, py, dL, grad2d, buf);
             }
         free(buf);
     }
+}
+
+void orc_render_bwd(int W, int H, int64_t N, const uint32_t *ranges, const uint32_t *values,
+                    const double *means2d, const double *conic, const double *opac, const double *rgb,
+                    const double *bg, const double *dL_dimage, double *grad2d)
+{
+    raster_in in = {W, H, (W + TILE - 1) / TILE, ranges, values, means2d, conic, opac, rgb, {bg[0], bg[1], bg[2]}};
+    (void)N;
+    render_bwd_in(&in, dL_dimage, grad2d);
 }
 
 /* ------------------------------------------------------------------ */
@@ -924,29 +967,41 @@ static uint64_t mix64(uint64_t h, uint64_t v)
     return h ^ (h >> 33);
 }
 
-uint64_t orc_decision_hash(int W, int H, const uint32_t *ranges, const uint32_t *values,
-                           const double *means2d, const double *conic, const double *opac)
+static uint64_t decision_hash_in(const raster_in *in)
 {
-    raster_in in = {W, H, (W + TILE - 1) / TILE, ranges, values, means2d, conic, opac, NULL, {0, 0, 0}};
+    const int W = in->W, H = in->H;
     uint64_t total = 0;
     for (int py = 0; py < H; ++py)
         for (int px = 0; px < W; ++px) {
-            int t = (py / TILE) * in.TX + px / TILE;
-            uint32_t s = ranges[2 * t], e = ranges[2 * t + 1];
+            int t = (py / TILE) * in->TX + px / TILE;
+            uint32_t s = in->ranges[2 * t], e = in->ranges[2 * t + 1];
             uint64_t h = mix64(0x1234567ULL, (uint64_t)py * W + px);
             double T = 1.0;
             for (uint32_t i = s; i < e; ++i) {
                 double oG;
-                double alpha = eval_alpha(&in, values[i], px + 0.5, py + 0.5, NULL, NULL, NULL, &oG);
+                surfel_eval_t se;
+                double alpha = eval_alpha(in, in->values[i], px + 0.5, py + 0.5, NULL, NULL, NULL, &oG);
                 if (alpha < ALPHA_MIN) continue;
                 double Tn = T * (1.0 - alpha);
                 if (Tn < T_MIN) { h = mix64(h, 0xffffffffULL + i); break; }
-                h = mix64(h, 2ULL * i + (oG > ALPHA_MAX ? 1 : 0));
+                uint64_t branch = 0;
+                if (in->surfel) {  /* which of the two falloffs is the larger also splits the pieces */
+                    surfel_eval(in, in->values[i], px + 0.5, py + 0.5, &se);
+                    branch = (uint64_t)se.branch3 << 1;
+                }
+                h = mix64(h, 4ULL * i + branch + (oG > ALPHA_MAX ? 1 : 0));
                 T = Tn;
             }
             total += h;
         }
     return total;
+}
+
+uint64_t orc_decision_hash(int W, int H, const uint32_t *ranges, const uint32_t *values,
+                           const double *means2d, const double *conic, const double *opac)
+{
+    raster_in in = {W, H, (W + TILE - 1) / TILE, ranges, values, means2d, conic, opac, NULL, {0, 0, 0}};
+    return decision_hash_in(&in);
 }
 
 /* O13 at the sampled pixels pix[i] = py * W + px only (grad2d accumulated). */
@@ -971,5 +1026,387 @@ void orc_render_bwd_pixels(int W, int H, int64_t N, const uint32_t *ranges, cons
             pixel_backward(&in, (int)(p % W), (int)(p / W), dL, grad2d, buf);
         }
         free(buf);
+    }
+}
+
+/* ================================================================== */
+/* 2D Gaussian surfels: S1-S10.                                         */
+/*                                                                      */
+/* The second pipeline is the one of "2D Gaussian Splatting for          */
+/* Geometrically Accurate Radiance Fields", which the Odin review page   */
+/* evaluates beside 3D Gaussian splatting (referee report summary) and   */
+/* lists among its references. The pages print none of its formulas;    */
+/* the steps are this project's reading of that method. A surfel is a    */
+/* planar Gaussian: centre mu, two tangent axes (the first two columns   */
+/* of its rotation), two scales (s_u, s_v), an opacity and SH colour.    */
+/*                                                                      */
+/*   S1  camera      X = R mu + t; cull z <= near, non-finite inputs     */
+/*   S2  frame       unit quaternion -> Rq, t_u = Rq e1, t_v = Rq e2;    */
+/*                   a = s_u R t_u, b = s_v R t_v (camera frame)         */
+/*   S3  homography  the surfel point (u, v) is the camera point         */
+/*                   X + u a + v b, i.e. the homogeneous screen point    */
+/*                   M (u, v, 1) with M = K [a | b | X],                 */
+/*                   K = [[fx, 0, cx], [0, fy, cy], [0, 0, 1]]           */
+/*   S4  centre      c = (fx X/Z + cx, fy Y/Z + cy), depth Z             */
+/*   S5  extent      the 3-sigma disc u^2 + v^2 <= 9 lies beyond the     */
+/*                   near plane (cull otherwise); its image is an        */
+/*                   ellipse, bounded by the tangents of the dual conic  */
+/*                   M diag(1, 1, -1/9) M^T; r = ceil of the largest     */
+/*                   distance from c to a side of that box, and at least */
+/*                   3 sigma_f of the screen filter                      */
+/*   S6  tile rect   O9 on (c, r)                                        */
+/*   S7  colour      O10                                                 */
+/*   S8  per pixel   rows M0, M1, M2 of M: h_x = M0 - x M2 and            */
+/*                   h_y = M1 - y M2 are the two planes through the      */
+/*                   pixel's ray, written in the surfel's (u, v, 1);     */
+/*                   k = h_x x h_y, (u, v) = (k0/k2, k1/k2) is where the */
+/*                   ray meets the surfel plane, rho3 = u^2 + v^2; the   */
+/*                   screen filter of variance sigma_f^2 = 1/2 gives     */
+/*                   rho2 = |pixel - c|^2 / sigma_f^2;                   */
+/*                   G = exp(-min(rho3, rho2)/2), alpha = min(0.99, o G) */
+/*                   (k2 = 0, a ray parallel to the plane: rho3 = inf);  */
+/*                   compositing as O12                                  */
+/*   S9  backward    O13, the 2D part through S8 (sums of dL/dM and      */
+/*                   dL/dc per surfel)                                   */
+/*   S10 chain rule  per surfel, back through S1-S4 and S7               */
+/* ================================================================== */
+static const double SURFEL_FILTER_VAR = 0.5; /* sigma_f^2, in pixels^2 */
+
+static void cross3(const double a[3], const double b[3], double o[3])
+{
+    o[0] = a[1] * b[2] - a[2] * b[1];
+    o[1] = a[2] * b[0] - a[0] * b[2];
+    o[2] = a[0] * b[1] - a[1] * b[0];
+}
+
+static double surfel_eval(const raster_in *in, uint32_t g, double pxc, double pyc, surfel_eval_t *e)
+{
+    const double *M = in->tf + 9 * (size_t)g;
+    for (int j = 0; j < 3; ++j) {
+        e->hx[j] = M[j] - pxc * M[6 + j];
+        e->hy[j] = M[3 + j] - pyc * M[6 + j];
+    }
+    cross3(e->hx, e->hy, e->k);
+    e->dx = pxc - in->means2d[2 * g];
+    e->dy = pyc - in->means2d[2 * g + 1];
+    e->rho2 = (e->dx * e->dx + e->dy * e->dy) / SURFEL_FILTER_VAR;
+    if (e->k[2] != 0.0) {
+        e->u = e->k[0] / e->k[2];
+        e->v = e->k[1] / e->k[2];
+        e->rho3 = e->u * e->u + e->v * e->v;
+    } else {
+        e->u = e->v = 0.0;
+        e->rho3 = INFINITY;
+    }
+    e->branch3 = e->rho3 <= e->rho2;
+    e->G = exp(-0.5 * (e->branch3 ? e->rho3 : e->rho2));
+    e->oG = in->opac[g] * e->G;
+    return e->oG < ALPHA_MAX ? e->oG : ALPHA_MAX;
+}
+
+/* S9: the 2D part of one blended (pixel, surfel) entry with dL/dalpha =
+ * dalpha (alpha below its clamp): d[3] dL/do, d[4..12] dL/dM (row-major),
+ * d[13..14] dL/dc. */
+static void surfel_pixel_grad(const raster_in *in, uint32_t g, double pxc, double pyc, double dalpha, double *d)
+{
+    surfel_eval_t e;
+    surfel_eval(in, g, pxc, pyc, &e);
+    d[3] = e.G * dalpha;
+    double drho = -0.5 * e.G * in->opac[g] * dalpha; /* alpha = o exp(-rho/2) */
+    if (e.branch3) {
+        double du = 2.0 * e.u * drho, dv = 2.0 * e.v * drho;
+        double dk[3] = {du / e.k[2], dv / e.k[2], -(du * e.u + dv * e.v) / e.k[2]};
+        double dhx[3], dhy[3];
+        cross3(e.hy, dk, dhx); /* d(dk . (hx x hy))/dhx = hy x dk */
+        cross3(dk, e.hx, dhy); /* and /dhy = dk x hx */
+        for (int j = 0; j < 3; ++j) {
+            d[4 + j] = dhx[j];
+            d[7 + j] = dhy[j];
+            d[10 + j] = -pxc * dhx[j] - pyc * dhy[j];
+        }
+    } else {
+        d[13] = drho * -2.0 * e.dx / SURFEL_FILTER_VAR;
+        d[14] = drho * -2.0 * e.dy / SURFEL_FILTER_VAR;
+    }
+}
+
+/* Everything S1-S7 derives for one surfel. */
+typedef struct {
+    int visible;
+    double X[3], qn[4], qnorm, Rq[9], Rtu[3], Rtv[3], a[3], b[3], M[9];
+    double c[2], ext;
+    int64_t r, rect[4];
+    double dir[3], dist, Y[16], raw[3], rgb[3];
+    unsigned char clamp[3];
+    double margin;
+} surfel_fwd;
+
+static void surfel_forward(const ocam *cam, int deg, double near_plane, const double *mean, const double *scale,
+                           const double *quat, double opac, const double *sh, surfel_fwd *o)
+{
+    memset(o, 0, sizeof(*o));
+    o->margin = INFINITY;
+    int K = (deg + 1) * (deg + 1);
+    int TX = (cam->W + TILE - 1) / TILE, TY = (cam->H + TILE - 1) / TILE;
+    int fin = isfin(opac) & isfin(scale[0]) & isfin(scale[1]);
+    for (int i = 0; i < 3; ++i) fin &= isfin(mean[i]);
+    for (int i = 0; i < 4; ++i) fin &= isfin(quat[i]);
+    for (int k = 0; k < K; ++k)
+        for (int c = 0; c < 3; ++c) fin &= isfin(sh[3 * k + c]);
+    if (!fin) return;
+    /* S1 */
+    for (int i = 0; i < 3; ++i)
+        o->X[i] = cam->R[3 * i] * mean[0] + cam->R[3 * i + 1] * mean[1] + cam->R[3 * i + 2] * mean[2] + cam->t[i];
+    double Z = o->X[2];
+    o->margin = fabs(Z - near_plane) / near_plane;
+    if (!(Z > near_plane)) return;
+    /* S2 */
+    double qq = quat[0] * quat[0] + quat[1] * quat[1] + quat[2] * quat[2] + quat[3] * quat[3];
+    if (!(qq > 0.0)) return;
+    o->qnorm = sqrt(qq);
+    for (int i = 0; i < 4; ++i) o->qn[i] = quat[i] / o->qnorm;
+    quat_to_rot(o->qn, o->Rq);
+    for (int i = 0; i < 3; ++i) {
+        double su = 0.0, sv = 0.0;
+        for (int k = 0; k < 3; ++k) {
+            su += cam->R[3 * i + k] * o->Rq[3 * k];
+            sv += cam->R[3 * i + k] * o->Rq[3 * k + 1];
+        }
+        o->Rtu[i] = su;
+        o->Rtv[i] = sv;
+        o->a[i] = scale[0] * su;
+        o->b[i] = scale[1] * sv;
+    }
+    /* S3: row i of K times the columns a, b, X */
+    const double Kr[3][3] = {{cam->fx, 0.0, cam->cx}, {0.0, cam->fy, cam->cy}, {0.0, 0.0, 1.0}};
+    for (int i = 0; i < 3; ++i) {
+        double ra = 0.0, rb = 0.0, rx = 0.0;
+        for (int k = 0; k < 3; ++k) {
+            ra += Kr[i][k] * o->a[k];
+            rb += Kr[i][k] * o->b[k];
+            rx += Kr[i][k] * o->X[k];
+        }
+        o->M[3 * i] = ra;
+        o->M[3 * i + 1] = rb;
+        o->M[3 * i + 2] = rx;
+    }
+    /* S4 */
+    o->c[0] = cam->fx * o->X[0] / Z + cam->cx;
+    o->c[1] = cam->fy * o->X[1] / Z + cam->cy;
+    /* S5: the disc in front of the near plane, then the box of its image */
+    double zmin = Z - 3.0 * sqrt(o->a[2] * o->a[2] + o->b[2] * o->b[2]);
+    {
+        double m = fabs(zmin - near_plane) / near_plane;
+        if (m < o->margin) o->margin = m;
+    }
+    if (!(zmin > near_plane)) return;
+    double Cd[9];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j)
+            Cd[3 * i + j] = o->M[3 * i] * o->M[3 * j] + o->M[3 * i + 1] * o->M[3 * j + 1] -
+                            o->M[3 * i + 2] * o->M[3 * j + 2] / 9.0;
+    double ext = 3.0 * sqrt(SURFEL_FILTER_VAR);
+    for (int ax = 0; ax < 2; ++ax) {
+        /* tangent lines x = s (ax 0) or y = s (ax 1): l = e_ax - s e_3, l^T Cd l = 0 */
+        double A = Cd[4 * ax], B = Cd[3 * ax + 2], C = Cd[8];
+        double disc = B * B - A * C;
+        if (!(disc >= 0.0) || C == 0.0) return;
+        double s1 = (B + sqrt(disc)) / C, s2 = (B - sqrt(disc)) / C;
+        double e1 = fabs(s1 - o->c[ax]), e2 = fabs(s2 - o->c[ax]);
+        if (e1 > ext) ext = e1;
+        if (e2 > ext) ext = e2;
+    }
+    o->ext = ext;
+    if (!isfin(o->c[0]) || !isfin(o->c[1]) || !isfin(ext)) return;
+    if (fabs(o->c[0]) > BIG || fabs(o->c[1]) > BIG || ext > BIG) return;
+    o->r = (int64_t)ceil(ext);
+    {
+        double m = frac_margin(ext);
+        if (m < o->margin) o->margin = m;
+        m = frac_margin(o->c[0]);
+        if (m < o->margin) o->margin = m;
+        m = frac_margin(o->c[1]);
+        if (m < o->margin) o->margin = m;
+    }
+    /* S6 */
+    int64_t fu = (int64_t)floor(o->c[0]), fv = (int64_t)floor(o->c[1]);
+    int64_t X0 = floordiv(fu - o->r, TILE), X1 = floordiv(fu + o->r, TILE);
+    int64_t Y0 = floordiv(fv - o->r, TILE), Y1 = floordiv(fv + o->r, TILE);
+    if (X0 < 0) X0 = 0;
+    if (Y0 < 0) Y0 = 0;
+    if (X1 > TX - 1) X1 = TX - 1;
+    if (Y1 > TY - 1) Y1 = TY - 1;
+    if (X0 > X1 || Y0 > Y1) return;
+    o->rect[0] = X0; o->rect[1] = X1; o->rect[2] = Y0; o->rect[3] = Y1;
+    /* S7 */
+    double campos[3];
+    for (int j = 0; j < 3; ++j)
+        campos[j] = -(cam->R[j] * cam->t[0] + cam->R[3 + j] * cam->t[1] + cam->R[6 + j] * cam->t[2]);
+    double d[3] = {mean[0] - campos[0], mean[1] - campos[1], mean[2] - campos[2]};
+    o->dist = sqrt(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
+    if (!(o->dist > 0.0)) return;
+    for (int j = 0; j < 3; ++j) o->dir[j] = d[j] / o->dist;
+    orc_sh_basis(deg, o->dir[0], o->dir[1], o->dir[2], o->Y);
+    for (int c = 0; c < 3; ++c) {
+        double s = 0.0;
+        for (int k = 0; k < K; ++k) s += sh[3 * k + c] * o->Y[k];
+        o->raw[c] = s + 0.5;
+        o->clamp[c] = o->raw[c] < 0.0;
+        o->rgb[c] = o->clamp[c] ? 0.0 : o->raw[c];
+    }
+    o->visible = 1;
+}
+
+/*
+ * orc_surfel_preprocess: S1-S7 for N surfels. Inputs as orc_preprocess, with
+ * scales[N,2] = (s_u, s_v). Outputs (any may be NULL): means2d[N,2] (c),
+ * depth[N], tf[N,9] (M, row-major), rgb[N,3], radii[N], rect[N,4], tiles[N],
+ * clamp[N,3], margin[N]. Culled surfels get zeros.
+ */
+void orc_surfel_preprocess(int64_t N, const double *camv, int deg, int sh_rows, double near_plane,
+                           const double *means, const double *scales, const double *quats, const double *opac,
+                           const double *sh, double *means2d, double *depth, double *tf, double *rgb,
+                           int32_t *radii, int64_t *rect, int64_t *tiles, uint8_t *clamp, double *margin)
+{
+    ocam cam = cam_from(camv);
+#pragma omp parallel for schedule(static)
+    for (int64_t g = 0; g < N; ++g) {
+        surfel_fwd o;
+        surfel_forward(&cam, deg, near_plane, means + 3 * g, scales + 2 * g, quats + 4 * g, opac[g],
+                       sh + (size_t)3 * sh_rows * g, &o);
+        int vis = o.visible;
+        if (means2d) { means2d[2 * g] = vis ? o.c[0] : 0.0; means2d[2 * g + 1] = vis ? o.c[1] : 0.0; }
+        if (depth) depth[g] = vis ? o.X[2] : 0.0;
+        if (tf) for (int i = 0; i < 9; ++i) tf[9 * g + i] = vis ? o.M[i] : 0.0;
+        if (rgb) for (int i = 0; i < 3; ++i) rgb[3 * g + i] = vis ? o.rgb[i] : 0.0;
+        if (radii) radii[g] = vis ? (int32_t)o.r : 0;
+        if (rect) for (int i = 0; i < 4; ++i) rect[4 * g + i] = vis ? o.rect[i] : 0;
+        if (tiles) tiles[g] = vis ? (o.rect[1] - o.rect[0] + 1) * (o.rect[3] - o.rect[2] + 1) : 0;
+        if (clamp) for (int i = 0; i < 3; ++i) clamp[3 * g + i] = vis ? o.clamp[i] : 0;
+        if (margin) margin[g] = o.margin;
+    }
+}
+
+/* S8 + O12 over the image, from the tile lists of orc_bin_sort on (c, r). */
+void orc_surfel_render_fwd(int W, int H, const uint32_t *ranges, const uint32_t *values, const double *means2d,
+                           const double *tf, const double *opac, const double *rgb, const double *bg, double *image,
+                           double *final_T, uint32_t *n_contrib)
+{
+    raster_in in = {W, H, (W + TILE - 1) / TILE, ranges, values, means2d, NULL, opac, rgb, {bg[0], bg[1], bg[2]},
+                    1, tf};
+    render_fwd_in(&in, image, final_T, n_contrib);
+}
+
+/* orc_match_fwd for surfels. */
+int64_t orc_surfel_match_fwd(int W, int H, const uint32_t *ranges, const uint32_t *values, const double *means2d,
+                             const double *tf, const double *opac, const double *rgb, const double *bg,
+                             const float *gpu_image, const float *gpu_T, const uint32_t *gpu_nc, double d_alpha,
+                             int max_amb, double tol, int8_t *status)
+{
+    raster_in in = {W, H, (W + TILE - 1) / TILE, ranges, values, means2d, NULL, opac, rgb, {bg[0], bg[1], bg[2]},
+                    1, tf};
+    return match_in(&in, gpu_image, gpu_T, gpu_nc, d_alpha, max_amb, tol, status);
+}
+
+/* S9: grad[N,15] accumulated: drgb[3], dopacity, dM[9] (row-major), dc[2]. */
+void orc_surfel_render_bwd(int W, int H, const uint32_t *ranges, const uint32_t *values, const double *means2d,
+                           const double *tf, const double *opac, const double *rgb, const double *bg,
+                           const double *dL_dimage, double *grad)
+{
+    raster_in in = {W, H, (W + TILE - 1) / TILE, ranges, values, means2d, NULL, opac, rgb, {bg[0], bg[1], bg[2]},
+                    1, tf};
+    render_bwd_in(&in, dL_dimage, grad);
+}
+
+uint64_t orc_surfel_decision_hash(int W, int H, const uint32_t *ranges, const uint32_t *values,
+                                  const double *means2d, const double *tf, const double *opac)
+{
+    raster_in in = {W, H, (W + TILE - 1) / TILE, ranges, values, means2d, NULL, opac, NULL, {0, 0, 0}, 1, tf};
+    return decision_hash_in(&in);
+}
+
+/*
+ * orc_surfel_preprocess_bwd: S10. grad[N,15] as orc_surfel_render_bwd gives
+ * it. Outputs ACCUMULATED: dmeans[N,3], dscales[N,2], dquats[N,4], dopac[N],
+ * dsh[N,sh_rows,3].
+ */
+void orc_surfel_preprocess_bwd(int64_t N, const double *camv, int deg, int sh_rows, double near_plane,
+                               const double *means, const double *scales, const double *quats, const double *opac,
+                               const double *sh, const double *grad, double *dmeans, double *dscales,
+                               double *dquats, double *dopac, double *dsh)
+{
+    ocam cam = cam_from(camv);
+    int K = (deg + 1) * (deg + 1);
+#pragma omp parallel for schedule(static)
+    for (int64_t g = 0; g < N; ++g) {
+        surfel_fwd o;
+        const double *shg = sh + (size_t)3 * sh_rows * g;
+        surfel_forward(&cam, deg, near_plane, means + 3 * g, scales + 2 * g, quats + 4 * g, opac[g], shg, &o);
+        if (!o.visible) continue;
+        const double *d = grad + (size_t)SURFEL_GRAD_N * g;
+        double dmu[3] = {0, 0, 0};
+        /* colour, as O14 */
+        double draw[3];
+        for (int c = 0; c < 3; ++c) draw[c] = o.clamp[c] ? 0.0 : d[c];
+        double dY[48];
+        orc_sh_basis_grad(deg, o.dir[0], o.dir[1], o.dir[2], dY);
+        double ddir[3] = {0, 0, 0};
+        for (int k = 0; k < K; ++k)
+            for (int c = 0; c < 3; ++c) {
+                dsh[(size_t)3 * sh_rows * g + 3 * k + c] += o.Y[k] * draw[c];
+                for (int j = 0; j < 3; ++j) ddir[j] += shg[3 * k + c] * dY[3 * k + j] * draw[c];
+            }
+        double dd = o.dir[0] * ddir[0] + o.dir[1] * ddir[1] + o.dir[2] * ddir[2];
+        for (int j = 0; j < 3; ++j) dmu[j] += (ddir[j] - o.dir[j] * dd) / o.dist;
+        /* S3: M = K [a | b | X], so the columns' gradients are K^T times dM's columns */
+        const double Kr[3][3] = {{cam.fx, 0.0, cam.cx}, {0.0, cam.fy, cam.cy}, {0.0, 0.0, 1.0}};
+        double da[3], db[3], dX[3];
+        for (int k = 0; k < 3; ++k) {
+            double sa = 0.0, sb = 0.0, sx = 0.0;
+            for (int i = 0; i < 3; ++i) {
+                sa += Kr[i][k] * d[4 + 3 * i];
+                sb += Kr[i][k] * d[4 + 3 * i + 1];
+                sx += Kr[i][k] * d[4 + 3 * i + 2];
+            }
+            da[k] = sa;
+            db[k] = sb;
+            dX[k] = sx;
+        }
+        /* S4 */
+        double Z = o.X[2];
+        dX[0] += cam.fx / Z * d[13];
+        dX[1] += cam.fy / Z * d[14];
+        dX[2] += -cam.fx * o.X[0] / (Z * Z) * d[13] - cam.fy * o.X[1] / (Z * Z) * d[14];
+        for (int j = 0; j < 3; ++j) dmu[j] += cam.R[j] * dX[0] + cam.R[3 + j] * dX[1] + cam.R[6 + j] * dX[2];
+        /* S2: a = s_u R t_u, b = s_v R t_v */
+        double dsu = 0.0, dsv = 0.0;
+        for (int i = 0; i < 3; ++i) {
+            dsu += o.Rtu[i] * da[i];
+            dsv += o.Rtv[i] * db[i];
+        }
+        dscales[2 * g] += dsu;
+        dscales[2 * g + 1] += dsv;
+        double Rb[9] = {0};  /* dL/dRq: columns 0 and 1 are dL/dt_u, dL/dt_v */
+        for (int k = 0; k < 3; ++k) {
+            double su = 0.0, sv = 0.0;
+            for (int i = 0; i < 3; ++i) {
+                su += cam.R[3 * i + k] * da[i];
+                sv += cam.R[3 * i + k] * db[i];
+            }
+            Rb[3 * k] = scales[2 * g] * su;
+            Rb[3 * k + 1] = scales[2 * g + 1] * sv;
+        }
+        double D[4][9], qb[4];
+        drot_dq(o.qn, D);
+        for (int k = 0; k < 4; ++k) {
+            double s = 0;
+            for (int i = 0; i < 9; ++i) s += Rb[i] * D[k][i];
+            qb[k] = s;
+        }
+        double qdot = 0;
+        for (int k = 0; k < 4; ++k) qdot += o.qn[k] * qb[k];
+        for (int k = 0; k < 4; ++k) dquats[4 * g + k] += (qb[k] - qdot * o.qn[k]) / o.qnorm;
+        dopac[g] += d[3];
+        for (int j = 0; j < 3; ++j) dmeans[3 * g + j] += dmu[j];
     }
 }

@@ -67,6 +67,18 @@ def lib():
             L.orc_sh_basis_grad.argtypes = [i32, f64, f64, f64, P]
             L.orc_decision_hash.argtypes = [i32, i32] + [P] * 5
             L.orc_decision_hash.restype = C.c_uint64
+            L.orc_surfel_preprocess.argtypes = [i64, P, i32, i32, f64] + [P] * 5 + [P] * 9
+            L.orc_surfel_preprocess.restype = None
+            L.orc_surfel_render_fwd.argtypes = [i32, i32] + [P] * 10
+            L.orc_surfel_render_fwd.restype = None
+            L.orc_surfel_match_fwd.argtypes = [i32, i32] + [P] * 10 + [f64, i32, f64, P]
+            L.orc_surfel_match_fwd.restype = i64
+            L.orc_surfel_render_bwd.argtypes = [i32, i32] + [P] * 9
+            L.orc_surfel_render_bwd.restype = None
+            L.orc_surfel_decision_hash.argtypes = [i32, i32] + [P] * 5
+            L.orc_surfel_decision_hash.restype = C.c_uint64
+            L.orc_surfel_preprocess_bwd.argtypes = [i64, P, i32, i32, f64] + [P] * 6 + [P] * 5
+            L.orc_surfel_preprocess_bwd.restype = None
             L.orc_set_threads.argtypes = [i32]
             L.orc_max_threads.restype = i32
             _lib = L
@@ -353,3 +365,102 @@ def densify_stats(grad2d, radii, grad_accum, count, max_radius):
     cnt[drawn] += 1
     mr[drawn] = np.maximum(mr[drawn], np.asarray(radii)[drawn])
     return acc, cnt, mr
+
+
+# ---------------------------------------------------------------- 2D Gaussian surfels (S1-S10)
+
+SURFEL_GRAD_N = 15  # drgb[3], dopacity, dM[9] (row-major), dc[2]
+
+
+def surfel_preprocess(means, scales, quats, opac, sh, cam, deg, near=0.2):
+    """Steps S1-S7 for every surfel (scales [N, 2]); returns a dict with means2d
+    (the projected centre c), depth, tf (the homography M [N, 9]), rgb, radii,
+    rect, tiles, clamp and margin."""
+    means, scales, quats, opac, sh = _d(means), _d(scales), _d(quats), _d(opac), _d(sh)
+    N = means.shape[0]
+    rows = sh.shape[1] if sh.ndim == 3 else 1
+    out = dict(means2d=np.zeros((N, 2)), depth=np.zeros(N), tf=np.zeros((N, 9)), rgb=np.zeros((N, 3)),
+               radii=np.zeros(N, np.int32), rect=np.zeros((N, 4), np.int64), tiles=np.zeros(N, np.int64),
+               clamp=np.zeros((N, 3), np.uint8), margin=np.zeros(N))
+    lib().orc_surfel_preprocess(N, _p(cam_array(cam)), deg, rows, float(np.float32(near)), _p(means), _p(scales),
+                                _p(quats), _p(opac), _p(sh), _p(out["means2d"]), _p(out["depth"]), _p(out["tf"]),
+                                _p(out["rgb"]), _p(out["radii"]), _p(out["rect"]), _p(out["tiles"]),
+                                _p(out["clamp"]), _p(out["margin"]))
+    return out
+
+
+def _vals(values):
+    return np.ascontiguousarray(values, np.uint32) if len(values) else np.zeros(1, np.uint32)
+
+
+def surfel_render_fwd(W, H, ranges, values, means2d, tf, opac, rgb, bg=(0.0, 0.0, 0.0)):
+    """S8 with O12 over the image: (image[3,H,W], final_T[H,W], n_contrib[H,W])."""
+    image, T, nc = np.zeros((3, H, W)), np.zeros((H, W)), np.zeros((H, W), np.uint32)
+    lib().orc_surfel_render_fwd(W, H, _p(np.ascontiguousarray(ranges, np.uint32)), _p(_vals(values)),
+                                _p(_d(means2d)), _p(_d(tf)), _p(_d(opac)), _p(_d(rgb)), _p(_d(bg)), _p(image),
+                                _p(T), _p(nc))
+    return image, T, nc
+
+
+def surfel_match_fwd(W, H, ranges, values, means2d, tf, opac, rgb, gpu_image, gpu_T, gpu_nc,
+                     bg=(0.0, 0.0, 0.0), d_alpha=4e-6, max_amb=4, tol=1e-5):
+    """:func:`match_fwd` for surfels."""
+    status = np.zeros((H, W), np.int8)
+    lib().orc_surfel_match_fwd(W, H, _p(np.ascontiguousarray(ranges, np.uint32)), _p(_vals(values)),
+                               _p(_d(means2d)), _p(_d(tf)), _p(_d(opac)), _p(_d(rgb)), _p(_d(bg)),
+                               _p(np.ascontiguousarray(gpu_image, np.float32)),
+                               _p(np.ascontiguousarray(gpu_T, np.float32)),
+                               _p(np.ascontiguousarray(gpu_nc, np.uint32)), float(d_alpha), int(max_amb),
+                               float(tol), _p(status))
+    return status
+
+
+def surfel_render_bwd(W, H, N, ranges, values, means2d, tf, opac, rgb, dL_dimage, bg=(0.0, 0.0, 0.0)):
+    """S9: per-surfel sums [N, 15] = (drgb, dopacity, dM row-major, dc)."""
+    grad = np.zeros((N, SURFEL_GRAD_N))
+    lib().orc_surfel_render_bwd(W, H, _p(np.ascontiguousarray(ranges, np.uint32)), _p(_vals(values)),
+                                _p(_d(means2d)), _p(_d(tf)), _p(_d(opac)), _p(_d(rgb)), _p(_d(bg)),
+                                _p(_d(dL_dimage)), _p(grad))
+    return grad
+
+
+def surfel_decision_hash(W, H, ranges, values, means2d, tf, opac):
+    return int(lib().orc_surfel_decision_hash(W, H, _p(np.ascontiguousarray(ranges, np.uint32)), _p(_vals(values)),
+                                              _p(_d(means2d)), _p(_d(tf)), _p(_d(opac))))
+
+
+def surfel_preprocess_bwd(means, scales, quats, opac, sh, cam, deg, grad, near=0.2):
+    """S10: parameter gradients (scales [N, 2]) from the S9 sums."""
+    means, scales, quats, opac, sh = _d(means), _d(scales), _d(quats), _d(opac), _d(sh)
+    N = means.shape[0]
+    rows = sh.shape[1] if sh.ndim == 3 else 1
+    g = dict(means=np.zeros((N, 3)), scales=np.zeros((N, 2)), quats=np.zeros((N, 4)), opacities=np.zeros(N),
+             sh=np.zeros_like(sh))
+    lib().orc_surfel_preprocess_bwd(N, _p(cam_array(cam)), deg, rows, float(np.float32(near)), _p(means),
+                                    _p(scales), _p(quats), _p(opac), _p(sh), _p(_d(grad)), _p(g["means"]),
+                                    _p(g["scales"]), _p(g["quats"]), _p(g["opacities"]), _p(g["sh"]))
+    return g
+
+
+def surfel_forward(params, cam, deg, near=0.2, bg=(0.0, 0.0, 0.0)):
+    """S1-S8 end to end (binning by O11 on (c, r))."""
+    pre = surfel_preprocess(params["means"], params["scales"], params["quats"], params["opacities"], params["sh"],
+                            cam, deg, near)
+    W, H = int(cam.width), int(cam.height)
+    keys, values, ranges = bin_sort(pre["means2d"], pre["radii"], pre["depth"].astype(np.float32), W, H)
+    image, T, nc = surfel_render_fwd(W, H, ranges, values, pre["means2d"], pre["tf"], params["opacities"],
+                                     pre["rgb"], bg)
+    return dict(pre=pre, keys=keys, values=values, ranges=ranges, image=image, final_T=T, n_contrib=nc)
+
+
+def surfel_backward(params, cam, deg, fwd, dL_dimage, near=0.2, bg=(0.0, 0.0, 0.0)):
+    """S9-S10 end to end from :func:`surfel_forward`'s intermediates."""
+    pre = fwd["pre"]
+    W, H = int(cam.width), int(cam.height)
+    N = pre["means2d"].shape[0]
+    grad = surfel_render_bwd(W, H, N, fwd["ranges"], fwd["values"], pre["means2d"], pre["tf"],
+                             params["opacities"], pre["rgb"], dL_dimage, bg)
+    g = surfel_preprocess_bwd(params["means"], params["scales"], params["quats"], params["opacities"],
+                              params["sh"], cam, deg, grad, near)
+    g["grad"] = grad
+    return g
