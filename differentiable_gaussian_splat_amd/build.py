@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgsplat_hip.so")
-SOURCES = ["api.hip", "preprocess.hip", "binsort.hip", "render.hip", "optim.hip", "microbench.hip"]
+SOURCES = ["api.hip", "preprocess.hip", "binsort.hip", "render.hip", "surfel.hip", "optim.hip", "microbench.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

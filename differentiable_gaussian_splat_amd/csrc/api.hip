@@ -565,6 +565,142 @@ gs_status gs_preprocess_bwd(const gs_camera* cam, const gs_options* opt, int64_t
     }
 }
 
+// ---------------------------------------------------------------- 2D Gaussian surfels
+
+gs_status gs_surfel_preprocess(const gs_camera* cam, const gs_options* opt, int64_t n, const float* means,
+                               const float* scales, const float* quats, const float* opacities, const float* sh,
+                               float* means2d, float* depths, float* transforms, float* rgb, int32_t* radii,
+                               uint32_t* tiles_touched, uint8_t* clamped, void* stream) {
+    try {
+        g_err[0] = 0;
+        Checked c;
+        gs_status st = check_common(cam, opt, n, c);
+        if (st != GS_OK) return st;
+        if (n == 0) return GS_OK;
+        REQUIRE(means && scales && quats && opacities && sh && means2d && depths && transforms && rgb && radii &&
+                    tiles_touched && clamped,
+                "gs_surfel_preprocess: NULL array");
+        REQUIRE(aligned(quats, 16) && aligned(transforms, 16) && aligned(means2d, 8),
+                "quats and transforms must be 16-byte aligned, means2d 8-byte aligned");
+        return hip_check(gs::launch_surfel_preprocess(c.cam, c.K, c.sh_rows, opt->near_plane, (int)n, means, scales,
+                                                      quats, opacities, sh, means2d, depths, transforms, rgb, radii,
+                                                      tiles_touched, clamped, (hipStream_t)stream),
+                         "gs_surfel_preprocess");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_surfel_preprocess: unexpected exception");
+    }
+}
+
+gs_status gs_surfel_render_fwd(const gs_camera* cam, const gs_options* opt, int64_t n, const uint32_t* ranges,
+                               const uint32_t* values, int64_t n_pairs, const float* transforms, const float* rgb,
+                               float* image, float* final_T, uint32_t* n_contrib, void* stream) {
+    try {
+        g_err[0] = 0;
+        Checked c;
+        gs_status st = check_common(cam, opt, n, c);
+        if (st != GS_OK) return st;
+        REQUIRE(ranges && image && final_T && n_contrib, "gs_surfel_render_fwd: NULL array");
+        REQUIRE(n_pairs >= 0 && n_pairs < ((int64_t)1 << 31), "n_pairs must be in [0, 2^31)");
+        REQUIRE(n_pairs == 0 || (values && transforms && rgb), "gs_surfel_render_fwd: NULL array");
+        REQUIRE(aligned(ranges, 8) && (!transforms || aligned(transforms, 16)),
+                "ranges must be 8-byte aligned, transforms 16-byte aligned");
+        return hip_check(gs::launch_surfel_render_fwd(c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values,
+                                                      transforms, rgb, opt->bg, image, final_T, n_contrib,
+                                                      (hipStream_t)stream),
+                         "gs_surfel_render_fwd");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_surfel_render_fwd: unexpected exception");
+    }
+}
+
+gs_status gs_surfel_render_bwd_raster(const gs_camera* cam, const gs_options* opt, int64_t n, const uint32_t* ranges,
+                                      const uint32_t* values, int64_t n_pairs, const float* transforms,
+                                      const float* rgb, const float* final_T, const uint32_t* n_contrib,
+                                      const float* dL_dimage, float* grad, void* stream) {
+    try {
+        g_err[0] = 0;
+        Checked c;
+        gs_status st = check_common(cam, opt, n, c);
+        if (st != GS_OK) return st;
+        if (n == 0) return GS_OK;
+        REQUIRE(ranges && final_T && n_contrib && dL_dimage && grad, "gs_surfel_render_bwd_raster: NULL array");
+        REQUIRE(n_pairs >= 0 && n_pairs < ((int64_t)1 << 31), "n_pairs must be in [0, 2^31)");
+        if (n_pairs == 0) return GS_OK;
+        REQUIRE(values && transforms && rgb, "gs_surfel_render_bwd_raster: NULL array");
+        REQUIRE(aligned(ranges, 8) && aligned(transforms, 16) && aligned(grad, 16),
+                "ranges must be 8-byte aligned, transforms and grad 16-byte aligned");
+        return hip_check(gs::launch_surfel_render_bwd(c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values,
+                                                      transforms, rgb, opt->bg, final_T, n_contrib, dL_dimage, grad,
+                                                      (hipStream_t)stream),
+                         "gs_surfel_render_bwd_raster");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_surfel_render_bwd_raster: unexpected exception");
+    }
+}
+
+gs_status gs_surfel_preprocess_bwd(const gs_camera* cam, const gs_options* opt, int64_t n, const float* means,
+                                   const float* scales, const float* quats, const float* sh, const float* transforms,
+                                   const int32_t* radii, const uint8_t* clamped, const float* grad, float* dL_dmeans,
+                                   float* dL_dscales, float* dL_dquats, float* dL_dopacities, float* dL_dsh,
+                                   void* stream) {
+    try {
+        g_err[0] = 0;
+        Checked c;
+        gs_status st = check_common(cam, opt, n, c);
+        if (st != GS_OK) return st;
+        if (n == 0) return GS_OK;
+        REQUIRE(means && scales && quats && sh && transforms && radii && clamped && grad && dL_dmeans && dL_dscales &&
+                    dL_dquats && dL_dopacities && dL_dsh,
+                "gs_surfel_preprocess_bwd: NULL array");
+        REQUIRE(aligned(quats, 16) && aligned(dL_dquats, 16) && aligned(transforms, 16) && aligned(grad, 16),
+                "quats, dL_dquats, transforms and grad must be 16-byte aligned");
+        return hip_check(gs::launch_surfel_preprocess_bwd(c.cam, c.K, c.sh_rows, (int)n, means, scales, quats, sh,
+                                                          transforms, radii, clamped, grad, dL_dmeans, dL_dscales,
+                                                          dL_dquats, dL_dopacities, dL_dsh,
+                                                          opt->overwrite_grads != 0, (hipStream_t)stream),
+                         "gs_surfel_preprocess_bwd");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_surfel_preprocess_bwd: unexpected exception");
+    }
+}
+
+size_t gs_surfel_render_bwd_workspace_size(int64_t n) {
+    if (n < 0) return 0;
+    return ((size_t)(n > 0 ? n : 1) * gs::SURFEL_GRAD_STRIDE * sizeof(float) + 255) & ~(size_t)255;
+}
+
+gs_status gs_surfel_render_bwd(const gs_camera* cam, const gs_options* opt, int64_t n, const float* means,
+                               const float* scales, const float* quats, const float* sh, const float* transforms,
+                               const float* rgb, const int32_t* radii, const uint8_t* clamped, const uint32_t* ranges,
+                               const uint32_t* values, int64_t n_pairs, const float* final_T,
+                               const uint32_t* n_contrib, const float* dL_dimage, float* dL_dmeans,
+                               float* dL_dscales, float* dL_dquats, float* dL_dopacities, float* dL_dsh,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    try {
+        g_err[0] = 0;
+        Checked c;
+        gs_status st = check_common(cam, opt, n, c);
+        if (st != GS_OK) return st;
+        if (n == 0) return GS_OK;
+        REQUIRE(workspace && aligned(workspace, 256), "workspace must be non-NULL and 256-byte aligned");
+        const size_t need = gs_surfel_render_bwd_workspace_size(n);
+        REQUIRE(workspace_bytes >= need, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+        float* grad = reinterpret_cast<float*>(workspace);
+        hipStream_t s = (hipStream_t)stream;
+        st = hip_check(gs::launch_fill_u32(reinterpret_cast<uint32_t*>(grad), (size_t)n * gs::SURFEL_GRAD_STRIDE, 0u,
+                                           s),
+                       "gs_surfel_render_bwd(zero)");
+        if (st != GS_OK) return st;
+        st = gs_surfel_render_bwd_raster(cam, opt, n, ranges, values, n_pairs, transforms, rgb, final_T, n_contrib,
+                                         dL_dimage, grad, stream);
+        if (st != GS_OK) return st;
+        return gs_surfel_preprocess_bwd(cam, opt, n, means, scales, quats, sh, transforms, radii, clamped, grad,
+                                        dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh, stream);
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_surfel_render_bwd: unexpected exception");
+    }
+}
+
 // ---------------------------------------------------------------- several views per launch
 
 gs_status gs_preprocess_views(const gs_camera* cams, int32_t n_views, const gs_options* opt, int64_t n,

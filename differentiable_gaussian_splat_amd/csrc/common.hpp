@@ -60,6 +60,16 @@ __device__ __forceinline__ bool tile_rect(float u, float v, int r, int TX, int T
     return X0 <= X1 && Y0 <= Y1;
 }
 
+// Tile `tile` of the grid of views stacked vertically (TX x TY tiles each):
+// its view, returned, and its column and row inside that view.
+__device__ __forceinline__ int view_of_tile(int tile, int TX, int TY, int& tx, int& ty) {
+    const int row = tile / TX;
+    const int view = row / TY;
+    tx = tile - row * TX;
+    ty = row - view * TY;
+    return view;
+}
+
 // j -> (j / w, j % w) for 0 <= j < 2^23 and 1 <= w <= 2^11: a float
 // reciprocal gives q within one of the quotient; one exact fixup each way.
 __device__ __forceinline__ void divmod_small(int j, int w, int& q, int& r) {

@@ -28,6 +28,27 @@ hipError_t launch_preprocess_bwd(const DevCam& cam, int K, int sh_rows, float lo
                                  float* d_opac, float* d_sh, float* d_means2d, bool overwrite,
                                  const DensifyStats& stats, hipStream_t stream);
 
+// 2D Gaussian surfels: projection (scales [n, 2]; tf [n, 12] = three float4 per
+// surfel: (M row 0, opacity), (M row 1, c_x), (M row 2, c_y)), and the chain rule
+// from the per-surfel pixel sums grad [n, 16].
+hipError_t launch_surfel_preprocess(const DevCam& cam, int K, int sh_rows, float near_plane, int n,
+                                    const float* means, const float* scales, const float* quats, const float* opac,
+                                    const float* sh, float* means2d, float* depths, float* tf, float* rgb,
+                                    int* radii, uint32_t* tiles, uint8_t* clamped, hipStream_t stream);
+hipError_t launch_surfel_preprocess_bwd(const DevCam& cam, int K, int sh_rows, int n, const float* means,
+                                        const float* scales, const float* quats, const float* sh, const float* tf,
+                                        const int* radii, const uint8_t* clamped, const float* grad, float* d_means,
+                                        float* d_scales, float* d_quats, float* d_opac, float* d_sh, bool overwrite,
+                                        hipStream_t stream);
+hipError_t launch_surfel_render_fwd(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
+                                    const float* tf, const float* rgb, const float* bg, float* image, float* final_T,
+                                    uint32_t* n_contrib, hipStream_t stream);
+hipError_t launch_surfel_render_bwd(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
+                                    const float* tf, const float* rgb, const float* bg, const float* final_T,
+                                    const uint32_t* n_contrib, const float* dL_dimage, float* grad,
+                                    hipStream_t stream);
+constexpr int SURFEL_GRAD_STRIDE = 16;  // floats per surfel record of pixel sums
+
 // The same for V views of one image size (per-view arrays of V x n entries).
 hipError_t launch_preprocess_views(const CamSet& cams, int V, int K, int sh_rows, float lowpass, float near_plane,
                                    int n, const float* means, const float* scales, const float* quats,

@@ -401,6 +401,78 @@ __device__ __forceinline__ bool project(const DevCam& cam, float lowpass, float 
     return tile_rect(p.u, p.v, p.r, cam.TX, cam.TY, p.X0, p.X1, p.Y0, p.Y1);
 }
 
+// The projection of one 2D Gaussian surfel (finite inputs): tangent axes
+// t_u, t_v (the first two columns of its rotation) scaled by (s_u, s_v) and
+// turned into the camera frame, a = s_u R t_u and b = s_v R t_v; the surfel
+// point (u, v) is the camera point X + u a + v b, so the homogeneous screen
+// point is M (u, v, 1) with M = K [a | b | X]. Its 3-sigma disc must lie beyond
+// the near plane; the bounding box of the disc's image (an ellipse) follows
+// from the dual conic M diag(1, 1, -1/9) M^T, whose vertical and horizontal
+// tangents solve a quadratic each. r is the largest distance from the
+// projected centre c to a side of that box, at least 3 sigma of the screen
+// filter (variance 1/2). In double, rounded once per output, as project().
+struct SurfelProj {
+    float M[9];
+    float u, v, depth;
+    int r, X0, X1, Y0, Y1;
+};
+
+constexpr double SURFEL_FILTER_VAR = 0.5;  // screen filter variance, pixels^2
+
+__device__ __forceinline__ bool project_surfel(const DevCam& cam, float near_plane, float mx, float my, float mz,
+                                              float su, float sv, float4 q, SurfelProj& p) {
+    const double X = mx, Y = my, Z = mz;
+    double R[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) R[i] = (double)cam.R[i];
+    const double x = fma(R[0], X, fma(R[1], Y, fma(R[2], Z, (double)cam.t[0])));
+    const double y = fma(R[3], X, fma(R[4], Y, fma(R[5], Z, (double)cam.t[1])));
+    const double z = fma(R[6], X, fma(R[7], Y, fma(R[8], Z, (double)cam.t[2])));
+    if (!(z > (double)near_plane)) return false;
+    const double qw = q.x, qx = q.y, qy = q.z, qz = q.w;
+    const double qq = fma(qw, qw, fma(qx, qx, fma(qy, qy, qz * qz)));
+    if (!(qq > 0.0)) return false;
+    const double inv = 1.0 / sqrt(qq);
+    const double w = qw * inv, a1 = qx * inv, b1 = qy * inv, c1 = qz * inv;
+    // columns 0 and 1 of the unit quaternion's rotation
+    const double tu[3] = {1.0 - 2.0 * (b1 * b1 + c1 * c1), 2.0 * (a1 * b1 + w * c1), 2.0 * (a1 * c1 - w * b1)};
+    const double tv[3] = {2.0 * (a1 * b1 - w * c1), 1.0 - 2.0 * (a1 * a1 + c1 * c1), 2.0 * (b1 * c1 + w * a1)};
+    double a[3], b[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        a[i] = (double)su * fma(R[3 * i], tu[0], fma(R[3 * i + 1], tu[1], R[3 * i + 2] * tu[2]));
+        b[i] = (double)sv * fma(R[3 * i], tv[0], fma(R[3 * i + 1], tv[1], R[3 * i + 2] * tv[2]));
+    }
+    if (!(z - 3.0 * sqrt(fma(a[2], a[2], b[2] * b[2])) > (double)near_plane)) return false;
+    const double fx = cam.fx, fy = cam.fy, cx = cam.cx, cy = cam.cy;
+    const double M[9] = {fma(fx, a[0], cx * a[2]), fma(fx, b[0], cx * b[2]), fma(fx, x, cx * z),
+                         fma(fy, a[1], cy * a[2]), fma(fy, b[1], cy * b[2]), fma(fy, y, cy * z),
+                         a[2],                     b[2],                     z};
+    const double u = fma(fx, x / z, cx), v = fma(fy, y / z, cy);
+    // dual conic entries D_ij = M_i0 M_j0 + M_i1 M_j1 - M_i2 M_j2 / 9
+    auto dual = [&](int i, int j) { return fma(M[3 * i], M[3 * j], fma(M[3 * i + 1], M[3 * j + 1], -M[3 * i + 2] * M[3 * j + 2] / 9.0)); };
+    const double D22 = dual(2, 2);
+    double ext = 3.0 * sqrt(SURFEL_FILTER_VAR);
+    const double cen[2] = {u, v};
+#pragma unroll
+    for (int ax = 0; ax < 2; ++ax) {
+        const double A = dual(ax, ax), B = dual(ax, 2);
+        const double disc = fma(B, B, -A * D22);
+        if (!(disc >= 0.0) || D22 == 0.0) return false;
+        const double sq = sqrt(disc);
+        ext = fmax(ext, fmax(fabs((B + sq) / D22 - cen[ax]), fabs((B - sq) / D22 - cen[ax])));
+    }
+    if (!(fabs(u) <= (double)BIG && fabs(v) <= (double)BIG && ext <= (double)BIG)) return false;  // also on NaN
+#pragma unroll
+    for (int i = 0; i < 9; ++i) p.M[i] = (float)M[i];
+    p.u = (float)u;
+    p.v = (float)v;
+    p.depth = (float)z;
+    p.r = (int)ceil(ext);
+    return tile_rect(p.u, p.v, p.r, cam.TX, cam.TY, p.X0, p.X1, p.Y0, p.Y1);
+}
+
+template <bool SURFEL>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(6))) void k_preprocess(
     DevCam cam, int K, int sh_rows, float lowpass, float near_plane, int n,
     const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
@@ -408,30 +480,52 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(6))) void k_
     float2* __restrict__ means2d, float* __restrict__ depths, float4* __restrict__ conic_op,
     float* __restrict__ rgb_out, int* __restrict__ radii, uint32_t* __restrict__ tiles,
     uint8_t* __restrict__ clamped) {
+    // SURFEL: scales hold (s_u, s_v) and conic_op three float4 per surfel, (M row 0, o),
+    // (M row 1, c_x), (M row 2, c_y); otherwise three scales and one float4 (a, beta, gamma, o).
     extern __shared__ float s_sh[];
     const int base = blockIdx.x * 64;
     const int gi = base + threadIdx.x;
     const bool live = gi < n;
     const size_t g = live ? (size_t)gi : (size_t)base;
     float mx = means[3 * g], my = means[3 * g + 1], mz = means[3 * g + 2];
-    float s0 = scales[3 * g], s1 = scales[3 * g + 1], s2 = scales[3 * g + 2];
+    constexpr int NS = SURFEL ? 2 : 3;
+    float s0 = scales[NS * g], s1 = scales[NS * g + 1], s2 = SURFEL ? 1.f : scales[NS * g + 2];
     float4 q = quats[g];
     float o = opac[g];
 
     bool ok = live && finitef(mx) && finitef(my) && finitef(mz) && finitef(s0) && finitef(s1) && finitef(s2) &&
               finitef(q.x) && finitef(q.y) && finitef(q.z) && finitef(q.w) && finitef(o);
-    Proj pr;
-    ok = ok && project(cam, lowpass, near_plane, mx, my, mz, s0, s1, s2, q, pr);
     // the projection's outputs first: the SH rows staged below need the registers
-    if (live) {
-        if (ok) {
-            means2d[g] = make_float2(pr.u, pr.v);
-            depths[g] = pr.depth;
-            conic_op[g] = make_float4(pr.a, pr.beta, pr.gamma, o);
-            radii[g] = pr.r;
-            tiles[g] = (uint32_t)((pr.X1 - pr.X0 + 1) * (pr.Y1 - pr.Y0 + 1));
-        } else {
-            write_culled(g, means2d, depths, conic_op, rgb_out, radii, tiles, clamped);
+    if constexpr (SURFEL) {
+        SurfelProj pr;
+        ok = ok && project_surfel(cam, near_plane, mx, my, mz, s0, s1, q, pr);
+        if (live) {
+            if (ok) {
+                means2d[g] = make_float2(pr.u, pr.v);
+                depths[g] = pr.depth;
+                conic_op[3 * g] = make_float4(pr.M[0], pr.M[1], pr.M[2], o);
+                conic_op[3 * g + 1] = make_float4(pr.M[3], pr.M[4], pr.M[5], pr.u);
+                conic_op[3 * g + 2] = make_float4(pr.M[6], pr.M[7], pr.M[8], pr.v);
+                radii[g] = pr.r;
+                tiles[g] = (uint32_t)((pr.X1 - pr.X0 + 1) * (pr.Y1 - pr.Y0 + 1));
+            } else {
+                write_culled(g, means2d, depths, conic_op + 2 * g, rgb_out, radii, tiles, clamped);  // [3 g]
+                conic_op[3 * g + 1] = conic_op[3 * g + 2] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+    } else {
+        Proj pr;
+        ok = ok && project(cam, lowpass, near_plane, mx, my, mz, s0, s1, s2, q, pr);
+        if (live) {
+            if (ok) {
+                means2d[g] = make_float2(pr.u, pr.v);
+                depths[g] = pr.depth;
+                conic_op[g] = make_float4(pr.a, pr.beta, pr.gamma, o);
+                radii[g] = pr.r;
+                tiles[g] = (uint32_t)((pr.X1 - pr.X0 + 1) * (pr.Y1 - pr.Y0 + 1));
+            } else {
+                write_culled(g, means2d, depths, conic_op, rgb_out, radii, tiles, clamped);
+            }
         }
     }
     // colour from the SH rows of the visible Gaussians, chunk by chunk through LDS
@@ -463,8 +557,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(6))) void k_
         }
     }
     if (!ok) return;
-    if (!(dist > 0.f && finitef(raw[0]) && finitef(raw[1]) && finitef(raw[2]))) {
-        write_culled(g, means2d, depths, conic_op, rgb_out, radii, tiles, clamped);  // culled after all
+    if (!(dist > 0.f && finitef(raw[0]) && finitef(raw[1]) && finitef(raw[2]))) {  // culled after all
+        if constexpr (SURFEL) {
+            write_culled(g, means2d, depths, conic_op + 2 * g, rgb_out, radii, tiles, clamped);  // [3 g]
+            conic_op[3 * g + 1] = conic_op[3 * g + 2] = make_float4(0.f, 0.f, 0.f, 0.f);
+        } else {
+            write_culled(g, means2d, depths, conic_op, rgb_out, radii, tiles, clamped);
+        }
         return;
     }
     uint8_t cl = 0;
@@ -993,6 +1092,167 @@ __global__ __launch_bounds__(64) void k_preprocess_bwd_views(
     }
 }
 
+
+// The chain rule of one view for 2D Gaussian surfels, one lane per surfel,
+// from its summed pixel terms (16 floats: dL/drgb, sum h, the sums of dL/dk
+// and of (pixel - c) times it for the expanded intersection
+// k = N01 + x N12 - y N02, the filter branch's sum of h (pixel - c), zero) to
+// the activated parameters. The cross
+// products N01 = M0 x M1, N12 = M1 x M2, N02 = M0 x M2 give dL/dM;
+// M = K [a | b | X] (a = s_u R t_u, b = s_v R t_v, X = R mu + t)
+// gives dL/da, dL/db and dL/dX as K^T times the columns of dL/dM; the
+// projected centre c adds through X; t_u and t_v are the first two columns of
+// the quaternion's rotation. Outputs accumulate (+=), or with OVERWRITE are
+// written (zeros for a culled surfel and for SH rows at or past the active
+// degree). The SH row moves through registers.
+template <bool OVERWRITE>
+__global__ __launch_bounds__(64) void k_surfel_preprocess_bwd(
+    DevCam cam, int K, int sh_rows, int n, const float* __restrict__ means, const float* __restrict__ scales,
+    const float4* __restrict__ quats, const float* __restrict__ sh, const float4* __restrict__ tf,
+    const int* __restrict__ radii, const uint8_t* __restrict__ clamped, const float4* __restrict__ grad,
+    float* __restrict__ d_means, float* __restrict__ d_scales, float* __restrict__ d_quats,
+    float* __restrict__ d_opac, float* __restrict__ d_sh) {
+    const int gi = blockIdx.x * 64 + threadIdx.x;
+    if (gi >= n) return;
+    const size_t g = (size_t)gi;
+    const float* shg = sh + g * 3 * sh_rows;
+    float* dsh = d_sh + g * 3 * sh_rows;
+    const bool drawn = radii[g] > 0;
+    const float mx = means[3 * g], my = means[3 * g + 1], mz = means[3 * g + 2];
+    const float X[3] = {fmaf(cam.R[0], mx, fmaf(cam.R[1], my, fmaf(cam.R[2], mz, cam.t[0]))),
+                        fmaf(cam.R[3], mx, fmaf(cam.R[4], my, fmaf(cam.R[5], mz, cam.t[1]))),
+                        fmaf(cam.R[6], mx, fmaf(cam.R[7], my, fmaf(cam.R[8], mz, cam.t[2])))};
+    const float4 q = quats[g];
+    const float qq = q.x * q.x + q.y * q.y + q.z * q.z + q.w * q.w;
+    const float ddx = mx - cam.campos[0], ddy = my - cam.campos[1], ddz = mz - cam.campos[2];
+    const float dist = sqrtf(fmaf(ddx, ddx, fmaf(ddy, ddy, ddz * ddz)));
+    if (!drawn || !(X[2] > 0.f) || !(qq > 0.f) || !(dist > 0.f)) {
+        if (OVERWRITE) {
+            d_means[3 * g] = d_means[3 * g + 1] = d_means[3 * g + 2] = 0.f;
+            d_scales[2 * g] = d_scales[2 * g + 1] = 0.f;
+            reinterpret_cast<float4*>(d_quats)[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+            d_opac[g] = 0.f;
+            for (int e = 0; e < 3 * sh_rows; ++e) dsh[e] = 0.f;
+        }
+        return;
+    }
+    const float su = scales[2 * g], sv = scales[2 * g + 1];
+    const float qn = sqrtf(qq), iq = 1.0f / qn;
+    const float w = q.x * iq, x = q.y * iq, y = q.z * iq, z = q.w * iq;
+    const float tu[3] = {1.f - 2.f * (y * y + z * z), 2.f * (x * y + w * z), 2.f * (x * z - w * y)};
+    const float tv[3] = {2.f * (x * y - w * z), 1.f - 2.f * (x * x + z * z), 2.f * (y * z + w * x)};
+    // record: g0 = (drgb, sum h), g1 = (sum dL/dk, sum dx dL/dk .x), g2 = (sum dx dL/dk .yz,
+    // sum dy dL/dk .xy), g3 = (sum dy dL/dk .z, sum_f h dx, sum_f h dy, 0), with (dx, dy) = pixel - c
+    // and k = N01 + x N12 - y N02, N01 = M0 x M1, N12 = M1 x M2, N02 = M0 x M2 (rows Mi of M):
+    // dL/dN01 = sum dL/dk, dL/dN12 = sum x dL/dk, dL/dN02 = -sum y dL/dk
+    const float4 g0 = grad[4 * g], g1 = grad[4 * g + 1], g2 = grad[4 * g + 2], g3 = grad[4 * g + 3];
+    const float4 t0 = tf[3 * g], t1 = tf[3 * g + 1], t2 = tf[3 * g + 2];
+    const float ccx = t1.w, ccy = t2.w;
+    const float dN01[3] = {g1.x, g1.y, g1.z};
+    const float dN12[3] = {fmaf(ccx, g1.x, g1.w), fmaf(ccx, g1.y, g2.x), fmaf(ccx, g1.z, g2.y)};
+    const float dN02[3] = {-fmaf(ccy, g1.x, g2.z), -fmaf(ccy, g1.y, g2.w), -fmaf(ccy, g1.z, g3.x)};
+    const float M0[3] = {t0.x, t0.y, t0.z}, M1[3] = {t1.x, t1.y, t1.z}, M2[3] = {t2.x, t2.y, t2.z};
+    auto cross = [](const float* p, const float* q, float* o) {
+        o[0] = fmaf(p[1], q[2], -p[2] * q[1]);
+        o[1] = fmaf(p[2], q[0], -p[0] * q[2]);
+        o[2] = fmaf(p[0], q[1], -p[1] * q[0]);
+    };
+    // dM0 = M1 x dN01 + M2 x dN02, dM1 = dN01 x M0 + M2 x dN12, dM2 = dN12 x M1 + dN02 x M0
+    float c1[3], c2[3], dM0[3], dM1[3], dM2[3];
+    cross(M1, dN01, c1);
+    cross(M2, dN02, c2);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) dM0[j] = c1[j] + c2[j];
+    cross(dN01, M0, c1);
+    cross(M2, dN12, c2);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) dM1[j] = c1[j] + c2[j];
+    cross(dN12, M1, c1);
+    cross(dN02, M0, c2);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) dM2[j] = c1[j] + c2[j];
+    const float fx = cam.fx, fy = cam.fy, cx = cam.cx, cy = cam.cy;
+    // K^T = [[fx, 0, 0], [0, fy, 0], [cx, cy, 1]] times the columns of dL/dM
+    const float da[3] = {fx * dM0[0], fy * dM1[0], fmaf(cx, dM0[0], fmaf(cy, dM1[0], dM2[0]))};
+    const float db[3] = {fx * dM0[1], fy * dM1[1], fmaf(cx, dM0[1], fmaf(cy, dM1[1], dM2[1]))};
+    float dX[3] = {fx * dM0[2], fy * dM1[2], fmaf(cx, dM0[2], fmaf(cy, dM1[2], dM2[2]))};
+    // the centre c = (fx X / Z + cx, fy Y / Z + cy): dL/dc = 2 sum_f h (pixel - c)
+    const float dcx = 2.f * g3.y, dcy = 2.f * g3.z;
+    const float iz = 1.0f / X[2];
+    dX[0] = fmaf(fx * iz, dcx, dX[0]);
+    dX[1] = fmaf(fy * iz, dcy, dX[1]);
+    dX[2] -= (fx * X[0] * dcx + fy * X[1] * dcy) * iz * iz;
+    float dmu[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) dmu[j] = fmaf(cam.R[j], dX[0], fmaf(cam.R[3 + j], dX[1], cam.R[6 + j] * dX[2]));
+    // a = s_u R t_u, b = s_v R t_v
+    float dsu = 0.f, dsv = 0.f, dtu[3], dtv[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const float rtu = fmaf(cam.R[3 * i], tu[0], fmaf(cam.R[3 * i + 1], tu[1], cam.R[3 * i + 2] * tu[2]));
+        const float rtv = fmaf(cam.R[3 * i], tv[0], fmaf(cam.R[3 * i + 1], tv[1], cam.R[3 * i + 2] * tv[2]));
+        dsu = fmaf(rtu, da[i], dsu);
+        dsv = fmaf(rtv, db[i], dsv);
+        dtu[i] = su * fmaf(cam.R[i], da[0], fmaf(cam.R[3 + i], da[1], cam.R[6 + i] * da[2]));
+        dtv[i] = sv * fmaf(cam.R[i], db[0], fmaf(cam.R[3 + i], db[1], cam.R[6 + i] * db[2]));
+    }
+    // dL/dRq (row-major): columns 0 and 1 are dL/dt_u and dL/dt_v, column 2 is zero
+    const float dR[9] = {dtu[0], dtv[0], 0.f, dtu[1], dtv[1], 0.f, dtu[2], dtv[2], 0.f};
+    const float gw = 2.f * (-z * dR[1] + y * dR[2] + z * dR[3] - x * dR[5] - y * dR[6] + x * dR[7]);
+    const float gx = 2.f * (y * dR[1] + z * dR[2] + y * dR[3] - 2.f * x * dR[4] - w * dR[5] + z * dR[6] +
+                            w * dR[7] - 2.f * x * dR[8]);
+    const float gy = 2.f * (-2.f * y * dR[0] + x * dR[1] + w * dR[2] + x * dR[3] + z * dR[5] - w * dR[6] +
+                            z * dR[7] - 2.f * y * dR[8]);
+    const float gz = 2.f * (-2.f * z * dR[0] - w * dR[1] + x * dR[2] + w * dR[3] - 2.f * z * dR[4] + y * dR[5] +
+                            x * dR[6] + y * dR[7]);
+    const float qdot = w * gw + x * gx + y * gy + z * gz;
+    const float4 dq = make_float4((gw - qdot * w) * iq, (gx - qdot * x) * iq, (gy - qdot * y) * iq,
+                                  (gz - qdot * z) * iq);
+    // colour: rgb = max(0, sum_k sh_k Y_k(dir) + 0.5), dir = (mu - campos) / |mu - campos|
+    const uint8_t cl = clamped[g];
+    float dcol[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) dcol[c] = (cl >> c) & 1 ? 0.f : (c == 0 ? g0.x : c == 1 ? g0.y : g0.z);
+    const float id = 1.0f / dist;
+    const float dxn = ddx * id, dyn = ddy * id, dzn = ddz * id;
+    float Y[16], wk[16];
+    sh_eval(K, dxn, dyn, dzn, Y);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        if (k < K) {
+            const float c0 = shg[3 * k], c1 = shg[3 * k + 1], c2 = shg[3 * k + 2];
+            wk[k] = fmaf(c0, dcol[0], fmaf(c1, dcol[1], c2 * dcol[2]));
+            const float p0 = OVERWRITE ? 0.f : dsh[3 * k], p1 = OVERWRITE ? 0.f : dsh[3 * k + 1],
+                        p2 = OVERWRITE ? 0.f : dsh[3 * k + 2];
+            dsh[3 * k] = fmaf(Y[k], dcol[0], p0);
+            dsh[3 * k + 1] = fmaf(Y[k], dcol[1], p1);
+            dsh[3 * k + 2] = fmaf(Y[k], dcol[2], p2);
+        }
+    }
+    if (OVERWRITE)
+        for (int e = 3 * K; e < 3 * sh_rows; ++e) dsh[e] = 0.f;
+    float3 gdir = make_float3(0.f, 0.f, 0.f);
+    sh_grad_accum(K, dxn, dyn, dzn, wk, gdir);
+    const float dd = dxn * gdir.x + dyn * gdir.y + dzn * gdir.z;
+    dmu[0] += (gdir.x - dxn * dd) * id;
+    dmu[1] += (gdir.y - dyn * dd) * id;
+    dmu[2] += (gdir.z - dzn * dd) * id;
+    const float o = t0.w;
+    auto prior = [&](const float* p) { return OVERWRITE ? 0.f : *p; };
+#pragma unroll
+    for (int j = 0; j < 3; ++j) d_means[3 * g + j] = prior(&d_means[3 * g + j]) + dmu[j];
+    d_scales[2 * g] = prior(&d_scales[2 * g]) + dsu;
+    d_scales[2 * g + 1] = prior(&d_scales[2 * g + 1]) + dsv;
+    float4* dqp = reinterpret_cast<float4*>(d_quats) + g;
+    float4 dq0 = OVERWRITE ? make_float4(0.f, 0.f, 0.f, 0.f) : *dqp;
+    dq0.x += dq.x;
+    dq0.y += dq.y;
+    dq0.z += dq.z;
+    dq0.w += dq.w;
+    *dqp = dq0;
+    d_opac[g] = prior(&d_opac[g]) + (o != 0.f ? g0.w / o : 0.f);
+}
+
 }  // namespace
 
 hipError_t launch_preprocess(const DevCam& cam, int K, int sh_rows, float lowpass, float near_plane, int n,
@@ -1002,10 +1262,45 @@ hipError_t launch_preprocess(const DevCam& cam, int K, int sh_rows, float lowpas
     if (n == 0) return hipSuccess;
     int blocks = (n + 63) / 64;
     size_t lds = sizeof(float) * 64 * CHUNK_STRIDE;
-    k_preprocess<<<blocks, 64, lds, stream>>>(cam, K, sh_rows, lowpass, near_plane, n, means, scales,
+    k_preprocess<false><<<blocks, 64, lds, stream>>>(cam, K, sh_rows, lowpass, near_plane, n, means, scales,
                                              reinterpret_cast<const float4*>(quats), opac, sh,
                                              reinterpret_cast<float2*>(means2d), depths,
                                              reinterpret_cast<float4*>(conic_op), rgb, radii, tiles, clamped);
+    return hipGetLastError();
+}
+
+hipError_t launch_surfel_preprocess(const DevCam& cam, int K, int sh_rows, float near_plane, int n,
+                                    const float* means, const float* scales, const float* quats, const float* opac,
+                                    const float* sh, float* means2d, float* depths, float* tf, float* rgb,
+                                    int* radii, uint32_t* tiles, uint8_t* clamped, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const int blocks = (n + 63) / 64;
+    const size_t lds = sizeof(float) * 64 * CHUNK_STRIDE;
+    k_preprocess<true><<<blocks, 64, lds, stream>>>(cam, K, sh_rows, 0.f, near_plane, n, means, scales,
+                                                    reinterpret_cast<const float4*>(quats), opac, sh,
+                                                    reinterpret_cast<float2*>(means2d), depths,
+                                                    reinterpret_cast<float4*>(tf), rgb, radii, tiles, clamped);
+    return hipGetLastError();
+}
+
+hipError_t launch_surfel_preprocess_bwd(const DevCam& cam, int K, int sh_rows, int n, const float* means,
+                                        const float* scales, const float* quats, const float* sh, const float* tf,
+                                        const int* radii, const uint8_t* clamped, const float* grad, float* d_means,
+                                        float* d_scales, float* d_quats, float* d_opac, float* d_sh, bool overwrite,
+                                        hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const int blocks = (n + 63) / 64;
+    auto* q4 = reinterpret_cast<const float4*>(quats);
+    auto* t4 = reinterpret_cast<const float4*>(tf);
+    auto* g4 = reinterpret_cast<const float4*>(grad);
+    if (overwrite)
+        k_surfel_preprocess_bwd<true><<<blocks, 64, 0, stream>>>(cam, K, sh_rows, n, means, scales, q4, sh, t4, radii,
+                                                                 clamped, g4, d_means, d_scales, d_quats, d_opac,
+                                                                 d_sh);
+    else
+        k_surfel_preprocess_bwd<false><<<blocks, 64, 0, stream>>>(cam, K, sh_rows, n, means, scales, q4, sh, t4,
+                                                                  radii, clamped, g4, d_means, d_scales, d_quats,
+                                                                  d_opac, d_sh);
     return hipGetLastError();
 }
 

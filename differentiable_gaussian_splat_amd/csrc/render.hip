@@ -142,15 +142,6 @@ __device__ __forceinline__ uint32_t stage_record_bands(uint32_t g, uint32_t pos,
 // walks and 0 once it has stopped (or lies outside the image): a stopped
 // pixel's effective alpha is 0, which changes nothing, and its T (>= 1e-4)
 // can never trigger the stop test again.
-// Tile `tile` of the grid of views stacked vertically (TX x TY tiles each):
-// its view, returned, and its column and row inside that view.
-__device__ __forceinline__ int view_of_tile(int tile, int TX, int TY, int& tx, int& ty) {
-    const int row = tile / TX;
-    const int view = row / TY;
-    tx = tile - row * TX;
-    ty = row - view * TY;
-    return view;
-}
 
 template <int PPL>
 __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY, int ntiles,

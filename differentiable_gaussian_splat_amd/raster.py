@@ -72,7 +72,9 @@ EXPORTS = ["gs_default_options", "gs_version", "gs_last_error", "gs_preprocess",
            "gs_preprocess_bwd", "gs_preprocess_views", "gs_bin_sort_views_workspace_size", "gs_bin_sort_views",
            "gs_render_fwd_views", "gs_render_bwd_raster_views", "gs_preprocess_bwd_views", "gs_adam_step",
            "gs_mb_render_bwd_naive", "gs_mb_hbm_read", "gs_mb_hbm_copy", "gs_mb_atomic", "gs_render_bwd_noalloc",
-           "gs_mb_render_counts"]
+           "gs_mb_render_counts", "gs_surfel_preprocess", "gs_surfel_render_fwd", "gs_surfel_render_bwd_raster",
+           "gs_surfel_preprocess_bwd", "gs_surfel_render_bwd_workspace_size", "gs_surfel_render_bwd"]
+SURFEL_GRAD_STRIDE = 16
 NOALLOC_MAX_N = 1 << 20  # GS_NOALLOC_MAX_N
 MAX_VIEWS = 32
 GRAD2D_STRIDE = 12
@@ -138,6 +140,19 @@ def load_library(path: str = LIB_PATH):
         L.gs_mb_render_bwd_naive.restype = i32
         L.gs_mb_render_counts.argtypes = [cam, opt, P, P, i64, P, P, P, P, P]
         L.gs_mb_render_counts.restype = i32
+        L.gs_surfel_preprocess.argtypes = [cam, opt, i64] + [P] * 5 + [P] * 7 + [P]
+        L.gs_surfel_preprocess.restype = i32
+        L.gs_surfel_render_fwd.argtypes = [cam, opt, i64, P, P, i64, P, P, P, P, P, P]
+        L.gs_surfel_render_fwd.restype = i32
+        L.gs_surfel_render_bwd_raster.argtypes = [cam, opt, i64, P, P, i64] + [P] * 6 + [P]
+        L.gs_surfel_render_bwd_raster.restype = i32
+        L.gs_surfel_preprocess_bwd.argtypes = [cam, opt, i64] + [P] * 8 + [P] * 5 + [P]
+        L.gs_surfel_preprocess_bwd.restype = i32
+        L.gs_surfel_render_bwd_workspace_size.argtypes = [i64]
+        L.gs_surfel_render_bwd_workspace_size.restype = sz
+        L.gs_surfel_render_bwd.argtypes = ([cam, opt, i64] + [P] * 8 + [P, P, i64] + [P] * 3 + [P] * 5 +
+                                           [P, sz, P])
+        L.gs_surfel_render_bwd.restype = i32
         L.gs_mb_hbm_read.argtypes = [P, sz, P, P]
         L.gs_mb_hbm_read.restype = i32
         L.gs_mb_hbm_copy.argtypes = [P, P, sz, P]
@@ -399,6 +414,59 @@ def gs_mb_render_counts(cam: GsCamera, opt: GsOptions, ranges, values, n_pairs, 
     _check(st, "gs_mb_render_counts")
 
 
+# ---------------------------------------------------------------- 2D Gaussian surfels
+
+def gs_surfel_preprocess(cam: GsCamera, opt: GsOptions, means, scales, quats, opacities, sh, means2d, depths,
+                         transforms, rgb, radii, tiles_touched, clamped, stream=None):
+    n = means.shape[0]
+    st = load_library().gs_surfel_preprocess(C.byref(cam), C.byref(opt), n, _p(means), _p(scales), _p(quats),
+                                             _p(opacities), _p(sh), _p(means2d), _p(depths), _p(transforms), _p(rgb),
+                                             _p(radii), _p(tiles_touched), _p(clamped), _stream(stream))
+    _check(st, "gs_surfel_preprocess")
+
+
+def gs_surfel_render_fwd(cam: GsCamera, opt: GsOptions, n, ranges, values, n_pairs, transforms, rgb, image, final_T,
+                         n_contrib, stream=None):
+    st = load_library().gs_surfel_render_fwd(C.byref(cam), C.byref(opt), n, _p(ranges), _p(values), n_pairs,
+                                             _p(transforms), _p(rgb), _p(image), _p(final_T), _p(n_contrib),
+                                             _stream(stream))
+    _check(st, "gs_surfel_render_fwd")
+
+
+def gs_surfel_render_bwd_raster(cam: GsCamera, opt: GsOptions, n, ranges, values, n_pairs, transforms, rgb, final_T,
+                                n_contrib, dL_dimage, grad, stream=None):
+    st = load_library().gs_surfel_render_bwd_raster(C.byref(cam), C.byref(opt), n, _p(ranges), _p(values), n_pairs,
+                                                    _p(transforms), _p(rgb), _p(final_T), _p(n_contrib),
+                                                    _p(dL_dimage), _p(grad), _stream(stream))
+    _check(st, "gs_surfel_render_bwd_raster")
+
+
+def gs_surfel_preprocess_bwd(cam: GsCamera, opt: GsOptions, means, scales, quats, sh, transforms, radii, clamped,
+                             grad, dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh, stream=None):
+    n = means.shape[0]
+    st = load_library().gs_surfel_preprocess_bwd(C.byref(cam), C.byref(opt), n, _p(means), _p(scales), _p(quats),
+                                                 _p(sh), _p(transforms), _p(radii), _p(clamped), _p(grad),
+                                                 _p(dL_dmeans), _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities),
+                                                 _p(dL_dsh), _stream(stream))
+    _check(st, "gs_surfel_preprocess_bwd")
+
+
+def gs_surfel_render_bwd_workspace_size(n) -> int:
+    return int(load_library().gs_surfel_render_bwd_workspace_size(n))
+
+
+def gs_surfel_render_bwd(cam: GsCamera, opt: GsOptions, means, scales, quats, sh, transforms, rgb, radii, clamped,
+                         ranges, values, n_pairs, final_T, n_contrib, dL_dimage, dL_dmeans, dL_dscales, dL_dquats,
+                         dL_dopacities, dL_dsh, workspace, stream=None):
+    n = means.shape[0]
+    st = load_library().gs_surfel_render_bwd(
+        C.byref(cam), C.byref(opt), n, _p(means), _p(scales), _p(quats), _p(sh), _p(transforms), _p(rgb), _p(radii),
+        _p(clamped), _p(ranges), _p(values), n_pairs, _p(final_T), _p(n_contrib), _p(dL_dimage), _p(dL_dmeans),
+        _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities), _p(dL_dsh), _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gs_surfel_render_bwd")
+
+
 def gs_mb_hbm_read(src, sink, stream=None):
     _check(load_library().gs_mb_hbm_read(_p(src), src.numel() * src.element_size(), _p(sink), _stream(stream)),
            "gs_mb_hbm_read")
@@ -538,6 +606,48 @@ class Rasterizer:
                       frame.final_T, frame.n_contrib, dL_dimage, grads["means"], grads["scales"], grads["quats"],
                       grads["opacities"], grads["sh"], grads.get("means2d") if want_means2d else None,
                       self._bwd_ws, stats, frame.ckpt)
+        return grads
+
+    def surfel_forward(self, camera, means, scales, quats, opacities, sh, sh_degree, near_plane=0.2,
+                       bg=(0.0, 0.0, 0.0)) -> "Frame":
+        """2D Gaussian surfels (scales [n, 2]): projection, the same binning, compositing.
+        The frame's conic_opacity field holds the surfels' transforms [n, 12]."""
+        cam = camera if isinstance(camera, GsCamera) else make_camera(camera)
+        opt = make_options(sh_degree, sh.shape[1], 0.3, near_plane, bg)
+        n, dev = means.shape[0], means.device
+        pre = dict(means2d=_empty((n, 2), torch.float32, dev), depths=_empty(n, torch.float32, dev),
+                   conic_opacity=_empty((n, 12), torch.float32, dev), rgb=_empty((n, 3), torch.float32, dev),
+                   radii=_empty(n, torch.int32, dev), tiles_touched=_empty(n, torch.int32, dev),
+                   clamped=_empty(n, torch.uint8, dev))
+        gs_surfel_preprocess(cam, opt, means, scales, quats, opacities, sh, pre["means2d"], pre["depths"],
+                             pre["conic_opacity"], pre["rgb"], pre["radii"], pre["tiles_touched"], pre["clamped"])
+        P, ranges = self.bin_sort(cam, opt, pre)
+        W, H = cam.width, cam.height
+        image = _empty((3, H, W), torch.float32, self.device)
+        final_T = _empty((H, W), torch.float32, self.device)
+        n_contrib = _empty((H, W), torch.int32, self.device)
+        gs_surfel_render_fwd(cam, opt, n, ranges, self._values, P, pre["conic_opacity"], pre["rgb"], image, final_T,
+                             n_contrib)
+        return Frame(cam, opt, W, H, pre["means2d"], pre["depths"], pre["conic_opacity"], pre["rgb"], pre["radii"],
+                     pre["tiles_touched"], pre["clamped"], P, self._keys, self._values, ranges, image, final_T,
+                     n_contrib, None)
+
+    def surfel_backward(self, frame: "Frame", means, scales, quats, sh, dL_dimage, grads: dict,
+                        overwrite: bool = False):
+        """Accumulates (or with ``overwrite`` writes) surfel parameter gradients
+        into ``grads`` (means [n,3], scales [n,2], quats, opacities, sh)."""
+        n = means.shape[0]
+        need = gs_surfel_render_bwd_workspace_size(n)
+        if self._bwd_ws is None or self._bwd_ws.numel() < need:
+            self._bwd_ws = _empty(need, torch.uint8, self.device)
+        opt = frame.opt
+        if overwrite:
+            opt = GsOptions.from_buffer_copy(frame.opt)
+            opt.overwrite_grads = 1
+        gs_surfel_render_bwd(frame.cam, opt, means, scales, quats, sh, frame.conic_opacity, frame.rgb, frame.radii,
+                             frame.clamped, frame.ranges, frame.values, frame.n_pairs, frame.final_T,
+                             frame.n_contrib, dL_dimage, grads["means"], grads["scales"], grads["quats"],
+                             grads["opacities"], grads["sh"], self._bwd_ws)
         return grads
 
 

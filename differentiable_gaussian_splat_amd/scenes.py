@@ -221,3 +221,10 @@ def subset(scene: Scene, idx) -> Scene:
                  scene.scales[idx].copy(), scene.quats[idx].copy(), scene.opacity_logits[idx].copy(),
                  scene.opacities[idx].copy(), scene.sh[idx].copy(), scene.sh_degree,
                  list(scene.cameras), scene.dL_dimage, scene.name)
+
+
+def surfel_scales(scene: Scene) -> np.ndarray:
+    """The 2D Gaussian surfel variant of a workload: the same draws, with a
+    surfel's two scales (s_u, s_v) taken from the first two of the Gaussian's
+    three (fp32, [N, 2])."""
+    return np.ascontiguousarray(scene.scales[:, :2])

@@ -301,6 +301,93 @@ gs_status gs_preprocess_bwd(const gs_camera *cam, const gs_options *opt, int64_t
                             float *dL_dopacities, float *dL_dsh, float *dL_dmeans2d,
                             const gs_densify_stats *stats, void *stream);
 
+/* ------------------------------------------------------------------------
+ * 2D Gaussian surfels (planar Gaussians): the second pipeline the Odin review
+ * page evaluates beside 3D Gaussian splatting (referee report summary: 3DGS,
+ * 2DGS, TamingGS, DashGS), after "2D Gaussian Splatting for Geometrically
+ * Accurate Radiance Fields" in its references. The page prints none of the
+ * method's formulas; the library's reading:
+ *  - a surfel has a centre mean[3], a unit quaternion whose rotation's first
+ *    two columns are its tangent axes t_u, t_v, two activated scales
+ *    scales[n,2] = (s_u, s_v), an opacity and SH colour (as gs_preprocess);
+ *  - the surfel point (u, v) is the world point mean + u s_u t_u + v s_v t_v;
+ *    with a = s_u R t_u, b = s_v R t_v, X = R mean + t (camera frame) it lands
+ *    at the homogeneous screen point M (u, v, 1), M = K [a | b | X],
+ *    K = [[fx, 0, cx], [0, fy, cy], [0, 0, 1]];
+ *  - culled when the centre's depth or the nearest point of the 3-sigma disc
+ *    u^2 + v^2 <= 9 is at or before the near plane, on non-finite inputs, or
+ *    when |c| or the extent passes 2^24 px;
+ *  - c = the projected centre, depth = its camera z; radius r = ceil of the
+ *    largest distance from c to a side of the bounding box of the disc's
+ *    image (tangents of the dual conic M diag(1, 1, -1/9) M^T), at least
+ *    3 sqrt(1/2) (the screen filter's 3 sigma); the tile rectangle is that of
+ *    gs_preprocess on (c, r), so gs_bin_sort bins surfels unchanged;
+ *  - per pixel centre (x, y): h_x = M0 - x M2, h_y = M1 - y M2 (rows of M),
+ *    k = h_x x h_y, (u, v) = (k0, k1) / k2; G = exp(-rho / 2) with
+ *    rho = min(u^2 + v^2, 2 |(x, y) - c|^2) (the surfel's own falloff or a
+ *    screen filter of variance 1/2, the wider one); alpha = min(0.99, o G)
+ *    and the compositing rules of gs_render_fwd.
+ * transforms[n,12] (16-byte aligned): three float4 per surfel,
+ * (M row 0, opacity), (M row 1, c_x), (M row 2, c_y).
+ * grad[n, GS_SURFEL_GRAD_STRIDE] pixel sums: [0..2] dL/drgb, [3] sum of
+ * h = alpha dL/dalpha (0 where alpha sat at 0.99), [4..6] sum of dL/dk,
+ * [7..9] sum of (x - c_x) dL/dk, [10..12] sum of (y - c_y) dL/dk, for the
+ * expansion k = h_x x h_y = N01 + x N12 - y N02 (N01 = M0 x M1, N12 = M1 x M2,
+ * N02 = M0 x M2), [13..14] sum of h ((x, y) - c) over the pixels where the
+ * screen filter is the wider falloff, [15] zero.
+ * Ownership, errors, streams and accumulation as the 3D Gaussian calls.
+ * ------------------------------------------------------------------------ */
+#define GS_SURFEL_GRAD_STRIDE 16
+
+/* The projection of n surfels: the outputs of gs_preprocess with transforms
+ * in place of conic_opacity (culled surfels: zeros). */
+gs_status gs_surfel_preprocess(const gs_camera *cam, const gs_options *opt, int64_t n,
+                               const float *means, const float *scales, const float *quats,
+                               const float *opacities, const float *sh,
+                               float *means2d, float *depths, float *transforms, float *rgb,
+                               int32_t *radii, uint32_t *tiles_touched, uint8_t *clamped, void *stream);
+
+/* Per-pixel compositing of the binned surfels (lists from gs_bin_sort on the
+ * surfels' means2d, depths, radii, tiles_touched): image[3,H,W], final_T[H,W],
+ * n_contrib[H,W] as gs_render_fwd. */
+gs_status gs_surfel_render_fwd(const gs_camera *cam, const gs_options *opt, int64_t n,
+                               const uint32_t *ranges, const uint32_t *values, int64_t n_pairs,
+                               const float *transforms, const float *rgb,
+                               float *image, float *final_T, uint32_t *n_contrib, void *stream);
+
+/* The reverse blend's per-surfel pixel sums of ONE view, ADDED to
+ * grad[n, GS_SURFEL_GRAD_STRIDE] (the caller zeroes it per view). */
+gs_status gs_surfel_render_bwd_raster(const gs_camera *cam, const gs_options *opt, int64_t n,
+                                      const uint32_t *ranges, const uint32_t *values, int64_t n_pairs,
+                                      const float *transforms, const float *rgb, const float *final_T,
+                                      const uint32_t *n_contrib, const float *dL_dimage, float *grad,
+                                      void *stream);
+
+/* The chain rule from grad to the activated parameters: ACCUMULATED (+=)
+ * dL_dmeans[n,3], dL_dscales[n,2], dL_dquats[n,4], dL_dopacities[n],
+ * dL_dsh[n, sh_rows, 3] (rows < K), or WRITTEN with opt->overwrite_grads = 1. */
+gs_status gs_surfel_preprocess_bwd(const gs_camera *cam, const gs_options *opt, int64_t n,
+                                   const float *means, const float *scales, const float *quats,
+                                   const float *sh, const float *transforms, const int32_t *radii,
+                                   const uint8_t *clamped, const float *grad, float *dL_dmeans,
+                                   float *dL_dscales, float *dL_dquats, float *dL_dopacities,
+                                   float *dL_dsh, void *stream);
+
+/* Workspace bytes of gs_surfel_render_bwd for n surfels. */
+size_t gs_surfel_render_bwd_workspace_size(int64_t n);
+
+/* gs_surfel_render_bwd_raster into a zeroed workspace, then
+ * gs_surfel_preprocess_bwd. */
+gs_status gs_surfel_render_bwd(const gs_camera *cam, const gs_options *opt, int64_t n,
+                               const float *means, const float *scales, const float *quats,
+                               const float *sh, const float *transforms, const float *rgb,
+                               const int32_t *radii, const uint8_t *clamped,
+                               const uint32_t *ranges, const uint32_t *values, int64_t n_pairs,
+                               const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
+                               float *dL_dmeans, float *dL_dscales, float *dL_dquats,
+                               float *dL_dopacities, float *dL_dsh,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Several views per launch
  *

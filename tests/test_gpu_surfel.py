@@ -1,0 +1,210 @@
+"""Parity of the 2D Gaussian surfel path (gs_surfel_*) with the fp64 surfel
+oracle (S1-S10), through the C ABI: projection against the oracle, binning
+bit for bit on the GPU's own projection, every pixel through the
+branch-exploring matcher, the pixel sums and the parameter gradients stage by
+stage and end to end. Workloads: the seeded scenes with each Gaussian's first
+two scales as the surfel's (s_u, s_v)."""
+import numpy as np
+import pytest
+import torch
+
+from differentiable_gaussian_splat_amd import raster
+from differentiable_gaussian_splat_amd.scenes import make_scene, surfel_scales
+from oracle import oracle as O
+from tests.gpu_helpers import rel_l2, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# The surfel's alpha goes through the ray-plane intersection (u, v) = (k0, k1) / k2
+# with k = h_x x h_y formed in fp32 from the staged, tile-relative rows of M: a
+# relative error of a few 1e-7 in u and v becomes |u| |du| + |v| |dv| in rho and half
+# that in alpha. Near the 1/255 skip (rho ~ 11) that is up to about 1e-5 relative,
+# so the matcher's ambiguity window for surfels is 2e-5 (4e-6 for 3D Gaussians).
+SURFEL_D_ALPHA = 2e-5
+
+
+def surfel_grads(n, rows, dev):
+    z = lambda *s: torch.zeros(s, dtype=torch.float32, device=dev)
+    return dict(means=z(n, 3), scales=z(n, 2), quats=z(n, 4), opacities=z(n), sh=z(n, rows, 3))
+
+
+def run(sc, view=0):
+    dev = torch.device("cuda:0")
+    s2 = surfel_scales(sc)
+    pd = dict(means=to_dev(sc.means), scales=to_dev(s2), quats=to_dev(sc.quats), opacities=to_dev(sc.opacities),
+              sh=to_dev(sc.sh))
+    r = raster.Rasterizer(dev, want_keys=True)
+    fr = r.surfel_forward(sc.cameras[view], pd["means"], pd["scales"], pd["quats"], pd["opacities"], pd["sh"],
+                          sc.sh_degree)
+    torch.cuda.synchronize()
+    P = fr.n_pairs
+    tf = fr.conic_opacity.cpu().numpy().reshape(-1, 3, 4)
+    g = dict(means2d=fr.means2d.cpu().numpy().astype(np.float64), depth32=fr.depths.cpu().numpy(),
+             M=tf[:, :, :3].reshape(-1, 9).astype(np.float64), opac=tf[:, 0, 3].astype(np.float64),
+             cw=tf[:, 1:, 3].astype(np.float64), rgb=fr.rgb.cpu().numpy().astype(np.float64),
+             radii=fr.radii.cpu().numpy(), tiles=fr.tiles_touched.cpu().numpy().view(np.uint32),
+             clamped=fr.clamped.cpu().numpy(), values=fr.values[:P].cpu().numpy().view(np.uint32).copy(),
+             keys=fr.keys[:P].cpu().numpy().view(np.uint64).copy(),
+             ranges=fr.ranges.cpu().numpy().view(np.uint32).copy(), image=fr.image.cpu().numpy(),
+             final_T=fr.final_T.cpu().numpy(), n_contrib=fr.n_contrib.cpu().numpy().view(np.uint32), P=P, s2=s2)
+    return r, pd, fr, g
+
+
+def check_projection(sc, g, view=0):
+    cam = sc.cameras[view]
+    o = O.surfel_preprocess(sc.means, g["s2"], sc.quats, sc.opacities, sc.sh, cam, sc.sh_degree)
+    amb = o["margin"] < 1e-5
+    vis_g, vis_o = g["radii"] > 0, o["radii"] > 0
+    assert np.all((vis_g == vis_o) | amb)
+    same = vis_g & vis_o
+    assert same.sum() > 0
+    assert np.all((g["radii"] == o["radii"])[same & ~amb])
+    assert np.all((g["tiles"] == o["tiles"])[same & ~amb])
+    # M, c and depth are formed in double and rounded once: within an ulp or two of the oracle's
+    Mo = o["tf"][same]
+    rows = np.repeat(np.linalg.norm(Mo.reshape(-1, 3, 3), axis=2), 3, axis=1)  # each entry's row norm
+    scale = np.maximum(np.abs(Mo), 1e-9 * rows)
+    err_M = (np.abs(g["M"][same] - Mo) / scale).max()
+    err_c = (np.abs(g["means2d"][same] - o["means2d"][same]) / (np.abs(o["means2d"][same]) + 1.0)).max()
+    print(f"surfel projection: {same.sum()} drawn, max rel err M {err_M:.2e} c {err_c:.2e}")
+    assert err_M <= 2.5e-7 and err_c <= 2.5e-7
+    np.testing.assert_array_equal(g["cw"][same], g["means2d"][same])  # c also rides in the transforms
+    np.testing.assert_allclose(g["depth32"][same], o["depth"][same], rtol=1e-6)
+    np.testing.assert_array_less(np.abs(g["rgb"] - o["rgb"])[same], 1e-5 * (1 + np.abs(o["rgb"][same])))
+    np.testing.assert_array_equal(g["clamped"][same], (o["clamp"][same] * [1, 2, 4]).sum(1))
+    return o
+
+
+def check_frame(sc, r, pd, fr, g, view=0, end_to_end=True):
+    cam = sc.cameras[view]
+    W, H = cam.width, cam.height
+    check_projection(sc, g, view)
+    keys, values, ranges = O.bin_sort(g["means2d"], g["radii"], g["depth32"], W, H)
+    assert g["P"] == len(values)
+    np.testing.assert_array_equal(g["values"], values)
+    np.testing.assert_array_equal(g["keys"], keys)
+    np.testing.assert_array_equal(g["ranges"], ranges)
+    st = O.surfel_match_fwd(W, H, g["ranges"], g["values"], g["means2d"], g["M"], g["opac"], g["rgb"], g["image"],
+                            g["final_T"], g["n_contrib"], d_alpha=SURFEL_D_ALPHA)
+    print(f"surfel forward: {st.size} pixels, {(st == 1).sum()} on another branch, {(st == 2).sum()} masked")
+    if int((st == 3).sum()):
+        img, T, nc = O.surfel_render_fwd(W, H, g["ranges"], g["values"], g["means2d"], g["M"], g["opac"], g["rgb"])
+        bad = np.argwhere(st == 3)[:6]
+        detail = [(int(y), int(x), g["image"][:, y, x].tolist(), float(g["final_T"][y, x]), int(g["n_contrib"][y, x]),
+                   img[:, y, x].tolist(), float(T[y, x]), int(nc[y, x])) for y, x in bad]
+        raise AssertionError(f"{int((st == 3).sum())} pixels match no branch: (y, x, gpu rgb, T, n, oracle rgb, T, n) "
+                             f"{detail}")
+    assert int((st >= 1).sum()) <= max(4, 2e-3 * st.size)
+    # stage-wise backward: the pixel sums on the GPU's own projection and lists
+    dL = sc.dL_dimage[view]
+    gsum = torch.zeros((sc.n, raster.SURFEL_GRAD_STRIDE), dtype=torch.float32, device=pd["means"].device)
+    raster.gs_surfel_render_bwd_raster(fr.cam, fr.opt, sc.n, fr.ranges, fr.values, fr.n_pairs, fr.conic_opacity,
+                                       fr.rgb, fr.final_T, fr.n_contrib, to_dev(dL), gsum)
+    torch.cuda.synchronize()
+    gs_ = gsum.cpu().numpy().astype(np.float64)
+    og = O.surfel_render_bwd(W, H, sc.n, g["ranges"], g["values"], g["means2d"], g["M"], g["opac"], g["rgb"], dL)
+    assert np.all(gs_[:, 15] == 0)
+    # the record holds sum h = sum alpha dL/dalpha; the oracle's dL/do is sum G dL/dalpha = that / o
+    gs_[:, 3] = np.where(g["opac"] > 0, gs_[:, 3] / np.where(g["opac"] > 0, g["opac"], 1.0), 0.0)
+    # and sum h (pixel - c) over the filter's pixels; dL/dc = 2 that (rho2 = 2 |pixel - c|^2, dL/drho = -h/2)
+    gs_[:, 13:15] *= 2.0
+    # the record holds sum dL/dk, sum (x - c_x) dL/dk and sum (y - c_y) dL/dk for k = N01 + x N12 - y N02
+    # (N01 = M0 x M1, N12 = M1 x M2, N02 = M0 x M2): to dL/dN and back to dL/dM through the cross
+    # products, on the GPU's own M and c
+    M = g["M"].reshape(-1, 3, 3)
+    cxy = g["means2d"]
+    dN01 = gs_[:, 4:7]
+    dN12 = gs_[:, 7:10] + cxy[:, :1] * dN01
+    dN02 = -(gs_[:, 10:13] + cxy[:, 1:] * dN01)
+    dM0 = np.cross(M[:, 1], dN01) + np.cross(M[:, 2], dN02)
+    dM1 = np.cross(dN01, M[:, 0]) + np.cross(M[:, 2], dN12)
+    dM2 = np.cross(dN12, M[:, 1]) + np.cross(dN02, M[:, 0])
+    gs_[:, 4:13] = np.concatenate([dM0, dM1, dM2], axis=1)
+    for name, sl in (("drgb", slice(0, 3)), ("dL/do", slice(3, 4)), ("dM", slice(4, 13)), ("dc", slice(13, 15))):
+        e = rel_l2(gs_[:, sl], og[:, sl])
+        print(f"surfel pixel sums {name}: rel L2 {e:.2e}")
+        assert e <= 1e-3, (name, e)
+    # the whole backward through the C ABI against the oracle's chain rule on those sums
+    grads = surfel_grads(sc.n, sc.sh.shape[1], pd["means"].device)
+    r.surfel_backward(fr, pd["means"], pd["scales"], pd["quats"], pd["sh"], to_dev(dL), grads)
+    torch.cuda.synchronize()
+    gg = {k: v.cpu().numpy().astype(np.float64) for k, v in grads.items()}
+    ob = O.surfel_preprocess_bwd(sc.means, g["s2"], sc.quats, sc.opacities, sc.sh, cam, sc.sh_degree, og)
+    for k in ("means", "scales", "quats", "opacities", "sh"):
+        e = rel_l2(gg[k], ob[k])
+        print(f"surfel grad {k}: rel L2 {e:.2e}")
+        assert e <= 1e-3, (k, e)
+    if end_to_end:
+        # End to end from the raw parameters. The projection hands fp32 values (M, c, rgb) to the
+        # blending, and a surfel seen at a grazing angle turns their rounding into flipped skip and
+        # stop decisions (the oracle itself, run on its own projection rounded to fp32, moves by
+        # up to 1.4e-3 in dL/dmeans on the 40k-Gaussian contention scene). The bar is 1e-3, or
+        # 1.25 times that irreducible spread where it is larger.
+        p = dict(means=sc.means, scales=g["s2"], quats=sc.quats, opacities=sc.opacities, sh=sc.sh)
+        f = O.surfel_forward(p, cam, sc.sh_degree)
+        b = O.surfel_backward(p, cam, sc.sh_degree, f, dL)
+        pre = f["pre"]
+        r32 = lambda a: a.astype(np.float32).astype(np.float64)
+        k32, v32, rg32 = O.bin_sort(r32(pre["means2d"]), pre["radii"], pre["depth"].astype(np.float32), W, H)
+        s32 = O.surfel_render_bwd(W, H, sc.n, rg32, v32, r32(pre["means2d"]), r32(pre["tf"]),
+                                  sc.opacities.astype(np.float64), r32(pre["rgb"]), dL)
+        b32 = O.surfel_preprocess_bwd(sc.means, g["s2"], sc.quats, sc.opacities, sc.sh, cam, sc.sh_degree, s32)
+        for k in ("means", "scales", "quats", "opacities", "sh"):
+            e, floor = rel_l2(gg[k], b[k]), rel_l2(b32[k], b[k])
+            print(f"surfel end to end {k}: rel L2 {e:.2e} (oracle on its fp32-rounded projection: {floor:.2e})")
+            assert e <= max(1e-3, 1.25 * floor), ("end to end", k, e, floor)
+    return gg
+
+
+@pytest.mark.parametrize("config,seed,n", [(1, 0, None), (1, 1, None), (2, 0, 20_000), (3, 0, 40_000), (4, 0, 600)])
+def test_surfel_parity(config, seed, n):
+    sc = make_scene(config, seed, n=n)
+    r, pd, fr, g = run(sc)
+    check_frame(sc, r, pd, fr, g)
+
+
+def test_surfel_overwrite_and_accumulate():
+    """The chain rule on fixed pixel sums: with overwrite_grads it writes every
+    row (from NaN-filled buffers) and equals one adding call into zeros; a
+    second adding call doubles the result (to the rounding of its fused
+    multiply-adds). The whole backward in either mode agrees to the order of
+    its atomic adds."""
+    sc = make_scene(2, 1, n=5000)
+    r, pd, fr, g = run(sc)
+    dL = to_dev(sc.dL_dimage[0])
+    dev = pd["means"].device
+    gsum = torch.zeros((sc.n, raster.SURFEL_GRAD_STRIDE), dtype=torch.float32, device=dev)
+    raster.gs_surfel_render_bwd_raster(fr.cam, fr.opt, sc.n, fr.ranges, fr.values, fr.n_pairs, fr.conic_opacity,
+                                       fr.rgb, fr.final_T, fr.n_contrib, dL, gsum)
+    ow = raster.GsOptions.from_buffer_copy(fr.opt)
+    ow.overwrite_grads = 1
+
+    def chain(opt, grads):
+        raster.gs_surfel_preprocess_bwd(fr.cam, opt, pd["means"], pd["scales"], pd["quats"], pd["sh"],
+                                        fr.conic_opacity, fr.radii, fr.clamped, gsum, grads["means"],
+                                        grads["scales"], grads["quats"], grads["opacities"], grads["sh"])
+
+    add = surfel_grads(sc.n, 16, dev)
+    chain(fr.opt, add)
+    nan = {k: torch.full_like(v, float("nan")) for k, v in add.items()}
+    chain(ow, nan)
+    twice = {k: v.clone() for k, v in add.items()}
+    chain(fr.opt, twice)
+    full_w = {k: torch.full_like(v, float("nan")) for k, v in add.items()}
+    r.surfel_backward(fr, pd["means"], pd["scales"], pd["quats"], pd["sh"], dL, full_w, overwrite=True)
+    torch.cuda.synchronize()
+    for k in add:
+        a, w, t2, fw = (x[k].cpu().numpy() for x in (add, nan, twice, full_w))
+        assert np.isfinite(w).all() and np.isfinite(fw).all(), k
+        np.testing.assert_array_equal(w, a)
+        assert rel_l2(t2, 2 * a) <= 1e-6, k
+        assert rel_l2(fw, a) <= 1e-4, (k, rel_l2(fw, a))
+
+
+def test_surfel_full_frame_contention_scene():
+    """The 1M-Gaussian, 1080p workload as surfels, stage-wise in full (the
+    configuration the benchmark's surfel line times)."""
+    sc = make_scene(3, 0)
+    r, pd, fr, g = run(sc)
+    check_frame(sc, r, pd, fr, g, end_to_end=False)
+    print(f"surfels at 1080p: pairs {g['P']}, drawn {(g['radii'] > 0).sum()}")
