@@ -267,6 +267,7 @@ def main():
 
     batched = time_batched_views(args, raster, dev, sc, cams, opt, means, scales, quats, opac, sh, dLs, last_P,
                                  1000.0 * elapsed / args.steps) if len(views) > 1 else None
+    surfel = time_surfels(args, raster, scenes, dev, sc, cams, opt, opt_first, means, quats, opac, sh, dLs)
 
     # measured denominators: HBM streaming read, and no-return fp32 atomic adds
     # in the backward's flush pattern (9 lanes on one record, records hashed
@@ -429,6 +430,7 @@ def main():
 
     if batched is not None:
         result["batched_views"] = batched
+    result["surfels"] = surfel
     if args.cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sc, args, fr_state=dict(
             means2d=means2d.cpu().numpy(), conic=conic.cpu().numpy(), rgb=rgb.cpu().numpy(),
@@ -510,6 +512,86 @@ def time_batched_views(args, raster, dev, sc, cams, opt, means, scales, quats, o
             "pairs": P_box[0], "stages_ms_per_view": {s: round(float(t), 4) for s, t in zip(BATCH_STAGES, st)},
             "note": "all views in one launch per phase (gs_*_views): parameters read once, one binning pass over "
                     "the stacked tile grids, gradients summed per Gaussian before one write"}
+
+
+SURFEL_STAGES = ["surfel_preprocess", "bin_sort", "surfel_render_fwd", "zero_pixel_sums", "surfel_render_bwd_raster",
+                 "surfel_preprocess_bwd"]
+
+
+def time_surfels(args, raster, scenes, dev, sc, cams, opt, opt_first, means, quats, opac, sh, dLs):
+    """The same frame with 2D Gaussian surfels (each Gaussian's first two scales
+    as the surfel's), timed the same way: the gs_surfel_* calls with the same
+    binning; not part of value."""
+    import torch
+    n = sc.n
+    scales2 = torch.from_numpy(scenes.surfel_scales(sc)).to(dev)
+    W, H = cams[0].width, cams[0].height
+    ntiles = ((W + 15) // 16) * ((H + 15) // 16)
+    E = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+    means2d, depths, tf, rgb = E((n, 2), torch.float32), E(n, torch.float32), E((n, 12), torch.float32), \
+        E((n, 3), torch.float32)
+    radii, tiles, clamped = E(n, torch.int32), E(n, torch.int32), E(n, torch.uint8)
+    ranges = E((ntiles, 2), torch.int32)
+    image, final_T, n_contrib = E((3, H, W), torch.float32), E((H, W), torch.float32), E((H, W), torch.int32)
+    grad = E((n, raster.SURFEL_GRAD_STRIDE), torch.float32)
+    grads = dict(means=E((n, 3), torch.float32), scales=E((n, 2), torch.float32), quats=E((n, 4), torch.float32),
+                 opacities=E(n, torch.float32), sh=E(tuple(sh.shape), torch.float32))
+    stream = torch.cuda.current_stream()
+    P_box = [0]
+    cap = 0
+    for cam in cams:  # pair buffers of their own, sized for the surfels' footprints
+        raster.gs_surfel_preprocess(cam, opt, means, scales2, quats, opac, sh, means2d, depths, tf, rgb, radii, tiles,
+                                    clamped)
+        cap = max(cap, int(tiles.to(torch.int64).sum().item() * 1.02) + 4096)
+    values = E(cap, torch.int32)
+    bin_ws = E(raster.gs_bin_sort_workspace_size(n, cap, W, H), torch.uint8)
+
+    def step(evs):
+        for vi, cam in enumerate(cams):
+            ev = evs[vi] if evs else None
+            mark = (lambda k: ev[k].record(stream)) if ev else (lambda k: None)
+            mark(0)
+            raster.gs_surfel_preprocess(cam, opt, means, scales2, quats, opac, sh, means2d, depths, tf, rgb, radii,
+                                        tiles, clamped)
+            mark(1)
+            P = raster.gs_bin_sort(cam, opt, means2d, depths, radii, tiles, bin_ws, cap, None, values, ranges)
+            P_box[0] = P
+            mark(2)
+            raster.gs_surfel_render_fwd(cam, opt, n, ranges, values, P, tf, rgb, image, final_T, n_contrib)
+            mark(3)
+            grad.zero_()
+            mark(4)
+            raster.gs_surfel_render_bwd_raster(cam, opt, n, ranges, values, P, tf, rgb, final_T, n_contrib, dLs[vi],
+                                               grad)
+            mark(5)
+            raster.gs_surfel_preprocess_bwd(cam, opt_first if vi == 0 else opt, means, scales2, quats, sh, tf, radii,
+                                            clamped, grad, grads["means"], grads["scales"], grads["quats"],
+                                            grads["opacities"], grads["sh"])
+            mark(6)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(None)
+    torch.cuda.synchronize()
+    ms = 1000.0 * (time.perf_counter() - t0) / (args.steps * len(cams))
+    reps = min(args.steps, 5)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(SURFEL_STAGES) + 1)] for _ in cams]
+           for _ in range(reps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    st = [sum(ev[k].elapsed_time(ev[k + 1]) for e in evs for ev in e) / (reps * len(cams))
+          for k in range(len(SURFEL_STAGES))]
+    log(f"[bench] surfels: {ms:.3f} ms/frame; " + ", ".join(f"{a} {b:.3f}" for a, b in zip(SURFEL_STAGES, st)))
+    del values, bin_ws
+    return {"ms_per_frame": round(ms, 4), "pairs": int(P_box[0]), "visible": int((radii > 0).sum().item()),
+            "stages_ms": {a: round(float(b), 4) for a, b in zip(SURFEL_STAGES, st)},
+            "note": "2D Gaussian surfels on the same draws (a surfel's two scales are the Gaussian's first two): "
+                    "gs_surfel_preprocess, gs_bin_sort, gs_surfel_render_fwd, gs_surfel_render_bwd_raster, "
+                    "gs_surfel_preprocess_bwd; timed like the frame, not part of value"}
 
 
 def pmc_traffic(kernel, config):
