@@ -386,12 +386,12 @@ def main():
         },
         "blend_counts": {
             "E_f": E_f, "E_f_eval": E_f_eval, "E_blend": E_blend, "E_b": E_b_cnt, "P": int(last_P[-1]), "P_c": P_c,
-            "bwd_band_steps": band_exec, "bwd_lane_use": round(E_blend / max(64 * band_exec, 1), 4),
+            "bwd_strip_steps": band_exec, "bwd_lane_use": round(E_blend / max(64 * band_exec, 1), 4),
             "bwd_tile_entries_walked": walked_cnt,
             "note": "one view, the forward's own decisions: E_f entries evaluated per pixel up to its stop (E_f_eval "
                     "those passing the 16x4 band's bound), E_blend blended, E_b walked by the reverse pass, P_c "
-                    "(tile, entry) pairs with a blended pixel, bwd_band_steps (16x4 band, entry) pairs the backward "
-                    "executes, bwd_lane_use = E_blend / (64 bwd_band_steps)",
+                    "(tile, entry) pairs with a blended pixel, bwd_strip_steps (4x16 column strip, entry) pairs the backward "
+                    "executes, bwd_lane_use = E_blend / (64 bwd_strip_steps)",
         },
         "stage_rooflines": stage_roof,
         "naive_atomic_bwd": {

@@ -18,6 +18,8 @@
 // partials of a 64-record batch meet in LDS, and the batch is flushed with all
 // lanes active: one fp32 atomic add per value per (band, Gaussian), 9
 // consecutive lanes per Gaussian record.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -132,6 +134,37 @@ __device__ __forceinline__ uint32_t stage_record_bands(uint32_t g, uint32_t pos,
     for (int b = 0; b < PPL; ++b) {
         const float y0 = y_lo + 4.f * b;
         if (pos < band_last[b] && !mt.misses(m.x, m.y, x_lo, x_hi, y0, y0 + 3.f)) mask |= 1u << b;
+    }
+    return mask;
+}
+
+// The backward's staging: as stage_record, but returns a mask of the wave's PPL
+// column strips (strip s = columns [4 s, 4 s + 4) of the tile, all 16 rows;
+// the wave's k-th strip is s = strip0 + k) the record may reach; bit k is also
+// clear when the record lies at or past every blended entry of strip k
+// (pos >= strip_last[k]). Bit 4 is set when the record's opacity exceeds 0.99,
+// so that its alpha may sit at the clamp; below, alpha = o G never reaches it.
+template <int PPL>
+__device__ __forceinline__ uint32_t stage_record_strips(uint32_t g, uint32_t pos, const uint32_t* strip_last,
+                                                        const float2* __restrict__ means2d,
+                                                        const float4* __restrict__ conic_op,
+                                                        const float* __restrict__ rgb, Staged* s_rec, int lane,
+                                                        double ox, double oy, float x_lo, float y_lo, float y_hi,
+                                                        int strip0) {
+    const float2 m = means2d[g];
+    const float4 c = conic_op[g];
+    const float4 k = falloff_consts(c);
+    const double ddy = oy - (double)m.y;
+    const double w0 = (ox - (double)m.x) + (double)c.y * ddy;
+    s_rec[lane].a = make_float4((float)w0, (float)ddy, k.x, k.y);
+    s_rec[lane].b = make_float4(k.z, k.w, rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1]);
+    s_rec[lane].c.x = rgb[3 * (size_t)g + 2];
+    const MissTest mt(c, k.w);
+    uint32_t mask = c.w > ALPHA_MAX ? 16u : 0u;
+#pragma unroll
+    for (int b = 0; b < PPL; ++b) {
+        const float x0 = x_lo + 4.f * (float)(strip0 + b);
+        if (pos < strip_last[b] && !mt.misses(m.x, m.y, x0, x0 + 3.f, y_lo, y_hi)) mask |= 1u << b;
     }
     return mask;
 }
@@ -278,18 +311,25 @@ struct BwdShared {
     uint32_t has[NB];
 };
 
-// The backward of one wave: band `band` (of 4 / PPL) of tile `tile`. Of its
-// PPL row bands (16x4 pixels each, band k holding the lanes' k-th pixels),
-// only those set in band_sel are walked, and only list entries [walk_lo,
-// walk_hi). A row band whose pixels blend nothing at or past walk_hi starts
-// from the final state (T = final_T, colour behind = background); the others
-// start from the forward's checkpoint `ck` after entry walk_hi - 1 (T there,
-// and the colour behind it, (C_final - C there + final_T bg) / T), with
-// ck_end holding C_final. ck is null when walk_hi is past the walk.
+// The backward of one wave: strip group `band` (of 4 / PPL) of tile `tile`.
+// Lane l owns the pixels of tile row r = l / 4 at columns 4 s + l % 4 of its
+// PPL column strips s = band PPL + k (strip s: columns [4 s, 4 s + 4), all 16
+// rows), so a lane's pixels share one row: dy and its exponent term are
+// formed once per entry, and the moments with dy factor out of the pixel loop
+// (sum h w dy = dy sum h w, sum h dy^2 = dy^2 sum h, sum h dy = dy sum h).
+// Only the strips set in band_sel are walked, and only list entries
+// [walk_lo, walk_hi). A pixel whose row band (rows [4 b, 4 b + 4)) blends
+// nothing at or past walk_hi in the forward (rb_walk, the forward's walk of
+// each row band) starts from the final state (T = final_T, colour behind =
+// background); the others start from the forward's checkpoint `ck` after
+// entry walk_hi - 1 (T there, and the colour behind it,
+// (C_final - C there + final_T bg) / T), with ck_end holding C_final; a
+// checkpoint slot holds pixel (r, c) at float4 16 r + c. ck is null when
+// walk_hi is past the walk.
 template <int PPL, int NB, bool NAIVE>
 __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, int walk_lo, int walk_hi,
                                          const float4* __restrict__ ck, const float4* __restrict__ ck_end,
-                                         int W, int H, int TX, int TY,
+                                         uint4 rb_walk, int W, int H, int TX, int TY,
                                          const uint2* __restrict__ ranges, const uint32_t* __restrict__ values,
                                          const float2* __restrict__ means2d, const float4* __restrict__ conic_op,
                                          const float* __restrict__ rgb, float bg0, float bg1, float bg2,
@@ -313,17 +353,20 @@ __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, 
     const bool c3 = ((rl >> 2) & 1) != 0;
     const bool writer = rl < 9;
     const int slot = rl < 8 ? (c1 ? 4 : 0) + (c2 ? 2 : 0) + (c3 ? 1 : 0) : 8;
-    const int px = tx * TILE + (lane & 15);
-    const int py0 = ty * TILE + band * 4 * PPL + (lane >> 4);
+    const int r = lane >> 2, q = lane & 3;  // this lane's row in the tile, column within a strip
+    const int strip0 = band * PPL;
+    const int py = ty * TILE + r;
     const double ox = (double)(tx * TILE) + 0.5, oy = (double)(ty * TILE) + 0.5;  // the tile's first pixel centre
-    const float lx = (float)(lane & 15);                                         // this lane's offset from it
+    const float ly = (float)r;                                                   // this lane's row offset
     const size_t HW = (size_t)W * H;
-    float ly[PPL], T[PPL], g0[PPL], g1[PPL], g2[PPL], S[PPL];
-    uint32_t last[PPL], band_last[PPL];
+    const uint32_t rbw = (r >> 2) == 0 ? rb_walk.x : (r >> 2) == 1 ? rb_walk.y : (r >> 2) == 2 ? rb_walk.z : rb_walk.w;
+    float lx[PPL], T[PPL], g0[PPL], g1[PPL], g2[PPL], S[PPL];
+    uint32_t last[PPL], strip_last[PPL];
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
-        const int py = py0 + 4 * k;
-        ly[k] = (float)(py - ty * TILE);
+        const int col = 4 * (strip0 + k) + q;
+        const int px = tx * TILE + col;
+        lx[k] = (float)col;
         const bool in = px < W && py < H;
         const size_t p = in ? (size_t)py * W + px : 0;
         T[k] = in ? final_T[p] : 1.f;
@@ -332,10 +375,10 @@ __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, 
         g1[k] = in ? dL_dimage[HW + p] : 0.f;
         g2[k] = in ? dL_dimage[2 * HW + p] : 0.f;
         S[k] = fmaf(bg0, g0[k], fmaf(bg1, g1[k], bg2 * g2[k]));
-        band_last[k] = __builtin_amdgcn_readfirstlane(wave_max_u32(last[k]));  // deepest blended entry of band k
-        if (!((band_sel >> k) & 1u)) band_last[k] = 0u;  // no entry of row k is walked
-        if (ck && band_last[k] > (uint32_t)walk_hi) {   // row band k walked past walk_hi in the forward
-            const int lp = (band * PPL + k) * 64 + lane;  // the pixel's float4 in a checkpoint slot
+        strip_last[k] = __builtin_amdgcn_readfirstlane(wave_max_u32(last[k]));  // deepest blended entry of strip k
+        if (!((band_sel >> k) & 1u)) strip_last[k] = 0u;  // no entry of strip k is walked
+        if (ck && rbw > (uint32_t)walk_hi) {  // this pixel's row band walked past walk_hi in the forward
+            const int lp = 16 * r + col;      // the pixel's float4 in a checkpoint slot
             const float4 c = ck[lp], e = ck_end[lp];
             const float behind = fmaf(g0[k], e.x - c.y, fmaf(g1[k], e.y - c.z, g2[k] * (e.z - c.w)));
             S[k] = in ? fmaf(T[k], S[k], behind) / c.x : 0.f;
@@ -344,9 +387,9 @@ __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, 
     }
     uint32_t mylast = 0;
 #pragma unroll
-    for (int k = 0; k < PPL; ++k) mylast = max(mylast, band_last[k]);
-    const float bx_lo = (float)(tx * TILE) + 0.5f, bx_hi = bx_lo + 15.f;
-    const float by_lo = (float)(ty * TILE + band * 4 * PPL) + 0.5f;
+    for (int k = 0; k < PPL; ++k) mylast = max(mylast, strip_last[k]);
+    const float bx_lo = (float)(tx * TILE) + 0.5f;
+    const float by_lo = (float)(ty * TILE) + 0.5f;
     const uint2 rg = ranges[tile];
     // never walk past the tile's list, whatever n_contrib holds
     const uint32_t maxlast = min(min(mylast, rg.y - rg.x), (uint32_t)walk_hi);
@@ -354,66 +397,113 @@ __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, 
     for (int hi = (int)maxlast; hi > walk_lo; hi -= NB) {
         const int lo = max(walk_lo, hi - NB);
         const int cnt = hi - lo;
-        uint32_t bands = 0u;
+        uint32_t strips = 0u;
         if (lane < cnt) {
             const uint32_t g = values[rg.x + lo + lane];
-            bands = stage_record_bands<PPL>(g, (uint32_t)(lo + lane), band_last, means2d, conic_op, rgb, s_rec,
-                                            lane, ox, oy, bx_lo, bx_hi, by_lo);
+            strips = stage_record_strips<PPL>(g, (uint32_t)(lo + lane), strip_last, means2d, conic_op, rgb, s_rec,
+                                              lane, ox, oy, bx_lo, by_lo, by_lo + 15.f, strip0);
             s_g[lane] = g;
             s_has[lane] = 0u;
         }
-        uint64_t todo = __ballot(bands != 0u);  // records some row band may blend
+        uint64_t todo = __ballot((strips & 0xFu) != 0u);  // records some strip may blend
         __syncthreads();
         while (todo) {
             const int j = 63 - __builtin_clzll(todo);  // backwards through the list
             todo &= ~(1ull << j);
-            const uint32_t bm = __builtin_amdgcn_readlane(bands, j);  // row bands this record may reach
+            const uint32_t bm = __builtin_amdgcn_readlane(strips, j);  // strips this record may reach
             const float4 A = s_rec[j].a;
             const float4 B = s_rec[j].b;
             const float cb = s_rec[j].c.x;
             const uint32_t pos = (uint32_t)(lo + j);
-            const float wl = A.x + lx;  // w at this lane's column, tile's first row
+            // this lane's row: dy and the exponent's dy term, as falloff() forms them
+            const float dy = A.y + ly;
+            float et;
+            {
+#pragma clang fp contract(off)
+                const float gdy = B.x * dy;
+                et = __fmaf_rn(gdy, dy, B.y);
+            }
             float acc[GRAD2D_N];
 #pragma unroll
             for (int c = 0; c < GRAD2D_N; ++c) acc[c] = 0.f;
+            float Hs = 0.f, HW1 = 0.f, HW2 = 0.f;  // sums over this lane's pixels of h, h w, h w^2
             bool any = false, mine = false;
+            // the strips' pixel work, in two versions: a record whose opacity is at most 0.99 never
+            // reaches the alpha clamp (alpha = o G <= o), so it skips the clamp's min and test
+            auto strips_pass = [&](auto clamp_tag) {
+                constexpr bool CLAMP = decltype(clamp_tag)::value;
+                // one pixel's blend test (the forward's own arithmetic: falloff() on the same values)
+                auto eval = [&](int k, float& w, float& oG, float& al) {
+#pragma clang fp contract(off)
+                    w = __fmaf_rn(A.w, ly, A.x + lx[k]);
+                    const float aw = A.z * w;
+                    oG = __builtin_amdgcn_exp2f(__fmaf_rn(aw, w, et));
+                    al = CLAMP ? fminf(ALPHA_MAX, oG) : oG;
+                };
+                // one pixel's gradient terms; a pixel that did not blend this entry takes alpha = 0,
+                // which leaves its T, S and every sum unchanged
+                auto grad = [&](int k, float w, float oG, float al, bool blended) {
+                    const float av = blended ? al : 0.f;
+                    T[k] = T[k] * __builtin_amdgcn_rcpf(1.0f - av);  // T in front of this entry
+                    const float wt = av * T[k];
+                    acc[0] = fmaf(wt, g0[k], acc[0]);
+                    acc[1] = fmaf(wt, g1[k], acc[1]);
+                    acc[2] = fmaf(wt, g2[k], acc[2]);
+                    const float cdl = fmaf(B.z, g0[k], fmaf(B.w, g1[k], cb * g2[k]));
+                    const float d = cdl - S[k];
+                    S[k] = fmaf(av, d, S[k]);
+                    // h = o G dL/dalpha = -2 dL/dQ = alpha T d where alpha = o G; zero where alpha
+                    // sat at its 0.99 clamp (and wherever the pixel did not blend: wt = 0). The
+                    // moments stay in (w, dy), the conic's own axes: sums in (dx, dy) would
+                    // cancel for elongated Gaussians.
+                    const float h = (!CLAMP || oG <= ALPHA_MAX) ? wt * d : 0.f;
+                    const float hw = h * w;
+                    Hs += h;
+                    HW2 = fmaf(hw, w, HW2);
+                    HW1 += hw;
+                };
+                constexpr uint32_t FULL = (1u << PPL) - 1u;
+                if ((bm & FULL) == FULL) {
+                    // every strip may blend: the strips' chains are independent, so all their tests
+                    // go first and all their gradient terms after, without a branch between them
+                    // (a strip none of whose pixels blends adds zeros, exactly)
+                    float w[PPL], oG[PPL], al[PPL];
+                    bool bl[PPL], anyb = false;
 #pragma unroll
-            for (int k = 0; k < PPL; ++k) {
-                if (!((bm >> k) & 1u)) continue;  // no pixel of band k blends this entry
-                // did this pixel blend the entry (the forward's own test)
-                const float dy = A.y + ly[k];
-                const float w = __fmaf_rn(A.w, ly[k], wl);
-                const float oG = falloff(w, dy, A.z, B.x, B.y);
-                const float al = fminf(ALPHA_MAX, oG);
-                const bool blended = pos < last[k] && al >= ALPHA_MIN;
-                if (!__any(blended)) continue;
-                any = true;
-                mine = mine || blended;
-                // branch-free within the band: a pixel that did not blend this entry takes
-                // alpha = 0, which leaves its T, S and every sum unchanged
-                const float av = blended ? al : 0.f;
-                T[k] = T[k] * __builtin_amdgcn_rcpf(1.0f - av);  // T in front of this entry
-                const float wt = av * T[k];
-                acc[0] = fmaf(wt, g0[k], acc[0]);
-                acc[1] = fmaf(wt, g1[k], acc[1]);
-                acc[2] = fmaf(wt, g2[k], acc[2]);
-                const float cdl = fmaf(B.z, g0[k], fmaf(B.w, g1[k], cb * g2[k]));
-                const float d = cdl - S[k];
-                S[k] = fmaf(av, d, S[k]);
-                // h = o G dL/dalpha = -2 dL/dQ = alpha T d where alpha = o G; zero where alpha
-                // sat at its 0.99 clamp (and wherever the pixel did not blend: wt = 0). The
-                // moments stay in (w, dy), the conic's own axes: sums in (dx, dy) would
-                // cancel for elongated Gaussians.
-                const float h = oG <= ALPHA_MAX ? wt * d : 0.f;
-                const float hw = h * w, hy = h * dy;
-                acc[3] += h;
-                acc[4] = fmaf(hw, w, acc[4]);
-                acc[5] = fmaf(hw, dy, acc[5]);
-                acc[6] = fmaf(hy, dy, acc[6]);
-                acc[7] += hw;
-                acc[8] += hy;
-            }
+                    for (int k = 0; k < PPL; ++k) {
+                        eval(k, w[k], oG[k], al[k]);
+                        bl[k] = pos < last[k] && al[k] >= ALPHA_MIN;
+                        anyb = anyb || bl[k];
+                    }
+                    if (!__any(anyb)) return;
+                    any = true;
+                    mine = mine || anyb;
+#pragma unroll
+                    for (int k = 0; k < PPL; ++k) grad(k, w[k], oG[k], al[k], bl[k]);
+                    return;
+                }
+#pragma unroll
+                for (int k = 0; k < PPL; ++k) {
+                    if (!((bm >> k) & 1u)) continue;  // no pixel of strip k can blend this entry
+                    float w, oG, al;
+                    eval(k, w, oG, al);
+                    const bool blended = pos < last[k] && al >= ALPHA_MIN;
+                    if (!__any(blended)) continue;
+                    any = true;
+                    mine = mine || blended;
+                    grad(k, w, oG, al, blended);
+                }
+            };
+            if (bm & 16u) strips_pass(std::true_type{});
+            else strips_pass(std::false_type{});
             if (!any) continue;
+            const float hy = Hs * dy;
+            acc[3] = Hs;
+            acc[4] = HW2;
+            acc[5] = HW1 * dy;
+            acc[6] = hy * dy;
+            acc[7] = HW1;
+            acc[8] = hy;
             if (NAIVE) {
                 if (mine) {
                     float* dst = grad2d + (size_t)s_g[j] * GRAD2D_STRIDE;
@@ -432,7 +522,7 @@ __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, 
             if (lane == 0) s_has[j] = 1u;
         }
         __syncthreads();
-        // one atomic add per value per (band, Gaussian): the 4 row partials summed here
+        // one atomic add per value per (wave, Gaussian): the 4 row partials summed here
         for (int v = lane; v < cnt * GRAD2D_N; v += 64) {
             const int e = v / GRAD2D_N;
             const int c = v - e * GRAD2D_N;
@@ -459,7 +549,8 @@ __global__ __launch_bounds__(64) void k_render_bwd(int W, int H, int TX, int TY,
     constexpr int BANDS = 4 / PPL;
     __shared__ BwdShared<NB> sh;
     const int tile = blockIdx.x / BANDS, band = blockIdx.x - tile * BANDS;
-    bwd_walk<PPL, NB, NAIVE>(tile, band, 0xFu, 0, INT32_MAX, nullptr, nullptr, W, H, TX, TY, ranges, values,
+    bwd_walk<PPL, NB, NAIVE>(tile, band, 0xFu, 0, INT32_MAX, nullptr, nullptr, make_uint4(0u, 0u, 0u, 0u), W, H, TX,
+                             TY, ranges, values,
                              means2d, conic_op, rgb, bg0, bg1, bg2, final_T, n_contrib, dL_dimage, grad2d, lane_hist,
                              sh);
 }
@@ -507,7 +598,8 @@ __global__ __launch_bounds__(64) void k_render_bwd_split(int W, int H, int TX, i
     walk = min((uint32_t)__builtin_amdgcn_readfirstlane(wave_max_u32(walk)), rg.y - rg.x);
     const bool split = walk >= split_walk;
     if (!split && sub != 0) return;
-    bwd_walk<4, NB, false>(tile, 0, split ? 3u << (2 * sub) : 0xFu, 0, INT32_MAX, nullptr, nullptr, W, H, TX, TY,
+    bwd_walk<4, NB, false>(tile, 0, split ? 3u << (2 * sub) : 0xFu, 0, INT32_MAX, nullptr, nullptr,
+                           make_uint4(0u, 0u, 0u, 0u), W, H, TX, TY,
                            ranges, values, means2d, conic_op, rgb, bg0, bg1, bg2, final_T, n_contrib, dL_dimage,
                            grad2d, nullptr, sh);
 }
@@ -575,7 +667,7 @@ __global__ __launch_bounds__(64) void k_render_bwd_pieces(int W, int H, int TX, 
     const int lo = piece * CKPT_EVERY, hi = tail ? INT32_MAX : lo + CKPT_EVERY;
     const float4* tck = ckpt + (size_t)tile * PIECES * 256;
     bwd_walk<4, NB, false>(tile, 0, sel, lo, hi, tail ? nullptr : tck + (size_t)piece * 256, tck + CKPT_SLOTS * 256,
-                           W, H, TX, TY, ranges, values, means2d, conic_op, rgb, bg0, bg1, bg2, final_T, n_contrib,
+                           bw, W, H, TX, TY, ranges, values, means2d, conic_op, rgb, bg0, bg1, bg2, final_T, n_contrib,
                            dL_dimage, grad2d, nullptr, sh);
 }
 
@@ -590,8 +682,8 @@ __global__ __launch_bounds__(64) void k_render_bwd_pieces(int W, int H, int TX, 
 //   2 E_blend    blended (pixel, entry) pairs
 //   3 E_b        sum of n_contrib: entries each pixel's reverse walk passes
 //   4 P_c        (tile, entry) pairs with at least one blended pixel
-//   5 band_exec  (16x4 row band, entry) pairs with at least one blended pixel:
-//                what the backward executes, 64 lanes each
+//   5 band_exec  (4x16 column strip, entry) pairs with at least one blended
+//                pixel: what the backward executes, 64 lanes each
 //   6 walked     sum over tiles of the deepest n_contrib (the backward's walk)
 __global__ __launch_bounds__(64) void k_render_counts(int W, int H, int TX, int TY, int ntiles,
                                                      const uint2* __restrict__ ranges,
@@ -639,7 +731,7 @@ __global__ __launch_bounds__(64) void k_render_counts(int W, int H, int TX, int 
             const float4 B = s_rec[j].b;
             const uint32_t pos = bs - rg.x + 1 + (uint32_t)j;
             const float wl = A.x + lx;
-            bool any_tile = false;
+            bool mine = false;  // this lane blended the entry at one of its pixels
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 ef += L[k] != 0.f ? 1u : 0u;
@@ -655,12 +747,15 @@ __global__ __launch_bounds__(64) void k_render_counts(int W, int H, int TX, int 
                 const bool blended = ae > 0.f;
                 last[k] = blended ? pos : last[k];
                 eblend += blended ? 1u : 0u;
-                if (__any(blended)) {
-                    any_tile = true;
-                    ++bandx;
-                }
+                mine = mine || blended;
             }
-            if (any_tile) ++pc;
+            // the backward's column strips (columns [4 s, 4 s + 4): lanes with (lane & 15) / 4 = s)
+            const uint64_t who = __ballot(mine);
+            if (who) {
+                ++pc;
+#pragma unroll
+                for (int st = 0; st < 4; ++st) bandx += (who & (0x000F000F000F000Full << (4 * st))) ? 1u : 0u;
+            }
         }
         __syncthreads();
     }

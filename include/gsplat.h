@@ -537,9 +537,10 @@ gs_status gs_mb_render_bwd_naive(const gs_camera *cam, const gs_options *opt, in
  *       stops it, else its tile's whole list); [1] those the forward evaluates
  *       (passing its 16x4 row band's bound); [2] blended (pixel, entry) pairs;
  *   [3] E_b = sum of n_contrib; [4] P_c: (tile, entry) pairs with a blended
- *       pixel; [5] (row band, entry) pairs with a blended pixel (the
- *       backward's executed band-steps, 64 lanes each); [6] sum over tiles of
- *       the deepest n_contrib. Inputs as gs_render_fwd; nothing else written. */
+ *       pixel; [5] (4x16 column strip, entry) pairs with a blended pixel (the
+ *       backward's executed strip-steps, 64 lanes each); [6] sum over tiles
+ *       of the deepest n_contrib. Inputs as gs_render_fwd; nothing else
+ *       written. */
 gs_status gs_mb_render_counts(const gs_camera *cam, const gs_options *opt, const uint32_t *ranges,
                               const uint32_t *values, int64_t n_pairs, const float *means2d,
                               const float *conic_opacity, const float *rgb, uint64_t *counts, void *stream);

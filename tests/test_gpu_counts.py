@@ -17,7 +17,7 @@ T_MIN = float(np.float32(1e-4))
 
 
 def recount(W, H, ranges, values, means2d, conic, opac):
-    """E_f, E_blend, P_c and the (16x4 band, entry) pairs with a blended pixel,
+    """E_f, E_blend, P_c and the (4x16 column strip, entry) pairs with a blended pixel,
     walking each tile's list front to back in fp64 (the compositing rule as the
     oracle states it)."""
     TX, TY = (W + 15) // 16, (H + 15) // 16
@@ -37,7 +37,7 @@ def recount(W, H, ranges, values, means2d, conic, opac):
         Q = a * dx * dx + 2 * b * dx * dy + c * dy * dy
         al = np.minimum(A_MAX, opac[g] * np.exp(-0.5 * Q))
         T = np.ones(256)
-        band = ys.ravel() // 4
+        band = xs.ravel() // 4  # the backward's column strips
         for j in range(len(g)):
             if not active.any():
                 break
