@@ -889,6 +889,12 @@ __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int
 // super-tile's earlier pieces) live one per lane, lane lt for tile lt. Stores
 // check their slot against P: always true, it keeps a broken invariant from
 // writing out of bounds.
+//
+// A piece's tiles are shared by PLACE_SPLIT waves, each taking 64 / PLACE_SPLIT
+// of them (whole rows of the super-tile): the per-tile loop is the kernel's
+// serial part, and a piece of large Gaussians visits all 64 tiles.
+constexpr int PLACE_SPLIT = 4;
+
 template <bool KEYS>
 __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int S, int SX, int TX, int TY,
                                                  const uint32_t* __restrict__ pfirst, const uint2* __restrict__ sr,
@@ -897,7 +903,8 @@ __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int S, int
                                                  uint32_t P, uint32_t* __restrict__ values, u64* __restrict__ keys64) {
     __shared__ uint2 s_stage[SB / 64][PIECE];  // per wave: (Gaussian, depth bits) of one tile's run
     const int lane = threadIdx.x & 63;
-    const int pidx = __builtin_amdgcn_readfirstlane(blockIdx.x * (SB / 64) + (int)(threadIdx.x >> 6));
+    const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * (SB / 64) + (int)(threadIdx.x >> 6));
+    const int pidx = wid / PLACE_SPLIT, part = wid - pidx * PLACE_SPLIT;
     if (pidx >= (int)*np_ptr) return;
     uint2* stage = s_stage[threadIdx.x >> 6];
     int s, e0, e1;
@@ -909,7 +916,8 @@ __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int S, int
     const uint64_t lt_mask = lanemask_lt();
     PieceTiles pt;
     pt.load(e0, e1, sx0, sy0, vw, vh, sval, rec);
-    uint64_t todo = pt.any;
+    constexpr int TPW = 64 / PLACE_SPLIT;  // tiles per wave
+    uint64_t todo = pt.any & (((TPW == 64) ? ~0ull : ((1ull << TPW) - 1ull)) << (TPW * part));
     while (todo) {
         const int l = __builtin_ctzll(todo);
         todo &= todo - 1ull;
@@ -1136,11 +1144,11 @@ hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const
              s);
     if (e != hipSuccess) return e;
     if (keys)
-        k_tile_place<true><<<(max_pieces + wpb - 1) / wpb, SB, 0, s>>>(
+        k_tile_place<true><<<(PLACE_SPLIT * max_pieces + wpb - 1) / wpb, SB, 0, s>>>(
             &counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur], rec, counts,
             reinterpret_cast<const uint2*>(ranges), (uint32_t)P, values, reinterpret_cast<u64*>(keys));
     else
-        k_tile_place<false><<<(max_pieces + wpb - 1) / wpb, SB, 0, s>>>(
+        k_tile_place<false><<<(PLACE_SPLIT * max_pieces + wpb - 1) / wpb, SB, 0, s>>>(
             &counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur], rec, counts,
             reinterpret_cast<const uint2*>(ranges), (uint32_t)P, values, nullptr);
     return hipGetLastError();
