@@ -85,18 +85,10 @@ struct LoadPlain {
     const uint32_t* p;
     __device__ uint32_t operator()(int i) const { return p[i]; }
 };
-struct LoadVisible {
-    const uint32_t* tiles;
-    __device__ uint32_t operator()(int i) const { return tiles[i] > 0u ? 1u : 0u; }
-};
 struct StoreInPlace {
     uint32_t* p;
     __device__ void operator()(int i, u64 pos, uint32_t) const { p[i] = (uint32_t)pos; }
 };
-// Visible Gaussian i, the pos-th in index order: its depth bits and compact
-// position (the depth sort's keys and values) and its record (index, tile
-// rectangle X0 | X1 << 16, Y0 | Y1 << 16, depth bits), read here in index
-// order so that the sorted order later gathers one 16-byte record each.
 // Tile rectangle of entry i in the stacked grid of the views (nper entries
 // and TYv tile rows per view; nper = 0 for a single view).
 __device__ __forceinline__ void stacked_rect(int i, int nper, int TX, int TYv, float2 m, int r, int& X0, int& X1,
@@ -107,27 +99,6 @@ __device__ __forceinline__ void stacked_rect(int i, int nper, int TX, int TYv, f
     Y1 += yo;
 }
 
-struct StoreCompact {
-    const float* depths;
-    const float2* means2d;
-    const int* radii;
-    int nper, TX, TYv;
-    uint32_t* keys;
-    uint32_t* idx;
-    uint4* crec;
-    __device__ void operator()(int i, u64 pos, uint32_t flag) const {
-        if (flag) {
-            const uint32_t d = __float_as_uint(depths[i]);
-            const float2 m = means2d[i];
-            int X0, X1, Y0, Y1;
-            stacked_rect(i, nper, TX, TYv, m, radii[i], X0, X1, Y0, Y1);
-            keys[pos] = d;
-            idx[pos] = (uint32_t)pos;
-            crec[pos] = make_uint4((uint32_t)i, (uint32_t)X0 | ((uint32_t)X1 << 16),
-                                   (uint32_t)Y0 | ((uint32_t)Y1 << 16), d);
-        }
-    }
-};
 struct StoreRanges {
     uint2* ranges;
     __device__ void operator()(int t, u64 pos, uint32_t cnt) const {
@@ -456,7 +427,6 @@ __global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem src, int n, const u
     const uint32_t mask = (1u << bits) - 1u;
     for (int k = lane; k < 256; k += 64) s_wcnt[w][k] = 0u;
     wave_lds_sync();
-    if (tid < 256) s_gbase[tid] = offsets[(size_t)blockIdx.x * 256 + tid];
     uint32_t kk[RR], vv[RR], rk[RR];
     const int ebase = p0 + w * RR * 64 + lane;
 #pragma unroll
@@ -469,6 +439,7 @@ __global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem src, int n, const u
             vv[r] = src.vals[p];
         }
     }
+    if (tid < 256) s_gbase[tid] = offsets[(size_t)blockIdx.x * 256 + tid];  // read after the last barrier below
     const uint64_t lt = lanemask_lt();
 #pragma unroll
     for (int r = 0; r < RR; ++r) {
@@ -557,7 +528,7 @@ __device__ __forceinline__ uint32_t super_count(int X0, int X1, int Y0, int Y1) 
 // P = sum of tiles_touched, P1 = number of (super-tile, Gaussian) entries and
 // the number of visible Gaussians, per block of ST Gaussians (index order),
 // into part[3 b .. 3 b + 2]; k_pair_sum then totals P and P1 and scans the
-// visible counts, so that the compaction (k_scan_down with LoadVisible) runs
+// visible counts, so that the compaction (k_compact_visible) runs
 // straight after it.
 __global__ __launch_bounds__(SB) void k_pair_totals(int n, const uint32_t* __restrict__ tiles,
                                                   const float2* __restrict__ means2d, const int* __restrict__ radii,
@@ -565,19 +536,23 @@ __global__ __launch_bounds__(SB) void k_pair_totals(int n, const uint32_t* __res
     __shared__ u64 s_w[3][SB / 64];
     u64 p = 0, p1 = 0, v = 0;
     const int base = blockIdx.x * ST;
+    // every load issued before any is used (at a clamped index past n, not counted)
     uint32_t t[SI];
+    float2 m[SI];
+    int rr[SI];
 #pragma unroll
     for (int j = 0; j < SI; ++j) {
-        const int i = base + j * SB + threadIdx.x;
-        t[j] = i < n ? tiles[i] : 0u;
+        const int i = min(base + j * SB + (int)threadIdx.x, n - 1);
+        t[j] = tiles[i];
+        m[j] = means2d[i];
+        rr[j] = radii[i];
     }
 #pragma unroll
     for (int j = 0; j < SI; ++j) {
-        if (t[j]) {
-            const int i = base + j * SB + threadIdx.x;
-            const float2 m = means2d[i];
+        const int i = base + j * SB + threadIdx.x;
+        if (i < n && t[j]) {
             int X0, X1, Y0, Y1;
-            stacked_rect(i, nper, TX, TYv, m, radii[i], X0, X1, Y0, Y1);
+            stacked_rect(i, nper, TX, TYv, m[j], rr[j], X0, X1, Y0, Y1);
             p += t[j];
             p1 += super_count(X0, X1, Y0, Y1);
             v += 1;
@@ -663,6 +638,70 @@ __global__ __launch_bounds__(1024) void k_pair_sum(int nb, const u64* __restrict
     }
 }
 
+// Stable compaction of the visible Gaussians (tiles_touched > 0), in the
+// blocks of ST Gaussians that k_pair_totals counted (vis_scan[b]: visible
+// ones before block b). Visible Gaussian i, the pos-th in index order, gets
+// its depth bits and compact position (the depth sort's keys and values) and
+// its record (index, tile rectangle X0 | X1 << 16, Y0 | Y1 << 16, depth
+// bits), written here in index order so that the sorted order later gathers
+// one 16-byte record each. Thread t takes Gaussians base + j SB + t, all
+// loads issued up front; ranks come from one ballot per wave and row j and a
+// scan of the block's 4 SI wave counts (index order is row, wave, lane).
+__global__ __launch_bounds__(SB) void k_compact_visible(int n, int nper, int TX, int TYv,
+                                                      const uint32_t* __restrict__ tiles,
+                                                      const float* __restrict__ depths,
+                                                      const float2* __restrict__ means2d,
+                                                      const int* __restrict__ radii,
+                                                      const u64* __restrict__ vis_scan, uint32_t* __restrict__ keys,
+                                                      uint32_t* __restrict__ idx, uint4* __restrict__ crec) {
+    static_assert(SI * (SB / 64) == 64, "one lane per (row, wave) count");
+    __shared__ uint32_t s_c[SI * (SB / 64)];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int base = blockIdx.x * ST;
+    uint32_t t[SI], d[SI];
+    float2 m[SI];
+    int rr[SI];
+#pragma unroll
+    for (int j = 0; j < SI; ++j) {
+        const int i = min(base + j * SB + (int)threadIdx.x, n - 1);  // past n: loaded, never stored
+        t[j] = tiles[i];
+        d[j] = __float_as_uint(depths[i]);
+        m[j] = means2d[i];
+        rr[j] = radii[i];
+    }
+    uint64_t vis[SI];
+#pragma unroll
+    for (int j = 0; j < SI; ++j) {
+        vis[j] = __ballot(base + j * SB + (int)threadIdx.x < n && t[j] > 0u);
+        if (lane == 0) s_c[j * (SB / 64) + w] = (uint32_t)__popcll(vis[j]);
+    }
+    __syncthreads();
+    // lane k = (row, wave) in index order: exclusive scan of the counts
+    const uint32_t c = s_c[lane];
+    uint32_t x = c;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)x, off);
+        if (lane >= off) x += y;
+    }
+    const uint32_t excl = x - c;
+    const u64 boff = vis_scan[blockIdx.x];
+#pragma unroll
+    for (int j = 0; j < SI; ++j) {
+        const uint32_t first = (uint32_t)__builtin_amdgcn_readlane((int)excl, j * (SB / 64) + w);
+        if ((vis[j] >> lane) & 1ull) {
+            const uint32_t pos = (uint32_t)boff + first +
+                                 __builtin_amdgcn_mbcnt_hi((uint32_t)(vis[j] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)vis[j], 0u));
+            const int i = base + j * SB + threadIdx.x;
+            int X0, X1, Y0, Y1;
+            stacked_rect(i, nper, TX, TYv, m[j], rr[j], X0, X1, Y0, Y1);
+            keys[pos] = d[j];
+            idx[pos] = pos;
+            crec[pos] = make_uint4((uint32_t)i, (uint32_t)X0 | ((uint32_t)X1 << 16), (uint32_t)Y0 | ((uint32_t)Y1 << 16),
+                                   d[j]);
+        }
+    }
+}
+
 // Per depth-sorted Gaussian i (one gather of its compact record): its record
 // (index, X0 | X1 << 16, Y0 | Y1 << 16, depth bits) and its super-tile count
 // n1[i]; per block of ST Gaussians, the sum of the counts (the reduce step of
@@ -673,18 +712,24 @@ __global__ __launch_bounds__(SB) void k_sorted_records(const u64* vis_ptr, const
     __shared__ u64 s_w[SB / 64];
     const int cnt = (int)*vis_ptr;
     const int base = blockIdx.x * ST;
+    if (base >= cnt) {  // no Gaussian here: a zero partial, as the scan expects one per block
+        if (threadIdx.x == 0) partials[blockIdx.x] = 0ull;
+        return;
+    }
+    // every gather issued before any is used (at a clamped index past cnt, not stored)
     uint32_t o[SI];
 #pragma unroll
-    for (int j = 0; j < SI; ++j) {
-        const int i = base + j * SB + threadIdx.x;
-        o[j] = i < cnt ? order[i] : 0u;
-    }
+    for (int j = 0; j < SI; ++j) o[j] = order[min(base + j * SB + (int)threadIdx.x, cnt - 1)];
+    __builtin_amdgcn_sched_barrier(0);  // all index loads in flight before the first gather waits on one
+    uint4 rr[SI];
+#pragma unroll
+    for (int j = 0; j < SI; ++j) rr[j] = crec[o[j]];
     u64 sum = 0;
 #pragma unroll
     for (int j = 0; j < SI; ++j) {
         const int i = base + j * SB + threadIdx.x;
         if (i < cnt) {
-            const uint4 r = crec[o[j]];
+            const uint4 r = rr[j];
             rec[i] = r;
             const uint32_t c = super_count((int)(r.y & 0xffffu), (int)(r.y >> 16), (int)(r.z & 0xffffu),
                                            (int)(r.z >> 16));
@@ -706,9 +751,10 @@ __global__ __launch_bounds__(SB) void k_super_emit(const u64* vis_ptr, const uin
     const int k = blockIdx.x * SB + threadIdx.x;
     if (k >= (int)*vis_ptr) return;
     const uint4 r = rec[k];
+    uint32_t pos = first[k];
+    asm volatile("" ::"v"(pos), "v"(r.y), "v"(r.z));  // both loads issued before either is waited on
     const int sx0 = (int)(r.y & 0xffffu) >> 3, sx1 = (int)(r.y >> 16) >> 3;
     const int sy0 = (int)(r.z & 0xffffu) >> 3, sy1 = (int)(r.z >> 16) >> 3;
-    uint32_t pos = first[k];
     for (int sy = sy0; sy <= sy1; ++sy)
         for (int sx = sx0; sx <= sx1; ++sx, ++pos)
             if (pos < P1) {
@@ -766,54 +812,19 @@ __device__ __forceinline__ uint64_t entry_tiles(uint4 r, bool valid, int sx0, in
 
 constexpr int PIECE_GROUPS = PIECE / 64;
 
-// A piece's records (at most PIECE_GROUPS groups of 64), all loaded up front,
-// their tile masks, and the OR of the masks over the piece.
-struct PieceTiles {
-    uint4 rq[PIECE_GROUPS];
-    uint32_t mlo[PIECE_GROUPS], mhi[PIECE_GROUPS];
-    uint64_t any;
-    int ng;
-    __device__ __forceinline__ void load(int e0, int e1, int sx0, int sy0, int vw, int vh,
-                                         const uint32_t* __restrict__ sval, const uint4* __restrict__ rec) {
-        const int lane = threadIdx.x & 63;
-        ng = (e1 - e0 + 63) / 64;
-        uint32_t gi[PIECE_GROUPS];
-#pragma unroll
-        for (int q = 0; q < PIECE_GROUPS; ++q) gi[q] = sval[min(e0 + 64 * q + lane, e1 - 1)];  // lanes past e1 repeat
-#pragma unroll
-        for (int q = 0; q < PIECE_GROUPS; ++q) rq[q] = rec[gi[q]];  // an entry; masked out below
-        uint32_t ulo = 0u, uhi = 0u;
-#pragma unroll
-        for (int q = 0; q < PIECE_GROUPS; ++q) {
-            const uint64_t mask = entry_tiles(rq[q], e0 + 64 * q + lane < e1, sx0, sy0, vw, vh);
-            mlo[q] = (uint32_t)mask;
-            mhi[q] = (uint32_t)(mask >> 32);
-            ulo |= mlo[q];
-            uhi |= mhi[q];
-        }
-        for (int off = 1; off < 64; off <<= 1) {
-            ulo |= (uint32_t)__shfl_xor((int)ulo, off);
-            uhi |= (uint32_t)__shfl_xor((int)uhi, off);
-        }
-        any = ((uint64_t)__builtin_amdgcn_readfirstlane(uhi) << 32) | __builtin_amdgcn_readfirstlane(ulo);
-    }
-    __device__ __forceinline__ bool holds(int q, int l) const {
-        return (((l < 32 ? mlo[q] : mhi[q]) >> (l & 31)) & 1u) != 0u;
-    }
-};
-
 // One wave per piece: for each tile lt of the super-tile (lane lt), the number
 // of the piece's entries whose rectangle holds it, to counts[pidx][lt]. An
 // entry's tiles inside the super-tile form a rectangle, so the counts are a
 // 2D prefix sum of a (SUPER + 1)^2 difference array: each entry adds +1 / -1
 // at its rectangle's four corners (LDS integer atomics, exact), then a row
-// pass and a column pass of running sums give every tile's count.
+// pass and a column pass of running sums give every tile's count. The
+// piece's super-tile and entry range go to pinfo for the placement.
 constexpr int DGRID = SUPER + 1;
 
 __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int SX, int TX, int TY,
                                                  const uint32_t* __restrict__ pfirst, const uint2* __restrict__ sr,
                                                  const uint32_t* __restrict__ sval, const uint4* __restrict__ rec,
-                                                 uint32_t* __restrict__ counts) {
+                                                 uint32_t* __restrict__ counts, uint4* __restrict__ pinfo) {
     __shared__ int s_diff[SB / 64][DGRID * DGRID];
     const int lane = threadIdx.x & 63;
     const int pidx = __builtin_amdgcn_readfirstlane(blockIdx.x * (SB / 64) + (int)(threadIdx.x >> 6));
@@ -822,6 +833,7 @@ __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int
     for (int k = lane; k < DGRID * DGRID; k += 64) d[k] = 0;
     int s, e0, e1;
     piece_of(pidx, S, pfirst, sr, s, e0, e1);
+    if (lane == 0) pinfo[pidx] = make_uint4((uint32_t)s, (uint32_t)e0, (uint32_t)e1, 0u);  // for the placement
     const int sx0 = (s % SX) * SUPER, sy0 = (s / SX) * SUPER;
     const int vw = min(SUPER, TX - sx0), vh = min(SUPER, TY - sy0);  // the super-tile's tiles inside the grid
     uint32_t gi[PIECE_GROUPS];
@@ -876,70 +888,123 @@ __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int
 }
 
 // Placement, with the roles turned: lane = entry of a 64-entry group of the
-// piece (a piece holds at most four groups, whose records are all loaded
-// before the first store), and a uniform loop over the super-tile's tiles
-// that some entry of the piece holds. Each lane holds its entry's tiles as a
-// 64-bit mask per group (bit 8 row + column inside the super-tile); the OR of
-// the masks lists the tiles to visit. For tile lt, one ballot per group gives
-// the group's entries that hold it; in depth order (group, then lane) they
-// are packed into an LDS staging run, which the wave then writes to the
-// tile's slots with every lane busy: a store instruction costs the address
-// unit about the same whatever its active lanes, so full ones are the cheap
-// ones. The cursors (the tile's first slot plus the counts of the
-// super-tile's earlier pieces) live one per lane, lane lt for tile lt. Stores
-// check their slot against P: always true, it keeps a broken invariant from
-// writing out of bounds.
-//
-// A piece's tiles are shared by PLACE_SPLIT waves, each taking 64 / PLACE_SPLIT
-// of them (whole rows of the super-tile): the per-tile loop is the kernel's
-// serial part, and a piece of large Gaussians visits all 64 tiles.
+// piece (a piece holds at most four groups), and a uniform loop over the
+// super-tile's tiles that some entry of the piece holds. One block of four
+// waves takes a piece: wave q loads group q's records and tile masks (bit
+// 8 row + column inside the super-tile) into LDS, and after one barrier every
+// wave holds all groups' masks, but only the 32-bit half with its own two rows
+// of tiles (wave w: tiles 16 w .. 16 w + 15), since the per-tile loop is the
+// kernel's serial part and a piece of large Gaussians visits all 64 tiles.
+// For tile l, one compare per group gives the group's entries that hold it;
+// their ranks (mbcnt, with the run's length so far folded in) pack them in
+// depth order (group, then lane) into an LDS staging run, which the wave then
+// writes to the tile's slots with every lane busy: a store instruction costs
+// the address unit about the same whatever its active lanes, so full ones are
+// the cheap ones. The cursors (the tile's first slot plus the counts of the
+// super-tile's earlier pieces) live one per lane, lane l for tile l. A run
+// whose slots would pass P (only with a broken invariant) is written with a
+// check per slot instead.
 constexpr int PLACE_SPLIT = 4;
+static_assert(SB / 64 == PLACE_SPLIT && PIECE / 64 == PLACE_SPLIT, "one wave per group and per two tile rows");
 
 template <bool KEYS>
-__global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int S, int SX, int TX, int TY,
-                                                 const uint32_t* __restrict__ pfirst, const uint2* __restrict__ sr,
+__global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int SX, int TX, int TY,
+                                                 const uint4* __restrict__ pinfo,
                                                  const uint32_t* __restrict__ sval, const uint4* __restrict__ rec,
                                                  const uint32_t* __restrict__ offs, const uint2* __restrict__ ranges,
                                                  uint32_t P, uint32_t* __restrict__ values, u64* __restrict__ keys64) {
-    __shared__ uint2 s_stage[SB / 64][PIECE];  // per wave: (Gaussian, depth bits) of one tile's run
+    __shared__ uint2 s_stage[SB / 64][PIECE];   // per wave: (Gaussian, depth bits) of one tile's run
+    __shared__ uint4 s_grp[PIECE_GROUPS][64];   // per group and lane: mask lo, mask hi, Gaussian, depth bits
+    __shared__ uint2 s_any[PIECE_GROUPS];       // per group: OR of its masks
     const int lane = threadIdx.x & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * (SB / 64) + (int)(threadIdx.x >> 6));
-    const int pidx = wid / PLACE_SPLIT, part = wid - pidx * PLACE_SPLIT;
-    if (pidx >= (int)*np_ptr) return;
-    uint2* stage = s_stage[threadIdx.x >> 6];
-    int s, e0, e1;
-    piece_of(pidx, S, pfirst, sr, s, e0, e1);
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    // Workgroups go to the 8 XCDs round-robin (b -> XCD b % 8); XCD x takes
+    // the x-th eighth of the pieces in order, so that consecutive pieces of a
+    // super-tile, whose runs meet inside cache lines, are written through the
+    // same L2 and leave it as whole lines.
+    const int np = (int)*np_ptr;
+    const int chunk = (np + 7) >> 3;
+    const int i = (int)(blockIdx.x >> 3);
+    const int pidx = (int)(blockIdx.x & 7u) * chunk + i;
+    if (i >= chunk || pidx >= np) return;  // the whole block: the barrier below is reached by all waves or none
+    uint2* stage = s_stage[w];
+    const uint4 pi = pinfo[pidx];  // written by k_tile_count
+    const int s = (int)pi.x, e0 = (int)pi.y, e1 = (int)pi.z;
     const int sx0 = (s % SX) * SUPER, sy0 = (s / SX) * SUPER;
     const int vw = min(SUPER, TX - sx0), vh = min(SUPER, TY - sy0);  // the super-tile's tiles inside the grid
+    const int ng = (e1 - e0 + 63) / 64;
+    {
+        uint4 g = make_uint4(0u, 0u, 0u, 0u);
+        if (w < ng) {
+            const int e = e0 + 64 * w + lane;
+            const uint4 r = rec[sval[min(e, e1 - 1)]];  // lanes past e1 repeat an entry; masked out below
+            const uint64_t m = entry_tiles(r, e < e1, sx0, sy0, vw, vh);
+            g = make_uint4((uint32_t)m, (uint32_t)(m >> 32), r.x, r.w);
+        }
+        s_grp[w][lane] = g;
+        uint32_t olo = g.x, ohi = g.y;
+        for (int off = 1; off < 64; off <<= 1) {
+            olo |= (uint32_t)__shfl_xor((int)olo, off);
+            ohi |= (uint32_t)__shfl_xor((int)ohi, off);
+        }
+        if (lane == 0) s_any[w] = make_uint2(olo, ohi);
+    }
     const int mtx = sx0 + (lane & 7), mty = sy0 + (lane >> 3);
     uint32_t cur = (mtx < TX && mty < TY) ? ranges[mty * TX + mtx].x + offs[(size_t)pidx * 64 + lane] : 0u;
-    const uint64_t lt_mask = lanemask_lt();
-    PieceTiles pt;
-    pt.load(e0, e1, sx0, sy0, vw, vh, sval, rec);
-    constexpr int TPW = 64 / PLACE_SPLIT;  // tiles per wave
-    uint64_t todo = pt.any & (((TPW == 64) ? ~0ull : ((1ull << TPW) - 1ull)) << (TPW * part));
+    __syncthreads();
+    // this wave's half of every group's masks: bits sh .. sh + 15 of word w / 2
+    const int sh = 16 * (w & 1);
+    uint32_t mw[PIECE_GROUPS], gany[PIECE_GROUPS];
+    uint2 pv[PIECE_GROUPS];
+    uint32_t any = 0u;
+#pragma unroll
+    for (int q = 0; q < PIECE_GROUPS; ++q) {
+        const uint4 g = s_grp[q][lane];
+        const uint2 a = s_any[q];
+        mw[q] = w < 2 ? g.x : g.y;
+        pv[q] = make_uint2(g.z, g.w);
+        gany[q] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(((w < 2 ? a.x : a.y) >> sh) & 0xffffu)) << sh;
+        any |= gany[q];
+    }
+    uint32_t todo = any;
     while (todo) {
-        const int l = __builtin_ctzll(todo);
-        todo &= todo - 1ull;
+        const int b = __builtin_ctz(todo);
+        todo &= todo - 1u;
+        const uint32_t bit = 1u << b;
+        const int l = 32 * (w >> 1) + b;  // the tile inside the super-tile
         // pack the piece's entries holding tile l, in depth order, into the staging run
         uint32_t cnt = 0;
 #pragma unroll
         for (int q = 0; q < PIECE_GROUPS; ++q) {
-            if (q >= pt.ng) break;
-            const bool in = pt.holds(q, l);
+            if (!(gany[q] & bit)) continue;  // no entry of group q holds it (also: group q absent)
+            const bool in = (mw[q] & bit) != 0u;
             const uint64_t m = __ballot(in);
-            if (in) stage[cnt + (uint32_t)__popcll(m & lt_mask)] = make_uint2(pt.rq[q].x, pt.rq[q].w);
+            const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, cnt));
+            if (in) stage[at] = pv[q];
             cnt += (uint32_t)__popcll(m);
         }
         wave_lds_sync();
         const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)cur, l);
-        const uint32_t tile = (uint32_t)((sy0 + (l >> 3)) * TX + sx0 + (l & 7));
-        for (uint32_t k = (uint32_t)lane; k < cnt; k += 64) {
-            const uint2 e = stage[k];
-            const uint32_t pos = base + k;
-            if (pos < P) {
-                values[pos] = e.x;
-                if (KEYS) keys64[pos] = ((u64)tile << 32) | (u64)e.y;
+        const u64 tkey = (u64)((sy0 + (l >> 3)) * TX + sx0 + (l & 7)) << 32;
+        if ((u64)base + cnt <= (u64)P) {
+            uint32_t* vdst = values + base + lane;
+            u64* kdst = KEYS ? keys64 + base + lane : nullptr;
+#pragma unroll
+            for (int j = 0; j < PIECE / 64; ++j) {
+                if ((uint32_t)(64 * j) >= cnt) break;
+                if ((uint32_t)(64 * j + lane) < cnt) {
+                    const uint2 e = stage[64 * j + lane];
+                    vdst[64 * j] = e.x;
+                    if (KEYS) kdst[64 * j] = tkey | (u64)e.y;
+                }
+            }
+        } else {
+            for (uint32_t k = (uint32_t)lane; k < cnt; k += 64) {
+                const uint2 e = stage[k];
+                if (base + k < P) {
+                    values[base + k] = e.x;
+                    if (KEYS) keys64[base + k] = tkey | (u64)e.y;
+                }
             }
         }
         wave_lds_sync();  // the run is read before the next tile overwrites it
@@ -947,36 +1012,65 @@ __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int S, int
     }
 }
 
-// One wave per super-tile, lane = tile: running sum over the super-tile's
-// pieces of the per-piece counts (in place, becoming each piece's offset
-// inside the tile's run) and the tile's total.
-__global__ __launch_bounds__(SB) void k_tile_prefix(const u64* np_ptr, int S, int SX, int TX, int TY,
-                                                  const uint32_t* __restrict__ pfirst, uint32_t* __restrict__ counts,
-                                                  uint32_t* __restrict__ tile_total) {
+// One block of PFX_WAVES waves per super-tile, lane = tile: running sum over
+// the super-tile's pieces of the per-piece counts (in place, becoming each
+// piece's offset inside the tile's run) and the tile's total. Wave w takes a
+// contiguous share of the pieces: their column sums, a scan of the shares
+// through LDS, then the running sums written back.
+constexpr int PFX_WAVES = 16;
+
+__global__ __launch_bounds__(64 * PFX_WAVES) void k_tile_prefix(const u64* np_ptr, int S, int SX, int TX, int TY,
+                                                              const uint32_t* __restrict__ pfirst,
+                                                              uint32_t* __restrict__ counts,
+                                                              uint32_t* __restrict__ tile_total) {
+    __shared__ uint32_t s_sum[PFX_WAVES][64];
     const int lane = threadIdx.x & 63;
-    const int s = __builtin_amdgcn_readfirstlane(blockIdx.x * (SB / 64) + (int)(threadIdx.x >> 6));
-    if (s >= S) return;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int s = blockIdx.x;
     const int p0 = (int)pfirst[s];
-    const int p1 = s + 1 < S ? (int)pfirst[s + 1] : (int)*np_ptr;
-    uint32_t run = 0;
-    int p = p0;
-    for (; p + 8 <= p1; p += 8) {
-        uint32_t c[8];
+    const int n = (s + 1 < S ? (int)pfirst[s + 1] : (int)*np_ptr) - p0;
+    const int per = (n + PFX_WAVES - 1) / PFX_WAVES;
+    const int a = p0 + min(n, w * per), b = p0 + min(n, (w + 1) * per);
+    constexpr int U = 8;
+    uint32_t c[U];  // the share's first U counts, kept for the second pass
+    uint32_t sum = 0u;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) c[u] = counts[(size_t)(p + u) * 64 + lane];
+    for (int u = 0; u < U; ++u) {
+        c[u] = a + u < b ? counts[(size_t)(a + u) * 64 + lane] : 0u;
+        sum += c[u];
+    }
+    for (int p = a + U; p < b; p += U) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            counts[(size_t)(p + u) * 64 + lane] = run;
+        for (int u = 0; u < U; ++u) sum += p + u < b ? counts[(size_t)(p + u) * 64 + lane] : 0u;
+    }
+    s_sum[w][lane] = sum;
+    __syncthreads();
+    uint32_t run = 0u, tot = 0u;
+#pragma unroll
+    for (int k = 0; k < PFX_WAVES; ++k) {
+        const uint32_t v = s_sum[k][lane];
+        run += k < w ? v : 0u;
+        tot += v;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (a + u < b) {
+            counts[(size_t)(a + u) * 64 + lane] = run;
             run += c[u];
         }
-    }
-    for (; p < p1; ++p) {
-        const uint32_t c = counts[(size_t)p * 64 + lane];
-        counts[(size_t)p * 64 + lane] = run;
-        run += c;
+    for (int p = a + U; p < b; p += U) {
+        uint32_t d[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) d[u] = p + u < b ? counts[(size_t)(p + u) * 64 + lane] : 0u;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (p + u < b) {
+                counts[(size_t)(p + u) * 64 + lane] = run;
+                run += d[u];
+            }
     }
     const int tx = (s % SX) * SUPER + (lane & 7), ty = (s / SX) * SUPER + (lane >> 3);
-    if (tx < TX && ty < TY) tile_total[ty * TX + tx] = run;
+    if (w == 0 && tx < TX && ty < TY) tile_total[ty * TX + tx] = tot;
 }
 
 struct Grid2 {
@@ -1026,6 +1120,7 @@ BinLayout bin_layout(int64_t n, int64_t capacity, int TX, int TY) {
     L.sranges = take(8 * S);
     L.pfirst = take(4 * (S + 1));
     L.counts = take(4 * 64 * max_pieces);
+    L.pinfo = take(16 * max_pieces);
     L.tile_total = take(4 * ntiles);
     size_t max_elems = nn > cap ? nn : cap;
     const size_t hist_entries = 256 * ((max_elems + RE - 1) / RE);
@@ -1072,9 +1167,8 @@ hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means
     uint32_t* di[2] = {reinterpret_cast<uint32_t*>(ws + L.didx[0]), reinterpret_cast<uint32_t*>(ws + L.didx[1])};
     // 1. visible compaction (index order kept): depth bits, compact positions, records
     uint4* crec = reinterpret_cast<uint4*>(ws + L.crec);
-    k_scan_down<LoadVisible, StoreCompact><<<nb, SB, 0, s>>>(
-        LoadVisible{tiles_touched}, StoreCompact{depths, m2, radii, nper, TX, TYv, dk[0], di[0], crec}, n, nullptr,
-        partials);
+    k_compact_visible<<<nb, SB, 0, s>>>(n, nper, TX, TYv, tiles_touched, depths, m2, radii, partials, dk[0], di[0],
+                                        crec);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // 2. stable sort by the 32 depth bits, 4 passes of 8: the result returns to buffer 0
@@ -1111,6 +1205,7 @@ hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const
     uint32_t* pfirst = reinterpret_cast<uint32_t*>(ws + L.pfirst);
     uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.counts);
     uint32_t* tile_total = reinterpret_cast<uint32_t*>(ws + L.tile_total);
+    uint4* pinfo = reinterpret_cast<uint4*>(ws + L.pinfo);
     const Grid2 G = super_grid(TX, TY);
 
     // 3. super-tile entries in depth order, then grouped by super-tile (stable)
@@ -1138,18 +1233,18 @@ hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const
     const int max_pieces = (P1 + PIECE - 1) / PIECE + G.S;
     const int wpb = SB / 64;
     k_tile_count<<<(max_pieces + wpb - 1) / wpb, SB, 0, s>>>(&counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur], rec,
-                                                             counts);
-    k_tile_prefix<<<(G.S + wpb - 1) / wpb, SB, 0, s>>>(&counters[4], G.S, G.SX, TX, TY, pfirst, counts, tile_total);
+                                                             counts, pinfo);
+    k_tile_prefix<<<G.S, 64 * PFX_WAVES, 0, s>>>(&counters[4], G.S, G.SX, TX, TY, pfirst, counts, tile_total);
     e = scan(LoadPlain{tile_total}, StoreRanges{reinterpret_cast<uint2*>(ranges)}, ntiles, nullptr, partials, nullptr,
              s);
     if (e != hipSuccess) return e;
     if (keys)
-        k_tile_place<true><<<(PLACE_SPLIT * max_pieces + wpb - 1) / wpb, SB, 0, s>>>(
-            &counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur], rec, counts,
+        k_tile_place<true><<<8 * ((max_pieces + 7) / 8), SB, 0, s>>>(
+            &counters[4], G.SX, TX, TY, pinfo, sv[cur], rec, counts,
             reinterpret_cast<const uint2*>(ranges), (uint32_t)P, values, reinterpret_cast<u64*>(keys));
     else
-        k_tile_place<false><<<(PLACE_SPLIT * max_pieces + wpb - 1) / wpb, SB, 0, s>>>(
-            &counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur], rec, counts,
+        k_tile_place<false><<<8 * ((max_pieces + 7) / 8), SB, 0, s>>>(
+            &counters[4], G.SX, TX, TY, pinfo, sv[cur], rec, counts,
             reinterpret_cast<const uint2*>(ranges), (uint32_t)P, values, nullptr);
     return hipGetLastError();
 }

@@ -72,6 +72,7 @@ struct BinLayout {
     size_t sranges;            // per super-tile entry range
     size_t pfirst;             // per super-tile first piece
     size_t counts;             // per piece and tile: count, then offset within the tile's run
+    size_t pinfo;              // per piece: super-tile, first entry, end entry
     size_t tile_total;         // pairs per tile
     size_t partials;           // u64 scan partials
     size_t pair_part;          // u64 per-block partial pair counts
