@@ -90,22 +90,45 @@ __device__ __forceinline__ bool band_misses(float u, float v, float4 c, float lo
     return MissTest(c, lo).misses(u, v, x_lo, x_hi, y_lo, y_hi);
 }
 
-// Stages record `lane` of a batch: (w0, dy0, a2, beta), (g2, log2 o, r, g), b,
-// where w0 and dy0 are w and dy at the tile's first pixel centre (ox, oy),
-// formed in double and rounded once. Returns whether the record misses the
-// band (see band_misses).
-__device__ __forceinline__ bool stage_record(uint32_t g, const float2* __restrict__ means2d,
-                                             const float4* __restrict__ conic_op, const float* __restrict__ rgb,
-                                             Staged* s_rec, int lane, double ox, double oy,
-                                             float x_lo, float x_hi, float y_lo, float y_hi) {
+// The forward's staged record: a2 and the colour, then for each of the band's
+// 4 rows the row's w at the tile's first column, wrow = beta ly + w0, and its
+// exponent term et = g2 dy^2 + log2 o (dy = dy0 + ly), each rounded as the
+// backward forms them (fp32, one fma each). A pixel then needs
+// w = wrow + lx and the exponent a2 w^2 + et.
+struct alignas(16) RowStaged {
+    float4 k;       // (a2, r, g, b)
+    float2 row[4];  // (wrow, et) per row
+};
+
+// Stages record `lane` of a batch for the 4 rows ly = y0 .. y0 + 3 of a band
+// (ly counted from the tile's first row); w0 and dy0, w and dy at the tile's
+// first pixel centre (ox, oy), are formed in double and rounded once. Returns
+// whether the record misses the band (see band_misses).
+__device__ __forceinline__ bool stage_record_rows(uint32_t g, const float2* __restrict__ means2d,
+                                                  const float4* __restrict__ conic_op,
+                                                  const float* __restrict__ rgb, RowStaged* s_rec, int lane,
+                                                  double ox, double oy, float y0, float x_lo, float x_hi,
+                                                  float y_lo, float y_hi) {
     const float2 m = means2d[g];
     const float4 c = conic_op[g];
     const float4 k = falloff_consts(c);
     const double ddy = oy - (double)m.y;
-    const double w0 = (ox - (double)m.x) + (double)c.y * ddy;
-    s_rec[lane].a = make_float4((float)w0, (float)ddy, k.x, k.y);
-    s_rec[lane].b = make_float4(k.z, k.w, rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1]);
-    s_rec[lane].c.x = rgb[3 * (size_t)g + 2];
+    const float w0 = (float)((ox - (double)m.x) + (double)c.y * ddy), dy0 = (float)ddy;
+    const float r = rgb[3 * (size_t)g], gg = rgb[3 * (size_t)g + 1], bb = rgb[3 * (size_t)g + 2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float ly = y0 + (float)i;
+        float wrow, et;
+        {
+#pragma clang fp contract(off)
+            wrow = __fmaf_rn(k.y, ly, w0);
+            const float dy = dy0 + ly;
+            const float gdy = k.z * dy;
+            et = __fmaf_rn(gdy, dy, k.w);
+        }
+        s_rec[lane].row[i] = make_float2(wrow, et);
+    }
+    s_rec[lane].k = make_float4(k.x, r, gg, bb);
     return band_misses(m.x, m.y, c, k.w, x_lo, x_hi, y_lo, y_hi);
 }
 
@@ -186,7 +209,7 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
                                                  float* __restrict__ final_T, uint32_t* __restrict__ n_contrib,
                                                  float4* __restrict__ ckpt) {
     static_assert(PPL == 1, "one band of 16x4 pixels per wave");
-    __shared__ Staged s_rec[BATCH];
+    __shared__ RowStaged s_rec[BATCH];
     // Workgroups go to the 8 XCDs round-robin by index (b -> XCD b % 8). Tile
     // 8q + x takes workgroups 32q + 8 band + x, so its four band waves, which
     // stage the same records, share XCD x and its L2.
@@ -199,30 +222,21 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
     final_T += view_px;
     n_contrib += view_px;
     const int lane = threadIdx.x;
+    const int row = lane >> 4;  // the lane's row of the band
     const int px = tx * TILE + (lane & 15);
-    const int py0 = ty * TILE + band * 4 * PPL + (lane >> 4);
+    const int py = ty * TILE + band * 4 + row;
     const double ox = (double)(tx * TILE) + 0.5, oy = (double)(ty * TILE) + 0.5;  // the tile's first pixel centre
     const float lx = (float)(lane & 15);                                         // this lane's offset from it
-    float ly[PPL], T[PPL], C0[PPL], C1[PPL], C2[PPL], L[PPL];
-    uint32_t last[PPL];
-#pragma unroll
-    for (int k = 0; k < PPL; ++k) {
-        const int py = py0 + 4 * k;
-        ly[k] = (float)(py - ty * TILE);
-        T[k] = 1.f;
-        C0[k] = C1[k] = C2[k] = 0.f;
-        last[k] = 0u;
-        L[k] = (px < W && py < H) ? 1.f : 0.f;
-    }
+    float T = 1.f, C0 = 0.f, C1 = 0.f, C2 = 0.f;
+    // an entry blends where alpha >= thr: ALPHA_MIN while the pixel walks, above any alpha (2) once it has
+    // stopped (or lies outside the image), so that a stopped pixel's alpha counts as 0 and its T (>= T_MIN)
+    // never triggers the stop test again
+    float thr = (px < W && py < H) ? ALPHA_MIN : 2.f;
+    uint32_t last = 0u;
     // pixel-centre rectangle of the band
     const float bx_lo = (float)(tx * TILE) + 0.5f, bx_hi = bx_lo + 15.f;
-    const float by_lo = (float)(ty * TILE + band * 4 * PPL) + 0.5f, by_hi = by_lo + (float)(4 * PPL - 1);
-    auto walking = [&]() {
-        float l = 0.f;
-#pragma unroll
-        for (int k = 0; k < PPL; ++k) l += L[k];
-        return __any(l != 0.f);
-    };
+    const float by_lo = (float)(ty * TILE + band * 4) + 0.5f, by_hi = by_lo + 3.f;
+    auto walking = [&]() { return __any(thr < 1.f); };
     const uint2 rg = ranges[tile];
     bool wrote_ckpt = false;
     for (uint32_t bs = rg.x; bs < rg.y; bs += BATCH) {
@@ -231,34 +245,41 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
         const uint32_t idx = bs + lane;
         bool miss = true;
         if (idx < rg.y)
-            miss = stage_record(values[idx], means2d, conic_op, rgb, s_rec, lane, ox, oy, bx_lo, bx_hi, by_lo,
-                                by_hi);
+            miss = stage_record_rows(values[idx], means2d, conic_op, rgb, s_rec, lane, ox, oy, (float)(band * 4),
+                                     bx_lo, bx_hi, by_lo, by_hi);
         uint64_t todo = __ballot(!miss);  // records some pixel of the band may blend, in list order
         __syncthreads();
         const uint32_t pos0 = bs - rg.x + 1;
-        for (int n = 1; todo; ++n) {
-            const int j = __builtin_ctzll(todo);
-            todo &= todo - 1ull;
-            if ((n & 7) == 0 && !walking()) break;
-            const float4 A = s_rec[j].a;
-            const float4 B = s_rec[j].b;
-            const float cb = s_rec[j].c.x;
-            const float wl = A.x + lx;  // w at this lane's column, tile's first row
+        // entries in runs of 8 (unrolled, one exit test each), the band's walk checked between runs
+        while (todo) {
 #pragma unroll
-            for (int k = 0; k < PPL; ++k) {
-                const float oG = falloff(__fmaf_rn(A.w, ly[k], wl), A.y + ly[k], A.z, B.x, B.y);
+            for (int m = 0; m < 8; ++m) {
+                if (!todo) break;
+                const int j = __builtin_ctzll(todo);
+                todo &= todo - 1ull;
+                const float4 K = s_rec[j].k;
+                const float2 R = s_rec[j].row[row];
+                float q;
+                {
+#pragma clang fp contract(off)
+                    const float w = R.x + lx;
+                    const float aw = K.x * w;
+                    q = __fmaf_rn(aw, w, R.y);
+                }
+                const float oG = __builtin_amdgcn_exp2f(q);
                 const float al = fminf(ALPHA_MAX, oG);
-                float ae = (al >= ALPHA_MIN ? al : 0.f) * L[k];
-                const bool stop = __fmaf_rn(-ae, T[k], T[k]) < T_MIN;
-                L[k] = stop ? 0.f : L[k];
+                float ae = al >= thr ? al : 0.f;
+                const bool stop = __fmaf_rn(-ae, T, T) < T_MIN;
+                thr = stop ? 2.f : thr;
                 ae = stop ? 0.f : ae;
-                const float wt = ae * T[k];
-                C0[k] = fmaf(B.z, wt, C0[k]);
-                C1[k] = fmaf(B.w, wt, C1[k]);
-                C2[k] = fmaf(cb, wt, C2[k]);
-                T[k] = __fmaf_rn(-ae, T[k], T[k]);
-                last[k] = ae > 0.f ? pos0 + (uint32_t)j : last[k];
+                const float wt = ae * T;
+                C0 = fmaf(K.y, wt, C0);
+                C1 = fmaf(K.z, wt, C1);
+                C2 = fmaf(K.w, wt, C2);
+                T = __fmaf_rn(-ae, T, T);
+                last = ae > 0.f ? pos0 + (uint32_t)j : last;
             }
+            if (!walking()) break;
         }
         __syncthreads();
         if (ckpt) {
@@ -266,31 +287,26 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
             const uint32_t done = bs - rg.x + BATCH;
             if (bs + BATCH <= rg.y && done % CKPT_EVERY == 0 && done / CKPT_EVERY <= CKPT_SLOTS && walking()) {
                 ckpt[((size_t)tile * (CKPT_SLOTS + 1) + done / CKPT_EVERY - 1) * 256 + band * 64 + lane] =
-                    make_float4(T[0], C0[0], C1[0], C2[0]);
+                    make_float4(T, C0, C1, C2);
                 wrote_ckpt = true;
             }
         }
     }
     if (wrote_ckpt)  // the final colour, beside the checkpoints
-        ckpt[((size_t)tile * (CKPT_SLOTS + 1) + CKPT_SLOTS) * 256 + band * 64 + lane] =
-            make_float4(C0[0], C1[0], C2[0], T[0]);
+        ckpt[((size_t)tile * (CKPT_SLOTS + 1) + CKPT_SLOTS) * 256 + band * 64 + lane] = make_float4(C0, C1, C2, T);
     if (ckpt) {  // the band's walk, for the backward's choice of pieces
-        const uint32_t bw = wave_max_u32(last[0]);
+        const uint32_t bw = wave_max_u32(last);
         if (lane == 0)
             reinterpret_cast<uint32_t*>(ckpt + (size_t)ntiles * (CKPT_SLOTS + 1) * 256)[4 * tile + band] = bw;
     }
     const size_t HW = (size_t)W * H;
-#pragma unroll
-    for (int k = 0; k < PPL; ++k) {
-        const int py = py0 + 4 * k;
-        if (px < W && py < H) {
-            const size_t p = (size_t)py * W + px;
-            image[p] = fmaf(T[k], bg0, C0[k]);
-            image[HW + p] = fmaf(T[k], bg1, C1[k]);
-            image[2 * HW + p] = fmaf(T[k], bg2, C2[k]);
-            final_T[p] = T[k];
-            n_contrib[p] = last[k];
-        }
+    if (px < W && py < H) {
+        const size_t p = (size_t)py * W + px;
+        image[p] = fmaf(T, bg0, C0);
+        image[HW + p] = fmaf(T, bg1, C1);
+        image[2 * HW + p] = fmaf(T, bg2, C2);
+        final_T[p] = T;
+        n_contrib[p] = last;
     }
 }
 
@@ -417,11 +433,12 @@ __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, 
             const uint32_t pos = (uint32_t)(lo + j);
             // this lane's row: dy and the exponent's dy term, as falloff() forms them
             const float dy = A.y + ly;
-            float et;
+            float et, wrow;
             {
 #pragma clang fp contract(off)
                 const float gdy = B.x * dy;
                 et = __fmaf_rn(gdy, dy, B.y);
+                wrow = __fmaf_rn(A.w, ly, A.x);
             }
             float acc[GRAD2D_N];
 #pragma unroll
@@ -435,7 +452,7 @@ __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, 
                 // one pixel's blend test (the forward's own arithmetic: falloff() on the same values)
                 auto eval = [&](int k, float& w, float& oG, float& al) {
 #pragma clang fp contract(off)
-                    w = __fmaf_rn(A.w, ly, A.x + lx[k]);
+                    w = wrow + lx[k];
                     const float aw = A.z * w;
                     oG = __builtin_amdgcn_exp2f(__fmaf_rn(aw, w, et));
                     al = CLAMP ? fminf(ALPHA_MAX, oG) : oG;
@@ -730,14 +747,18 @@ __global__ __launch_bounds__(64) void k_render_counts(int W, int H, int TX, int 
             const float4 A = s_rec[j].a;
             const float4 B = s_rec[j].b;
             const uint32_t pos = bs - rg.x + 1 + (uint32_t)j;
-            const float wl = A.x + lx;
             bool mine = false;  // this lane blended the entry at one of its pixels
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 ef += L[k] != 0.f ? 1u : 0u;
                 if (!((bm >> k) & 1u)) continue;
                 efk += L[k] != 0.f ? 1u : 0u;
-                const float oG = falloff(__fmaf_rn(A.w, ly[k], wl), A.y + ly[k], A.z, B.x, B.y);
+                float w;
+                {
+#pragma clang fp contract(off)
+                    w = __fmaf_rn(A.w, ly[k], A.x) + lx;  // as the forward and backward form it
+                }
+                const float oG = falloff(w, A.y + ly[k], A.z, B.x, B.y);
                 const float al = fminf(ALPHA_MAX, oG);
                 float ae = (al >= ALPHA_MIN ? al : 0.f) * L[k];
                 const bool stop = __fmaf_rn(-ae, T[k], T[k]) < T_MIN;
