@@ -392,7 +392,10 @@ __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, 
         g2[k] = in ? dL_dimage[2 * HW + p] : 0.f;
         S[k] = fmaf(bg0, g0[k], fmaf(bg1, g1[k], bg2 * g2[k]));
         strip_last[k] = __builtin_amdgcn_readfirstlane(wave_max_u32(last[k]));  // deepest blended entry of strip k
-        if (!((band_sel >> k) & 1u)) strip_last[k] = 0u;  // no entry of strip k is walked
+        if (!((band_sel >> k) & 1u)) {  // strip k belongs to another wave: none of its entries is walked here
+            strip_last[k] = 0u;
+            last[k] = 0u;  // and its pixels blend nothing (the strip pass evaluates every strip)
+        }
         if (ck && rbw > (uint32_t)walk_hi) {  // this pixel's row band walked past walk_hi in the forward
             const int lp = 16 * r + col;      // the pixel's float4 in a checkpoint slot
             const float4 c = ck[lp], e = ck_end[lp];
@@ -426,7 +429,7 @@ __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, 
         while (todo) {
             const int j = 63 - __builtin_clzll(todo);  // backwards through the list
             todo &= ~(1ull << j);
-            const uint32_t bm = __builtin_amdgcn_readlane(strips, j);  // strips this record may reach
+            const uint32_t bm = __builtin_amdgcn_readlane(strips, j);  // bit 4: opacity above the clamp
             const float4 A = s_rec[j].a;
             const float4 B = s_rec[j].b;
             const float cb = s_rec[j].c.x;
@@ -446,10 +449,14 @@ __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, 
             float Hs = 0.f, HW1 = 0.f, HW2 = 0.f;  // sums over this lane's pixels of h, h w, h w^2
             bool any = false, mine = false;
             // the strips' pixel work, in two versions: a record whose opacity is at most 0.99 never
-            // reaches the alpha clamp (alpha = o G <= o), so it skips the clamp's min and test
+            // reaches the alpha clamp (alpha = o G <= o), so it skips the clamp's min and test. All
+            // strips go through it, even those the record cannot reach (their pixels fail the
+            // alpha test and add zeros, exactly): the strips' chains are independent, so all their
+            // tests go first and all their gradient terms after, without a branch between them,
+            // which costs less than skipping the unreachable ones
             auto strips_pass = [&](auto clamp_tag) {
                 constexpr bool CLAMP = decltype(clamp_tag)::value;
-                // one pixel's blend test (the forward's own arithmetic: falloff() on the same values)
+                // one pixel's blend test (the forward's own arithmetic on the same values)
                 auto eval = [&](int k, float& w, float& oG, float& al) {
 #pragma clang fp contract(off)
                     w = wrow + lx[k];
@@ -479,37 +486,19 @@ __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, 
                     HW2 = fmaf(hw, w, HW2);
                     HW1 += hw;
                 };
-                constexpr uint32_t FULL = (1u << PPL) - 1u;
-                if ((bm & FULL) == FULL) {
-                    // every strip may blend: the strips' chains are independent, so all their tests
-                    // go first and all their gradient terms after, without a branch between them
-                    // (a strip none of whose pixels blends adds zeros, exactly)
-                    float w[PPL], oG[PPL], al[PPL];
-                    bool bl[PPL], anyb = false;
-#pragma unroll
-                    for (int k = 0; k < PPL; ++k) {
-                        eval(k, w[k], oG[k], al[k]);
-                        bl[k] = pos < last[k] && al[k] >= ALPHA_MIN;
-                        anyb = anyb || bl[k];
-                    }
-                    if (!__any(anyb)) return;
-                    any = true;
-                    mine = mine || anyb;
-#pragma unroll
-                    for (int k = 0; k < PPL; ++k) grad(k, w[k], oG[k], al[k], bl[k]);
-                    return;
-                }
+                float w[PPL], oG[PPL], al[PPL];
+                bool bl[PPL], anyb = false;
 #pragma unroll
                 for (int k = 0; k < PPL; ++k) {
-                    if (!((bm >> k) & 1u)) continue;  // no pixel of strip k can blend this entry
-                    float w, oG, al;
-                    eval(k, w, oG, al);
-                    const bool blended = pos < last[k] && al >= ALPHA_MIN;
-                    if (!__any(blended)) continue;
-                    any = true;
-                    mine = mine || blended;
-                    grad(k, w, oG, al, blended);
+                    eval(k, w[k], oG[k], al[k]);
+                    bl[k] = pos < last[k] && al[k] >= ALPHA_MIN;
+                    anyb = anyb || bl[k];
                 }
+                if (!__any(anyb)) return;
+                any = true;
+                mine = mine || anyb;
+#pragma unroll
+                for (int k = 0; k < PPL; ++k) grad(k, w[k], oG[k], al[k], bl[k]);
             };
             if (bm & 16u) strips_pass(std::true_type{});
             else strips_pass(std::false_type{});
