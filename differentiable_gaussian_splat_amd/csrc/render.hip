@@ -268,16 +268,19 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
                 }
                 const float oG = __builtin_amdgcn_exp2f(q);
                 const float al = fminf(ALPHA_MAX, oG);
-                float ae = al >= thr ? al : 0.f;
-                const bool stop = __fmaf_rn(-ae, T, T) < T_MIN;
+                // the entry passes the alpha test; it blends unless it would take T below T_MIN, which
+                // ends the pixel instead
+                const bool pass = al >= thr;
+                const float Tn = __fmaf_rn(-al, T, T);
+                const bool stop = pass && Tn < T_MIN;
+                const bool blend = pass && !stop;
                 thr = stop ? 2.f : thr;
-                ae = stop ? 0.f : ae;
-                const float wt = ae * T;
+                const float wt = blend ? al * T : 0.f;
                 C0 = fmaf(K.y, wt, C0);
                 C1 = fmaf(K.z, wt, C1);
                 C2 = fmaf(K.w, wt, C2);
-                T = __fmaf_rn(-ae, T, T);
-                last = ae > 0.f ? pos0 + (uint32_t)j : last;
+                T = blend ? Tn : T;
+                last = blend ? pos0 + (uint32_t)j : last;
             }
             if (!walking()) break;
         }
