@@ -131,7 +131,8 @@ gs_status check_views(const gs_camera* cams, int32_t V, const gs_options* opt, i
 
 // Host side of gs_bin_sort's pair-count readback: a small pinned, host-coherent
 // buffer (written by a kernel through its device address) and an event per
-// (thread, device), created on first use and kept for the process.
+// (thread, device), created on first use and kept until the thread calls
+// gs_release_thread_state (or the process ends).
 struct Readback {
     int device = -1;
     unsigned long long* host = nullptr;
@@ -139,12 +140,15 @@ struct Readback {
     hipEvent_t ev = nullptr;
 };
 
+constexpr int READBACK_DEVICES = 16;
+thread_local Readback t_readback[READBACK_DEVICES];
+
 gs_status readback_for_current_device(Readback*& out) {
-    thread_local Readback slots[16];
+    Readback* slots = t_readback;
     int dev = 0;
     gs_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
     if (st != GS_OK) return st;
-    if (dev < 0 || dev >= 16) return fail(GS_ERR_UNSUPPORTED, "device index %d >= 16", dev);
+    if (dev < 0 || dev >= READBACK_DEVICES) return fail(GS_ERR_UNSUPPORTED, "device index %d >= 16", dev);
     Readback& r = slots[dev];
     if (r.device != dev) {
         st = hip_check(hipHostMalloc((void**)&r.host, 64, hipHostMallocMapped | hipHostMallocCoherent),
@@ -179,6 +183,24 @@ gs_options gs_default_options(void) {
 const char* gs_version(void) { return "gsplat-hip 0.1.0 (gfx950)"; }
 
 const char* gs_last_error(void) { return g_err; }
+
+gs_status gs_release_thread_state(void) {
+    gs_status st = GS_OK;
+    for (int d = 0; d < READBACK_DEVICES; ++d) {
+        Readback& r = t_readback[d];
+        if (r.device < 0) continue;
+        // a failed gs_bin_sort may have left its count kernel in flight: let it write first
+        gs_status e = hip_check(hipEventSynchronize(r.ev), "gs_release_thread_state(wait)");
+        if (e == GS_OK) e = hip_check(hipEventDestroy(r.ev), "gs_release_thread_state(event)");
+        if (e == GS_OK) e = hip_check(hipHostFree(r.host), "gs_release_thread_state(host buffer)");
+        if (e != GS_OK) {
+            st = e;
+            continue;  // kept: a later call may retry
+        }
+        r = Readback{};
+    }
+    return st;
+}
 
 gs_status gs_preprocess(const gs_camera* cam, const gs_options* opt, int64_t n, const float* means,
                         const float* scales, const float* quats, const float* opacities, const float* sh,
@@ -410,7 +432,7 @@ gs_status scratch_for_current_device(float*& out) {
     int dev = 0;
     gs_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
     if (st != GS_OK) return st;
-    if (dev < 0 || dev >= 16) return fail(GS_ERR_UNSUPPORTED, "device index %d >= 16", dev);
+    if (dev < 0 || dev >= READBACK_DEVICES) return fail(GS_ERR_UNSUPPORTED, "device index %d >= 16", dev);
     ScratchSlot& sl = slots[dev];
     // the current device is `dev` here, so the address is that device's copy
     std::call_once(sl.once, [&sl] { sl.err = hipGetSymbolAddress((void**)&sl.ptr, HIP_SYMBOL(scratch)); });

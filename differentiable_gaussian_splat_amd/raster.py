@@ -66,7 +66,8 @@ class GsAdamOptions(C.Structure):
                 ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float), ("step", C.c_int32)]
 
 
-EXPORTS = ["gs_default_options", "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_sort_workspace_size",
+EXPORTS = ["gs_default_options", "gs_version", "gs_last_error", "gs_release_thread_state", "gs_preprocess",
+           "gs_bin_sort_workspace_size",
            "gs_bin_sort", "gs_render_fwd", "gs_render_ckpt_bytes", "gs_render_bwd_workspace_size", "gs_render_bwd",
            "gs_render_bwd_raster",
            "gs_preprocess_bwd", "gs_preprocess_views", "gs_bin_sort_views_workspace_size", "gs_bin_sort_views",
@@ -98,6 +99,8 @@ def load_library(path: str = LIB_PATH):
         L.gs_default_options.restype = GsOptions
         L.gs_version.restype = C.c_char_p
         L.gs_last_error.restype = C.c_char_p
+        L.gs_release_thread_state.argtypes = []
+        L.gs_release_thread_state.restype = i32
         L.gs_preprocess.argtypes = [cam, opt, i64] + [P] * 5 + [P] * 7 + [P]
         L.gs_preprocess.restype = i32
         L.gs_bin_sort_workspace_size.argtypes = [i64, i64, i32, i32]
@@ -203,6 +206,11 @@ def make_options(sh_degree=3, sh_rows=0, lowpass=0.3, near_plane=0.2, bg=(0.0, 0
 
 def gs_version() -> str:
     return load_library().gs_version().decode()
+
+
+def gs_release_thread_state():
+    """Frees the calling thread's pair-count readback buffers (gs_bin_sort makes them again)."""
+    _check(load_library().gs_release_thread_state(), "gs_release_thread_state")
 
 
 def gs_preprocess(cam: GsCamera, opt: GsOptions, means, scales, quats, opacities, sh, means2d, depths,

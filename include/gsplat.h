@@ -22,7 +22,12 @@
  * --------------------------------
  * - Every array argument is a DEVICE pointer to caller-owned, contiguous,
  *   row-major memory unless marked "host". The library allocates no device
- *   memory: scratch comes from a caller-supplied workspace.
+ *   memory: scratch comes from a caller-supplied workspace. Two things it
+ *   does keep: gs_bin_sort's pair-count readback, a 64-byte pinned, mapped
+ *   host buffer and a HIP event per (calling thread, device), created on the
+ *   thread's first call on that device and kept until the thread calls
+ *   gs_release_thread_state() (or the process ends); and the fixed scratch
+ *   array of gs_render_bwd_noalloc, one per GPU, kept until the process ends.
  * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *   stream). The single exception is gs_bin_sort, which blocks the calling
  *   thread once, until the pair count has reached the host.
@@ -91,6 +96,15 @@ gs_options gs_default_options(void);
 const char *gs_version(void);
 /* Message of the last failed call on this thread ("" if none). */
 const char *gs_last_error(void);
+
+/*
+ * gs_release_thread_state -- frees the calling thread's pair-count readback
+ * buffers and events (see the conventions above), after waiting for any
+ * count kernel still writing them. For callers that start and end many
+ * threads; a later gs_bin_sort on the thread creates them again. Returns
+ * GS_ERR_HIP if a HIP call fails (what could not be freed is kept).
+ */
+gs_status gs_release_thread_state(void);
 
 /*
  * gs_preprocess -- per-Gaussian projection (phase P).

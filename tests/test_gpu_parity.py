@@ -57,6 +57,38 @@ def test_bin_sort_bit_exact(c, s, n):
     np.testing.assert_array_equal(g["ranges"], ranges)
 
 
+def test_release_thread_state_then_bin_sort_again():
+    """gs_release_thread_state frees the calling thread's pair-count readback buffer and event;
+    the next gs_bin_sort on that thread makes them again. Checked on the main thread (twice in a
+    row: the second call has nothing to free) and on a second thread that bins, releases and
+    bins again: every run gives the same lists."""
+    import threading
+    sc = scene(2, 0, 20_000)
+    ref = frame_np(gpu_frame(sc, 0)[2])
+    raster.gs_release_thread_state()
+    raster.gs_release_thread_state()
+    out = {}
+
+    def worker():
+        try:
+            out["a"] = frame_np(gpu_frame(sc, 0)[2])
+            raster.gs_release_thread_state()
+            out["b"] = frame_np(gpu_frame(sc, 0)[2])
+            raster.gs_release_thread_state()
+        except Exception as e:  # reported below
+            out["err"] = e
+
+    t = threading.Thread(target=worker)
+    t.start()
+    t.join()
+    assert "err" not in out, out.get("err")
+    again = frame_np(gpu_frame(sc, 0)[2])
+    for g in (out["a"], out["b"], again):
+        assert g["P"] == ref["P"]
+        np.testing.assert_array_equal(g["values"], ref["values"])
+        np.testing.assert_array_equal(g["ranges"], ref["ranges"])
+
+
 @pytest.mark.parametrize("c,s,n", CASES, ids=IDS)
 def test_forward_parity(c, s, n):
     sc = scene(c, s, n)
