@@ -784,14 +784,30 @@ struct LoadPieces {
 
 // The piece a wave takes: super-tile s (the last one whose first piece is at
 // or before pidx) and its entry range [e0, e1).
+// Up to 64 SEARCH_ROUNDS super-tiles, every lane compares a share of pfirst
+// with all loads in flight at once (a ballot count per round); beyond, a
+// binary search (one dependent load per step).
+constexpr int SEARCH_ROUNDS = 8;
+
 __device__ __forceinline__ void piece_of(int pidx, int S, const uint32_t* __restrict__ pfirst,
                                          const uint2* __restrict__ sr, int& s, int& e0, int& e1) {
-    int lo = 0, hi = S;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if ((int)pfirst[mid] <= pidx) lo = mid + 1; else hi = mid;
+    if (S <= 64 * SEARCH_ROUNDS) {
+        const int lane = threadIdx.x & 63;
+        uint32_t v[SEARCH_ROUNDS];
+#pragma unroll
+        for (int r = 0; r < SEARCH_ROUNDS; ++r) v[r] = lane + 64 * r < S ? pfirst[lane + 64 * r] : 0xFFFFFFFFu;
+        int cnt = 0;  // super-tiles whose first piece is at or before pidx (pfirst does not decrease)
+#pragma unroll
+        for (int r = 0; r < SEARCH_ROUNDS; ++r) cnt += __popcll(__ballot(v[r] <= (uint32_t)pidx));
+        s = cnt - 1;
+    } else {
+        int lo = 0, hi = S;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((int)pfirst[mid] <= pidx) lo = mid + 1; else hi = mid;
+        }
+        s = lo - 1;
     }
-    s = lo - 1;
     const uint2 r = sr[s];
     e0 = (int)r.x + (pidx - (int)pfirst[s]) * PIECE;
     e1 = min((int)r.y, e0 + PIECE);
@@ -812,25 +828,25 @@ __device__ __forceinline__ uint64_t entry_tiles(uint4 r, bool valid, int sx0, in
 
 constexpr int PIECE_GROUPS = PIECE / 64;
 
-// One wave per piece: for each tile lt of the super-tile (lane lt), the number
-// of the piece's entries whose rectangle holds it, to counts[pidx][lt]. An
-// entry's tiles inside the super-tile form a rectangle, so the counts are a
-// 2D prefix sum of a (SUPER + 1)^2 difference array: each entry adds +1 / -1
-// at its rectangle's four corners (LDS integer atomics, exact), then a row
-// pass and a column pass of running sums give every tile's count. The
-// piece's super-tile and entry range go to pinfo for the placement.
-constexpr int DGRID = SUPER + 1;
-
+// One wave per piece: for each tile l of the super-tile (lane l = 8 row +
+// column), the number of the piece's entries whose rectangle holds it, to
+// counts[pidx][l]. An entry's tiles inside the super-tile form a rectangle,
+// so the counts are the 2D prefix sum of an 8 x 8 difference array: each
+// entry adds +1 / -1 at its rectangle's corners that fall inside the super-
+// tile (LDS integer atomics, exact; a corner past row or column 7 touches no
+// tile), then lane l takes cell l and the running sums go along the rows and
+// then the columns by lane shuffles. The piece's super-tile and entry range go
+// to pinfo for the placement.
 __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int SX, int TX, int TY,
                                                  const uint32_t* __restrict__ pfirst, const uint2* __restrict__ sr,
                                                  const uint32_t* __restrict__ sval, const uint4* __restrict__ rec,
                                                  uint32_t* __restrict__ counts, uint4* __restrict__ pinfo) {
-    __shared__ int s_diff[SB / 64][DGRID * DGRID];
+    __shared__ int s_diff[SB / 64][SUPER * SUPER];
     const int lane = threadIdx.x & 63;
     const int pidx = __builtin_amdgcn_readfirstlane(blockIdx.x * (SB / 64) + (int)(threadIdx.x >> 6));
     if (pidx >= (int)*np_ptr) return;  // the whole wave: no block barrier follows
     int* d = s_diff[threadIdx.x >> 6];
-    for (int k = lane; k < DGRID * DGRID; k += 64) d[k] = 0;
+    d[lane] = 0;
     int s, e0, e1;
     piece_of(pidx, S, pfirst, sr, s, e0, e1);
     if (lane == 0) pinfo[pidx] = make_uint4((uint32_t)s, (uint32_t)e0, (uint32_t)e1, 0u);  // for the placement
@@ -843,7 +859,7 @@ __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int
 #pragma unroll
     for (int q = 0; q < PIECE_GROUPS; ++q) rq[q] = rec[gi[q]];
     wave_lds_sync();  // the cleared array is seen before the corners are added
-    // entries covering the whole super-tile (large Gaussians) share their four corners: they are
+    // entries covering the whole super-tile (large Gaussians) share their corners: they are
     // counted with one ballot per group and added once, the others add their own corners
     int n_full = 0;
 #pragma unroll
@@ -855,36 +871,32 @@ __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int
         const bool full = valid && cx0 == 0 && cy0 == 0 && cx1 == vw - 1 && cy1 == vh - 1;
         n_full += __popcll(__ballot(full));
         if (valid && !full) {
-            atomicAdd(&d[cy0 * DGRID + cx0], 1);
-            atomicAdd(&d[cy0 * DGRID + cx1 + 1], -1);
-            atomicAdd(&d[(cy1 + 1) * DGRID + cx0], -1);
-            atomicAdd(&d[(cy1 + 1) * DGRID + cx1 + 1], 1);
+            const bool right = cx1 + 1 < SUPER, below = cy1 + 1 < SUPER;
+            atomicAdd(&d[cy0 * SUPER + cx0], 1);
+            if (right) atomicAdd(&d[cy0 * SUPER + cx1 + 1], -1);
+            if (below) atomicAdd(&d[(cy1 + 1) * SUPER + cx0], -1);
+            if (right && below) atomicAdd(&d[(cy1 + 1) * SUPER + cx1 + 1], 1);
         }
     }
     if (n_full && lane == 0) {
         atomicAdd(&d[0], n_full);
-        atomicAdd(&d[vw], -n_full);
-        atomicAdd(&d[vh * DGRID], -n_full);
-        atomicAdd(&d[vh * DGRID + vw], n_full);
+        if (vw < SUPER) atomicAdd(&d[vw], -n_full);
+        if (vh < SUPER) atomicAdd(&d[vh * SUPER], -n_full);
+        if (vw < SUPER && vh < SUPER) atomicAdd(&d[vh * SUPER + vw], n_full);
     }
     wave_lds_sync();
-    if (lane < DGRID) {  // running sums along each row
-        int run = 0;
-        for (int c = 0; c < DGRID; ++c) {
-            run += d[lane * DGRID + c];
-            d[lane * DGRID + c] = run;
-        }
+    int x = d[lane];
+#pragma unroll
+    for (int off = 1; off < SUPER; off <<= 1) {  // along the row: lanes 8 r .. 8 r + 7
+        const int y = __shfl_up(x, off, SUPER);
+        if ((lane & (SUPER - 1)) >= off) x += y;
     }
-    wave_lds_sync();
-    if (lane < DGRID) {  // then down each column
-        int run = 0;
-        for (int r = 0; r < DGRID; ++r) {
-            run += d[r * DGRID + lane];
-            d[r * DGRID + lane] = run;
-        }
+#pragma unroll
+    for (int off = SUPER; off < 64; off <<= 1) {  // down the column: lanes c, c + 8, ...
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
     }
-    wave_lds_sync();
-    counts[(size_t)pidx * 64 + lane] = (uint32_t)d[(lane >> 3) * DGRID + (lane & 7)];
+    counts[(size_t)pidx * 64 + lane] = (uint32_t)x;
 }
 
 // Placement, with the roles turned: lane = entry of a 64-entry group of the
