@@ -330,6 +330,15 @@ def main():
     raster.gs_mb_render_bwd_naive(cam_last, opt, n, ranges, r._values, last_P[-1], means2d, conic, rgb, final_T,
                                   n_contrib, dl_last, g2n, lane_hist)
     lh = lane_hist.cpu().numpy().astype(np.float64)
+    # the adaptive switch (direct atomics when few lanes blend an entry, else the wave reduction) on the
+    # pieces kernel, at several lane counts; 0 is the reduced kernel itself
+    adaptive = None
+    if ckpt is not None:
+        adaptive = {}
+        for dm in (0, 4, 8, 16, 64):
+            adaptive[str(dm)] = round(1e3 * timed(lambda: raster.gs_mb_render_bwd_adaptive(
+                cam_last, opt, n, ranges, r._values, last_P[-1], means2d, conic, rgb, final_T, n_contrib, dl_last,
+                g2n, ckpt, dm), 5), 4)
     del g2n
     atomic_rate = n_atomics / t_at
     del recs
@@ -404,6 +413,12 @@ def main():
                                                (0.25, 0.5, 0.75)]},
             "note": "gs_mb_render_bwd_naive: each lane adds its own pixel's nine terms with its own atomics (about "
                     "9 per blended pixel-entry), against the wave-reduced backward raster (9 per tile-entry)",
+        },
+        "adaptive_bwd": None if adaptive is None else {
+            "ms_by_direct_max": adaptive,
+            "note": "gs_mb_render_bwd_adaptive: per (wave, entry), at most direct_max blending lanes add their "
+                    "terms with their own atomics, more reduce over the wave (0: the reduced kernel; 64: direct "
+                    "atomics always); the last view, after the timed steps",
         },
         "bwd_hbm_atomic_roofline": {
             "hbm_bytes": bwd_bytes,

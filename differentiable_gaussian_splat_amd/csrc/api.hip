@@ -976,6 +976,38 @@ gs_status gs_adam_step(const gs_adam_options* opt, int64_t n, int32_t sh_rows, f
     }
 }
 
+gs_status gs_mb_render_bwd_adaptive(const gs_camera* cam, const gs_options* opt, int64_t n, const uint32_t* ranges,
+                                    const uint32_t* values, int64_t n_pairs, const float* means2d,
+                                    const float* conic_opacity, const float* rgb, const float* final_T,
+                                    const uint32_t* n_contrib, const float* dL_dimage, float* grad2d,
+                                    const void* ckpt, size_t ckpt_bytes, int32_t direct_max, void* stream) {
+    try {
+        g_err[0] = 0;
+        Checked c;
+        gs_status st = check_common(cam, opt, n, c);
+        if (st != GS_OK) return st;
+        REQUIRE(direct_max >= 0 && direct_max <= 64, "direct_max must be in [0, 64], got %d", direct_max);
+        if (n == 0 || n_pairs == 0) return GS_OK;
+        REQUIRE(n_pairs > 0 && n_pairs < ((int64_t)1 << 31), "n_pairs must be in [0, 2^31)");
+        REQUIRE(ranges && values && means2d && conic_opacity && rgb && final_T && n_contrib && dL_dimage && grad2d,
+                "gs_mb_render_bwd_adaptive: NULL array");
+        REQUIRE(aligned(grad2d, 16) && aligned(conic_opacity, 16) && aligned(means2d, 8) && aligned(ranges, 8),
+                "gs_mb_render_bwd_adaptive: misaligned array");
+        if (!ckpt || gs::render_ckpt_bytes(c.cam.TX, c.cam.TY) == 0)
+            return fail(GS_ERR_UNSUPPORTED,
+                        "gs_mb_render_bwd_adaptive: needs the forward's checkpoints (grids of 4096..32767 tiles)");
+        st = check_ckpt(ckpt, ckpt_bytes, c);
+        if (st != GS_OK) return st;
+        return hip_check(gs::launch_render_bwd_adaptive(c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values, means2d,
+                                                        conic_opacity, rgb, opt->bg, final_T, n_contrib, dL_dimage,
+                                                        grad2d, static_cast<const float*>(ckpt), direct_max,
+                                                        (hipStream_t)stream),
+                         "gs_mb_render_bwd_adaptive");
+    } catch (...) {
+        return fail(GS_ERR_HIP, "gs_mb_render_bwd_adaptive: unexpected exception");
+    }
+}
+
 gs_status gs_mb_render_bwd_naive(const gs_camera* cam, const gs_options* opt, int64_t n, const uint32_t* ranges,
                                  const uint32_t* values, int64_t n_pairs, const float* means2d,
                                  const float* conic_opacity, const float* rgb, const float* final_T,

@@ -117,6 +117,13 @@ hipError_t launch_render_bwd(int views, int W, int H, int TX, int TY, const uint
 
 // The backward raster with per-pixel atomics (no wave reduction), one view: measurement only.
 // lane_hist (nullable, 65 counters): per (wave, entry) step, the count of lanes updating the Gaussian.
+// The pieces backward (one view with checkpoints, grids of 4096..32767 tiles),
+// reducing an entry over the wave only when more than direct_max lanes blend
+// it (hipErrorInvalidValue for other grids or without checkpoints).
+hipError_t launch_render_bwd_adaptive(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
+                                      const float* means2d, const float* conic_op, const float* rgb, const float* bg,
+                                      const float* final_T, const uint32_t* n_contrib, const float* dL_dimage,
+                                      float* grad2d, const float* ckpt, int direct_max, hipStream_t stream);
 hipError_t launch_render_bwd_naive(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
                                    const float* means2d, const float* conic_op, const float* rgb, const float* bg,
                                    const float* final_T, const uint32_t* n_contrib, const float* dL_dimage,

@@ -319,7 +319,11 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
 // dL/dalpha = T (rgb . dL/dC - S).
 // NAIVE (measurement only, PPL = 1): every lane adds its own pixel's terms
 // with its own atomics, the per-pixel pattern the DISTWAR and ARC pages
-// measure, instead of reducing over the wave first.
+// measure, instead of reducing over the wave first. ADAPT (measurement only):
+// per entry, the wave reduces only when more than direct_max of its lanes
+// blend; otherwise those lanes add their terms directly (the switch between
+// reduction and direct atomics by the number of lanes that the ARC page's
+// title names).
 // LDS of one backward wave: a batch of staged records, their Gaussians, the
 // per-row partial sums and which entries some pixel blended.
 template <int NB>
@@ -345,7 +349,7 @@ struct BwdShared {
 // (C_final - C there + final_T bg) / T), with ck_end holding C_final; a
 // checkpoint slot holds pixel (r, c) at float4 16 r + c. ck is null when
 // walk_hi is past the walk.
-template <int PPL, int NB, bool NAIVE>
+template <int PPL, int NB, bool NAIVE, bool ADAPT = false>
 __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, int walk_lo, int walk_hi,
                                          const float4* __restrict__ ck, const float4* __restrict__ ck_end,
                                          uint4 rb_walk, int W, int H, int TX, int TY,
@@ -354,7 +358,7 @@ __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, 
                                          const float* __restrict__ rgb, float bg0, float bg1, float bg2,
                                          const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib,
                                          const float* __restrict__ dL_dimage, float* __restrict__ grad2d,
-                                         uint32_t* __restrict__ lane_hist, BwdShared<NB>& sh) {
+                                         uint32_t* __restrict__ lane_hist, BwdShared<NB>& sh, int direct_max = -1) {
     Staged* s_rec = sh.rec;
     uint32_t* s_g = sh.g;
     float* s_part = sh.part;
@@ -524,6 +528,18 @@ __device__ __forceinline__ void bwd_walk(int tile, int band, uint32_t band_sel, 
                 if (lane_hist && lane == 0) atomicAdd(&lane_hist[__popcll(who)], 1u);
                 continue;
             }
+            if (ADAPT) {
+                // measurement: when at most direct_max lanes blend the entry, they add their own terms
+                // with their own atomics instead of reducing over the wave first
+                if (__popcll(__ballot(mine)) <= (uint32_t)direct_max) {
+                    if (mine) {
+                        float* dst = grad2d + (size_t)s_g[j] * GRAD2D_STRIDE;
+#pragma unroll
+                        for (int c = 0; c < GRAD2D_N; ++c) atomicAdd(&dst[c], acc[c]);
+                    }
+                    continue;
+                }
+            }
             // per 16-lane row: values 0..7 by reduce-scatter (lane slot holds one), value 8 by a row sum
             const float u = row_reduce_scatter8(acc, c1, c2, c3);
             const float x8 = row_sum16(acc[8]);
@@ -620,7 +636,7 @@ __global__ __launch_bounds__(64) void k_render_bwd_split(int W, int H, int TX, i
 // extra per-entry reductions of a split by bands. A walk longer than
 // (CKPT_SLOTS + 1) pieces ends in a tail piece [CKPT_SLOTS CKPT_EVERY, walk)
 // from the final state, which two waves share by row bands.
-template <int NB>
+template <int NB, bool ADAPT = false>
 __global__ __launch_bounds__(64) void k_render_bwd_pieces(int W, int H, int TX, int TY, int ntiles,
                                                         const float4* __restrict__ ckpt,
                                                         const uint2* __restrict__ ranges,
@@ -631,7 +647,7 @@ __global__ __launch_bounds__(64) void k_render_bwd_pieces(int W, int H, int TX, 
                                                         const float* __restrict__ final_T,
                                                         const uint32_t* __restrict__ n_contrib,
                                                         const float* __restrict__ dL_dimage,
-                                                        float* __restrict__ grad2d) {
+                                                        float* __restrict__ grad2d, int direct_max = -1) {
     __shared__ BwdShared<NB> sh;
     constexpr int PIECES = CKPT_SLOTS + 1;  // slots in the checkpoint buffer per tile
     constexpr int WAVES = CKPT_SLOTS + 2;   // waves per tile
@@ -675,9 +691,9 @@ __global__ __launch_bounds__(64) void k_render_bwd_pieces(int W, int H, int TX, 
     const bool tail = piece >= pieces - 1;  // the last piece walks to the end from the final state
     const int lo = piece * CKPT_EVERY, hi = tail ? INT32_MAX : lo + CKPT_EVERY;
     const float4* tck = ckpt + (size_t)tile * PIECES * 256;
-    bwd_walk<4, NB, false>(tile, 0, sel, lo, hi, tail ? nullptr : tck + (size_t)piece * 256, tck + CKPT_SLOTS * 256,
-                           bw, W, H, TX, TY, ranges, values, means2d, conic_op, rgb, bg0, bg1, bg2, final_T, n_contrib,
-                           dL_dimage, grad2d, nullptr, sh);
+    bwd_walk<4, NB, false, ADAPT>(tile, 0, sel, lo, hi, tail ? nullptr : tck + (size_t)piece * 256,
+                                  tck + CKPT_SLOTS * 256, bw, W, H, TX, TY, ranges, values, means2d, conic_op, rgb, bg0,
+                                  bg1, bg2, final_T, n_contrib, dL_dimage, grad2d, nullptr, sh, direct_max);
 }
 
 // Measurement: the work of one view's blending, counted with the forward's own
@@ -891,6 +907,21 @@ hipError_t launch_render_bwd(int views, int W, int H, int TX, int TY, const uint
                                                                  bg[2], final_T, n_contrib, dL_dimage, grad2d);
             break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_render_bwd_adaptive(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
+                                      const float* means2d, const float* conic_op, const float* rgb, const float* bg,
+                                      const float* final_T, const uint32_t* n_contrib, const float* dL_dimage,
+                                      float* grad2d, const float* ckpt, int direct_max, hipStream_t stream) {
+    const int ntiles = TX * TY;
+    if (ntiles == 0) return hipSuccess;
+    if (!ckpt || bwd_layout(ntiles) != BwdLayout::Split) return hipErrorInvalidValue;
+    k_render_bwd_pieces<BWD_BATCH, true>
+        <<<(CKPT_SLOTS + 2) * PIECES_CHUNK * ((ntiles + PIECES_CHUNK - 1) / PIECES_CHUNK), 64, 0, stream>>>(
+            W, H, TX, TY, ntiles, reinterpret_cast<const float4*>(ckpt), reinterpret_cast<const uint2*>(ranges), values,
+            reinterpret_cast<const float2*>(means2d), reinterpret_cast<const float4*>(conic_op), rgb, bg[0], bg[1],
+            bg[2], final_T, n_contrib, dL_dimage, grad2d, direct_max);
     return hipGetLastError();
 }
 

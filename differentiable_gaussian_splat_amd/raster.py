@@ -72,7 +72,7 @@ EXPORTS = ["gs_default_options", "gs_version", "gs_last_error", "gs_release_thre
            "gs_render_bwd_raster",
            "gs_preprocess_bwd", "gs_preprocess_views", "gs_bin_sort_views_workspace_size", "gs_bin_sort_views",
            "gs_render_fwd_views", "gs_render_bwd_raster_views", "gs_preprocess_bwd_views", "gs_adam_step",
-           "gs_mb_render_bwd_naive", "gs_mb_hbm_read", "gs_mb_hbm_copy", "gs_mb_atomic", "gs_render_bwd_noalloc",
+           "gs_mb_render_bwd_naive", "gs_mb_render_bwd_adaptive", "gs_mb_hbm_read", "gs_mb_hbm_copy", "gs_mb_atomic", "gs_render_bwd_noalloc",
            "gs_mb_render_counts", "gs_surfel_preprocess", "gs_surfel_render_fwd", "gs_surfel_render_bwd_raster",
            "gs_surfel_preprocess_bwd", "gs_surfel_render_bwd_workspace_size", "gs_surfel_render_bwd"]
 SURFEL_GRAD_STRIDE = 16
@@ -141,6 +141,8 @@ def load_library(path: str = LIB_PATH):
         L.gs_adam_step.restype = i32
         L.gs_mb_render_bwd_naive.argtypes = [cam, opt, i64, P, P, i64] + [P] * 7 + [P, P]
         L.gs_mb_render_bwd_naive.restype = i32
+        L.gs_mb_render_bwd_adaptive.argtypes = [cam, opt, i64, P, P, i64] + [P] * 7 + [P, sz, i32, P]
+        L.gs_mb_render_bwd_adaptive.restype = i32
         L.gs_mb_render_counts.argtypes = [cam, opt, P, P, i64, P, P, P, P, P]
         L.gs_mb_render_counts.restype = i32
         L.gs_surfel_preprocess.argtypes = [cam, opt, i64] + [P] * 5 + [P] * 7 + [P]
@@ -410,6 +412,15 @@ def gs_mb_render_bwd_naive(cam: GsCamera, opt: GsOptions, n, ranges, values, n_p
                                                _p(means2d), _p(conic_opacity), _p(rgb), _p(final_T), _p(n_contrib),
                                                _p(dL_dimage), _p(grad2d), _p(lane_hist), _stream(stream))
     _check(st, "gs_mb_render_bwd_naive")
+
+
+def gs_mb_render_bwd_adaptive(cam: GsCamera, opt: GsOptions, n, ranges, values, n_pairs, means2d, conic_opacity,
+                              rgb, final_T, n_contrib, dL_dimage, grad2d, ckpt, direct_max, stream=None):
+    st = load_library().gs_mb_render_bwd_adaptive(C.byref(cam), C.byref(opt), n, _p(ranges), _p(values), n_pairs,
+                                                  _p(means2d), _p(conic_opacity), _p(rgb), _p(final_T),
+                                                  _p(n_contrib), _p(dL_dimage), _p(grad2d), _p(ckpt), _nbytes(ckpt),
+                                                  int(direct_max), _stream(stream))
+    _check(st, "gs_mb_render_bwd_adaptive")
 
 
 def gs_mb_render_counts(cam: GsCamera, opt: GsOptions, ranges, values, n_pairs, means2d, conic_opacity, rgb, counts,

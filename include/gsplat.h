@@ -545,6 +545,22 @@ gs_status gs_mb_render_bwd_naive(const gs_camera *cam, const gs_options *opt, in
                                  const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
                                  float *grad2d, uint32_t *lane_hist, void *stream);
 
+/* gs_render_bwd_raster of one view with the forward's checkpoints (grids of
+ * 4096..32767 tiles), switching per (wave, list entry) between the wave
+ * reduction and direct atomics by the number of lanes that blend the entry:
+ * at most direct_max (0..64) lanes add their own terms with their own fp32
+ * atomics, more reduce over the wave first. The adaptive scheme of the ARC
+ * page ("ARC: Warp-level Adaptive Atomic Reduction in GPUs to Accelerate
+ * Differentiable Rendering", title and abstract); direct_max = 0 is the
+ * reduced backward. Same arguments and result as gs_render_bwd_raster, up to
+ * summation order; GS_ERR_UNSUPPORTED without checkpoints. For timing only. */
+gs_status gs_mb_render_bwd_adaptive(const gs_camera *cam, const gs_options *opt, int64_t n,
+                                    const uint32_t *ranges, const uint32_t *values, int64_t n_pairs,
+                                    const float *means2d, const float *conic_opacity, const float *rgb,
+                                    const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
+                                    float *grad2d, const void *ckpt, size_t ckpt_bytes, int32_t direct_max,
+                                    void *stream);
+
 /* The work of one view's blending, counted with the forward's own decisions
  * (one wave per tile, 4 pixels per lane), ADDED to counts[7] (u64):
  *   [0] E_f: entries each pixel evaluates (up to and including the one that

@@ -454,6 +454,32 @@ def test_backward_split_of_deep_tiles(bg):
         assert rel_l2(sums[0][:, c], sums[1][:, c]) < 1e-5, (c, rel_l2(sums[0][:, c], sums[1][:, c]))
 
 
+@pytest.mark.parametrize("direct_max", [0, 8, 64])
+def test_adaptive_backward_matches_reduced(direct_max):
+    """The measurement kernel that switches per (wave, entry) between the wave
+    reduction and direct atomics by the number of blending lanes computes the
+    same pixel sums as the reduced backward raster (up to summation order), at
+    0 (always reduce), 8 and 64 (always direct) lanes. A 1080p grid, so that the
+    forward's checkpoints and the pieces kernel are in play."""
+    sc = make_scene(3, 0, n=40_000)
+    r, pd, fr = gpu_frame(sc, 0)
+    assert fr.ckpt is not None
+    n = sc.n
+    dL = to_dev(sc.dL_dimage[0])
+    red = torch.zeros((n, raster.GRAD2D_STRIDE), dtype=torch.float32, device=pd["means"].device)
+    ada = torch.zeros_like(red)
+    args = (fr.cam, fr.opt, n, fr.ranges, fr.values, fr.n_pairs, fr.means2d, fr.conic_opacity, fr.rgb, fr.final_T,
+            fr.n_contrib, dL)
+    raster.gs_render_bwd_raster(*args, red, fr.ckpt)
+    raster.gs_mb_render_bwd_adaptive(*args, ada, fr.ckpt, direct_max)
+    torch.cuda.synchronize()
+    a, b = red.cpu().numpy().astype(np.float64), ada.cpu().numpy().astype(np.float64)
+    assert np.count_nonzero(a[:, :9]) > 0
+    for c in range(9):
+        assert rel_l2(b[:, c], a[:, c]) < 1e-5, (c, rel_l2(b[:, c], a[:, c]))
+    assert not b[:, 9:].any()
+
+
 def test_naive_atomic_backward_matches_reduced():
     """The measurement kernel with per-pixel atomics computes the same pixel
     sums as the wave-reduced backward raster (up to summation order)."""
