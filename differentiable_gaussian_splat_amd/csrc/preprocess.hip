@@ -9,6 +9,15 @@
 // fp32; where it needs T0 x T1 it uses the closed form
 // T0 x T1 = (fx fy / z^3) s1 s2 s3 diag(1/s) Rq^T (mu - campos) (Lagrange's
 // identity gives det(T T^T) = |T0 x T1|^2), which has no cancellation.
+//
+// No floating-point contraction in this file: a product feeds an add only
+// where an fma is written out. The same functions are inlined into several
+// kernels (one view or many, SH rows in LDS or in registers, adding or
+// writing the gradients); without contraction each kernel rounds every
+// operation exactly as written, so their results agree bit for bit. (Set
+// before the includes, so that it covers the shared helpers too.)
+#pragma clang fp contract(off)
+
 #include "common.hpp"
 #include "launch.hpp"
 
