@@ -8,9 +8,12 @@
 // Work layout: each 64-lane wave owns 64 consecutive Gaussians. The small
 // parameter groups go lane = Gaussian. The SH block of the 64 Gaussians is
 // one contiguous run in every array and is walked as flat float4s with
-// consecutive lanes on consecutive addresses (the update is element-wise);
-// each lane adds its squared gradients into its Gaussian's LDS slot, which
-// the Gaussian's own lane reads at the end.
+// consecutive lanes on consecutive addresses (the update is element-wise).
+// The squared SH gradients of one step's lanes that belong to one Gaussian
+// (consecutive lanes) are summed by a segmented tree over the wave, and the
+// segment's first lane adds the sum to the Gaussian's LDS slot, which the
+// Gaussian's own lane reads at the end: a fixed order, so the norm is the
+// same bit for bit from run to run.
 #include <cmath>
 
 #include "common.hpp"
@@ -43,6 +46,23 @@ __device__ __forceinline__ float sigmoidf(float x, float* deriv = nullptr) {
     return x >= 0.f ? sp : e * sp;
 }
 
+// Adds x into s[j] for every valid lane, where the lanes sharing a j are
+// consecutive: a segmented tree sum (lane i takes lane i + off's partial when
+// both lie in one segment), then the segment's first lane adds, with a plain
+// LDS update (one writer per j per call; the wave's calls run in order).
+__device__ __forceinline__ void seg_add(float* s, int j, float x, bool valid) {
+    const int lane = threadIdx.x & 63;
+    const int key = valid ? j : -1 - lane;  // invalid lanes form segments of their own
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_down(x, off);
+        const int ky = __shfl_down(key, off);
+        if (lane + off < 64 && ky == key) x += y;
+    }
+    const int kprev = __shfl_up(key, 1);
+    if (valid && (lane == 0 || kprev != key)) s[j] += x;
+}
+
 __global__ __launch_bounds__(OB) void k_adam_step(AdamLr lr, AdamK k, int n, int rec, float* __restrict__ means,
                                                  float* __restrict__ lsc, float4* __restrict__ quats,
                                                  float* __restrict__ logit, float* __restrict__ sh,
@@ -65,38 +85,51 @@ __global__ __launch_bounds__(OB) void k_adam_step(AdamLr lr, AdamK k, int n, int
     // SH: the wave's run of cnt * rec floats, element-wise
     const size_t r0 = (size_t)base * rec;
     const int total = cnt * rec;
+    // every lane runs every step (the segmented sums need the whole wave); lanes past the run idle
     if ((rec & 3) == 0) {
-        for (int f = lane; 4 * f < total; f += 64) {
-            const size_t o = r0 + 4 * (size_t)f;
-            float4 p = *reinterpret_cast<const float4*>(sh + o);
-            const float4 g = *reinterpret_cast<const float4*>(g_sh + o);
-            float4 m = *reinterpret_cast<const float4*>(m_sh + o);
-            float4 v = *reinterpret_cast<const float4*>(v_sh + o);
-            int j, e;
-            divmod_small(4 * f, rec, j, e);  // Gaussian j of the wave, its element e (a float4 stays in one record)
-            const float l0 = e < 3 ? lr.sh_dc : lr.sh_rest, l1 = e + 1 < 3 ? lr.sh_dc : lr.sh_rest;
-            const float l2 = e + 2 < 3 ? lr.sh_dc : lr.sh_rest;
-            adam1(p.x, m.x, v.x, g.x, l0, k);
-            adam1(p.y, m.y, v.y, g.y, l1, k);
-            adam1(p.z, m.z, v.z, g.z, l2, k);
-            adam1(p.w, m.w, v.w, g.w, lr.sh_rest, k);  // element e + 3 >= 3
-            *reinterpret_cast<float4*>(sh + o) = p;
-            *reinterpret_cast<float4*>(m_sh + o) = m;
-            *reinterpret_cast<float4*>(v_sh + o) = v;
-            atomicAdd(&s_norm[w][j], fmaf(g.x, g.x, fmaf(g.y, g.y, fmaf(g.z, g.z, g.w * g.w))));
+        for (int f0 = 0; 4 * f0 < total; f0 += 64) {
+            const int f = f0 + lane;
+            const bool valid = 4 * f < total;
+            int j = 0, e = 0;
+            float sq = 0.f;
+            if (valid) {
+                const size_t o = r0 + 4 * (size_t)f;
+                float4 p = *reinterpret_cast<const float4*>(sh + o);
+                const float4 g = *reinterpret_cast<const float4*>(g_sh + o);
+                float4 m = *reinterpret_cast<const float4*>(m_sh + o);
+                float4 v = *reinterpret_cast<const float4*>(v_sh + o);
+                divmod_small(4 * f, rec, j, e);  // Gaussian j of the wave, its element e (a float4 stays in one record)
+                const float l0 = e < 3 ? lr.sh_dc : lr.sh_rest, l1 = e + 1 < 3 ? lr.sh_dc : lr.sh_rest;
+                const float l2 = e + 2 < 3 ? lr.sh_dc : lr.sh_rest;
+                adam1(p.x, m.x, v.x, g.x, l0, k);
+                adam1(p.y, m.y, v.y, g.y, l1, k);
+                adam1(p.z, m.z, v.z, g.z, l2, k);
+                adam1(p.w, m.w, v.w, g.w, lr.sh_rest, k);  // element e + 3 >= 3
+                *reinterpret_cast<float4*>(sh + o) = p;
+                *reinterpret_cast<float4*>(m_sh + o) = m;
+                *reinterpret_cast<float4*>(v_sh + o) = v;
+                sq = fmaf(g.x, g.x, fmaf(g.y, g.y, fmaf(g.z, g.z, g.w * g.w)));
+            }
+            seg_add(s_norm[w], j, sq, valid);
         }
     } else {
-        for (int f = lane; f < total; f += 64) {
-            const size_t o = r0 + (size_t)f;
-            float p = sh[o], m = m_sh[o], v = v_sh[o];
-            const float g = g_sh[o];
-            int j, e;
-            divmod_small(f, rec, j, e);
-            adam1(p, m, v, g, e < 3 ? lr.sh_dc : lr.sh_rest, k);
-            sh[o] = p;
-            m_sh[o] = m;
-            v_sh[o] = v;
-            atomicAdd(&s_norm[w][j], g * g);
+        for (int f0 = 0; f0 < total; f0 += 64) {
+            const int f = f0 + lane;
+            const bool valid = f < total;
+            int j = 0, e = 0;
+            float sq = 0.f;
+            if (valid) {
+                const size_t o = r0 + (size_t)f;
+                float p = sh[o], m = m_sh[o], v = v_sh[o];
+                const float g = g_sh[o];
+                divmod_small(f, rec, j, e);
+                adam1(p, m, v, g, e < 3 ? lr.sh_dc : lr.sh_rest, k);
+                sh[o] = p;
+                m_sh[o] = m;
+                v_sh[o] = v;
+                sq = g * g;
+            }
+            seg_add(s_norm[w], j, sq, valid);
         }
     }
     wave_lds_sync();
