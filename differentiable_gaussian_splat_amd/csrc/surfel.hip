@@ -115,30 +115,41 @@ __global__ __launch_bounds__(64) void k_surfel_fwd(int W, int H, int TX, int nti
     const int px = tx * TILE + (lane & 15), py = ty * TILE + band * 4 + (lane >> 4);
     const double ox = (double)(tx * TILE) + 0.5, oy = (double)(ty * TILE) + 0.5;
     const float lx = (float)(lane & 15), ly = (float)(band * 4 + (lane >> 4));
-    float T = 1.f, C0 = 0.f, C1 = 0.f, C2 = 0.f, L = (px < W && py < H) ? 1.f : 0.f;
+    float T = 1.f, C0 = 0.f, C1 = 0.f, C2 = 0.f;
+    // an entry blends where alpha >= thr: ALPHA_MIN while the pixel walks, 2 (above any alpha) once it has
+    // stopped or lies outside the image
+    float thr = (px < W && py < H) ? ALPHA_MIN : 2.f;
     uint32_t last = 0u;
     const uint2 rg = ranges[tile];
     for (uint32_t bs = rg.x; bs < rg.y; bs += FWD_BATCH) {
-        if (!__any(L != 0.f)) break;
+        if (!__any(thr < 1.f)) break;
         const uint32_t idx = bs + lane;
         if (idx < rg.y) stage_surfel(values[idx], tf, rgb, s_rec[lane], ox, oy);
         __syncthreads();
         const int cnt = (int)min((uint32_t)FWD_BATCH, rg.y - bs);
-        for (int j = 0; j < cnt; ++j) {
-            if ((j & 7) == 0 && !__any(L != 0.f)) break;
-            SurfelHit e;
-            surfel_hit(s_rec[j], lx, ly, e);
-            const float al = fminf(ALPHA_MAX, e.oG);
-            float ae = (al >= ALPHA_MIN ? al : 0.f) * L;
-            const bool stop = __fmaf_rn(-ae, T, T) < T_MIN;
-            L = stop ? 0.f : L;
-            ae = stop ? 0.f : ae;
-            const float wt = ae * T;
-            C0 = fmaf(s_rec[j].d.x, wt, C0);
-            C1 = fmaf(s_rec[j].d.y, wt, C1);
-            C2 = fmaf(s_rec[j].d.z, wt, C2);
-            T = __fmaf_rn(-ae, T, T);
-            last = ae > 0.f ? bs - rg.x + 1 + (uint32_t)j : last;
+        const uint32_t pos0 = bs - rg.x + 1;
+        // entries in runs of 8 (unrolled, one exit test each), the walk test between runs
+        for (int j0 = 0; j0 < cnt; j0 += 8) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int j = j0 + m;
+                if (j >= cnt) break;
+                SurfelHit e;
+                surfel_hit(s_rec[j], lx, ly, e);
+                const float al = fminf(ALPHA_MAX, e.oG);
+                const bool pass = al >= thr;
+                const float Tn = __fmaf_rn(-al, T, T);
+                const bool stop = pass && Tn < T_MIN;  // the entry would end the pixel: not blended
+                const bool blend = pass && !stop;
+                thr = stop ? 2.f : thr;
+                const float wt = blend ? al * T : 0.f;
+                C0 = fmaf(s_rec[j].d.x, wt, C0);
+                C1 = fmaf(s_rec[j].d.y, wt, C1);
+                C2 = fmaf(s_rec[j].d.z, wt, C2);
+                T = blend ? Tn : T;
+                last = blend ? pos0 + (uint32_t)j : last;
+            }
+            if (!__any(thr < 1.f)) break;
         }
         __syncthreads();
     }
@@ -227,17 +238,23 @@ __global__ __launch_bounds__(64) void k_surfel_bwd(int W, int H, int TX, const u
             float acc[SURFEL_GRAD_STRIDE];
 #pragma unroll
             for (int c = 0; c < SURFEL_GRAD_STRIDE; ++c) acc[c] = 0.f;
-            bool any = false;
+            // every band's pixel through one branch-free pass: the blend tests first, one wave vote,
+            // then the gradient terms (a pixel that did not blend takes alpha = 0, which leaves T, S
+            // and every sum unchanged)
+            SurfelHit e[PPL];
+            float al[PPL];
+            bool bl[PPL], anyb = false;
 #pragma unroll
             for (int k = 0; k < PPL; ++k) {
-                if (pos >= band_last[k]) continue;  // past every blended entry of row band k
-                SurfelHit e;
-                surfel_hit(R, lx, ly[k], e);
-                const float al = fminf(ALPHA_MAX, e.oG);
-                const bool blended = pos < last[k] && al >= ALPHA_MIN;
-                if (!__any(blended)) continue;
-                any = true;
-                const float av = blended ? al : 0.f;
+                surfel_hit(R, lx, ly[k], e[k]);
+                al[k] = fminf(ALPHA_MAX, e[k].oG);
+                bl[k] = pos < last[k] && al[k] >= ALPHA_MIN;
+                anyb = anyb || bl[k];
+            }
+            if (!__any(anyb)) continue;
+#pragma unroll
+            for (int k = 0; k < PPL; ++k) {
+                const float av = bl[k] ? al[k] : 0.f;
                 T[k] = T[k] * __builtin_amdgcn_rcpf(1.0f - av);  // T in front of this entry
                 const float wt = av * T[k];
                 acc[0] = fmaf(wt, g0[k], acc[0]);
@@ -246,25 +263,24 @@ __global__ __launch_bounds__(64) void k_surfel_bwd(int W, int H, int TX, const u
                 const float cdl = fmaf(R.d.x, g0[k], fmaf(R.d.y, g1[k], R.d.z * g2[k]));
                 const float d = cdl - S[k];
                 S[k] = fmaf(av, d, S[k]);
-                const float h = e.oG <= ALPHA_MAX ? wt * d : 0.f;  // alpha dL/dalpha
+                const float h = e[k].oG <= ALPHA_MAX ? wt * d : 0.f;  // alpha dL/dalpha
                 acc[3] += h;
-                const float h3 = e.own ? h : 0.f, hf = e.own ? 0.f : h;
+                const float h3 = e[k].own ? h : 0.f, hf = e[k].own ? 0.f : h;
                 // dL/dk = h / k2 (-u, -v, u^2 + v^2) on the surfel's own branch
-                const float q = h3 * e.inv;
-                const float dk0 = -e.u * q, dk1 = -e.v * q, dk2 = e.own ? e.rho3 * q : 0.f;
+                const float q = h3 * e[k].inv;
+                const float dk0 = -e[k].u * q, dk1 = -e[k].v * q, dk2 = e[k].own ? e[k].rho3 * q : 0.f;
                 acc[4] += dk0;
                 acc[5] += dk1;
                 acc[6] += dk2;
-                acc[7] = fmaf(e.dx, dk0, acc[7]);
-                acc[8] = fmaf(e.dx, dk1, acc[8]);
-                acc[9] = fmaf(e.dx, dk2, acc[9]);
-                acc[10] = fmaf(e.dy, dk0, acc[10]);
-                acc[11] = fmaf(e.dy, dk1, acc[11]);
-                acc[12] = fmaf(e.dy, dk2, acc[12]);
-                acc[13] = fmaf(hf, e.dx, acc[13]);
-                acc[14] = fmaf(hf, e.dy, acc[14]);
+                acc[7] = fmaf(e[k].dx, dk0, acc[7]);
+                acc[8] = fmaf(e[k].dx, dk1, acc[8]);
+                acc[9] = fmaf(e[k].dx, dk2, acc[9]);
+                acc[10] = fmaf(e[k].dy, dk0, acc[10]);
+                acc[11] = fmaf(e[k].dy, dk1, acc[11]);
+                acc[12] = fmaf(e[k].dy, dk2, acc[12]);
+                acc[13] = fmaf(hf, e[k].dx, acc[13]);
+                acc[14] = fmaf(hf, e[k].dy, acc[14]);
             }
-            if (!any) continue;
             // per 16-lane row: values 0-7 and 8-15 by two reduce-scatters (lanes 0-7 hold them)
             const float ua = row_reduce_scatter8(acc, c1, c2, c3);
             const float ub = row_reduce_scatter8(acc + 8, c1, c2, c3);
