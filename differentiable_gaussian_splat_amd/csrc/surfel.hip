@@ -74,6 +74,62 @@ __device__ __forceinline__ void stage_surfel(uint32_t g, const float4* __restric
     s.d = make_float4(rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1], rgb[3 * (size_t)g + 2], 0.f);
 }
 
+// Whether some pixel centre of a rectangle [x_lo, x_hi] x [y_lo, y_hi] may
+// reach alpha >= 1/255 for this surfel (misses: certainly not) (M rows r0..r2 with o in r0.w and the
+// projected centre c in (r1.w, r2.w)). alpha >= 1/255 needs rho <= qthr =
+// 2 ln(255 o), so either the screen filter's 2 |pixel - c|^2 <= qthr, or the
+// ray's hit on the plane within u^2 + v^2 <= qthr: its screen image is the
+// conic with dual D = M diag(1, 1, -1/qthr) M^T, whose bounding box has, per
+// axis, the tangent lines t = (D_a2 +- sqrt(D_a2^2 - D_aa D_22)) / D_22 (in
+// double). qthr is enlarged by 0.1% + 1e-3 and the filter's bound shrunk by
+// 0.1%, far above the fp32 rounding of the per-pixel test, so a record this
+// skips is one the per-pixel test would skip too. A disc whose image is not a
+// bounded ellipse (D_22 >= 0: it reaches the camera plane) is never skipped.
+struct SurfelReach {
+    float qthr, cx, cy;
+    bool none;  // o below 1/255: no pixel reaches the threshold
+    bool box;   // the own branch's image is bounded by [x0, x1] x [y0, y1]
+    double x0, x1, y0, y1;
+    __device__ __forceinline__ SurfelReach(float4 r0, float4 r1, float4 r2) {
+        qthr = 1.3862943611198906f * (__builtin_amdgcn_logf(r0.w) + 7.9943534368588578f) * 1.001f + 1e-3f;
+        none = !(qthr > 0.f);
+        cx = r1.w;
+        cy = r2.w;
+        box = false;
+        x0 = x1 = y0 = y1 = 0.0;
+        if (none) return;
+        const double M[9] = {r0.x, r0.y, r0.z, r1.x, r1.y, r1.z, r2.x, r2.y, r2.z};
+        const double iq = 1.0 / (double)qthr;
+        auto dual = [&](int i, int j) {
+            return fma(M[3 * i], M[3 * j], fma(M[3 * i + 1], M[3 * j + 1], -M[3 * i + 2] * M[3 * j + 2] * iq));
+        };
+        const double D22 = dual(2, 2);
+        if (!(D22 < 0.0)) return;
+        double t[4];
+#pragma unroll
+        for (int ax = 0; ax < 2; ++ax) {
+            const double A = dual(ax, ax), B = dual(ax, 2);
+            const double disc = fma(B, B, -A * D22);
+            if (!(disc >= 0.0)) return;
+            const double sq = sqrt(disc);
+            t[2 * ax] = (B + sq) / D22;  // D22 < 0: the lower tangent
+            t[2 * ax + 1] = (B - sq) / D22;
+        }
+        box = true;
+        x0 = t[0] - 0.01;
+        x1 = t[1] + 0.01;
+        y0 = t[2] - 0.01;
+        y1 = t[3] + 0.01;
+    }
+    __device__ __forceinline__ bool misses(float x_lo, float x_hi, float y_lo, float y_hi) const {
+        if (none) return true;
+        const float ddx = fmaxf(0.f, fmaxf(x_lo - cx, cx - x_hi)), ddy = fmaxf(0.f, fmaxf(y_lo - cy, cy - y_hi));
+        if (2.f * (ddx * ddx + ddy * ddy) * 0.999f <= qthr) return false;  // the filter may reach the rectangle
+        if (!box) return false;
+        return x1 < (double)x_lo || x0 > (double)x_hi || y1 < (double)y_lo || y0 > (double)y_hi;
+    }
+};
+
 // One (pixel, surfel) evaluation at offset (lx, ly) from the tile's first
 // pixel centre; the forward and the backward call it on the same staged
 // values, so both take the same decisions bit for bit (contraction fixed).
@@ -120,20 +176,30 @@ __global__ __launch_bounds__(64) void k_surfel_fwd(int W, int H, int TX, int nti
     // stopped or lies outside the image
     float thr = (px < W && py < H) ? ALPHA_MIN : 2.f;
     uint32_t last = 0u;
+    // pixel-centre rectangle of the band
+    const float bx_lo = (float)(tx * TILE) + 0.5f, bx_hi = bx_lo + 15.f;
+    const float by_lo = (float)(ty * TILE + band * 4) + 0.5f, by_hi = by_lo + 3.f;
     const uint2 rg = ranges[tile];
     for (uint32_t bs = rg.x; bs < rg.y; bs += FWD_BATCH) {
         if (!__any(thr < 1.f)) break;
         const uint32_t idx = bs + lane;
-        if (idx < rg.y) stage_surfel(values[idx], tf, rgb, s_rec[lane], ox, oy);
+        bool miss = true;
+        if (idx < rg.y) {
+            const uint32_t g = values[idx];
+            stage_surfel(g, tf, rgb, s_rec[lane], ox, oy);
+            miss = SurfelReach(tf[3 * (size_t)g], tf[3 * (size_t)g + 1], tf[3 * (size_t)g + 2])
+                       .misses(bx_lo, bx_hi, by_lo, by_hi);
+        }
+        uint64_t todo = __ballot(!miss);  // records some pixel of the band may blend, in list order
         __syncthreads();
-        const int cnt = (int)min((uint32_t)FWD_BATCH, rg.y - bs);
         const uint32_t pos0 = bs - rg.x + 1;
         // entries in runs of 8 (unrolled, one exit test each), the walk test between runs
-        for (int j0 = 0; j0 < cnt; j0 += 8) {
+        while (todo) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
-                const int j = j0 + m;
-                if (j >= cnt) break;
+                if (!todo) break;
+                const int j = __builtin_ctzll(todo);
+                todo &= todo - 1ull;
                 SurfelHit e;
                 surfel_hit(s_rec[j], lx, ly, e);
                 const float al = fminf(ALPHA_MAX, e.oG);
@@ -222,17 +288,31 @@ __global__ __launch_bounds__(64) void k_surfel_bwd(int W, int H, int TX, const u
     }
     const uint2 rg = ranges[tile];
     const uint32_t maxlast = min(mylast, rg.y - rg.x);
+    // pixel-centre rectangle of the wave's first row band (band k lies 4 k rows lower)
+    const float bx_lo = (float)(tx * TILE) + 0.5f, bx_hi = bx_lo + 15.f;
+    const float by_lo = (float)(ty * TILE + band * 4 * PPL) + 0.5f;
     for (int hi = (int)maxlast; hi > 0; hi -= NB) {
         const int lo = max(0, hi - NB);
         const int cnt = hi - lo;
+        bool reach = false;  // some row band this wave walks past the entry may blend it
         if (lane < cnt) {
             const uint32_t gg = values[rg.x + lo + lane];
             stage_surfel(gg, tf, rgb, sh.rec[lane], ox, oy);
             sh.g[lane] = gg;
             sh.has[lane] = 0u;
+            const SurfelReach sr(tf[3 * (size_t)gg], tf[3 * (size_t)gg + 1], tf[3 * (size_t)gg + 2]);
+            const uint32_t pl = (uint32_t)(lo + lane);
+#pragma unroll
+            for (int k = 0; k < PPL; ++k) {
+                const float y0 = by_lo + (float)(4 * k);
+                reach = reach || (pl < band_last[k] && !sr.misses(bx_lo, bx_hi, y0, y0 + 3.f));
+            }
         }
+        uint64_t todo = __ballot(reach);
         __syncthreads();
-        for (int j = cnt - 1; j >= 0; --j) {
+        while (todo) {
+            const int j = 63 - __builtin_clzll(todo);  // backwards through the list
+            todo &= ~(1ull << j);
             const uint32_t pos = (uint32_t)(lo + j);
             const SurfelRec& R = sh.rec[j];
             float acc[SURFEL_GRAD_STRIDE];
