@@ -41,8 +41,9 @@ class Camera:
     t: np.ndarray  # (3,) float32
 
     def as_array(self) -> np.ndarray:
-        """18 doubles: W, H, fx, fy, cx, cy, R (row-major), t (exact fp32 values)."""
-        v = [self.width, self.height, self.fx, self.fy, self.cx, self.cy]
+        """18 doubles: W, H, fx, fy, cx, cy, R (row-major), t, the last 13 as the
+        fp32 values the rasterizer's camera holds (exactly)."""
+        v = [self.width, self.height] + [float(np.float32(x)) for x in (self.fx, self.fy, self.cx, self.cy)]
         v += [float(x) for x in np.asarray(self.R, np.float32).reshape(9)]
         v += [float(x) for x in np.asarray(self.t, np.float32).reshape(3)]
         return np.array(v, dtype=np.float64)

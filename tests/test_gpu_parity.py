@@ -143,11 +143,13 @@ def test_backward_parity_end_to_end(c, s, n):
 # ---------------------------------------------------------------- edge cases
 
 def _tiny_cam(W, H, rng=None):
+    """Intrinsics as fp32 values (the rasterizer's camera holds fp32; the oracle gets the same values)."""
     if rng is None:
         return Camera(W, H, 90.0, 90.0, W / 2, H / 2, np.eye(3, dtype=np.float32), np.zeros(3, np.float32))
     from scipy.spatial.transform import Rotation
     R = Rotation.random(random_state=rng).as_matrix().astype(np.float32)
-    return Camera(W, H, 90.0, 85.0, W / 2 + 0.3, H / 2 - 0.7, R, rng.normal(0, 0.3, 3).astype(np.float32))
+    f32 = lambda x: float(np.float32(x))
+    return Camera(W, H, 90.0, 85.0, f32(W / 2 + 0.3), f32(H / 2 - 0.7), R, rng.normal(0, 0.3, 3).astype(np.float32))
 
 
 def _scene_for(cam, n, rng, deg=1, big=0):

@@ -12,6 +12,7 @@ from differentiable_gaussian_splat_amd import raster
 from differentiable_gaussian_splat_amd.scenes import make_scene, surfel_scales
 from oracle import oracle as O
 from tests.gpu_helpers import rel_l2, to_dev
+from tests.test_gpu_parity import _scene_for, _tiny_cam
 
 pytestmark = pytest.mark.gpu
 
@@ -28,14 +29,14 @@ def surfel_grads(n, rows, dev):
     return dict(means=z(n, 3), scales=z(n, 2), quats=z(n, 4), opacities=z(n), sh=z(n, rows, 3))
 
 
-def run(sc, view=0):
+def run(sc, view=0, bg=(0.0, 0.0, 0.0)):
     dev = torch.device("cuda:0")
     s2 = surfel_scales(sc)
     pd = dict(means=to_dev(sc.means), scales=to_dev(s2), quats=to_dev(sc.quats), opacities=to_dev(sc.opacities),
               sh=to_dev(sc.sh))
     r = raster.Rasterizer(dev, want_keys=True)
     fr = r.surfel_forward(sc.cameras[view], pd["means"], pd["scales"], pd["quats"], pd["opacities"], pd["sh"],
-                          sc.sh_degree)
+                          sc.sh_degree, bg=bg)
     torch.cuda.synchronize()
     P = fr.n_pairs
     tf = fr.conic_opacity.cpu().numpy().reshape(-1, 3, 4)
@@ -75,7 +76,7 @@ def check_projection(sc, g, view=0):
     return o
 
 
-def check_frame(sc, r, pd, fr, g, view=0, end_to_end=True):
+def check_frame(sc, r, pd, fr, g, view=0, end_to_end=True, bg=(0.0, 0.0, 0.0)):
     cam = sc.cameras[view]
     W, H = cam.width, cam.height
     check_projection(sc, g, view)
@@ -85,10 +86,11 @@ def check_frame(sc, r, pd, fr, g, view=0, end_to_end=True):
     np.testing.assert_array_equal(g["keys"], keys)
     np.testing.assert_array_equal(g["ranges"], ranges)
     st = O.surfel_match_fwd(W, H, g["ranges"], g["values"], g["means2d"], g["M"], g["opac"], g["rgb"], g["image"],
-                            g["final_T"], g["n_contrib"], d_alpha=SURFEL_D_ALPHA)
+                            g["final_T"], g["n_contrib"], bg=bg, d_alpha=SURFEL_D_ALPHA)
     print(f"surfel forward: {st.size} pixels, {(st == 1).sum()} on another branch, {(st == 2).sum()} masked")
     if int((st == 3).sum()):
-        img, T, nc = O.surfel_render_fwd(W, H, g["ranges"], g["values"], g["means2d"], g["M"], g["opac"], g["rgb"])
+        img, T, nc = O.surfel_render_fwd(W, H, g["ranges"], g["values"], g["means2d"], g["M"], g["opac"], g["rgb"],
+                                         bg=bg)
         bad = np.argwhere(st == 3)[:6]
         detail = [(int(y), int(x), g["image"][:, y, x].tolist(), float(g["final_T"][y, x]), int(g["n_contrib"][y, x]),
                    img[:, y, x].tolist(), float(T[y, x]), int(nc[y, x])) for y, x in bad]
@@ -102,7 +104,8 @@ def check_frame(sc, r, pd, fr, g, view=0, end_to_end=True):
                                        fr.rgb, fr.final_T, fr.n_contrib, to_dev(dL), gsum)
     torch.cuda.synchronize()
     gs_ = gsum.cpu().numpy().astype(np.float64)
-    og = O.surfel_render_bwd(W, H, sc.n, g["ranges"], g["values"], g["means2d"], g["M"], g["opac"], g["rgb"], dL)
+    og = O.surfel_render_bwd(W, H, sc.n, g["ranges"], g["values"], g["means2d"], g["M"], g["opac"], g["rgb"], dL,
+                             bg=bg)
     assert np.all(gs_[:, 15] == 0)
     # the record holds sum h = sum alpha dL/dalpha; the oracle's dL/do is sum G dL/dalpha = that / o
     gs_[:, 3] = np.where(g["opac"] > 0, gs_[:, 3] / np.where(g["opac"] > 0, g["opac"], 1.0), 0.0)
@@ -141,13 +144,13 @@ def check_frame(sc, r, pd, fr, g, view=0, end_to_end=True):
         # up to 1.4e-3 in dL/dmeans on the 40k-Gaussian contention scene). The bar is 1e-3, or
         # 1.25 times that irreducible spread where it is larger.
         p = dict(means=sc.means, scales=g["s2"], quats=sc.quats, opacities=sc.opacities, sh=sc.sh)
-        f = O.surfel_forward(p, cam, sc.sh_degree)
-        b = O.surfel_backward(p, cam, sc.sh_degree, f, dL)
+        f = O.surfel_forward(p, cam, sc.sh_degree, bg=bg)
+        b = O.surfel_backward(p, cam, sc.sh_degree, f, dL, bg=bg)
         pre = f["pre"]
         r32 = lambda a: a.astype(np.float32).astype(np.float64)
         k32, v32, rg32 = O.bin_sort(r32(pre["means2d"]), pre["radii"], pre["depth"].astype(np.float32), W, H)
         s32 = O.surfel_render_bwd(W, H, sc.n, rg32, v32, r32(pre["means2d"]), r32(pre["tf"]),
-                                  sc.opacities.astype(np.float64), r32(pre["rgb"]), dL)
+                                  sc.opacities.astype(np.float64), r32(pre["rgb"]), dL, bg=bg)
         b32 = O.surfel_preprocess_bwd(sc.means, g["s2"], sc.quats, sc.opacities, sc.sh, cam, sc.sh_degree, s32)
         for k in ("means", "scales", "quats", "opacities", "sh"):
             e, floor = rel_l2(gg[k], b[k]), rel_l2(b32[k], b[k])
@@ -208,3 +211,56 @@ def test_surfel_full_frame_contention_scene():
     r, pd, fr, g = run(sc)
     check_frame(sc, r, pd, fr, g, end_to_end=False)
     print(f"surfels at 1080p: pairs {g['P']}, drawn {(g['radii'] > 0).sum()}")
+
+
+def test_surfel_ragged_image_rotated_camera_and_background():
+    """A 100x70 image (ragged tiles on both axes) under a rotated, translated
+    camera, a coloured background and SH degree 2: binning bit for bit, every
+    pixel through the matcher, the pixel sums and the gradients, stage-wise
+    and end to end, with that background."""
+    rng = np.random.default_rng(13)
+    sc = _scene_for(_tiny_cam(100, 70, rng), 300, rng, deg=2)
+    bg = (0.2, 0.5, 0.9)
+    r, pd, fr, g = run(sc, bg=bg)
+    assert g["P"] > 0
+    check_frame(sc, r, pd, fr, g, bg=bg)
+
+
+def test_surfel_empty_and_fully_culled_scenes():
+    """No surfel, or every surfel behind the camera: no pairs, the image is the
+    background, T = 1, n_contrib = 0, and the backward writes zeros."""
+    rng = np.random.default_rng(14)
+    cam = _tiny_cam(64, 48)
+    bg = (0.1, 0.2, 0.3)
+    for n in (0, 50):
+        sc = _scene_for(cam, n, rng)
+        if n:
+            sc.means[:, 2] = -5.0  # behind the camera
+        r, pd, fr, g = run(sc, bg=bg)
+        assert fr.n_pairs == 0 and np.all(g["radii"] == 0)
+        for ch, b in enumerate(bg):
+            assert np.all(g["image"][ch] == np.float32(b))
+        assert np.all(g["final_T"] == 1.0) and np.all(g["n_contrib"] == 0)
+        grads = surfel_grads(n, sc.sh.shape[1], pd["means"].device)
+        r.surfel_backward(fr, pd["means"], pd["scales"], pd["quats"], pd["sh"], to_dev(sc.dL_dimage[0]), grads)
+        torch.cuda.synchronize()
+        for k, v in grads.items():
+            assert torch.all(v == 0), k
+
+
+def test_surfel_non_finite_inputs_are_culled():
+    """A surfel with a NaN or infinite mean, scale, opacity or SH coefficient, or
+    a zero quaternion, is culled (as by the oracle), and the frame around it is
+    unchanged."""
+    rng = np.random.default_rng(15)
+    sc = _scene_for(_tiny_cam(64, 64), 100, rng)
+    sc.means[0, 0] = np.nan
+    sc.scales[1, 1] = np.inf
+    sc.quats[2] = 0.0
+    sc.opacities[3] = np.nan
+    sc.sh[4, 1, 2] = np.inf
+    r, pd, fr, g = run(sc)
+    assert np.all(g["radii"][:5] == 0)
+    o = O.surfel_preprocess(sc.means, g["s2"], sc.quats, sc.opacities, sc.sh, sc.cameras[0], sc.sh_degree)
+    assert np.all(o["radii"][:5] == 0)
+    check_frame(sc, r, pd, fr, g, end_to_end=False)

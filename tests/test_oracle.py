@@ -23,9 +23,12 @@ T_MIN = float(np.float32(1e-4))
 
 
 def cam_of(W, H, f, cx, cy, R=None, t=None, fy=None):
+    """A camera whose intrinsics, rotation and translation are fp32 values, as the rasterizer's camera
+    holds them (the oracle receives exactly those)."""
     R = np.eye(3, dtype=np.float32) if R is None else np.asarray(R, np.float32)
     t = np.zeros(3, np.float32) if t is None else np.asarray(t, np.float32)
-    return Camera(W, H, float(f), float(f if fy is None else fy), float(cx), float(cy), R, t)
+    f32 = lambda x: float(np.float32(x))
+    return Camera(W, H, f32(f), f32(f if fy is None else fy), f32(cx), f32(cy), R, t)
 
 
 def world_of(cam, xc):
