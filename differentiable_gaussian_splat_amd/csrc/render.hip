@@ -98,17 +98,17 @@ __device__ __forceinline__ bool band_misses(float u, float v, float4 c, float lo
 struct alignas(16) RowStaged {
     float4 k;       // (a2, r, g, b)
     float2 row[4];  // (wrow, et) per row
+    uint32_t pos;   // the entry's position in the tile's list, counted from 1
 };
 
-// Stages record `lane` of a batch for the 4 rows ly = y0 .. y0 + 3 of a band
-// (ly counted from the tile's first row); w0 and dy0, w and dy at the tile's
-// first pixel centre (ox, oy), are formed in double and rounded once. Returns
-// whether the record misses the band (see band_misses).
-__device__ __forceinline__ bool stage_record_rows(uint32_t g, const float2* __restrict__ means2d,
-                                                  const float4* __restrict__ conic_op,
-                                                  const float* __restrict__ rgb, RowStaged* s_rec, int lane,
-                                                  double ox, double oy, float y0, float x_lo, float x_hi,
-                                                  float y_lo, float y_hi) {
+// Forms the staged record of Gaussian g for the 4 rows ly = y0 .. y0 + 3 of a
+// band (ly counted from the tile's first row); w0 and dy0, w and dy at the
+// tile's first pixel centre (ox, oy), are formed in double and rounded once.
+// Returns whether the record misses the band (see band_misses).
+__device__ __forceinline__ bool form_record_rows(uint32_t g, const float2* __restrict__ means2d,
+                                                 const float4* __restrict__ conic_op,
+                                                 const float* __restrict__ rgb, RowStaged& rec, double ox, double oy,
+                                                 float y0, float x_lo, float x_hi, float y_lo, float y_hi) {
     const float2 m = means2d[g];
     const float4 c = conic_op[g];
     const float4 k = falloff_consts(c);
@@ -126,9 +126,9 @@ __device__ __forceinline__ bool stage_record_rows(uint32_t g, const float2* __re
             const float gdy = k.z * dy;
             et = __fmaf_rn(gdy, dy, k.w);
         }
-        s_rec[lane].row[i] = make_float2(wrow, et);
+        rec.row[i] = make_float2(wrow, et);
     }
-    s_rec[lane].k = make_float4(k.x, r, gg, bb);
+    rec.k = make_float4(k.x, r, gg, bb);
     return band_misses(m.x, m.y, c, k.w, x_lo, x_hi, y_lo, y_hi);
 }
 
@@ -244,21 +244,34 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
         set_walk_priority(bs - rg.x);  // a wave still walking deep into its list is a heavy one
         const uint32_t idx = bs + lane;
         bool miss = true;
+        RowStaged rec;
         if (idx < rg.y)
-            miss = stage_record_rows(values[idx], means2d, conic_op, rgb, s_rec, lane, ox, oy, (float)(band * 4),
-                                     bx_lo, bx_hi, by_lo, by_hi);
-        uint64_t todo = __ballot(!miss);  // records some pixel of the band may blend, in list order
+            miss = form_record_rows(values[idx], means2d, conic_op, rgb, rec, ox, oy, (float)(band * 4), bx_lo,
+                                    bx_hi, by_lo, by_hi);
+        // the records some pixel of the band may blend, packed in list order: the walk below then reads
+        // consecutive slots at fixed offsets from one base per run, with each entry's list position
+        // (counted from 1) beside it
+        const uint64_t keep = __ballot(!miss);
+        const int cnt = __popcll(keep);
+        if (!miss) {
+            const int slot = __builtin_amdgcn_mbcnt_hi((uint32_t)(keep >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)keep, 0u));
+            rec.pos = bs - rg.x + 1 + (uint32_t)lane;
+            s_rec[slot] = rec;
+        }
         __syncthreads();
-        const uint32_t pos0 = bs - rg.x + 1;
         // entries in runs of 8 (unrolled, one exit test each), the band's walk checked between runs
-        while (todo) {
+        for (int m0 = 0; m0 < cnt; m0 += 8) {
+            // the run's base offset is held in a vector register (opaque to the compiler), so that every
+            // read of the run addresses from it with a constant offset instead of re-forming it per entry
+            uint32_t run_off = (uint32_t)m0 * (uint32_t)sizeof(RowStaged);
+            asm volatile("" : "+v"(run_off));
+            const RowStaged* run = reinterpret_cast<const RowStaged*>(reinterpret_cast<const char*>(s_rec) + run_off);
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
-                if (!todo) break;
-                const int j = __builtin_ctzll(todo);
-                todo &= todo - 1ull;
-                const float4 K = s_rec[j].k;
-                const float2 R = s_rec[j].row[row];
+                if (m0 + m >= cnt) break;
+                const float4 K = run[m].k;
+                const float2 R = run[m].row[row];
+                const uint32_t pos = run[m].pos;
                 float q;
                 {
 #pragma clang fp contract(off)
@@ -280,7 +293,8 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
                 C1 = fmaf(K.z, wt, C1);
                 C2 = fmaf(K.w, wt, C2);
                 T = blend ? Tn : T;
-                last = blend ? pos0 + (uint32_t)j : last;
+                last = blend ? pos : last;
+                asm volatile("" : "+v"(last) : "v"(pos));  // pos is read with the record, not under the blend mask
             }
             if (!walking()) break;
         }
