@@ -43,7 +43,8 @@ namespace {
 constexpr int FWD_BATCH = 64;
 constexpr int BWD_BATCH = 32;
 
-// (Kc, N12.x), (N12.y, N12.z, N02.x, N02.y), (N02.z, dx0, dy0, log2 o), (rgb, -),
+// (Kc, N12.x), (N12.y, N12.z, N02.x, N02.y), (N02.z, dx0, dy0, log2 o), (rgb, -; the
+// forward keeps the entry's list position there),
 // (dx0, dy0) = (ox, oy) - c at the tile's first pixel centre (ox, oy)
 struct alignas(16) SurfelRec {
     float4 a, b, c, d;
@@ -184,24 +185,34 @@ __global__ __launch_bounds__(64) void k_surfel_fwd(int W, int H, int TX, int nti
         if (!__any(thr < 1.f)) break;
         const uint32_t idx = bs + lane;
         bool miss = true;
+        SurfelRec rec;
         if (idx < rg.y) {
             const uint32_t g = values[idx];
-            stage_surfel(g, tf, rgb, s_rec[lane], ox, oy);
+            stage_surfel(g, tf, rgb, rec, ox, oy);
             miss = SurfelReach(tf[3 * (size_t)g], tf[3 * (size_t)g + 1], tf[3 * (size_t)g + 2])
                        .misses(bx_lo, bx_hi, by_lo, by_hi);
         }
-        uint64_t todo = __ballot(!miss);  // records some pixel of the band may blend, in list order
+        // the records some pixel of the band may blend, packed in list order, each with its list position
+        // (counted from 1) in its last word: the walk reads each run of eight at constant offsets from one base
+        const uint64_t keep = __ballot(!miss);
+        const int cnt = __popcll(keep);
+        if (!miss) {
+            rec.d.w = __uint_as_float(bs - rg.x + 1 + (uint32_t)lane);
+            s_rec[__builtin_amdgcn_mbcnt_hi((uint32_t)(keep >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)keep, 0u))] =
+                rec;
+        }
         __syncthreads();
-        const uint32_t pos0 = bs - rg.x + 1;
         // entries in runs of 8 (unrolled, one exit test each), the walk test between runs
-        while (todo) {
+        for (int m0 = 0; m0 < cnt; m0 += 8) {
+            uint32_t run_off = (uint32_t)m0 * (uint32_t)sizeof(SurfelRec);
+            asm volatile("" : "+v"(run_off));  // one base register per run (opaque to the compiler)
+            const SurfelRec* run = reinterpret_cast<const SurfelRec*>(reinterpret_cast<const char*>(s_rec) + run_off);
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
-                if (!todo) break;
-                const int j = __builtin_ctzll(todo);
-                todo &= todo - 1ull;
+                if (m0 + m >= cnt) break;
                 SurfelHit e;
-                surfel_hit(s_rec[j], lx, ly, e);
+                surfel_hit(run[m], lx, ly, e);
+                const float4 D = run[m].d;
                 const float al = fminf(ALPHA_MAX, e.oG);
                 const bool pass = al >= thr;
                 const float Tn = __fmaf_rn(-al, T, T);
@@ -209,11 +220,11 @@ __global__ __launch_bounds__(64) void k_surfel_fwd(int W, int H, int TX, int nti
                 const bool blend = pass && !stop;
                 thr = stop ? 2.f : thr;
                 const float wt = blend ? al * T : 0.f;
-                C0 = fmaf(s_rec[j].d.x, wt, C0);
-                C1 = fmaf(s_rec[j].d.y, wt, C1);
-                C2 = fmaf(s_rec[j].d.z, wt, C2);
+                C0 = fmaf(D.x, wt, C0);
+                C1 = fmaf(D.y, wt, C1);
+                C2 = fmaf(D.z, wt, C2);
                 T = blend ? Tn : T;
-                last = blend ? pos0 + (uint32_t)j : last;
+                last = blend ? __float_as_uint(D.w) : last;
             }
             if (!__any(thr < 1.f)) break;
         }
