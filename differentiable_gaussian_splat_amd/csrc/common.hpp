@@ -13,6 +13,9 @@ namespace gs {
 
 constexpr int TILE = 16;             // tile edge in pixels
 constexpr float ALPHA_MAX = 0.99f;   // alpha = min(0.99, o G)
+// At or below this opacity, o G (formed as exp2 of an exponent at most log2 o, each step a few ulps
+// off) stays far below ALPHA_MAX, so the clamp's min and test can be left out exactly.
+constexpr float CLAMP_FREE_OPACITY = 0.989f;
 constexpr float ALPHA_MIN = 1.0f / 255.0f;  // entries below are skipped
 constexpr float T_MIN = 1e-4f;       // a pixel stops before T would drop below
 constexpr float BIG = 16777216.0f;   // 2^24: beyond this fp32 no longer resolves pixels

@@ -104,11 +104,13 @@ struct alignas(16) RowStaged {
 // Forms the staged record of Gaussian g for the 4 rows ly = y0 .. y0 + 3 of a
 // band (ly counted from the tile's first row); w0 and dy0, w and dy at the
 // tile's first pixel centre (ox, oy), are formed in double and rounded once.
-// Returns whether the record misses the band (see band_misses).
+// Returns whether the record misses the band (see band_misses); clamp tells
+// whether its alpha may reach the 0.99 clamp.
 __device__ __forceinline__ bool form_record_rows(uint32_t g, const float2* __restrict__ means2d,
                                                  const float4* __restrict__ conic_op,
-                                                 const float* __restrict__ rgb, RowStaged& rec, double ox, double oy,
-                                                 float y0, float x_lo, float x_hi, float y_lo, float y_hi) {
+                                                 const float* __restrict__ rgb, RowStaged& rec, bool& clamp,
+                                                 double ox, double oy, float y0, float x_lo, float x_hi, float y_lo,
+                                                 float y_hi) {
     const float2 m = means2d[g];
     const float4 c = conic_op[g];
     const float4 k = falloff_consts(c);
@@ -129,6 +131,7 @@ __device__ __forceinline__ bool form_record_rows(uint32_t g, const float2* __res
         rec.row[i] = make_float2(wrow, et);
     }
     rec.k = make_float4(k.x, r, gg, bb);
+    clamp = c.w > CLAMP_FREE_OPACITY;
     return band_misses(m.x, m.y, c, k.w, x_lo, x_hi, y_lo, y_hi);
 }
 
@@ -165,8 +168,8 @@ __device__ __forceinline__ uint32_t stage_record_bands(uint32_t g, uint32_t pos,
 // column strips (strip s = columns [4 s, 4 s + 4) of the tile, all 16 rows;
 // the wave's k-th strip is s = strip0 + k) the record may reach; bit k is also
 // clear when the record lies at or past every blended entry of strip k
-// (pos >= strip_last[k]). Bit 4 is set when the record's opacity exceeds 0.99,
-// so that its alpha may sit at the clamp; below, alpha = o G never reaches it.
+// (pos >= strip_last[k]). Bit 4 is set when the record's alpha may sit at the
+// clamp (opacity above CLAMP_FREE_OPACITY); below, alpha = o G never reaches it.
 template <int PPL>
 __device__ __forceinline__ uint32_t stage_record_strips(uint32_t g, uint32_t pos, const uint32_t* strip_last,
                                                         const float2* __restrict__ means2d,
@@ -183,7 +186,7 @@ __device__ __forceinline__ uint32_t stage_record_strips(uint32_t g, uint32_t pos
     s_rec[lane].b = make_float4(k.z, k.w, rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1]);
     s_rec[lane].c.x = rgb[3 * (size_t)g + 2];
     const MissTest mt(c, k.w);
-    uint32_t mask = c.w > ALPHA_MAX ? 16u : 0u;
+    uint32_t mask = c.w > CLAMP_FREE_OPACITY ? 16u : 0u;
 #pragma unroll
     for (int b = 0; b < PPL; ++b) {
         const float x0 = x_lo + 4.f * (float)(strip0 + b);
@@ -243,11 +246,11 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
         if (!walking()) break;
         set_walk_priority(bs - rg.x);  // a wave still walking deep into its list is a heavy one
         const uint32_t idx = bs + lane;
-        bool miss = true;
+        bool miss = true, clamp = false;
         RowStaged rec;
         if (idx < rg.y)
-            miss = form_record_rows(values[idx], means2d, conic_op, rgb, rec, ox, oy, (float)(band * 4), bx_lo,
-                                    bx_hi, by_lo, by_hi);
+            miss = form_record_rows(values[idx], means2d, conic_op, rgb, rec, clamp, ox, oy, (float)(band * 4),
+                                    bx_lo, bx_hi, by_lo, by_hi);
         // the records some pixel of the band may blend, packed in list order: the walk below then reads
         // consecutive slots at fixed offsets from one base per run, with each entry's list position
         // (counted from 1) beside it
@@ -259,45 +262,52 @@ __global__ __launch_bounds__(64) void k_render_fwd(int W, int H, int TX, int TY,
             s_rec[slot] = rec;
         }
         __syncthreads();
-        // entries in runs of 8 (unrolled, one exit test each), the band's walk checked between runs
-        for (int m0 = 0; m0 < cnt; m0 += 8) {
-            // the run's base offset is held in a vector register (opaque to the compiler), so that every
-            // read of the run addresses from it with a constant offset instead of re-forming it per entry
-            uint32_t run_off = (uint32_t)m0 * (uint32_t)sizeof(RowStaged);
-            asm volatile("" : "+v"(run_off));
-            const RowStaged* run = reinterpret_cast<const RowStaged*>(reinterpret_cast<const char*>(s_rec) + run_off);
+        // entries in runs of 8 (unrolled, one exit test each), the band's walk checked between runs; a batch
+        // none of whose records can reach the alpha clamp takes a copy without the clamp's min
+        auto walk_runs = [&](auto clamp_tag) {
+            constexpr bool CLAMP = decltype(clamp_tag)::value;
+            for (int m0 = 0; m0 < cnt; m0 += 8) {
+                // the run's base offset is held in a vector register (opaque to the compiler), so that every
+                // read of the run addresses from it with a constant offset instead of re-forming it per entry
+                uint32_t run_off = (uint32_t)m0 * (uint32_t)sizeof(RowStaged);
+                asm volatile("" : "+v"(run_off));
+                const RowStaged* run =
+                    reinterpret_cast<const RowStaged*>(reinterpret_cast<const char*>(s_rec) + run_off);
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                if (m0 + m >= cnt) break;
-                const float4 K = run[m].k;
-                const float2 R = run[m].row[row];
-                const uint32_t pos = run[m].pos;
-                float q;
-                {
+                for (int m = 0; m < 8; ++m) {
+                    if (m0 + m >= cnt) break;
+                    const float4 K = run[m].k;
+                    const float2 R = run[m].row[row];
+                    const uint32_t pos = run[m].pos;
+                    float q;
+                    {
 #pragma clang fp contract(off)
-                    const float w = R.x + lx;
-                    const float aw = K.x * w;
-                    q = __fmaf_rn(aw, w, R.y);
+                        const float w = R.x + lx;
+                        const float aw = K.x * w;
+                        q = __fmaf_rn(aw, w, R.y);
+                    }
+                    const float oG = __builtin_amdgcn_exp2f(q);
+                    const float al = CLAMP ? fminf(ALPHA_MAX, oG) : oG;
+                    // the entry passes the alpha test; it blends unless it would take T below T_MIN, which
+                    // ends the pixel instead
+                    const bool pass = al >= thr;
+                    const float Tn = __fmaf_rn(-al, T, T);
+                    const bool stop = pass && Tn < T_MIN;
+                    const bool blend = pass && !stop;
+                    thr = stop ? 2.f : thr;
+                    const float wt = blend ? al * T : 0.f;
+                    C0 = fmaf(K.y, wt, C0);
+                    C1 = fmaf(K.z, wt, C1);
+                    C2 = fmaf(K.w, wt, C2);
+                    T = blend ? Tn : T;
+                    last = blend ? pos : last;
+                    asm volatile("" : "+v"(last) : "v"(pos));  // pos is read with the record, not under the mask
                 }
-                const float oG = __builtin_amdgcn_exp2f(q);
-                const float al = fminf(ALPHA_MAX, oG);
-                // the entry passes the alpha test; it blends unless it would take T below T_MIN, which
-                // ends the pixel instead
-                const bool pass = al >= thr;
-                const float Tn = __fmaf_rn(-al, T, T);
-                const bool stop = pass && Tn < T_MIN;
-                const bool blend = pass && !stop;
-                thr = stop ? 2.f : thr;
-                const float wt = blend ? al * T : 0.f;
-                C0 = fmaf(K.y, wt, C0);
-                C1 = fmaf(K.z, wt, C1);
-                C2 = fmaf(K.w, wt, C2);
-                T = blend ? Tn : T;
-                last = blend ? pos : last;
-                asm volatile("" : "+v"(last) : "v"(pos));  // pos is read with the record, not under the blend mask
+                if (!walking()) break;
             }
-            if (!walking()) break;
-        }
+        };
+        if (__ballot(!miss && clamp)) walk_runs(std::true_type{});
+        else walk_runs(std::false_type{});
         __syncthreads();
         if (ckpt) {
             // the state after a whole batch that ends a checkpoint interval, while still walking
