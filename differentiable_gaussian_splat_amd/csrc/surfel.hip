@@ -33,6 +33,8 @@
 // in the backward one wave per tile (four pixels per lane) or, on small grids,
 // one per band, with the per-entry sums reduced over each 16-lane row by DPP
 // before one atomic add per value per (tile or band, surfel).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -56,8 +58,9 @@ __device__ __forceinline__ void cross_d(const double p[3], const double q[3], do
     o[2] = fma(p[0], q[1], -p[1] * q[0]);
 }
 
-__device__ __forceinline__ void stage_surfel(uint32_t g, const float4* __restrict__ tf, const float* __restrict__ rgb,
-                                             SurfelRec& s, double ox, double oy) {
+// Returns the surfel's opacity.
+__device__ __forceinline__ float stage_surfel(uint32_t g, const float4* __restrict__ tf, const float* __restrict__ rgb,
+                                              SurfelRec& s, double ox, double oy) {
     const float4 r0 = tf[3 * (size_t)g], r1 = tf[3 * (size_t)g + 1], r2 = tf[3 * (size_t)g + 2];
     const double M0[3] = {r0.x, r0.y, r0.z}, M1[3] = {r1.x, r1.y, r1.z}, M2[3] = {r2.x, r2.y, r2.z};
     double N01[3], N12[3], N02[3];
@@ -73,6 +76,7 @@ __device__ __forceinline__ void stage_surfel(uint32_t g, const float4* __restric
     s.c = make_float4((float)N02[2], (float)(ox - (double)r1.w), (float)(oy - (double)r2.w),
                       __builtin_amdgcn_logf(r0.w));
     s.d = make_float4(rgb[3 * (size_t)g], rgb[3 * (size_t)g + 1], rgb[3 * (size_t)g + 2], 0.f);
+    return r0.w;
 }
 
 // Whether some pixel centre of a rectangle [x_lo, x_hi] x [y_lo, y_hi] may
@@ -306,9 +310,10 @@ __global__ __launch_bounds__(64) void k_surfel_bwd(int W, int H, int TX, const u
         const int lo = max(0, hi - NB);
         const int cnt = hi - lo;
         bool reach = false;  // some row band this wave walks past the entry may blend it
+        bool clamp = false;  // its alpha may reach the 0.99 clamp
         if (lane < cnt) {
             const uint32_t gg = values[rg.x + lo + lane];
-            stage_surfel(gg, tf, rgb, sh.rec[lane], ox, oy);
+            clamp = stage_surfel(gg, tf, rgb, sh.rec[lane], ox, oy) > CLAMP_FREE_OPACITY;
             sh.g[lane] = gg;
             sh.has[lane] = 0u;
             const SurfelReach sr(tf[3 * (size_t)gg], tf[3 * (size_t)gg + 1], tf[3 * (size_t)gg + 2]);
@@ -320,67 +325,75 @@ __global__ __launch_bounds__(64) void k_surfel_bwd(int W, int H, int TX, const u
             }
         }
         uint64_t todo = __ballot(reach);
+        const bool clamp_batch = __ballot(reach && clamp) != 0ull;
         __syncthreads();
-        while (todo) {
-            const int j = 63 - __builtin_clzll(todo);  // backwards through the list
-            todo &= ~(1ull << j);
-            const uint32_t pos = (uint32_t)(lo + j);
-            const SurfelRec& R = sh.rec[j];
-            float acc[SURFEL_GRAD_STRIDE];
+        // a batch none of whose walked records can reach the alpha clamp (rho >= 0: o G <= o) takes a copy
+        // without the clamp's min and test
+        auto walk_entries = [&](auto clamp_tag) {
+            constexpr bool CLAMP = decltype(clamp_tag)::value;
+            while (todo) {
+                const int j = 63 - __builtin_clzll(todo);  // backwards through the list
+                todo &= ~(1ull << j);
+                const uint32_t pos = (uint32_t)(lo + j);
+                const SurfelRec& R = sh.rec[j];
+                float acc[SURFEL_GRAD_STRIDE];
 #pragma unroll
-            for (int c = 0; c < SURFEL_GRAD_STRIDE; ++c) acc[c] = 0.f;
-            // every band's pixel through one branch-free pass: the blend tests first, one wave vote,
-            // then the gradient terms (a pixel that did not blend takes alpha = 0, which leaves T, S
-            // and every sum unchanged)
-            SurfelHit e[PPL];
-            float al[PPL];
-            bool bl[PPL], anyb = false;
+                for (int c = 0; c < SURFEL_GRAD_STRIDE; ++c) acc[c] = 0.f;
+                // every band's pixel through one branch-free pass: the blend tests first, one wave vote,
+                // then the gradient terms (a pixel that did not blend takes alpha = 0, which leaves T, S
+                // and every sum unchanged)
+                SurfelHit e[PPL];
+                float al[PPL];
+                bool bl[PPL], anyb = false;
 #pragma unroll
-            for (int k = 0; k < PPL; ++k) {
-                surfel_hit(R, lx, ly[k], e[k]);
-                al[k] = fminf(ALPHA_MAX, e[k].oG);
-                bl[k] = pos < last[k] && al[k] >= ALPHA_MIN;
-                anyb = anyb || bl[k];
-            }
-            if (!__any(anyb)) continue;
+                for (int k = 0; k < PPL; ++k) {
+                    surfel_hit(R, lx, ly[k], e[k]);
+                    al[k] = CLAMP ? fminf(ALPHA_MAX, e[k].oG) : e[k].oG;
+                    bl[k] = pos < last[k] && al[k] >= ALPHA_MIN;
+                    anyb = anyb || bl[k];
+                }
+                if (!__any(anyb)) continue;
 #pragma unroll
-            for (int k = 0; k < PPL; ++k) {
-                const float av = bl[k] ? al[k] : 0.f;
-                T[k] = T[k] * __builtin_amdgcn_rcpf(1.0f - av);  // T in front of this entry
-                const float wt = av * T[k];
-                acc[0] = fmaf(wt, g0[k], acc[0]);
-                acc[1] = fmaf(wt, g1[k], acc[1]);
-                acc[2] = fmaf(wt, g2[k], acc[2]);
-                const float cdl = fmaf(R.d.x, g0[k], fmaf(R.d.y, g1[k], R.d.z * g2[k]));
-                const float d = cdl - S[k];
-                S[k] = fmaf(av, d, S[k]);
-                const float h = e[k].oG <= ALPHA_MAX ? wt * d : 0.f;  // alpha dL/dalpha
-                acc[3] += h;
-                const float h3 = e[k].own ? h : 0.f, hf = e[k].own ? 0.f : h;
-                // dL/dk = h / k2 (-u, -v, u^2 + v^2) on the surfel's own branch
-                const float q = h3 * e[k].inv;
-                const float dk0 = -e[k].u * q, dk1 = -e[k].v * q, dk2 = e[k].own ? e[k].rho3 * q : 0.f;
-                acc[4] += dk0;
-                acc[5] += dk1;
-                acc[6] += dk2;
-                acc[7] = fmaf(e[k].dx, dk0, acc[7]);
-                acc[8] = fmaf(e[k].dx, dk1, acc[8]);
-                acc[9] = fmaf(e[k].dx, dk2, acc[9]);
-                acc[10] = fmaf(e[k].dy, dk0, acc[10]);
-                acc[11] = fmaf(e[k].dy, dk1, acc[11]);
-                acc[12] = fmaf(e[k].dy, dk2, acc[12]);
-                acc[13] = fmaf(hf, e[k].dx, acc[13]);
-                acc[14] = fmaf(hf, e[k].dy, acc[14]);
+                for (int k = 0; k < PPL; ++k) {
+                    const float av = bl[k] ? al[k] : 0.f;
+                    T[k] = T[k] * __builtin_amdgcn_rcpf(1.0f - av);  // T in front of this entry
+                    const float wt = av * T[k];
+                    acc[0] = fmaf(wt, g0[k], acc[0]);
+                    acc[1] = fmaf(wt, g1[k], acc[1]);
+                    acc[2] = fmaf(wt, g2[k], acc[2]);
+                    const float cdl = fmaf(R.d.x, g0[k], fmaf(R.d.y, g1[k], R.d.z * g2[k]));
+                    const float d = cdl - S[k];
+                    S[k] = fmaf(av, d, S[k]);
+                    const float h = (!CLAMP || e[k].oG <= ALPHA_MAX) ? wt * d : 0.f;  // alpha dL/dalpha
+                    acc[3] += h;
+                    const float h3 = e[k].own ? h : 0.f, hf = e[k].own ? 0.f : h;
+                    // dL/dk = h / k2 (-u, -v, u^2 + v^2) on the surfel's own branch
+                    const float q = h3 * e[k].inv;
+                    const float dk0 = -e[k].u * q, dk1 = -e[k].v * q, dk2 = e[k].own ? e[k].rho3 * q : 0.f;
+                    acc[4] += dk0;
+                    acc[5] += dk1;
+                    acc[6] += dk2;
+                    acc[7] = fmaf(e[k].dx, dk0, acc[7]);
+                    acc[8] = fmaf(e[k].dx, dk1, acc[8]);
+                    acc[9] = fmaf(e[k].dx, dk2, acc[9]);
+                    acc[10] = fmaf(e[k].dy, dk0, acc[10]);
+                    acc[11] = fmaf(e[k].dy, dk1, acc[11]);
+                    acc[12] = fmaf(e[k].dy, dk2, acc[12]);
+                    acc[13] = fmaf(hf, e[k].dx, acc[13]);
+                    acc[14] = fmaf(hf, e[k].dy, acc[14]);
+                }
+                // per 16-lane row: values 0-7 and 8-15 by two reduce-scatters (lanes 0-7 hold them)
+                const float ua = row_reduce_scatter8(acc, c1, c2, c3);
+                const float ub = row_reduce_scatter8(acc + 8, c1, c2, c3);
+                if (rl < 8) {
+                    sh.part[(j * 4 + row) * SURFEL_GRAD_STRIDE + slot] = ua;
+                    sh.part[(j * 4 + row) * SURFEL_GRAD_STRIDE + 8 + slot] = ub;
+                }
+                if (lane == 0) sh.has[j] = 1u;
             }
-            // per 16-lane row: values 0-7 and 8-15 by two reduce-scatters (lanes 0-7 hold them)
-            const float ua = row_reduce_scatter8(acc, c1, c2, c3);
-            const float ub = row_reduce_scatter8(acc + 8, c1, c2, c3);
-            if (rl < 8) {
-                sh.part[(j * 4 + row) * SURFEL_GRAD_STRIDE + slot] = ua;
-                sh.part[(j * 4 + row) * SURFEL_GRAD_STRIDE + 8 + slot] = ub;
-            }
-            if (lane == 0) sh.has[j] = 1u;
-        }
+        };
+        if (clamp_batch) walk_entries(std::true_type{});
+        else walk_entries(std::false_type{});
         __syncthreads();
         // one atomic add per value per (tile or band, surfel)
         for (int v = lane; v < cnt * 15; v += 64) {
