@@ -293,6 +293,7 @@ hipError_t scan(Load ld, Store st, int n, const u64* dcount, u64* partials, u64*
 //     their totals + sum over blocks < b of digit d's counts. It also clears
 //     the next pass's totals (spare[RT][256]), so passes alternate two buffers.
 //   k_radix_scatter: stable scatter with those offsets.
+constexpr int PIECE = 256;           // super-tile entries one wave walks in the per-tile passes
 constexpr int RB = 1024;             // threads per radix block (16 waves)
 constexpr int RE = 4096;             // elements per radix block
 constexpr int RW = RB / 64;          // waves per radix block
@@ -353,19 +354,54 @@ __global__ __launch_bounds__(RB) void k_radix_hist(SrcMem src, int n, const u64*
 }
 
 // Block d (64 lanes): digit d's base from the totals, then its running offsets
-// over the blocks, each lane a contiguous run of blocks.
+// over the blocks, each lane a contiguous run of blocks. PIECES (the one pass
+// that groups super-tile entries, digit = super-tile): block d also writes
+// super-tile d's entry range sr[d] = [base, base + total) and its first piece
+// pfirst[d] (pieces of PIECE entries before it), and block 255 the number of
+// pieces, for the per-tile passes.
+template <bool PIECES>
 __global__ __launch_bounds__(64) void k_radix_offsets(int nblocks, uint32_t* __restrict__ hist,
-                                                    const uint32_t* __restrict__ tot, uint32_t* __restrict__ spare) {
+                                                    const uint32_t* __restrict__ tot, uint32_t* __restrict__ spare,
+                                                    int S, uint2* __restrict__ sr, uint32_t* __restrict__ pfirst,
+                                                    u64* __restrict__ npieces) {
     const int d = blockIdx.x, lane = threadIdx.x;
-    // base = sum of the totals of digits below d
+    // base = sum of the totals of digits below d; lane holds digits 4 lane .. 4 lane + 3
     const int j = 4 * lane;
-    uint32_t below = 0;
+    uint32_t t[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
         const uint4 t4 = reinterpret_cast<const uint4*>(tot + r * 256)[lane];
-        below += (j < d ? t4.x : 0u) + (j + 1 < d ? t4.y : 0u) + (j + 2 < d ? t4.z : 0u) + (j + 3 < d ? t4.w : 0u);
+        t[0] += t4.x;
+        t[1] += t4.y;
+        t[2] += t4.z;
+        t[3] += t4.w;
     }
-    for (int off = 32; off > 0; off >>= 1) below += (uint32_t)__shfl_xor((int)below, off);
+    uint32_t below = 0, pbelow = 0, pall = 0, mine = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        below += j + i < d ? t[i] : 0u;
+        if (PIECES) {
+            const uint32_t pc = (t[i] + PIECE - 1) / PIECE;
+            pbelow += j + i < d ? pc : 0u;
+            pall += pc;
+            mine += j + i == d ? t[i] : 0u;
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        below += (uint32_t)__shfl_xor((int)below, off);
+        if (PIECES) {
+            pbelow += (uint32_t)__shfl_xor((int)pbelow, off);
+            pall += (uint32_t)__shfl_xor((int)pall, off);
+            mine += (uint32_t)__shfl_xor((int)mine, off);
+        }
+    }
+    if (PIECES && lane == 0) {
+        if (d < S) {
+            sr[d] = make_uint2(below, below + mine);
+            pfirst[d] = pbelow;
+        }
+        if (d == 255) *npieces = pall;
+    }
     constexpr int U = 8;
     const int per = (nblocks + 63) / 64;
     const int b0 = lane * per;
@@ -493,16 +529,28 @@ __global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem src, int n, const u
     }
 }
 
+// The super-tile table a grouping pass can write beside its offsets (see
+// k_radix_offsets<true>); pfirst == nullptr: none.
+struct PieceTable {
+    int S = 0;
+    uint2* sr = nullptr;
+    uint32_t* pfirst = nullptr;
+    u64* npieces = nullptr;
+};
+
 // hist: 256 words per block. rtot: two RT x 256-word total buffers; pass number
 // `pass` adds into rtot[pass & 1] (zero on entry) and clears the other.
 hipError_t radix_pass(SrcMem src, int n, const u64* dcount, int shift, int bits, uint32_t* hist, uint32_t* rtot,
-                      int pass, uint32_t* keys_out, uint32_t* vals_out, hipStream_t s) {
+                      int pass, uint32_t* keys_out, uint32_t* vals_out, hipStream_t s, PieceTable pt = {}) {
     const int nblocks = (n + RE - 1) / RE;
     if (nblocks == 0) return hipSuccess;
     uint32_t* tot = rtot + RT * 256 * (pass & 1);
     uint32_t* spare = rtot + RT * 256 * ((pass & 1) ^ 1);
     k_radix_hist<<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, tot);
-    k_radix_offsets<<<256, 64, 0, s>>>(nblocks, hist, tot, spare);
+    if (pt.pfirst)
+        k_radix_offsets<true><<<256, 64, 0, s>>>(nblocks, hist, tot, spare, pt.S, pt.sr, pt.pfirst, pt.npieces);
+    else
+        k_radix_offsets<false><<<256, 64, 0, s>>>(nblocks, hist, tot, spare, 0, nullptr, nullptr, nullptr);
     k_radix_scatter<<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, keys_out, vals_out);
     return hipGetLastError();
 }
@@ -519,7 +567,6 @@ int bits_for(int ntiles) {
 // ---------------------------------------------------------------- two-level tile binning
 
 constexpr int SUPER = 8;      // a super-tile is SUPER x SUPER tiles: one wave lane per tile
-constexpr int PIECE = 256;    // super-tile entries one wave walks in the per-tile passes
 
 __device__ __forceinline__ uint32_t super_count(int X0, int X1, int Y0, int Y1) {
     return (uint32_t)(((X1 >> 3) - (X0 >> 3) + 1) * ((Y1 >> 3) - (Y0 >> 3) + 1));
@@ -1228,19 +1275,25 @@ hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const
     const int passes = (sbits + 7) / 8;
     const int bpp = (sbits + passes - 1) / passes;
     int cur = 0;
+    // with one pass (up to 256 super-tiles) its digit totals are the super-tiles' entry counts: the pass
+    // writes their ranges and first pieces itself
+    const PieceTable pt{G.S, sr, pfirst, &counters[4]};
     for (int pass = 0; pass < passes; ++pass) {
         const int shift = pass * bpp;
         const int bits = min(bpp, sbits - shift);
-        e = radix_pass(SrcMem{sk[cur], sv[cur]}, P1, nullptr, shift, bits, hist, rtot, pass, sk[cur ^ 1], sv[cur ^ 1], s);
+        e = radix_pass(SrcMem{sk[cur], sv[cur]}, P1, nullptr, shift, bits, hist, rtot, pass, sk[cur ^ 1], sv[cur ^ 1], s,
+                       passes == 1 ? pt : PieceTable{});
         if (e != hipSuccess) return e;
         cur ^= 1;
     }
-    e = fill(reinterpret_cast<uint32_t*>(sr), (size_t)2 * G.S, 0u, s);
-    if (e != hipSuccess) return e;
-    k_super_ranges<<<(P1 + SB - 1) / SB, SB, 0, s>>>(P1, sk[cur], G.S, sr);
-    // pieces of PIECE entries, per super-tile
-    e = scan(LoadPieces{sr}, StoreInPlace{pfirst}, G.S, nullptr, partials, &counters[4], s);
-    if (e != hipSuccess) return e;
+    if (passes > 1) {
+        e = fill(reinterpret_cast<uint32_t*>(sr), (size_t)2 * G.S, 0u, s);
+        if (e != hipSuccess) return e;
+        k_super_ranges<<<(P1 + SB - 1) / SB, SB, 0, s>>>(P1, sk[cur], G.S, sr);
+        // pieces of PIECE entries, per super-tile
+        e = scan(LoadPieces{sr}, StoreInPlace{pfirst}, G.S, nullptr, partials, &counters[4], s);
+        if (e != hipSuccess) return e;
+    }
     // 4. per-tile counts per piece, their running sums and tile totals, tile ranges, placement
     const int max_pieces = (P1 + PIECE - 1) / PIECE + G.S;
     const int wpb = SB / 64;
