@@ -560,6 +560,8 @@ def time_surfels(args, raster, scenes, dev, sc, cams, opt, opt_first, means, qua
         cap = max(cap, int(tiles.to(torch.int64).sum().item() * 1.02) + 4096)
     values = E(cap, torch.int32)
     bin_ws = E(raster.gs_bin_sort_workspace_size(n, cap, W, H), torch.uint8)
+    nck = raster.gs_render_ckpt_bytes(W, H)
+    ckpt = E(nck, torch.uint8) if nck else None  # render checkpoints, as in the frame above
 
     def step(evs):
         for vi, cam in enumerate(cams):
@@ -572,12 +574,12 @@ def time_surfels(args, raster, scenes, dev, sc, cams, opt, opt_first, means, qua
             P = raster.gs_bin_sort(cam, opt, means2d, depths, radii, tiles, bin_ws, cap, None, values, ranges)
             P_box[0] = P
             mark(2)
-            raster.gs_surfel_render_fwd(cam, opt, n, ranges, values, P, tf, rgb, image, final_T, n_contrib)
+            raster.gs_surfel_render_fwd(cam, opt, n, ranges, values, P, tf, rgb, image, final_T, n_contrib, ckpt)
             mark(3)
             grad.zero_()
             mark(4)
             raster.gs_surfel_render_bwd_raster(cam, opt, n, ranges, values, P, tf, rgb, final_T, n_contrib, dLs[vi],
-                                               grad)
+                                               grad, ckpt)
             mark(5)
             raster.gs_surfel_preprocess_bwd(cam, opt_first if vi == 0 else opt, means, scales2, quats, sh, tf, radii,
                                             clamped, grad, grads["means"], grads["scales"], grads["quats"],
@@ -601,12 +603,13 @@ def time_surfels(args, raster, scenes, dev, sc, cams, opt, opt_first, means, qua
     st = [sum(ev[k].elapsed_time(ev[k + 1]) for e in evs for ev in e) / (reps * len(cams))
           for k in range(len(SURFEL_STAGES))]
     log(f"[bench] surfels: {ms:.3f} ms/frame; " + ", ".join(f"{a} {b:.3f}" for a, b in zip(SURFEL_STAGES, st)))
-    del values, bin_ws
+    del values, bin_ws, ckpt
     return {"ms_per_frame": round(ms, 4), "pairs": int(P_box[0]), "visible": int((radii > 0).sum().item()),
             "stages_ms": {a: round(float(b), 4) for a, b in zip(SURFEL_STAGES, st)},
             "note": "2D Gaussian surfels on the same draws (a surfel's two scales are the Gaussian's first two): "
-                    "gs_surfel_preprocess, gs_bin_sort, gs_surfel_render_fwd, gs_surfel_render_bwd_raster, "
-                    "gs_surfel_preprocess_bwd; timed like the frame, not part of value"}
+                    "gs_surfel_preprocess, gs_bin_sort, gs_surfel_render_fwd and gs_surfel_render_bwd_raster "
+                    "(with render checkpoints, as the frame), gs_surfel_preprocess_bwd; timed like the frame, "
+                    "not part of value"}
 
 
 def pmc_traffic(kernel, config):

@@ -615,20 +615,23 @@ gs_status gs_surfel_preprocess(const gs_camera* cam, const gs_options* opt, int6
 
 gs_status gs_surfel_render_fwd(const gs_camera* cam, const gs_options* opt, int64_t n, const uint32_t* ranges,
                                const uint32_t* values, int64_t n_pairs, const float* transforms, const float* rgb,
-                               float* image, float* final_T, uint32_t* n_contrib, void* stream) {
+                               float* image, float* final_T, uint32_t* n_contrib, void* ckpt, size_t ckpt_bytes,
+                               void* stream) {
     try {
         g_err[0] = 0;
         Checked c;
         gs_status st = check_common(cam, opt, n, c);
         if (st != GS_OK) return st;
         REQUIRE(ranges && image && final_T && n_contrib, "gs_surfel_render_fwd: NULL array");
+        st = check_ckpt(ckpt, ckpt_bytes, c);
+        if (st != GS_OK) return st;
         REQUIRE(n_pairs >= 0 && n_pairs < ((int64_t)1 << 31), "n_pairs must be in [0, 2^31)");
         REQUIRE(n_pairs == 0 || (values && transforms && rgb), "gs_surfel_render_fwd: NULL array");
         REQUIRE(aligned(ranges, 8) && (!transforms || aligned(transforms, 16)),
                 "ranges must be 8-byte aligned, transforms 16-byte aligned");
         return hip_check(gs::launch_surfel_render_fwd(c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values,
                                                       transforms, rgb, opt->bg, image, final_T, n_contrib,
-                                                      (hipStream_t)stream),
+                                                      static_cast<float*>(ckpt), (hipStream_t)stream),
                          "gs_surfel_render_fwd");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_surfel_render_fwd: unexpected exception");
@@ -638,7 +641,8 @@ gs_status gs_surfel_render_fwd(const gs_camera* cam, const gs_options* opt, int6
 gs_status gs_surfel_render_bwd_raster(const gs_camera* cam, const gs_options* opt, int64_t n, const uint32_t* ranges,
                                       const uint32_t* values, int64_t n_pairs, const float* transforms,
                                       const float* rgb, const float* final_T, const uint32_t* n_contrib,
-                                      const float* dL_dimage, float* grad, void* stream) {
+                                      const float* dL_dimage, float* grad, const void* ckpt, size_t ckpt_bytes,
+                                      void* stream) {
     try {
         g_err[0] = 0;
         Checked c;
@@ -646,6 +650,8 @@ gs_status gs_surfel_render_bwd_raster(const gs_camera* cam, const gs_options* op
         if (st != GS_OK) return st;
         if (n == 0) return GS_OK;
         REQUIRE(ranges && final_T && n_contrib && dL_dimage && grad, "gs_surfel_render_bwd_raster: NULL array");
+        st = check_ckpt(ckpt, ckpt_bytes, c);
+        if (st != GS_OK) return st;
         REQUIRE(n_pairs >= 0 && n_pairs < ((int64_t)1 << 31), "n_pairs must be in [0, 2^31)");
         if (n_pairs == 0) return GS_OK;
         REQUIRE(values && transforms && rgb, "gs_surfel_render_bwd_raster: NULL array");
@@ -653,7 +659,7 @@ gs_status gs_surfel_render_bwd_raster(const gs_camera* cam, const gs_options* op
                 "ranges must be 8-byte aligned, transforms and grad 16-byte aligned");
         return hip_check(gs::launch_surfel_render_bwd(c.cam.W, c.cam.H, c.cam.TX, c.cam.TY, ranges, values,
                                                       transforms, rgb, opt->bg, final_T, n_contrib, dL_dimage, grad,
-                                                      (hipStream_t)stream),
+                                                      static_cast<const float*>(ckpt), (hipStream_t)stream),
                          "gs_surfel_render_bwd_raster");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_surfel_render_bwd_raster: unexpected exception");
@@ -697,7 +703,8 @@ gs_status gs_surfel_render_bwd(const gs_camera* cam, const gs_options* opt, int6
                                const uint32_t* values, int64_t n_pairs, const float* final_T,
                                const uint32_t* n_contrib, const float* dL_dimage, float* dL_dmeans,
                                float* dL_dscales, float* dL_dquats, float* dL_dopacities, float* dL_dsh,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               void* workspace, size_t workspace_bytes, const void* ckpt, size_t ckpt_bytes,
+                               void* stream) {
     try {
         g_err[0] = 0;
         Checked c;
@@ -714,7 +721,7 @@ gs_status gs_surfel_render_bwd(const gs_camera* cam, const gs_options* opt, int6
                        "gs_surfel_render_bwd(zero)");
         if (st != GS_OK) return st;
         st = gs_surfel_render_bwd_raster(cam, opt, n, ranges, values, n_pairs, transforms, rgb, final_T, n_contrib,
-                                         dL_dimage, grad, stream);
+                                         dL_dimage, grad, ckpt, ckpt_bytes, stream);
         if (st != GS_OK) return st;
         return gs_surfel_preprocess_bwd(cam, opt, n, means, scales, quats, sh, transforms, radii, clamped, grad,
                                         dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh, stream);

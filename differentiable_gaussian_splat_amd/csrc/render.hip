@@ -29,16 +29,6 @@ namespace {
 
 constexpr int BATCH = 64;  // records staged per LDS batch
 
-// Render checkpoints (one view's tile grid): for each tile, the forward's
-// per-pixel state (T, C) after list entries CKPT_EVERY k - 1, k = 1..CKPT_SLOTS,
-// then the pixel's final colour: (CKPT_SLOTS + 1) x 256 float4 per tile, pixel
-// (row r, column c) of the tile at float4 16 r + c of a slot. A slot is written
-// only when the tile's band wave walks past its entry; the backward reads only
-// such slots (see bwd_walk). After all tiles' slots, one uint4 per tile: each
-// row band's walk (its deepest blended entry), always written.
-constexpr int PIECES_CHUNK = 1024;  // tiles per dispatch chunk of the pieces backward
-constexpr int CKPT_EVERY = 256;
-constexpr int CKPT_SLOTS = 4;
 static_assert(CKPT_EVERY % BATCH == 0, "checkpoints fall on batch ends");
 
 // A staged record: (w0, dy0, a2, beta), (g2, log2 o, r, g), b. One LDS

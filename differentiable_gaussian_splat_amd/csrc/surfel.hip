@@ -43,6 +43,7 @@ namespace gs {
 namespace {
 
 constexpr int FWD_BATCH = 64;
+static_assert(CKPT_EVERY % FWD_BATCH == 0, "checkpoints fall on batch ends");
 constexpr int BWD_BATCH = 32;
 
 // (Kc, N12.x), (N12.y, N12.z, N02.x, N02.y), (N02.z, dx0, dy0, log2 o), (rgb, -; the
@@ -162,11 +163,13 @@ __device__ __forceinline__ void surfel_hit(const SurfelRec& s, float lx, float l
 
 // Forward: four waves per tile, one per 16x4 band, one pixel per lane
 // (tile 8q + x on workgroups 32q + 8 band + x: its four bands share XCD x).
+// ckpt (nullable): the render checkpoints (layout beside CKPT_EVERY), for the
+// backward's pieces.
 __global__ __launch_bounds__(64) void k_surfel_fwd(int W, int H, int TX, int ntiles, const uint2* __restrict__ ranges,
                                                  const uint32_t* __restrict__ values, const float4* __restrict__ tf,
                                                  const float* __restrict__ rgb, float bg0, float bg1, float bg2,
                                                  float* __restrict__ image, float* __restrict__ final_T,
-                                                 uint32_t* __restrict__ n_contrib) {
+                                                 uint32_t* __restrict__ n_contrib, float4* __restrict__ ckpt) {
     __shared__ SurfelRec s_rec[FWD_BATCH];
     const int b = blockIdx.x;
     const int tile = ((b >> 5) << 3) + (b & 7), band = (b >> 3) & 3;
@@ -185,6 +188,7 @@ __global__ __launch_bounds__(64) void k_surfel_fwd(int W, int H, int TX, int nti
     const float bx_lo = (float)(tx * TILE) + 0.5f, bx_hi = bx_lo + 15.f;
     const float by_lo = (float)(ty * TILE + band * 4) + 0.5f, by_hi = by_lo + 3.f;
     const uint2 rg = ranges[tile];
+    bool wrote_ckpt = false;
     for (uint32_t bs = rg.x; bs < rg.y; bs += FWD_BATCH) {
         if (!__any(thr < 1.f)) break;
         const uint32_t idx = bs + lane;
@@ -233,6 +237,23 @@ __global__ __launch_bounds__(64) void k_surfel_fwd(int W, int H, int TX, int nti
             if (!__any(thr < 1.f)) break;
         }
         __syncthreads();
+        if (ckpt) {
+            // the state after a whole batch that ends a checkpoint interval, while still walking
+            const uint32_t done = bs - rg.x + FWD_BATCH;
+            if (bs + FWD_BATCH <= rg.y && done % CKPT_EVERY == 0 && done / CKPT_EVERY <= CKPT_SLOTS &&
+                __any(thr < 1.f)) {
+                ckpt[((size_t)tile * (CKPT_SLOTS + 1) + done / CKPT_EVERY - 1) * 256 + band * 64 + lane] =
+                    make_float4(T, C0, C1, C2);
+                wrote_ckpt = true;
+            }
+        }
+    }
+    if (wrote_ckpt)  // the final colour, beside the checkpoints
+        ckpt[((size_t)tile * (CKPT_SLOTS + 1) + CKPT_SLOTS) * 256 + band * 64 + lane] = make_float4(C0, C1, C2, T);
+    if (ckpt) {  // the band's walk, for the backward's choice of pieces
+        const uint32_t bw = wave_max_u32(last);
+        if (lane == 0)
+            reinterpret_cast<uint32_t*>(ckpt + (size_t)ntiles * (CKPT_SLOTS + 1) * 256)[4 * tile + band] = bw;
     }
     if (px < W && py < H) {
         const size_t HW = (size_t)W * H, p = (size_t)py * W + px;
@@ -260,17 +281,25 @@ struct SurfelBwdShared {
 // the filter's branch h (pixel - c) is summed for dL/dc. Record per surfel
 // (16 floats): dL/drgb, sum h, sum dL/dk, sum dx dL/dk, sum dy dL/dk,
 // sum h (pixel - c) over filter-branch pixels, 0.
+// One wave's walk: bands band PPL .. band PPL + PPL - 1 of tile `tile` (pixel
+// k of a lane lies in band band PPL + k), only those set in band_sel (bit k),
+// over list entries [walk_lo, walk_hi). A pixel whose row band blends nothing
+// at or past walk_hi in the forward (rb_walk: each band's walk) starts from the
+// final state; the others from the forward's checkpoint ck after entry
+// walk_hi - 1 (T there, and the colour behind it, (C_final - C there +
+// final_T bg) / T, with ck_end holding C_final). ck is null when walk_hi is
+// past the walk.
 template <int PPL>
-__global__ __launch_bounds__(64) void k_surfel_bwd(int W, int H, int TX, const uint2* __restrict__ ranges,
-                                                 const uint32_t* __restrict__ values, const float4* __restrict__ tf,
-                                                 const float* __restrict__ rgb, float bg0, float bg1, float bg2,
-                                                 const float* __restrict__ final_T,
-                                                 const uint32_t* __restrict__ n_contrib,
-                                                 const float* __restrict__ dL_dimage, float* __restrict__ grad) {
+__device__ __forceinline__ void surfel_bwd_walk(int tile, int band, uint32_t band_sel, int walk_lo, int walk_hi,
+                                                const float4* __restrict__ ck, const float4* __restrict__ ck_end,
+                                                uint4 rb_walk, int W, int H, int TX,
+                                                const uint2* __restrict__ ranges, const uint32_t* __restrict__ values,
+                                                const float4* __restrict__ tf, const float* __restrict__ rgb,
+                                                float bg0, float bg1, float bg2, const float* __restrict__ final_T,
+                                                const uint32_t* __restrict__ n_contrib,
+                                                const float* __restrict__ dL_dimage, float* __restrict__ grad,
+                                                SurfelBwdShared<BWD_BATCH>& sh) {
     constexpr int NB = BWD_BATCH;
-    constexpr int BANDS = 4 / PPL;
-    __shared__ SurfelBwdShared<NB> sh;
-    const int tile = blockIdx.x / BANDS, band = blockIdx.x - tile * BANDS;
     const int ty = tile / TX, tx = tile - ty * TX;
     const int lane = threadIdx.x;
     const int rl = lane & 15, row = lane >> 4;
@@ -299,15 +328,29 @@ __global__ __launch_bounds__(64) void k_surfel_bwd(int W, int H, int TX, const u
         g2[k] = in ? dL_dimage[2 * HW + p] : 0.f;
         S[k] = fmaf(bg0, g0[k], fmaf(bg1, g1[k], bg2 * g2[k]));
         band_last[k] = __builtin_amdgcn_readfirstlane(wave_max_u32(last[k]));
+        if (!((band_sel >> k) & 1u)) {  // the band belongs to another wave: none of its entries is walked here
+            band_last[k] = 0u;
+            last[k] = 0u;
+        }
+        const int rb = r >> 2;
+        const uint32_t rbw = rb == 0 ? rb_walk.x : rb == 1 ? rb_walk.y : rb == 2 ? rb_walk.z : rb_walk.w;
+        if (ck && rbw > (uint32_t)walk_hi) {  // this pixel's row band walked past walk_hi in the forward
+            const int lp = 16 * r + rl;       // the pixel's float4 in a checkpoint slot
+            const float4 c = ck[lp], e = ck_end[lp];
+            const float behind = fmaf(g0[k], e.x - c.y, fmaf(g1[k], e.y - c.z, g2[k] * (e.z - c.w)));
+            S[k] = in ? fmaf(T[k], S[k], behind) / c.x : 0.f;
+            T[k] = in ? c.x : 1.f;
+        }
         mylast = max(mylast, band_last[k]);
     }
     const uint2 rg = ranges[tile];
-    const uint32_t maxlast = min(mylast, rg.y - rg.x);
+    // never walk past the tile's list, whatever n_contrib holds
+    const uint32_t maxlast = min(min(mylast, rg.y - rg.x), (uint32_t)walk_hi);
     // pixel-centre rectangle of the wave's first row band (band k lies 4 k rows lower)
     const float bx_lo = (float)(tx * TILE) + 0.5f, bx_hi = bx_lo + 15.f;
     const float by_lo = (float)(ty * TILE + band * 4 * PPL) + 0.5f;
-    for (int hi = (int)maxlast; hi > 0; hi -= NB) {
-        const int lo = max(0, hi - NB);
+    for (int hi = (int)maxlast; hi > walk_lo; hi -= NB) {
+        const int lo = max(walk_lo, hi - NB);
         const int cnt = hi - lo;
         bool reach = false;  // some row band this wave walks past the entry may blend it
         bool clamp = false;  // its alpha may reach the 0.99 clamp
@@ -411,27 +454,106 @@ __global__ __launch_bounds__(64) void k_surfel_bwd(int W, int H, int TX, const u
     }
 }
 
+template <int PPL>
+__global__ __launch_bounds__(64) void k_surfel_bwd(int W, int H, int TX, const uint2* __restrict__ ranges,
+                                                 const uint32_t* __restrict__ values, const float4* __restrict__ tf,
+                                                 const float* __restrict__ rgb, float bg0, float bg1, float bg2,
+                                                 const float* __restrict__ final_T,
+                                                 const uint32_t* __restrict__ n_contrib,
+                                                 const float* __restrict__ dL_dimage, float* __restrict__ grad) {
+    constexpr int BANDS = 4 / PPL;
+    __shared__ SurfelBwdShared<BWD_BATCH> sh;
+    const int tile = blockIdx.x / BANDS, band = blockIdx.x - tile * BANDS;
+    surfel_bwd_walk<PPL>(tile, band, 0xFu, 0, INT32_MAX, nullptr, nullptr, make_uint4(0u, 0u, 0u, 0u), W, H, TX, ranges,
+                         values, tf, rgb, bg0, bg1, bg2, final_T, n_contrib, dL_dimage, grad, sh);
+}
+
+// The backward cut along deep tiles' walks, from the forward's checkpoints: a
+// tile gets one wave per piece of CKPT_EVERY entries, each piece starting from
+// the checkpoint after its last entry, so the pieces are independent; a walk
+// past the last checkpoint ends in a tail piece from the final state that two
+// waves share by row bands. Dispatch order as the 3D backward's pieces: by
+// chunks of PIECES_CHUNK tiles, the chunk's later waves first (most return at
+// once), then its first pieces.
+__global__ __launch_bounds__(64) void k_surfel_bwd_pieces(int W, int H, int TX, int ntiles,
+                                                        const float4* __restrict__ ckpt,
+                                                        const uint2* __restrict__ ranges,
+                                                        const uint32_t* __restrict__ values,
+                                                        const float4* __restrict__ tf, const float* __restrict__ rgb,
+                                                        float bg0, float bg1, float bg2,
+                                                        const float* __restrict__ final_T,
+                                                        const uint32_t* __restrict__ n_contrib,
+                                                        const float* __restrict__ dL_dimage,
+                                                        float* __restrict__ grad) {
+    __shared__ SurfelBwdShared<BWD_BATCH> sh;
+    constexpr int PIECES = CKPT_SLOTS + 1;  // slots in the checkpoint buffer per tile
+    constexpr int WAVES = CKPT_SLOTS + 2;   // waves per tile
+    const int b = blockIdx.x;
+    const int cb = b / (WAVES * PIECES_CHUNK), r = b - cb * WAVES * PIECES_CHUNK;
+    const int t0 = cb * PIECES_CHUNK, tn = min(PIECES_CHUNK, ntiles - t0);
+    if (r >= WAVES * tn) return;  // past the last tile
+    int w, tile;
+    if (r < (WAVES - 1) * tn) {
+        w = 1 + r / tn;
+        tile = t0 + r % tn;
+    } else {
+        w = 0;
+        tile = t0 + r - (WAVES - 1) * tn;
+    }
+    // the tile's walk, from its row bands' walks the forward left after the checkpoints, at most
+    // the list's length
+    const uint4 bw = reinterpret_cast<const uint4*>(ckpt + (size_t)ntiles * PIECES * 256)[tile];
+    const uint2 rg = ranges[tile];
+    const uint32_t walk = min(max(max(bw.x, bw.y), max(bw.z, bw.w)), rg.y - rg.x);
+    const int need = (int)((walk + CKPT_EVERY - 1) / CKPT_EVERY);
+    const bool deep = need > PIECES;
+    int piece = w;
+    uint32_t sel = 0xFu;
+    if (deep) {
+        if (w >= CKPT_SLOTS) {  // the tail, bands 0-1 or 2-3
+            piece = CKPT_SLOTS;
+            sel = w == CKPT_SLOTS ? 0x3u : 0xCu;
+        }
+    } else if (w >= max(need, 1)) {
+        return;
+    }
+    const int pieces = deep ? PIECES : need;
+    const bool tail = piece >= pieces - 1;  // the last piece walks to the end from the final state
+    const int lo = piece * CKPT_EVERY, hi = tail ? INT32_MAX : lo + CKPT_EVERY;
+    const float4* tck = ckpt + (size_t)tile * PIECES * 256;
+    surfel_bwd_walk<4>(tile, 0, sel, lo, hi, tail ? nullptr : tck + (size_t)piece * 256, tck + CKPT_SLOTS * 256, bw, W,
+                       H, TX, ranges, values, tf, rgb, bg0, bg1, bg2, final_T, n_contrib, dL_dimage, grad, sh);
+}
+
 }  // namespace
 
 hipError_t launch_surfel_render_fwd(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
                                     const float* tf, const float* rgb, const float* bg, float* image, float* final_T,
-                                    uint32_t* n_contrib, hipStream_t stream) {
+                                    uint32_t* n_contrib, float* ckpt, hipStream_t stream) {
     const int ntiles = TX * TY;
     if (ntiles == 0) return hipSuccess;
+    // checkpoints only where the backward reads them
+    float4* ck = render_ckpt_bytes(TX, TY) ? reinterpret_cast<float4*>(ckpt) : nullptr;
     k_surfel_fwd<<<32 * ((ntiles + 7) / 8), 64, 0, stream>>>(W, H, TX, ntiles, reinterpret_cast<const uint2*>(ranges),
                                                              values, reinterpret_cast<const float4*>(tf), rgb, bg[0],
-                                                             bg[1], bg[2], image, final_T, n_contrib);
+                                                             bg[1], bg[2], image, final_T, n_contrib, ck);
     return hipGetLastError();
 }
 
 hipError_t launch_surfel_render_bwd(int W, int H, int TX, int TY, const uint32_t* ranges, const uint32_t* values,
                                     const float* tf, const float* rgb, const float* bg, const float* final_T,
-                                    const uint32_t* n_contrib, const float* dL_dimage, float* grad,
+                                    const uint32_t* n_contrib, const float* dL_dimage, float* grad, const float* ckpt,
                                     hipStream_t stream) {
     const int ntiles = TX * TY;
     if (ntiles == 0) return hipSuccess;
     const uint2* rg = reinterpret_cast<const uint2*>(ranges);
     const float4* t4 = reinterpret_cast<const float4*>(tf);
+    if (ckpt && render_ckpt_bytes(TX, TY)) {  // deep tiles cut into pieces from the forward's checkpoints
+        k_surfel_bwd_pieces<<<(CKPT_SLOTS + 2) * PIECES_CHUNK * ((ntiles + PIECES_CHUNK - 1) / PIECES_CHUNK), 64, 0,
+                              stream>>>(W, H, TX, ntiles, reinterpret_cast<const float4*>(ckpt), rg, values, t4, rgb,
+                                        bg[0], bg[1], bg[2], final_T, n_contrib, dL_dimage, grad);
+        return hipGetLastError();
+    }
     // small grids: a wave per 16x4 band keeps more SIMDs busy; large ones: a wave per tile
     if (ntiles < 2048)
         k_surfel_bwd<1><<<ntiles * 4, 64, 0, stream>>>(W, H, TX, rg, values, t4, rgb, bg[0], bg[1], bg[2], final_T,

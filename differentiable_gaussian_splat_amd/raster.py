@@ -147,16 +147,16 @@ def load_library(path: str = LIB_PATH):
         L.gs_mb_render_counts.restype = i32
         L.gs_surfel_preprocess.argtypes = [cam, opt, i64] + [P] * 5 + [P] * 7 + [P]
         L.gs_surfel_preprocess.restype = i32
-        L.gs_surfel_render_fwd.argtypes = [cam, opt, i64, P, P, i64, P, P, P, P, P, P]
+        L.gs_surfel_render_fwd.argtypes = [cam, opt, i64, P, P, i64, P, P, P, P, P, P, sz, P]
         L.gs_surfel_render_fwd.restype = i32
-        L.gs_surfel_render_bwd_raster.argtypes = [cam, opt, i64, P, P, i64] + [P] * 6 + [P]
+        L.gs_surfel_render_bwd_raster.argtypes = [cam, opt, i64, P, P, i64] + [P] * 6 + [P, sz, P]
         L.gs_surfel_render_bwd_raster.restype = i32
         L.gs_surfel_preprocess_bwd.argtypes = [cam, opt, i64] + [P] * 8 + [P] * 5 + [P]
         L.gs_surfel_preprocess_bwd.restype = i32
         L.gs_surfel_render_bwd_workspace_size.argtypes = [i64]
         L.gs_surfel_render_bwd_workspace_size.restype = sz
         L.gs_surfel_render_bwd.argtypes = ([cam, opt, i64] + [P] * 8 + [P, P, i64] + [P] * 3 + [P] * 5 +
-                                           [P, sz, P])
+                                           [P, sz, P, sz, P])
         L.gs_surfel_render_bwd.restype = i32
         L.gs_mb_hbm_read.argtypes = [P, sz, P, P]
         L.gs_mb_hbm_read.restype = i32
@@ -445,18 +445,19 @@ def gs_surfel_preprocess(cam: GsCamera, opt: GsOptions, means, scales, quats, op
 
 
 def gs_surfel_render_fwd(cam: GsCamera, opt: GsOptions, n, ranges, values, n_pairs, transforms, rgb, image, final_T,
-                         n_contrib, stream=None):
+                         n_contrib, ckpt=None, stream=None):
     st = load_library().gs_surfel_render_fwd(C.byref(cam), C.byref(opt), n, _p(ranges), _p(values), n_pairs,
                                              _p(transforms), _p(rgb), _p(image), _p(final_T), _p(n_contrib),
-                                             _stream(stream))
+                                             _p(ckpt), _nbytes(ckpt), _stream(stream))
     _check(st, "gs_surfel_render_fwd")
 
 
 def gs_surfel_render_bwd_raster(cam: GsCamera, opt: GsOptions, n, ranges, values, n_pairs, transforms, rgb, final_T,
-                                n_contrib, dL_dimage, grad, stream=None):
+                                n_contrib, dL_dimage, grad, ckpt=None, stream=None):
     st = load_library().gs_surfel_render_bwd_raster(C.byref(cam), C.byref(opt), n, _p(ranges), _p(values), n_pairs,
                                                     _p(transforms), _p(rgb), _p(final_T), _p(n_contrib),
-                                                    _p(dL_dimage), _p(grad), _stream(stream))
+                                                    _p(dL_dimage), _p(grad), _p(ckpt), _nbytes(ckpt),
+                                                    _stream(stream))
     _check(st, "gs_surfel_render_bwd_raster")
 
 
@@ -476,13 +477,13 @@ def gs_surfel_render_bwd_workspace_size(n) -> int:
 
 def gs_surfel_render_bwd(cam: GsCamera, opt: GsOptions, means, scales, quats, sh, transforms, rgb, radii, clamped,
                          ranges, values, n_pairs, final_T, n_contrib, dL_dimage, dL_dmeans, dL_dscales, dL_dquats,
-                         dL_dopacities, dL_dsh, workspace, stream=None):
+                         dL_dopacities, dL_dsh, workspace, ckpt=None, stream=None):
     n = means.shape[0]
     st = load_library().gs_surfel_render_bwd(
         C.byref(cam), C.byref(opt), n, _p(means), _p(scales), _p(quats), _p(sh), _p(transforms), _p(rgb), _p(radii),
         _p(clamped), _p(ranges), _p(values), n_pairs, _p(final_T), _p(n_contrib), _p(dL_dimage), _p(dL_dmeans),
         _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities), _p(dL_dsh), _p(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream))
+        workspace.numel() * workspace.element_size(), _p(ckpt), _nbytes(ckpt), _stream(stream))
     _check(st, "gs_surfel_render_bwd")
 
 
@@ -645,11 +646,13 @@ class Rasterizer:
         image = _empty((3, H, W), torch.float32, self.device)
         final_T = _empty((H, W), torch.float32, self.device)
         n_contrib = _empty((H, W), torch.int32, self.device)
+        nck = gs_render_ckpt_bytes(W, H)
+        ckpt = _empty(nck, torch.uint8, self.device) if nck else None
         gs_surfel_render_fwd(cam, opt, n, ranges, self._values, P, pre["conic_opacity"], pre["rgb"], image, final_T,
-                             n_contrib)
+                             n_contrib, ckpt)
         return Frame(cam, opt, W, H, pre["means2d"], pre["depths"], pre["conic_opacity"], pre["rgb"], pre["radii"],
                      pre["tiles_touched"], pre["clamped"], P, self._keys, self._values, ranges, image, final_T,
-                     n_contrib, None)
+                     n_contrib, ckpt)
 
     def surfel_backward(self, frame: "Frame", means, scales, quats, sh, dL_dimage, grads: dict,
                         overwrite: bool = False):
@@ -666,7 +669,7 @@ class Rasterizer:
         gs_surfel_render_bwd(frame.cam, opt, means, scales, quats, sh, frame.conic_opacity, frame.rgb, frame.radii,
                              frame.clamped, frame.ranges, frame.values, frame.n_pairs, frame.final_T,
                              frame.n_contrib, dL_dimage, grads["means"], grads["scales"], grads["quats"],
-                             grads["opacities"], grads["sh"], self._bwd_ws)
+                             grads["opacities"], grads["sh"], self._bwd_ws, frame.ckpt)
         return grads
 
 

@@ -363,19 +363,24 @@ gs_status gs_surfel_preprocess(const gs_camera *cam, const gs_options *opt, int6
 
 /* Per-pixel compositing of the binned surfels (lists from gs_bin_sort on the
  * surfels' means2d, depths, radii, tiles_touched): image[3,H,W], final_T[H,W],
- * n_contrib[H,W] as gs_render_fwd. */
+ * n_contrib[H,W] as gs_render_fwd. ckpt (nullable): render checkpoints for the
+ * backward of the same frame, exactly as gs_render_fwd's (same size,
+ * gs_render_ckpt_bytes(W, H), and the same contract). */
 gs_status gs_surfel_render_fwd(const gs_camera *cam, const gs_options *opt, int64_t n,
                                const uint32_t *ranges, const uint32_t *values, int64_t n_pairs,
                                const float *transforms, const float *rgb,
-                               float *image, float *final_T, uint32_t *n_contrib, void *stream);
+                               float *image, float *final_T, uint32_t *n_contrib,
+                               void *ckpt, size_t ckpt_bytes, void *stream);
 
 /* The reverse blend's per-surfel pixel sums of ONE view, ADDED to
- * grad[n, GS_SURFEL_GRAD_STRIDE] (the caller zeroes it per view). */
+ * grad[n, GS_SURFEL_GRAD_STRIDE] (the caller zeroes it per view). ckpt
+ * (nullable): the checkpoints gs_surfel_render_fwd wrote for this frame (same
+ * buffer and size), which let deep tiles' walks be cut into pieces, or NULL. */
 gs_status gs_surfel_render_bwd_raster(const gs_camera *cam, const gs_options *opt, int64_t n,
                                       const uint32_t *ranges, const uint32_t *values, int64_t n_pairs,
                                       const float *transforms, const float *rgb, const float *final_T,
                                       const uint32_t *n_contrib, const float *dL_dimage, float *grad,
-                                      void *stream);
+                                      const void *ckpt, size_t ckpt_bytes, void *stream);
 
 /* The chain rule from grad to the activated parameters: ACCUMULATED (+=)
  * dL_dmeans[n,3], dL_dscales[n,2], dL_dquats[n,4], dL_dopacities[n],
@@ -390,8 +395,8 @@ gs_status gs_surfel_preprocess_bwd(const gs_camera *cam, const gs_options *opt, 
 /* Workspace bytes of gs_surfel_render_bwd for n surfels. */
 size_t gs_surfel_render_bwd_workspace_size(int64_t n);
 
-/* gs_surfel_render_bwd_raster into a zeroed workspace, then
- * gs_surfel_preprocess_bwd. */
+/* gs_surfel_render_bwd_raster into a zeroed workspace (with ckpt, nullable, as
+ * there), then gs_surfel_preprocess_bwd. */
 gs_status gs_surfel_render_bwd(const gs_camera *cam, const gs_options *opt, int64_t n,
                                const float *means, const float *scales, const float *quats,
                                const float *sh, const float *transforms, const float *rgb,
@@ -400,7 +405,8 @@ gs_status gs_surfel_render_bwd(const gs_camera *cam, const gs_options *opt, int6
                                const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
                                float *dL_dmeans, float *dL_dscales, float *dL_dquats,
                                float *dL_dopacities, float *dL_dsh,
-                               void *workspace, size_t workspace_bytes, void *stream);
+                               void *workspace, size_t workspace_bytes, const void *ckpt, size_t ckpt_bytes,
+                               void *stream);
 
 /* ---------------------------------------------------------------------------
  * Several views per launch

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from differentiable_gaussian_splat_amd import raster
-from differentiable_gaussian_splat_amd.scenes import make_scene, surfel_scales
+from differentiable_gaussian_splat_amd.scenes import Camera, make_scene, surfel_scales
 from oracle import oracle as O
 from tests.gpu_helpers import rel_l2, to_dev
 from tests.test_gpu_parity import _scene_for, _tiny_cam
@@ -101,7 +101,7 @@ def check_frame(sc, r, pd, fr, g, view=0, end_to_end=True, bg=(0.0, 0.0, 0.0)):
     dL = sc.dL_dimage[view]
     gsum = torch.zeros((sc.n, raster.SURFEL_GRAD_STRIDE), dtype=torch.float32, device=pd["means"].device)
     raster.gs_surfel_render_bwd_raster(fr.cam, fr.opt, sc.n, fr.ranges, fr.values, fr.n_pairs, fr.conic_opacity,
-                                       fr.rgb, fr.final_T, fr.n_contrib, to_dev(dL), gsum)
+                                       fr.rgb, fr.final_T, fr.n_contrib, to_dev(dL), gsum, fr.ckpt)
     torch.cuda.synchronize()
     gs_ = gsum.cpu().numpy().astype(np.float64)
     og = O.surfel_render_bwd(W, H, sc.n, g["ranges"], g["values"], g["means2d"], g["M"], g["opac"], g["rgb"], dL,
@@ -211,6 +211,57 @@ def test_surfel_full_frame_contention_scene():
     r, pd, fr, g = run(sc)
     check_frame(sc, r, pd, fr, g, end_to_end=False)
     print(f"surfels at 1080p: pairs {g['P']}, drawn {(g['radii'] > 0).sum()}")
+
+
+@pytest.mark.parametrize("bg", [(0.0, 0.0, 0.0), (0.2, 0.5, 0.9)])
+def test_surfel_backward_pieces_of_deep_tiles(bg):
+    """On grids of 4096 tiles or more the surfel backward, given the forward's
+    checkpoints, cuts a deep tile's walk into pieces of 256 entries (a walk
+    past the fifth piece ends in a tail shared by two waves by row bands).
+    1500 faint surfels heaped on the middle of a 1024x1024 frame walk over
+    1280 entries there, a few hundred more lie thinly elsewhere: stage-wise
+    against the oracle on that path, and the same pixel sums as the one-wave-
+    per-tile backward without checkpoints, up to summation order. With a
+    background, each piece's colour behind its start takes the T_final bg
+    term. The surfels are tilted at most 60 degrees from facing the camera:
+    near grazing incidence the fp32 ray-plane intersection loses precision in
+    proportion to the cancellation in k2, beyond the matcher's alpha window
+    (one such surfel here, seen 86 px from its centre, put three pixels 1e-5
+    off the fp64 colour, exactly what a CPU emulation of the kernel's fp32
+    steps gives); the forward's parity on freely oriented surfels is the other
+    tests' part."""
+    rng = np.random.default_rng(11)
+    cam = Camera(1024, 1024, 1000.0, 1000.0, 512.0, 512.0, np.eye(3, dtype=np.float32), np.zeros(3, np.float32))
+    n_heap, n_rest = 1500, 400
+    sc = _scene_for(cam, n_heap + n_rest, rng, deg=1)
+    # unit quaternions (w, x, y, z) turning the surfel's normal (the rotation's third column, +z when
+    # w = 1) by up to 60 degrees about an axis in the image plane
+    half = 0.5 * np.radians(rng.uniform(0.0, 60.0, sc.n))
+    phi = rng.uniform(0.0, 2 * np.pi, sc.n)
+    sc.quats = np.stack([np.cos(half), np.sin(half) * np.cos(phi), np.sin(half) * np.sin(phi), np.zeros(sc.n)],
+                        1).astype(np.float32)
+    z = rng.uniform(3.0, 5.0, n_heap)
+    uv = rng.normal(512.0, 12.0, (n_heap, 2))
+    sc.means[:n_heap] = np.stack([(uv[:, 0] - 512.0) * z / 1000.0, (uv[:, 1] - 512.0) * z / 1000.0, z],
+                                 1).astype(np.float32)
+    sc.scales[:n_heap] = np.exp(rng.normal(-3.5, 0.2, (n_heap, 3))).astype(np.float32)
+    sc.opacities[:n_heap] = rng.uniform(0.01, 0.03, n_heap).astype(np.float32)
+    r, pd, fr, g = run(sc, bg=bg)
+    assert fr.ckpt is not None
+    walks = g["n_contrib"].astype(np.int64).reshape(64, 16, 64, 16).max(axis=(1, 3))
+    assert (walks > 1280).sum() >= 1 and ((walks > 0) & (walks < 512)).sum() > 100, \
+        (walks.max(), (walks > 1280).sum())
+    check_frame(sc, r, pd, fr, g, bg=bg)
+    dL = to_dev(sc.dL_dimage[0])
+    sums = []
+    for ck in (fr.ckpt, None):
+        gsum = torch.zeros((sc.n, raster.SURFEL_GRAD_STRIDE), dtype=torch.float32, device=dL.device)
+        raster.gs_surfel_render_bwd_raster(fr.cam, fr.opt, sc.n, fr.ranges, fr.values, fr.n_pairs, fr.conic_opacity,
+                                           fr.rgb, fr.final_T, fr.n_contrib, dL, gsum, ck)
+        torch.cuda.synchronize()
+        sums.append(gsum.cpu().numpy().astype(np.float64))
+    for c in range(15):
+        assert rel_l2(sums[0][:, c], sums[1][:, c]) < 1e-5, (c, rel_l2(sums[0][:, c], sums[1][:, c]))
 
 
 def test_surfel_ragged_image_rotated_camera_and_background():
