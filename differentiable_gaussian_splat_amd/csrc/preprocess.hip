@@ -18,6 +18,8 @@
 // before the includes, so that it covers the shared helpers too.)
 #pragma clang fp contract(off)
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -1114,7 +1116,10 @@ __global__ __launch_bounds__(64) void k_preprocess_bwd_views(
 // the quaternion's rotation. Outputs accumulate (+=), or with OVERWRITE are
 // written (zeros for a culled surfel and for SH rows at or past the active
 // degree). The SH row moves through registers.
-template <bool OVERWRITE>
+// VEC: SH rows of 16 coefficients (12 float4, 16-byte aligned) move as float4,
+// so that each row is read and written whole; otherwise coefficient by
+// coefficient.
+template <bool OVERWRITE, bool VEC>
 __global__ __launch_bounds__(64) void k_surfel_preprocess_bwd(
     DevCam cam, int K, int sh_rows, int n, const float* __restrict__ means, const float* __restrict__ scales,
     const float4* __restrict__ quats, const float* __restrict__ sh, const float4* __restrict__ tf,
@@ -1141,9 +1146,26 @@ __global__ __launch_bounds__(64) void k_surfel_preprocess_bwd(
             d_scales[2 * g] = d_scales[2 * g + 1] = 0.f;
             reinterpret_cast<float4*>(d_quats)[g] = make_float4(0.f, 0.f, 0.f, 0.f);
             d_opac[g] = 0.f;
-            for (int e = 0; e < 3 * sh_rows; ++e) dsh[e] = 0.f;
+            if (VEC) {
+#pragma unroll
+                for (int q = 0; q < 12; ++q) reinterpret_cast<float4*>(dsh)[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            } else {
+                for (int e = 0; e < 3 * sh_rows; ++e) dsh[e] = 0.f;
+            }
         }
         return;
+    }
+    // the SH row first (VEC): its loads go out with the rest of the record's
+    float cf[VEC ? 48 : 1];
+    if (VEC) {
+#pragma unroll
+        for (int q = 0; q < 12; ++q) {
+            const float4 v = reinterpret_cast<const float4*>(shg)[q];
+            cf[4 * q] = v.x;
+            cf[4 * q + 1] = v.y;
+            cf[4 * q + 2] = v.z;
+            cf[4 * q + 3] = v.w;
+        }
     }
     const float su = scales[2 * g], sv = scales[2 * g + 1];
     const float qn = sqrtf(qq), iq = 1.0f / qn;
@@ -1226,20 +1248,44 @@ __global__ __launch_bounds__(64) void k_surfel_preprocess_bwd(
     const float dxn = ddx * id, dyn = ddy * id, dzn = ddz * id;
     float Y[16], wk[16];
     sh_eval(K, dxn, dyn, dzn, Y);
+    if (VEC) {
+        float out[48];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        if (k < K) {
-            const float c0 = shg[3 * k], c1 = shg[3 * k + 1], c2 = shg[3 * k + 2];
-            wk[k] = fmaf(c0, dcol[0], fmaf(c1, dcol[1], c2 * dcol[2]));
-            const float p0 = OVERWRITE ? 0.f : dsh[3 * k], p1 = OVERWRITE ? 0.f : dsh[3 * k + 1],
-                        p2 = OVERWRITE ? 0.f : dsh[3 * k + 2];
-            dsh[3 * k] = fmaf(Y[k], dcol[0], p0);
-            dsh[3 * k + 1] = fmaf(Y[k], dcol[1], p1);
-            dsh[3 * k + 2] = fmaf(Y[k], dcol[2], p2);
+        for (int k = 0; k < 16; ++k) {
+            const bool act = k < K;
+            wk[k] = act ? fmaf(cf[3 * k], dcol[0], fmaf(cf[3 * k + 1], dcol[1], cf[3 * k + 2] * dcol[2])) : 0.f;
+#pragma unroll
+            for (int c = 0; c < 3; ++c) out[3 * k + c] = act ? Y[k] * dcol[c] : 0.f;
         }
+        float4* d4 = reinterpret_cast<float4*>(dsh);
+        if (!OVERWRITE) {
+#pragma unroll
+            for (int q = 0; q < 12; ++q) {
+                const float4 p = d4[q];
+                out[4 * q] += p.x;
+                out[4 * q + 1] += p.y;
+                out[4 * q + 2] += p.z;
+                out[4 * q + 3] += p.w;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 12; ++q) d4[q] = make_float4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (k < K) {
+                const float c0 = shg[3 * k], c1 = shg[3 * k + 1], c2 = shg[3 * k + 2];
+                wk[k] = fmaf(c0, dcol[0], fmaf(c1, dcol[1], c2 * dcol[2]));
+                const float p0 = OVERWRITE ? 0.f : dsh[3 * k], p1 = OVERWRITE ? 0.f : dsh[3 * k + 1],
+                            p2 = OVERWRITE ? 0.f : dsh[3 * k + 2];
+                dsh[3 * k] = fmaf(Y[k], dcol[0], p0);
+                dsh[3 * k + 1] = fmaf(Y[k], dcol[1], p1);
+                dsh[3 * k + 2] = fmaf(Y[k], dcol[2], p2);
+            }
+        }
+        if (OVERWRITE)
+            for (int e = 3 * K; e < 3 * sh_rows; ++e) dsh[e] = 0.f;
     }
-    if (OVERWRITE)
-        for (int e = 3 * K; e < 3 * sh_rows; ++e) dsh[e] = 0.f;
     float3 gdir = make_float3(0.f, 0.f, 0.f);
     sh_grad_accum(K, dxn, dyn, dzn, wk, gdir);
     const float dd = dxn * gdir.x + dyn * gdir.y + dzn * gdir.z;
@@ -1302,14 +1348,19 @@ hipError_t launch_surfel_preprocess_bwd(const DevCam& cam, int K, int sh_rows, i
     auto* q4 = reinterpret_cast<const float4*>(quats);
     auto* t4 = reinterpret_cast<const float4*>(tf);
     auto* g4 = reinterpret_cast<const float4*>(grad);
-    if (overwrite)
-        k_surfel_preprocess_bwd<true><<<blocks, 64, 0, stream>>>(cam, K, sh_rows, n, means, scales, q4, sh, t4, radii,
-                                                                 clamped, g4, d_means, d_scales, d_quats, d_opac,
-                                                                 d_sh);
-    else
-        k_surfel_preprocess_bwd<false><<<blocks, 64, 0, stream>>>(cam, K, sh_rows, n, means, scales, q4, sh, t4,
-                                                                  radii, clamped, g4, d_means, d_scales, d_quats,
-                                                                  d_opac, d_sh);
+    const bool vec = sh_rows == 16 && ((uintptr_t)sh & 15u) == 0 && ((uintptr_t)d_sh & 15u) == 0;
+    auto go = [&](auto ow, auto vc) {
+        k_surfel_preprocess_bwd<decltype(ow)::value, decltype(vc)::value><<<blocks, 64, 0, stream>>>(
+            cam, K, sh_rows, n, means, scales, q4, sh, t4, radii, clamped, g4, d_means, d_scales, d_quats, d_opac,
+            d_sh);
+    };
+    if (overwrite) {
+        if (vec) go(std::true_type{}, std::true_type{});
+        else go(std::true_type{}, std::false_type{});
+    } else {
+        if (vec) go(std::false_type{}, std::true_type{});
+        else go(std::false_type{}, std::false_type{});
+    }
     return hipGetLastError();
 }
 
