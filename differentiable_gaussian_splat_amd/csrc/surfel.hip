@@ -46,8 +46,7 @@ constexpr int FWD_BATCH = 64;
 static_assert(CKPT_EVERY % FWD_BATCH == 0, "checkpoints fall on batch ends");
 constexpr int BWD_BATCH = 32;
 
-// (Kc, N12.x), (N12.y, N12.z, N02.x, N02.y), (N02.z, dx0, dy0, log2 o), (rgb, -; the
-// forward keeps the entry's list position there),
+// (Kc, N12.x), (N12.y, N12.z, N02.x, N02.y), (N02.z, dx0, dy0, log2 o), (rgb, -),
 // (dx0, dy0) = (ox, oy) - c at the tile's first pixel centre (ox, oy)
 struct alignas(16) SurfelRec {
     float4 a, b, c, d;
@@ -161,6 +160,45 @@ __device__ __forceinline__ void surfel_hit(const SurfelRec& s, float lx, float l
     e.oG = __builtin_amdgcn_exp2f(__fmaf_rn(rho, NEG_HALF_LOG2E, s.c.w));
 }
 
+// The forward's staged surfel: per row of its band the terms of surfel_hit
+// that depend only on the row, (k_j at the row's first column before the
+// column term, dy^2), then (N12, dx0), (log2 o, rgb) and the entry's list
+// position. surfel_hit_row with them takes the same fp32 steps as surfel_hit,
+// so the forward's decisions are the backward's bit for bit.
+struct alignas(16) SurfelRowRec {
+    float4 row[4];
+    float4 n;
+    float4 e;
+    uint32_t pos;
+};
+
+__device__ __forceinline__ void surfel_row_rec(const SurfelRec& s, float ly0, SurfelRowRec& r) {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float dy = s.c.z + (ly0 + (float)i);
+        r.row[i] = make_float4(__fmaf_rn(-dy, s.b.z, s.a.x), __fmaf_rn(-dy, s.b.w, s.a.y),
+                               __fmaf_rn(-dy, s.c.x, s.a.z), dy * dy);
+    }
+    r.n = make_float4(s.a.w, s.b.x, s.b.y, s.c.y);
+    r.e = make_float4(s.c.w, s.d.x, s.d.y, s.d.z);
+}
+
+// surfel_hit's alpha at column lx of a row: K = (k_j at the row, dy^2), N = (N12, dx0)
+__device__ __forceinline__ float surfel_hit_row(float4 K, float4 N, float lo, float lx) {
+#pragma clang fp contract(off)
+    const float dx = N.w + lx;
+    const float k0 = __fmaf_rn(dx, N.x, K.x);
+    const float k1 = __fmaf_rn(dx, N.y, K.y);
+    const float k2 = __fmaf_rn(dx, N.z, K.z);
+    const float inv = __builtin_amdgcn_rcpf(k2);
+    const float u = k0 * inv, v = k1 * inv;
+    const float rho3 = __fmaf_rn(u, u, v * v);
+    const float rho2 = 2.f * __fmaf_rn(dx, dx, K.w);
+    const float rho = rho3 <= rho2 ? rho3 : rho2;
+    return __builtin_amdgcn_exp2f(__fmaf_rn(rho, NEG_HALF_LOG2E, lo));
+}
+
 // Forward: four waves per tile, one per 16x4 band, one pixel per lane
 // (tile 8q + x on workgroups 32q + 8 band + x: its four bands share XCD x).
 // ckpt (nullable): the render checkpoints (layout beside CKPT_EVERY), for the
@@ -170,7 +208,7 @@ __global__ __launch_bounds__(64) void k_surfel_fwd(int W, int H, int TX, int nti
                                                  const float* __restrict__ rgb, float bg0, float bg1, float bg2,
                                                  float* __restrict__ image, float* __restrict__ final_T,
                                                  uint32_t* __restrict__ n_contrib, float4* __restrict__ ckpt) {
-    __shared__ SurfelRec s_rec[FWD_BATCH];
+    __shared__ SurfelRowRec s_rec[FWD_BATCH];
     const int b = blockIdx.x;
     const int tile = ((b >> 5) << 3) + (b & 7), band = (b >> 3) & 3;
     if (tile >= ntiles) return;
@@ -178,7 +216,8 @@ __global__ __launch_bounds__(64) void k_surfel_fwd(int W, int H, int TX, int nti
     const int lane = threadIdx.x;
     const int px = tx * TILE + (lane & 15), py = ty * TILE + band * 4 + (lane >> 4);
     const double ox = (double)(tx * TILE) + 0.5, oy = (double)(ty * TILE) + 0.5;
-    const float lx = (float)(lane & 15), ly = (float)(band * 4 + (lane >> 4));
+    const float lx = (float)(lane & 15);
+    const int row = lane >> 4;  // the lane's row of the band
     float T = 1.f, C0 = 0.f, C1 = 0.f, C2 = 0.f;
     // an entry blends where alpha >= thr: ALPHA_MIN while the pixel walks, 2 (above any alpha) once it has
     // stopped or lies outside the image
@@ -193,10 +232,12 @@ __global__ __launch_bounds__(64) void k_surfel_fwd(int W, int H, int TX, int nti
         if (!__any(thr < 1.f)) break;
         const uint32_t idx = bs + lane;
         bool miss = true;
-        SurfelRec rec;
+        SurfelRowRec rec;
         if (idx < rg.y) {
             const uint32_t g = values[idx];
-            stage_surfel(g, tf, rgb, rec, ox, oy);
+            SurfelRec full;
+            stage_surfel(g, tf, rgb, full, ox, oy);
+            surfel_row_rec(full, (float)(band * 4), rec);
             miss = SurfelReach(tf[3 * (size_t)g], tf[3 * (size_t)g + 1], tf[3 * (size_t)g + 2])
                        .misses(bx_lo, bx_hi, by_lo, by_hi);
         }
@@ -205,34 +246,36 @@ __global__ __launch_bounds__(64) void k_surfel_fwd(int W, int H, int TX, int nti
         const uint64_t keep = __ballot(!miss);
         const int cnt = __popcll(keep);
         if (!miss) {
-            rec.d.w = __uint_as_float(bs - rg.x + 1 + (uint32_t)lane);
+            rec.pos = bs - rg.x + 1 + (uint32_t)lane;
             s_rec[__builtin_amdgcn_mbcnt_hi((uint32_t)(keep >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)keep, 0u))] =
                 rec;
         }
         __syncthreads();
         // entries in runs of 8 (unrolled, one exit test each), the walk test between runs
         for (int m0 = 0; m0 < cnt; m0 += 8) {
-            uint32_t run_off = (uint32_t)m0 * (uint32_t)sizeof(SurfelRec);
+            uint32_t run_off = (uint32_t)m0 * (uint32_t)sizeof(SurfelRowRec);
             asm volatile("" : "+v"(run_off));  // one base register per run (opaque to the compiler)
-            const SurfelRec* run = reinterpret_cast<const SurfelRec*>(reinterpret_cast<const char*>(s_rec) + run_off);
+            const SurfelRowRec* run =
+                reinterpret_cast<const SurfelRowRec*>(reinterpret_cast<const char*>(s_rec) + run_off);
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 if (m0 + m >= cnt) break;
-                SurfelHit e;
-                surfel_hit(run[m], lx, ly, e);
-                const float4 D = run[m].d;
-                const float al = fminf(ALPHA_MAX, e.oG);
+                const float4 D = run[m].e;  // (log2 o, rgb)
+                const float oG = surfel_hit_row(run[m].row[row], run[m].n, D.x, lx);
+                const uint32_t pos = run[m].pos;
+                const float al = fminf(ALPHA_MAX, oG);
                 const bool pass = al >= thr;
                 const float Tn = __fmaf_rn(-al, T, T);
                 const bool stop = pass && Tn < T_MIN;  // the entry would end the pixel: not blended
                 const bool blend = pass && !stop;
                 thr = stop ? 2.f : thr;
                 const float wt = blend ? al * T : 0.f;
-                C0 = fmaf(D.x, wt, C0);
-                C1 = fmaf(D.y, wt, C1);
-                C2 = fmaf(D.z, wt, C2);
+                C0 = fmaf(D.y, wt, C0);
+                C1 = fmaf(D.z, wt, C1);
+                C2 = fmaf(D.w, wt, C2);
                 T = blend ? Tn : T;
-                last = blend ? __float_as_uint(D.w) : last;
+                last = blend ? pos : last;
+                asm volatile("" : "+v"(last) : "v"(pos));  // pos is read with the record, not under the mask
             }
             if (!__any(thr < 1.f)) break;
         }
