@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "common.hpp"
+#include "pieces.hpp"
 
 namespace gs {
 
@@ -51,17 +52,6 @@ hipError_t launch_surfel_render_bwd(int W, int H, int TX, int TY, const uint32_t
                                     hipStream_t stream);
 constexpr int SURFEL_GRAD_STRIDE = 16;  // floats per surfel record of pixel sums
 
-// Render checkpoints (one view's tile grid, written by the forward of 3D
-// Gaussians or of surfels): for each tile, the forward's per-pixel state
-// (T, C) after list entries CKPT_EVERY k - 1, k = 1..CKPT_SLOTS, then the
-// pixel's final colour: (CKPT_SLOTS + 1) x 256 float4 per tile, pixel (row r,
-// column c) of the tile at float4 16 r + c of a slot. A slot is written only
-// when the tile's band wave walks past its entry; the backward reads only such
-// slots. After all tiles' slots, one uint4 per tile: each row band's walk (its
-// deepest blended entry), always written.
-constexpr int PIECES_CHUNK = 1024;  // tiles per dispatch chunk of the pieces backward
-constexpr int CKPT_EVERY = 256;
-constexpr int CKPT_SLOTS = 4;
 
 // The same for V views of one image size (per-view arrays of V x n entries).
 hipError_t launch_preprocess_views(const CamSet& cams, int V, int K, int sh_rows, float lowpass, float near_plane,

@@ -663,51 +663,14 @@ __global__ __launch_bounds__(64) void k_render_bwd_pieces(int W, int H, int TX, 
                                                         const float* __restrict__ dL_dimage,
                                                         float* __restrict__ grad2d, int direct_max = -1) {
     __shared__ BwdShared<NB> sh;
-    constexpr int PIECES = CKPT_SLOTS + 1;  // slots in the checkpoint buffer per tile
-    constexpr int WAVES = CKPT_SLOTS + 2;   // waves per tile
-    const int b = blockIdx.x;
-    // Dispatch order, by chunks of PIECES_CHUNK tiles: the chunk's later waves (most return at
-    // once), then its first pieces. A deep tile's pieces start together, and the first
-    // pieces of the early chunks do not wait behind every tile's later waves (one chunk
-    // for the whole grid: 0.466 -> 0.451 ms on 1M Gaussians at 1080p, 0.572 -> 0.567 ms on
-    // 20k large ones).
-    const int cb = b / (WAVES * PIECES_CHUNK), r = b - cb * WAVES * PIECES_CHUNK;
-    const int t0 = cb * PIECES_CHUNK, tn = min(PIECES_CHUNK, ntiles - t0);
-    if (r >= WAVES * tn) return;  // past the last tile
-    int w, tile;
-    if (r < (WAVES - 1) * tn) {
-        w = 1 + r / tn;
-        tile = t0 + r % tn;
-    } else {
-        w = 0;
-        tile = t0 + r - (WAVES - 1) * tn;
-    }
-    // the tile's walk, from its row bands' walks the forward left after the checkpoints, at most
-    // the list's length
-    const uint4 bw = reinterpret_cast<const uint4*>(ckpt + (size_t)ntiles * PIECES * 256)[tile];
-    const uint2 rg = ranges[tile];
-    uint32_t walk = min(max(max(bw.x, bw.y), max(bw.z, bw.w)), rg.y - rg.x);
-    // pieces of CKPT_EVERY entries; a walk longer than the checkpoints reach ends in a tail
-    // piece from the last checkpoint on, shared by two waves by row bands
-    const int need = (int)((walk + CKPT_EVERY - 1) / CKPT_EVERY);
-    const bool deep = need > PIECES;
-    int piece = w;
-    uint32_t sel = 0xFu;
-    if (deep) {
-        if (w >= CKPT_SLOTS) {  // the tail, bands 0-1 or 2-3
-            piece = CKPT_SLOTS;
-            sel = w == CKPT_SLOTS ? 0x3u : 0xCu;
-        }
-    } else if (w >= max(need, 1)) {
-        return;
-    }
-    const int pieces = deep ? PIECES : need;
-    const bool tail = piece >= pieces - 1;  // the last piece walks to the end from the final state
-    const int lo = piece * CKPT_EVERY, hi = tail ? INT32_MAX : lo + CKPT_EVERY;
-    const float4* tck = ckpt + (size_t)tile * PIECES * 256;
-    bwd_walk<4, NB, false, ADAPT>(tile, 0, sel, lo, hi, tail ? nullptr : tck + (size_t)piece * 256,
-                                  tck + CKPT_SLOTS * 256, bw, W, H, TX, TY, ranges, values, means2d, conic_op, rgb, bg0,
-                                  bg1, bg2, final_T, n_contrib, dL_dimage, grad2d, nullptr, sh, direct_max);
+    // the pieces and their dispatch order: piece_work (chunks of PIECES_CHUNK tiles measured against
+    // one chunk for the whole grid: 0.466 -> 0.451 ms on 1M Gaussians at 1080p, 0.572 -> 0.567 ms on
+    // 20k large ones)
+    PieceWork pw;
+    if (!piece_work(blockIdx.x, ntiles, ckpt, ranges, pw)) return;
+    bwd_walk<4, NB, false, ADAPT>(pw.tile, 0, pw.sel, pw.lo, pw.hi, pw.ck, pw.ck_end, pw.bw, W, H, TX, TY, ranges,
+                                  values, means2d, conic_op, rgb, bg0, bg1, bg2, final_T, n_contrib, dL_dimage, grad2d,
+                                  nullptr, sh, direct_max);
 }
 
 // Measurement: the work of one view's blending, counted with the forward's own

@@ -511,13 +511,9 @@ __global__ __launch_bounds__(64) void k_surfel_bwd(int W, int H, int TX, const u
                          values, tf, rgb, bg0, bg1, bg2, final_T, n_contrib, dL_dimage, grad, sh);
 }
 
-// The backward cut along deep tiles' walks, from the forward's checkpoints: a
-// tile gets one wave per piece of CKPT_EVERY entries, each piece starting from
-// the checkpoint after its last entry, so the pieces are independent; a walk
-// past the last checkpoint ends in a tail piece from the final state that two
-// waves share by row bands. Dispatch order as the 3D backward's pieces: by
-// chunks of PIECES_CHUNK tiles, the chunk's later waves first (most return at
-// once), then its first pieces.
+// The backward cut along deep tiles' walks, from the forward's checkpoints
+// (piece_work: one wave per piece of CKPT_EVERY entries, each starting from
+// the checkpoint after its last entry, so the pieces are independent).
 __global__ __launch_bounds__(64) void k_surfel_bwd_pieces(int W, int H, int TX, int ntiles,
                                                         const float4* __restrict__ ckpt,
                                                         const uint2* __restrict__ ranges,
@@ -529,43 +525,10 @@ __global__ __launch_bounds__(64) void k_surfel_bwd_pieces(int W, int H, int TX, 
                                                         const float* __restrict__ dL_dimage,
                                                         float* __restrict__ grad) {
     __shared__ SurfelBwdShared<BWD_BATCH> sh;
-    constexpr int PIECES = CKPT_SLOTS + 1;  // slots in the checkpoint buffer per tile
-    constexpr int WAVES = CKPT_SLOTS + 2;   // waves per tile
-    const int b = blockIdx.x;
-    const int cb = b / (WAVES * PIECES_CHUNK), r = b - cb * WAVES * PIECES_CHUNK;
-    const int t0 = cb * PIECES_CHUNK, tn = min(PIECES_CHUNK, ntiles - t0);
-    if (r >= WAVES * tn) return;  // past the last tile
-    int w, tile;
-    if (r < (WAVES - 1) * tn) {
-        w = 1 + r / tn;
-        tile = t0 + r % tn;
-    } else {
-        w = 0;
-        tile = t0 + r - (WAVES - 1) * tn;
-    }
-    // the tile's walk, from its row bands' walks the forward left after the checkpoints, at most
-    // the list's length
-    const uint4 bw = reinterpret_cast<const uint4*>(ckpt + (size_t)ntiles * PIECES * 256)[tile];
-    const uint2 rg = ranges[tile];
-    const uint32_t walk = min(max(max(bw.x, bw.y), max(bw.z, bw.w)), rg.y - rg.x);
-    const int need = (int)((walk + CKPT_EVERY - 1) / CKPT_EVERY);
-    const bool deep = need > PIECES;
-    int piece = w;
-    uint32_t sel = 0xFu;
-    if (deep) {
-        if (w >= CKPT_SLOTS) {  // the tail, bands 0-1 or 2-3
-            piece = CKPT_SLOTS;
-            sel = w == CKPT_SLOTS ? 0x3u : 0xCu;
-        }
-    } else if (w >= max(need, 1)) {
-        return;
-    }
-    const int pieces = deep ? PIECES : need;
-    const bool tail = piece >= pieces - 1;  // the last piece walks to the end from the final state
-    const int lo = piece * CKPT_EVERY, hi = tail ? INT32_MAX : lo + CKPT_EVERY;
-    const float4* tck = ckpt + (size_t)tile * PIECES * 256;
-    surfel_bwd_walk<4>(tile, 0, sel, lo, hi, tail ? nullptr : tck + (size_t)piece * 256, tck + CKPT_SLOTS * 256, bw, W,
-                       H, TX, ranges, values, tf, rgb, bg0, bg1, bg2, final_T, n_contrib, dL_dimage, grad, sh);
+    PieceWork pw;
+    if (!piece_work(blockIdx.x, ntiles, ckpt, ranges, pw)) return;
+    surfel_bwd_walk<4>(pw.tile, 0, pw.sel, pw.lo, pw.hi, pw.ck, pw.ck_end, pw.bw, W, H, TX, ranges, values, tf, rgb,
+                       bg0, bg1, bg2, final_T, n_contrib, dL_dimage, grad, sh);
 }
 
 }  // namespace
