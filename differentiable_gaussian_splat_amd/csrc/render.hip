@@ -818,6 +818,7 @@ __global__ __launch_bounds__(64) void k_render_counts(int W, int H, int TX, int 
 // tile.
 constexpr int FWD_PPL = 1;
 constexpr int BWD_BATCH = 32;
+constexpr int PIECES_BATCH = 64;  // the pieces backward's batch (its walks are the deep ones)
 constexpr uint32_t BWD_SPLIT_WALK = 512;
 
 // Backward layouts by launch size (tiles over all views of the launch).
@@ -859,7 +860,7 @@ hipError_t launch_render_bwd(int views, int W, int H, int TX, int TY, const uint
     const float2* m2 = reinterpret_cast<const float2*>(means2d);
     const float4* co = reinterpret_cast<const float4*>(conic_op);
     if (ckpt && views == 1 && bwd_layout(ntiles) == BwdLayout::Split) {
-        k_render_bwd_pieces<BWD_BATCH><<<(CKPT_SLOTS + 2) * PIECES_CHUNK * ((ntiles + PIECES_CHUNK - 1) / PIECES_CHUNK),
+        k_render_bwd_pieces<PIECES_BATCH><<<(CKPT_SLOTS + 2) * PIECES_CHUNK * ((ntiles + PIECES_CHUNK - 1) / PIECES_CHUNK),
                                          64, 0, stream>>>(
             W, H, TX, TY, ntiles, reinterpret_cast<const float4*>(ckpt), rg, values, m2, co, rgb, bg[0], bg[1], bg[2],
             final_T, n_contrib, dL_dimage, grad2d);
@@ -894,7 +895,7 @@ hipError_t launch_render_bwd_adaptive(int W, int H, int TX, int TY, const uint32
     const int ntiles = TX * TY;
     if (ntiles == 0) return hipSuccess;
     if (!ckpt || bwd_layout(ntiles) != BwdLayout::Split) return hipErrorInvalidValue;
-    k_render_bwd_pieces<BWD_BATCH, true>
+    k_render_bwd_pieces<PIECES_BATCH, true>
         <<<(CKPT_SLOTS + 2) * PIECES_CHUNK * ((ntiles + PIECES_CHUNK - 1) / PIECES_CHUNK), 64, 0, stream>>>(
             W, H, TX, TY, ntiles, reinterpret_cast<const float4*>(ckpt), reinterpret_cast<const uint2*>(ranges), values,
             reinterpret_cast<const float2*>(means2d), reinterpret_cast<const float4*>(conic_op), rgb, bg[0], bg[1],
