@@ -14,7 +14,8 @@ namespace gs {
 // slot. A slot is written only when the tile's band wave walks past its entry;
 // the backward reads only such slots. After all tiles' slots, one uint4 per
 // tile: each row band's walk (its deepest blended entry), always written.
-constexpr int PIECES_CHUNK = 1024;  // tiles per dispatch chunk of the pieces backward
+constexpr int PIECES_CHUNK = 1024;         // tiles per dispatch chunk of the 3D pieces backward
+constexpr int SURFEL_PIECES_CHUNK = 2048;  // and of the surfel one
 constexpr int CKPT_EVERY = 256;
 constexpr int CKPT_SLOTS = 4;
 
@@ -30,20 +31,20 @@ struct PieceWork {
     uint4 bw;
 };
 
-// Block b of a pieces launch ((CKPT_SLOTS + 2) PIECES_CHUNK blocks per chunk of
-// PIECES_CHUNK tiles): false when it has no work. A tile gets one wave per
+// Block b of a pieces launch ((CKPT_SLOTS + 2) chunk blocks per chunk of
+// `chunk` tiles): false when it has no work. A tile gets one wave per
 // piece of CKPT_EVERY entries, each piece starting from the checkpoint after
 // its last entry; a walk past the last checkpoint ends in a tail piece from
 // the final state that two waves share by row bands (0-1 and 2-3). Dispatch
 // order, chunk by chunk: the chunk's later waves (most return at once), then
 // its first pieces, so that a deep tile's pieces start together and the first
 // pieces of the early chunks do not wait behind every tile's later waves.
-__device__ __forceinline__ bool piece_work(int b, int ntiles, const float4* __restrict__ ckpt,
+__device__ __forceinline__ bool piece_work(int b, int ntiles, int chunk, const float4* __restrict__ ckpt,
                                            const uint2* __restrict__ ranges, PieceWork& pw) {
     constexpr int PIECES = CKPT_SLOTS + 1;  // slots in the checkpoint buffer per tile
     constexpr int WAVES = CKPT_SLOTS + 2;   // waves per tile
-    const int cb = b / (WAVES * PIECES_CHUNK), r = b - cb * WAVES * PIECES_CHUNK;
-    const int t0 = cb * PIECES_CHUNK, tn = min(PIECES_CHUNK, ntiles - t0);
+    const int cb = b / (WAVES * chunk), r = b - cb * WAVES * chunk;
+    const int t0 = cb * chunk, tn = min(chunk, ntiles - t0);
     if (r >= WAVES * tn) return false;  // past the last tile
     int w, tile;
     if (r < (WAVES - 1) * tn) {

@@ -667,7 +667,7 @@ __global__ __launch_bounds__(64) void k_render_bwd_pieces(int W, int H, int TX, 
     // one chunk for the whole grid: 0.466 -> 0.451 ms on 1M Gaussians at 1080p, 0.572 -> 0.567 ms on
     // 20k large ones)
     PieceWork pw;
-    if (!piece_work(blockIdx.x, ntiles, ckpt, ranges, pw)) return;
+    if (!piece_work(blockIdx.x, ntiles, PIECES_CHUNK, ckpt, ranges, pw)) return;
     bwd_walk<4, NB, false, ADAPT>(pw.tile, 0, pw.sel, pw.lo, pw.hi, pw.ck, pw.ck_end, pw.bw, W, H, TX, TY, ranges,
                                   values, means2d, conic_op, rgb, bg0, bg1, bg2, final_T, n_contrib, dL_dimage, grad2d,
                                   nullptr, sh, direct_max);

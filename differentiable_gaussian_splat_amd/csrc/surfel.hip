@@ -526,7 +526,7 @@ __global__ __launch_bounds__(64) void k_surfel_bwd_pieces(int W, int H, int TX, 
                                                         float* __restrict__ grad) {
     __shared__ SurfelBwdShared<BWD_BATCH> sh;
     PieceWork pw;
-    if (!piece_work(blockIdx.x, ntiles, ckpt, ranges, pw)) return;
+    if (!piece_work(blockIdx.x, ntiles, SURFEL_PIECES_CHUNK, ckpt, ranges, pw)) return;
     surfel_bwd_walk<4>(pw.tile, 0, pw.sel, pw.lo, pw.hi, pw.ck, pw.ck_end, pw.bw, W, H, TX, ranges, values, tf, rgb,
                        bg0, bg1, bg2, final_T, n_contrib, dL_dimage, grad, sh);
 }
@@ -555,8 +555,9 @@ hipError_t launch_surfel_render_bwd(int W, int H, int TX, int TY, const uint32_t
     const uint2* rg = reinterpret_cast<const uint2*>(ranges);
     const float4* t4 = reinterpret_cast<const float4*>(tf);
     if (ckpt && render_ckpt_bytes(TX, TY)) {  // deep tiles cut into pieces from the forward's checkpoints
-        k_surfel_bwd_pieces<<<(CKPT_SLOTS + 2) * PIECES_CHUNK * ((ntiles + PIECES_CHUNK - 1) / PIECES_CHUNK), 64, 0,
-                              stream>>>(W, H, TX, ntiles, reinterpret_cast<const float4*>(ckpt), rg, values, t4, rgb,
+        k_surfel_bwd_pieces<<<(CKPT_SLOTS + 2) * SURFEL_PIECES_CHUNK *
+                                  ((ntiles + SURFEL_PIECES_CHUNK - 1) / SURFEL_PIECES_CHUNK),
+                              64, 0, stream>>>(W, H, TX, ntiles, reinterpret_cast<const float4*>(ckpt), rg, values, t4, rgb,
                                         bg[0], bg[1], bg[2], final_T, n_contrib, dL_dimage, grad);
         return hipGetLastError();
     }
