@@ -292,6 +292,8 @@ hipError_t scan(Load ld, Store st, int n, const u64* dcount, u64* partials, u64*
 //     pass's output offsets, digit-major: offset[b][d] = sum over digits < d of
 //     their totals + sum over blocks < b of digit d's counts. It also clears
 //     the next pass's totals (spare[RT][256]), so passes alternate two buffers.
+//     With up to RADIX_INLINE_BLOCKS blocks the scatter computes the same
+//     offsets itself and this launch is left out;
 //   k_radix_scatter: stable scatter with those offsets.
 constexpr int PIECE = 256;           // super-tile entries one wave walks in the per-tile passes
 constexpr int RB = 1024;             // threads per radix block (16 waves)
@@ -439,27 +441,103 @@ __global__ __launch_bounds__(64) void k_radix_offsets(int nblocks, uint32_t* __r
     if (lane < RT) spare[lane * 256 + d] = 0u;
 }
 
+// The super-tile table a grouping pass can write beside its offsets (see
+// k_radix_offsets<true>); pfirst == nullptr: none.
+struct PieceTable {
+    int S = 0;
+    uint2* sr = nullptr;
+    uint32_t* pfirst = nullptr;
+    u64* npieces = nullptr;
+};
+
+// Wave 0 of a block: digit d's first output position (the exclusive scan of
+// the digit totals, summed over the RT rows of tot) into s_base[d]; with
+// `table` (block 0 of a grouping pass), also the super-tile ranges, first
+// pieces and piece count that k_radix_offsets<true> writes.
+__device__ __forceinline__ void digit_bases(const uint32_t* __restrict__ tot, uint32_t* s_base, const PieceTable& pt,
+                                            bool table) {
+    const int lane = threadIdx.x & 63;
+    uint32_t t[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const uint4 t4 = reinterpret_cast<const uint4*>(tot + r * 256)[lane];
+        t[0] += t4.x;
+        t[1] += t4.y;
+        t[2] += t4.z;
+        t[3] += t4.w;
+    }
+    const uint32_t sum = t[0] + t[1] + t[2] + t[3];
+    uint32_t x = sum;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)x, off);
+        if (lane >= off) x += y;
+    }
+    uint32_t b[4];
+    uint32_t run = x - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        b[i] = run;
+        run += t[i];
+    }
+    reinterpret_cast<uint4*>(s_base)[lane] = make_uint4(b[0], b[1], b[2], b[3]);
+    if (table) {
+        uint32_t pc[4], ps = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pc[i] = (t[i] + PIECE - 1) / PIECE;
+            ps += pc[i];
+        }
+        uint32_t y = ps;
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t z = (uint32_t)__shfl_up((int)y, off);
+            if (lane >= off) y += z;
+        }
+        uint32_t prun = y - ps;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d = 4 * lane + i;
+            if (d < pt.S) {
+                pt.sr[d] = make_uint2(b[i], b[i] + t[i]);
+                pt.pfirst[d] = prun;
+            }
+            prun += pc[i];
+        }
+        if (lane == 63) *pt.npieces = y;
+    }
+}
+
 // Stable scatter of one digit. Wave w owns the block's elements
 // [w RE/RW, (w+1) RE/RW) in rounds of 64 consecutive ones; within a round,
 // lanes with equal digits are matched by ballots and ranked against the wave's
 // own LDS counters (no barrier per round); after one barrier the per-digit
 // wave offsets are combined, the block is reordered in LDS by (digit, rank),
 // and written out so that each digit's elements form one contiguous run.
+// The block's output offsets: from k_radix_offsets' table (offsets, INLINE
+// false), or (INLINE) computed here from the per-block counts hist and the
+// digit totals dtot: digit d's base plus its counts in the blocks before this
+// one, summed by the 16 waves over rows w, w + 16, ... while the keys load;
+// block 0 then also does k_radix_offsets' other work (clearing spare, the
+// piece table).
+template <bool INLINE>
 __global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem src, int n, const u64* dcount, int shift, int bits,
                                                     const uint32_t* __restrict__ offsets,
-                                                    uint32_t* __restrict__ keys_out,
+                                                    const uint32_t* __restrict__ dtot, uint32_t* __restrict__ spare,
+                                                    PieceTable pt, uint32_t* __restrict__ keys_out,
                                                     uint32_t* __restrict__ vals_out) {
     __shared__ uint32_t s_keys[RE];
-    __shared__ uint32_t s_vals[RE];
+    __shared__ uint32_t s_vals[RE];  // INLINE: first the waves' column sums of hist, 256 words each
     __shared__ uint32_t s_wcnt[RW][256];  // per-wave digit counts, then each wave's first slot per digit
     __shared__ uint32_t s_dstart[256];
     __shared__ uint32_t s_gbase[256];
+    __shared__ uint32_t s_base[256];
     __shared__ uint32_t s_w[4];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (INLINE && blockIdx.x == 0)
+        for (int k = tid; k < RT * 256; k += RB) spare[k] = 0u;
     const int cnt = eff_count(n, dcount);
     const int p0 = blockIdx.x * RE;
     if (p0 >= cnt) return;
     const int p1 = min(cnt, p0 + RE);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const uint32_t mask = (1u << bits) - 1u;
     for (int k = lane; k < 256; k += 64) s_wcnt[w][k] = 0u;
     wave_lds_sync();
@@ -475,7 +553,31 @@ __global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem src, int n, const u
             vv[r] = src.vals[p];
         }
     }
-    if (tid < 256) s_gbase[tid] = offsets[(size_t)blockIdx.x * 256 + tid];  // read after the last barrier below
+    if (INLINE) {
+        const uint4* h4 = reinterpret_cast<const uint4*>(offsets);
+        const int b = blockIdx.x;
+        constexpr int U = 16;
+        uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+        for (int j0 = w; j0 < b; j0 += RW * U) {
+            uint4 v[U];
+#pragma unroll
+            for (int c = 0; c < U; ++c) {
+                const int j = j0 + RW * c;
+                v[c] = j < b ? h4[(size_t)j * 64 + lane] : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int c = 0; c < U; ++c) {
+                acc.x += v[c].x;
+                acc.y += v[c].y;
+                acc.z += v[c].z;
+                acc.w += v[c].w;
+            }
+        }
+        reinterpret_cast<uint4*>(s_vals)[w * 64 + lane] = acc;  // read after the first barrier below
+        if (w == 0) digit_bases(dtot, s_base, pt, b == 0 && pt.pfirst);
+    } else if (tid < 256) {
+        s_gbase[tid] = offsets[(size_t)blockIdx.x * 256 + tid];  // read after the last barrier below
+    }
     const uint64_t lt = lanemask_lt();
 #pragma unroll
     for (int r = 0; r < RR; ++r) {
@@ -506,6 +608,12 @@ __global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem src, int n, const u
             s_wcnt[k][tid] = run;
             run += c;
         }
+        if (INLINE) {
+            uint32_t g = s_base[tid];
+#pragma unroll
+            for (int k = 0; k < RW; ++k) g += s_vals[k * 256 + tid];
+            s_gbase[tid] = g;
+        }
     }
     __syncthreads();
 #pragma unroll
@@ -529,17 +637,12 @@ __global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem src, int n, const u
     }
 }
 
-// The super-tile table a grouping pass can write beside its offsets (see
-// k_radix_offsets<true>); pfirst == nullptr: none.
-struct PieceTable {
-    int S = 0;
-    uint2* sr = nullptr;
-    uint32_t* pfirst = nullptr;
-    u64* npieces = nullptr;
-};
-
 // hist: 256 words per block. rtot: two RT x 256-word total buffers; pass number
-// `pass` adds into rtot[pass & 1] (zero on entry) and clears the other.
+// `pass` adds into rtot[pass & 1] (zero on entry) and clears the other. Up to
+// RADIX_INLINE_BLOCKS blocks the scatter computes its own offsets (the blocks
+// together read nblocks^2 / 2 rows of hist); beyond, k_radix_offsets does.
+constexpr int RADIX_INLINE_BLOCKS = 512;
+
 hipError_t radix_pass(SrcMem src, int n, const u64* dcount, int shift, int bits, uint32_t* hist, uint32_t* rtot,
                       int pass, uint32_t* keys_out, uint32_t* vals_out, hipStream_t s, PieceTable pt = {}) {
     const int nblocks = (n + RE - 1) / RE;
@@ -547,11 +650,17 @@ hipError_t radix_pass(SrcMem src, int n, const u64* dcount, int shift, int bits,
     uint32_t* tot = rtot + RT * 256 * (pass & 1);
     uint32_t* spare = rtot + RT * 256 * ((pass & 1) ^ 1);
     k_radix_hist<<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, tot);
+    if (nblocks <= RADIX_INLINE_BLOCKS) {
+        k_radix_scatter<true><<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, tot, spare, pt, keys_out,
+                                                     vals_out);
+        return hipGetLastError();
+    }
     if (pt.pfirst)
         k_radix_offsets<true><<<256, 64, 0, s>>>(nblocks, hist, tot, spare, pt.S, pt.sr, pt.pfirst, pt.npieces);
     else
         k_radix_offsets<false><<<256, 64, 0, s>>>(nblocks, hist, tot, spare, 0, nullptr, nullptr, nullptr);
-    k_radix_scatter<<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, keys_out, vals_out);
+    k_radix_scatter<false><<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, nullptr, nullptr, {}, keys_out,
+                                                  vals_out);
     return hipGetLastError();
 }
 
@@ -687,24 +796,76 @@ __global__ __launch_bounds__(1024) void k_pair_sum(int nb, const u64* __restrict
 
 // Stable compaction of the visible Gaussians (tiles_touched > 0), in the
 // blocks of ST Gaussians that k_pair_totals counted (vis_scan[b]: visible
-// ones before block b). Visible Gaussian i, the pos-th in index order, gets
-// its depth bits and compact position (the depth sort's keys and values) and
-// its record (index, tile rectangle X0 | X1 << 16, Y0 | Y1 << 16, depth
+// ones before block b, as k_pair_sum scans them). Visible Gaussian i, the
+// pos-th in index order, gets its depth bits and compact position (the depth
+// sort's keys and values) and its record (index, tile rectangle X0 | X1 << 16, Y0 | Y1 << 16, depth
 // bits), written here in index order so that the sorted order later gathers
 // one 16-byte record each. Thread t takes Gaussians base + j SB + t, all
 // loads issued up front; ranks come from one ballot per wave and row j and a
 // scan of the block's 4 SI wave counts (index order is row, wave, lane).
+//
+// SELF (up to COMPACT_SELF_SUM_BLOCKS blocks, in place of k_pair_sum): vis_scan
+// is k_pair_totals' table part itself; each block sums the visible counts of
+// the blocks before it, and block 0 also does k_pair_sum's other work (the
+// totals into counters and host, the digit-total buffers cleared).
+constexpr int COMPACT_SELF_SUM_BLOCKS = 4096;
+
+template <bool SELF>
 __global__ __launch_bounds__(SB) void k_compact_visible(int n, int nper, int TX, int TYv,
                                                       const uint32_t* __restrict__ tiles,
                                                       const float* __restrict__ depths,
                                                       const float2* __restrict__ means2d,
                                                       const int* __restrict__ radii,
                                                       const u64* __restrict__ vis_scan, uint32_t* __restrict__ keys,
-                                                      uint32_t* __restrict__ idx, uint4* __restrict__ crec) {
+                                                      uint32_t* __restrict__ idx, uint4* __restrict__ crec,
+                                                      u64* __restrict__ counters, uint32_t* __restrict__ rtot,
+                                                      int rtot_words, u64* __restrict__ host) {
     static_assert(SI * (SB / 64) == 64, "one lane per (row, wave) count");
     __shared__ uint32_t s_c[SI * (SB / 64)];
+    __shared__ u64 s_v[SB / 64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int base = blockIdx.x * ST;
+    if (SELF && blockIdx.x == 0) {
+        __shared__ u64 s_t[3][SB / 64];
+        for (int k = threadIdx.x; k < rtot_words; k += SB) rtot[k] = 0u;
+        const int nb = gridDim.x;
+        u64 p = 0, p1 = 0, v = 0;
+        for (int k = threadIdx.x; k < nb; k += SB) {
+            p += vis_scan[3 * k];
+            p1 += vis_scan[3 * k + 1];
+            v += vis_scan[3 * k + 2];
+        }
+        for (int off = 32; off > 0; off >>= 1) {
+            p += __shfl_xor(p, off);
+            p1 += __shfl_xor(p1, off);
+            v += __shfl_xor(v, off);
+        }
+        if (lane == 0) {
+            s_t[0][w] = p;
+            s_t[1][w] = p1;
+            s_t[2][w] = v;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            u64 a = 0, c = 0, t = 0;
+            for (int k = 0; k < SB / 64; ++k) {
+                a += s_t[0][k];
+                c += s_t[1][k];
+                t += s_t[2][k];
+            }
+            counters[0] = t;
+            counters[1] = 0ull;
+            counters[2] = a;
+            counters[3] = c;
+            counters[4] = 0ull;
+            host[0] = a;
+            host[1] = c;
+            __threadfence_system();
+        }
+    }
+    u64 vb = 0;  // SELF: visible Gaussians in the blocks before this one
+    if (SELF)
+        for (int k = threadIdx.x; k < (int)blockIdx.x; k += SB) vb += vis_scan[3 * k + 2];
     uint32_t t[SI], d[SI];
     float2 m[SI];
     int rr[SI];
@@ -722,6 +883,10 @@ __global__ __launch_bounds__(SB) void k_compact_visible(int n, int nper, int TX,
         vis[j] = __ballot(base + j * SB + (int)threadIdx.x < n && t[j] > 0u);
         if (lane == 0) s_c[j * (SB / 64) + w] = (uint32_t)__popcll(vis[j]);
     }
+    if (SELF) {
+        for (int off = 32; off > 0; off >>= 1) vb += __shfl_xor(vb, off);
+        if (lane == 0) s_v[w] = vb;
+    }
     __syncthreads();
     // lane k = (row, wave) in index order: exclusive scan of the counts
     const uint32_t c = s_c[lane];
@@ -731,7 +896,13 @@ __global__ __launch_bounds__(SB) void k_compact_visible(int n, int nper, int TX,
         if (lane >= off) x += y;
     }
     const uint32_t excl = x - c;
-    const u64 boff = vis_scan[blockIdx.x];
+    u64 boff = 0;
+    if (SELF) {
+#pragma unroll
+        for (int k = 0; k < SB / 64; ++k) boff += s_v[k];
+    } else {
+        boff = vis_scan[blockIdx.x];
+    }
 #pragma unroll
     for (int j = 0; j < SI; ++j) {
         const uint32_t first = (uint32_t)__builtin_amdgcn_readlane((int)excl, j * (SB / 64) + w);
@@ -750,17 +921,24 @@ __global__ __launch_bounds__(SB) void k_compact_visible(int n, int nper, int TX,
 }
 
 // Per depth-sorted Gaussian i (one gather of its compact record): its record
-// (index, X0 | X1 << 16, Y0 | Y1 << 16, depth bits) and its super-tile count
-// n1[i]; per block of ST Gaussians, the sum of the counts (the reduce step of
-// the scan that gives each Gaussian its first super-tile entry).
+// (index, X0 | X1 << 16, Y0 | Y1 << 16, depth bits); per block of ST
+// Gaussians the sum of their super-tile counts (coarse[b]), and per row of
+// SB of them (row j: Gaussians base + j SB .. + SB - 1) the row's sum
+// (fine[16 b + j]): the reduce step of the scan that gives each Gaussian its
+// first super-tile entry. The 16 row sums come out of one reduce-scatter per
+// wave: four exchanges halve the rows a lane holds (masks 32, 16, 8, 4), two
+// more finish the sums, and lane l ends with row l / 4.
+static_assert(ST == 16 * SB && SI == 16, "16 rows of one block's width per scan block");
+
 __global__ __launch_bounds__(SB) void k_sorted_records(const u64* vis_ptr, const uint32_t* __restrict__ order,
                                                      const uint4* __restrict__ crec, uint4* __restrict__ rec,
-                                                     uint32_t* __restrict__ n1, u64* __restrict__ partials) {
-    __shared__ u64 s_w[SB / 64];
+                                                     u64* __restrict__ coarse, uint32_t* __restrict__ fine) {
+    __shared__ uint32_t s_f[SB / 64][SI];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int cnt = (int)*vis_ptr;
     const int base = blockIdx.x * ST;
-    if (base >= cnt) {  // no Gaussian here: a zero partial, as the scan expects one per block
-        if (threadIdx.x == 0) partials[blockIdx.x] = 0ull;
+    if (base >= cnt) {  // no Gaussian here: a zero sum, for a scan over all blocks
+        if (threadIdx.x == 0) coarse[blockIdx.x] = 0ull;
         return;
     }
     // every gather issued before any is used (at a clamped index past cnt, not stored)
@@ -771,43 +949,117 @@ __global__ __launch_bounds__(SB) void k_sorted_records(const u64* vis_ptr, const
     uint4 rr[SI];
 #pragma unroll
     for (int j = 0; j < SI; ++j) rr[j] = crec[o[j]];
-    u64 sum = 0;
+    uint32_t v[SI];
 #pragma unroll
     for (int j = 0; j < SI; ++j) {
         const int i = base + j * SB + threadIdx.x;
+        v[j] = 0u;
         if (i < cnt) {
             const uint4 r = rr[j];
             rec[i] = r;
-            const uint32_t c = super_count((int)(r.y & 0xffffu), (int)(r.y >> 16), (int)(r.z & 0xffffu),
-                                           (int)(r.z >> 16));
-            n1[i] = c;
-            sum += c;
+            v[j] = super_count((int)(r.y & 0xffffu), (int)(r.y >> 16), (int)(r.z & 0xffffu), (int)(r.z >> 16));
         }
     }
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = sum;
+#pragma unroll
+    for (int m = 32, k = SI / 2; m >= 4; m >>= 1, k >>= 1) {
+        const bool up = (lane & m) != 0;  // keeps the upper half of its rows
+#pragma unroll
+        for (int q = 0; q < k; ++q) {
+            const uint32_t keep = up ? v[q + k] : v[q];
+            const uint32_t give = up ? v[q] : v[q + k];
+            v[q] = keep + (uint32_t)__shfl_xor((int)give, m);
+        }
+    }
+    v[0] += (uint32_t)__shfl_xor((int)v[0], 2);
+    v[0] += (uint32_t)__shfl_xor((int)v[0], 1);
+    if ((lane & 3) == 0) s_f[w][lane >> 2] = v[0];
     __syncthreads();
-    if (threadIdx.x == 0) partials[blockIdx.x] = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+    if (threadIdx.x < 64) {
+        uint32_t f = 0u;
+        if (lane < SI) {
+#pragma unroll
+            for (int k = 0; k < SB / 64; ++k) f += s_f[k][lane];
+            fine[(size_t)blockIdx.x * SI + lane] = f;
+        }
+        u64 t = f;
+        for (int off = 8; off > 0; off >>= 1) t += __shfl_xor(t, off);
+        if (lane == 0) coarse[blockIdx.x] = t;
+    }
 }
 
-// One thread per depth-sorted Gaussian: its entries (super-tile id, sorted
-// index), row-major over its super-tile rectangle.
+// One thread per depth-sorted Gaussian, blocks of SB (block e is row e % 16
+// of k_sorted_records' block e / 16). A Gaussian's first entry is the block's
+// offset (the coarse sums of the scan blocks before its own, or with
+// `scanned` their exclusive scan, plus the row sums before it in its own)
+// plus the exclusive scan of the counts inside the block. Each wave then
+// writes its Gaussians' entries (super-tile id, sorted index) 64 at a time,
+// lane l taking the wave's entry e0 + l: a binary search of the wave's
+// running counts in LDS gives the Gaussian and the entry's place in it,
+// row-major over its super-tile rectangle, so that each store is contiguous.
+// Up to EMIT_SELF_SUM_BLOCKS scan blocks every block sums the coarse sums it
+// needs itself; beyond, k_scan_top scans them first.
+constexpr int EMIT_SELF_SUM_BLOCKS = 512;
+
 __global__ __launch_bounds__(SB) void k_super_emit(const u64* vis_ptr, const uint4* __restrict__ rec,
-                                                 const uint32_t* __restrict__ first, int SX, uint32_t P1,
-                                                 uint32_t* __restrict__ skey, uint32_t* __restrict__ sval) {
-    const int k = blockIdx.x * SB + threadIdx.x;
-    if (k >= (int)*vis_ptr) return;
-    const uint4 r = rec[k];
-    uint32_t pos = first[k];
-    asm volatile("" ::"v"(pos), "v"(r.y), "v"(r.z));  // both loads issued before either is waited on
+                                                 const u64* __restrict__ coarse, const uint32_t* __restrict__ fine,
+                                                 int scanned, int SX, uint32_t P1, uint32_t* __restrict__ skey,
+                                                 uint32_t* __restrict__ sval) {
+    __shared__ uint32_t s_inc[SB];   // per wave: running counts of its Gaussians, inclusive
+    __shared__ uint32_t s_org[SB];   // sx0 | sy0 << 16
+    __shared__ uint32_t s_wid[SB];   // super-tile columns of the rectangle
+    __shared__ uint32_t s_tot[SB / 64];
+    __shared__ u64 s_off[SB / 64];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int cnt = (int)*vis_ptr;
+    const int e = blockIdx.x;
+    if (e * SB >= cnt) return;
+    const int i = e * SB + tid;
+    const uint4 r = rec[min(i, cnt - 1)];  // past cnt: loaded, not used
+    const int q = e >> 4, row = e & 15;
+    u64 off = 0;
+    if (!scanned)
+        for (int k = tid; k < q; k += SB) off += coarse[k];
+    if (tid < row) off += fine[(size_t)q * SI + tid];
     const int sx0 = (int)(r.y & 0xffffu) >> 3, sx1 = (int)(r.y >> 16) >> 3;
     const int sy0 = (int)(r.z & 0xffffu) >> 3, sy1 = (int)(r.z >> 16) >> 3;
-    for (int sy = sy0; sy <= sy1; ++sy)
-        for (int sx = sx0; sx <= sx1; ++sx, ++pos)
-            if (pos < P1) {
-                skey[pos] = (uint32_t)(sy * SX + sx);
-                sval[pos] = (uint32_t)k;
-            }
+    const uint32_t c = i < cnt ? (uint32_t)((sx1 - sx0 + 1) * (sy1 - sy0 + 1)) : 0u;
+    uint32_t x = c;
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)x, o);
+        if (lane >= o) x += y;
+    }
+    for (int o = 32; o > 0; o >>= 1) off += __shfl_xor(off, o);
+    s_inc[tid] = x;
+    s_org[tid] = (uint32_t)sx0 | ((uint32_t)sy0 << 16);
+    s_wid[tid] = (uint32_t)(sx1 - sx0 + 1);
+    if (lane == 63) s_tot[w] = x;
+    if (lane == 0) s_off[w] = off;
+    __syncthreads();
+    u64 boff = scanned ? coarse[q] : 0ull;
+    uint32_t before = 0u;
+#pragma unroll
+    for (int k = 0; k < SB / 64; ++k) {
+        boff += s_off[k];
+        before += k < w ? s_tot[k] : 0u;
+    }
+    const uint32_t wbase = (uint32_t)boff + before, T = s_tot[w];
+    const uint32_t* inc = s_inc + w * 64;
+    for (uint32_t e0 = 0; e0 < T; e0 += 64) {
+        const uint32_t ent = e0 + (uint32_t)lane;
+        if (ent >= T) break;
+        int g = 0;  // the first of the wave's Gaussians whose running count passes ent
+#pragma unroll
+        for (int step = 32; step > 0; step >>= 1)
+            if (inc[g + step - 1] <= ent) g += step;
+        const uint32_t k = ent - (g ? inc[g - 1] : 0u);
+        const uint32_t wid = s_wid[w * 64 + g], org = s_org[w * 64 + g];
+        const uint32_t dy = k / wid, dx = k - dy * wid;
+        const uint32_t pos = wbase + ent;
+        if (pos < P1) {
+            skey[pos] = ((org >> 16) + dy) * (uint32_t)SX + (org & 0xffffu) + dx;
+            sval[pos] = (uint32_t)(e * SB + w * 64 + g);
+        }
+    }
 }
 
 // [first, last + 1) of each super-tile in the grouped entries (left at (0, 0) if empty).
@@ -1143,7 +1395,7 @@ Grid2 super_grid(int TX, int TY) {
     return g;
 }
 
-// Counters (u64): [0] visible, [1] super entries (scan), [2] P, [3] P1, [4] pieces.
+// Counters (u64): [0] visible, [1] zero, [2] P, [3] P1, [4] pieces.
 constexpr int NCOUNTERS = 8;
 
 }  // namespace
@@ -1169,7 +1421,6 @@ BinLayout bin_layout(int64_t n, int64_t capacity, int TX, int TY) {
     L.dkeys[1] = take(4 * nn);
     L.didx[0] = take(4 * nn);
     L.didx[1] = take(4 * nn);
-    L.first = take(4 * nn);
     L.rec = take(16 * nn);
     L.crec = take(16 * nn);
     L.skey[0] = take(4 * cap);  // super entries: at most one per pair
@@ -1189,6 +1440,7 @@ BinLayout bin_layout(int64_t n, int64_t capacity, int TX, int TY) {
     if (S > max_scan) max_scan = S;
     L.partials = take(8 * ((max_scan + ST - 1) / ST + 1));
     L.pair_part = take(8 * 3 * ((nn + ST - 1) / ST));
+    L.fine = take(4 * SI * ((nn + ST - 1) / ST));
     L.hist = take(4 * hist_entries);
     L.counters = take(8 * NCOUNTERS + 4 * 2 * RT * 256);  // counters, then the radix passes' two digit-total buffers
     L.total = off;
@@ -1214,21 +1466,30 @@ hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means
     // the pair counts first, on their way to the host while the rest runs; the
     // same pass counts the visible Gaussians per block for the compaction, and
     // clears both radix total buffers (the depth sort's four passes leave
-    // buffer 0 clear again for the super-tile pass of launch_bin_emit)
+    // buffer 0 clear again for the super-tile pass of launch_bin_emit). Up to
+    // COMPACT_SELF_SUM_BLOCKS blocks the compaction does k_pair_sum's work.
     const int nb = (n + ST - 1) / ST;
+    const bool self_sum = nb <= COMPACT_SELF_SUM_BLOCKS;
     u64* part = reinterpret_cast<u64*>(ws + L.pair_part);
     k_pair_totals<<<nb, SB, 0, s>>>(n, tiles_touched, m2, radii, nper, TX, TYv, part);
-    k_pair_sum<<<1, 1024, 0, s>>>(nb, part, partials, counters, rtot, rtot_words, host);
-    e = hipGetLastError();
-    if (e == hipSuccess) e = hipEventRecord(ev, s);
-    if (e != hipSuccess) return e;
+    if (!self_sum) {
+        k_pair_sum<<<1, 1024, 0, s>>>(nb, part, partials, counters, rtot, rtot_words, host);
+        e = hipGetLastError();
+        if (e == hipSuccess) e = hipEventRecord(ev, s);
+        if (e != hipSuccess) return e;
+    }
     uint32_t* dk[2] = {reinterpret_cast<uint32_t*>(ws + L.dkeys[0]), reinterpret_cast<uint32_t*>(ws + L.dkeys[1])};
     uint32_t* di[2] = {reinterpret_cast<uint32_t*>(ws + L.didx[0]), reinterpret_cast<uint32_t*>(ws + L.didx[1])};
     // 1. visible compaction (index order kept): depth bits, compact positions, records
     uint4* crec = reinterpret_cast<uint4*>(ws + L.crec);
-    k_compact_visible<<<nb, SB, 0, s>>>(n, nper, TX, TYv, tiles_touched, depths, m2, radii, partials, dk[0], di[0],
-                                        crec);
+    if (self_sum)
+        k_compact_visible<true><<<nb, SB, 0, s>>>(n, nper, TX, TYv, tiles_touched, depths, m2, radii, part, dk[0],
+                                                  di[0], crec, counters, rtot, rtot_words, host);
+    else
+        k_compact_visible<false><<<nb, SB, 0, s>>>(n, nper, TX, TYv, tiles_touched, depths, m2, radii, partials,
+                                                   dk[0], di[0], crec, nullptr, nullptr, 0, nullptr);
     e = hipGetLastError();
+    if (e == hipSuccess && self_sum) e = hipEventRecord(ev, s);
     if (e != hipSuccess) return e;
     // 2. stable sort by the 32 depth bits, 4 passes of 8: the result returns to buffer 0
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
@@ -1237,14 +1498,13 @@ hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means
         e = radix_pass(SrcMem{dk[c], di[c]}, n, &counters[0], 8 * pass, 8, hist, rtot, pass, dk[c ^ 1], di[c ^ 1], s);
         if (e != hipSuccess) return e;
     }
-    // 3. per depth-sorted Gaussian: record, super-tile count (in the free depth
-    //    key buffer) and first super-tile entry
-    uint32_t* first = reinterpret_cast<uint32_t*>(ws + L.first);
+    // 3. per depth-sorted Gaussian its record, and per block of them the sum of
+    //    their super-tile counts (scanned here only for more blocks than
+    //    k_super_emit sums itself)
     uint4* rec = reinterpret_cast<uint4*>(ws + L.rec);
-    k_sorted_records<<<nb, SB, 0, s>>>(&counters[0], di[0], crec, rec, dk[1], partials);
-    k_scan_top<<<1, 1024, 0, s>>>(partials, nb, &counters[1]);
-    k_scan_down<LoadPlain, StoreInPlace><<<nb, SB, 0, s>>>(LoadPlain{dk[1]}, StoreInPlace{first}, n, &counters[0],
-                                                          partials);
+    uint32_t* fine = reinterpret_cast<uint32_t*>(ws + L.fine);
+    k_sorted_records<<<nb, SB, 0, s>>>(&counters[0], di[0], crec, rec, partials, fine);
+    if (nb > EMIT_SELF_SUM_BLOCKS) k_scan_top<<<1, 1024, 0, s>>>(partials, nb, nullptr);
     return hipGetLastError();
 }
 
@@ -1256,7 +1516,6 @@ hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const
     u64* partials = reinterpret_cast<u64*>(ws + L.partials);
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
     uint32_t* rtot = reinterpret_cast<uint32_t*>(ws + L.counters) + 2 * NCOUNTERS;
-    const uint32_t* first = reinterpret_cast<const uint32_t*>(ws + L.first);
     const uint4* rec = reinterpret_cast<const uint4*>(ws + L.rec);
     uint32_t* sk[2] = {reinterpret_cast<uint32_t*>(ws + L.skey[0]), reinterpret_cast<uint32_t*>(ws + L.skey[1])};
     uint32_t* sv[2] = {reinterpret_cast<uint32_t*>(ws + L.sval[0]), reinterpret_cast<uint32_t*>(ws + L.sval[1])};
@@ -1268,7 +1527,10 @@ hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const
     const Grid2 G = super_grid(TX, TY);
 
     // 3. super-tile entries in depth order, then grouped by super-tile (stable)
-    k_super_emit<<<(n + SB - 1) / SB, SB, 0, s>>>(&counters[0], rec, first, G.SX, (uint32_t)P1, sk[0], sv[0]);
+    const int nb = (n + ST - 1) / ST;
+    const uint32_t* fine = reinterpret_cast<const uint32_t*>(ws + L.fine);
+    k_super_emit<<<(n + SB - 1) / SB, SB, 0, s>>>(&counters[0], rec, partials, fine, nb > EMIT_SELF_SUM_BLOCKS, G.SX,
+                                                  (uint32_t)P1, sk[0], sv[0]);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int sbits = bits_for(G.S);

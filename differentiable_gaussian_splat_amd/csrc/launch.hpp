@@ -69,7 +69,6 @@ hipError_t launch_preprocess_bwd_views(const CamSet& cams, int V, int K, int sh_
 // Binning. The workspace layout is computed by bin_layout (binsort.hip).
 struct BinLayout {
     size_t dkeys[2], didx[2];  // depth-sort ping-pong (n entries each)
-    size_t first;              // per depth-sorted Gaussian: first super-tile entry (n)
     size_t rec;                // per depth-sorted Gaussian: uint4 record (n)
     size_t crec;               // per visible Gaussian in index order: the same record (n)
     size_t skey[2], sval[2];   // super-tile entries (super-tile id, sorted index), ping-pong (capacity each)
@@ -80,6 +79,7 @@ struct BinLayout {
     size_t tile_total;         // pairs per tile
     size_t partials;           // u64 scan partials
     size_t pair_part;          // u64 per-block partial pair counts
+    size_t fine;               // per row of SB depth-sorted Gaussians: the sum of their super-tile counts
     size_t hist;               // radix histograms
     size_t counters;           // u64 counters
     size_t total;
