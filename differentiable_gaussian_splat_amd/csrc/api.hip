@@ -294,7 +294,7 @@ gs_status gs_bin_sort(const gs_camera* cam, const gs_options* opt, int64_t n, co
             return fail(GS_ERR_CAPACITY, "pair count %llu exceeds capacity %lld", P, (long long)pair_capacity);
         // every super-tile entry holds at least one of the Gaussian's pairs
         if (P1 > P) return fail(GS_ERR_HIP, "super-tile entries %llu exceed pairs %llu", P1, P);
-        return hip_check(gs::launch_bin_emit((int)n, (int)P, (int)P1, c.cam.TX, c.cam.TY, ws, L, keys,
+        return hip_check(gs::launch_bin_emit((int)n, (int)P, (int)P1, c.cam.TX, c.cam.TY, depths, ws, L, keys,
                                              values, ranges, s),
                          "gs_bin_sort(emit)");
     } catch (...) {
@@ -824,8 +824,8 @@ gs_status gs_bin_sort_views(const gs_camera* cams, int32_t n_views, const gs_opt
         if ((int64_t)P > pair_capacity)
             return fail(GS_ERR_CAPACITY, "pair count %llu exceeds capacity %lld", P, (long long)pair_capacity);
         if (P1 > P) return fail(GS_ERR_HIP, "super-tile entries %llu exceed pairs %llu", P1, P);
-        return hip_check(gs::launch_bin_emit((int)total, (int)P, (int)P1, TX, c.V * TY, ws, L, keys, values, ranges,
-                                             s),
+        return hip_check(gs::launch_bin_emit((int)total, (int)P, (int)P1, TX, c.V * TY, depths, ws, L, keys, values,
+                                             ranges, s),
                          "gs_bin_sort_views(emit)");
     } catch (...) {
         return fail(GS_ERR_HIP, "gs_bin_sort_views: unexpected exception");

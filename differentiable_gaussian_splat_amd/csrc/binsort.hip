@@ -302,9 +302,10 @@ constexpr int RW = RB / 64;          // waves per radix block
 constexpr int RR = RE / RB;          // elements per thread
 constexpr int RT = 8;                // rows of the digit-total buffers
 
+template <class V>
 struct SrcMem {
     const uint32_t* keys;
-    const uint32_t* vals;
+    const V* vals;
 };
 
 // Exclusive scan of v over threads 0..255 of the block (other threads pass 0
@@ -324,7 +325,7 @@ __device__ __forceinline__ uint32_t digit_excl_scan(uint32_t v, uint32_t* s_w) {
     return tid < 256 ? pre + x - v : 0u;
 }
 
-__global__ __launch_bounds__(RB) void k_radix_hist(SrcMem src, int n, const u64* dcount, int shift, int bits,
+__global__ __launch_bounds__(RB) void k_radix_hist(const uint32_t* __restrict__ keys, int n, const u64* dcount, int shift, int bits,
                                                  uint32_t* __restrict__ hist, uint32_t* __restrict__ tot) {
     __shared__ uint32_t s_h[RW][256];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(RB) void k_radix_hist(SrcMem src, int n, const u64*
 #pragma unroll
     for (int r = 0; r < RR; ++r) {
         const int p = p0 + (w * RR + r) * 64 + lane;
-        kk[r] = p < p1 ? src.keys[p] : 0u;
+        kk[r] = p < p1 ? keys[p] : 0u;
     }
 #pragma unroll
     for (int r = 0; r < RR; ++r) {
@@ -518,14 +519,15 @@ __device__ __forceinline__ void digit_bases(const uint32_t* __restrict__ tot, ui
 // one, summed by the 16 waves over rows w, w + 16, ... while the keys load;
 // block 0 then also does k_radix_offsets' other work (clearing spare, the
 // piece table).
-template <bool INLINE>
-__global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem src, int n, const u64* dcount, int shift, int bits,
+template <bool INLINE, class V>
+__global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem<V> src, int n, const u64* dcount, int shift, int bits,
                                                     const uint32_t* __restrict__ offsets,
                                                     const uint32_t* __restrict__ dtot, uint32_t* __restrict__ spare,
                                                     PieceTable pt, uint32_t* __restrict__ keys_out,
-                                                    uint32_t* __restrict__ vals_out) {
+                                                    V* __restrict__ vals_out) {
+    static_assert(sizeof(V) * RE >= 16 * RW * 64, "the waves' column sums fit in s_vals");
     __shared__ uint32_t s_keys[RE];
-    __shared__ uint32_t s_vals[RE];  // INLINE: first the waves' column sums of hist, 256 words each
+    __shared__ __align__(16) V s_vals[RE];  // INLINE: first the waves' column sums of hist, 256 words each
     __shared__ uint32_t s_wcnt[RW][256];  // per-wave digit counts, then each wave's first slot per digit
     __shared__ uint32_t s_dstart[256];
     __shared__ uint32_t s_gbase[256];
@@ -541,13 +543,14 @@ __global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem src, int n, const u
     const uint32_t mask = (1u << bits) - 1u;
     for (int k = lane; k < 256; k += 64) s_wcnt[w][k] = 0u;
     wave_lds_sync();
-    uint32_t kk[RR], vv[RR], rk[RR];
+    uint32_t kk[RR], rk[RR];
+    V vv[RR];
     const int ebase = p0 + w * RR * 64 + lane;
 #pragma unroll
     for (int r = 0; r < RR; ++r) {
         const int p = ebase + r * 64;
         kk[r] = 0u;
-        vv[r] = 0u;
+        vv[r] = V{};
         if (p < p1) {
             kk[r] = src.keys[p];
             vv[r] = src.vals[p];
@@ -611,7 +614,7 @@ __global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem src, int n, const u
         if (INLINE) {
             uint32_t g = s_base[tid];
 #pragma unroll
-            for (int k = 0; k < RW; ++k) g += s_vals[k * 256 + tid];
+            for (int k = 0; k < RW; ++k) g += reinterpret_cast<const uint32_t*>(s_vals)[k * 256 + tid];
             s_gbase[tid] = g;
         }
     }
@@ -643,24 +646,25 @@ __global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem src, int n, const u
 // together read nblocks^2 / 2 rows of hist); beyond, k_radix_offsets does.
 constexpr int RADIX_INLINE_BLOCKS = 512;
 
-hipError_t radix_pass(SrcMem src, int n, const u64* dcount, int shift, int bits, uint32_t* hist, uint32_t* rtot,
-                      int pass, uint32_t* keys_out, uint32_t* vals_out, hipStream_t s, PieceTable pt = {}) {
+template <class V>
+hipError_t radix_pass(SrcMem<V> src, int n, const u64* dcount, int shift, int bits, uint32_t* hist, uint32_t* rtot,
+                      int pass, uint32_t* keys_out, V* vals_out, hipStream_t s, PieceTable pt = {}) {
     const int nblocks = (n + RE - 1) / RE;
     if (nblocks == 0) return hipSuccess;
     uint32_t* tot = rtot + RT * 256 * (pass & 1);
     uint32_t* spare = rtot + RT * 256 * ((pass & 1) ^ 1);
-    k_radix_hist<<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, tot);
+    k_radix_hist<<<nblocks, RB, 0, s>>>(src.keys, n, dcount, shift, bits, hist, tot);
     if (nblocks <= RADIX_INLINE_BLOCKS) {
-        k_radix_scatter<true><<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, tot, spare, pt, keys_out,
-                                                     vals_out);
+        k_radix_scatter<true, V><<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, tot, spare, pt, keys_out,
+                                                        vals_out);
         return hipGetLastError();
     }
     if (pt.pfirst)
         k_radix_offsets<true><<<256, 64, 0, s>>>(nblocks, hist, tot, spare, pt.S, pt.sr, pt.pfirst, pt.npieces);
     else
         k_radix_offsets<false><<<256, 64, 0, s>>>(nblocks, hist, tot, spare, 0, nullptr, nullptr, nullptr);
-    k_radix_scatter<false><<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, nullptr, nullptr, {}, keys_out,
-                                                  vals_out);
+    k_radix_scatter<false, V><<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, nullptr, nullptr, {},
+                                                     keys_out, vals_out);
     return hipGetLastError();
 }
 
@@ -992,10 +996,14 @@ __global__ __launch_bounds__(SB) void k_sorted_records(const u64* vis_ptr, const
 // offset (the coarse sums of the scan blocks before its own, or with
 // `scanned` their exclusive scan, plus the row sums before it in its own)
 // plus the exclusive scan of the counts inside the block. Each wave then
-// writes its Gaussians' entries (super-tile id, sorted index) 64 at a time,
-// lane l taking the wave's entry e0 + l: a binary search of the wave's
-// running counts in LDS gives the Gaussian and the entry's place in it,
-// row-major over its super-tile rectangle, so that each store is contiguous.
+// writes its Gaussians' entries 64 at a time, lane l taking the wave's entry
+// e0 + l: a binary search of the wave's running counts in LDS gives the
+// Gaussian and the entry's place in it, row-major over its super-tile
+// rectangle, so that each store is contiguous. An entry is the super-tile id
+// (the key of the grouping pass) and its payload: the Gaussian's index and
+// its tile rectangle clipped to the super-tile, relative to its corner
+// (cx0 | cx1 << 3 | cy0 << 6 | cy1 << 9), which is all the per-tile passes
+// read of it.
 // Up to EMIT_SELF_SUM_BLOCKS scan blocks every block sums the coarse sums it
 // needs itself; beyond, k_scan_top scans them first.
 constexpr int EMIT_SELF_SUM_BLOCKS = 512;
@@ -1003,9 +1011,9 @@ constexpr int EMIT_SELF_SUM_BLOCKS = 512;
 __global__ __launch_bounds__(SB) void k_super_emit(const u64* vis_ptr, const uint4* __restrict__ rec,
                                                  const u64* __restrict__ coarse, const uint32_t* __restrict__ fine,
                                                  int scanned, int SX, uint32_t P1, uint32_t* __restrict__ skey,
-                                                 uint32_t* __restrict__ sval) {
+                                                 uint2* __restrict__ spay) {
     __shared__ uint32_t s_inc[SB];   // per wave: running counts of its Gaussians, inclusive
-    __shared__ uint32_t s_org[SB];   // sx0 | sy0 << 16
+    __shared__ uint4 s_rec[SB];      // the Gaussians' records
     __shared__ uint32_t s_wid[SB];   // super-tile columns of the rectangle
     __shared__ uint32_t s_tot[SB / 64];
     __shared__ u64 s_off[SB / 64];
@@ -1030,7 +1038,7 @@ __global__ __launch_bounds__(SB) void k_super_emit(const u64* vis_ptr, const uin
     }
     for (int o = 32; o > 0; o >>= 1) off += __shfl_xor(off, o);
     s_inc[tid] = x;
-    s_org[tid] = (uint32_t)sx0 | ((uint32_t)sy0 << 16);
+    s_rec[tid] = r;
     s_wid[tid] = (uint32_t)(sx1 - sx0 + 1);
     if (lane == 63) s_tot[w] = x;
     if (lane == 0) s_off[w] = off;
@@ -1052,12 +1060,16 @@ __global__ __launch_bounds__(SB) void k_super_emit(const u64* vis_ptr, const uin
         for (int step = 32; step > 0; step >>= 1)
             if (inc[g + step - 1] <= ent) g += step;
         const uint32_t k = ent - (g ? inc[g - 1] : 0u);
-        const uint32_t wid = s_wid[w * 64 + g], org = s_org[w * 64 + g];
+        const uint32_t wid = s_wid[w * 64 + g];
+        const uint4 gr = s_rec[w * 64 + g];
         const uint32_t dy = k / wid, dx = k - dy * wid;
+        const int sx = (int)((gr.y & 0xffffu) >> 3) + (int)dx, sy = (int)((gr.z & 0xffffu) >> 3) + (int)dy;
+        const int cx0 = max((int)(gr.y & 0xffffu) - SUPER * sx, 0), cx1 = min((int)(gr.y >> 16) - SUPER * sx, SUPER - 1);
+        const int cy0 = max((int)(gr.z & 0xffffu) - SUPER * sy, 0), cy1 = min((int)(gr.z >> 16) - SUPER * sy, SUPER - 1);
         const uint32_t pos = wbase + ent;
         if (pos < P1) {
-            skey[pos] = ((org >> 16) + dy) * (uint32_t)SX + (org & 0xffffu) + dx;
-            sval[pos] = (uint32_t)(e * SB + w * 64 + g);
+            skey[pos] = (uint32_t)(sy * SX + sx);
+            spay[pos] = make_uint2(gr.x, (uint32_t)(cx0 | (cx1 << 3) | (cy0 << 6) | (cy1 << 9)));
         }
     }
 }
@@ -1112,13 +1124,12 @@ __device__ __forceinline__ void piece_of(int pidx, int S, const uint32_t* __rest
     e1 = min((int)r.y, e0 + PIECE);
 }
 
-// Each lane's tiles of the super-tile at (sx0, sy0) (vw x vh of them inside
-// the grid) for its entry of group q of a piece [e0, e1): a 64-bit mask, bit
-// 8 row + column.
-__device__ __forceinline__ uint64_t entry_tiles(uint4 r, bool valid, int sx0, int sy0, int vw, int vh) {
-    const int cx0 = max((int)(r.y & 0xffffu) - sx0, 0), cx1 = min((int)(r.y >> 16) - sx0, vw - 1);
-    const int cy0 = max((int)(r.z & 0xffffu) - sy0, 0), cy1 = min((int)(r.z >> 16) - sy0, vh - 1);
-    if (!valid || cx0 > cx1 || cy0 > cy1) return 0ull;
+// The tiles of the super-tile that an entry's clipped rectangle (payload
+// bits cx0 | cx1 << 3 | cy0 << 6 | cy1 << 9) holds: a 64-bit mask, bit
+// 8 row + column; none for an invalid entry.
+__device__ __forceinline__ uint64_t entry_tiles(uint32_t rc, bool valid) {
+    if (!valid) return 0ull;
+    const int cx0 = (int)(rc & 7u), cx1 = (int)((rc >> 3) & 7u), cy0 = (int)((rc >> 6) & 7u), cy1 = (int)((rc >> 9) & 7u);
     const uint64_t cols = (uint64_t)(((2u << cx1) - 1u) & ~((1u << cx0) - 1u));
     const uint64_t below_hi = cy1 == SUPER - 1 ? ~0ull : (1ull << (8 * (cy1 + 1))) - 1ull;
     const uint64_t rows = below_hi & ~((1ull << (8 * cy0)) - 1ull) & 0x0101010101010101ull;
@@ -1138,8 +1149,8 @@ constexpr int PIECE_GROUPS = PIECE / 64;
 // to pinfo for the placement.
 __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int SX, int TX, int TY,
                                                  const uint32_t* __restrict__ pfirst, const uint2* __restrict__ sr,
-                                                 const uint32_t* __restrict__ sval, const uint4* __restrict__ rec,
-                                                 uint32_t* __restrict__ counts, uint4* __restrict__ pinfo) {
+                                                 const uint2* __restrict__ spay, uint32_t* __restrict__ counts,
+                                                 uint4* __restrict__ pinfo) {
     __shared__ int s_diff[SB / 64][SUPER * SUPER];
     const int lane = threadIdx.x & 63;
     const int pidx = __builtin_amdgcn_readfirstlane(blockIdx.x * (SB / 64) + (int)(threadIdx.x >> 6));
@@ -1151,21 +1162,18 @@ __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int
     if (lane == 0) pinfo[pidx] = make_uint4((uint32_t)s, (uint32_t)e0, (uint32_t)e1, 0u);  // for the placement
     const int sx0 = (s % SX) * SUPER, sy0 = (s / SX) * SUPER;
     const int vw = min(SUPER, TX - sx0), vh = min(SUPER, TY - sy0);  // the super-tile's tiles inside the grid
-    uint32_t gi[PIECE_GROUPS];
-    uint4 rq[PIECE_GROUPS];
+    uint32_t rq[PIECE_GROUPS];
 #pragma unroll
-    for (int q = 0; q < PIECE_GROUPS; ++q) gi[q] = sval[min(e0 + 64 * q + lane, e1 - 1)];  // lanes past e1 repeat
-#pragma unroll
-    for (int q = 0; q < PIECE_GROUPS; ++q) rq[q] = rec[gi[q]];
+    for (int q = 0; q < PIECE_GROUPS; ++q) rq[q] = spay[min(e0 + 64 * q + lane, e1 - 1)].y;  // lanes past e1 repeat
     wave_lds_sync();  // the cleared array is seen before the corners are added
     // entries covering the whole super-tile (large Gaussians) share their corners: they are
     // counted with one ballot per group and added once, the others add their own corners
     int n_full = 0;
 #pragma unroll
     for (int q = 0; q < PIECE_GROUPS; ++q) {
-        const uint4 r = rq[q];
-        const int cx0 = max((int)(r.y & 0xffffu) - sx0, 0), cx1 = min((int)(r.y >> 16) - sx0, vw - 1);
-        const int cy0 = max((int)(r.z & 0xffffu) - sy0, 0), cy1 = min((int)(r.z >> 16) - sy0, vh - 1);
+        const uint32_t rc = rq[q];
+        const int cx0 = (int)(rc & 7u), cx1 = (int)((rc >> 3) & 7u), cy0 = (int)((rc >> 6) & 7u),
+                  cy1 = (int)((rc >> 9) & 7u);
         const bool valid = e0 + 64 * q + lane < e1 && cx0 <= cx1 && cy0 <= cy1;
         const bool full = valid && cx0 == 0 && cy0 == 0 && cx1 == vw - 1 && cy1 == vh - 1;
         n_full += __popcll(__ballot(full));
@@ -1221,7 +1229,7 @@ static_assert(SB / 64 == PLACE_SPLIT && PIECE / 64 == PLACE_SPLIT, "one wave per
 template <bool KEYS>
 __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int SX, int TX, int TY,
                                                  const uint4* __restrict__ pinfo,
-                                                 const uint32_t* __restrict__ sval, const uint4* __restrict__ rec,
+                                                 const uint2* __restrict__ spay, const float* __restrict__ depths,
                                                  const uint32_t* __restrict__ offs, const uint2* __restrict__ ranges,
                                                  uint32_t P, uint32_t* __restrict__ values, u64* __restrict__ keys64) {
     __shared__ uint2 s_stage[SB / 64][PIECE];   // per wave: (Gaussian, depth bits) of one tile's run
@@ -1242,15 +1250,14 @@ __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int SX, in
     const uint4 pi = pinfo[pidx];  // written by k_tile_count
     const int s = (int)pi.x, e0 = (int)pi.y, e1 = (int)pi.z;
     const int sx0 = (s % SX) * SUPER, sy0 = (s / SX) * SUPER;
-    const int vw = min(SUPER, TX - sx0), vh = min(SUPER, TY - sy0);  // the super-tile's tiles inside the grid
     const int ng = (e1 - e0 + 63) / 64;
     {
         uint4 g = make_uint4(0u, 0u, 0u, 0u);
         if (w < ng) {
             const int e = e0 + 64 * w + lane;
-            const uint4 r = rec[sval[min(e, e1 - 1)]];  // lanes past e1 repeat an entry; masked out below
-            const uint64_t m = entry_tiles(r, e < e1, sx0, sy0, vw, vh);
-            g = make_uint4((uint32_t)m, (uint32_t)(m >> 32), r.x, r.w);
+            const uint2 pl = spay[min(e, e1 - 1)];  // lanes past e1 repeat an entry; masked out below
+            const uint64_t m = entry_tiles(pl.y, e < e1);
+            g = make_uint4((uint32_t)m, (uint32_t)(m >> 32), pl.x, KEYS ? __float_as_uint(depths[pl.x]) : 0u);
         }
         s_grp[w][lane] = g;
         uint32_t olo = g.x, ohi = g.y;
@@ -1425,8 +1432,8 @@ BinLayout bin_layout(int64_t n, int64_t capacity, int TX, int TY) {
     L.crec = take(16 * nn);
     L.skey[0] = take(4 * cap);  // super entries: at most one per pair
     L.skey[1] = take(4 * cap);
-    L.sval[0] = take(4 * cap);
-    L.sval[1] = take(4 * cap);
+    L.sval[0] = take(8 * cap);  // payloads: Gaussian, clipped rectangle
+    L.sval[1] = take(8 * cap);
     L.sranges = take(8 * S);
     L.pfirst = take(4 * (S + 1));
     L.counts = take(4 * 64 * max_pieces);
@@ -1495,7 +1502,7 @@ hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
     for (int pass = 0; pass < 4; ++pass) {
         int c = pass & 1;
-        e = radix_pass(SrcMem{dk[c], di[c]}, n, &counters[0], 8 * pass, 8, hist, rtot, pass, dk[c ^ 1], di[c ^ 1], s);
+        e = radix_pass(SrcMem<uint32_t>{dk[c], di[c]}, n, &counters[0], 8 * pass, 8, hist, rtot, pass, dk[c ^ 1], di[c ^ 1], s);
         if (e != hipSuccess) return e;
     }
     // 3. per depth-sorted Gaussian its record, and per block of them the sum of
@@ -1508,7 +1515,7 @@ hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means
     return hipGetLastError();
 }
 
-hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const BinLayout& L,
+hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, const float* depths, char* ws, const BinLayout& L,
                            uint64_t* keys, uint32_t* values, uint32_t* ranges, hipStream_t s) {
     const int ntiles = TX * TY;
     if (P == 0 || n == 0 || P1 == 0) return fill(ranges, (size_t)2 * ntiles, 0u, s);
@@ -1518,7 +1525,7 @@ hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const
     uint32_t* rtot = reinterpret_cast<uint32_t*>(ws + L.counters) + 2 * NCOUNTERS;
     const uint4* rec = reinterpret_cast<const uint4*>(ws + L.rec);
     uint32_t* sk[2] = {reinterpret_cast<uint32_t*>(ws + L.skey[0]), reinterpret_cast<uint32_t*>(ws + L.skey[1])};
-    uint32_t* sv[2] = {reinterpret_cast<uint32_t*>(ws + L.sval[0]), reinterpret_cast<uint32_t*>(ws + L.sval[1])};
+    uint2* sv[2] = {reinterpret_cast<uint2*>(ws + L.sval[0]), reinterpret_cast<uint2*>(ws + L.sval[1])};
     uint2* sr = reinterpret_cast<uint2*>(ws + L.sranges);
     uint32_t* pfirst = reinterpret_cast<uint32_t*>(ws + L.pfirst);
     uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.counts);
@@ -1543,7 +1550,7 @@ hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const
     for (int pass = 0; pass < passes; ++pass) {
         const int shift = pass * bpp;
         const int bits = min(bpp, sbits - shift);
-        e = radix_pass(SrcMem{sk[cur], sv[cur]}, P1, nullptr, shift, bits, hist, rtot, pass, sk[cur ^ 1], sv[cur ^ 1], s,
+        e = radix_pass(SrcMem<uint2>{sk[cur], sv[cur]}, P1, nullptr, shift, bits, hist, rtot, pass, sk[cur ^ 1], sv[cur ^ 1], s,
                        passes == 1 ? pt : PieceTable{});
         if (e != hipSuccess) return e;
         cur ^= 1;
@@ -1559,7 +1566,7 @@ hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const
     // 4. per-tile counts per piece, their running sums and tile totals, tile ranges, placement
     const int max_pieces = (P1 + PIECE - 1) / PIECE + G.S;
     const int wpb = SB / 64;
-    k_tile_count<<<(max_pieces + wpb - 1) / wpb, SB, 0, s>>>(&counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur], rec,
+    k_tile_count<<<(max_pieces + wpb - 1) / wpb, SB, 0, s>>>(&counters[4], G.S, G.SX, TX, TY, pfirst, sr, sv[cur],
                                                              counts, pinfo);
     k_tile_prefix<<<G.S, 64 * PFX_WAVES, 0, s>>>(&counters[4], G.S, G.SX, TX, TY, pfirst, counts, tile_total);
     e = scan(LoadPlain{tile_total}, StoreRanges{reinterpret_cast<uint2*>(ranges)}, ntiles, nullptr, partials, nullptr,
@@ -1567,11 +1574,11 @@ hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const
     if (e != hipSuccess) return e;
     if (keys)
         k_tile_place<true><<<8 * ((max_pieces + 7) / 8), SB, 0, s>>>(
-            &counters[4], G.SX, TX, TY, pinfo, sv[cur], rec, counts,
+            &counters[4], G.SX, TX, TY, pinfo, sv[cur], depths, counts,
             reinterpret_cast<const uint2*>(ranges), (uint32_t)P, values, reinterpret_cast<u64*>(keys));
     else
         k_tile_place<false><<<8 * ((max_pieces + 7) / 8), SB, 0, s>>>(
-            &counters[4], G.SX, TX, TY, pinfo, sv[cur], rec, counts,
+            &counters[4], G.SX, TX, TY, pinfo, sv[cur], nullptr, counts,
             reinterpret_cast<const uint2*>(ranges), (uint32_t)P, values, nullptr);
     return hipGetLastError();
 }

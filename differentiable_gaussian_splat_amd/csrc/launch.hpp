@@ -71,7 +71,7 @@ struct BinLayout {
     size_t dkeys[2], didx[2];  // depth-sort ping-pong (n entries each)
     size_t rec;                // per depth-sorted Gaussian: uint4 record (n)
     size_t crec;               // per visible Gaussian in index order: the same record (n)
-    size_t skey[2], sval[2];   // super-tile entries (super-tile id, sorted index), ping-pong (capacity each)
+    size_t skey[2], sval[2];   // super-tile entries (super-tile id; Gaussian, clipped rectangle), ping-pong (capacity each)
     size_t sranges;            // per super-tile entry range
     size_t pfirst;             // per super-tile first piece
     size_t counts;             // per piece and tile: count, then offset within the tile's run
@@ -96,9 +96,10 @@ hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means
                             const float* depths, const uint32_t* tiles_touched, char* ws, const BinLayout& L,
                             unsigned long long* mapped_counts, hipEvent_t ev, hipStream_t stream);
 // Phase 2 (P, P1 known on the host, P within capacity): the pairs in (tile,
-// depth, index) order into `values` (and the 64-bit keys if non-NULL), and
-// ranges; TY is the whole (stacked) grid's tile rows.
-hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, char* ws, const BinLayout& L,
+// depth, index) order into `values` (and the 64-bit keys if non-NULL, their
+// depth bits read from `depths`), and ranges; TY is the whole (stacked)
+// grid's tile rows.
+hipError_t launch_bin_emit(int n, int P, int P1, int TX, int TY, const float* depths, char* ws, const BinLayout& L,
                            uint64_t* keys, uint32_t* values, uint32_t* ranges, hipStream_t stream);
 
 hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_t stream);
