@@ -1215,14 +1215,16 @@ __global__ __launch_bounds__(SB) void k_tile_count(const u64* np_ptr, int S, int
 // of tiles (wave w: tiles 16 w .. 16 w + 15), since the per-tile loop is the
 // kernel's serial part and a piece of large Gaussians visits all 64 tiles.
 // For tile l, one compare per group gives the group's entries that hold it;
-// their ranks (mbcnt, with the run's length so far folded in) pack them in
-// depth order (group, then lane) into an LDS staging run, which the wave then
-// writes to the tile's slots with every lane busy: a store instruction costs
-// the address unit about the same whatever its active lanes, so full ones are
-// the cheap ones. The cursors (the tile's first slot plus the counts of the
-// super-tile's earlier pieces) live one per lane, lane l for tile l. A run
-// whose slots would pass P (only with a broken invariant) is written with a
-// check per slot instead.
+// their ranks (mbcnt, with the run's length so far folded in) are their slots
+// in depth order (group, then lane). Without keys each group's entries store
+// their Gaussians straight to those slots (one store per group, its active
+// lanes on consecutive words); with keys (8-byte stores) they go through an
+// LDS staging run first, which the wave then writes with every lane busy:
+// there a store instruction costs the address unit about the same whatever
+// its active lanes, so full ones are the cheap ones. The cursors (the tile's
+// first slot plus the counts of the super-tile's earlier pieces) live one per
+// lane, lane l for tile l. Slots at or past P (only with a broken invariant)
+// are not written.
 constexpr int PLACE_SPLIT = 4;
 static_assert(SB / 64 == PLACE_SPLIT && PIECE / 64 == PLACE_SPLIT, "one wave per group and per two tile rows");
 
@@ -1232,7 +1234,7 @@ __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int SX, in
                                                  const uint2* __restrict__ spay, const float* __restrict__ depths,
                                                  const uint32_t* __restrict__ offs, const uint2* __restrict__ ranges,
                                                  uint32_t P, uint32_t* __restrict__ values, u64* __restrict__ keys64) {
-    __shared__ uint2 s_stage[SB / 64][PIECE];   // per wave: (Gaussian, depth bits) of one tile's run
+    __shared__ uint2 s_stage[KEYS ? SB / 64 : 1][KEYS ? PIECE : 1];  // per wave: (Gaussian, depth bits) of a run
     __shared__ uint4 s_grp[PIECE_GROUPS][64];   // per group and lane: mask lo, mask hi, Gaussian, depth bits
     __shared__ uint2 s_any[PIECE_GROUPS];       // per group: OR of its masks
     const int lane = threadIdx.x & 63;
@@ -1246,7 +1248,7 @@ __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int SX, in
     const int i = (int)(blockIdx.x >> 3);
     const int pidx = (int)(blockIdx.x & 7u) * chunk + i;
     if (i >= chunk || pidx >= np) return;  // the whole block: the barrier below is reached by all waves or none
-    uint2* stage = s_stage[w];
+    uint2* stage = s_stage[KEYS ? w : 0];
     const uint4 pi = pinfo[pidx];  // written by k_tile_count
     const int s = (int)pi.x, e0 = (int)pi.y, e1 = (int)pi.z;
     const int sx0 = (s % SX) * SUPER, sy0 = (s / SX) * SUPER;
@@ -1290,6 +1292,22 @@ __global__ __launch_bounds__(SB) void k_tile_place(const u64* np_ptr, int SX, in
         todo &= todo - 1u;
         const uint32_t bit = 1u << b;
         const int l = 32 * (w >> 1) + b;  // the tile inside the super-tile
+        if (!KEYS) {
+            const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)cur, l);
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int q = 0; q < PIECE_GROUPS; ++q) {
+                if (!(gany[q] & bit)) continue;  // no entry of group q holds it (also: group q absent)
+                const bool in = (mw[q] & bit) != 0u;
+                const uint64_t m = __ballot(in);
+                const uint32_t at =
+                    base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, cnt));
+                if (in && at < P) values[at] = pv[q].x;
+                cnt += (uint32_t)__popcll(m);
+            }
+            cur = lane == l ? base + cnt : cur;
+            continue;
+        }
         // pack the piece's entries holding tile l, in depth order, into the staging run
         uint32_t cnt = 0;
 #pragma unroll
