@@ -8,7 +8,7 @@
 //   2. LSD radix sort of those by their 32 depth bits (stable: equal depths
 //      stay in index order); every tile's list is a subsequence of this order;
 //   3. super-tiles of 8 x 8 tiles: each depth-sorted Gaussian emits one entry
-//      per super-tile its tile rectangle meets (about 1.3 entries per Gaussian
+//      per super-tile its tile rectangle meets (about 2.3 entries per Gaussian
 //      at 1080p), and a stable radix pass groups the entries by super-tile,
 //      keeping depth order inside each group;
 //   4. one wave per piece of a super-tile's group, lane = tile of the 8 x 8
