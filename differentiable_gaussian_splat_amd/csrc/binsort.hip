@@ -518,13 +518,15 @@ __device__ __forceinline__ void digit_bases(const uint32_t* __restrict__ tot, ui
 // digit totals dtot: digit d's base plus its counts in the blocks before this
 // one, summed by the 16 waves over rows w, w + 16, ... while the keys load;
 // block 0 then also does k_radix_offsets' other work (clearing spare, the
-// piece table).
+// piece table). bstart (nullable, INLINE only): block b owns elements
+// [bstart[b], bstart[b + 1]) (at most RE; the last block ends at the count)
+// instead of [b RE, b RE + RE).
 template <bool INLINE, class V>
 __global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem<V> src, int n, const u64* dcount, int shift, int bits,
                                                     const uint32_t* __restrict__ offsets,
                                                     const uint32_t* __restrict__ dtot, uint32_t* __restrict__ spare,
-                                                    PieceTable pt, uint32_t* __restrict__ keys_out,
-                                                    V* __restrict__ vals_out) {
+                                                    PieceTable pt, const u64* __restrict__ bstart,
+                                                    uint32_t* __restrict__ keys_out, V* __restrict__ vals_out) {
     static_assert(sizeof(V) * RE >= 16 * RW * 64, "the waves' column sums fit in s_vals");
     __shared__ uint32_t s_keys[RE];
     __shared__ __align__(16) V s_vals[RE];  // INLINE: first the waves' column sums of hist, 256 words each
@@ -537,9 +539,13 @@ __global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem<V> src, int n, cons
     if (INLINE && blockIdx.x == 0)
         for (int k = tid; k < RT * 256; k += RB) spare[k] = 0u;
     const int cnt = eff_count(n, dcount);
-    const int p0 = blockIdx.x * RE;
-    if (p0 >= cnt) return;
-    const int p1 = min(cnt, p0 + RE);
+    int p0 = blockIdx.x * RE, p1 = min(cnt, p0 + RE);
+    if (INLINE && bstart) {
+        p0 = (int)bstart[blockIdx.x];
+        p1 = blockIdx.x + 1 < gridDim.x ? (int)bstart[blockIdx.x + 1] : cnt;
+        p1 = min(min(p1, cnt), p0 + RE);  // a consistent table keeps these
+    }
+    if (p0 >= p1) return;
     const uint32_t mask = (1u << bits) - 1u;
     for (int k = lane; k < 256; k += 64) s_wcnt[w][k] = 0u;
     wave_lds_sync();
@@ -646,17 +652,21 @@ __global__ __launch_bounds__(RB) void k_radix_scatter(SrcMem<V> src, int n, cons
 // together read nblocks^2 / 2 rows of hist); beyond, k_radix_offsets does.
 constexpr int RADIX_INLINE_BLOCKS = 512;
 
+// bstart (nullable): the histogram and digit totals are already there, for
+// blocks of elements [bstart[b], bstart[b + 1]) (RADIX_INLINE_BLOCKS at most).
 template <class V>
 hipError_t radix_pass(SrcMem<V> src, int n, const u64* dcount, int shift, int bits, uint32_t* hist, uint32_t* rtot,
-                      int pass, uint32_t* keys_out, V* vals_out, hipStream_t s, PieceTable pt = {}) {
+                      int pass, uint32_t* keys_out, V* vals_out, hipStream_t s, PieceTable pt = {},
+                      const u64* bstart = nullptr) {
     const int nblocks = (n + RE - 1) / RE;
     if (nblocks == 0) return hipSuccess;
     uint32_t* tot = rtot + RT * 256 * (pass & 1);
     uint32_t* spare = rtot + RT * 256 * ((pass & 1) ^ 1);
-    k_radix_hist<<<nblocks, RB, 0, s>>>(src.keys, n, dcount, shift, bits, hist, tot);
+    if (bstart && nblocks > RADIX_INLINE_BLOCKS) return hipErrorInvalidValue;
+    if (!bstart) k_radix_hist<<<nblocks, RB, 0, s>>>(src.keys, n, dcount, shift, bits, hist, tot);
     if (nblocks <= RADIX_INLINE_BLOCKS) {
-        k_radix_scatter<true, V><<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, tot, spare, pt, keys_out,
-                                                        vals_out);
+        k_radix_scatter<true, V><<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, tot, spare, pt, bstart,
+                                                        keys_out, vals_out);
         return hipGetLastError();
     }
     if (pt.pfirst)
@@ -664,7 +674,7 @@ hipError_t radix_pass(SrcMem<V> src, int n, const u64* dcount, int shift, int bi
     else
         k_radix_offsets<false><<<256, 64, 0, s>>>(nblocks, hist, tot, spare, 0, nullptr, nullptr, nullptr);
     k_radix_scatter<false, V><<<nblocks, RB, 0, s>>>(src, n, dcount, shift, bits, hist, nullptr, nullptr, {},
-                                                     keys_out, vals_out);
+                                                     nullptr, keys_out, vals_out);
     return hipGetLastError();
 }
 
@@ -692,8 +702,11 @@ __device__ __forceinline__ uint32_t super_count(int X0, int X1, int Y0, int Y1) 
 // straight after it.
 __global__ __launch_bounds__(SB) void k_pair_totals(int n, const uint32_t* __restrict__ tiles,
                                                   const float2* __restrict__ means2d, const int* __restrict__ radii,
-                                                  int nper, int TX, int TYv, u64* __restrict__ part) {
+                                                  int nper, int TX, int TYv, u64* __restrict__ part,
+                                                  uint32_t* __restrict__ rtot, int rtot_words) {
     __shared__ u64 s_w[3][SB / 64];
+    if (blockIdx.x == 0)  // the radix passes' digit totals start at zero (the compaction adds the first)
+        for (int k = threadIdx.x; k < rtot_words; k += SB) rtot[k] = 0u;
     u64 p = 0, p1 = 0, v = 0;
     const int base = blockIdx.x * ST;
     // every load issued before any is used (at a clamped index past n, not counted)
@@ -810,11 +823,15 @@ __global__ __launch_bounds__(1024) void k_pair_sum(int nb, const u64* __restrict
 //
 // SELF (up to COMPACT_SELF_SUM_BLOCKS blocks, in place of k_pair_sum): vis_scan
 // is k_pair_totals' table part itself; each block sums the visible counts of
-// the blocks before it, and block 0 also does k_pair_sum's other work (the
-// totals into counters and host, the digit-total buffers cleared).
+// the blocks before it, writes that offset to bstart[b], and block 0 also
+// does k_pair_sum's other work (the totals into counters and host).
+// HIST (up to RADIX_INLINE_BLOCKS blocks): the block's visible Gaussians are
+// also the first depth pass's block b (compact positions [bstart[b],
+// bstart[b + 1])): their low-byte histogram goes to hist[b] and is added to
+// the digit totals tot, in place of that pass's histogram kernel.
 constexpr int COMPACT_SELF_SUM_BLOCKS = 4096;
 
-template <bool SELF>
+template <bool SELF, bool HIST>
 __global__ __launch_bounds__(SB) void k_compact_visible(int n, int nper, int TX, int TYv,
                                                       const uint32_t* __restrict__ tiles,
                                                       const float* __restrict__ depths,
@@ -822,16 +839,19 @@ __global__ __launch_bounds__(SB) void k_compact_visible(int n, int nper, int TX,
                                                       const int* __restrict__ radii,
                                                       const u64* __restrict__ vis_scan, uint32_t* __restrict__ keys,
                                                       uint32_t* __restrict__ idx, uint4* __restrict__ crec,
-                                                      u64* __restrict__ counters, uint32_t* __restrict__ rtot,
-                                                      int rtot_words, u64* __restrict__ host) {
+                                                      u64* __restrict__ counters, u64* __restrict__ bstart,
+                                                      uint32_t* __restrict__ hist, uint32_t* __restrict__ tot,
+                                                      u64* __restrict__ host) {
     static_assert(SI * (SB / 64) == 64, "one lane per (row, wave) count");
+    static_assert(SB == 256 && ST == RE, "one histogram bin per thread; a compaction block is a radix block");
     __shared__ uint32_t s_c[SI * (SB / 64)];
     __shared__ u64 s_v[SB / 64];
+    __shared__ uint32_t s_h[HIST ? 256 : 1];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int base = blockIdx.x * ST;
+    if (HIST) s_h[threadIdx.x] = 0u;  // added to after the barrier below
     if (SELF && blockIdx.x == 0) {
         __shared__ u64 s_t[3][SB / 64];
-        for (int k = threadIdx.x; k < rtot_words; k += SB) rtot[k] = 0u;
         const int nb = gridDim.x;
         u64 p = 0, p1 = 0, v = 0;
         for (int k = threadIdx.x; k < nb; k += SB) {
@@ -904,6 +924,7 @@ __global__ __launch_bounds__(SB) void k_compact_visible(int n, int nper, int TX,
     if (SELF) {
 #pragma unroll
         for (int k = 0; k < SB / 64; ++k) boff += s_v[k];
+        if (threadIdx.x == 0) bstart[blockIdx.x] = boff;
     } else {
         boff = vis_scan[blockIdx.x];
     }
@@ -920,7 +941,14 @@ __global__ __launch_bounds__(SB) void k_compact_visible(int n, int nper, int TX,
             idx[pos] = pos;
             crec[pos] = make_uint4((uint32_t)i, (uint32_t)X0 | ((uint32_t)X1 << 16), (uint32_t)Y0 | ((uint32_t)Y1 << 16),
                                    d[j]);
+            if (HIST) atomicAdd(&s_h[d[j] & 0xffu], 1u);
         }
+    }
+    if (HIST) {
+        __syncthreads();
+        const uint32_t c = s_h[threadIdx.x];
+        hist[(size_t)blockIdx.x * 256 + threadIdx.x] = c;
+        if (c) atomicAdd(&tot[(blockIdx.x % RT) * 256 + threadIdx.x], c);
     }
 }
 
@@ -1496,7 +1524,7 @@ hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means
     const int nb = (n + ST - 1) / ST;
     const bool self_sum = nb <= COMPACT_SELF_SUM_BLOCKS;
     u64* part = reinterpret_cast<u64*>(ws + L.pair_part);
-    k_pair_totals<<<nb, SB, 0, s>>>(n, tiles_touched, m2, radii, nper, TX, TYv, part);
+    k_pair_totals<<<nb, SB, 0, s>>>(n, tiles_touched, m2, radii, nper, TX, TYv, part, rtot, rtot_words);
     if (!self_sum) {
         k_pair_sum<<<1, 1024, 0, s>>>(nb, part, partials, counters, rtot, rtot_words, host);
         e = hipGetLastError();
@@ -1507,20 +1535,29 @@ hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means
     uint32_t* di[2] = {reinterpret_cast<uint32_t*>(ws + L.didx[0]), reinterpret_cast<uint32_t*>(ws + L.didx[1])};
     // 1. visible compaction (index order kept): depth bits, compact positions, records
     uint4* crec = reinterpret_cast<uint4*>(ws + L.crec);
-    if (self_sum)
-        k_compact_visible<true><<<nb, SB, 0, s>>>(n, nper, TX, TYv, tiles_touched, depths, m2, radii, part, dk[0],
-                                                  di[0], crec, counters, rtot, rtot_words, host);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+    // up to RADIX_INLINE_BLOCKS blocks the compaction also histograms the first
+    // depth pass, whose blocks are then the compaction's (starts in partials)
+    const bool first_hist = nb <= RADIX_INLINE_BLOCKS;
+    if (self_sum && first_hist)
+        k_compact_visible<true, true><<<nb, SB, 0, s>>>(n, nper, TX, TYv, tiles_touched, depths, m2, radii, part,
+                                                        dk[0], di[0], crec, counters, partials, hist, rtot, host);
+    else if (self_sum)
+        k_compact_visible<true, false><<<nb, SB, 0, s>>>(n, nper, TX, TYv, tiles_touched, depths, m2, radii, part,
+                                                         dk[0], di[0], crec, counters, partials, nullptr, nullptr,
+                                                         host);
     else
-        k_compact_visible<false><<<nb, SB, 0, s>>>(n, nper, TX, TYv, tiles_touched, depths, m2, radii, partials,
-                                                   dk[0], di[0], crec, nullptr, nullptr, 0, nullptr);
+        k_compact_visible<false, false><<<nb, SB, 0, s>>>(n, nper, TX, TYv, tiles_touched, depths, m2, radii,
+                                                          partials, dk[0], di[0], crec, nullptr, nullptr, nullptr,
+                                                          nullptr, nullptr);
     e = hipGetLastError();
     if (e == hipSuccess && self_sum) e = hipEventRecord(ev, s);
     if (e != hipSuccess) return e;
     // 2. stable sort by the 32 depth bits, 4 passes of 8: the result returns to buffer 0
-    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
     for (int pass = 0; pass < 4; ++pass) {
         int c = pass & 1;
-        e = radix_pass(SrcMem<uint32_t>{dk[c], di[c]}, n, &counters[0], 8 * pass, 8, hist, rtot, pass, dk[c ^ 1], di[c ^ 1], s);
+        e = radix_pass(SrcMem<uint32_t>{dk[c], di[c]}, n, &counters[0], 8 * pass, 8, hist, rtot, pass, dk[c ^ 1],
+                       di[c ^ 1], s, PieceTable{}, pass == 0 && self_sum && first_hist ? partials : nullptr);
         if (e != hipSuccess) return e;
     }
     // 3. per depth-sorted Gaussian its record, and per block of them the sum of
