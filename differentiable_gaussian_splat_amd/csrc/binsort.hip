@@ -700,29 +700,31 @@ __device__ __forceinline__ uint32_t super_count(int X0, int X1, int Y0, int Y1) 
 // into part[3 b .. 3 b + 2]; k_pair_sum then totals P and P1 and scans the
 // visible counts, so that the compaction (k_compact_visible) runs
 // straight after it.
-__global__ __launch_bounds__(SB) void k_pair_totals(int n, const uint32_t* __restrict__ tiles,
+constexpr int CT = 1024, CI = ST / CT;  // threads and items per thread of the per-Gaussian passes
+
+__global__ __launch_bounds__(CT) void k_pair_totals(int n, const uint32_t* __restrict__ tiles,
                                                   const float2* __restrict__ means2d, const int* __restrict__ radii,
                                                   int nper, int TX, int TYv, u64* __restrict__ part,
                                                   uint32_t* __restrict__ rtot, int rtot_words) {
-    __shared__ u64 s_w[3][SB / 64];
+    __shared__ u64 s_w[3][CT / 64];
     if (blockIdx.x == 0)  // the radix passes' digit totals start at zero (the compaction adds the first)
-        for (int k = threadIdx.x; k < rtot_words; k += SB) rtot[k] = 0u;
+        for (int k = threadIdx.x; k < rtot_words; k += CT) rtot[k] = 0u;
     u64 p = 0, p1 = 0, v = 0;
     const int base = blockIdx.x * ST;
     // every load issued before any is used (at a clamped index past n, not counted)
-    uint32_t t[SI];
-    float2 m[SI];
-    int rr[SI];
+    uint32_t t[CI];
+    float2 m[CI];
+    int rr[CI];
 #pragma unroll
-    for (int j = 0; j < SI; ++j) {
-        const int i = min(base + j * SB + (int)threadIdx.x, n - 1);
+    for (int j = 0; j < CI; ++j) {
+        const int i = min(base + j * CT + (int)threadIdx.x, n - 1);
         t[j] = tiles[i];
         m[j] = means2d[i];
         rr[j] = radii[i];
     }
 #pragma unroll
-    for (int j = 0; j < SI; ++j) {
-        const int i = base + j * SB + threadIdx.x;
+    for (int j = 0; j < CI; ++j) {
+        const int i = base + j * CT + threadIdx.x;
         if (i < n && t[j]) {
             int X0, X1, Y0, Y1;
             stacked_rect(i, nper, TX, TYv, m[j], rr[j], X0, X1, Y0, Y1);
@@ -743,8 +745,11 @@ __global__ __launch_bounds__(SB) void k_pair_totals(int n, const uint32_t* __res
     }
     __syncthreads();
     if (threadIdx.x < 3)
-        part[3 * blockIdx.x + threadIdx.x] =
-            s_w[threadIdx.x][0] + s_w[threadIdx.x][1] + s_w[threadIdx.x][2] + s_w[threadIdx.x][3];
+    {
+        u64 t3 = 0;
+        for (int k = 0; k < CT / 64; ++k) t3 += s_w[threadIdx.x][k];
+        part[3 * blockIdx.x + threadIdx.x] = t3;
+    }
 }
 
 // One 1024-thread block: counters[2] = P, counters[3] = P1, vis_scan[b] = the
@@ -817,9 +822,9 @@ __global__ __launch_bounds__(1024) void k_pair_sum(int nb, const u64* __restrict
 // pos-th in index order, gets its depth bits and compact position (the depth
 // sort's keys and values) and its record (index, tile rectangle X0 | X1 << 16, Y0 | Y1 << 16, depth
 // bits), written here in index order so that the sorted order later gathers
-// one 16-byte record each. Thread t takes Gaussians base + j SB + t, all
+// one 16-byte record each. Thread t takes Gaussians base + j CT + t, all
 // loads issued up front; ranks come from one ballot per wave and row j and a
-// scan of the block's 4 SI wave counts (index order is row, wave, lane).
+// scan of the block's 64 (row, wave) counts (index order is row, wave, lane).
 //
 // SELF (up to COMPACT_SELF_SUM_BLOCKS blocks, in place of k_pair_sum): vis_scan
 // is k_pair_totals' table part itself; each block sums the visible counts of
@@ -832,7 +837,7 @@ __global__ __launch_bounds__(1024) void k_pair_sum(int nb, const u64* __restrict
 constexpr int COMPACT_SELF_SUM_BLOCKS = 4096;
 
 template <bool SELF, bool HIST>
-__global__ __launch_bounds__(SB) void k_compact_visible(int n, int nper, int TX, int TYv,
+__global__ __launch_bounds__(CT) void k_compact_visible(int n, int nper, int TX, int TYv,
                                                       const uint32_t* __restrict__ tiles,
                                                       const float* __restrict__ depths,
                                                       const float2* __restrict__ means2d,
@@ -842,19 +847,19 @@ __global__ __launch_bounds__(SB) void k_compact_visible(int n, int nper, int TX,
                                                       u64* __restrict__ counters, u64* __restrict__ bstart,
                                                       uint32_t* __restrict__ hist, uint32_t* __restrict__ tot,
                                                       u64* __restrict__ host) {
-    static_assert(SI * (SB / 64) == 64, "one lane per (row, wave) count");
-    static_assert(SB == 256 && ST == RE, "one histogram bin per thread; a compaction block is a radix block");
-    __shared__ uint32_t s_c[SI * (SB / 64)];
-    __shared__ u64 s_v[SB / 64];
+    static_assert(CI * (CT / 64) == 64, "one lane per (row, wave) count");
+    static_assert(CT >= 256 && ST == RE, "one histogram bin per thread; a compaction block is a radix block");
+    __shared__ uint32_t s_c[CI * (CT / 64)];
+    __shared__ u64 s_v[CT / 64];
     __shared__ uint32_t s_h[HIST ? 256 : 1];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int base = blockIdx.x * ST;
-    if (HIST) s_h[threadIdx.x] = 0u;  // added to after the barrier below
+    if (HIST && threadIdx.x < 256) s_h[threadIdx.x] = 0u;  // added to after the barrier below
     if (SELF && blockIdx.x == 0) {
-        __shared__ u64 s_t[3][SB / 64];
+        __shared__ u64 s_t[3][CT / 64];
         const int nb = gridDim.x;
         u64 p = 0, p1 = 0, v = 0;
-        for (int k = threadIdx.x; k < nb; k += SB) {
+        for (int k = threadIdx.x; k < nb; k += CT) {
             p += vis_scan[3 * k];
             p1 += vis_scan[3 * k + 1];
             v += vis_scan[3 * k + 2];
@@ -872,7 +877,7 @@ __global__ __launch_bounds__(SB) void k_compact_visible(int n, int nper, int TX,
         __syncthreads();
         if (threadIdx.x == 0) {
             u64 a = 0, c = 0, t = 0;
-            for (int k = 0; k < SB / 64; ++k) {
+            for (int k = 0; k < CT / 64; ++k) {
                 a += s_t[0][k];
                 c += s_t[1][k];
                 t += s_t[2][k];
@@ -889,23 +894,23 @@ __global__ __launch_bounds__(SB) void k_compact_visible(int n, int nper, int TX,
     }
     u64 vb = 0;  // SELF: visible Gaussians in the blocks before this one
     if (SELF)
-        for (int k = threadIdx.x; k < (int)blockIdx.x; k += SB) vb += vis_scan[3 * k + 2];
-    uint32_t t[SI], d[SI];
-    float2 m[SI];
-    int rr[SI];
+        for (int k = threadIdx.x; k < (int)blockIdx.x; k += CT) vb += vis_scan[3 * k + 2];
+    uint32_t t[CI], d[CI];
+    float2 m[CI];
+    int rr[CI];
 #pragma unroll
-    for (int j = 0; j < SI; ++j) {
-        const int i = min(base + j * SB + (int)threadIdx.x, n - 1);  // past n: loaded, never stored
+    for (int j = 0; j < CI; ++j) {
+        const int i = min(base + j * CT + (int)threadIdx.x, n - 1);  // past n: loaded, never stored
         t[j] = tiles[i];
         d[j] = __float_as_uint(depths[i]);
         m[j] = means2d[i];
         rr[j] = radii[i];
     }
-    uint64_t vis[SI];
+    uint64_t vis[CI];
 #pragma unroll
-    for (int j = 0; j < SI; ++j) {
-        vis[j] = __ballot(base + j * SB + (int)threadIdx.x < n && t[j] > 0u);
-        if (lane == 0) s_c[j * (SB / 64) + w] = (uint32_t)__popcll(vis[j]);
+    for (int j = 0; j < CI; ++j) {
+        vis[j] = __ballot(base + j * CT + (int)threadIdx.x < n && t[j] > 0u);
+        if (lane == 0) s_c[j * (CT / 64) + w] = (uint32_t)__popcll(vis[j]);
     }
     if (SELF) {
         for (int off = 32; off > 0; off >>= 1) vb += __shfl_xor(vb, off);
@@ -923,18 +928,18 @@ __global__ __launch_bounds__(SB) void k_compact_visible(int n, int nper, int TX,
     u64 boff = 0;
     if (SELF) {
 #pragma unroll
-        for (int k = 0; k < SB / 64; ++k) boff += s_v[k];
+        for (int k = 0; k < CT / 64; ++k) boff += s_v[k];
         if (threadIdx.x == 0) bstart[blockIdx.x] = boff;
     } else {
         boff = vis_scan[blockIdx.x];
     }
 #pragma unroll
-    for (int j = 0; j < SI; ++j) {
-        const uint32_t first = (uint32_t)__builtin_amdgcn_readlane((int)excl, j * (SB / 64) + w);
+    for (int j = 0; j < CI; ++j) {
+        const uint32_t first = (uint32_t)__builtin_amdgcn_readlane((int)excl, j * (CT / 64) + w);
         if ((vis[j] >> lane) & 1ull) {
             const uint32_t pos = (uint32_t)boff + first +
                                  __builtin_amdgcn_mbcnt_hi((uint32_t)(vis[j] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)vis[j], 0u));
-            const int i = base + j * SB + threadIdx.x;
+            const int i = base + j * CT + threadIdx.x;
             int X0, X1, Y0, Y1;
             stacked_rect(i, nper, TX, TYv, m[j], rr[j], X0, X1, Y0, Y1);
             keys[pos] = d[j];
@@ -946,6 +951,7 @@ __global__ __launch_bounds__(SB) void k_compact_visible(int n, int nper, int TX,
     }
     if (HIST) {
         __syncthreads();
+        if (threadIdx.x >= 256) return;
         const uint32_t c = s_h[threadIdx.x];
         hist[(size_t)blockIdx.x * 256 + threadIdx.x] = c;
         if (c) atomicAdd(&tot[(blockIdx.x % RT) * 256 + threadIdx.x], c);
@@ -1524,7 +1530,7 @@ hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means
     const int nb = (n + ST - 1) / ST;
     const bool self_sum = nb <= COMPACT_SELF_SUM_BLOCKS;
     u64* part = reinterpret_cast<u64*>(ws + L.pair_part);
-    k_pair_totals<<<nb, SB, 0, s>>>(n, tiles_touched, m2, radii, nper, TX, TYv, part, rtot, rtot_words);
+    k_pair_totals<<<nb, CT, 0, s>>>(n, tiles_touched, m2, radii, nper, TX, TYv, part, rtot, rtot_words);
     if (!self_sum) {
         k_pair_sum<<<1, 1024, 0, s>>>(nb, part, partials, counters, rtot, rtot_words, host);
         e = hipGetLastError();
@@ -1540,14 +1546,14 @@ hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means
     // depth pass, whose blocks are then the compaction's (starts in partials)
     const bool first_hist = nb <= RADIX_INLINE_BLOCKS;
     if (self_sum && first_hist)
-        k_compact_visible<true, true><<<nb, SB, 0, s>>>(n, nper, TX, TYv, tiles_touched, depths, m2, radii, part,
+        k_compact_visible<true, true><<<nb, CT, 0, s>>>(n, nper, TX, TYv, tiles_touched, depths, m2, radii, part,
                                                         dk[0], di[0], crec, counters, partials, hist, rtot, host);
     else if (self_sum)
-        k_compact_visible<true, false><<<nb, SB, 0, s>>>(n, nper, TX, TYv, tiles_touched, depths, m2, radii, part,
+        k_compact_visible<true, false><<<nb, CT, 0, s>>>(n, nper, TX, TYv, tiles_touched, depths, m2, radii, part,
                                                          dk[0], di[0], crec, counters, partials, nullptr, nullptr,
                                                          host);
     else
-        k_compact_visible<false, false><<<nb, SB, 0, s>>>(n, nper, TX, TYv, tiles_touched, depths, m2, radii,
+        k_compact_visible<false, false><<<nb, CT, 0, s>>>(n, nper, TX, TYv, tiles_touched, depths, m2, radii,
                                                           partials, dk[0], di[0], crec, nullptr, nullptr, nullptr,
                                                           nullptr, nullptr);
     e = hipGetLastError();
