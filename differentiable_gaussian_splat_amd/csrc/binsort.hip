@@ -963,15 +963,14 @@ __global__ __launch_bounds__(CT) void k_compact_visible(int n, int nper, int TX,
 // Gaussians the sum of their super-tile counts (coarse[b]), and per row of
 // SB of them (row j: Gaussians base + j SB .. + SB - 1) the row's sum
 // (fine[16 b + j]): the reduce step of the scan that gives each Gaussian its
-// first super-tile entry. The 16 row sums come out of one reduce-scatter per
-// wave: four exchanges halve the rows a lane holds (masks 32, 16, 8, 4), two
-// more finish the sums, and lane l ends with row l / 4.
-static_assert(ST == 16 * SB && SI == 16, "16 rows of one block's width per scan block");
+// first super-tile entry. Thread t takes Gaussians base + j CT + t, so that
+// row 4 j + q holds item j of waves 4 q .. 4 q + 3.
+static_assert(ST == 16 * SB && CI == 4, "rows of SB Gaussians: 4 per item of a thread");
 
-__global__ __launch_bounds__(SB) void k_sorted_records(const u64* vis_ptr, const uint32_t* __restrict__ order,
+__global__ __launch_bounds__(CT) void k_sorted_records(const u64* vis_ptr, const uint32_t* __restrict__ order,
                                                      const uint4* __restrict__ crec, uint4* __restrict__ rec,
                                                      u64* __restrict__ coarse, uint32_t* __restrict__ fine) {
-    __shared__ uint32_t s_f[SB / 64][SI];
+    __shared__ uint32_t s_f[CT / 64][CI];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int cnt = (int)*vis_ptr;
     const int base = blockIdx.x * ST;
@@ -980,17 +979,17 @@ __global__ __launch_bounds__(SB) void k_sorted_records(const u64* vis_ptr, const
         return;
     }
     // every gather issued before any is used (at a clamped index past cnt, not stored)
-    uint32_t o[SI];
+    uint32_t o[CI];
 #pragma unroll
-    for (int j = 0; j < SI; ++j) o[j] = order[min(base + j * SB + (int)threadIdx.x, cnt - 1)];
+    for (int j = 0; j < CI; ++j) o[j] = order[min(base + j * CT + (int)threadIdx.x, cnt - 1)];
     __builtin_amdgcn_sched_barrier(0);  // all index loads in flight before the first gather waits on one
-    uint4 rr[SI];
+    uint4 rr[CI];
 #pragma unroll
-    for (int j = 0; j < SI; ++j) rr[j] = crec[o[j]];
-    uint32_t v[SI];
+    for (int j = 0; j < CI; ++j) rr[j] = crec[o[j]];
+    uint32_t v[CI];
 #pragma unroll
-    for (int j = 0; j < SI; ++j) {
-        const int i = base + j * SB + threadIdx.x;
+    for (int j = 0; j < CI; ++j) {
+        const int i = base + j * CT + threadIdx.x;
         v[j] = 0u;
         if (i < cnt) {
             const uint4 r = rr[j];
@@ -998,9 +997,11 @@ __global__ __launch_bounds__(SB) void k_sorted_records(const u64* vis_ptr, const
             v[j] = super_count((int)(r.y & 0xffffu), (int)(r.y >> 16), (int)(r.z & 0xffffu), (int)(r.z >> 16));
         }
     }
+    // the wave's sums of its four items: two halving exchanges (masks 32, 16), four more finish
+    // them, and lane l ends with item (l / 16) % 4
 #pragma unroll
-    for (int m = 32, k = SI / 2; m >= 4; m >>= 1, k >>= 1) {
-        const bool up = (lane & m) != 0;  // keeps the upper half of its rows
+    for (int m = 32, k = CI / 2; m >= 16; m >>= 1, k >>= 1) {
+        const bool up = (lane & m) != 0;
 #pragma unroll
         for (int q = 0; q < k; ++q) {
             const uint32_t keep = up ? v[q + k] : v[q];
@@ -1008,16 +1009,18 @@ __global__ __launch_bounds__(SB) void k_sorted_records(const u64* vis_ptr, const
             v[q] = keep + (uint32_t)__shfl_xor((int)give, m);
         }
     }
-    v[0] += (uint32_t)__shfl_xor((int)v[0], 2);
-    v[0] += (uint32_t)__shfl_xor((int)v[0], 1);
-    if ((lane & 3) == 0) s_f[w][lane >> 2] = v[0];
+#pragma unroll
+    for (int m = 8; m > 0; m >>= 1) v[0] += (uint32_t)__shfl_xor((int)v[0], m);
+    if ((lane & 15) == 0) s_f[w][lane >> 4] = v[0];
     __syncthreads();
+    // row r = 4 j + q of SB Gaussians: item j of waves 4 q .. 4 q + 3
     if (threadIdx.x < 64) {
         uint32_t f = 0u;
-        if (lane < SI) {
+        if (lane < 16) {
+            const int j = lane >> 2, q = lane & 3;
 #pragma unroll
-            for (int k = 0; k < SB / 64; ++k) f += s_f[k][lane];
-            fine[(size_t)blockIdx.x * SI + lane] = f;
+            for (int k = 0; k < 4; ++k) f += s_f[4 * q + k][j];
+            fine[(size_t)blockIdx.x * 16 + lane] = f;
         }
         u64 t = f;
         for (int off = 8; off > 0; off >>= 1) t += __shfl_xor(t, off);
@@ -1571,7 +1574,7 @@ hipError_t launch_bin_count(int n, int nper, int TX, int TYv, const float* means
     //    k_super_emit sums itself)
     uint4* rec = reinterpret_cast<uint4*>(ws + L.rec);
     uint32_t* fine = reinterpret_cast<uint32_t*>(ws + L.fine);
-    k_sorted_records<<<nb, SB, 0, s>>>(&counters[0], di[0], crec, rec, partials, fine);
+    k_sorted_records<<<nb, CT, 0, s>>>(&counters[0], di[0], crec, rec, partials, fine);
     if (nb > EMIT_SELF_SUM_BLOCKS) k_scan_top<<<1, 1024, 0, s>>>(partials, nb, nullptr);
     return hipGetLastError();
 }
