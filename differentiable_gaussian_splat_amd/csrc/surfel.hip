@@ -30,9 +30,10 @@
 // dL/dN12 = sum x dL/dk and dL/dN02 = -sum y dL/dk, and those into dL/dM.
 //
 // Layout as the 3D kernels: one 64-lane wave per 16x4 row band in the forward;
-// in the backward one wave per tile (four pixels per lane) or, on small grids,
-// one per band, with the per-entry sums reduced over each 16-lane row by DPP
-// before one atomic add per value per (tile or band, surfel).
+// in the backward one wave per tile (a lane's four pixels in one row, one in
+// each 4-column strip) or, on small grids, one per strip, with the per-entry
+// sums reduced over each 16-lane row by DPP before one atomic add per value
+// per (tile or strip, surfel).
 #include <type_traits>
 
 #include "common.hpp"
@@ -136,35 +137,52 @@ struct SurfelReach {
 };
 
 // One (pixel, surfel) evaluation at offset (lx, ly) from the tile's first
-// pixel centre; the forward and the backward call it on the same staged
-// values, so both take the same decisions bit for bit (contraction fixed).
+// pixel centre, in two parts: the terms that depend only on the row
+// (surfel_row_terms: dy, k_j before its column term, dy^2), formed once for
+// the pixels of a row, and the rest (surfel_hit_in_row). The forward stages
+// the same row terms and takes the same fp32 steps (contraction fixed), so
+// the forward and the backward take the same decisions bit for bit.
 struct SurfelHit {
     float inv, u, v, rho3, dx, dy, oG;
     bool own;  // the surfel's own falloff is the wider one
 };
 
-__device__ __forceinline__ void surfel_hit(const SurfelRec& s, float lx, float ly, SurfelHit& e) {
+struct SurfelRowTerms {
+    float dy, r0, r1, r2, dy2;
+};
+__device__ __forceinline__ SurfelRowTerms surfel_row_terms(const SurfelRec& s, float ly) {
+#pragma clang fp contract(off)
+    SurfelRowTerms t;
+    t.dy = s.c.z + ly;
+    t.r0 = __fmaf_rn(-t.dy, s.b.z, s.a.x);
+    t.r1 = __fmaf_rn(-t.dy, s.b.w, s.a.y);
+    t.r2 = __fmaf_rn(-t.dy, s.c.x, s.a.z);
+    t.dy2 = t.dy * t.dy;
+    return t;
+}
+__device__ __forceinline__ void surfel_hit_in_row(const SurfelRec& s, const SurfelRowTerms& t, float lx, SurfelHit& e) {
 #pragma clang fp contract(off)
     e.dx = s.c.y + lx;
-    e.dy = s.c.z + ly;
-    const float k0 = __fmaf_rn(e.dx, s.a.w, __fmaf_rn(-e.dy, s.b.z, s.a.x));
-    const float k1 = __fmaf_rn(e.dx, s.b.x, __fmaf_rn(-e.dy, s.b.w, s.a.y));
-    const float k2 = __fmaf_rn(e.dx, s.b.y, __fmaf_rn(-e.dy, s.c.x, s.a.z));
+    e.dy = t.dy;
+    const float k0 = __fmaf_rn(e.dx, s.a.w, t.r0);
+    const float k1 = __fmaf_rn(e.dx, s.b.x, t.r1);
+    const float k2 = __fmaf_rn(e.dx, s.b.y, t.r2);
     e.inv = __builtin_amdgcn_rcpf(k2);
     e.u = k0 * e.inv;
     e.v = k1 * e.inv;
-    e.rho3 = __fmaf_rn(e.u, e.u, e.v * e.v);  // +inf or NaN when the ray runs along the plane (k2 = 0)
-    const float rho2 = 2.f * __fmaf_rn(e.dx, e.dx, e.dy * e.dy);
-    e.own = e.rho3 <= rho2;                     // false for NaN
+    e.rho3 = __fmaf_rn(e.u, e.u, e.v * e.v);
+    const float rho2 = 2.f * __fmaf_rn(e.dx, e.dx, t.dy2);
+    e.own = e.rho3 <= rho2;
     const float rho = e.own ? e.rho3 : rho2;
     e.oG = __builtin_amdgcn_exp2f(__fmaf_rn(rho, NEG_HALF_LOG2E, s.c.w));
 }
 
-// The forward's staged surfel: per row of its band the terms of surfel_hit
-// that depend only on the row, (k_j at the row's first column before the
-// column term, dy^2), then (N12, dx0), (log2 o, rgb) and the entry's list
-// position. surfel_hit_row with them takes the same fp32 steps as surfel_hit,
-// so the forward's decisions are the backward's bit for bit.
+// The forward's staged surfel: per row of its band the terms of the hit that
+// depend only on the row, (k_j at the row's first column before the column
+// term, dy^2, as surfel_row_terms), then (N12, dx0), (log2 o, rgb) and the
+// entry's list position. surfel_hit_row with them takes the same fp32 steps
+// as surfel_hit_in_row, so the forward's decisions are the backward's bit for
+// bit.
 struct alignas(16) SurfelRowRec {
     float4 row[4];
     float4 n;
@@ -184,7 +202,8 @@ __device__ __forceinline__ void surfel_row_rec(const SurfelRec& s, float ly0, Su
     r.e = make_float4(s.c.w, s.d.x, s.d.y, s.d.z);
 }
 
-// surfel_hit's alpha at column lx of a row: K = (k_j at the row, dy^2), N = (N12, dx0)
+// The hit's alpha at column lx of a row (surfel_hit_in_row's): K = (k_j at
+// the row, dy^2), N = (N12, dx0).
 __device__ __forceinline__ float surfel_hit_row(float4 K, float4 N, float lo, float lx) {
 #pragma clang fp contract(off)
     const float dx = N.w + lx;
@@ -317,15 +336,18 @@ struct SurfelBwdShared {
 };
 
 // Backward: the forward's blended entries in reverse per pixel (T restored as
-// T / (1 - alpha), S = the colour behind . dL/dC), PPL pixels per lane (rows
-// band 4 PPL + lane / 16 + 4 k). Per blended entry, with h = alpha dL/dalpha
+// T / (1 - alpha), S = the colour behind . dL/dC). Lane l owns the pixels of
+// tile row r = l / 4 at columns 4 s + l % 4 of its PPL column strips
+// s = band PPL + k (strip s: columns [4 s, 4 s + 4), all 16 rows), so a
+// lane's pixels share one row: the hit's row terms are formed once per entry
+// (surfel_row_terms), and the sums times dy factor out of the pixel loop. Per blended entry, with h = alpha dL/dalpha
 // (zero where alpha sat at 0.99): dL/drho = -h/2. On the surfel's own branch
 // dL/dk = h / k2 (-u, -v, u^2 + v^2), summed as is and times dx and dy; on
 // the filter's branch h (pixel - c) is summed for dL/dc. Record per surfel
 // (16 floats): dL/drgb, sum h, sum dL/dk, sum dx dL/dk, sum dy dL/dk,
 // sum h (pixel - c) over filter-branch pixels, 0.
-// One wave's walk: bands band PPL .. band PPL + PPL - 1 of tile `tile` (pixel
-// k of a lane lies in band band PPL + k), only those set in band_sel (bit k),
+// One wave's walk: strips band PPL .. band PPL + PPL - 1 of tile `tile` (pixel
+// k of a lane lies in strip band PPL + k), only those set in band_sel (bit k),
 // over list entries [walk_lo, walk_hi). A pixel whose row band blends nothing
 // at or past walk_hi in the forward (rb_walk: each band's walk) starts from the
 // final state; the others from the forward's checkpoint ck after entry
@@ -351,17 +373,20 @@ __device__ __forceinline__ void surfel_bwd_walk(int tile, int band, uint32_t ban
     const bool c3 = ((rl >> 2) & 1) != 0;
     const int slot = (c1 ? 4 : 0) + (c2 ? 2 : 0) + (c3 ? 1 : 0);
     const double ox = (double)(tx * TILE) + 0.5, oy = (double)(ty * TILE) + 0.5;
-    const float lx = (float)rl;
+    const int r = lane >> 2, q4 = lane & 3;  // this lane's row in the tile, column within a strip
+    const float ly = (float)r;
     const size_t HW = (size_t)W * H;
-    const int px = tx * TILE + rl;
-    float ly[PPL], T[PPL], g0[PPL], g1[PPL], g2[PPL], S[PPL];
+    const int py = ty * TILE + r;
+    const int rb = r >> 2;
+    const uint32_t rbw = rb == 0 ? rb_walk.x : rb == 1 ? rb_walk.y : rb == 2 ? rb_walk.z : rb_walk.w;
+    float lx[PPL], T[PPL], g0[PPL], g1[PPL], g2[PPL], S[PPL];
     uint32_t last[PPL], band_last[PPL];
     uint32_t mylast = 0u;
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
-        const int r = band * 4 * PPL + row + 4 * k;
-        const int py = ty * TILE + r;
-        ly[k] = (float)r;
+        const int col = 4 * (band * PPL + k) + q4;
+        const int px = tx * TILE + col;
+        lx[k] = (float)col;
         const bool in = px < W && py < H;
         const size_t p = in ? (size_t)py * W + px : 0;
         T[k] = in ? final_T[p] : 1.f;
@@ -371,14 +396,12 @@ __device__ __forceinline__ void surfel_bwd_walk(int tile, int band, uint32_t ban
         g2[k] = in ? dL_dimage[2 * HW + p] : 0.f;
         S[k] = fmaf(bg0, g0[k], fmaf(bg1, g1[k], bg2 * g2[k]));
         band_last[k] = __builtin_amdgcn_readfirstlane(wave_max_u32(last[k]));
-        if (!((band_sel >> k) & 1u)) {  // the band belongs to another wave: none of its entries is walked here
+        if (!((band_sel >> k) & 1u)) {  // the strip belongs to another wave: none of its entries is walked here
             band_last[k] = 0u;
             last[k] = 0u;
         }
-        const int rb = r >> 2;
-        const uint32_t rbw = rb == 0 ? rb_walk.x : rb == 1 ? rb_walk.y : rb == 2 ? rb_walk.z : rb_walk.w;
         if (ck && rbw > (uint32_t)walk_hi) {  // this pixel's row band walked past walk_hi in the forward
-            const int lp = 16 * r + rl;       // the pixel's float4 in a checkpoint slot
+            const int lp = 16 * r + col;      // the pixel's float4 in a checkpoint slot
             const float4 c = ck[lp], e = ck_end[lp];
             const float behind = fmaf(g0[k], e.x - c.y, fmaf(g1[k], e.y - c.z, g2[k] * (e.z - c.w)));
             S[k] = in ? fmaf(T[k], S[k], behind) / c.x : 0.f;
@@ -389,13 +412,13 @@ __device__ __forceinline__ void surfel_bwd_walk(int tile, int band, uint32_t ban
     const uint2 rg = ranges[tile];
     // never walk past the tile's list, whatever n_contrib holds
     const uint32_t maxlast = min(min(mylast, rg.y - rg.x), (uint32_t)walk_hi);
-    // pixel-centre rectangle of the wave's first row band (band k lies 4 k rows lower)
-    const float bx_lo = (float)(tx * TILE) + 0.5f, bx_hi = bx_lo + 15.f;
-    const float by_lo = (float)(ty * TILE + band * 4 * PPL) + 0.5f;
+    // pixel-centre rectangle of the wave's first strip (strip k lies 4 k columns right)
+    const float bx_lo = (float)(tx * TILE + 4 * band * PPL) + 0.5f;
+    const float by_lo = (float)(ty * TILE) + 0.5f, by_hi = by_lo + 15.f;
     for (int hi = (int)maxlast; hi > walk_lo; hi -= NB) {
         const int lo = max(walk_lo, hi - NB);
         const int cnt = hi - lo;
-        bool reach = false;  // some row band this wave walks past the entry may blend it
+        bool reach = false;  // some strip this wave walks past the entry may blend it
         bool clamp = false;  // its alpha may reach the 0.99 clamp
         if (lane < cnt) {
             const uint32_t gg = values[rg.x + lo + lane];
@@ -406,8 +429,8 @@ __device__ __forceinline__ void surfel_bwd_walk(int tile, int band, uint32_t ban
             const uint32_t pl = (uint32_t)(lo + lane);
 #pragma unroll
             for (int k = 0; k < PPL; ++k) {
-                const float y0 = by_lo + (float)(4 * k);
-                reach = reach || (pl < band_last[k] && !sr.misses(bx_lo, bx_hi, y0, y0 + 3.f));
+                const float x0 = bx_lo + (float)(4 * k);
+                reach = reach || (pl < band_last[k] && !sr.misses(x0, x0 + 3.f, by_lo, by_hi));
             }
         }
         uint64_t todo = __ballot(reach);
@@ -425,15 +448,16 @@ __device__ __forceinline__ void surfel_bwd_walk(int tile, int band, uint32_t ban
                 float acc[SURFEL_GRAD_STRIDE];
 #pragma unroll
                 for (int c = 0; c < SURFEL_GRAD_STRIDE; ++c) acc[c] = 0.f;
-                // every band's pixel through one branch-free pass: the blend tests first, one wave vote,
+                // every strip's pixel through one branch-free pass: the blend tests first, one wave vote,
                 // then the gradient terms (a pixel that did not blend takes alpha = 0, which leaves T, S
                 // and every sum unchanged)
+                const SurfelRowTerms rt = surfel_row_terms(R, ly);
                 SurfelHit e[PPL];
                 float al[PPL];
                 bool bl[PPL], anyb = false;
 #pragma unroll
                 for (int k = 0; k < PPL; ++k) {
-                    surfel_hit(R, lx, ly[k], e[k]);
+                    surfel_hit_in_row(R, rt, lx[k], e[k]);
                     al[k] = CLAMP ? fminf(ALPHA_MAX, e[k].oG) : e[k].oG;
                     bl[k] = pos < last[k] && al[k] >= ALPHA_MIN;
                     anyb = anyb || bl[k];
@@ -462,12 +486,13 @@ __device__ __forceinline__ void surfel_bwd_walk(int tile, int band, uint32_t ban
                     acc[7] = fmaf(e[k].dx, dk0, acc[7]);
                     acc[8] = fmaf(e[k].dx, dk1, acc[8]);
                     acc[9] = fmaf(e[k].dx, dk2, acc[9]);
-                    acc[10] = fmaf(e[k].dy, dk0, acc[10]);
-                    acc[11] = fmaf(e[k].dy, dk1, acc[11]);
-                    acc[12] = fmaf(e[k].dy, dk2, acc[12]);
                     acc[13] = fmaf(hf, e[k].dx, acc[13]);
-                    acc[14] = fmaf(hf, e[k].dy, acc[14]);
+                    acc[14] += hf;  // times dy below: the lane's pixels share dy
                 }
+                acc[10] = rt.dy * acc[4];
+                acc[11] = rt.dy * acc[5];
+                acc[12] = rt.dy * acc[6];
+                acc[14] *= rt.dy;
                 // per 16-lane row: values 0-7 and 8-15 by two reduce-scatters (lanes 0-7 hold them)
                 const float ua = row_reduce_scatter8(acc, c1, c2, c3);
                 const float ub = row_reduce_scatter8(acc + 8, c1, c2, c3);
