@@ -250,12 +250,12 @@ __global__ __launch_bounds__(64) void k_surfel_fwd(int W, int H, int TX, int nti
     for (uint32_t bs = rg.x; bs < rg.y; bs += FWD_BATCH) {
         if (!__any(thr < 1.f)) break;
         const uint32_t idx = bs + lane;
-        bool miss = true;
+        bool miss = true, clamp = false;
         SurfelRowRec rec;
         if (idx < rg.y) {
             const uint32_t g = values[idx];
             SurfelRec full;
-            stage_surfel(g, tf, rgb, full, ox, oy);
+            clamp = stage_surfel(g, tf, rgb, full, ox, oy) > CLAMP_FREE_OPACITY;
             surfel_row_rec(full, (float)(band * 4), rec);
             miss = SurfelReach(tf[3 * (size_t)g], tf[3 * (size_t)g + 1], tf[3 * (size_t)g + 2])
                        .misses(bx_lo, bx_hi, by_lo, by_hi);
@@ -269,35 +269,43 @@ __global__ __launch_bounds__(64) void k_surfel_fwd(int W, int H, int TX, int nti
             s_rec[__builtin_amdgcn_mbcnt_hi((uint32_t)(keep >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)keep, 0u))] =
                 rec;
         }
+        const bool clamp_batch = __ballot(!miss && clamp) != 0ull;
         __syncthreads();
-        // entries in runs of 8 (unrolled, one exit test each), the walk test between runs
-        for (int m0 = 0; m0 < cnt; m0 += 8) {
-            uint32_t run_off = (uint32_t)m0 * (uint32_t)sizeof(SurfelRowRec);
-            asm volatile("" : "+v"(run_off));  // one base register per run (opaque to the compiler)
-            const SurfelRowRec* run =
-                reinterpret_cast<const SurfelRowRec*>(reinterpret_cast<const char*>(s_rec) + run_off);
+        // entries in runs of 8 (unrolled, one exit test each), the walk test between runs; a batch none of
+        // whose kept records has an opacity above CLAMP_FREE_OPACITY never reaches the alpha clamp (o G <= o)
+        // and takes a copy without the clamp's min
+        auto walk_runs = [&](auto clamp_tag) {
+            constexpr bool CLAMP = decltype(clamp_tag)::value;
+            for (int m0 = 0; m0 < cnt; m0 += 8) {
+                uint32_t run_off = (uint32_t)m0 * (uint32_t)sizeof(SurfelRowRec);
+                asm volatile("" : "+v"(run_off));  // one base register per run (opaque to the compiler)
+                const SurfelRowRec* run =
+                    reinterpret_cast<const SurfelRowRec*>(reinterpret_cast<const char*>(s_rec) + run_off);
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                if (m0 + m >= cnt) break;
-                const float4 D = run[m].e;  // (log2 o, rgb)
-                const float oG = surfel_hit_row(run[m].row[row], run[m].n, D.x, lx);
-                const uint32_t pos = run[m].pos;
-                const float al = fminf(ALPHA_MAX, oG);
-                const bool pass = al >= thr;
-                const float Tn = __fmaf_rn(-al, T, T);
-                const bool stop = pass && Tn < T_MIN;  // the entry would end the pixel: not blended
-                const bool blend = pass && !stop;
-                thr = stop ? 2.f : thr;
-                const float wt = blend ? al * T : 0.f;
-                C0 = fmaf(D.y, wt, C0);
-                C1 = fmaf(D.z, wt, C1);
-                C2 = fmaf(D.w, wt, C2);
-                T = blend ? Tn : T;
-                last = blend ? pos : last;
-                asm volatile("" : "+v"(last) : "v"(pos));  // pos is read with the record, not under the mask
+                for (int m = 0; m < 8; ++m) {
+                    if (m0 + m >= cnt) break;
+                    const float4 D = run[m].e;  // (log2 o, rgb)
+                    const float oG = surfel_hit_row(run[m].row[row], run[m].n, D.x, lx);
+                    const uint32_t pos = run[m].pos;
+                    const float al = CLAMP ? fminf(ALPHA_MAX, oG) : oG;
+                    const bool pass = al >= thr;
+                    const float Tn = __fmaf_rn(-al, T, T);
+                    const bool stop = pass && Tn < T_MIN;  // the entry would end the pixel: not blended
+                    const bool blend = pass && !stop;
+                    thr = stop ? 2.f : thr;
+                    const float wt = blend ? al * T : 0.f;
+                    C0 = fmaf(D.y, wt, C0);
+                    C1 = fmaf(D.z, wt, C1);
+                    C2 = fmaf(D.w, wt, C2);
+                    T = blend ? Tn : T;
+                    last = blend ? pos : last;
+                    asm volatile("" : "+v"(last) : "v"(pos));  // pos is read with the record, not under the mask
+                }
+                if (!__any(thr < 1.f)) break;
             }
-            if (!__any(thr < 1.f)) break;
-        }
+        };
+        if (clamp_batch) walk_runs(std::true_type{});
+        else walk_runs(std::false_type{});
         __syncthreads();
         if (ckpt) {
             // the state after a whole batch that ends a checkpoint interval, while still walking
