@@ -697,9 +697,10 @@ __device__ __forceinline__ uint32_t super_count(int X0, int X1, int Y0, int Y1) 
 
 // P = sum of tiles_touched, P1 = number of (super-tile, Gaussian) entries and
 // the number of visible Gaussians, per block of ST Gaussians (index order),
-// into part[3 b .. 3 b + 2]; k_pair_sum then totals P and P1 and scans the
-// visible counts, so that the compaction (k_compact_visible) runs
-// straight after it.
+// into part[3 b .. 3 b + 2]; the compaction (k_compact_visible) totals P and
+// P1 and sums the visible counts before each block itself, or, for more
+// blocks than it does that for, k_pair_sum does both first. Block 0 also
+// clears the radix passes' digit-total buffers.
 constexpr int CT = 1024, CI = ST / CT;  // threads and items per thread of the per-Gaussian passes
 
 __global__ __launch_bounds__(CT) void k_pair_totals(int n, const uint32_t* __restrict__ tiles,
